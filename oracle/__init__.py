@@ -1,0 +1,180 @@
+"""CPU oracle for the int8 paged KV cache (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library and its Python binding
+never do: the two implementations share no code.
+
+The arithmetic lives in ``q8_oracle.c`` (plain C, binary32 quantizer and
+binary64 decode); this module only builds it with gcc and marshals numpy arrays
+through ctypes.  Each C function cites the page passage it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q8_oracle.c")
+_LIB = os.path.join(_HERE, "libq8oracle.so")
+PAD_SLOT = 0xFFFFFFFF
+
+_ERRORS = {1: "shape", 2: "index out of range", 3: "input outside the contract", 4: "out of memory"}
+
+
+def build(force: bool = True) -> str:
+    """Compile q8_oracle.c into libq8oracle.so next to it (gcc, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        U = ctypes.c_uint32
+        lib.q8o_quantize_row.argtypes = [P, U, P]
+        lib.q8o_quantize_row.restype = ctypes.c_int
+        lib.q8o_dequantize_row.argtypes = [P, U, P]
+        lib.q8o_dequantize_row.restype = None
+        lib.q8o_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U]
+        lib.q8o_cache_write.restype = ctypes.c_int
+        dec = [P, U, P, P, P, U, P, U, P, P, U, U, U, U, U, U, U, ctypes.c_float, ctypes.c_int]
+        lib.q8o_paged_decode.argtypes = [P] + dec
+        lib.q8o_paged_decode.restype = ctypes.c_int
+        lib.q8o_paged_decode_units.argtypes = [P, P, U] + dec
+        lib.q8o_paged_decode_units.restype = ctypes.c_int
+        lib.q8o_max_threads.argtypes = []
+        lib.q8o_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError("oracle %s failed: %s (code %d)" % (what, _ERRORS.get(rc, "?"), rc))
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def max_threads() -> int:
+    return int(_load().q8o_max_threads())
+
+
+def quantize_row(x) -> np.ndarray:
+    """Pack one f32 vector into head_size/4 code words plus one scale word."""
+    x = _c(x, np.float32)
+    hs = x.shape[-1]
+    row = np.zeros(hs // 4 + 1, dtype=np.uint32)
+    _check(_load().q8o_quantize_row(_ptr(x), hs, _ptr(row)), "quantize_row")
+    return row
+
+
+def quantize_rows(x) -> np.ndarray:
+    """Apply quantize_row to every vector along the last axis."""
+    x = _c(x, np.float32)
+    hs = x.shape[-1]
+    flat = x.reshape(-1, hs)
+    out = np.zeros((flat.shape[0], hs // 4 + 1), dtype=np.uint32)
+    lib = _load()
+    for i in range(flat.shape[0]):
+        _check(lib.q8o_quantize_row(_ptr(flat[i]), hs, _ptr(out[i])), "quantize_row")
+    return out.reshape(x.shape[:-1] + (hs // 4 + 1,))
+
+
+def dequantize_row(row, head_size: int) -> np.ndarray:
+    row = _c(row, np.uint32)
+    out = np.zeros(head_size, dtype=np.float64)
+    _load().q8o_dequantize_row(_ptr(row), head_size, _ptr(out))
+    return out
+
+
+def cache_write(key, value, key_cache, value_cache, slot_mapping, num_kv_heads, head_size,
+                block_size, num_blocks=None, key_stride=None, value_stride=None):
+    """Quantize + pack K and V rows into the caches, in place (numpy u32 arrays).
+
+    key/value: f32 arrays whose first axis is the token; row t's head h starts at
+    t*stride + h*head_size in the flattened array.
+    """
+    key = _c(key, np.float32)
+    value = _c(value, np.float32)
+    slot_mapping = _c(slot_mapping, np.uint32)
+    for c in (key_cache, value_cache):
+        if c.dtype != np.uint32 or not c.flags.c_contiguous:
+            raise ValueError("caches must be contiguous uint32 arrays")
+    T = slot_mapping.shape[0]
+    ks = key_stride if key_stride is not None else (key.size // T if T else num_kv_heads * head_size)
+    vs = value_stride if value_stride is not None else (value.size // T if T else num_kv_heads * head_size)
+    wpt = head_size // 4 + 1
+    nb = num_blocks if num_blocks is not None else key_cache.size // (num_kv_heads * block_size * wpt)
+    _check(_load().q8o_cache_write(_ptr(key), ks, _ptr(value), vs, _ptr(key_cache),
+                                   _ptr(value_cache), _ptr(slot_mapping), T, num_kv_heads,
+                                   head_size, block_size, nb), "cache_write")
+
+
+def _decode_common(q, key_cache, value_cache, block_tables, context_lens, max_context_len,
+                   num_kv_heads, block_size, visible_pos, num_visible, vis_stride, num_blocks):
+    q = _c(q, np.float32)
+    S, H, hs = q.shape
+    bt = _c(block_tables, np.uint32)
+    cl = _c(context_lens, np.uint32)
+    vp = None if visible_pos is None else _c(visible_pos, np.uint32)
+    nv = None if num_visible is None else _c(num_visible, np.uint32)
+    if vp is not None and vis_stride is None:
+        vis_stride = vp.shape[-1]
+    wpt = hs // 4 + 1
+    nb = num_blocks if num_blocks is not None else key_cache.size // (num_kv_heads * block_size * wpt)
+    if max_context_len is None:
+        max_context_len = int(cl.max()) if cl.size else 0
+    return q, S, H, hs, bt, cl, vp, nv, vis_stride or 0, nb, max_context_len
+
+
+def paged_decode(q, key_cache, value_cache, block_tables, context_lens, scale, num_kv_heads,
+                 block_size, max_context_len=None, visible_pos=None, num_visible=None,
+                 vis_stride=None, num_blocks=None, nthreads=0) -> np.ndarray:
+    """Decode every (seq, head); q is [S, H, hs] f32, result [S, H, hs] f32."""
+    q, S, H, hs, bt, cl, vp, nv, vstr, nb, mcl = _decode_common(
+        q, key_cache, value_cache, block_tables, context_lens, max_context_len, num_kv_heads,
+        block_size, visible_pos, num_visible, vis_stride, num_blocks)
+    out = np.zeros((S, H, hs), dtype=np.float32)
+    _check(_load().q8o_paged_decode(_ptr(out), _ptr(q), H * hs, _ptr(key_cache), _ptr(value_cache),
+                                    _ptr(bt), bt.shape[-1], _ptr(cl), mcl, _ptr(vp), _ptr(nv), vstr,
+                                    S, H, num_kv_heads, hs, block_size, nb, float(scale), nthreads),
+           "paged_decode")
+    return out
+
+
+def paged_decode_units(units, q, key_cache, value_cache, block_tables, context_lens, scale,
+                       num_kv_heads, block_size, max_context_len=None, visible_pos=None,
+                       num_visible=None, vis_stride=None, num_blocks=None, nthreads=0) -> np.ndarray:
+    """Decode only the listed (seq, head) pairs; result [len(units), hs] f32."""
+    q, S, H, hs, bt, cl, vp, nv, vstr, nb, mcl = _decode_common(
+        q, key_cache, value_cache, block_tables, context_lens, max_context_len, num_kv_heads,
+        block_size, visible_pos, num_visible, vis_stride, num_blocks)
+    u = _c(np.asarray(units).reshape(-1, 2), np.uint32)
+    out = np.zeros((u.shape[0], hs), dtype=np.float32)
+    _check(_load().q8o_paged_decode_units(_ptr(out), _ptr(u), u.shape[0], _ptr(q), H * hs,
+                                          _ptr(key_cache), _ptr(value_cache), _ptr(bt), bt.shape[-1],
+                                          _ptr(cl), mcl, _ptr(vp), _ptr(nv), vstr, S, H,
+                                          num_kv_heads, hs, block_size, nb, float(scale), nthreads),
+           "paged_decode_units")
+    return out

@@ -1,0 +1,312 @@
+/*
+ * q8_oracle.c -- plain, slow CPU oracle for the int8 paged KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg load this library.  The HIP library never calls it, and the
+ * two share no code, headers, tables or helpers.
+ *
+ * What it computes, and the passage each part follows:
+ *
+ *   Cache format ("paged_attn_q8.comp" and "reshape_and_cache_q8.comp" pages,
+ *   header comments on the quantized cache): a u32 buffer laid out
+ *   [num_blocks, num_kv_heads, block_size, words_per_token] with
+ *   words_per_token = head_size/4 + 1.  A token's vector for one kv head is
+ *   head_size/4 code words, four int8 codes per word with element 4w+l in byte
+ *   l (little-endian lane), followed by one word holding the f32 scale's bits.
+ *
+ *   Quantize + pack ("reshape_and_cache_q8.comp" page, main(): the KEY block
+ *   "amax reduce -> scale -> pack" and the identical VALUE block).  Binary32,
+ *   one IEEE operation per step, as the page's shader states them:
+ *     amax = max_d |x_d| (starting from 0)
+ *     inv  = amax > 0 ? 127/amax : 0
+ *     code = clamp(round(x_d * inv), -127, 127), ties to even (the page leaves
+ *            the tie rule to the implementation; this build fixes even)
+ *     scale word = bits(amax > 0 ? amax/127 : 1.0)
+ *   A slot equal to 0xFFFFFFFF is a pad: nothing is read or written.
+ *
+ *   Decode ("paged_attn_q8.comp" page, main(): output = softmax(scale*Q.K^T).V
+ *   with K and V dequantized on read as code * token_scale).  This oracle writes
+ *   out the plain definition in binary64, not the page's three-pass structure:
+ *     L     = min(context_lens[s], max_context_len)   (or a visible list)
+ *     kvh   = h / (num_heads / num_kv_heads)
+ *     k_hat = code * kscale, v_hat = code * vscale    (exact in binary64)
+ *     z_t   = scale * sum_d q_d * k_hat_{t,d}
+ *     o_d   = sum_t exp(z_t - max z) v_hat_{t,d} / sum_t exp(z_t - max z)
+ *   rounded once to f32.  An empty position set gives a zero row (the page's
+ *   1/(exp_sum + 1e-6) with exp_sum = 0 multiplies a zero accumulator).  For a
+ *   non-empty set the page's 1e-6 is dropped: exp_sum >= 1 there, so it moves
+ *   the result by at most 1e-6 relative, below the parity tolerance.
+ *
+ *   Visible-list decode (the "attention.rs" page, the selective branch of the
+ *   per-row split decode that binds the row's visible token list): the row
+ *   attends exactly the listed logical positions; context_lens is unused.
+ *
+ * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fopenmp -fPIC
+ * -shared.  On x86-64 (SSE, FLT_EVAL_METHOD == 0) every float operation above
+ * rounds to binary32 once.  OpenMP only spreads independent (seq, head) units
+ * over threads; each unit's arithmetic is sequential, so the result does not
+ * depend on the thread count.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define Q8O_PAD_SLOT 0xFFFFFFFFu
+
+enum {
+    Q8O_OK = 0,
+    Q8O_ERR_SHAPE = 1,   /* head_size not a positive multiple of 4, etc. */
+    Q8O_ERR_RANGE = 2,   /* an index read from an input array is out of range */
+    Q8O_ERR_INPUT = 3,   /* non-finite input, or 0 < amax < 2^-100 (outside the contract) */
+    Q8O_ERR_NOMEM = 4
+};
+
+static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* One token vector x[0..head_size) -> head_size/4 code words + 1 scale word. */
+int q8o_quantize_row(const float* x, uint32_t head_size, uint32_t* row)
+{
+    if (head_size == 0 || head_size % 4 != 0) return Q8O_ERR_SHAPE;
+    float amax = 0.0f;
+    for (uint32_t d = 0; d < head_size; ++d) {
+        if (!isfinite(x[d])) return Q8O_ERR_INPUT;
+        float a = fabsf(x[d]);
+        if (a > amax) amax = a;
+    }
+    if (amax > 0.0f && amax < 0x1p-100f) return Q8O_ERR_INPUT;
+    float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    for (uint32_t w = 0; w < head_size / 4; ++w) {
+        uint32_t word = 0;
+        for (uint32_t l = 0; l < 4; ++l) {
+            float p = x[4 * w + l] * inv;      /* one f32 multiply */
+            float r = nearbyintf(p);           /* default mode: nearest, ties to even */
+            if (r < -127.0f) r = -127.0f;
+            if (r > 127.0f) r = 127.0f;
+            int8_t c = (int8_t)(int)r;
+            word |= (uint32_t)(uint8_t)c << (8u * l);
+        }
+        row[w] = word;
+    }
+    row[head_size / 4] = f32_to_bits(amax > 0.0f ? amax / 127.0f : 1.0f);
+    return Q8O_OK;
+}
+
+/* Signed code of element d of a packed row: byte d%4 of word d/4, sign-extended. */
+static int code_at(const uint32_t* row, uint32_t d)
+{
+    uint32_t byte = (row[d / 4] >> (8u * (d % 4))) & 0xFFu;
+    return (int)(int8_t)(uint8_t)byte;
+}
+
+/* Dequantize a packed row to binary64: out[d] = code_d * scale (exact). */
+void q8o_dequantize_row(const uint32_t* row, uint32_t head_size, double* out)
+{
+    double scale = (double)bits_to_f32(row[head_size / 4]);
+    for (uint32_t d = 0; d < head_size; ++d) out[d] = (double)code_at(row, d) * scale;
+}
+
+/* Word offset of (slot, kv head) in a cache laid out [blocks, kv heads, block_size, wpt]. */
+static uint64_t row_offset(uint64_t block, uint64_t off, uint64_t kvh,
+                           uint64_t num_kv_heads, uint64_t block_size, uint64_t wpt)
+{
+    return ((block * num_kv_heads + kvh) * block_size + off) * wpt;
+}
+
+int q8o_cache_write(const float* key, uint32_t key_stride,
+                    const float* value, uint32_t value_stride,
+                    uint32_t* key_cache, uint32_t* value_cache,
+                    const uint32_t* slot_mapping, uint32_t num_tokens,
+                    uint32_t num_kv_heads, uint32_t head_size,
+                    uint32_t block_size, uint32_t num_blocks)
+{
+    if (head_size == 0 || head_size % 4 != 0 || block_size == 0 || num_kv_heads == 0)
+        return Q8O_ERR_SHAPE;
+    if ((uint64_t)key_stride < (uint64_t)num_kv_heads * head_size ||
+        (uint64_t)value_stride < (uint64_t)num_kv_heads * head_size)
+        return Q8O_ERR_SHAPE;
+    uint32_t wpt = head_size / 4 + 1;
+    for (uint32_t t = 0; t < num_tokens; ++t) {
+        uint32_t slot = slot_mapping[t];
+        if (slot == Q8O_PAD_SLOT) continue;
+        uint64_t block = slot / block_size, off = slot % block_size;
+        if (block >= num_blocks) return Q8O_ERR_RANGE;
+        for (uint32_t h = 0; h < num_kv_heads; ++h) {
+            uint64_t dst = row_offset(block, off, h, num_kv_heads, block_size, wpt);
+            int rc = q8o_quantize_row(key + (uint64_t)t * key_stride + (uint64_t)h * head_size,
+                                      head_size, key_cache + dst);
+            if (rc != Q8O_OK) return rc;
+            rc = q8o_quantize_row(value + (uint64_t)t * value_stride + (uint64_t)h * head_size,
+                                  head_size, value_cache + dst);
+            if (rc != Q8O_OK) return rc;
+        }
+    }
+    return Q8O_OK;
+}
+
+typedef struct {
+    const float* q; uint32_t q_stride;
+    const uint32_t* key_cache; const uint32_t* value_cache;
+    const uint32_t* block_tables; uint32_t max_num_blocks_per_seq;
+    const uint32_t* context_lens; uint32_t max_context_len;
+    const uint32_t* visible_pos; const uint32_t* num_visible; uint32_t vis_stride;
+    uint32_t num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks;
+    double scale;
+} decode_args;
+
+/*
+ * One (seq, head) unit.  out_row gets head_size floats; work holds 2*head_size
+ * doubles plus one double per attended position.
+ */
+static int decode_unit(const decode_args* a, uint32_t s, uint32_t h, float* out_row)
+{
+    const uint32_t hs = a->head_size, wpt = hs / 4 + 1;
+    const uint32_t kvh = h / (a->num_heads / a->num_kv_heads);
+    uint32_t n;
+    const uint32_t* pos = NULL;
+    if (a->visible_pos) {
+        n = a->num_visible[s];
+        if (n > a->vis_stride) return Q8O_ERR_RANGE;
+        pos = a->visible_pos + (uint64_t)s * a->vis_stride;
+    } else {
+        n = a->context_lens[s];
+        if (n > a->max_context_len) n = a->max_context_len;
+    }
+    if (n == 0) {
+        for (uint32_t d = 0; d < hs; ++d) out_row[d] = 0.0f;
+        return Q8O_OK;
+    }
+    double* z = (double*)malloc(sizeof(double) * ((size_t)n + 2u * hs));
+    if (!z) return Q8O_ERR_NOMEM;
+    double* k_hat = z + n;
+    double* o = k_hat + hs;
+    const float* qv = a->q + (uint64_t)s * a->q_stride + (uint64_t)h * hs;
+    const uint32_t* bt = a->block_tables + (uint64_t)s * a->max_num_blocks_per_seq;
+
+    /* pass over positions: logits z_t = scale * <q, k_hat_t> */
+    double zmax = -INFINITY;
+    for (uint32_t i = 0; i < n; ++i) {
+        uint32_t t = pos ? pos[i] : i;
+        uint32_t j = t / a->block_size;
+        if (j >= a->max_num_blocks_per_seq) { free(z); return Q8O_ERR_RANGE; }
+        uint32_t phys = bt[j];
+        if (phys >= a->num_blocks) { free(z); return Q8O_ERR_RANGE; }
+        const uint32_t* krow = a->key_cache +
+            row_offset(phys, t % a->block_size, kvh, a->num_kv_heads, a->block_size, wpt);
+        q8o_dequantize_row(krow, hs, k_hat);
+        double dot = 0.0;
+        for (uint32_t d = 0; d < hs; ++d) dot += (double)qv[d] * k_hat[d];
+        z[i] = a->scale * dot;
+        if (!(z[i] > -INFINITY && z[i] < INFINITY)) { free(z); return Q8O_ERR_INPUT; }
+        if (z[i] > zmax) zmax = z[i];
+    }
+    /* weights and weighted sum of dequantized V */
+    double denom = 0.0;
+    for (uint32_t d = 0; d < hs; ++d) o[d] = 0.0;
+    for (uint32_t i = 0; i < n; ++i) {
+        uint32_t t = pos ? pos[i] : i;
+        uint32_t phys = bt[t / a->block_size];
+        const uint32_t* vrow = a->value_cache +
+            row_offset(phys, t % a->block_size, kvh, a->num_kv_heads, a->block_size, wpt);
+        double w = exp(z[i] - zmax);
+        denom += w;
+        q8o_dequantize_row(vrow, hs, k_hat);     /* reuse buffer for v_hat */
+        for (uint32_t d = 0; d < hs; ++d) o[d] += w * k_hat[d];
+    }
+    for (uint32_t d = 0; d < hs; ++d) out_row[d] = (float)(o[d] / denom);
+    free(z);
+    return Q8O_OK;
+}
+
+static int check_decode_shape(const decode_args* a)
+{
+    if (a->head_size == 0 || a->head_size % 4 != 0 || a->block_size == 0 ||
+        a->num_kv_heads == 0 || a->num_heads == 0 || a->num_heads % a->num_kv_heads != 0)
+        return Q8O_ERR_SHAPE;
+    if ((uint64_t)a->q_stride < (uint64_t)a->num_heads * a->head_size) return Q8O_ERR_SHAPE;
+    return Q8O_OK;
+}
+
+/*
+ * Decode selected (seq, head) units: units[2*i] = seq, units[2*i+1] = head;
+ * out receives head_size floats per unit, in unit order.  visible_pos == NULL
+ * selects dense mode.  nthreads <= 0 uses the OpenMP default.
+ */
+int q8o_paged_decode_units(float* out, const uint32_t* units, uint32_t num_units,
+                           const float* q, uint32_t q_stride,
+                           const uint32_t* key_cache, const uint32_t* value_cache,
+                           const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                           const uint32_t* context_lens, uint32_t max_context_len,
+                           const uint32_t* visible_pos, const uint32_t* num_visible,
+                           uint32_t vis_stride,
+                           uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                           uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                           float scale, int nthreads)
+{
+    decode_args a = { q, q_stride, key_cache, value_cache, block_tables,
+                      max_num_blocks_per_seq, context_lens, max_context_len,
+                      visible_pos, num_visible, vis_stride, num_seqs, num_heads,
+                      num_kv_heads, head_size, block_size, num_blocks, (double)scale };
+    int rc = check_decode_shape(&a);
+    if (rc != Q8O_OK) return rc;
+    for (uint32_t i = 0; i < num_units; ++i)
+        if (units[2 * i] >= num_seqs || units[2 * i + 1] >= num_heads) return Q8O_ERR_RANGE;
+    int err = Q8O_OK;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < (int64_t)num_units; ++i) {
+        int r = decode_unit(&a, units[2 * i], units[2 * i + 1], out + (uint64_t)i * head_size);
+        if (r != Q8O_OK) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+            err = r;
+        }
+    }
+    (void)nthreads;
+    return err;
+}
+
+/* Decode every (seq, head): out is [num_seqs, num_heads, head_size] dense f32. */
+int q8o_paged_decode(float* out, const float* q, uint32_t q_stride,
+                     const uint32_t* key_cache, const uint32_t* value_cache,
+                     const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                     const uint32_t* context_lens, uint32_t max_context_len,
+                     const uint32_t* visible_pos, const uint32_t* num_visible,
+                     uint32_t vis_stride,
+                     uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                     uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                     float scale, int nthreads)
+{
+    uint64_t nu = (uint64_t)num_seqs * num_heads;
+    uint32_t* units = (uint32_t*)malloc(sizeof(uint32_t) * 2 * (nu ? nu : 1));
+    if (!units) return Q8O_ERR_NOMEM;
+    for (uint64_t i = 0; i < nu; ++i) {
+        units[2 * i] = (uint32_t)(i / num_heads);
+        units[2 * i + 1] = (uint32_t)(i % num_heads);
+    }
+    int rc = q8o_paged_decode_units(out, units, (uint32_t)nu, q, q_stride, key_cache,
+                                    value_cache, block_tables, max_num_blocks_per_seq,
+                                    context_lens, max_context_len, visible_pos,
+                                    num_visible, vis_stride, num_seqs, num_heads,
+                                    num_kv_heads, head_size, block_size, num_blocks,
+                                    scale, nthreads);
+    free(units);
+    return rc;
+}
+
+int q8o_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
