@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the int8 paged-KV decode step on one MI355X.
+
+One step = the whole hot path on the Llama-3-8B-shaped batch (64 sequences,
+32 query heads, 8 kv heads, head_size 128, block_size 16, context lengths
+uniform in [512, 4096]): q8_cache_write of the 64 new tokens (one per
+sequence) followed by q8_paged_decode over every sequence's full context.
+
+Inputs are resident in HBM before timing.  The step rotates over several
+layer caches (copies of the filled cache at different addresses), as a model's
+layers do, so each step reads its KV from HBM rather than from the 256 MB
+Infinity Cache left warm by the previous step.
+
+Printed: one JSON line with the effective int8-KV read rate (codes + scale
+word of every attended row, K and V) as GB/s, its fraction of the 8 TB/s HBM
+peak, decode (seq, head)/s, per-launch kernel timing from HIP events, the
+roofline entry of the decode kernel and the CPU oracle's rate on the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective int8 KV read GB/s (% of HBM peak) + decode (seq,head)/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q8_paged_decode_llama_traffic.txt")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--layers", type=int, default=8, help="layer caches rotated over (MALL defeat)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--hot", action="store_true", help="also time back-to-back steps on one cache")
+    return p.parse_args()
+
+
+def kernel_sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "int8_paged_kv_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(digest: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when it is absent or was taken on different kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_sources_sha256_16") != digest:
+            return None
+        return float(kv["hbm_bytes_per_step"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the decode hot path has no multi-GPU step in this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int8_paged_kv_amd import q8_cache_write, q8_paged_decode, q8_paged_decode_workspace_size, load_library
+    from int8_paged_kv_amd import workloads as wl
+
+    load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.llama()
+
+    def u32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to(dev)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    # ---- fill one cache, replicate it per layer ----
+    t_setup = time.time()
+    kh, vh = w.empty_caches()
+    kc0, vc0 = u32(kh), u32(vh)
+    fill_host = []
+    for slots, k, v in w.fill_chunks():
+        q8_cache_write(f32(k), f32(v), kc0, vc0, u32(slots), w.num_kv_heads, w.head_size, w.block_size)
+        fill_host.append((slots, k, v))
+    step_slots, step_k, step_v = w.step_write()
+    torch.cuda.synchronize()
+    layers = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(args.layers - 1)]
+    q = f32(w.q())
+    bt, cl = u32(w.block_tables), u32(w.context_lens)
+    sk, sv, ss = f32(step_k), f32(step_v), u32(step_slots)
+    S, H, Hkv, hs = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size
+    mcl = w.max_context_len
+    ws = torch.empty(max(1, q8_paged_decode_workspace_size(S, H, Hkv, hs, w.block_size, mcl)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((S, H, hs), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    def step(i, ev=None):
+        kc, vc = layers[i % len(layers)]
+        if ev is not None:
+            ev[0].record()
+        q8_cache_write(sk, sv, kc, vc, ss, Hkv, hs, w.block_size)
+        if ev is not None:
+            ev[1].record()
+        q8_paged_decode(q, kc, vc, bt, cl, w.scale, Hkv, w.block_size, max_context_len=mcl,
+                        out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, wall clock ----
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- per-launch durations with HIP events on the launch stream ----
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3    # us
+    t_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+
+    hot = None
+    if args.hot:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(0, ev[i])
+        torch.cuda.synchronize()
+        th = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+        hot = {"decode_us_median": float(np.median(th)),
+               "effective_GBps": w.effective_kv_bytes() / (np.median(th) * 1e-6) / 1e9}
+
+    B = w.effective_kv_bytes()
+    step_s = ms_per_step * 1e-3
+    value = B / step_s / 1e9
+    dec_mean = float(t_dec.mean())
+    achieved = B / (dec_mean * 1e-6) / 1e9
+    digest = kernel_sources_digest()
+    traffic = read_traffic(digest)
+
+    # ---- correctness of the timed configuration + CPU oracle baseline ----
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        import oracle
+        oracle.build(force=False)
+        for slots, k, v in fill_host:
+            oracle.cache_write(k, v, kh, vh, slots, Hkv, hs, w.block_size)
+        oracle.cache_write(step_k, step_v, kh, vh, step_slots, Hkv, hs, w.block_size)
+        nthreads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16") or 16))
+        qh = w.q()
+        reps, t_cpu = 0, 0.0
+        ref = None
+        while t_cpu < args.cpu_seconds or reps == 0:
+            c0 = time.perf_counter()
+            ref = oracle.paged_decode(qh, kh, vh, w.block_tables, w.context_lens, w.scale, Hkv, w.block_size,
+                                      max_context_len=mcl, nthreads=nthreads)
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        cpu = {"value": B * reps / t_cpu / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+               "sample": "the full decode step (all 2048 (seq,head) rows, binary64 plain definition) "
+                         "repeated %d times in %.1f s" % (reps, t_cpu)}
+        got = out.cpu().numpy()
+        err = np.abs(got.astype(np.float64) - ref)
+        parity = {"max_abs_err": float(err.max()),
+                  "within_1e-4": bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3-8B-shaped decode step: 64-token q8 cache write + q8 paged decode, "
+                               "S=64 H=32 Hkv=8 hs=128 bs=16 L~U[512,4096] (seed 2), %d rotated layer caches"
+                               % len(layers),
+                   "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv, "head_size": hs, "block_size": w.block_size,
+                   "attended_tokens": int(w.attended_counts().sum()), "effective_kv_bytes": B,
+                   "kv_storage": "int8 codes + f32 per-token scale"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_heads_per_s": round(S * H / step_s, 1),
+        "decode": {"us_mean": round(dec_mean, 2), "us_median": round(float(np.median(t_dec)), 2),
+                   "us_p10": round(float(np.percentile(t_dec, 10)), 2),
+                   "us_p90": round(float(np.percentile(t_dec, 90)), 2),
+                   "effective_GBps": round(achieved, 1),
+                   "seq_heads_per_s": round(S * H / (dec_mean * 1e-6), 1)},
+        "cache_write": {"us_mean": round(float(t_write.mean()), 2), "tokens": int(step_slots.size)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "q8_paged_decode (split + merge launches)",
+                     "algorithmic_bytes_per_launch": B},
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+        "hot_single_cache": hot,
+        "setup_s": round(setup_s, 1),
+        "kernel_sources_sha256_16": digest,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * q8kv.h -- C ABI of libq8kv.so: int8 paged KV cache write and single-query
+ * paged decode attention on AMD MI355X (gfx950).
+ *
+ * Cache format (the "paged_attn_q8.comp" and "reshape_and_cache_q8.comp"
+ * pages, header comment "Quantized cache (K and V), u32 buffer"):
+ *   a u32 buffer [num_blocks, num_kv_heads, block_size, words_per_token],
+ *   words_per_token = head_size/4 + 1.  One token's vector for one kv head is
+ *   head_size/4 code words, each holding four signed int8 codes with element
+ *   4w+l in byte l (little-endian lane), followed by one word holding the bits
+ *   of the f32 per-token scale.  K and V use two separate buffers of this shape.
+ *   A value dequantizes as code * scale.
+ *
+ * Conventions for every entry point:
+ *   - Array pointers are DEVICE pointers owned by the caller.  The library
+ *     keeps no per-call state and allocates no memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work; they never synchronize.  They are reentrant.
+ *   - Shapes are validated on the host before anything is enqueued; on any
+ *     non-OK return nothing has been enqueued.
+ *   - The CONTENTS of device arrays are a caller contract and are not checked
+ *     (as in the pages' shaders): slots below num_blocks*block_size or the pad
+ *     value, distinct non-pad slots within one write, block ids below
+ *     num_blocks, block-table rows holding valid ids for every block a
+ *     sequence uses, finite inputs.  Breaking it is undefined behaviour.
+ *   - head_size must be a multiple of 4 and at most 256 (the pages' maximum).
+ */
+#ifndef Q8KV_H
+#define Q8KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* slot_mapping value meaning "skip this token" (the writer page's PAD_SLOT). */
+#define Q8_PAD_SLOT 0xFFFFFFFFu
+#define Q8_MAX_HEAD_SIZE 256u
+
+typedef enum {
+    Q8_OK = 0,
+    Q8_ERR_NULL = 1,         /* a required pointer is NULL */
+    Q8_ERR_SHAPE = 2,        /* sizes or strides violate the limits listed per call */
+    Q8_ERR_WORKSPACE = 3,    /* workspace too small or not 16-byte aligned */
+    Q8_ERR_HIP = 4,          /* a HIP launch failed; see q8_last_hip_error() */
+    Q8_ERR_UNSUPPORTED = 5   /* a valid combination this build does not handle */
+} q8_status;
+
+/*
+ * q8_cache_write -- quantize the new K and V vectors of num_tokens tokens and
+ * pack them into the paged caches ("reshape_and_cache_q8.comp" page, main():
+ * per (token, kv head), amax = max|x|, inv = amax > 0 ? 127/amax : 0, code =
+ * clamp(round(x*inv), -127, 127), scale word = bits(amax > 0 ? amax/127 : 1.0);
+ * K and V are both written by the one call).
+ *
+ *   key, value   f32 device arrays: element d of kv head h of token t is at
+ *                key[t*key_stride + h*head_size + d] (resp. value_stride).
+ *   key_cache,   u32 device caches [num_blocks, num_kv_heads, block_size,
+ *   value_cache  head_size/4 + 1], written at row (slot/block_size, h,
+ *                slot%block_size) for every non-pad slot.
+ *   slot_mapping u32 [num_tokens]; Q8_PAD_SLOT skips the token entirely
+ *                (nothing read, nothing written).
+ *
+ * Rounding: every step is one IEEE binary32 operation with round-to-nearest,
+ * and the round() of the page is round-half-even.  The output is bit-exact.
+ * Errors: Q8_ERR_NULL for a NULL array with num_tokens > 0; Q8_ERR_SHAPE when
+ * head_size is 0, not a multiple of 4 or above 256, when block_size or
+ * num_kv_heads is 0, or when a stride is below num_kv_heads*head_size.
+ * num_tokens == 0 returns Q8_OK and enqueues nothing.
+ */
+q8_status q8_cache_write(const float* key, uint32_t key_stride,
+                         const float* value, uint32_t value_stride,
+                         uint32_t* key_cache, uint32_t* value_cache,
+                         const uint32_t* slot_mapping, uint32_t num_tokens,
+                         uint32_t num_kv_heads, uint32_t head_size,
+                         uint32_t block_size, uint32_t num_blocks, void* stream);
+
+/*
+ * q8_paged_decode_workspace_size -- bytes of device workspace q8_paged_decode
+ * needs for these sizes (per-split softmax partials: running max, sum and the
+ * unnormalized output row of every query head and context split; the split
+ * plan follows the "attention.rs" page's split-T decode followed by a combine
+ * pass).  max_positions is max_context_len in dense mode and vis_stride in
+ * visible-list mode.  Returns 0 when no workspace is needed.
+ */
+size_t q8_paged_decode_workspace_size(uint32_t num_seqs, uint32_t num_heads,
+                                      uint32_t num_kv_heads, uint32_t head_size,
+                                      uint32_t block_size, uint32_t max_positions);
+
+/*
+ * q8_paged_decode -- single-query decode attention over the int8 paged cache
+ * ("paged_attn_q8.comp" page: output = softmax(scale * Q.K^T) . V with K and
+ * V dequantized on read, kv head = h / (num_heads/num_kv_heads), token t at
+ * block_tables[s*max_num_blocks_per_seq + t/block_size], offset
+ * t % block_size, context length clamped to max_context_len).
+ *
+ *   out           f32 [num_seqs, num_heads, head_size], dense.
+ *   q             f32; element d of head h of seq s at q[s*q_stride + h*head_size + d].
+ *   key_cache,    u32 caches in the format above.
+ *   value_cache
+ *   block_tables  u32 [num_seqs, max_num_blocks_per_seq].
+ *   context_lens  u32 [num_seqs]; seq s attends positions
+ *                 0 .. min(context_lens[s], max_context_len) - 1.
+ *   visible_pos,  optional visible-list mode (the "attention.rs" page's
+ *   num_visible,  selective decode over the row's visible token list): when
+ *   vis_stride    visible_pos != NULL, seq s attends exactly the positions
+ *                 visible_pos[s*vis_stride + i], i < num_visible[s]
+ *                 (num_visible[s] <= vis_stride; positions distinct);
+ *                 context_lens and max_context_len are then unused.
+ *   scale         f32 softmax scale applied to q.k.
+ *   workspace     device memory of at least q8_paged_decode_workspace_size()
+ *                 bytes, 16-byte aligned; contents on entry do not matter and
+ *                 are clobbered.  Concurrent calls need distinct workspaces.
+ *
+ * An empty position set gives a zero output row.  Accuracy: each output is
+ * within 1e-4 + 1e-4*|exact| of the exact attention over the dequantized cache
+ * for the documented workloads (f32 arithmetic throughout).
+ * Errors: Q8_ERR_NULL for a NULL required pointer; Q8_ERR_SHAPE when
+ * head_size is 0, not a multiple of 4 or above 256, block_size, num_heads or
+ * num_kv_heads is 0, num_heads % num_kv_heads != 0, q_stride <
+ * num_heads*head_size, max_num_blocks_per_seq is 0 while positions are
+ * possible, or vis_stride is 0 in visible-list mode; Q8_ERR_WORKSPACE when the
+ * workspace is too small or misaligned.  num_seqs == 0 enqueues nothing.
+ */
+q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
+                          const uint32_t* key_cache, const uint32_t* value_cache,
+                          const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                          const uint32_t* context_lens, uint32_t max_context_len,
+                          const uint32_t* visible_pos, const uint32_t* num_visible,
+                          uint32_t vis_stride,
+                          uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                          uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                          float scale, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* hipError_t code behind the calling thread's last Q8_ERR_HIP (0 if none). */
+int q8_last_hip_error(void);
+
+/* Static, human-readable name of a status code. */
+const char* q8_status_string(q8_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8KV_H */

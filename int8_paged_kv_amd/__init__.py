@@ -1,0 +1,23 @@
+"""int8 paged KV cache for AMD MI355X (gfx950).
+
+Two operations behind the C ABI of libq8kv.so (include/q8kv.h):
+
+* ``q8_cache_write``: symmetric per-token int8 quantize + pack of new K/V
+  vectors into the paged cache (the "reshape_and_cache_q8.comp" page).
+* ``q8_paged_decode``: single-query decode attention over that cache (the
+  "paged_attn_q8.comp" page), optionally over per-sequence visible-position
+  lists (the selective decode of the "attention.rs" page).
+
+The binding loads the library lazily, so ``int8_paged_kv_amd.workloads`` can
+be imported on a machine without the library or a GPU.
+"""
+
+__all__ = ["q8_cache_write", "q8_paged_decode", "q8_paged_decode_workspace_size",
+           "load_library", "Q8Error", "PAD_SLOT"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)

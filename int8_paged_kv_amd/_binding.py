@@ -1,0 +1,170 @@
+"""Thin ctypes binding of libq8kv.so.
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the path runs in the library's kernels.
+There is no CPU fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+PAD_SLOT = 0xFFFFFFFF
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8kv.so")
+
+_STATUS = {0: "Q8_OK", 1: "Q8_ERR_NULL", 2: "Q8_ERR_SHAPE", 3: "Q8_ERR_WORKSPACE",
+           4: "Q8_ERR_HIP", 5: "Q8_ERR_UNSUPPORTED"}
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        msg = "%s returned %s" % (what, _STATUS.get(status, str(status)))
+        if hip_error:
+            msg += " (hipError %d)" % hip_error
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libq8kv.so (built by int8_paged_kv_amd/build.py); raise if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libq8kv.so is not built (%s); run int8_paged_kv_amd/build.py" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        P, U = ctypes.c_void_p, ctypes.c_uint32
+        lib.q8_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U, P]
+        lib.q8_cache_write.restype = ctypes.c_int
+        lib.q8_paged_decode_workspace_size.argtypes = [U, U, U, U, U, U]
+        lib.q8_paged_decode_workspace_size.restype = ctypes.c_size_t
+        lib.q8_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U, P, P, U,
+                                        U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
+        lib.q8_paged_decode.restype = ctypes.c_int
+        lib.q8_last_hip_error.argtypes = []
+        lib.q8_last_hip_error.restype = ctypes.c_int
+        lib.q8_status_string.argtypes = [ctypes.c_int]
+        lib.q8_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        lib = load_library()
+        raise Q8Error(status, what, lib.q8_last_hip_error() if status == 4 else 0)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _u32(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    """uint32 arrays travel as int32 or uint32 tensors (same bits)."""
+    if t is None:
+        return None
+    if t.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("%s must be an int32/uint32 tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return _dev(t, name, t.dtype)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _rows(x: torch.Tensor, name: str):
+    """(pointer, row stride) of a [T, ...] f32 tensor whose rows are dense."""
+    if x.dim() < 2 or (x.numel() and not x[0].is_contiguous()):
+        raise ValueError("%s must be [T, num_kv_heads, head_size] with dense rows" % name)
+    return _dev(x, name, torch.float32), x.stride(0)
+
+
+def q8_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                   value_cache: torch.Tensor, slot_mapping: torch.Tensor, num_kv_heads: int,
+                   head_size: int, block_size: int, num_blocks: Optional[int] = None, stream=None) -> None:
+    """Quantize + pack K/V rows into the paged caches (see include/q8kv.h)."""
+    lib = load_library()
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    wpt = head_size // 4 + 1
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * wpt)
+    st = lib.q8_cache_write(kp, ks, vp, vs, _u32(key_cache, "key_cache"), _u32(value_cache, "value_cache"),
+                            _u32(slot_mapping, "slot_mapping"), slot_mapping.numel(), num_kv_heads,
+                            head_size, block_size, num_blocks, _stream(stream))
+    _check(st, "q8_cache_write")
+
+
+def q8_paged_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
+                                   block_size: int, max_positions: int) -> int:
+    return int(load_library().q8_paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                             head_size, block_size, max_positions))
+
+
+def q8_paged_decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                    block_tables: torch.Tensor, context_lens: Optional[torch.Tensor], scale: float,
+                    num_kv_heads: int, block_size: int, max_context_len: Optional[int] = None,
+                    visible_pos: Optional[torch.Tensor] = None, num_visible: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    num_blocks: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Decode attention over the int8 paged cache; q is [S, H, hs] f32 (see include/q8kv.h).
+
+    max_context_len must be given in dense mode (reading context_lens would
+    synchronize).  In visible-list mode vis_stride is visible_pos.shape[1]."""
+    lib = load_library()
+    if q.dim() != 3 or (q.numel() and not q[0].is_contiguous()):
+        raise ValueError("q must be [S, H, head_size] with dense rows")
+    S, H, hs = q.shape
+    if out is None:
+        out = torch.empty((S, H, hs), dtype=torch.float32, device=q.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (S, H, hs):
+        raise ValueError("out must be a contiguous [S, H, head_size] f32 tensor")
+    vis = visible_pos is not None
+    if vis:
+        if visible_pos.dim() != 2:
+            raise ValueError("visible_pos must be [S, vis_stride]")
+        vis_stride = visible_pos.shape[1]
+        max_pos = vis_stride
+        mcl = 0
+    else:
+        vis_stride = 0
+        if max_context_len is None:
+            raise ValueError("max_context_len is required in dense mode")
+        mcl = int(max_context_len)
+        max_pos = mcl
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [S, max_num_blocks_per_seq]")
+    wpt = hs // 4 + 1
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * wpt)
+    need = lib.q8_paged_decode_workspace_size(S, H, num_kv_heads, hs, block_size, max_pos)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp = None if workspace is None else workspace.data_ptr()
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.q8_paged_decode(_dev(out, "out", torch.float32), _dev(q, "q", torch.float32), q.stride(0),
+                             _u32(key_cache, "key_cache"), _u32(value_cache, "value_cache"),
+                             _u32(block_tables, "block_tables"), block_tables.shape[1],
+                             _u32(context_lens, "context_lens"), mcl,
+                             _u32(visible_pos, "visible_pos"), _u32(num_visible, "num_visible"), vis_stride,
+                             S, H, num_kv_heads, hs, block_size, num_blocks, float(scale), wp, wb,
+                             _stream(stream))
+    _check(st, "q8_paged_decode")
+    return out

@@ -1,0 +1,133 @@
+// C ABI of libq8kv.so: argument validation, split planning, kernel launches.
+// Declarations and the contract of every entry point are in include/q8kv.h.
+#include "q8kv.h"
+#include "q8kv_internal.h"
+
+#include <cmath>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+q8_status hip_fail(hipError_t e) {
+    g_last_hip_error = static_cast<int>(e);
+    return Q8_ERR_HIP;
+}
+
+bool head_size_ok(uint32_t hs) { return hs != 0 && hs % 4 == 0 && hs <= Q8_MAX_HEAD_SIZE; }
+
+}  // namespace
+
+extern "C" {
+
+q8_status q8_cache_write(const float* key, uint32_t key_stride,
+                         const float* value, uint32_t value_stride,
+                         uint32_t* key_cache, uint32_t* value_cache,
+                         const uint32_t* slot_mapping, uint32_t num_tokens,
+                         uint32_t num_kv_heads, uint32_t head_size,
+                         uint32_t block_size, uint32_t num_blocks, void* stream) {
+    if (!head_size_ok(head_size) || block_size == 0 || num_kv_heads == 0) return Q8_ERR_SHAPE;
+    const uint64_t row = static_cast<uint64_t>(num_kv_heads) * head_size;
+    if (key_stride < row || value_stride < row) return Q8_ERR_SHAPE;
+    if (num_tokens == 0) return Q8_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping) return Q8_ERR_NULL;
+    if (num_blocks == 0) return Q8_ERR_SHAPE;
+    q8kv::CacheWriteArgs a{};
+    a.key = key;
+    a.value = value;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.slot_mapping = slot_mapping;
+    a.key_stride = key_stride;
+    a.value_stride = value_stride;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.head_size = head_size;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    const hipError_t e = q8kv::launch_cache_write(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+size_t q8_paged_decode_workspace_size(uint32_t num_seqs, uint32_t num_heads,
+                                      uint32_t num_kv_heads, uint32_t head_size,
+                                      uint32_t block_size, uint32_t max_positions) {
+    if (num_kv_heads == 0 || num_heads % num_kv_heads != 0) return 0;
+    return q8kv::plan_decode(num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                             max_positions).bytes;
+}
+
+q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
+                          const uint32_t* key_cache, const uint32_t* value_cache,
+                          const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                          const uint32_t* context_lens, uint32_t max_context_len,
+                          const uint32_t* visible_pos, const uint32_t* num_visible,
+                          uint32_t vis_stride,
+                          uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                          uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                          float scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (!head_size_ok(head_size) || block_size == 0 || num_heads == 0 || num_kv_heads == 0 ||
+        num_heads % num_kv_heads != 0)
+        return Q8_ERR_SHAPE;
+    if (static_cast<uint64_t>(q_stride) < static_cast<uint64_t>(num_heads) * head_size) return Q8_ERR_SHAPE;
+    const bool vis = visible_pos != nullptr;
+    if (vis && vis_stride == 0) return Q8_ERR_SHAPE;
+    if (num_seqs == 0) return Q8_OK;
+    if (!out || !q || !key_cache || !value_cache || !block_tables) return Q8_ERR_NULL;
+    if (vis ? !num_visible : !context_lens) return Q8_ERR_NULL;
+    const uint32_t max_pos = vis ? vis_stride : max_context_len;
+    if (max_pos > 0 && (max_num_blocks_per_seq == 0 || num_blocks == 0)) return Q8_ERR_SHAPE;
+    if (!std::isfinite(scale)) return Q8_ERR_SHAPE;
+    // Grid limits: one workgroup per work item in a 1-D grid.
+    const q8kv::DecodePlan p = q8kv::plan_decode(num_seqs, num_heads, num_kv_heads, head_size,
+                                                 block_size, max_pos);
+    const uint64_t items = static_cast<uint64_t>(num_seqs) * num_kv_heads * p.num_groups * p.num_splits;
+    if (items > 0x7FFFFFFFull || static_cast<uint64_t>(num_seqs) * num_heads > 0x7FFFFFFFull)
+        return Q8_ERR_UNSUPPORTED;
+    if (p.bytes > 0) {
+        if (!workspace || workspace_bytes < p.bytes) return Q8_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return Q8_ERR_WORKSPACE;
+    }
+    q8kv::DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.visible_pos = visible_pos;
+    a.num_visible = num_visible;
+    char* ws = static_cast<char*>(workspace);
+    a.part_acc = p.bytes ? reinterpret_cast<float*>(ws + p.acc_offset) : nullptr;
+    a.part_ml = p.bytes ? reinterpret_cast<float*>(ws + p.ml_offset) : nullptr;
+    a.q_stride = q_stride;
+    a.max_num_blocks_per_seq = max_num_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.vis_stride = vis_stride;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_size = head_size;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const hipError_t e = q8kv::launch_decode(a, p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+int q8_last_hip_error(void) { return g_last_hip_error; }
+
+const char* q8_status_string(q8_status status) {
+    switch (status) {
+        case Q8_OK: return "Q8_OK";
+        case Q8_ERR_NULL: return "Q8_ERR_NULL";
+        case Q8_ERR_SHAPE: return "Q8_ERR_SHAPE";
+        case Q8_ERR_WORKSPACE: return "Q8_ERR_WORKSPACE";
+        case Q8_ERR_HIP: return "Q8_ERR_HIP";
+        case Q8_ERR_UNSUPPORTED: return "Q8_ERR_UNSUPPORTED";
+    }
+    return "Q8_UNKNOWN";
+}
+
+}  // extern "C"

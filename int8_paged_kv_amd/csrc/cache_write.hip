@@ -1,0 +1,93 @@
+// Quantize + pack new K/V vectors into the int8 paged cache.
+//
+// Follows the "reshape_and_cache_q8.comp" page, main(): for each (token, kv
+// head) and for K then V, amax = max|x| (from 0), inv = amax > 0 ? 127/amax : 0,
+// code = clamp(round(x * inv), -127, 127) packed four per u32 word with element
+// 4w+l in byte l, then one word with the bits of amax/127 (1.0 when amax == 0).
+// A pad slot (0xFFFFFFFF) skips the token.  round() is round-half-even here.
+//
+// MI355X mapping: one wavefront per (token, kv head).  When head_size <= 128
+// the two 32-lane halves quantize K and V side by side; otherwise the whole
+// wave does K and then V.  Each lane owns one code word: a 16-byte load of four
+// f32 values, an amax reduction across the lanes of its half (or wave), four
+// IEEE multiplies, v_rndne, clamp and a byte pack.  Every step is a single
+// binary32 operation with round-to-nearest, so the packed words are bit-exact
+// (no FMA contraction applies: there is no add).
+#include "q8kv_internal.h"
+
+namespace q8kv {
+namespace {
+
+__device__ __forceinline__ float4 load4(const float* p, bool vec4) {
+    if (vec4) return *reinterpret_cast<const float4*>(p);
+    return make_float4(p[0], p[1], p[2], p[3]);
+}
+
+__device__ __forceinline__ uint32_t pack_code(float x, float inv, uint32_t lane_byte) {
+    float r = __builtin_rintf(x * inv);          // nearest, ties to even
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8u * lane_byte);
+}
+
+// Packs one vector: lanes [0, width) of the group cooperate; lane w owns word w.
+template <int WIDTH>
+__device__ __forceinline__ void pack_vector(const float* src, uint32_t* dst, uint32_t hs4,
+                                            uint32_t w, bool vec4) {
+    const bool active = w < hs4;
+    float4 x = active ? load4(src + 4 * w, vec4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float amax = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, off, WIDTH));
+    const float inv = amax > 0.0f ? __fdiv_rn(127.0f, amax) : 0.0f;
+    if (active) {
+        uint32_t word = pack_code(x.x, inv, 0) | pack_code(x.y, inv, 1) |
+                        pack_code(x.z, inv, 2) | pack_code(x.w, inv, 3);
+        dst[w] = word;
+    }
+    if (w == 0) {
+        const float s = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 1.0f;
+        dst[hs4] = __float_as_uint(s);
+    }
+}
+
+template <bool HALF>
+__global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool vec4) {
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint64_t pair = static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (pair >= static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads) return;
+    const uint32_t t = static_cast<uint32_t>(pair / a.num_kv_heads);
+    const uint32_t h = static_cast<uint32_t>(pair % a.num_kv_heads);
+    const uint32_t slot = a.slot_mapping[t];
+    if (slot == kPadSlot) return;
+    const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
+    const uint64_t block = slot / a.block_size, off = slot % a.block_size;
+    if (block >= a.num_blocks) return;   // out of contract; skipped rather than written out of bounds
+    const uint64_t dst = ((block * a.num_kv_heads + h) * a.block_size + off) * wpt;
+    const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
+    const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
+    if (HALF) {
+        const bool is_v = lane >= 32;
+        pack_vector<32>(is_v ? vsrc : ksrc, (is_v ? a.value_cache : a.key_cache) + dst, hs4, lane & 31, vec4);
+    } else {
+        pack_vector<64>(ksrc, a.key_cache + dst, hs4, lane, vec4);
+        pack_vector<64>(vsrc, a.value_cache + dst, hs4, lane, vec4);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
+    const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
+    const uint64_t blocks = (pairs + 3) / 4;
+    const bool vec4 = (reinterpret_cast<uintptr_t>(a.key) % 16 == 0) &&
+                      (reinterpret_cast<uintptr_t>(a.value) % 16 == 0) &&
+                      a.key_stride % 4 == 0 && a.value_stride % 4 == 0;
+    if (a.head_size / 4 <= 32)
+        hipLaunchKernelGGL(cache_write_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, a, vec4);
+    else
+        hipLaunchKernelGGL(cache_write_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, a, vec4);
+    return hipGetLastError();
+}
+
+}  // namespace q8kv

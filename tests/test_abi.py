@@ -1,0 +1,97 @@
+"""The C-ABI library loads and exports every symbol include/q8kv.h declares;
+host-side validation rejects bad shapes before anything reaches a GPU (CPU only).
+
+No call here launches a kernel: every call returns from argument validation
+or is a pure host query."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8kv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from int8_paged_kv_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        import int8_paged_kv_amd.build as b
+        b.build()
+    return _binding.load_library()
+
+
+def test_header_declares_the_two_operations():
+    names = declared_functions()
+    assert "q8_cache_write" in names and "q8_paged_decode" in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    assert lib.q8_status_string(0) == b"Q8_OK"
+    assert lib.q8_status_string(3) == b"Q8_ERR_WORKSPACE"
+    assert lib.q8_status_string(99) == b"Q8_UNKNOWN"
+    assert lib.q8_last_hip_error() == 0
+
+
+def test_pad_slot_constant_matches_header():
+    from int8_paged_kv_amd import workloads, PAD_SLOT
+    text = open(HEADER).read()
+    assert re.search(r"#define Q8_PAD_SLOT 0xFFFFFFFFu", text)
+    assert PAD_SLOT == workloads.PAD_SLOT == 0xFFFFFFFF
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("hs,bs,hkv,stride,want", [
+    (0, 16, 2, 256, 2), (6, 16, 2, 256, 2), (260, 16, 1, 260, 2), (128, 0, 2, 256, 2),
+    (128, 16, 0, 256, 2), (128, 16, 2, 255, 2),
+])
+def test_cache_write_shape_errors(lib, hs, bs, hkv, stride, want):
+    assert lib.q8_cache_write(FAKE, stride, FAKE, stride, FAKE, FAKE, FAKE, 4, hkv, hs, bs, 8, None) == want
+
+
+def test_cache_write_null_and_empty(lib):
+    assert lib.q8_cache_write(None, 256, FAKE, 256, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    assert lib.q8_cache_write(None, 256, None, 256, None, None, None, 0, 2, 128, 16, 8, None) == 0
+
+
+def decode_args(**kw):
+    a = dict(out=FAKE, q=FAKE, q_stride=4 * 128, kc=FAKE, vc=FAKE, bt=FAKE, max_nb=8, cl=FAKE, mcl=5000,
+             vis=None, nvis=None, vis_stride=0, S=2, H=4, Hkv=2, hs=128, bs=16, nb=64, scale=0.1,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "q_stride", "kc", "vc", "bt", "max_nb", "cl", "mcl", "vis", "nvis",
+                           "vis_stride", "S", "H", "Hkv", "hs", "bs", "nb", "scale", "ws", "wsb", "stream")]
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(hs=130), 2), (dict(hs=512), 2), (dict(H=5), 2), (dict(Hkv=0), 2), (dict(bs=0), 2),
+    (dict(q_stride=511), 2), (dict(vis=FAKE, nvis=FAKE, vis_stride=0), 2), (dict(max_nb=0), 2),
+    (dict(scale=float("nan")), 2), (dict(out=None), 1), (dict(bt=None), 1), (dict(cl=None), 1),
+    (dict(vis=FAKE, nvis=None, vis_stride=8), 1), (dict(ws=None), 3), (dict(wsb=16), 3),
+    (dict(ws=ctypes.c_void_p(0x1004)), 3), (dict(S=0), 0),
+])
+def test_decode_validation(lib, kw, want):
+    assert lib.q8_paged_decode(*decode_args(**kw)) == want
+
+
+def test_workspace_size_matches_plan(lib):
+    # single split: no workspace; long contexts: partials for every (seq, head, split)
+    assert lib.q8_paged_decode_workspace_size(2, 4, 2, 128, 16, 64) == 0
+    big = lib.q8_paged_decode_workspace_size(64, 32, 8, 128, 16, 4096)
+    assert big > 64 * 32 * 2 * 130 * 4
+    assert big % 4 == 0
