@@ -47,16 +47,44 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+// Reductions over the 16 lanes that share (lane % 4): two DPP row rotations
+// (within each row of 16 lanes) and the gfx950 row-swap permutes across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+// v_permlane{16,32}_swap with both operands = v: the two results hold v with
+// rows (16 lanes) exchanged pairwise, so combining them reduces across rows.
+// The elements are copied out before the bit cast (a bit cast of a vector
+// element expression reads element 0 with this compiler).
+__device__ __forceinline__ void swap16(float v, float& x, float& y) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const unsigned a0 = s[0], a1 = s[1];
+    x = __uint_as_float(a0);
+    y = __uint_as_float(a1);
+}
+__device__ __forceinline__ void swap32(float v, float& x, float& y) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const unsigned a0 = s[0], a1 = s[1];
+    x = __uint_as_float(a0);
+    y = __uint_as_float(a1);
+}
+__device__ __forceinline__ float swap16_max(float v) { float x, y; swap16(v, x, y); return fmaxf(x, y); }
+__device__ __forceinline__ float swap32_max(float v) { float x, y; swap32(v, x, y); return fmaxf(x, y); }
+__device__ __forceinline__ float swap16_sum(float v) { float x, y; swap16(v, x, y); return x + y; }
+__device__ __forceinline__ float swap32_sum(float v) { float x, y; swap32(v, x, y); return x + y; }
+__device__ __forceinline__ float group_max(float v) {
+    v = fmaxf(v, dpp_mov<kRowRor4>(v));
+    v = fmaxf(v, dpp_mov<kRowRor8>(v));
+    return swap32_max(swap16_max(v));
+}
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_mov<kRowRor4>(v);
+    v += dpp_mov<kRowRor8>(v);
+    return swap32_sum(swap16_sum(v));
 }
 
 struct SplitConsts {
@@ -208,10 +236,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
         }
     };
 
-    // Online-softmax state (log2 units), per head of the group; uniform across lanes.
-    float m_run[G], l_run[G];
+    // Online-softmax state (log2 units) of head 4g + (lane % 4), one entry per MFMA head group.
+    float m_run[NG4], l_run[NG4];
 #pragma unroll
-    for (int i = 0; i < G; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.0f; }
+    for (int g = 0; g < NG4; ++g) { m_run[g] = -INFINITY; l_run[g] = 0.0f; }
     f32x4 acc[NG4][4];
 #pragma unroll
     for (int g = 0; g < NG4; ++g)
@@ -242,44 +270,85 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
         }
         __syncthreads();
 
-        // ---- q . K^T: lane l holds the logits of token l for heads 4g+0..3 ----
-        f32x4 dot[NG4];
+        // ---- q . K^T on MFMA: A = codes (lane 4b+i: token 4b+i), B = q (lane
+        // 4b+n: head 4g+n).  Lane 4b+n ends with the logits of tokens 4b..4b+3
+        // for head 4g+n.  Two accumulators (even / odd words) halve the
+        // dependent MFMA chain. ----
+        f32x4 dot[NG4], dot1[NG4];
 #pragma unroll
-        for (int g = 0; g < NG4; ++g) dot[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int qk_words = EXACT ? HS4P : static_cast<int>(hs4);
-#pragma unroll 4
-        for (int w = 0; w < qk_words; ++w) {
-            const uint32_t kw = sK[lane * wpt + w];
-            const float c0 = code_f32(kw, 0), c1 = code_f32(kw, 1), c2 = code_f32(kw, 2), c3 = code_f32(kw, 3);
+        for (int g = 0; g < NG4; ++g) { dot[g] = f32x4{0.f, 0.f, 0.f, 0.f}; dot1[g] = dot[g]; }
+        const int qk_pairs = (EXACT ? HS4P : static_cast<int>(hs4)) / 2;
+#pragma unroll 2
+        for (int w2 = 0; w2 < qk_pairs; ++w2) {
+            const int w = 2 * w2;
+            const uint32_t kw0 = sK[lane * wpt + w];
+            const uint32_t kw1 = sK[lane * wpt + w + 1];
 #pragma unroll
             for (int g = 0; g < NG4; ++g) {
                 const float4 qa = *reinterpret_cast<const float4*>(&sQ[((4 * g + m4) * HS4P + w) * 4]);
-                dot[g] = mfma4(qa.x, c0, dot[g]);
-                dot[g] = mfma4(qa.y, c1, dot[g]);
-                dot[g] = mfma4(qa.z, c2, dot[g]);
-                dot[g] = mfma4(qa.w, c3, dot[g]);
+                const float4 qb = *reinterpret_cast<const float4*>(&sQ[((4 * g + m4) * HS4P + w + 1) * 4]);
+                dot[g] = mfma4(code_f32(kw0, 0), qa.x, dot[g]);
+                dot1[g] = mfma4(code_f32(kw1, 0), qb.x, dot1[g]);
+                dot[g] = mfma4(code_f32(kw0, 1), qa.y, dot[g]);
+                dot1[g] = mfma4(code_f32(kw1, 1), qb.y, dot1[g]);
+                dot[g] = mfma4(code_f32(kw0, 2), qa.z, dot[g]);
+                dot1[g] = mfma4(code_f32(kw1, 2), qb.z, dot1[g]);
+                dot[g] = mfma4(code_f32(kw0, 3), qa.w, dot[g]);
+                dot1[g] = mfma4(code_f32(kw1, 3), qb.w, dot1[g]);
             }
         }
-        const bool valid = lane < nv;
-        const float ks = __uint_as_float(sK[lane * wpt + hs4]);
-        const float vs = __uint_as_float(sV[lane * wpt + hs4]);
-        const float zk = ks * a.scale_log2;
+        if (!EXACT && (hs4 & 1)) {
+            const uint32_t w = hs4 - 1;
+            const uint32_t kw0 = sK[lane * wpt + w];
+#pragma unroll
+            for (int g = 0; g < NG4; ++g) {
+                const float4 qa = *reinterpret_cast<const float4*>(&sQ[((4 * g + m4) * HS4P + w) * 4]);
+                dot[g] = mfma4(code_f32(kw0, 0), qa.x, dot[g]);
+                dot[g] = mfma4(code_f32(kw0, 1), qa.y, dot[g]);
+                dot[g] = mfma4(code_f32(kw0, 2), qa.z, dot[g]);
+                dot[g] = mfma4(code_f32(kw0, 3), qa.w, dot[g]);
+            }
+        }
 
-        // ---- online softmax over this chunk ----
+        // ---- online softmax: this lane's head is 4g+m4, its tokens 4*blk+i ----
+        const uint32_t blk = lane >> 2;
+        float zk[4], vsc[4];
+        bool val[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t t = 4 * blk + i;
+            val[i] = t < nv;
+            zk[i] = __uint_as_float(sK[t * wpt + hs4]) * a.scale_log2;
+            vsc[i] = __uint_as_float(sV[t * wpt + hs4]);
+        }
 #pragma unroll
         for (int g = 0; g < NG4; ++g) {
+            const f32x4 d = dot[g] + dot1[g];
+            float z[4];
+            float cmax = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int hh = 4 * g + i;
-                const float z = valid ? dot[g][i] * zk : -INFINITY;
-                const float m_new = fmaxf(m_run[hh], wave_max(z));
-                const float alpha = exp2f(m_run[hh] - m_new);
-                const float p = exp2f(z - m_new);
-                l_run[hh] = l_run[hh] * alpha + wave_sum(p);
-                m_run[hh] = m_new;
-                sP[lane * G + hh] = valid ? p * vs : 0.0f;
+                z[i] = val[i] ? d[i] * zk[i] : -INFINITY;   // select: poison rows never leak
+                cmax = fmaxf(cmax, z[i]);
+            }
+            const float m_new = fmaxf(m_run[g], group_max(cmax));
+            const float alpha = exp2f(m_run[g] - m_new);
+            float psum = 0.0f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[g][j][i] *= alpha;
+            for (int i = 0; i < 4; ++i) {
+                const float p = exp2f(z[i] - m_new);
+                psum += p;
+                sP[(4 * blk + i) * G + 4 * g + m4] = val[i] ? p * vsc[i] : 0.0f;
+            }
+            l_run[g] = l_run[g] * alpha + group_sum(psum);
+            m_run[g] = m_new;
+            // P.V accumulators hold all four heads of the group: rescale head i
+            // by the factor computed in lanes with m4 == i.
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), i));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[g][j][i] *= ai;
             }
         }
         __syncthreads();
@@ -316,6 +385,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[g][j][i] += __shfl_xor(acc[g][j][i], off, 64);
 
+    // m and l of head 4g+i live in lanes with lane % 4 == i.
+    float mh[G], lh[G];
+#pragma unroll
+    for (int g = 0; g < NG4; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mh[4 * g + i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_run[g]), i));
+            lh[4 * g + i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_run[g]), i));
+        }
     if (ph != 0 || pw >= hs4) return;
     const uint64_t row_sh = static_cast<uint64_t>(s) * a.num_heads;
 #pragma unroll
@@ -327,15 +405,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
             const uint64_t h = row_sh + h0 + hh;
             float4 v = make_float4(acc[g][0][i], acc[g][1][i], acc[g][2][i], acc[g][3][i]);
             if (n_split_s == 1) {
-                const float inv = 1.0f / l_run[hh];
+                const float inv = 1.0f / lh[hh];
                 v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
                 *reinterpret_cast<float4*>(a.out + h * hs + 4 * pw) = v;
             } else {
                 const uint64_t rec = h * c.num_splits + split;
                 *reinterpret_cast<float4*>(a.part_acc + rec * hs + 4 * pw) = v;
                 if (pw == 0) {
-                    a.part_ml[2 * rec] = m_run[hh];
-                    a.part_ml[2 * rec + 1] = l_run[hh];
+                    a.part_ml[2 * rec] = mh[hh];
+                    a.part_ml[2 * rec + 1] = lh[hh];
                 }
             }
         }
