@@ -11,80 +11,106 @@
 //
 // MI355X design (not the page's one-workgroup-per-(seq, head) three-pass
 // shader):
-//   * Work item = one wavefront for (seq, kv head, group of G <= 8 query heads
-//     sharing that kv head, context split).  Each K/V byte is read from HBM
-//     once for the whole GQA group.
-//   * Positions are processed in chunks of 64, one per lane.  A chunk of
-//     consecutive, 64-aligned positions is a run of whole cache tiles (or one
-//     64-row slice of a larger tile): it is fetched with coalesced 16-byte
-//     loads into registers one chunk ahead of use, then written to LDS.  Other
-//     chunks (visible lists with gaps) are gathered row by row.
-//   * q.K^T and P.V run on the matrix cores as f32 MFMA
-//     (v_mfma_f32_4x4x1_16b_f32): 16 blocks of 4x4 outer products.  For
-//     q.K^T the 4 rows are 4 query heads and the 64 columns (16 blocks x 4) are
-//     the chunk's 64 tokens; one MFMA per head dimension.  For P.V the rows are
-//     again 4 query heads, each lane owns one code word (4 dimensions, one
-//     MFMA per byte) of one token phase.  Codes are converted with one
-//     sign-extending byte-select v_cvt_f32_i32 each, and products are exact
-//     f32 products accumulated in f32, like a scalar FMA loop.
-//   * Online softmax in the exp2 domain (scale folded with log2 e); running
-//     max, sum and the unnormalized output of each split are written to the
-//     workspace, and a merge kernel combines the splits (single-split rows are
-//     written out directly).
+//   * Work item = one wavefront for (seq, kv head, up to 8 query heads sharing
+//     that kv head, context split).  Each K/V byte is read from HBM once for
+//     the whole GQA group.
+//   * Positions are processed in chunks of 64.  A chunk of consecutive,
+//     64-aligned positions is a run of whole cache tiles (or one 64-row slice
+//     of a larger tile): it is fetched with coalesced 16-byte loads into
+//     registers one chunk ahead of use, then written to LDS.  Other chunks
+//     (visible lists with gaps) are gathered row by row.
+//   * Both contractions run on the int8 matrix cores
+//     (v_mfma_i32_16x16x64_i8), whose operands include the cache's own codes:
+//       q.K^T: each query head's q row is scaled by a power of two and rounded
+//       to an integer below 2^30 in magnitude, written as four balanced
+//       base-256 digits; the 16 MFMA rows are (4 heads x 4 digits), the
+//       columns 16 tokens, k the head dimension.
+//       P.V: the softmax weights of a chunk times the V token scales are
+//       scaled by a power of two and rounded to integers below 2^29, again as
+//       four digits; rows (4 heads x 4 digits), k = 64 tokens, columns 16 head
+//       dimensions.  V codes are transposed to token-major bytes with v_perm.
+//     The int32 digit sums are exact and are combined exactly in f64; q and
+//     the weights keep 30 significant bits, finer than binary32, so the result
+//     carries f32-level rounding error only.
+//   * Online softmax in the exp2 domain (scale folded with log2 e).  Each
+//     MFMA output row group is one head, so the per-head max and sum reduce
+//     over the 16 lanes of a DPP row.  Running max, sum and the unnormalized
+//     output of each split go to the workspace, and a merge kernel combines
+//     the splits (single-split rows are written out directly).
 #include "q8kv_internal.h"
 
 namespace q8kv {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float code_f32(uint32_t word, int byte) {
-    return static_cast<float>(static_cast<int8_t>(word >> (8 * byte)));
+constexpr uint32_t kDigitBias = 0x80808080u;
+
+__device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+// Four balanced base-256 digits of a signed integer |n| <= 2^30, one per
+// byte, each read back as a signed int8: sum_k byte_k * 256^k == n.
+__device__ __forceinline__ uint32_t to_digits(int32_t n) {
+    return (static_cast<uint32_t>(n) + kDigitBias) ^ kDigitBias;
 }
 
-// Reductions over the 16 lanes that share (lane % 4): two DPP row rotations
-// (within each row of 16 lanes) and the gfx950 row-swap permutes across rows.
+// Exact value of sum_k d[k] * 256^k for int32 digit sums |d[k]| < 2^22.
+__device__ __forceinline__ double combine_digits(i32x4 d) {
+    const int32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3];
+    const int32_t lo = d0 + d1 * 256;
+    const int32_t hi = d2 + d3 * 256;
+    return static_cast<double>(hi) * 65536.0 + static_cast<double>(lo);
+}
+
+// v_perm_b32: byte i of the result is byte sel_i of the 8-byte value (a:b),
+// selectors 0-3 picking bytes of b and 4-7 bytes of a.
+__device__ __forceinline__ uint32_t perm(uint32_t a, uint32_t b, uint32_t sel) {
+    return __builtin_amdgcn_perm(a, b, sel);
+}
+
+// 4x4 byte transpose: byte b of y[j] = byte j of x[b].
+__device__ __forceinline__ void transpose4(const uint32_t x[4], uint32_t y[4]) {
+    const uint32_t t01l = perm(x[1], x[0], 0x05010400u);   // x0.0 x1.0 x0.1 x1.1
+    const uint32_t t01h = perm(x[1], x[0], 0x07030602u);   // x0.2 x1.2 x0.3 x1.3
+    const uint32_t t23l = perm(x[3], x[2], 0x05010400u);
+    const uint32_t t23h = perm(x[3], x[2], 0x07030602u);
+    y[0] = perm(t23l, t01l, 0x05040100u);
+    y[1] = perm(t23l, t01l, 0x07060302u);
+    y[2] = perm(t23h, t01h, 0x05040100u);
+    y[3] = perm(t23h, t01h, 0x07060302u);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+constexpr int kRowRor1 = 0x121;
+constexpr int kRowRor2 = 0x122;
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
 
-// v_permlane{16,32}_swap with both operands = v: the two results hold v with
-// rows (16 lanes) exchanged pairwise, so combining them reduces across rows.
-// The elements are copied out before the bit cast (a bit cast of a vector
-// element expression reads element 0 with this compiler).
-__device__ __forceinline__ void swap16(float v, float& x, float& y) {
-    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const unsigned a0 = s[0], a1 = s[1];
-    x = __uint_as_float(a0);
-    y = __uint_as_float(a1);
-}
-__device__ __forceinline__ void swap32(float v, float& x, float& y) {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const unsigned a0 = s[0], a1 = s[1];
-    x = __uint_as_float(a0);
-    y = __uint_as_float(a1);
-}
-__device__ __forceinline__ float swap16_max(float v) { float x, y; swap16(v, x, y); return fmaxf(x, y); }
-__device__ __forceinline__ float swap32_max(float v) { float x, y; swap32(v, x, y); return fmaxf(x, y); }
-__device__ __forceinline__ float swap16_sum(float v) { float x, y; swap16(v, x, y); return x + y; }
-__device__ __forceinline__ float swap32_sum(float v) { float x, y; swap32(v, x, y); return x + y; }
-__device__ __forceinline__ float group_max(float v) {
+// Reductions over the 16 lanes of a DPP row (rotations within the row).
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dpp_mov<kRowRor1>(v));
+    v = fmaxf(v, dpp_mov<kRowRor2>(v));
     v = fmaxf(v, dpp_mov<kRowRor4>(v));
-    v = fmaxf(v, dpp_mov<kRowRor8>(v));
-    return swap32_max(swap16_max(v));
+    return fmaxf(v, dpp_mov<kRowRor8>(v));
 }
-__device__ __forceinline__ float group_sum(float v) {
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp_mov<kRowRor1>(v);
+    v += dpp_mov<kRowRor2>(v);
     v += dpp_mov<kRowRor4>(v);
-    v += dpp_mov<kRowRor8>(v);
-    return swap32_sum(swap16_sum(v));
+    return v + dpp_mov<kRowRor8>(v);
+}
+
+// Exponent e with |x| < 2^e for finite nonzero x (frexp convention).
+__device__ __forceinline__ int exponent_bound(float x) {
+    int e = 0;
+    (void)frexpf(x, &e);
+    return e;
 }
 
 struct SplitConsts {
@@ -116,31 +142,44 @@ __device__ __forceinline__ uint32_t position_at(const DecodeArgs& a, uint32_t s,
     return VIS ? a.visible_pos[static_cast<uint64_t>(s) * a.vis_stride + idx] : idx;
 }
 
-// Word offset of the (block, kv head) tile row `row` holding logical position pos.
-__device__ __forceinline__ uint64_t row_word_offset(const DecodeArgs& a, uint32_t s, uint32_t kvh,
-                                                    uint32_t pos, uint32_t num_blocks_m1, uint32_t wpt) {
-    uint32_t j = pos / a.block_size;
-    j = j < a.max_num_blocks_per_seq ? j : a.max_num_blocks_per_seq - 1;
-    uint32_t phys = a.block_tables[static_cast<uint64_t>(s) * a.max_num_blocks_per_seq + j];
-    phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
-    return ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size + pos % a.block_size) * wpt;
-}
-
-// HS4P: code words per row rounded up to 16, 32 or 64 (the lane layout);
-// EXACT: head_size/4 == HS4P; G: query heads per work item (4 or 8).
-template <int HS4P, bool EXACT, int G, bool VIS>
+// Split-kernel lane roles.  Lane l = 16*g + r.
+//   q.K^T (v_mfma_i32_16x16x64_i8): lane (r, g) supplies MFMA row r = (head
+//   r/4, digit r%4) of the q digits and column r = token 16*tg + r of the
+//   codes, both over the 16 head dimensions 64*kb + 16*g + 0..15, and
+//   receives the digit sums of token 16*tg + r for head g.
+//   P.V: lane (r, g) supplies row r = (head r/4, digit r%4) of the weight
+//   digits and column r of the codes, both over the 16 tokens 4*g + w + 16*b
+//   (w, b = 0..3; byte 4*w + b of the operand), where column r of column
+//   block cw is dimension 4*NCW*r + 4*cw + j of MFMA j; it receives the digit
+//   sums of those dimensions for head g.
+//
+// Data movement: no K/V staging in LDS.  Every lane loads its own MFMA
+// operands straight from the cache rows (16-byte loads of K code words,
+// NCW-word loads of V code words, the two scale words).  The K words of chunk
+// c+1 are requested right after q.K^T of chunk c, the V words and scales right
+// after its P.V, so each load has a softmax plus a matrix product to arrive.
+// The word offsets of a chunk's 64 cache rows sit in a small LDS table that is
+// built two chunks ahead from the block table (and, in visible-list mode, from
+// the split's positions staged in LDS), which handles any block size.
+//
+// HS4P: code words per row rounded up to 16, 32, 48 or 64; EXACT: head_size /
+// 4 == HS4P (wide loads; otherwise word-by-word loads that never pass the
+// row's scale word); NHS: sets of 4 query heads per work item (1 or 2).
+template <int HS4P, bool EXACT, int NHS, bool VIS>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
-    constexpr int NG4 = G / 4;                 // MFMA head groups of 4
-    constexpr int NPH = kWave / HS4P;          // token phases in P.V
-    constexpr int WPT_MAX = HS4P + 1;
-    constexpr int NU = (kChunk * WPT_MAX + 4 * kWave - 1) / (4 * kWave);   // 16-byte slots per lane
+    constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
+    constexpr int NCW = HS4P / 16;             // V code words per lane and row
+    constexpr int G = 4 * NHS;
+    constexpr int QD = NKB * 64;               // padded q row length
 
-    __shared__ __align__(16) uint32_t sK[kChunk * WPT_MAX + HS4P + 4];
-    __shared__ __align__(16) uint32_t sV[kChunk * WPT_MAX + HS4P + 4];
-    __shared__ __align__(16) float sQ[G * HS4P * 4];
-    __shared__ float sP[kChunk * G];
+    __shared__ __align__(16) float sQ[G * QD];
+    __shared__ __align__(16) uint32_t sA[NHS * 16 * 16];   // [set][head*4+digit][w]: weight digits, 4 tokens a word
+    __shared__ __align__(8) uint64_t sRow[2][kChunk];       // word offsets of a chunk's cache rows
+    __shared__ uint32_t sPos[VIS ? kMaxSplit : 1];          // visible positions of this split
+    __shared__ int sEq[G];
 
     const uint32_t lane = threadIdx.x;
+    const uint32_t r = lane & 15, g = lane >> 4;
     // Work item = ((s * num_kv_heads + kvh) * num_groups + grp) * num_splits + split.
     const uint32_t split = blockIdx.x % c.num_splits;
     const uint32_t sg = blockIdx.x / c.num_splits;
@@ -152,268 +191,273 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
     if (t0 >= n_pos) return;
     const uint32_t t1 = min(n_pos, t0 + c.split_tokens);
     const uint32_t n_split_s = (n_pos + c.split_tokens - 1) / c.split_tokens;
+    const uint32_t n_chunks = (t1 - t0 + kChunk - 1) / kChunk;
 
     const uint32_t hs = a.head_size, hs4 = EXACT ? HS4P : hs / 4, wpt = hs4 + 1;
     const uint32_t n_rep = a.num_heads / a.num_kv_heads;
     const uint32_t h0 = kvh * n_rep + grp * G;
     const uint32_t nh = min(static_cast<uint32_t>(G), n_rep - grp * G);
+    const uint64_t seq_bt = static_cast<uint64_t>(s) * a.max_num_blocks_per_seq;
 
-    // Stage q rows of the group (zero for padded dims and absent heads).
-    for (uint32_t i = lane; i < G * HS4P * 4; i += kWave) {
-        const uint32_t hi = i / (HS4P * 4), d = i % (HS4P * 4);
+    // ---- stage q rows (zero for padded dims and absent heads) and positions ----
+    for (uint32_t i = lane; i < G * QD; i += kWave) {
+        const uint32_t hi = i / QD, d = i % QD;
         float v = 0.0f;
         if (hi < nh && d < hs) v = a.q[static_cast<uint64_t>(s) * a.q_stride + static_cast<uint64_t>(h0 + hi) * hs + d];
         sQ[i] = v;
     }
+    if (VIS)
+        for (uint32_t i = lane; i < t1 - t0; i += kWave) sPos[i] = position_at<VIS>(a, s, t0 + i);
+    __syncthreads();
 
-    // Per-lane 16-byte slot map of a tiled chunk (chunk independent).
-    const uint32_t chunk_u4 = kChunk * wpt / 4;
-    uint32_t slot_seg[NU], slot_off[NU];
+    // ---- row table: lane t computes the row of chunk position t ----
+    // (positions past the chunk's end repeat its last row, so every load stays in bounds)
+    uint32_t pend_pos = 0;
+    auto table_issue = [&](uint32_t ci) __attribute__((always_inline)) -> uint32_t {
+        const uint32_t cs = t0 + kChunk * ci;
+        const uint32_t nv = min(static_cast<uint32_t>(kChunk), t1 - cs);
+        const uint32_t idx = cs + min(lane, nv - 1);
+        pend_pos = VIS ? sPos[idx - t0] : idx;
+        uint32_t j = pend_pos / a.block_size;
+        j = j < a.max_num_blocks_per_seq ? j : a.max_num_blocks_per_seq - 1;
+        return a.block_tables[seq_bt + j];
+    };
+    auto table_finish = [&](uint32_t ci, uint32_t phys, uint32_t pos) __attribute__((always_inline)) {
+        phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
+        sRow[ci & 1][lane] = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size + pos % a.block_size) * wpt;
+    };
+
+    // ---- q digits: MFMA row r = (head r/4, digit r%4), k = dims 64kb+16g+0..15 ----
+    i32x4 qa[NHS][NKB];
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const uint32_t u = lane + kWave * i;
-        const uint32_t k = __umulhi(u, c.seg_magic);
-        slot_seg[i] = k;
-        slot_off[i] = (u - k * c.seg_u4) * 4;
+    for (int hset = 0; hset < NHS; ++hset) {
+        const uint32_t hq = 4 * hset + r / 4, dig = r % 4;
+        const float* row = &sQ[hq * QD];
+        float amax = 0.0f;
+        for (int d = 0; d < QD; d += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(row + d);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+        const int eq = amax > 0.0f ? 30 - exponent_bound(amax) : 0;    // |q * 2^eq| < 2^30
+        if (g == 0 && dig == 0) sEq[hq] = eq;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            uint32_t packed[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float4 v = *reinterpret_cast<const float4*>(row + 64 * kb + 16 * g + 4 * w);
+                const uint32_t b0 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.x, eq)))) >> (8 * dig)) & 0xFFu;
+                const uint32_t b1 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.y, eq)))) >> (8 * dig)) & 0xFFu;
+                const uint32_t b2 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.z, eq)))) >> (8 * dig)) & 0xFFu;
+                const uint32_t b3 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.w, eq)))) >> (8 * dig)) & 0xFFu;
+                packed[w] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+            }
+            qa[hset][kb] = i32x4{static_cast<int32_t>(packed[0]), static_cast<int32_t>(packed[1]),
+                                 static_cast<int32_t>(packed[2]), static_cast<int32_t>(packed[3])};
+        }
     }
 
-    const uint64_t kv_stride = static_cast<uint64_t>(a.num_kv_heads) * a.block_size * wpt;  // words per block
-    const uint64_t kvh_off = static_cast<uint64_t>(kvh) * a.block_size * wpt;
-    const uint64_t seq_bt = static_cast<uint64_t>(s) * a.max_num_blocks_per_seq;
-
-    u32x4 kreg[NU], vreg[NU];
-
-    // Is the chunk starting at list index cs a run of consecutive positions
-    // from a 64-aligned first position (so it maps onto whole tile segments)?
-    auto chunk_tiled = [&](uint32_t cs, uint32_t nv) __attribute__((always_inline)) -> bool {
-        if (!c.tiled_ok) return false;
-        if (!VIS) return true;
-        const uint32_t p0 = position_at<VIS>(a, s, cs);
-        const uint32_t pl = position_at<VIS>(a, s, cs + nv - 1);
-        return (p0 % kChunk == 0) && (pl - p0 == nv - 1);
-    };
-    auto issue_tiled = [&](uint32_t cs, uint32_t nv) __attribute__((always_inline)) {
-        const uint32_t p0 = position_at<VIS>(a, s, cs);
-        const uint32_t blk0 = p0 / a.block_size;
-        const uint32_t row0 = p0 % a.block_size;     // nonzero only when block_size > 64
+    // ---- operand loads of chunk ci (its row table must be in sRow[ci & 1]) ----
+    i32x4 kop[4][NKB];           // q.K^T B operands, token group tg
+    uint32_t vw[4][4][NCW];      // V code words [w][b][cw] of rows 4g + w + 16b
+    float ksc[4], vsc[4];        // scales of rows 16*tg + r
+    auto load_k = [&](uint32_t ci) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            const uint32_t u = lane + kWave * i;
-            const uint32_t k = slot_seg[i];
-            const bool live = (u < chunk_u4) && (k * c.seg_rows < nv);
-            if (live) {
-                uint32_t j = blk0 + (a.block_size <= kChunk ? k : 0);
-                j = j < a.max_num_blocks_per_seq ? j : a.max_num_blocks_per_seq - 1;
-                uint32_t phys = a.block_tables[seq_bt + j];
-                phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
-                const uint64_t w = phys * kv_stride + kvh_off + static_cast<uint64_t>(row0) * wpt + slot_off[i];
-                kreg[i] = *reinterpret_cast<const u32x4*>(a.key_cache + w);
-                vreg[i] = *reinterpret_cast<const u32x4*>(a.value_cache + w);
+        for (int tg = 0; tg < 4; ++tg) {
+            const uint32_t* rowp = a.key_cache + sRow[ci & 1][16 * tg + r];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const uint32_t w0 = 16 * kb + 4 * g;
+                if (EXACT) {
+                    u32x4 v;
+                    __builtin_memcpy(&v, rowp + w0, 16);
+                    kop[tg][kb] = i32x4{static_cast<int32_t>(v.x), static_cast<int32_t>(v.y),
+                                        static_cast<int32_t>(v.z), static_cast<int32_t>(v.w)};
+                } else {
+                    int32_t e[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) e[q] = (w0 + q < hs4) ? static_cast<int32_t>(rowp[w0 + q]) : 0;
+                    kop[tg][kb] = i32x4{e[0], e[1], e[2], e[3]};
+                }
             }
         }
     };
-    auto store_tiled = [&](uint32_t nv) __attribute__((always_inline)) {
+    auto load_v = [&](uint32_t ci) __attribute__((always_inline)) {
+        // scales first: the softmax waits for them, P.V later for the code words
 #pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            const uint32_t u = lane + kWave * i;
-            if (u < chunk_u4 && slot_seg[i] * c.seg_rows < nv) {
-                *reinterpret_cast<u32x4*>(&sK[4 * u]) = kreg[i];
-                *reinterpret_cast<u32x4*>(&sV[4 * u]) = vreg[i];
-            }
+        for (int tg = 0; tg < 4; ++tg) {
+            const uint64_t off = sRow[ci & 1][16 * tg + r] + hs4;
+            ksc[tg] = __uint_as_float(a.key_cache[off]);
+            vsc[tg] = __uint_as_float(a.value_cache[off]);
         }
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t* rowp = a.value_cache + sRow[ci & 1][4 * g + w + 16 * b];
+                const uint32_t w0 = NCW * r;
+                if (EXACT) {
+                    __builtin_memcpy(vw[w][b], rowp + w0, 4 * NCW);
+                } else {
+#pragma unroll
+                    for (int cw = 0; cw < NCW; ++cw) vw[w][b][cw] = (w0 + cw < hs4) ? rowp[w0 + cw] : 0u;
+                }
+            }
     };
-    auto copy_rows = [&](uint32_t cs, uint32_t nv) __attribute__((always_inline)) {
-        uint64_t my_row = 0;
-        if (lane < nv) my_row = row_word_offset(a, s, kvh, position_at<VIS>(a, s, cs + lane), num_blocks_m1, wpt);
-        for (uint32_t r = 0; r < nv; ++r) {
-            const uint32_t lo = __shfl(static_cast<uint32_t>(my_row), r, 64);
-            const uint32_t hi = __shfl(static_cast<uint32_t>(my_row >> 32), r, 64);
-            const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
-            for (uint32_t w = lane; w < wpt; w += kWave) {
-                sK[r * wpt + w] = a.key_cache[base + w];
-                sV[r * wpt + w] = a.value_cache[base + w];
+
+    // Online-softmax state (log2 units) of head 4*hset + g, uniform across the lane's row.
+    float m_run[NHS], l_run[NHS];
+    float acc[NHS][NCW][4];      // dims 4*NCW*r + 4*cw + j of head 4*hset + g
+#pragma unroll
+    for (int hset = 0; hset < NHS; ++hset) {
+        m_run[hset] = -INFINITY;
+        l_run[hset] = 0.0f;
+#pragma unroll
+        for (int cw = 0; cw < NCW; ++cw)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[hset][cw][j] = 0.0f;
+    }
+
+    // ---- prologue: tables of chunks 0 and 1, operands of chunk 0 ----
+    {
+        const uint32_t ph = table_issue(0);
+        table_finish(0, ph, pend_pos);
+    }
+    uint32_t nphys = 0, npos = 0;
+    if (n_chunks > 1) { nphys = table_issue(1); npos = pend_pos; }
+    __syncthreads();
+    load_k(0);
+    load_v(0);
+    if (n_chunks > 1) table_finish(1, nphys, npos);
+    __syncthreads();
+
+    // One chunk: q.K^T, online softmax, P.V.  `after_qk` runs between q.K^T
+    // and the softmax (the next chunk's K loads go there).
+    auto process = [&](uint32_t ci, auto after_qk) __attribute__((always_inline)) {
+        const uint32_t nv = min(static_cast<uint32_t>(kChunk), t1 - (t0 + kChunk * ci));
+
+        // ---- q . K^T ----
+        i32x4 dsum[NHS][4];
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+            for (int hset = 0; hset < NHS; ++hset) {
+                dsum[hset][tg] = i32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) dsum[hset][tg] = mfma_i8(qa[hset][kb], kop[tg][kb], dsum[hset][tg]);
             }
-        }
-    };
+        after_qk();
 
-    // Online-softmax state (log2 units) of head 4g + (lane % 4), one entry per MFMA head group.
-    float m_run[NG4], l_run[NG4];
-#pragma unroll
-    for (int g = 0; g < NG4; ++g) { m_run[g] = -INFINITY; l_run[g] = 0.0f; }
-    f32x4 acc[NG4][4];
-#pragma unroll
-    for (int g = 0; g < NG4; ++g)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const uint32_t m4 = lane & 3;            // MFMA row owned by this lane (head within 4)
-    const uint32_t pw = lane % HS4P;          // P.V: code word owned by this lane
-    const uint32_t ph = lane / HS4P;          // P.V: token phase
-
-    uint32_t cs = t0;
-    uint32_t nv = min(static_cast<uint32_t>(kChunk), t1 - cs);
-    bool tiled = chunk_tiled(cs, nv);
-    if (tiled) issue_tiled(cs, nv);
-
-    while (true) {
-        // ---- land this chunk in LDS, prefetch the next one ----
-        if (tiled) store_tiled(nv);
-        else copy_rows(cs, nv);
-        const uint32_t ncs = cs + kChunk;
-        const bool more = ncs < t1;
-        uint32_t nnv = 0;
-        bool ntiled = false;
-        if (more) {
-            nnv = min(static_cast<uint32_t>(kChunk), t1 - ncs);
-            ntiled = chunk_tiled(ncs, nnv);
-            if (ntiled) issue_tiled(ncs, nnv);
-        }
-        __syncthreads();
-
-        // ---- q . K^T on MFMA: A = codes (lane 4b+i: token 4b+i), B = q (lane
-        // 4b+n: head 4g+n).  Lane 4b+n ends with the logits of tokens 4b..4b+3
-        // for head 4g+n.  Two accumulators (even / odd words) halve the
-        // dependent MFMA chain. ----
-        f32x4 dot[NG4], dot1[NG4];
-#pragma unroll
-        for (int g = 0; g < NG4; ++g) { dot[g] = f32x4{0.f, 0.f, 0.f, 0.f}; dot1[g] = dot[g]; }
-        const int qk_pairs = (EXACT ? HS4P : static_cast<int>(hs4)) / 2;
-#pragma unroll 2
-        for (int w2 = 0; w2 < qk_pairs; ++w2) {
-            const int w = 2 * w2;
-            const uint32_t kw0 = sK[lane * wpt + w];
-            const uint32_t kw1 = sK[lane * wpt + w + 1];
-#pragma unroll
-            for (int g = 0; g < NG4; ++g) {
-                const float4 qa = *reinterpret_cast<const float4*>(&sQ[((4 * g + m4) * HS4P + w) * 4]);
-                const float4 qb = *reinterpret_cast<const float4*>(&sQ[((4 * g + m4) * HS4P + w + 1) * 4]);
-                dot[g] = mfma4(code_f32(kw0, 0), qa.x, dot[g]);
-                dot1[g] = mfma4(code_f32(kw1, 0), qb.x, dot1[g]);
-                dot[g] = mfma4(code_f32(kw0, 1), qa.y, dot[g]);
-                dot1[g] = mfma4(code_f32(kw1, 1), qb.y, dot1[g]);
-                dot[g] = mfma4(code_f32(kw0, 2), qa.z, dot[g]);
-                dot1[g] = mfma4(code_f32(kw1, 2), qb.z, dot1[g]);
-                dot[g] = mfma4(code_f32(kw0, 3), qa.w, dot[g]);
-                dot1[g] = mfma4(code_f32(kw1, 3), qb.w, dot1[g]);
-            }
-        }
-        if (!EXACT && (hs4 & 1)) {
-            const uint32_t w = hs4 - 1;
-            const uint32_t kw0 = sK[lane * wpt + w];
-#pragma unroll
-            for (int g = 0; g < NG4; ++g) {
-                const float4 qa = *reinterpret_cast<const float4*>(&sQ[((4 * g + m4) * HS4P + w) * 4]);
-                dot[g] = mfma4(code_f32(kw0, 0), qa.x, dot[g]);
-                dot[g] = mfma4(code_f32(kw0, 1), qa.y, dot[g]);
-                dot[g] = mfma4(code_f32(kw0, 2), qa.z, dot[g]);
-                dot[g] = mfma4(code_f32(kw0, 3), qa.w, dot[g]);
-            }
-        }
-
-        // ---- online softmax: this lane's head is 4g+m4, its tokens 4*blk+i ----
-        const uint32_t blk = lane >> 2;
-        float zk[4], vsc[4];
+        // ---- online softmax; weights to integers, digits to LDS ----
         bool val[4];
+        float vmax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t t = 4 * blk + i;
-            val[i] = t < nv;
-            zk[i] = __uint_as_float(sK[t * wpt + hs4]) * a.scale_log2;
-            vsc[i] = __uint_as_float(sV[t * wpt + hs4]);
+        for (int tg = 0; tg < 4; ++tg) {
+            val[tg] = 16 * tg + r < nv;
+            vmax = val[tg] ? fmaxf(vmax, vsc[tg]) : vmax;     // select: unwritten rows never leak
         }
+        vmax = row_max(vmax);
+        const int ep = 29 - exponent_bound(vmax);             // weight * 2^ep < 2^29
 #pragma unroll
-        for (int g = 0; g < NG4; ++g) {
-            const f32x4 d = dot[g] + dot1[g];
+        for (int hset = 0; hset < NHS; ++hset) {
+            const int eq = sEq[4 * hset + g];
             float z[4];
             float cmax = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                z[i] = val[i] ? d[i] * zk[i] : -INFINITY;   // select: poison rows never leak
-                cmax = fmaxf(cmax, z[i]);
+            for (int tg = 0; tg < 4; ++tg) {
+                const float zq = ldexpf(static_cast<float>(combine_digits(dsum[hset][tg])), -eq);
+                z[tg] = val[tg] ? zq * (ksc[tg] * a.scale_log2) : -INFINITY;
+                cmax = fmaxf(cmax, z[tg]);
             }
-            const float m_new = fmaxf(m_run[g], group_max(cmax));
-            const float alpha = exp2f(m_run[g] - m_new);
+            const float m_new = fmaxf(m_run[hset], row_max(cmax));
+            const float alpha = exp2f(m_run[hset] - m_new);
             float psum = 0.0f;
+            uint32_t wd[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = exp2f(z[i] - m_new);
+            for (int tg = 0; tg < 4; ++tg) {
+                const float p = exp2f(z[tg] - m_new);
                 psum += p;
-                sP[(4 * blk + i) * G + 4 * g + m4] = val[i] ? p * vsc[i] : 0.0f;
+                const float pv = val[tg] ? p * vsc[tg] : 0.0f;
+                wd[tg] = to_digits(static_cast<int32_t>(rintf(ldexpf(pv, ep))));
             }
-            l_run[g] = l_run[g] * alpha + group_sum(psum);
-            m_run[g] = m_new;
-            // P.V accumulators hold all four heads of the group: rescale head i
-            // by the factor computed in lanes with m4 == i.
+            l_run[hset] = l_run[hset] * alpha + row_sum(psum);
+            m_run[hset] = m_new;
+            uint32_t td[4];
+            transpose4(wd, td);       // byte tg of td[digit] = digit of token r + 16*tg
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), i));
+            for (int dg = 0; dg < 4; ++dg) sA[(hset * 16 + 4 * g + dg) * 16 + r] = td[dg];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[g][j][i] *= ai;
-            }
+            for (int cw = 0; cw < NCW; ++cw)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[hset][cw][j] *= alpha;
         }
         __syncthreads();
 
-        // ---- P . V: lane owns word pw of the tokens of phase ph ----
-#pragma unroll 4
-        for (int k = 0; k < HS4P; ++k) {
-            const uint32_t tok = k * NPH + ph;
-            const uint32_t vw = sV[tok * wpt + pw];
-            const float c0 = code_f32(vw, 0), c1 = code_f32(vw, 1), c2 = code_f32(vw, 2), c3 = code_f32(vw, 3);
+        // ---- P . V ----
+        i32x4 pa[NHS];
 #pragma unroll
-            for (int g = 0; g < NG4; ++g) {
-                const float pa = sP[tok * G + 4 * g + m4];
-                acc[g][0] = mfma4(pa, c0, acc[g][0]);
-                acc[g][1] = mfma4(pa, c1, acc[g][1]);
-                acc[g][2] = mfma4(pa, c2, acc[g][2]);
-                acc[g][3] = mfma4(pa, c3, acc[g][3]);
+        for (int hset = 0; hset < NHS; ++hset)
+            pa[hset] = *reinterpret_cast<const i32x4*>(&sA[(hset * 16 + r) * 16 + 4 * g]);
+        const double pscale = ldexp(1.0, -ep);
+#pragma unroll
+        for (int cw = 0; cw < NCW; ++cw) {
+            uint32_t bj[4][4];      // [byte j][w]: codes of tokens 4g + w + 16*b (byte b)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x[4] = {vw[w][0][cw], vw[w][1][cw], vw[w][2][cw], vw[w][3][cw]};
+                uint32_t y[4];
+                transpose4(x, y);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bj[j][w] = y[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const i32x4 b = i32x4{static_cast<int32_t>(bj[j][0]), static_cast<int32_t>(bj[j][1]),
+                                      static_cast<int32_t>(bj[j][2]), static_cast<int32_t>(bj[j][3])};
+#pragma unroll
+                for (int hset = 0; hset < NHS; ++hset) {
+                    const i32x4 d = mfma_i8(pa[hset], b, i32x4{0, 0, 0, 0});
+                    acc[hset][cw][j] += static_cast<float>(combine_digits(d) * pscale);
+                }
             }
         }
-        if (!more) break;
+    };
+
+    // Chunks with a successor: every load is issued unconditionally, so the
+    // wait counts the compiler derives stay exact across the loop.
+    for (uint32_t ci = 0; ci + 1 < n_chunks; ++ci) {
+        const uint32_t c2 = min(ci + 2, n_chunks - 1);
+        nphys = table_issue(c2);
+        npos = pend_pos;
+        process(ci, [&]() __attribute__((always_inline)) { load_k(ci + 1); });
+        load_v(ci + 1);
+        if (ci + 2 < n_chunks) table_finish(ci + 2, nphys, npos);
         __syncthreads();
-        cs = ncs;
-        nv = nnv;
-        tiled = ntiled;
     }
+    process(n_chunks - 1, []() {});
 
-    // ---- combine token phases: lanes with equal pw hold partial sums ----
-#pragma unroll
-    for (int off = HS4P; off < kWave; off <<= 1)
-#pragma unroll
-        for (int g = 0; g < NG4; ++g)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[g][j][i] += __shfl_xor(acc[g][j][i], off, 64);
-
-    // m and l of head 4g+i live in lanes with lane % 4 == i.
-    float mh[G], lh[G];
-#pragma unroll
-    for (int g = 0; g < NG4; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            mh[4 * g + i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_run[g]), i));
-            lh[4 * g + i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_run[g]), i));
-        }
-    if (ph != 0 || pw >= hs4) return;
+    // ---- write: lane (r, g) holds dims 4*NCW*r + 4*cw + j of head 4*hset + g ----
     const uint64_t row_sh = static_cast<uint64_t>(s) * a.num_heads;
 #pragma unroll
-    for (int g = 0; g < NG4; ++g) {
+    for (int hset = 0; hset < NHS; ++hset) {
+        const uint32_t hh = 4 * hset + g;
+        if (hh >= nh) continue;
+        const uint64_t h = row_sh + h0 + hh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t hh = 4 * g + i;
-            if (hh >= nh) continue;
-            const uint64_t h = row_sh + h0 + hh;
-            float4 v = make_float4(acc[g][0][i], acc[g][1][i], acc[g][2][i], acc[g][3][i]);
+        for (int cw = 0; cw < NCW; ++cw) {
+            const uint32_t word = NCW * r + cw;
+            if (word >= hs4) continue;
+            float4 v = make_float4(acc[hset][cw][0], acc[hset][cw][1], acc[hset][cw][2], acc[hset][cw][3]);
             if (n_split_s == 1) {
-                const float inv = 1.0f / lh[hh];
+                const float inv = 1.0f / l_run[hset];
                 v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
-                *reinterpret_cast<float4*>(a.out + h * hs + 4 * pw) = v;
+                *reinterpret_cast<float4*>(a.out + h * hs + 4 * word) = v;
             } else {
                 const uint64_t rec = h * c.num_splits + split;
-                *reinterpret_cast<float4*>(a.part_acc + rec * hs + 4 * pw) = v;
-                if (pw == 0) {
-                    a.part_ml[2 * rec] = mh[hh];
-                    a.part_ml[2 * rec + 1] = lh[hh];
+                *reinterpret_cast<float4*>(a.part_acc + rec * hs + 4 * word) = v;
+                if (word == 0) {
+                    a.part_ml[2 * rec] = m_run[hset];
+                    a.part_ml[2 * rec + 1] = l_run[hset];
                 }
             }
         }
@@ -456,19 +500,19 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, uint32_t
     }
 }
 
-template <int HS4P, bool EXACT, int G>
+template <int HS4P, bool EXACT, int NHS>
 hipError_t launch_split_t(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st, bool vis) {
     if (vis)
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, G, true>), grid, dim3(64), 0, st, a, c, nbm1);
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, true>), grid, dim3(64), 0, st, a, c, nbm1);
     else
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, G, false>), grid, dim3(64), 0, st, a, c, nbm1);
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, false>), grid, dim3(64), 0, st, a, c, nbm1);
     return hipGetLastError();
 }
 
 template <int HS4P, bool EXACT>
 hipError_t launch_split_g(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st, bool vis) {
-    if (c.group == 8) return launch_split_t<HS4P, EXACT, 8>(a, c, nbm1, grid, st, vis);
-    return launch_split_t<HS4P, EXACT, 4>(a, c, nbm1, grid, st, vis);
+    if (c.group == 8) return launch_split_t<HS4P, EXACT, 2>(a, c, nbm1, grid, st, vis);
+    return launch_split_t<HS4P, EXACT, 1>(a, c, nbm1, grid, st, vis);
 }
 
 }  // namespace
@@ -492,6 +536,7 @@ DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_he
         const long v = atol(e);
         if (v >= kChunk) per = static_cast<uint64_t>(v) / kChunk * kChunk;
     }
+    if (per > kMaxSplit) per = kMaxSplit;
     p.split_tokens = static_cast<uint32_t>(per);
     p.num_splits = max_positions ? (max_positions + p.split_tokens - 1) / p.split_tokens : 0;
     const uint64_t recs = static_cast<uint64_t>(num_seqs) * num_heads * p.num_splits;
@@ -526,9 +571,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
         hipError_t err;
         if (hs4 == 16) err = launch_split_g<16, true>(a, c, nbm1, grid, stream, vis);
         else if (hs4 == 32) err = launch_split_g<32, true>(a, c, nbm1, grid, stream, vis);
+        else if (hs4 == 48) err = launch_split_g<48, true>(a, c, nbm1, grid, stream, vis);
         else if (hs4 == 64) err = launch_split_g<64, true>(a, c, nbm1, grid, stream, vis);
         else if (hs4 < 16) err = launch_split_g<16, false>(a, c, nbm1, grid, stream, vis);
         else if (hs4 < 32) err = launch_split_g<32, false>(a, c, nbm1, grid, stream, vis);
+        else if (hs4 < 48) err = launch_split_g<48, false>(a, c, nbm1, grid, stream, vis);
         else err = launch_split_g<64, false>(a, c, nbm1, grid, stream, vis);
         if (err != hipSuccess) return err;
     }

@@ -8,7 +8,8 @@ namespace q8kv {
 
 constexpr uint32_t kPadSlot = 0xFFFFFFFFu;
 constexpr int kWave = 64;          // CDNA wavefront width
-constexpr int kChunk = 64;         // decode positions per chunk: one per lane
+constexpr int kChunk = 64;         // decode positions per chunk
+constexpr uint32_t kMaxSplit = 1024;   // longest context split (positions) of one work item
 
 struct CacheWriteArgs {
     const float* key;
