@@ -153,39 +153,41 @@ __device__ __forceinline__ uint32_t position_at(const DecodeArgs& a, uint32_t s,
 //   block cw is dimension 4*NCW*r + 4*cw + j of MFMA j; it receives the digit
 //   sums of those dimensions for head g.
 //
-// Data movement: no K/V staging in LDS.  Every lane loads its own MFMA
-// operands straight from the cache rows (16-byte loads of K code words,
-// NCW-word loads of V code words, the two scale words).  The K words of chunk
-// c+1 are requested right after q.K^T of chunk c, the V words and scales right
-// after its P.V, so each load has a softmax plus a matrix product to arrive.
-// The word offsets of a chunk's 64 cache rows sit in a small LDS table that is
-// built two chunks ahead from the block table (and, in visible-list mode, from
-// the split's positions staged in LDS), which handles any block size.
+// Data movement: a chunk of 64 consecutive, 64-aligned positions is a run of
+// whole cache tiles (or a 64-row slice of a larger tile), so its K and V rows
+// arrive with fully coalesced 16-byte loads (one KiB per instruction) into
+// registers, one chunk ahead of use, and are then written to LDS, from where
+// each lane reads its MFMA operands.  Chunks of a visible list that are not
+// such runs are gathered row by row.  The block ids a chunk needs are read two
+// chunks ahead, so no block-table read sits between a data load and its use.
 //
 // HS4P: code words per row rounded up to 16, 32, 48 or 64; EXACT: head_size /
-// 4 == HS4P (wide loads; otherwise word-by-word loads that never pass the
-// row's scale word); NHS: sets of 4 query heads per work item (1 or 2).
+// 4 == HS4P; NHS: sets of 4 query heads per work item (1 or 2).
 template <int HS4P, bool EXACT, int NHS, bool VIS>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
+__global__ __launch_bounds__(64, (HS4P <= 32 && NHS == 1) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
     constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
     constexpr int NCW = HS4P / 16;             // V code words per lane and row
     constexpr int G = 4 * NHS;
     constexpr int QD = NKB * 64;               // padded q row length
+    constexpr int WPT_MAX = HS4P + 1;
+    constexpr int NU = (kChunk * WPT_MAX + 4 * kWave - 1) / (4 * kWave);   // 16-byte slots per lane
 
+    __shared__ __align__(16) uint32_t sK[kChunk * WPT_MAX + 64];
+    __shared__ __align__(16) uint32_t sV[kChunk * WPT_MAX + 64];
     __shared__ __align__(16) float sQ[G * QD];
     __shared__ __align__(16) uint32_t sA[NHS * 16 * 16];   // [set][head*4+digit][w]: weight digits, 4 tokens a word
-    __shared__ __align__(8) uint64_t sRow[2][kChunk];       // word offsets of a chunk's cache rows
-    __shared__ uint32_t sPos[VIS ? kMaxSplit : 1];          // visible positions of this split
     __shared__ int sEq[G];
 
     const uint32_t lane = threadIdx.x;
     const uint32_t r = lane & 15, g = lane >> 4;
-    // Work item = ((s * num_kv_heads + kvh) * num_groups + grp) * num_splits + split.
-    const uint32_t split = blockIdx.x % c.num_splits;
-    const uint32_t sg = blockIdx.x / c.num_splits;
-    const uint32_t grp = sg % c.num_groups;
-    const uint32_t kvh = (sg / c.num_groups) % a.num_kv_heads;
-    const uint32_t s = sg / c.num_groups / a.num_kv_heads;
+    // Work item = ((s * num_splits + split) * num_kv_heads + kvh) * num_groups + grp:
+    // the kv heads of one (seq, split) are dispatched together, so the slices of
+    // each cache block that they read reach the memory controllers close in time.
+    const uint32_t grp = blockIdx.x % c.num_groups;
+    const uint32_t kvh = (blockIdx.x / c.num_groups) % a.num_kv_heads;
+    const uint32_t ss = blockIdx.x / c.num_groups / a.num_kv_heads;
+    const uint32_t split = ss % c.num_splits;
+    const uint32_t s = ss / c.num_splits;
     const uint32_t n_pos = positions_of<VIS>(a, s);
     const uint32_t t0 = split * c.split_tokens;
     if (t0 >= n_pos) return;
@@ -198,34 +200,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
     const uint32_t h0 = kvh * n_rep + grp * G;
     const uint32_t nh = min(static_cast<uint32_t>(G), n_rep - grp * G);
     const uint64_t seq_bt = static_cast<uint64_t>(s) * a.max_num_blocks_per_seq;
+    const uint64_t kv_stride = static_cast<uint64_t>(a.num_kv_heads) * a.block_size * wpt;  // words per block
+    const uint64_t kvh_off = static_cast<uint64_t>(kvh) * a.block_size * wpt;
+    const uint32_t chunk_u4 = kChunk * wpt / 4;
+    const uint32_t nseg = kChunk / c.seg_rows;            // tile segments per tiled chunk
 
-    // ---- stage q rows (zero for padded dims and absent heads) and positions ----
+    // ---- stage q rows (zero for padded dims and absent heads) ----
     for (uint32_t i = lane; i < G * QD; i += kWave) {
         const uint32_t hi = i / QD, d = i % QD;
         float v = 0.0f;
         if (hi < nh && d < hs) v = a.q[static_cast<uint64_t>(s) * a.q_stride + static_cast<uint64_t>(h0 + hi) * hs + d];
         sQ[i] = v;
     }
-    if (VIS)
-        for (uint32_t i = lane; i < t1 - t0; i += kWave) sPos[i] = position_at<VIS>(a, s, t0 + i);
     __syncthreads();
-
-    // ---- row table: lane t computes the row of chunk position t ----
-    // (positions past the chunk's end repeat its last row, so every load stays in bounds)
-    uint32_t pend_pos = 0;
-    auto table_issue = [&](uint32_t ci) __attribute__((always_inline)) -> uint32_t {
-        const uint32_t cs = t0 + kChunk * ci;
-        const uint32_t nv = min(static_cast<uint32_t>(kChunk), t1 - cs);
-        const uint32_t idx = cs + min(lane, nv - 1);
-        pend_pos = VIS ? sPos[idx - t0] : idx;
-        uint32_t j = pend_pos / a.block_size;
-        j = j < a.max_num_blocks_per_seq ? j : a.max_num_blocks_per_seq - 1;
-        return a.block_tables[seq_bt + j];
-    };
-    auto table_finish = [&](uint32_t ci, uint32_t phys, uint32_t pos) __attribute__((always_inline)) {
-        phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
-        sRow[ci & 1][lane] = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size + pos % a.block_size) * wpt;
-    };
 
     // ---- q digits: MFMA row r = (head r/4, digit r%4), k = dims 64kb+16g+0..15 ----
     i32x4 qa[NHS][NKB];
@@ -256,53 +243,83 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
                                  static_cast<int32_t>(packed[2]), static_cast<int32_t>(packed[3])};
         }
     }
+    __syncthreads();
+    int eq_out[NHS];       // q exponent of this lane's output head 4*hset + g
+#pragma unroll
+    for (int hset = 0; hset < NHS; ++hset) eq_out[hset] = sEq[4 * hset + g];
 
-    // ---- operand loads of chunk ci (its row table must be in sRow[ci & 1]) ----
-    i32x4 kop[4][NKB];           // q.K^T B operands, token group tg
-    uint32_t vw[4][4][NCW];      // V code words [w][b][cw] of rows 4g + w + 16b
-    float ksc[4], vsc[4];        // scales of rows 16*tg + r
-    auto load_k = [&](uint32_t ci) __attribute__((always_inline)) {
+    // ---- chunk metadata, prepared two chunks ahead ----
+    // Tiled chunk: lane k holds the block id of segment k.  Row-gathered chunk:
+    // lane i holds the block id and in-block row of the chunk's i-th position.
+    struct Meta {
+        uint32_t cs, nv, p0, id, row, tiled;
+    };
+    auto meta_of = [&](uint32_t cs_) __attribute__((always_inline)) -> Meta {
+        Meta m;
+        m.cs = cs_;
+        m.nv = min(static_cast<uint32_t>(kChunk), t1 - cs_);
+        m.p0 = position_at<VIS>(a, s, cs_);
+        m.tiled = c.tiled_ok;
+        if (VIS && m.tiled) {
+            const uint32_t pl = position_at<VIS>(a, s, cs_ + m.nv - 1);
+            m.tiled = (m.p0 % kChunk == 0) && (pl - m.p0 == m.nv - 1) ? 1u : 0u;
+        }
+        uint32_t j;
+        m.row = 0;
+        if (m.tiled) {
+            const uint32_t k = min(lane, nseg - 1);
+            j = m.p0 / a.block_size + (a.block_size <= kChunk ? k : 0);
+        } else {
+            const uint32_t pos = position_at<VIS>(a, s, cs_ + min(lane, m.nv - 1));
+            j = pos / a.block_size;
+            m.row = pos % a.block_size;
+        }
+        j = j < a.max_num_blocks_per_seq ? j : a.max_num_blocks_per_seq - 1;
+        m.id = a.block_tables[seq_bt + j];
+        return m;
+    };
+
+    // ---- tiled chunk: 16-byte slot u = lane + 64*i lies in segment u / seg_u4 ----
+    u32x4 kreg[NU], vreg[NU];
+    auto issue_data = [&](const Meta& m) __attribute__((always_inline)) {
+        const uint32_t row0 = m.p0 % a.block_size;     // nonzero only when block_size > 64
 #pragma unroll
-        for (int tg = 0; tg < 4; ++tg) {
-            const uint32_t* rowp = a.key_cache + sRow[ci & 1][16 * tg + r];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const uint32_t w0 = 16 * kb + 4 * g;
-                if (EXACT) {
-                    u32x4 v;
-                    __builtin_memcpy(&v, rowp + w0, 16);
-                    kop[tg][kb] = i32x4{static_cast<int32_t>(v.x), static_cast<int32_t>(v.y),
-                                        static_cast<int32_t>(v.z), static_cast<int32_t>(v.w)};
-                } else {
-                    int32_t e[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) e[q] = (w0 + q < hs4) ? static_cast<int32_t>(rowp[w0 + q]) : 0;
-                    kop[tg][kb] = i32x4{e[0], e[1], e[2], e[3]};
-                }
+        for (int i = 0; i < NU; ++i) {
+            const uint32_t u = lane + kWave * i;
+            const uint32_t k = __umulhi(u, c.seg_magic);
+            uint32_t phys = __shfl(m.id, static_cast<int>(min(k, nseg - 1)), 64);
+            phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
+            if ((u < chunk_u4) && (k * c.seg_rows < m.nv)) {
+                const uint32_t off = (u - k * c.seg_u4) * 4;
+                const uint64_t w = phys * kv_stride + kvh_off + static_cast<uint64_t>(row0) * wpt + off;
+                kreg[i] = *reinterpret_cast<const u32x4*>(a.key_cache + w);
+                vreg[i] = *reinterpret_cast<const u32x4*>(a.value_cache + w);
             }
         }
     };
-    auto load_v = [&](uint32_t ci) __attribute__((always_inline)) {
-        // scales first: the softmax waits for them, P.V later for the code words
+    auto store = [&](const Meta& m) __attribute__((always_inline)) {
+        if (m.tiled) {
 #pragma unroll
-        for (int tg = 0; tg < 4; ++tg) {
-            const uint64_t off = sRow[ci & 1][16 * tg + r] + hs4;
-            ksc[tg] = __uint_as_float(a.key_cache[off]);
-            vsc[tg] = __uint_as_float(a.value_cache[off]);
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t* rowp = a.value_cache + sRow[ci & 1][4 * g + w + 16 * b];
-                const uint32_t w0 = NCW * r;
-                if (EXACT) {
-                    __builtin_memcpy(vw[w][b], rowp + w0, 4 * NCW);
-                } else {
-#pragma unroll
-                    for (int cw = 0; cw < NCW; ++cw) vw[w][b][cw] = (w0 + cw < hs4) ? rowp[w0 + cw] : 0u;
+            for (int i = 0; i < NU; ++i) {
+                const uint32_t u = lane + kWave * i;
+                if (u < chunk_u4 && __umulhi(u, c.seg_magic) * c.seg_rows < m.nv) {
+                    *reinterpret_cast<u32x4*>(&sK[4 * u]) = kreg[i];
+                    *reinterpret_cast<u32x4*>(&sV[4 * u]) = vreg[i];
                 }
             }
+        } else {
+            const uint32_t phys = m.id < num_blocks_m1 ? m.id : num_blocks_m1;
+            const uint64_t my_row = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size + m.row) * wpt;
+            for (uint32_t rr = 0; rr < m.nv; ++rr) {
+                const uint32_t lo = __shfl(static_cast<uint32_t>(my_row), rr, 64);
+                const uint32_t hi = __shfl(static_cast<uint32_t>(my_row >> 32), rr, 64);
+                const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
+                for (uint32_t w = lane; w < wpt; w += kWave) {
+                    sK[rr * wpt + w] = a.key_cache[base + w];
+                    sV[rr * wpt + w] = a.value_cache[base + w];
+                }
+            }
+        }
     };
 
     // Online-softmax state (log2 units) of head 4*hset + g, uniform across the lane's row.
@@ -318,54 +335,53 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
             for (int j = 0; j < 4; ++j) acc[hset][cw][j] = 0.0f;
     }
 
-    // ---- prologue: tables of chunks 0 and 1, operands of chunk 0 ----
-    {
-        const uint32_t ph = table_issue(0);
-        table_finish(0, ph, pend_pos);
-    }
-    uint32_t nphys = 0, npos = 0;
-    if (n_chunks > 1) { nphys = table_issue(1); npos = pend_pos; }
-    __syncthreads();
-    load_k(0);
-    load_v(0);
-    if (n_chunks > 1) table_finish(1, nphys, npos);
-    __syncthreads();
-
-    // One chunk: q.K^T, online softmax, P.V.  `after_qk` runs between q.K^T
-    // and the softmax (the next chunk's K loads go there).
-    auto process = [&](uint32_t ci, auto after_qk) __attribute__((always_inline)) {
-        const uint32_t nv = min(static_cast<uint32_t>(kChunk), t1 - (t0 + kChunk * ci));
-
+    // One chunk from LDS: q.K^T, online softmax, P.V.
+    auto process = [&](uint32_t nv) __attribute__((always_inline)) {
         // ---- q . K^T ----
         i32x4 dsum[NHS][4];
 #pragma unroll
-        for (int tg = 0; tg < 4; ++tg)
+        for (int tg = 0; tg < 4; ++tg) {
+            const uint32_t* krow = &sK[(16 * tg + r) * wpt + 4 * g];
 #pragma unroll
-            for (int hset = 0; hset < NHS; ++hset) {
-                dsum[hset][tg] = i32x4{0, 0, 0, 0};
+            for (int hset = 0; hset < NHS; ++hset) dsum[hset][tg] = i32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) dsum[hset][tg] = mfma_i8(qa[hset][kb], kop[tg][kb], dsum[hset][tg]);
+            for (int kb = 0; kb < NKB; ++kb) {
+                i32x4 b;
+                if (EXACT) {
+                    __builtin_memcpy(&b, krow + 16 * kb, 16);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        b[q] = (16 * kb + 4 * g + q < hs4) ? static_cast<int32_t>(krow[16 * kb + q]) : 0;
+                }
+#pragma unroll
+                for (int hset = 0; hset < NHS; ++hset) dsum[hset][tg] = mfma_i8(qa[hset][kb], b, dsum[hset][tg]);
             }
-        after_qk();
+        }
 
-        // ---- online softmax; weights to integers, digits to LDS ----
+        // ---- token scales of rows 16*tg + r ----
+        float ksc[4], vsc[4];
         bool val[4];
         float vmax = 0.0f;
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-            val[tg] = 16 * tg + r < nv;
+            const uint32_t t = 16 * tg + r;
+            val[tg] = t < nv;
+            ksc[tg] = __uint_as_float(sK[t * wpt + hs4]);
+            vsc[tg] = __uint_as_float(sV[t * wpt + hs4]);
             vmax = val[tg] ? fmaxf(vmax, vsc[tg]) : vmax;     // select: unwritten rows never leak
         }
         vmax = row_max(vmax);
         const int ep = 29 - exponent_bound(vmax);             // weight * 2^ep < 2^29
+
+        // ---- online softmax; weights to integers, digits to LDS ----
 #pragma unroll
         for (int hset = 0; hset < NHS; ++hset) {
-            const int eq = sEq[4 * hset + g];
             float z[4];
             float cmax = -INFINITY;
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) {
-                const float zq = ldexpf(static_cast<float>(combine_digits(dsum[hset][tg])), -eq);
+                const float zq = ldexpf(static_cast<float>(combine_digits(dsum[hset][tg])), -eq_out[hset]);
                 z[tg] = val[tg] ? zq * (ksc[tg] * a.scale_log2) : -INFINITY;
                 cmax = fmaxf(cmax, z[tg]);
             }
@@ -404,8 +420,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
             uint32_t bj[4][4];      // [byte j][w]: codes of tokens 4g + w + 16*b (byte b)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const uint32_t x[4] = {vw[w][0][cw], vw[w][1][cw], vw[w][2][cw], vw[w][3][cw]};
-                uint32_t y[4];
+                uint32_t x[4], y[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t word = NCW * r + cw;
+                    x[b] = (EXACT || word < hs4) ? sV[(4 * g + w + 16 * b) * wpt + word] : 0u;
+                }
                 transpose4(x, y);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) bj[j][w] = y[j];
@@ -423,18 +443,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a, SplitCon
         }
     };
 
-    // Chunks with a successor: every load is issued unconditionally, so the
-    // wait counts the compiler derives stay exact across the loop.
-    for (uint32_t ci = 0; ci + 1 < n_chunks; ++ci) {
-        const uint32_t c2 = min(ci + 2, n_chunks - 1);
-        nphys = table_issue(c2);
-        npos = pend_pos;
-        process(ci, [&]() __attribute__((always_inline)) { load_k(ci + 1); });
-        load_v(ci + 1);
-        if (ci + 2 < n_chunks) table_finish(ci + 2, nphys, npos);
+    // ---- pipeline: data one chunk ahead, block ids two chunks ahead ----
+    Meta cur = meta_of(t0);
+    if (cur.tiled) issue_data(cur);
+    Meta nxt = cur;
+    if (n_chunks > 1) nxt = meta_of(t0 + kChunk);
+    for (uint32_t ci = 0;; ++ci) {
+        store(cur);
+        const bool more = ci + 1 < n_chunks;
+        Meta nxt2 = nxt;
+        if (ci + 2 < n_chunks) nxt2 = meta_of(cur.cs + 2 * kChunk);
+        if (more && nxt.tiled) issue_data(nxt);
         __syncthreads();
+        process(cur.nv);
+        if (!more) break;
+        __syncthreads();
+        cur = nxt;
+        nxt = nxt2;
     }
-    process(n_chunks - 1, []() {});
 
     // ---- write: lane (r, g) holds dims 4*NCW*r + 4*cw + j of head 4*hset + g ----
     const uint64_t row_sh = static_cast<uint64_t>(s) * a.num_heads;
@@ -524,10 +550,10 @@ DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_he
     p.group = n_rep > 4 ? 8 : 4;
     p.num_groups = (n_rep + p.group - 1) / p.group;
     (void)block_size;
-    // Aim for about 8 work items per compute unit when every row is at the
+    // Aim for about 16 work items per compute unit when every row is at the
     // longest length, with splits of 256..1024 positions (multiples of 64).
     const uint64_t units = static_cast<uint64_t>(num_seqs) * num_kv_heads * p.num_groups;
-    const uint64_t target_items = 256ull * 8;
+    const uint64_t target_items = 256ull * 16;
     uint64_t per = units ? (static_cast<uint64_t>(max_positions) * units + target_items - 1) / target_items : max_positions;
     per = (per + kChunk - 1) / kChunk * kChunk;
     if (per < 256) per = 256;
