@@ -44,7 +44,27 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--hot", action="store_true", help="also time back-to-back steps on one cache")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB five times (the known-size "
+                        "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    """Five launches of torch's contiguous copy kernel over `mib` MiB: each
+    reads and writes exactly mib * 2^20 bytes of HBM (source and destination
+    are far larger than any cache once rotated over three buffer pairs)."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 4
+    pairs = [(torch.ones(n, dtype=torch.int32, device=dev), torch.empty(n, dtype=torch.int32, device=dev))
+             for _ in range(3)]
+    torch.cuda.synchronize()
+    for i in range(5):
+        src, dst = pairs[i % 3]
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n * 4, "launches": 5}), flush=True)
 
 
 def kernel_sources_digest() -> str:
@@ -76,6 +96,9 @@ def read_traffic(digest: str):
 
 def main():
     args = parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode hot path has no multi-GPU step in this build "
               "(run with --gpus 1)", file=sys.stderr)

@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Turn rocprofv3 output of bench.py runs into the text summaries under profiles/.
+
+Expected layout of DIR (what the commands printed in each summary write):
+  DIR/trace/bench_kernel_stats.csv, DIR/trace/bench_kernel_trace.csv
+      rocprofv3 --kernel-trace --stats -f csv -o bench, of bench.py
+  DIR/pmc_FETCH_SIZE/bench_counter_collection.csv, DIR/pmc_WRITE_SIZE/...
+      rocprofv3 --pmc FETCH_SIZE (resp. WRITE_SIZE) -f csv -o bench, of bench.py
+  DIR/copy_FETCH_SIZE/copy_counter_collection.csv, DIR/copy_WRITE_SIZE/...
+      the same counters over bench.py --copy-calibration MIB (a plain copy of
+      known size), which give the factor from each counter to HBM bytes
+  DIR/pmc_FETCH_SIZE.log, DIR/pmc_WRITE_SIZE.log, DIR/copy_FETCH_SIZE.log
+      stdout of those runs (bench's JSON line carries the kernel-source digest)
+
+Writes profiles/q8_paged_decode_llama_kernel_trace.txt and
+profiles/q8_paged_decode_llama_traffic.txt; the latter is what bench.py reads
+for roofline.traffic while the kernel sources still match its digest.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import statistics
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DECODE_KERNELS = ("decode_split_kernel", "decode_merge_kernel")
+WRITE_KERNEL = "cache_write_kernel"
+
+TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d {d}/trace -o bench -f csv "
+             "-- python3 /root/repo/bench.py --steps 20 --warmup 5 --no-cpu")
+PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {c} -d {d}/pmc_{c} -o bench -f csv "
+           "-- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu")
+COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} -d {d}/copy_{c} -o copy -f csv "
+            "-- python3 /root/repo/bench.py --copy-calibration {mib}")
+
+
+def short(name: str) -> str:
+    for k in DECODE_KERNELS + (WRITE_KERNEL, "copyBuffer"):
+        if k in name:
+            return name.replace("void ", "").replace("q8kv::(anonymous namespace)::", "").split("(")[0]
+    return name[:60]
+
+
+def last_json(path: str) -> dict:
+    with open(path) as f:
+        lines = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+    return json.loads(lines[-1])
+
+
+def counters(path: str):
+    """{(kernel, grid): [counter value per dispatch]}"""
+    out = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return out
+
+
+def step_dispatches(cnt, step_grid_of):
+    """Counter values of the decode-step launches: the grid the step uses for each kernel."""
+    res = {}
+    for (name, grid), vals in cnt.items():
+        for k in DECODE_KERNELS + (WRITE_KERNEL,):
+            if k in name and grid == step_grid_of.get(k):
+                res[k] = (name, grid, vals)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("dir", help="directory holding the rocprofv3 outputs")
+    ap.add_argument("--cmd-dir", default="/root/repo/gpurun_out/prof",
+                    help="DIR as written in the recorded commands")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args()
+    d = args.dir
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+
+    # ---- kernel trace: per-kernel durations of the step's launches ----
+    trace = defaultdict(list)
+    with open(os.path.join(d, "trace", "bench_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            trace[(r["Kernel_Name"], grid, int(r["Workgroup_Size_X"]), int(r["VGPR_Count"]),
+                   int(r["Accum_VGPR_Count"]), int(r["SGPR_Count"]), int(r["LDS_Block_Size"]),
+                   int(r["Scratch_Size"]))].append(dur)
+    bench_trace = last_json(os.path.join(d, "trace.log"))
+    digest = bench_trace["kernel_sources_sha256_16"]
+    # The step's launches are the ones with as many dispatches as the step count
+    # (warmup + timed + event-timed steps); fill-phase launches use other grids.
+    n_step = 2 * bench_trace["steps"] + bench_trace["warmup"]
+    step_grid = {}
+    rows = []
+    for key, durs in sorted(trace.items(), key=lambda kv: -sum(kv[1])):
+        name, grid, wg, vgpr, agpr, sgpr, lds, scr = key
+        tag = next((k for k in DECODE_KERNELS + (WRITE_KERNEL,) if k in name), None)
+        if tag and len(durs) == n_step:
+            step_grid[tag] = grid
+        rows.append((short(name), grid, wg, len(durs), statistics.mean(durs), statistics.median(durs),
+                     min(durs), max(durs), vgpr, agpr, sgpr, lds, scr, tag is not None and len(durs) == n_step))
+
+    split_us = mean_of(rows, "decode_split_kernel")
+    merge_us = mean_of(rows, "decode_merge_kernel")
+    write_us = mean_of(rows, "cache_write_kernel")
+    eff = bench_trace["config"]["effective_kv_bytes"]
+    lines = [
+        "# rocprofv3 kernel trace of the decode step, Llama-3-8B-shaped batch",
+        "# (S=64 H=32 Hkv=8 head_size=128 block_size=16, context lengths U[512,4096], seed 2)",
+        "#",
+        "# command (from any directory on the GPU machine):",
+        "#   " + TRACE_CMD.format(d=args.cmd_dir),
+        "# summarised with: python3 bench_profile.py <that -d directory's parent>",
+        "#",
+        "# kernel_sources_sha256_16: %s" % digest,
+        "# durations in microseconds per dispatch; step = one launch each of cache_write, decode_split, "
+        "decode_merge",
+        "",
+        "%-52s %9s %4s %5s %9s %9s %9s %9s %5s %5s %5s %6s %6s" % (
+            "kernel", "grid", "wg", "calls", "mean_us", "median_us", "min_us", "max_us", "vgpr", "agpr", "sgpr",
+            "lds", "scratch"),
+    ]
+    for r in rows:
+        lines.append("%-52s %9d %4d %5d %9.2f %9.2f %9.2f %9.2f %5d %5d %5d %6d %6d%s" % (
+            r[0][:52], r[1], r[2], r[3], r[4], r[5], r[6], r[7], r[8], r[9], r[10], r[11], r[12],
+            "  <- step" if r[13] else ""))
+    lines += [
+        "",
+        "decode per step (split + merge mean): %.2f us" % (split_us + merge_us),
+        "  decode_split_kernel mean: %.2f us, decode_merge_kernel mean: %.2f us" % (split_us, merge_us),
+        "  effective int8 KV bytes per decode: %d -> %.1f GB/s over split+merge" % (
+            eff, eff / ((split_us + merge_us) * 1e-6) / 1e9),
+        "cache_write (64 tokens) mean: %.2f us" % write_us,
+        "bench.py in the same run (HIP events on the launch stream): decode us_mean %.2f, effective %.1f GB/s" % (
+            bench_trace["decode"]["us_mean"], bench_trace["decode"]["effective_GBps"]),
+        "",
+        "rocprofv3 --stats table (all dispatches of each kernel, fill phase included):",
+    ]
+    with open(os.path.join(d, "trace", "bench_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            lines.append("  %-52s calls %4s avg_ns %12s min_ns %9s max_ns %9s" % (
+                short(r["Name"])[:52], r["Calls"], r["AverageNs"], r["MinNs"], r["MaxNs"]))
+    with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # ---- HBM traffic from FETCH_SIZE / WRITE_SIZE, calibrated by the copy ----
+    mib = args.copy_mib
+    copy_bytes = mib * (1 << 20)
+    factor = {}
+    raw_copy = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cc = counters(os.path.join(d, "copy_" + c, "copy_counter_collection.csv"))
+        vals = [v for (name, _), vs in cc.items() if "copyBuffer" in name for v in vs]
+        kib = statistics.median(vals)
+        raw_copy[c] = kib
+        factor[c] = copy_bytes / (kib * 1024.0)
+    pmc = {}
+    pmc_digest = set()
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        pmc[c] = step_dispatches(counters(os.path.join(d, "pmc_" + c, "bench_counter_collection.csv")), step_grid)
+        pmc_digest.add(last_json(os.path.join(d, "pmc_%s.log" % c))["kernel_sources_sha256_16"])
+    if pmc_digest != {digest}:
+        raise SystemExit("counter runs and trace run were taken on different kernel sources: %s vs %s"
+                         % (pmc_digest, digest))
+    per_kernel = {}
+    for k in DECODE_KERNELS + (WRITE_KERNEL,):
+        rd = statistics.median(pmc["FETCH_SIZE"][k][2]) * 1024.0 * factor["FETCH_SIZE"]
+        wr = statistics.median(pmc["WRITE_SIZE"][k][2]) * 1024.0 * factor["WRITE_SIZE"]
+        per_kernel[k] = (statistics.median(pmc["FETCH_SIZE"][k][2]), statistics.median(pmc["WRITE_SIZE"][k][2]),
+                         rd, wr)
+    dec_bytes = sum(per_kernel[k][2] + per_kernel[k][3] for k in DECODE_KERNELS)
+    t = [
+        "# HBM traffic of the decode launches (split + merge), Llama-3-8B-shaped batch",
+        "# (S=64 H=32 Hkv=8 head_size=128 block_size=16, context lengths U[512,4096], seed 2)",
+        "#",
+        "# commands (from any directory on the GPU machine), one counter per run:",
+        "#   " + PMC_CMD.format(c="FETCH_SIZE", d=args.cmd_dir),
+        "#   " + PMC_CMD.format(c="WRITE_SIZE", d=args.cmd_dir),
+        "#   " + COPY_CMD.format(c="FETCH_SIZE", d=args.cmd_dir, mib=mib),
+        "#   " + COPY_CMD.format(c="WRITE_SIZE", d=args.cmd_dir, mib=mib),
+        "# summarised with: python3 bench_profile.py <that -d directory's parent>",
+        "#",
+        "# Calibration: a plain copy of %d bytes (rocclr copyBuffer, %d MiB) reads FETCH_SIZE %.1f KiB and" % (
+            copy_bytes, mib, raw_copy["FETCH_SIZE"]),
+        "# WRITE_SIZE %.1f KiB per dispatch, so HBM bytes = FETCH_SIZE KiB * 1024 * %.4f and" % (
+            raw_copy["WRITE_SIZE"], factor["FETCH_SIZE"]),
+        "# WRITE_SIZE KiB * 1024 * %.4f." % factor["WRITE_SIZE"],
+        "#",
+        "# per dispatch (median over the step's launches):",
+    ]
+    for k in DECODE_KERNELS + (WRITE_KERNEL,):
+        fk, wk, rd, wr = per_kernel[k]
+        t.append("#   %-20s FETCH_SIZE %10.1f KiB -> %12.0f B read, WRITE_SIZE %9.1f KiB -> %11.0f B written" % (
+            k, fk, rd, wk, wr))
+    t += [
+        "#   algorithmic int8 KV bytes per decode (codes + scale word of every attended row, K and V): %d" % eff,
+        "#   measured decode traffic / algorithmic = %.4f" % (dec_bytes / eff),
+        "",
+        "kernel_sources_sha256_16: %s" % digest,
+        "fetch_factor: %.6f" % factor["FETCH_SIZE"],
+        "write_factor: %.6f" % factor["WRITE_SIZE"],
+        "split_read_bytes: %.0f" % per_kernel["decode_split_kernel"][2],
+        "split_write_bytes: %.0f" % per_kernel["decode_split_kernel"][3],
+        "merge_read_bytes: %.0f" % per_kernel["decode_merge_kernel"][2],
+        "merge_write_bytes: %.0f" % per_kernel["decode_merge_kernel"][3],
+        "hbm_bytes_per_step: %.0f" % dec_bytes,
+    ]
+    with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_traffic.txt"), "w") as f:
+        f.write("\n".join(t) + "\n")
+    print("wrote profiles/q8_paged_decode_llama_kernel_trace.txt and profiles/q8_paged_decode_llama_traffic.txt")
+
+
+def mean_of(rows, tag):
+    sel = [r for r in rows if tag in r[0] and r[13]]
+    return sel[0][4] if sel else float("nan")
+
+
+if __name__ == "__main__":
+    main()
