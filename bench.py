@@ -105,7 +105,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from int8_paged_kv_amd import q8_cache_write, q8_paged_decode, q8_paged_decode_workspace_size, load_library
+    from int8_paged_kv_amd import q8_cache_write, q8_paged_decode, q8_paged_decode_workspace_bytes, load_library
     from int8_paged_kv_amd import workloads as wl
 
     load_library()
@@ -135,7 +135,7 @@ def main():
     sk, sv, ss = f32(step_k), f32(step_v), u32(step_slots)
     S, H, Hkv, hs = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size
     mcl = w.max_context_len
-    ws = torch.empty(max(1, q8_paged_decode_workspace_size(S, H, Hkv, hs, w.block_size, mcl)),
+    ws = torch.empty(max(1, q8_paged_decode_workspace_bytes(S, H, Hkv, hs, w.block_size, mcl)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((S, H, hs), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()

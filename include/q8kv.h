@@ -78,16 +78,16 @@ q8_status q8_cache_write(const float* key, uint32_t key_stride,
                          uint32_t block_size, uint32_t num_blocks, void* stream);
 
 /*
- * q8_paged_decode_workspace_size -- bytes of device workspace q8_paged_decode
+ * q8_paged_decode_workspace_bytes -- bytes of device workspace q8_paged_decode
  * needs for these sizes (per-split softmax partials: running max, sum and the
  * unnormalized output row of every query head and context split; the split
  * plan follows the "attention.rs" page's split-T decode followed by a combine
  * pass).  max_positions is max_context_len in dense mode and vis_stride in
  * visible-list mode.  Returns 0 when no workspace is needed.
  */
-size_t q8_paged_decode_workspace_size(uint32_t num_seqs, uint32_t num_heads,
-                                      uint32_t num_kv_heads, uint32_t head_size,
-                                      uint32_t block_size, uint32_t max_positions);
+size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
+                                       uint32_t num_kv_heads, uint32_t head_size,
+                                       uint32_t block_size, uint32_t max_positions);
 
 /*
  * q8_paged_decode -- single-query decode attention over the int8 paged cache
@@ -110,7 +110,7 @@ size_t q8_paged_decode_workspace_size(uint32_t num_seqs, uint32_t num_heads,
  *                 (num_visible[s] <= vis_stride; positions distinct);
  *                 context_lens and max_context_len are then unused.
  *   scale         f32 softmax scale applied to q.k.
- *   workspace     device memory of at least q8_paged_decode_workspace_size()
+ *   workspace     device memory of at least q8_paged_decode_workspace_bytes()
  *                 bytes, 16-byte aligned; contents on entry do not matter and
  *                 are clobbered.  Concurrent calls need distinct workspaces.
  *

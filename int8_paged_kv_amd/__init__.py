@@ -12,7 +12,7 @@ The binding loads the library lazily, so ``int8_paged_kv_amd.workloads`` can
 be imported on a machine without the library or a GPU.
 """
 
-__all__ = ["q8_cache_write", "q8_paged_decode", "q8_paged_decode_workspace_size",
+__all__ = ["q8_cache_write", "q8_paged_decode", "q8_paged_decode_workspace_bytes",
            "load_library", "Q8Error", "PAD_SLOT"]
 
 

@@ -41,8 +41,8 @@ def load_library() -> ctypes.CDLL:
         P, U = ctypes.c_void_p, ctypes.c_uint32
         lib.q8_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U, P]
         lib.q8_cache_write.restype = ctypes.c_int
-        lib.q8_paged_decode_workspace_size.argtypes = [U, U, U, U, U, U]
-        lib.q8_paged_decode_workspace_size.restype = ctypes.c_size_t
+        lib.q8_paged_decode_workspace_bytes.argtypes = [U, U, U, U, U, U]
+        lib.q8_paged_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.q8_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U, P, P, U,
                                         U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.q8_paged_decode.restype = ctypes.c_int
@@ -112,9 +112,9 @@ def q8_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
     _check(st, "q8_cache_write")
 
 
-def q8_paged_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
+def q8_paged_decode_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
                                    block_size: int, max_positions: int) -> int:
-    return int(load_library().q8_paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads,
+    return int(load_library().q8_paged_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads,
                                                              head_size, block_size, max_positions))
 
 
@@ -154,7 +154,7 @@ def q8_paged_decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     wpt = hs // 4 + 1
     if num_blocks is None:
         num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * wpt)
-    need = lib.q8_paged_decode_workspace_size(S, H, num_kv_heads, hs, block_size, max_pos)
+    need = lib.q8_paged_decode_workspace_bytes(S, H, num_kv_heads, hs, block_size, max_pos)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wp = None if workspace is None else workspace.data_ptr()

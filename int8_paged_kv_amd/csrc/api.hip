@@ -49,9 +49,9 @@ q8_status q8_cache_write(const float* key, uint32_t key_stride,
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
-size_t q8_paged_decode_workspace_size(uint32_t num_seqs, uint32_t num_heads,
-                                      uint32_t num_kv_heads, uint32_t head_size,
-                                      uint32_t block_size, uint32_t max_positions) {
+size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
+                                       uint32_t num_kv_heads, uint32_t head_size,
+                                       uint32_t block_size, uint32_t max_positions) {
     if (num_kv_heads == 0 || num_heads % num_kv_heads != 0) return 0;
     return q8kv::plan_decode(num_seqs, num_heads, num_kv_heads, head_size, block_size,
                              max_positions).bytes;

@@ -91,7 +91,7 @@ def test_decode_validation(lib, kw, want):
 
 def test_workspace_size_matches_plan(lib):
     # single split: no workspace; long contexts: partials for every (seq, head, split)
-    assert lib.q8_paged_decode_workspace_size(2, 4, 2, 128, 16, 64) == 0
-    big = lib.q8_paged_decode_workspace_size(64, 32, 8, 128, 16, 4096)
+    assert lib.q8_paged_decode_workspace_bytes(2, 4, 2, 128, 16, 64) == 0
+    big = lib.q8_paged_decode_workspace_bytes(64, 32, 8, 128, 16, 4096)
     assert big > 64 * 32 * 2 * 130 * 4
     assert big % 4 == 0
