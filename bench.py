@@ -135,7 +135,7 @@ def main():
     sk, sv, ss = f32(step_k), f32(step_v), u32(step_slots)
     S, H, Hkv, hs = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size
     mcl = w.max_context_len
-    ws = torch.empty(max(1, q8_paged_decode_workspace_bytes(S, H, Hkv, hs, w.block_size, mcl)),
+    ws = torch.zeros(max(1, q8_paged_decode_workspace_bytes(S, H, Hkv, hs, w.block_size, mcl)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((S, H, hs), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()

@@ -79,11 +79,13 @@ q8_status q8_cache_write(const float* key, uint32_t key_stride,
 
 /*
  * q8_paged_decode_workspace_bytes -- bytes of device workspace q8_paged_decode
- * needs for these sizes (per-split softmax partials: running max, sum and the
- * unnormalized output row of every query head and context split; the split
- * plan follows the "attention.rs" page's split-T decode followed by a combine
- * pass).  max_positions is max_context_len in dense mode and vis_stride in
- * visible-list mode.  Returns 0 when no workspace is needed.
+ * needs for these sizes: softmax partials (running max, sum and unnormalized
+ * output row per query head) of sequences whose positions are split over
+ * several wavefronts, plus one arrival counter per (kv head group, sequence);
+ * the split-context decode with a combine step follows the "attention.rs"
+ * page.  max_positions is max_context_len in dense mode and vis_stride in
+ * visible-list mode.  Returns 0 when no workspace is needed (every sequence
+ * has at most 64 positions).  Pure host arithmetic; needs no GPU.
  */
 size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
                                        uint32_t num_kv_heads, uint32_t head_size,
@@ -96,7 +98,7 @@ size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
  * block_tables[s*max_num_blocks_per_seq + t/block_size], offset
  * t % block_size, context length clamped to max_context_len).
  *
- *   out           f32 [num_seqs, num_heads, head_size], dense.
+ *   out           f32 [num_seqs, num_heads, head_size], dense, 16-byte aligned.
  *   q             f32; element d of head h of seq s at q[s*q_stride + h*head_size + d].
  *   key_cache,    u32 caches in the format above.
  *   value_cache
@@ -111,8 +113,12 @@ size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
  *                 context_lens and max_context_len are then unused.
  *   scale         f32 softmax scale applied to q.k.
  *   workspace     device memory of at least q8_paged_decode_workspace_bytes()
- *                 bytes, 16-byte aligned; contents on entry do not matter and
- *                 are clobbered.  Concurrent calls need distinct workspaces.
+ *                 bytes, 16-byte aligned, ZERO-FILLED before its first use
+ *                 (e.g. hipMemset once after allocation).  Each completed
+ *                 call leaves its counters at zero again, so the same
+ *                 workspace serves any later call without clearing; after a
+ *                 failed or aborted launch, zero it again.  Concurrent calls
+ *                 need distinct workspaces.
  *
  * An empty position set gives a zero output row.  Accuracy: each output is
  * within 1e-4 + 1e-4*|exact| of the exact attention over the dequantized cache
@@ -122,7 +128,8 @@ size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
  * num_kv_heads is 0, num_heads % num_kv_heads != 0, q_stride <
  * num_heads*head_size, max_num_blocks_per_seq is 0 while positions are
  * possible, or vis_stride is 0 in visible-list mode; Q8_ERR_WORKSPACE when the
- * workspace is too small or misaligned.  num_seqs == 0 enqueues nothing.
+ * workspace is too small or misaligned; Q8_ERR_UNSUPPORTED when out is not
+ * 16-byte aligned.  num_seqs == 0 enqueues nothing.
  */
 q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
                           const uint32_t* key_cache, const uint32_t* value_cache,

@@ -127,7 +127,9 @@ def q8_paged_decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
     """Decode attention over the int8 paged cache; q is [S, H, hs] f32 (see include/q8kv.h).
 
     max_context_len must be given in dense mode (reading context_lens would
-    synchronize).  In visible-list mode vis_stride is visible_pos.shape[1]."""
+    synchronize).  In visible-list mode vis_stride is visible_pos.shape[1].
+    A caller-provided workspace must have been zero-filled before its first
+    use; every call leaves it ready for the next one."""
     lib = load_library()
     if q.dim() != 3 or (q.numel() and not q[0].is_contiguous()):
         raise ValueError("q must be [S, H, head_size] with dense rows")
@@ -156,7 +158,7 @@ def q8_paged_decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
         num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * wpt)
     need = lib.q8_paged_decode_workspace_bytes(S, H, num_kv_heads, hs, block_size, max_pos)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)   # zero before first use
     wp = None if workspace is None else workspace.data_ptr()
     wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.q8_paged_decode(_dev(out, "out", torch.float32), _dev(q, "q", torch.float32), q.stride(0),

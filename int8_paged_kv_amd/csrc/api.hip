@@ -79,11 +79,11 @@ q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
     const uint32_t max_pos = vis ? vis_stride : max_context_len;
     if (max_pos > 0 && (max_num_blocks_per_seq == 0 || num_blocks == 0)) return Q8_ERR_SHAPE;
     if (!std::isfinite(scale)) return Q8_ERR_SHAPE;
-    // Grid limits: one workgroup per work item in a 1-D grid.
+    if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return Q8_ERR_UNSUPPORTED;   // rows are written as 16-byte stores
+    // Grid limits: one wavefront per workgroup in 1-D grids.
     const q8kv::DecodePlan p = q8kv::plan_decode(num_seqs, num_heads, num_kv_heads, head_size,
                                                  block_size, max_pos);
-    const uint64_t items = static_cast<uint64_t>(num_seqs) * num_kv_heads * p.num_groups * p.num_splits;
-    if (items > 0x7FFFFFFFull || static_cast<uint64_t>(num_seqs) * num_heads > 0x7FFFFFFFull)
+    if (p.num_waves > 0x7FFFFFFFull || static_cast<uint64_t>(num_seqs) * num_heads > 0x7FFFFFFFull)
         return Q8_ERR_UNSUPPORTED;
     if (p.bytes > 0) {
         if (!workspace || workspace_bytes < p.bytes) return Q8_ERR_WORKSPACE;
@@ -99,6 +99,7 @@ q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
     a.visible_pos = visible_pos;
     a.num_visible = num_visible;
     char* ws = static_cast<char*>(workspace);
+    a.counters = p.bytes ? reinterpret_cast<uint32_t*>(ws + p.counters_offset) : nullptr;
     a.part_acc = p.bytes ? reinterpret_cast<float*>(ws + p.acc_offset) : nullptr;
     a.part_ml = p.bytes ? reinterpret_cast<float*>(ws + p.ml_offset) : nullptr;
     a.q_stride = q_stride;

@@ -11,14 +11,23 @@
 //
 // MI355X design (not the page's one-workgroup-per-(seq, head) three-pass
 // shader):
-//   * Work item = one wavefront for (seq, kv head, up to 8 query heads sharing
-//     that kv head, context split).  Each K/V byte is read from HBM once for
-//     the whole GQA group.
-//   * Positions are processed in chunks of 64.  A chunk of consecutive,
-//     64-aligned positions is a run of whole cache tiles (or one 64-row slice
-//     of a larger tile): it is fetched with coalesced 16-byte loads into
-//     registers one chunk ahead of use, then written to LDS.  Other chunks
-//     (visible lists with gaps) are gathered row by row.
+//   * Positions are processed in chunks of 64.  For one row group (kv head,
+//     up to 8 query heads sharing it) the chunks of all sequences form one
+//     sequence of C chunks; a fixed number of persistent wavefronts per row
+//     group each take an equal contiguous range of it (the split-context idea
+//     of the "attention.rs" page, balanced over the whole batch instead of per
+//     sequence), so every wave does the same amount of work and there is no
+//     tail.  A wave that covers a whole sequence writes its output directly;
+//     otherwise it writes softmax partials (running max, sum, unnormalized
+//     output) and a merge kernel combines them.  Wavefronts are numbered kv
+//     head fastest, so the kv-head slices of the same cache blocks are
+//     requested together.  Each K/V byte is read once per row group.
+//   * A chunk of 64 consecutive, 64-aligned positions is a run of whole cache
+//     tiles (or one 64-row slice of a larger tile): it is fetched with
+//     coalesced 16-byte loads into registers, up to two chunks ahead of use,
+//     then written to LDS.  The loads are unconditional (masked slots read a
+//     fixed line), so the compiler's wait counts stay exact across the loop.
+//     Other chunks (visible lists with gaps) are gathered row by row.
 //   * Both contractions run on the int8 matrix cores
 //     (v_mfma_i32_16x16x64_i8), whose operands include the cache's own codes:
 //       q.K^T: each query head's q row is scaled by a power of two and rounded
@@ -34,9 +43,7 @@
 //     carries f32-level rounding error only.
 //   * Online softmax in the exp2 domain (scale folded with log2 e).  Each
 //     MFMA output row group is one head, so the per-head max and sum reduce
-//     over the 16 lanes of a DPP row.  Running max, sum and the unnormalized
-//     output of each split go to the workspace, and a merge kernel combines
-//     the splits (single-split rows are written out directly).
+//     over the 16 lanes of a DPP row.
 #include "q8kv_internal.h"
 
 namespace q8kv {
@@ -113,8 +120,47 @@ __device__ __forceinline__ int exponent_bound(float x) {
     return e;
 }
 
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t t = __shfl_up(v, d, kWave);
+        if (lane >= static_cast<uint32_t>(d)) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), static_cast<int>(l)));
+}
+
+// Chunks of K/V loaded ahead of use by the split kernel (1 or 2; 2 needs
+// about 66 more VGPRs at head_size 128).
+#ifndef Q8KV_DECODE_DEPTH
+#define Q8KV_DECODE_DEPTH 1
+#endif
+constexpr int kPrefetchDepth = Q8KV_DECODE_DEPTH;
+
 struct SplitConsts {
-    uint32_t split_tokens, num_splits, group, num_groups;
+    uint32_t waves_per_rg;  // persistent wavefronts per row group (before capping by the chunk count)
+    uint32_t num_rg;        // row groups: num_kv_heads * num_groups
+    uint32_t group, num_groups;
+    uint32_t recs_per_rg;   // partial records per row group: waves_per_rg + num_seqs - 1
     uint32_t seg_u4;        // 16-byte units per tile segment in a chunk
     uint32_t seg_magic;     // ceil(2^32 / seg_u4): u / seg_u4 == mulhi(u, magic) for u < 2^16
     uint32_t seg_rows;      // rows per segment = min(block_size, 64)
@@ -138,8 +184,80 @@ __device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s
 }
 
 template <bool VIS>
+__device__ __forceinline__ uint32_t chunks_of(const DecodeArgs& a, uint32_t s) {
+    return (positions_of<VIS>(a, s) + kChunk - 1) / kChunk;
+}
+
+template <bool VIS>
 __device__ __forceinline__ uint32_t position_at(const DecodeArgs& a, uint32_t s, uint32_t idx) {
     return VIS ? a.visible_pos[static_cast<uint64_t>(s) * a.vis_stride + idx] : idx;
+}
+
+// Device-coherent (agent scope) accesses for data handed between wavefronts
+// that may run on different XCDs: they bypass the non-coherent L2 copies, so
+// no whole-cache write-back or invalidation is needed.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Zero output rows of sequences [s_begin, s_end) for query heads h0 .. h0+nh-1.
+__device__ void zero_rows(const DecodeArgs& a, uint32_t lane, uint32_t s_begin, uint32_t s_end, uint32_t h0,
+                          uint32_t nh) {
+    const uint32_t hs4 = a.head_size / 4;
+    for (uint32_t s = s_begin; s < s_end; ++s)
+        for (uint32_t p = lane; p < nh * hs4; p += kWave) {
+            const uint64_t row = static_cast<uint64_t>(s) * a.num_heads + h0 + p / hs4;
+            *reinterpret_cast<float4*>(a.out + row * a.head_size + 4 * (p % hs4)) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+}
+
+// Chunk sequence of one row group: the chunks of sequence 0, then sequence 1,
+// ...  Wave-uniform results.
+//   chunk_totals: total chunk count C and the chunks of sequences before s.
+template <bool VIS>
+__device__ void chunk_totals(const DecodeArgs& a, uint32_t lane, uint32_t s, uint32_t& total, uint32_t& before) {
+    total = 0;
+    before = 0;
+    for (uint32_t b = 0; b < a.num_seqs; b += kWave) {
+        const uint32_t t = b + lane;
+        const uint32_t nc = t < a.num_seqs ? chunks_of<VIS>(a, t) : 0u;
+        const uint32_t incl = wave_incl_scan(nc, lane);
+        const uint32_t wt = lane_value(incl, kWave - 1);
+        if (s >= b + kWave) before += wt;
+        else if (s > b) before += lane_value(incl, s - b - 1);
+        total += wt;
+    }
+}
+
+//   locate_chunk: the sequence holding chunk x (x < C) and the chunks before it.
+template <bool VIS>
+__device__ void locate_chunk(const DecodeArgs& a, uint32_t lane, uint32_t x, uint32_t& row, uint32_t& before) {
+    uint32_t base = 0;
+    row = a.num_seqs;
+    before = 0;
+    for (uint32_t b = 0; b < a.num_seqs; b += kWave) {
+        const uint32_t t = b + lane;
+        const uint32_t nc = t < a.num_seqs ? chunks_of<VIS>(a, t) : 0u;
+        const uint32_t incl = wave_incl_scan(nc, lane);
+        const uint32_t wt = lane_value(incl, kWave - 1);
+        if (x < base + wt) {
+            const uint64_t m = __ballot(base + incl > x);
+            const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(m));
+            row = b + l;
+            before = base + lane_value(incl - nc, l);
+            return;
+        }
+        base += wt;
+    }
+}
+
+// Wave (of the W covering the C chunks of a row group) whose range holds chunk
+// x: wave j covers [floor(j*C/W), floor((j+1)*C/W)).
+__device__ __forceinline__ uint32_t wave_of_chunk(uint32_t x, uint32_t C, uint32_t W) {
+    return static_cast<uint32_t>(((static_cast<uint64_t>(x) + 1) * W - 1) / C);
 }
 
 // Split-kernel lane roles.  Lane l = 16*g + r.
@@ -153,164 +271,203 @@ __device__ __forceinline__ uint32_t position_at(const DecodeArgs& a, uint32_t s,
 //   block cw is dimension 4*NCW*r + 4*cw + j of MFMA j; it receives the digit
 //   sums of those dimensions for head g.
 //
-// Data movement: a chunk of 64 consecutive, 64-aligned positions is a run of
-// whole cache tiles (or a 64-row slice of a larger tile), so its K and V rows
-// arrive with fully coalesced 16-byte loads (one KiB per instruction) into
-// registers, one chunk ahead of use, and are then written to LDS, from where
-// each lane reads its MFMA operands.  Chunks of a visible list that are not
-// such runs are gathered row by row.  The block ids a chunk needs are read two
-// chunks ahead, so no block-table read sits between a data load and its use.
-//
 // HS4P: code words per row rounded up to 16, 32, 48 or 64; EXACT: head_size /
-// 4 == HS4P; NHS: sets of 4 query heads per work item (1 or 2).
-template <int HS4P, bool EXACT, int NHS, bool VIS>
-__global__ __launch_bounds__(64, (HS4P <= 32 && NHS == 1) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
+// 4 == HS4P; NHS: sets of 4 query heads per wavefront (1 or 2); VIS: visible
+// list positions; TILED: every chunk is known to be a tile run (dense
+// positions, aligned caches, block_size dividing or a multiple of 64).
+template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED>
+__global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
     constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
     constexpr int NCW = HS4P / 16;             // V code words per lane and row
     constexpr int G = 4 * NHS;
     constexpr int QD = NKB * 64;               // padded q row length
     constexpr int WPT_MAX = HS4P + 1;
     constexpr int NU = (kChunk * WPT_MAX + 4 * kWave - 1) / (4 * kWave);   // 16-byte slots per lane
+    // An exact head size makes a chunk 64*(HS4P+1) words: HS4P/4 full 16-byte
+    // slots per lane plus one 4-byte tail slot per lane.
+    constexpr int NF = EXACT ? HS4P / 4 : NU;
+    struct Buf {
+        u32x4 k[NF], v[NF];
+        uint32_t kt, vt;
+    };
+    constexpr int DEPTH = (HS4P <= 32 && NHS == 1) ? kPrefetchDepth : 1;  // chunks loaded ahead
 
-    __shared__ __align__(16) uint32_t sK[kChunk * WPT_MAX + 64];
-    __shared__ __align__(16) uint32_t sV[kChunk * WPT_MAX + 64];
-    __shared__ __align__(16) float sQ[G * QD];
+    __shared__ __align__(16) uint32_t sK[NU * 4 * kWave];   // also stages q rows at sequence changes
+    __shared__ __align__(16) uint32_t sV[NU * 4 * kWave];
     __shared__ __align__(16) uint32_t sA[NHS * 16 * 16];   // [set][head*4+digit][w]: weight digits, 4 tokens a word
     __shared__ int sEq[G];
+    __shared__ float sMerge[2 * G];                           // per-head (max, sum) while combining records
+    float* const sQ = reinterpret_cast<float*>(sK);
 
     const uint32_t lane = threadIdx.x;
     const uint32_t r = lane & 15, g = lane >> 4;
-    // Work item = ((s * num_splits + split) * num_kv_heads + kvh) * num_groups + grp:
-    // the kv heads of one (seq, split) are dispatched together, so the slices of
-    // each cache block that they read reach the memory controllers close in time.
-    const uint32_t grp = blockIdx.x % c.num_groups;
-    const uint32_t kvh = (blockIdx.x / c.num_groups) % a.num_kv_heads;
-    const uint32_t ss = blockIdx.x / c.num_groups / a.num_kv_heads;
-    const uint32_t split = ss % c.num_splits;
-    const uint32_t s = ss / c.num_splits;
-    const uint32_t n_pos = positions_of<VIS>(a, s);
-    const uint32_t t0 = split * c.split_tokens;
-    if (t0 >= n_pos) return;
-    const uint32_t t1 = min(n_pos, t0 + c.split_tokens);
-    const uint32_t n_split_s = (n_pos + c.split_tokens - 1) / c.split_tokens;
-    const uint32_t n_chunks = (t1 - t0 + kChunk - 1) / kChunk;
+    const uint32_t rg = blockIdx.x % c.num_rg;
+    const uint32_t j = blockIdx.x / c.num_rg;
+    const uint32_t kvh = rg % a.num_kv_heads;
+    const uint32_t grp = rg / a.num_kv_heads;
 
-    const uint32_t hs = a.head_size, hs4 = EXACT ? HS4P : hs / 4, wpt = hs4 + 1;
+    // ---- this wave's chunk range [x0, x1) of the row group's chunk sequence ----
+    // Up to 64 sequences: one load and one scan give the total, the range and
+    // the sequence holding its first chunk.
+    const bool one_window = a.num_seqs <= static_cast<uint32_t>(kWave);
+    uint32_t C, win_np = 0, win_nc = 0, win_incl = 0;
+    if (one_window) {
+        win_np = lane < a.num_seqs ? positions_of<VIS>(a, lane) : 0u;
+        win_nc = (win_np + kChunk - 1) / kChunk;
+        win_incl = wave_incl_scan(win_nc, lane);
+        C = lane_value(win_incl, kWave - 1);
+    } else {
+        uint32_t unused;
+        chunk_totals<VIS>(a, lane, 0, C, unused);
+    }
+    C = uniform(C);
+    const uint32_t W = min(c.waves_per_rg, C);
     const uint32_t n_rep = a.num_heads / a.num_kv_heads;
     const uint32_t h0 = kvh * n_rep + grp * G;
     const uint32_t nh = min(static_cast<uint32_t>(G), n_rep - grp * G);
-    const uint64_t seq_bt = static_cast<uint64_t>(s) * a.max_num_blocks_per_seq;
+    if (j >= W) {
+        if (C == 0 && j == 0) zero_rows(a, lane, 0, a.num_seqs, h0, nh);
+        return;
+    }
+    const uint32_t x0 = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j) * C / W));
+    const uint32_t x1 = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j + 1) * C / W));
+    const uint32_t n = x1 - x0;
+    uint32_t s0, p0c, np0 = 0;
+    if (one_window) {
+        const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(__ballot(win_incl > x0)));
+        s0 = l;
+        p0c = lane_value(win_incl - win_nc, l);
+        np0 = lane_value(win_np, l);
+    } else {
+        locate_chunk<VIS>(a, lane, x0, s0, p0c);
+    }
+    if (uniform(s0) >= a.num_seqs) return;    // unreachable for x0 < C
+
+    const uint32_t hs = a.head_size, hs4 = EXACT ? HS4P : hs / 4, wpt = hs4 + 1;
     const uint64_t kv_stride = static_cast<uint64_t>(a.num_kv_heads) * a.block_size * wpt;  // words per block
     const uint64_t kvh_off = static_cast<uint64_t>(kvh) * a.block_size * wpt;
     const uint32_t chunk_u4 = kChunk * wpt / 4;
     const uint32_t nseg = kChunk / c.seg_rows;            // tile segments per tiled chunk
 
-    // ---- stage q rows (zero for padded dims and absent heads) ----
-    for (uint32_t i = lane; i < G * QD; i += kWave) {
-        const uint32_t hi = i / QD, d = i % QD;
-        float v = 0.0f;
-        if (hi < nh && d < hs) v = a.q[static_cast<uint64_t>(s) * a.q_stride + static_cast<uint64_t>(h0 + hi) * hs + d];
-        sQ[i] = v;
-    }
-    __syncthreads();
-
-    // ---- q digits: MFMA row r = (head r/4, digit r%4), k = dims 64kb+16g+0..15 ----
-    i32x4 qa[NHS][NKB];
-#pragma unroll
-    for (int hset = 0; hset < NHS; ++hset) {
-        const uint32_t hq = 4 * hset + r / 4, dig = r % 4;
-        const float* row = &sQ[hq * QD];
-        float amax = 0.0f;
-        for (int d = 0; d < QD; d += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(row + d);
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        }
-        const int eq = amax > 0.0f ? 30 - exponent_bound(amax) : 0;    // |q * 2^eq| < 2^30
-        if (g == 0 && dig == 0) sEq[hq] = eq;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            uint32_t packed[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float4 v = *reinterpret_cast<const float4*>(row + 64 * kb + 16 * g + 4 * w);
-                const uint32_t b0 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.x, eq)))) >> (8 * dig)) & 0xFFu;
-                const uint32_t b1 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.y, eq)))) >> (8 * dig)) & 0xFFu;
-                const uint32_t b2 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.z, eq)))) >> (8 * dig)) & 0xFFu;
-                const uint32_t b3 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.w, eq)))) >> (8 * dig)) & 0xFFu;
-                packed[w] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-            }
-            qa[hset][kb] = i32x4{static_cast<int32_t>(packed[0]), static_cast<int32_t>(packed[1]),
-                                 static_cast<int32_t>(packed[2]), static_cast<int32_t>(packed[3])};
-        }
-    }
-    __syncthreads();
-    int eq_out[NHS];       // q exponent of this lane's output head 4*hset + g
-#pragma unroll
-    for (int hset = 0; hset < NHS; ++hset) eq_out[hset] = sEq[4 * hset + g];
-
-    // ---- chunk metadata, prepared two chunks ahead ----
-    // Tiled chunk: lane k holds the block id of segment k.  Row-gathered chunk:
-    // lane i holds the block id and in-block row of the chunk's i-th position.
-    struct Meta {
-        uint32_t cs, nv, p0, id, row, tiled;
+    // ---- cursor over the chunk sequence (wave-uniform) ----
+    struct Cursor {
+        uint32_t s, ci, npos, before;    // sequence, chunk index in it, its positions, chunks before it
     };
-    auto meta_of = [&](uint32_t cs_) __attribute__((always_inline)) -> Meta {
+    Cursor cur{uniform(s0), 0, 0, uniform(p0c)};
+    cur.ci = x0 - cur.before;
+    cur.npos = one_window ? uniform(np0) : uniform(positions_of<VIS>(a, cur.s));
+    // Sequences with no positions get zero rows.  Each is written by exactly
+    // one wave of the row group: the one whose range it falls inside, wave 0
+    // for those before the first chunk, the last wave for those after it.
+    auto advance = [&]() __attribute__((always_inline)) {
+        ++cur.ci;
+        if (cur.ci * kChunk >= cur.npos) {
+            cur.before += (cur.npos + kChunk - 1) / kChunk;
+            cur.ci = 0;
+            while (true) {
+                ++cur.s;
+                cur.npos = cur.s < a.num_seqs ? uniform(positions_of<VIS>(a, cur.s)) : static_cast<uint32_t>(kChunk);
+                if (cur.npos != 0) break;
+                zero_rows(a, lane, cur.s, cur.s + 1, h0, nh);
+            }
+        }
+    };
+    if (j == 0) zero_rows(a, lane, 0, cur.s, h0, nh);
+
+    // ---- chunk metadata (uniform except the block id of segment `lane`) ----
+    // info: bits 0-6 valid positions (0 for a chunk past the wave's range),
+    // bit 7 tiled chunk, bits 8-31 the number of waves whose ranges share the
+    // sequence (1: it lies wholly in this wave's range); jf: the first of them.
+    struct Meta {
+        uint32_t s, cs, p0, info, jf, id;
+    };
+    auto meta_nv = [](const Meta& m) __attribute__((always_inline)) { return m.info & 0x7Fu; };
+    auto meta_tiled = [](const Meta& m) __attribute__((always_inline)) { return TILED || (m.info & 0x80u) != 0; };
+    auto meta_nrec = [](const Meta& m) __attribute__((always_inline)) { return m.info >> 8; };
+    auto meta_of = [&](bool live) __attribute__((always_inline)) -> Meta {
         Meta m;
-        m.cs = cs_;
-        m.nv = min(static_cast<uint32_t>(kChunk), t1 - cs_);
-        m.p0 = position_at<VIS>(a, s, cs_);
-        m.tiled = c.tiled_ok;
-        if (VIS && m.tiled) {
-            const uint32_t pl = position_at<VIS>(a, s, cs_ + m.nv - 1);
-            m.tiled = (m.p0 % kChunk == 0) && (pl - m.p0 == m.nv - 1) ? 1u : 0u;
+        m.s = cur.s;
+        m.cs = cur.ci * kChunk;
+        const uint32_t nv = live ? min(static_cast<uint32_t>(kChunk), cur.npos - m.cs) : 0u;
+        m.p0 = VIS ? uniform(position_at<VIS>(a, m.s, m.cs)) : m.cs;
+        uint32_t tiled = 1;
+        if (!TILED) {
+            tiled = c.tiled_ok;
+            if (VIS && tiled && nv > 0) {
+                const uint32_t pl = uniform(position_at<VIS>(a, m.s, m.cs + nv - 1));
+                tiled = (m.p0 % kChunk == 0) && (pl - m.p0 == nv - 1) ? 1u : 0u;
+            }
         }
-        uint32_t j;
-        m.row = 0;
-        if (m.tiled) {
-            const uint32_t k = min(lane, nseg - 1);
-            j = m.p0 / a.block_size + (a.block_size <= kChunk ? k : 0);
-        } else {
-            const uint32_t pos = position_at<VIS>(a, s, cs_ + min(lane, m.nv - 1));
-            j = pos / a.block_size;
-            m.row = pos % a.block_size;
-        }
-        j = j < a.max_num_blocks_per_seq ? j : a.max_num_blocks_per_seq - 1;
-        m.id = a.block_tables[seq_bt + j];
+        const uint32_t nc = (cur.npos + kChunk - 1) / kChunk;
+        m.jf = wave_of_chunk(cur.before, C, W);
+        const uint32_t nrec = wave_of_chunk(cur.before + nc - 1, C, W) - m.jf + 1;
+        m.info = nv | (tiled << 7) | (nrec << 8);
+        const uint32_t k = min(lane, nseg - 1);
+        uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(kChunk) ? k : 0u);
+        jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
+        m.id = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
         return m;
     };
 
-    // ---- tiled chunk: 16-byte slot u = lane + 64*i lies in segment u / seg_u4 ----
-    u32x4 kreg[NU], vreg[NU];
-    auto issue_data = [&](const Meta& m) __attribute__((always_inline)) {
+    // ---- tiled chunk loads: 16-byte slot u = lane + 64*i lies in segment u / seg_u4 ----
+    // Slots outside the chunk's valid segments read the first line of this kv
+    // head's tile of block 0 instead (always in bounds, one cached line).
+    auto issue_data = [&](const Meta& m, Buf& b) __attribute__((always_inline)) {
+        if (!TILED && !c.tiled_ok) return;     // no tile loads at all (caches not 16-byte aligned, odd block_size)
         const uint32_t row0 = m.p0 % a.block_size;     // nonzero only when block_size > 64
+        const bool ok = meta_tiled(m);
+        const uint32_t nv = meta_nv(m);
+        const uint64_t base = kvh_off + static_cast<uint64_t>(row0) * wpt;
+        // Recompute the slot geometry per chunk (a few VALU ops) rather than
+        // keeping it live across the loop.
+        uint32_t ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            const uint32_t u = lane + kWave * i;
+        for (int i = 0; i < NF; ++i) {
+            const uint32_t u = ln + kWave * i;
             const uint32_t k = __umulhi(u, c.seg_magic);
             uint32_t phys = __shfl(m.id, static_cast<int>(min(k, nseg - 1)), 64);
             phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
-            if ((u < chunk_u4) && (k * c.seg_rows < m.nv)) {
-                const uint32_t off = (u - k * c.seg_u4) * 4;
-                const uint64_t w = phys * kv_stride + kvh_off + static_cast<uint64_t>(row0) * wpt + off;
-                kreg[i] = *reinterpret_cast<const u32x4*>(a.key_cache + w);
-                vreg[i] = *reinterpret_cast<const u32x4*>(a.value_cache + w);
-            }
+            const bool valid = ok && (EXACT || u < chunk_u4) && (k * c.seg_rows < nv);
+            const uint64_t w = valid ? phys * kv_stride + base + (u - k * c.seg_u4) * 4 : kvh_off;
+            b.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.key_cache + w));
+            b.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.value_cache + w));
+        }
+        if (EXACT) {
+            const uint32_t wi = 4 * kWave * NF + ln;
+            const uint32_t k = __umulhi(wi >> 2, c.seg_magic);
+            uint32_t phys = __shfl(m.id, static_cast<int>(min(k, nseg - 1)), 64);
+            phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
+            const bool valid = ok && (k * c.seg_rows < nv);
+            const uint64_t w = valid ? phys * kv_stride + base + (wi - 4 * k * c.seg_u4) : kvh_off;
+            b.kt = __builtin_nontemporal_load(a.key_cache + w);
+            b.vt = __builtin_nontemporal_load(a.value_cache + w);
         }
     };
-    auto store = [&](const Meta& m) __attribute__((always_inline)) {
-        if (m.tiled) {
+    auto store = [&](const Meta& m, const Buf& b) __attribute__((always_inline)) {
+        if (meta_tiled(m)) {
 #pragma unroll
-            for (int i = 0; i < NU; ++i) {
+            for (int i = 0; i < NF; ++i) {
                 const uint32_t u = lane + kWave * i;
-                if (u < chunk_u4 && __umulhi(u, c.seg_magic) * c.seg_rows < m.nv) {
-                    *reinterpret_cast<u32x4*>(&sK[4 * u]) = kreg[i];
-                    *reinterpret_cast<u32x4*>(&sV[4 * u]) = vreg[i];
-                }
+                *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k[i];
+                *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v[i];
+            }
+            if (EXACT) {
+                sK[4 * kWave * NF + lane] = b.kt;
+                sV[4 * kWave * NF + lane] = b.vt;
             }
         } else {
-            const uint32_t phys = m.id < num_blocks_m1 ? m.id : num_blocks_m1;
-            const uint64_t my_row = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size + m.row) * wpt;
-            for (uint32_t rr = 0; rr < m.nv; ++rr) {
+            // Row gather: lane i resolves the chunk's i-th position, then the
+            // wave copies the rows one after another.
+            const uint32_t nv = meta_nv(m);
+            const uint32_t pos = position_at<VIS>(a, m.s, m.cs + min(lane, nv - 1));
+            uint32_t jb = pos / a.block_size;
+            jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
+            uint32_t phys = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
+            phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
+            const uint64_t my_row = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size +
+                                     pos % a.block_size) * wpt;
+            for (uint32_t rr = 0; rr < nv; ++rr) {
                 const uint32_t lo = __shfl(static_cast<uint32_t>(my_row), rr, 64);
                 const uint32_t hi = __shfl(static_cast<uint32_t>(my_row >> 32), rr, 64);
                 const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
@@ -322,18 +479,74 @@ __global__ __launch_bounds__(64, (HS4P <= 32 && NHS == 1) ? 2 : 1) void decode_s
         }
     };
 
+    // ---- q digits of the current sequence: MFMA row r = (head r/4, digit r%4) ----
+    i32x4 qa[NHS][NKB];
+    int eq_out[NHS];       // q exponent of this lane's output head 4*hset + g
+    constexpr int QV = G * QD / kWave;                        // q values staged per lane
+    float qv[QV];
+    auto q_issue = [&](uint32_t s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < QV; ++t) {
+            const uint32_t i = lane + kWave * t;
+            const uint32_t hi = i / QD, d = i % QD;
+            qv[t] = (hi < nh && d < hs) ? a.q[static_cast<uint64_t>(s) * a.q_stride + static_cast<uint64_t>(h0 + hi) * hs + d]
+                                        : 0.0f;
+        }
+    };
+    auto q_finish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < QV; ++t) sQ[lane + kWave * t] = qv[t];
+        __syncthreads();
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) {
+            const uint32_t hq = 4 * hset + r / 4, dig = r % 4;
+            const float* row = &sQ[hq * QD];
+            float amax = 0.0f;
+            for (int d = 0; d < QD; d += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(row + d);
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+            const int eq = amax > 0.0f ? 30 - exponent_bound(amax) : 0;    // |q * 2^eq| < 2^30
+            if (g == 0 && dig == 0) sEq[hq] = eq;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                uint32_t packed[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float4 v = *reinterpret_cast<const float4*>(row + 64 * kb + 16 * g + 4 * w);
+                    const uint32_t b0 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.x, eq)))) >> (8 * dig)) & 0xFFu;
+                    const uint32_t b1 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.y, eq)))) >> (8 * dig)) & 0xFFu;
+                    const uint32_t b2 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.z, eq)))) >> (8 * dig)) & 0xFFu;
+                    const uint32_t b3 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.w, eq)))) >> (8 * dig)) & 0xFFu;
+                    packed[w] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+                }
+                qa[hset][kb] = i32x4{static_cast<int32_t>(packed[0]), static_cast<int32_t>(packed[1]),
+                                     static_cast<int32_t>(packed[2]), static_cast<int32_t>(packed[3])};
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) eq_out[hset] = sEq[4 * hset + g];
+    };
+    auto load_q = [&](uint32_t s) __attribute__((always_inline)) {
+        q_issue(s);
+        q_finish();
+    };
+
     // Online-softmax state (log2 units) of head 4*hset + g, uniform across the lane's row.
     float m_run[NHS], l_run[NHS];
     float acc[NHS][NCW][4];      // dims 4*NCW*r + 4*cw + j of head 4*hset + g
+    auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int hset = 0; hset < NHS; ++hset) {
-        m_run[hset] = -INFINITY;
-        l_run[hset] = 0.0f;
+        for (int hset = 0; hset < NHS; ++hset) {
+            m_run[hset] = -INFINITY;
+            l_run[hset] = 0.0f;
 #pragma unroll
-        for (int cw = 0; cw < NCW; ++cw)
+            for (int cw = 0; cw < NCW; ++cw)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[hset][cw][j] = 0.0f;
-    }
+                for (int jj = 0; jj < 4; ++jj) acc[hset][cw][jj] = 0.0f;
+        }
+    };
 
     // One chunk from LDS: q.K^T, online softmax, P.V.
     auto process = [&](uint32_t nv) __attribute__((always_inline)) {
@@ -405,7 +618,7 @@ __global__ __launch_bounds__(64, (HS4P <= 32 && NHS == 1) ? 2 : 1) void decode_s
 #pragma unroll
             for (int cw = 0; cw < NCW; ++cw)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[hset][cw][j] *= alpha;
+                for (int jj = 0; jj < 4; ++jj) acc[hset][cw][jj] *= alpha;
         }
         __syncthreads();
 
@@ -428,117 +641,239 @@ __global__ __launch_bounds__(64, (HS4P <= 32 && NHS == 1) ? 2 : 1) void decode_s
                 }
                 transpose4(x, y);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bj[j][w] = y[j];
+                for (int jj = 0; jj < 4; ++jj) bj[jj][w] = y[jj];
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const i32x4 b = i32x4{static_cast<int32_t>(bj[j][0]), static_cast<int32_t>(bj[j][1]),
-                                      static_cast<int32_t>(bj[j][2]), static_cast<int32_t>(bj[j][3])};
+            for (int jj = 0; jj < 4; ++jj) {
+                const i32x4 b = i32x4{static_cast<int32_t>(bj[jj][0]), static_cast<int32_t>(bj[jj][1]),
+                                      static_cast<int32_t>(bj[jj][2]), static_cast<int32_t>(bj[jj][3])};
 #pragma unroll
                 for (int hset = 0; hset < NHS; ++hset) {
                     const i32x4 d = mfma_i8(pa[hset], b, i32x4{0, 0, 0, 0});
-                    acc[hset][cw][j] += static_cast<float>(combine_digits(d) * pscale);
+                    acc[hset][cw][jj] += static_cast<float>(combine_digits(d) * pscale);
                 }
             }
         }
     };
 
-    // ---- pipeline: data one chunk ahead, block ids two chunks ahead ----
-    Meta cur = meta_of(t0);
-    if (cur.tiled) issue_data(cur);
-    Meta nxt = cur;
-    if (n_chunks > 1) nxt = meta_of(t0 + kChunk);
-    for (uint32_t ci = 0;; ++ci) {
-        store(cur);
-        const bool more = ci + 1 < n_chunks;
-        Meta nxt2 = nxt;
-        if (ci + 2 < n_chunks) nxt2 = meta_of(cur.cs + 2 * kChunk);
-        if (more && nxt.tiled) issue_data(nxt);
+    // Combine the nrec records of sequence ms (waves jf .. jf+nrec-1) into its
+    // output rows.  All loads of a pass are independent, so each pass costs
+    // about one memory round trip: per-head (max, sum) with lanes over
+    // records, then the outputs with lanes over head dimensions.
+    auto merge = [&](uint32_t ms, uint32_t jf, uint32_t nrec) __attribute__((always_inline)) {
+        const uint64_t row_sh = static_cast<uint64_t>(ms) * a.num_heads;
+        const uint64_t ml0 = (static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf) * G;   // record 0, head 0
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            float M = -INFINITY, L = 0.0f;
+            if (static_cast<uint32_t>(hh) < nh) {
+                for (uint32_t ib = 0; ib < nrec; ib += kWave) {
+                    const uint32_t i = ib + lane;
+                    const bool ok = i < nrec;
+                    const uint64_t slot = ml0 + static_cast<uint64_t>(ok ? i : 0) * G + hh;
+                    const float mi = ok ? coherent_load(a.part_ml + 2 * slot) : -INFINITY;
+                    const float li = ok ? coherent_load(a.part_ml + 2 * slot + 1) : 0.0f;
+                    const float bm = wave_max(mi);
+                    const float nm = fmaxf(M, bm);
+                    L = L * exp2f(M - nm) + wave_sum(ok ? exp2f(mi - nm) * li : 0.0f);
+                    M = nm;
+                }
+            }
+            if (lane == 0) { sMerge[2 * hh] = M; sMerge[2 * hh + 1] = L; }
+        }
         __syncthreads();
-        process(cur.nv);
-        if (!more) break;
-        __syncthreads();
-        cur = nxt;
-        nxt = nxt2;
-    }
+        float* const sW = reinterpret_cast<float*>(sK);          // chunk data are no longer needed
+        constexpr uint32_t kWCap = NU * 4 * kWave / G;           // records per LDS batch
+        constexpr int ITEMS = (G * HS4P + kWave - 1) / kWave;    // (head, word) items per lane
+        float4 o[ITEMS];
+#pragma unroll
+        for (int u = 0; u < ITEMS; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (uint32_t ib = 0; ib < nrec; ib += kWCap) {
+            const uint32_t nb = min(kWCap, nrec - ib);
+            for (uint32_t t = lane; t < nb * G; t += kWave) {
+                const uint32_t i = t / G, hh = t % G;
+                float w = 0.0f;
+                if (hh < nh)
+                    w = exp2f(coherent_load(a.part_ml + 2 * (ml0 + static_cast<uint64_t>(ib + i) * G + hh)) -
+                              sMerge[2 * hh]) / sMerge[2 * hh + 1];
+                sW[t] = w;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < ITEMS; ++u) {
+                const uint32_t p = lane + kWave * u;
+                const uint32_t hh = p / hs4, word = p % hs4;
+                if (hh >= nh) continue;
+                for (uint32_t i0 = 0; i0 < nb; i0 += 8) {
+                    float4 v[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const bool ok = i0 + k < nb;
+                        const float* pa_ = a.part_acc + (ml0 + static_cast<uint64_t>(ib + (ok ? i0 + k : 0)) * G + hh) * hs + 4 * word;
+                        v[k] = ok ? make_float4(coherent_load(pa_), coherent_load(pa_ + 1), coherent_load(pa_ + 2),
+                                                coherent_load(pa_ + 3))
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float w = i0 + k < nb ? sW[(i0 + k) * G + hh] : 0.0f;
+                        o[u].x += w * v[k].x; o[u].y += w * v[k].y; o[u].z += w * v[k].z; o[u].w += w * v[k].w;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int u = 0; u < ITEMS; ++u) {
+            const uint32_t p = lane + kWave * u;
+            const uint32_t hh = p / hs4, word = p % hs4;
+            if (hh < nh) *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) = o[u];
+        }
+    };
 
-    // ---- write: lane (r, g) holds dims 4*NCW*r + 4*cw + j of head 4*hset + g ----
-    const uint64_t row_sh = static_cast<uint64_t>(s) * a.num_heads;
+    uint32_t npend = 0, pend_s0 = 0, pend_jf0 = 0, pend_n0 = 0, pend_s1 = 0, pend_jf1 = 0, pend_n1 = 0;
+
+    // ---- end of a sequence's share: final output or a partial record ----
+    // Lane (r, g) holds dims 4*NCW*r + 4*cw + j of head 4*hset + g.  Record id
+    // j + s is unique within the row group: a wave's sequences increase, and a
+    // later wave starts at or after the sequence where the previous one ended.
+    // The last of the sequence's waves to arrive (a counter per (row group,
+    // sequence), which it sets back to zero) later combines all its records.
+    auto flush = [&](const Meta& m) __attribute__((always_inline)) {
+        const uint32_t nrec = meta_nrec(m);
+        const uint64_t row_sh = static_cast<uint64_t>(m.s) * a.num_heads;
+        const uint64_t rec0 = static_cast<uint64_t>(rg) * c.recs_per_rg + m.s;    // record of wave jj: rec0 + jj
 #pragma unroll
-    for (int hset = 0; hset < NHS; ++hset) {
-        const uint32_t hh = 4 * hset + g;
-        if (hh >= nh) continue;
-        const uint64_t h = row_sh + h0 + hh;
+        for (int hset = 0; hset < NHS; ++hset) {
+            const uint32_t hh = 4 * hset + g;
+            if (hh >= nh) continue;
 #pragma unroll
-        for (int cw = 0; cw < NCW; ++cw) {
-            const uint32_t word = NCW * r + cw;
-            if (word >= hs4) continue;
-            float4 v = make_float4(acc[hset][cw][0], acc[hset][cw][1], acc[hset][cw][2], acc[hset][cw][3]);
-            if (n_split_s == 1) {
-                const float inv = 1.0f / l_run[hset];
-                v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
-                *reinterpret_cast<float4*>(a.out + h * hs + 4 * word) = v;
-            } else {
-                const uint64_t rec = h * c.num_splits + split;
-                *reinterpret_cast<float4*>(a.part_acc + rec * hs + 4 * word) = v;
-                if (word == 0) {
-                    a.part_ml[2 * rec] = m_run[hset];
-                    a.part_ml[2 * rec + 1] = l_run[hset];
+            for (int cw = 0; cw < NCW; ++cw) {
+                const uint32_t word = NCW * r + cw;
+                if (word >= hs4) continue;
+                float4 v = make_float4(acc[hset][cw][0], acc[hset][cw][1], acc[hset][cw][2], acc[hset][cw][3]);
+                if (nrec == 1) {
+                    const float inv = 1.0f / l_run[hset];
+                    v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
+                    *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) = v;
+                } else {
+                    const uint64_t slot = (rec0 + j) * G + hh;
+                    float* pa_ = a.part_acc + slot * hs + 4 * word;
+                    coherent_store(pa_, v.x);
+                    coherent_store(pa_ + 1, v.y);
+                    coherent_store(pa_ + 2, v.z);
+                    coherent_store(pa_ + 3, v.w);
+                    if (word == 0) {
+                        coherent_store(a.part_ml + 2 * slot, m_run[hset]);
+                        coherent_store(a.part_ml + 2 * slot + 1, l_run[hset]);
+                    }
                 }
             }
         }
-    }
-}
+        reset();
+        if (nrec == 1) return;
+        // The record was written with device-coherent stores; once they have
+        // completed, count this wave in.  No cache maintenance is needed (a
+        // device-scope fence would write back and invalidate the whole L2).
+        __builtin_amdgcn_s_waitcnt(0);
+        uint32_t prev = 0;
+        if (lane == 0)
+            prev = __hip_atomic_fetch_add(a.counters + static_cast<uint64_t>(rg) * a.num_seqs + m.s, 1u,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = uniform(prev);
+        if (prev != nrec - 1) return;
+        // Last arrival: reset the counter for the next call; the records are
+        // combined after the main loop, when the tile registers are free.  A
+        // sequence shared with other waves extends past one end of this
+        // wave's range, so there are at most two such sequences per wave.
+        if (lane == 0)
+            __hip_atomic_store(a.counters + static_cast<uint64_t>(rg) * a.num_seqs + m.s, 0u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (npend == 0) { pend_s0 = m.s; pend_jf0 = m.jf; pend_n0 = nrec; }
+        else { pend_s1 = m.s; pend_jf1 = m.jf; pend_n1 = nrec; }
+        ++npend;
+    };
 
-// One wavefront per (seq, head): combine the split partials of rows with more
-// than one split, write zero rows for empty position sets.
-template <bool VIS>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, uint32_t split_tokens, uint32_t num_splits) {
-    const uint32_t lane = threadIdx.x;
-    const uint32_t s = blockIdx.x / a.num_heads;
-    const uint64_t h = blockIdx.x;   // s * num_heads + head
-    const uint32_t n_pos = positions_of<VIS>(a, s);
-    const uint32_t ns = (n_pos + split_tokens - 1) / split_tokens;
-    if (ns == 1) return;
-    const uint32_t hs = a.head_size;
-    float* o = a.out + h * hs;
-    if (ns == 0) {
-        for (uint32_t d = lane; d < hs; d += kWave) o[d] = 0.0f;
-        return;
-    }
-    const float* ml = a.part_ml + 2 * h * num_splits;
-    float M = -INFINITY;
-    for (uint32_t i = 0; i < ns; ++i) M = fmaxf(M, ml[2 * i]);
-    float L = 0.0f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const bool act = 4 * lane < hs;
-    for (uint32_t i = 0; i < ns; ++i) {
-        const float w = exp2f(ml[2 * i] - M);
-        L += w * ml[2 * i + 1];
-        if (act) {
-            const float4 v = *reinterpret_cast<const float4*>(a.part_acc + (h * num_splits + i) * hs + 4 * lane);
-            acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+    // ---- pipeline over the wave's chunks x0 .. x1-1 ----
+    // Step for chunk x (relative index xr): its data sit in registers `kb/vb`;
+    // the next DEPTH-1 chunks are in flight in the other buffer.  The step
+    // stores chunk x to LDS, reads the block ids of chunk x+DEPTH+1, reuses the
+    // registers for chunk x+DEPTH, and processes chunk x.
+    reset();
+    // Prologue order: block ids of chunk x0, q of its sequence, chunk x0's
+    // tiles, block ids of x0+1; the q digits are formed while tiles arrive.
+    Buf bA;
+    Meta mc = meta_of(true);
+    q_issue(mc.s);
+    issue_data(mc, bA);
+    Meta mn1;
+    if (n > 1) advance();
+    mn1 = meta_of(n > 1);
+    q_finish();
+    uint32_t q_seq = mc.s;
+    if (DEPTH == 1) {
+        for (uint32_t xr = 0;; ++xr) {
+            if (mc.s != q_seq) { load_q(mc.s); q_seq = mc.s; }
+            store(mc, bA);
+            if (xr + 2 < n) advance();
+            const Meta mn2 = meta_of(xr + 2 < n);
+            issue_data(mn1, bA);
+            __syncthreads();
+            process(meta_nv(mc));
+            if (xr + 1 == n || mn1.s != mc.s) flush(mc);
+            if (xr + 1 == n) break;
+            __syncthreads();
+            mc = mn1;
+            mn1 = mn2;
+        }
+    } else {
+        Buf bB;
+        issue_data(mn1, bB);
+        if (n > 2) advance();
+        Meta mn2 = meta_of(n > 2);
+        auto step = [&](uint32_t xr, Buf& b) __attribute__((always_inline)) -> bool {
+            if (mc.s != q_seq) { load_q(mc.s); q_seq = mc.s; }
+            store(mc, b);
+            if (xr + 3 < n) advance();
+            const Meta mn3 = meta_of(xr + 3 < n);
+            issue_data(mn2, b);
+            __syncthreads();
+            process(meta_nv(mc));
+            if (xr + 1 == n || mn1.s != mc.s) flush(mc);
+            if (xr + 1 == n) return false;
+            __syncthreads();
+            mc = mn1;
+            mn1 = mn2;
+            mn2 = mn3;
+            return true;
+        };
+        for (uint32_t xr = 0;; xr += 2) {
+            if (!step(xr, bA)) break;
+            if (!step(xr + 1, bB)) break;
         }
     }
-    if (act) {
-        const float inv = 1.0f / L;
-        *reinterpret_cast<float4*>(o + 4 * lane) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
+    if (npend > 0) merge(pend_s0, pend_jf0, pend_n0);
+    if (npend > 1) merge(pend_s1, pend_jf1, pend_n1);
+    if (j == W - 1) zero_rows(a, lane, mc.s + 1, a.num_seqs, h0, nh);
 }
 
 template <int HS4P, bool EXACT, int NHS>
-hipError_t launch_split_t(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st, bool vis) {
+hipError_t launch_split_t(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
+                          bool vis, bool tiled) {
     if (vis)
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, true>), grid, dim3(64), 0, st, a, c, nbm1);
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, true, false>), grid, dim3(64), 0, st, a, c, nbm1);
+    else if (EXACT && tiled)
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, false, EXACT>), grid, dim3(64), 0, st, a, c, nbm1);
     else
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, false>), grid, dim3(64), 0, st, a, c, nbm1);
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, false, false>), grid, dim3(64), 0, st, a, c, nbm1);
     return hipGetLastError();
 }
 
 template <int HS4P, bool EXACT>
-hipError_t launch_split_g(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st, bool vis) {
-    if (c.group == 8) return launch_split_t<HS4P, EXACT, 2>(a, c, nbm1, grid, st, vis);
-    return launch_split_t<HS4P, EXACT, 1>(a, c, nbm1, grid, st, vis);
+hipError_t launch_split_g(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
+                          bool vis, bool tiled) {
+    if (c.group == 8) return launch_split_t<HS4P, EXACT, 2>(a, c, nbm1, grid, st, vis, tiled);
+    return launch_split_t<HS4P, EXACT, 1>(a, c, nbm1, grid, st, vis, tiled);
 }
 
 }  // namespace
@@ -550,25 +885,27 @@ DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_he
     p.group = n_rep > 4 ? 8 : 4;
     p.num_groups = (n_rep + p.group - 1) / p.group;
     (void)block_size;
-    // Aim for about 16 work items per compute unit when every row is at the
-    // longest length, with splits of 256..1024 positions (multiples of 64).
-    const uint64_t units = static_cast<uint64_t>(num_seqs) * num_kv_heads * p.num_groups;
-    const uint64_t target_items = 256ull * 16;
-    uint64_t per = units ? (static_cast<uint64_t>(max_positions) * units + target_items - 1) / target_items : max_positions;
-    per = (per + kChunk - 1) / kChunk * kChunk;
-    if (per < 256) per = 256;
-    if (per > 1024) per = 1024;
-    if (const char* e = getenv("Q8KV_SPLIT_TOKENS")) {
+    // Persistent wavefronts: 4 per compute unit of an MI355X (256 CUs),
+    // shared evenly by the row groups.
+    uint64_t target = kDecodeWaves;
+    if (const char* e = getenv("Q8KV_DECODE_WAVES")) {
         const long v = atol(e);
-        if (v >= kChunk) per = static_cast<uint64_t>(v) / kChunk * kChunk;
+        if (v >= 1 && v <= (1L << 20)) target = static_cast<uint64_t>(v);
     }
-    if (per > kMaxSplit) per = kMaxSplit;
-    p.split_tokens = static_cast<uint32_t>(per);
-    p.num_splits = max_positions ? (max_positions + p.split_tokens - 1) / p.split_tokens : 0;
-    const uint64_t recs = static_cast<uint64_t>(num_seqs) * num_heads * p.num_splits;
-    p.acc_offset = 0;
-    p.ml_offset = (recs * head_size * sizeof(float) + 255) / 256 * 256;
-    p.bytes = p.num_splits > 1 ? p.ml_offset + recs * 2 * sizeof(float) : 0;
+    const uint64_t num_rg = static_cast<uint64_t>(num_kv_heads) * p.num_groups;
+    uint64_t per = num_rg ? target / num_rg : 1;
+    if (per < 1) per = 1;
+    p.waves_per_rg = static_cast<uint32_t>(per);
+    p.num_waves = num_rg * per;
+    p.recs_per_rg = p.waves_per_rg + (num_seqs ? num_seqs - 1 : 0);
+    // Workspace: one arrival counter per (row group, sequence), then the
+    // partial records.  A sequence of at most one chunk always lies in a
+    // single wave's range, so then no workspace is needed at all.
+    const uint64_t slots = num_rg * p.recs_per_rg * p.group;
+    p.counters_offset = 0;
+    p.acc_offset = (num_rg * num_seqs * sizeof(uint32_t) + 255) / 256 * 256;
+    p.ml_offset = p.acc_offset + (slots * head_size * sizeof(float) + 255) / 256 * 256;
+    p.bytes = max_positions > static_cast<uint32_t>(kChunk) ? p.ml_offset + slots * 2 * sizeof(float) : 0;
     return p;
 }
 
@@ -577,10 +914,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
     const uint32_t hs4 = a.head_size / 4;
     const uint32_t wpt = hs4 + 1;
     SplitConsts c{};
-    c.split_tokens = p.split_tokens;
-    c.num_splits = p.num_splits;
+    c.waves_per_rg = p.waves_per_rg;
+    c.num_rg = a.num_kv_heads * p.num_groups;
     c.group = p.group;
     c.num_groups = p.num_groups;
+    c.recs_per_rg = p.recs_per_rg;
     c.seg_rows = a.block_size < static_cast<uint32_t>(kChunk) ? a.block_size : kChunk;
     const bool shape_ok = a.block_size % 4 == 0 &&
                           (kChunk % a.block_size == 0 || a.block_size % kChunk == 0);
@@ -590,27 +928,23 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
     c.seg_u4 = c.seg_rows * wpt / 4;
     if (c.seg_u4 == 0) c.seg_u4 = 1;
     c.seg_magic = static_cast<uint32_t>((0x100000000ull + c.seg_u4 - 1) / c.seg_u4);
-    const uint32_t nbm1 = a.num_blocks - 1;
-    if (p.num_splits > 0) {
-        const uint64_t items = static_cast<uint64_t>(a.num_seqs) * a.num_kv_heads * p.num_groups * p.num_splits;
-        const dim3 grid(static_cast<uint32_t>(items));
+    // With no block table or no blocks every sequence attends nothing
+    // (positions are capped by the table); the kernel then only writes zeros.
+    const uint32_t nbm1 = a.num_blocks ? a.num_blocks - 1 : 0;
+    {
+        const dim3 grid(static_cast<uint32_t>(p.num_waves));
         hipError_t err;
-        if (hs4 == 16) err = launch_split_g<16, true>(a, c, nbm1, grid, stream, vis);
-        else if (hs4 == 32) err = launch_split_g<32, true>(a, c, nbm1, grid, stream, vis);
-        else if (hs4 == 48) err = launch_split_g<48, true>(a, c, nbm1, grid, stream, vis);
-        else if (hs4 == 64) err = launch_split_g<64, true>(a, c, nbm1, grid, stream, vis);
-        else if (hs4 < 16) err = launch_split_g<16, false>(a, c, nbm1, grid, stream, vis);
-        else if (hs4 < 32) err = launch_split_g<32, false>(a, c, nbm1, grid, stream, vis);
-        else if (hs4 < 48) err = launch_split_g<48, false>(a, c, nbm1, grid, stream, vis);
-        else err = launch_split_g<64, false>(a, c, nbm1, grid, stream, vis);
+        const bool t = c.tiled_ok != 0;
+        if (hs4 == 16) err = launch_split_g<16, true>(a, c, nbm1, grid, stream, vis, t);
+        else if (hs4 == 32) err = launch_split_g<32, true>(a, c, nbm1, grid, stream, vis, t);
+        else if (hs4 == 48) err = launch_split_g<48, true>(a, c, nbm1, grid, stream, vis, t);
+        else if (hs4 == 64) err = launch_split_g<64, true>(a, c, nbm1, grid, stream, vis, t);
+        else if (hs4 < 16) err = launch_split_g<16, false>(a, c, nbm1, grid, stream, vis, t);
+        else if (hs4 < 32) err = launch_split_g<32, false>(a, c, nbm1, grid, stream, vis, t);
+        else if (hs4 < 48) err = launch_split_g<48, false>(a, c, nbm1, grid, stream, vis, t);
+        else err = launch_split_g<64, false>(a, c, nbm1, grid, stream, vis, t);
         if (err != hipSuccess) return err;
     }
-    const uint32_t st = p.split_tokens ? p.split_tokens : 1;
-    const dim3 mgrid(a.num_seqs * a.num_heads);
-    if (vis)
-        hipLaunchKernelGGL(decode_merge_kernel<true>, mgrid, dim3(64), 0, stream, a, st, p.num_splits);
-    else
-        hipLaunchKernelGGL(decode_merge_kernel<false>, mgrid, dim3(64), 0, stream, a, st, p.num_splits);
     return hipGetLastError();
 }
 

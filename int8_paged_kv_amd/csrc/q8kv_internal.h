@@ -9,7 +9,7 @@ namespace q8kv {
 constexpr uint32_t kPadSlot = 0xFFFFFFFFu;
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kChunk = 64;         // decode positions per chunk
-constexpr uint32_t kMaxSplit = 1024;   // longest context split (positions) of one work item
+constexpr uint32_t kDecodeWaves = 1024;   // persistent decode wavefronts: 4 per CU of an MI355X
 
 struct CacheWriteArgs {
     const float* key;
@@ -23,13 +23,18 @@ struct CacheWriteArgs {
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
 
-// Split plan shared by the workspace query and the decode call.
+// Decode plan shared by the workspace query and the decode call.  For each
+// row group (kv head, group of query heads sharing it) waves_per_rg
+// persistent wavefronts split the batch's 64-position chunks evenly; a
+// sequence covered by more than one wavefront leaves one partial record per
+// wavefront.
 struct DecodePlan {
-    uint32_t split_tokens;   // positions per split, a multiple of kChunk
-    uint32_t num_splits;     // splits of the longest possible position list
     uint32_t group;          // query heads handled together per kv head (4 or 8)
     uint32_t num_groups;     // ceil(n_rep / group)
-    size_t ml_offset, acc_offset, bytes;
+    uint32_t waves_per_rg;   // persistent wavefronts per row group
+    uint32_t recs_per_rg;    // partial record slots per row group: waves_per_rg + num_seqs - 1
+    uint64_t num_waves;      // grid: row groups * waves_per_rg
+    size_t counters_offset, ml_offset, acc_offset, bytes;
 };
 
 DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
@@ -44,8 +49,9 @@ struct DecodeArgs {
     const uint32_t* context_lens;
     const uint32_t* visible_pos;
     const uint32_t* num_visible;
-    float* part_ml;          // [S, H, num_splits, 2]: running max (log2 units), sum
-    float* part_acc;         // [S, H, num_splits, head_size]: unnormalized output
+    uint32_t* counters;      // [row group, seq]: arrivals of a sequence's waves; zero between calls
+    float* part_ml;          // [row group, record, head in group, 2]: running max (log2 units), sum
+    float* part_acc;         // [row group, record, head in group, head_size]: unnormalized output
     uint32_t q_stride, max_num_blocks_per_seq, max_context_len, vis_stride;
     uint32_t num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks;
     float scale_log2;        // softmax scale * log2(e)

@@ -83,15 +83,27 @@ def decode_args(**kw):
     (dict(q_stride=511), 2), (dict(vis=FAKE, nvis=FAKE, vis_stride=0), 2), (dict(max_nb=0), 2),
     (dict(scale=float("nan")), 2), (dict(out=None), 1), (dict(bt=None), 1), (dict(cl=None), 1),
     (dict(vis=FAKE, nvis=None, vis_stride=8), 1), (dict(ws=None), 3), (dict(wsb=16), 3),
-    (dict(ws=ctypes.c_void_p(0x1004)), 3), (dict(S=0), 0),
+    (dict(ws=ctypes.c_void_p(0x1004)), 3), (dict(out=ctypes.c_void_p(0x2004)), 5), (dict(S=0), 0),
 ])
 def test_decode_validation(lib, kw, want):
     assert lib.q8_paged_decode(*decode_args(**kw)) == want
 
 
 def test_workspace_size_matches_plan(lib):
-    # single split: no workspace; long contexts: partials for every (seq, head, split)
+    # At most one 64-position chunk per sequence: every sequence lies in one
+    # wavefront's range, no partials.
     assert lib.q8_paged_decode_workspace_bytes(2, 4, 2, 128, 16, 64) == 0
-    big = lib.q8_paged_decode_workspace_bytes(64, 32, 8, 128, 16, 4096)
-    assert big > 64 * 32 * 2 * 130 * 4
-    assert big % 4 == 0
+    # Otherwise: per row group (kv head, group of 4 or 8 query heads),
+    # (waves per group + S - 1) records of (head_size + 2) floats per head.
+    # Layout: arrival counters (one u32 per row group and sequence), then the
+    # records' outputs, then their (max, sum) pairs, each 256-byte aligned.
+    def want(S, hs, rg, group):
+        recs = 1024 // rg + S - 1
+        slots = rg * recs * group
+        r256 = lambda b: (b + 255) // 256 * 256
+        return r256(rg * S * 4) + r256(slots * hs * 4) + slots * 2 * 4
+    assert lib.q8_paged_decode_workspace_bytes(64, 32, 8, 128, 16, 4096) == want(64, 128, 8, 4)
+    # n_rep 8 uses groups of 8 query heads
+    assert lib.q8_paged_decode_workspace_bytes(8, 64, 8, 128, 32, 32768) == want(8, 128, 8, 8)
+    # n_rep 16: two groups of 8 per kv head
+    assert lib.q8_paged_decode_workspace_bytes(2, 32, 2, 64, 16, 500) == want(2, 64, 4, 8)

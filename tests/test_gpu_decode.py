@@ -14,12 +14,13 @@ torch = pytest.importorskip("torch")
 
 
 @pytest.fixture
-def split_tokens():
-    """Force the planner's split length (positions per split) for one test."""
+def decode_waves():
+    """Force the planner's persistent wavefront count for one test, which moves
+    every boundary between wavefronts' chunk ranges."""
     def set_(n):
-        os.environ["Q8KV_SPLIT_TOKENS"] = str(n)
+        os.environ["Q8KV_DECODE_WAVES"] = str(n)
     yield set_
-    os.environ.pop("Q8KV_SPLIT_TOKENS", None)
+    os.environ.pop("Q8KV_DECODE_WAVES", None)
 
 
 def test_tiny_workload(oracle_mod):
@@ -30,6 +31,7 @@ def test_tiny_workload(oracle_mod):
 
 @pytest.mark.parametrize("S,H,Hkv,hs,bs,lens", [
     (3, 4, 2, 64, 16, [0, 1, 17]),              # empty, one token, partial block
+    (2, 4, 2, 64, 16, [0, 0]),                  # nothing to attend anywhere: zero rows
     (2, 8, 8, 128, 16, [100, 33]),              # MHA (n_rep 1)
     (2, 4, 2, 128, 16, [300, 64]),              # n_rep 2
     (2, 6, 2, 128, 16, [129, 70]),              # n_rep 3
@@ -52,13 +54,16 @@ def test_shapes_and_paths(oracle_mod, S, H, Hkv, hs, bs, lens):
     assert_close(c.gpu(), c.oracle(oracle_mod), "shape %s" % ((S, H, Hkv, hs, bs, lens),))
 
 
-@pytest.mark.parametrize("split", [64, 128, 256, 1024])
-def test_split_boundaries(oracle_mod, split_tokens, split):
+@pytest.mark.parametrize("waves", [1, 7, 64, 333, 4096])
+def test_wavefront_range_boundaries(oracle_mod, decode_waves, waves):
+    """Chunk ranges of the persistent wavefronts: one wave for everything,
+    waves spanning several sequences (and empty ones), sequences split over
+    many waves, and one chunk per wave."""
     from gpu_util import RandomCase, assert_close
-    lens = [63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 2049]
-    split_tokens(split)
-    c = RandomCase(oracle_mod, 5 + split, len(lens), 8, 2, 128, 16, lens, outliers=True)
-    assert_close(c.gpu(), c.oracle(oracle_mod), "split %d" % split)
+    lens = [0, 63, 64, 65, 255, 256, 257, 0, 1023, 1024, 1025, 2049, 1]
+    decode_waves(waves)
+    c = RandomCase(oracle_mod, 5 + waves, len(lens), 8, 2, 128, 16, lens, outliers=True)
+    assert_close(c.gpu(), c.oracle(oracle_mod), "waves %d" % waves)
 
 
 def test_context_clamp_and_q_stride(oracle_mod):
@@ -79,7 +84,7 @@ def test_one_token_returns_dequantized_v_exactly(oracle_mod):
 
 
 @pytest.mark.parametrize("kind", ["dense_list", "aligned_runs", "gaps", "empty_and_single"])
-def test_visible_lists(oracle_mod, kind, split_tokens):
+def test_visible_lists(oracle_mod, kind, decode_waves):
     from gpu_util import RandomCase, assert_close
     lens = [3000, 1500, 777]
     c = RandomCase(oracle_mod, 31, 3, 8, 2, 128, 16, lens)
@@ -101,7 +106,7 @@ def test_visible_lists(oracle_mod, kind, split_tokens):
         vis[s, :p.size] = p
         nvis[s] = p.size
     if kind == "gaps":
-        split_tokens(128)
+        decode_waves(37)
     got = c.gpu(vis=vis, nvis=nvis)
     assert_close(got, c.oracle(oracle_mod, vis=vis, nvis=nvis), kind)
     if kind == "dense_list":
@@ -131,6 +136,25 @@ def test_gqa_equals_duplicated_mha(oracle_mod):
     c.Hkv = 8
     b = c.gpu()
     assert np.all(np.abs(a - b) <= 1e-6 + 1e-6 * np.abs(a))
+
+
+def test_workspace_reuse_leaves_counters_zero(oracle_mod, decode_waves):
+    """One zero-filled workspace serves several calls of different shapes:
+    every call is correct and leaves the arrival counters at zero."""
+    from int8_paged_kv_amd import q8_paged_decode_workspace_bytes
+    from gpu_util import RandomCase, assert_close
+    decode_waves(96)
+    cases = [RandomCase(oracle_mod, 71, 5, 8, 2, 128, 16, [900, 65, 0, 2000, 300]),
+             RandomCase(oracle_mod, 72, 3, 16, 2, 64, 16, [1500, 10, 700]),
+             RandomCase(oracle_mod, 73, 5, 8, 2, 128, 16, [130, 1200, 64, 640, 3])]
+    need = max(q8_paged_decode_workspace_bytes(c.S, c.H, c.Hkv, c.hs, c.bs, int(c.lens.max())) for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    for i, c in enumerate(cases * 2):
+        assert_close(c.gpu(workspace=ws), c.oracle(oracle_mod), "reuse %d" % i)
+        n_rep = c.H // c.Hkv
+        groups = -(-n_rep // (8 if n_rep > 4 else 4))
+        counters = ws[:c.Hkv * groups * c.S * 4].cpu().numpy()
+        assert not counters.any(), "arrival counters not left at zero"
 
 
 def test_workspace_too_small_is_rejected(oracle_mod):
