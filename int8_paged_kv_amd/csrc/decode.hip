@@ -120,6 +120,15 @@ __device__ __forceinline__ int exponent_bound(float x) {
     return e;
 }
 
+// LDS hand-off between the lanes of one wavefront: LDS operations of a
+// wavefront execute in order, so only compiler reordering must be prevented
+// (the wavefronts of a workgroup never wait for each other).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
 }
@@ -134,27 +143,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t lane) {
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
-
 __device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) {
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), static_cast<int>(l)));
 }
 
 // Chunks of K/V loaded ahead of use by the split kernel (1 or 2; 2 needs
-// about 66 more VGPRs at head_size 128).
+// about 66 more VGPRs at head_size 128, so one wavefront per SIMD).
 #ifndef Q8KV_DECODE_DEPTH
 #define Q8KV_DECODE_DEPTH 1
 #endif
 constexpr int kPrefetchDepth = Q8KV_DECODE_DEPTH;
+// Independent wavefronts packed per workgroup (fewer workgroups to dispatch).
+constexpr uint32_t kWavesPerGroup = 4;
 
 struct SplitConsts {
     uint32_t waves_per_rg;  // persistent wavefronts per row group (before capping by the chunk count)
@@ -165,6 +165,7 @@ struct SplitConsts {
     uint32_t seg_magic;     // ceil(2^32 / seg_u4): u / seg_u4 == mulhi(u, magic) for u < 2^16
     uint32_t seg_rows;      // rows per segment = min(block_size, 64)
     uint32_t tiled_ok;      // segment copies are legal (alignment, block_size shape)
+    uint32_t q_vec_ok;      // q rows of every sequence are 16-byte aligned
 };
 
 // Number of positions sequence s attends.
@@ -274,9 +275,13 @@ __device__ __forceinline__ uint32_t wave_of_chunk(uint32_t x, uint32_t C, uint32
 // HS4P: code words per row rounded up to 16, 32, 48 or 64; EXACT: head_size /
 // 4 == HS4P; NHS: sets of 4 query heads per wavefront (1 or 2); VIS: visible
 // list positions; TILED: every chunk is known to be a tile run (dense
-// positions, aligned caches, block_size dividing or a multiple of 64).
-template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED>
-__global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
+// positions, aligned caches, block_size dividing or a multiple of 64); SEGR:
+// when nonzero (16 or 32, with EXACT), the rows per tile segment, for which
+// each segment of a chunk fills whole 64-lane slots (SEGR*HS4P/256 of them)
+// plus SEGR/4 trailing 16-byte units: every full slot then loads from one
+// segment with a scalar base address and a fixed per-lane offset.
+template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED, int SEGR>
+__global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDepth == 1) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
     constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
     constexpr int NCW = HS4P / 16;             // V code words per lane and row
     constexpr int G = 4 * NHS;
@@ -286,23 +291,37 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
     // An exact head size makes a chunk 64*(HS4P+1) words: HS4P/4 full 16-byte
     // slots per lane plus one 4-byte tail slot per lane.
     constexpr int NF = EXACT ? HS4P / 4 : NU;
+    constexpr bool FAST = SEGR > 0;
+    static_assert(!FAST || (EXACT && (SEGR * HS4P) % 256 == 0 && SEGR <= kChunk), "segment layout");
+    constexpr int FSEG = FAST ? kChunk / SEGR : 1;          // segments per chunk
+    constexpr int FS = FAST ? SEGR * HS4P / 256 : 0;         // full slots per segment (FSEG * FS == NF)
+    constexpr int FLO = FAST ? SEGR / 4 : 1;                 // trailing 16-byte units per segment
+    constexpr int SEG_U4 = FAST ? SEGR * (HS4P + 1) / 4 : 1; // 16-byte units per segment
     struct Buf {
         u32x4 k[NF], v[NF];
-        uint32_t kt, vt;
+        uint32_t kt, vt;        // EXACT generic layout: one 4-byte tail slot per lane
+        u32x4 k4, v4;           // FAST layout: the segments' trailing units (lanes 0-15)
     };
     constexpr int DEPTH = (HS4P <= 32 && NHS == 1) ? kPrefetchDepth : 1;  // chunks loaded ahead
 
-    __shared__ __align__(16) uint32_t sK[NU * 4 * kWave];   // also stages q rows at sequence changes
-    __shared__ __align__(16) uint32_t sV[NU * 4 * kWave];
-    __shared__ __align__(16) uint32_t sA[NHS * 16 * 16];   // [set][head*4+digit][w]: weight digits, 4 tokens a word
-    __shared__ int sEq[G];
-    __shared__ float sMerge[2 * G];                           // per-head (max, sum) while combining records
+    // Per-wavefront LDS regions: the wavefronts of a workgroup are independent.
+    __shared__ __align__(16) uint32_t sK_[kWavesPerGroup][NU * 4 * kWave];   // also stages q rows at sequence changes
+    __shared__ __align__(16) uint32_t sV_[kWavesPerGroup][NU * 4 * kWave];
+    __shared__ __align__(16) uint32_t sA_[kWavesPerGroup][NHS * 16 * 16];    // [set][head*4+digit][w]: weight digits
+    __shared__ int sEq_[kWavesPerGroup][G];
+    const uint32_t wid = uniform(threadIdx.x / kWave);
+    uint32_t* const sK = sK_[wid];
+    uint32_t* const sV = sV_[wid];
+    uint32_t* const sA = sA_[wid];
+    int* const sEq = sEq_[wid];
     float* const sQ = reinterpret_cast<float*>(sK);
 
-    const uint32_t lane = threadIdx.x;
+    const uint32_t lane = threadIdx.x % kWave;
     const uint32_t r = lane & 15, g = lane >> 4;
-    const uint32_t rg = blockIdx.x % c.num_rg;
-    const uint32_t j = blockIdx.x / c.num_rg;
+    const uint32_t gw = blockIdx.x * kWavesPerGroup + wid;      // persistent wavefront index
+    if (gw >= c.num_rg * c.waves_per_rg) return;
+    const uint32_t rg = gw % c.num_rg;
+    const uint32_t j = gw / c.num_rg;
     const uint32_t kvh = rg % a.num_kv_heads;
     const uint32_t grp = rg / a.num_kv_heads;
 
@@ -366,7 +385,9 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
             cur.ci = 0;
             while (true) {
                 ++cur.s;
-                cur.npos = cur.s < a.num_seqs ? uniform(positions_of<VIS>(a, cur.s)) : static_cast<uint32_t>(kChunk);
+                cur.npos = cur.s >= a.num_seqs ? static_cast<uint32_t>(kChunk)
+                           : one_window ? lane_value(win_np, cur.s)
+                                        : uniform(positions_of<VIS>(a, cur.s));
                 if (cur.npos != 0) break;
                 zero_rows(a, lane, cur.s, cur.s + 1, h0, nh);
             }
@@ -410,9 +431,43 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
     };
 
     // ---- tiled chunk loads: 16-byte slot u = lane + 64*i lies in segment u / seg_u4 ----
-    // Slots outside the chunk's valid segments read the first line of this kv
-    // head's tile of block 0 instead (always in bounds, one cached line).
     auto issue_data = [&](const Meta& m, Buf& b) __attribute__((always_inline)) {
+        if (FAST) {
+            // Segment k's tile (block id from lane k) starts at a uniform
+            // address; an invalid segment reads the cache's first bytes.
+            const bool ok = meta_tiled(m);
+            const uint32_t nv = meta_nv(m);
+            const char* kb[FSEG];
+            const char* vb[FSEG];
+#pragma unroll
+            for (int k = 0; k < FSEG; ++k) {
+                uint32_t ph = lane_value(m.id, k);
+                ph = ph < num_blocks_m1 ? ph : num_blocks_m1;
+                const bool valid = ok && static_cast<uint32_t>(k * SEGR) < nv;
+                const uint64_t off = valid ? static_cast<uint64_t>(ph) * kv_stride + kvh_off : 0;
+                kb[k] = reinterpret_cast<const char*>(a.key_cache + off);
+                vb[k] = reinterpret_cast<const char*>(a.value_cache + off);
+            }
+            const uint32_t lb = lane * 16;
+#pragma unroll
+            for (int k = 0; k < FSEG; ++k)
+#pragma unroll
+                for (int f = 0; f < FS; ++f) {
+                    b.k[k * FS + f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb[k] + lb + f * 1024));
+                    b.v[k * FS + f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb[k] + lb + f * 1024));
+                }
+            // Trailing units: lane l < 16 takes unit l % FLO of segment l / FLO.
+            const uint32_t kk = lane / FLO;
+            const char* pk = reinterpret_cast<const char*>(a.key_cache);
+            const char* pv = reinterpret_cast<const char*>(a.value_cache);
+#pragma unroll
+            for (int k = 0; k < FSEG; ++k)
+                if (kk == static_cast<uint32_t>(k)) { pk = kb[k]; pv = vb[k]; }
+            const uint32_t tb = (lane < 16u) ? (FS * 64 + lane % FLO) * 16 : lb;
+            b.k4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pk + tb));
+            b.v4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pv + tb));
+            return;
+        }
         if (!TILED && !c.tiled_ok) return;     // no tile loads at all (caches not 16-byte aligned, odd block_size)
         const uint32_t row0 = m.p0 % a.block_size;     // nonzero only when block_size > 64
         const bool ok = meta_tiled(m);
@@ -422,30 +477,58 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
         // keeping it live across the loop.
         uint32_t ln = lane;
         asm volatile("" : "+v"(ln));
+        // All block-id exchanges first (one LDS round trip), then the loads.
+        // An invalid slot's word offset is masked to 0, so it reads the
+        // cache's first line: branch-free, in bounds, and one cached line.
+        constexpr int NS = NF + (EXACT ? 1 : 0);
+        uint32_t kseg[NS], phys[NS];
 #pragma unroll
-        for (int i = 0; i < NF; ++i) {
-            const uint32_t u = ln + kWave * i;
-            const uint32_t k = __umulhi(u, c.seg_magic);
-            uint32_t phys = __shfl(m.id, static_cast<int>(min(k, nseg - 1)), 64);
-            phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
-            const bool valid = ok && (EXACT || u < chunk_u4) && (k * c.seg_rows < nv);
-            const uint64_t w = valid ? phys * kv_stride + base + (u - k * c.seg_u4) * 4 : kvh_off;
-            b.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.key_cache + w));
-            b.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.value_cache + w));
+        for (int i = 0; i < NS; ++i) {
+            const uint32_t u = (i < NF) ? ln + kWave * i : (4 * kWave * NF + ln) >> 2;
+            kseg[i] = __umulhi(u, c.seg_magic);
+            phys[i] = __shfl(m.id, static_cast<int>(min(kseg[i], nseg - 1)), 64);
         }
-        if (EXACT) {
-            const uint32_t wi = 4 * kWave * NF + ln;
-            const uint32_t k = __umulhi(wi >> 2, c.seg_magic);
-            uint32_t phys = __shfl(m.id, static_cast<int>(min(k, nseg - 1)), 64);
-            phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
-            const bool valid = ok && (k * c.seg_rows < nv);
-            const uint64_t w = valid ? phys * kv_stride + base + (wi - 4 * k * c.seg_u4) : kvh_off;
-            b.kt = __builtin_nontemporal_load(a.key_cache + w);
-            b.vt = __builtin_nontemporal_load(a.value_cache + w);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const uint32_t k = kseg[i];
+            const uint32_t ph = phys[i] < num_blocks_m1 ? phys[i] : num_blocks_m1;
+            uint64_t w;
+            bool valid;
+            if (i < NF) {
+                const uint32_t u = ln + kWave * i;
+                valid = ok && (EXACT || u < chunk_u4) && (k * c.seg_rows < nv);
+                w = ph * kv_stride + base + (u - k * c.seg_u4) * 4;
+            } else {
+                const uint32_t wi = 4 * kWave * NF + ln;
+                valid = ok && (k * c.seg_rows < nv);
+                w = ph * kv_stride + base + (wi - 4 * k * c.seg_u4);
+            }
+            w &= 0ull - static_cast<uint64_t>(valid);
+            if (i < NF) {
+                b.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.key_cache + w));
+                b.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.value_cache + w));
+            } else {
+                b.kt = __builtin_nontemporal_load(a.key_cache + w);
+                b.vt = __builtin_nontemporal_load(a.value_cache + w);
+            }
         }
     };
     auto store = [&](const Meta& m, const Buf& b) __attribute__((always_inline)) {
-        if (meta_tiled(m)) {
+        if (FAST && meta_tiled(m)) {
+#pragma unroll
+            for (int k = 0; k < FSEG; ++k)
+#pragma unroll
+                for (int f = 0; f < FS; ++f) {
+                    const uint32_t u = k * SEG_U4 + f * 64 + lane;
+                    *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k[k * FS + f];
+                    *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v[k * FS + f];
+                }
+            if (lane < 16u) {
+                const uint32_t u = (lane / FLO) * SEG_U4 + FS * 64 + lane % FLO;
+                *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k4;
+                *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v4;
+            }
+        } else if (meta_tiled(m)) {
 #pragma unroll
             for (int i = 0; i < NF; ++i) {
                 const uint32_t u = lane + kWave * i;
@@ -482,21 +565,32 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
     // ---- q digits of the current sequence: MFMA row r = (head r/4, digit r%4) ----
     i32x4 qa[NHS][NKB];
     int eq_out[NHS];       // q exponent of this lane's output head 4*hset + g
-    constexpr int QV = G * QD / kWave;                        // q values staged per lane
-    float qv[QV];
+    // q rows of the query heads h0 .. h0+nh-1 (padded to G heads of QD
+    // values) staged per lane as QF 16-byte slots: lane l, slot t holds padded
+    // elements 4*(l + 64*t) .. +3.
+    constexpr int QF = G * QD / (4 * kWave);
+    float4 qv[QF];
     auto q_issue = [&](uint32_t s) __attribute__((always_inline)) {
+        const uint64_t row = static_cast<uint64_t>(s) * a.q_stride;
 #pragma unroll
-        for (int t = 0; t < QV; ++t) {
-            const uint32_t i = lane + kWave * t;
-            const uint32_t hi = i / QD, d = i % QD;
-            qv[t] = (hi < nh && d < hs) ? a.q[static_cast<uint64_t>(s) * a.q_stride + static_cast<uint64_t>(h0 + hi) * hs + d]
-                                        : 0.0f;
+        for (int t = 0; t < QF; ++t) {
+            const uint32_t e = 4 * (lane + kWave * t);
+            const uint32_t hi = e / QD, d = e % QD;
+            const bool ok = hi < nh && d < hs;               // d % 4 == 0 and hs % 4 == 0: all four or none
+            const float* src = a.q + (ok ? row + static_cast<uint64_t>(h0 + hi) * hs + d : row);
+            float4 v;
+            if (c.q_vec_ok) {
+                v = *reinterpret_cast<const float4*>(src);
+            } else {
+                v = make_float4(src[0], ok ? src[1] : 0.f, ok ? src[2] : 0.f, ok ? src[3] : 0.f);
+            }
+            qv[t] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     auto q_finish = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < QV; ++t) sQ[lane + kWave * t] = qv[t];
-        __syncthreads();
+        for (int t = 0; t < QF; ++t) *reinterpret_cast<float4*>(&sQ[4 * (lane + kWave * t)]) = qv[t];
+        wave_sync();
 #pragma unroll
         for (int hset = 0; hset < NHS; ++hset) {
             const uint32_t hq = 4 * hset + r / 4, dig = r % 4;
@@ -524,13 +618,9 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
                                      static_cast<int32_t>(packed[2]), static_cast<int32_t>(packed[3])};
             }
         }
-        __syncthreads();
+        wave_sync();
 #pragma unroll
         for (int hset = 0; hset < NHS; ++hset) eq_out[hset] = sEq[4 * hset + g];
-    };
-    auto load_q = [&](uint32_t s) __attribute__((always_inline)) {
-        q_issue(s);
-        q_finish();
     };
 
     // Online-softmax state (log2 units) of head 4*hset + g, uniform across the lane's row.
@@ -620,7 +710,7 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) acc[hset][cw][jj] *= alpha;
         }
-        __syncthreads();
+        wave_sync();
 
         // ---- P . V ----
         i32x4 pa[NHS];
@@ -657,77 +747,47 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
     };
 
     // Combine the nrec records of sequence ms (waves jf .. jf+nrec-1) into its
-    // output rows.  All loads of a pass are independent, so each pass costs
-    // about one memory round trip: per-head (max, sum) with lanes over
-    // records, then the outputs with lanes over head dimensions.
+    // output rows.  Lane items are (head, 4 dims); for each item every
+    // record's (max, sum, 4 dims) is loaded in one batch of independent
+    // loads (8 records at a time), so a typical combine is one memory round
+    // trip.  Running max and rescaling as in the online softmax.
     auto merge = [&](uint32_t ms, uint32_t jf, uint32_t nrec) __attribute__((always_inline)) {
         const uint64_t row_sh = static_cast<uint64_t>(ms) * a.num_heads;
         const uint64_t ml0 = (static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf) * G;   // record 0, head 0
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            float M = -INFINITY, L = 0.0f;
-            if (static_cast<uint32_t>(hh) < nh) {
-                for (uint32_t ib = 0; ib < nrec; ib += kWave) {
-                    const uint32_t i = ib + lane;
-                    const bool ok = i < nrec;
-                    const uint64_t slot = ml0 + static_cast<uint64_t>(ok ? i : 0) * G + hh;
-                    const float mi = ok ? coherent_load(a.part_ml + 2 * slot) : -INFINITY;
-                    const float li = ok ? coherent_load(a.part_ml + 2 * slot + 1) : 0.0f;
-                    const float bm = wave_max(mi);
-                    const float nm = fmaxf(M, bm);
-                    L = L * exp2f(M - nm) + wave_sum(ok ? exp2f(mi - nm) * li : 0.0f);
-                    M = nm;
-                }
-            }
-            if (lane == 0) { sMerge[2 * hh] = M; sMerge[2 * hh + 1] = L; }
-        }
-        __syncthreads();
-        float* const sW = reinterpret_cast<float*>(sK);          // chunk data are no longer needed
-        constexpr uint32_t kWCap = NU * 4 * kWave / G;           // records per LDS batch
-        constexpr int ITEMS = (G * HS4P + kWave - 1) / kWave;    // (head, word) items per lane
-        float4 o[ITEMS];
-#pragma unroll
-        for (int u = 0; u < ITEMS; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (uint32_t ib = 0; ib < nrec; ib += kWCap) {
-            const uint32_t nb = min(kWCap, nrec - ib);
-            for (uint32_t t = lane; t < nb * G; t += kWave) {
-                const uint32_t i = t / G, hh = t % G;
-                float w = 0.0f;
-                if (hh < nh)
-                    w = exp2f(coherent_load(a.part_ml + 2 * (ml0 + static_cast<uint64_t>(ib + i) * G + hh)) -
-                              sMerge[2 * hh]) / sMerge[2 * hh + 1];
-                sW[t] = w;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < ITEMS; ++u) {
-                const uint32_t p = lane + kWave * u;
-                const uint32_t hh = p / hs4, word = p % hs4;
-                if (hh >= nh) continue;
-                for (uint32_t i0 = 0; i0 < nb; i0 += 8) {
-                    float4 v[8];
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const bool ok = i0 + k < nb;
-                        const float* pa_ = a.part_acc + (ml0 + static_cast<uint64_t>(ib + (ok ? i0 + k : 0)) * G + hh) * hs + 4 * word;
-                        v[k] = ok ? make_float4(coherent_load(pa_), coherent_load(pa_ + 1), coherent_load(pa_ + 2),
-                                                coherent_load(pa_ + 3))
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-                    }
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const float w = i0 + k < nb ? sW[(i0 + k) * G + hh] : 0.0f;
-                        o[u].x += w * v[k].x; o[u].y += w * v[k].y; o[u].z += w * v[k].z; o[u].w += w * v[k].w;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-#pragma unroll
-        for (int u = 0; u < ITEMS; ++u) {
-            const uint32_t p = lane + kWave * u;
+        for (uint32_t p = lane; p < nh * hs4; p += kWave) {
             const uint32_t hh = p / hs4, word = p % hs4;
-            if (hh < nh) *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) = o[u];
+            float M = -INFINITY, L = 0.0f;
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (uint32_t i0 = 0; i0 < nrec; i0 += 8) {
+                float mi[8], li[8];
+                float4 vi[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t i = min(i0 + k, nrec - 1);
+                    const uint64_t slot = ml0 + static_cast<uint64_t>(i) * G + hh;
+                    const float* pa_ = a.part_acc + slot * hs + 4 * word;
+                    mi[k] = coherent_load(a.part_ml + 2 * slot);
+                    li[k] = coherent_load(a.part_ml + 2 * slot + 1);
+                    vi[k] = make_float4(coherent_load(pa_), coherent_load(pa_ + 1), coherent_load(pa_ + 2),
+                                        coherent_load(pa_ + 3));
+                }
+                float bm = M;
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (i0 + k < nrec) bm = fmaxf(bm, mi[k]);
+                const float sc = exp2f(M - bm);
+                L *= sc; o.x *= sc; o.y *= sc; o.z *= sc; o.w *= sc;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float w = i0 + k < nrec ? exp2f(mi[k] - bm) : 0.0f;
+                    L += w * li[k];
+                    o.x += w * vi[k].x; o.y += w * vi[k].y; o.z += w * vi[k].z; o.w += w * vi[k].w;
+                }
+                M = bm;
+            }
+            const float inv = 1.0f / L;
+            *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) =
+                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
         }
     };
 
@@ -813,16 +873,17 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
     uint32_t q_seq = mc.s;
     if (DEPTH == 1) {
         for (uint32_t xr = 0;; ++xr) {
-            if (mc.s != q_seq) { load_q(mc.s); q_seq = mc.s; }
+            if (mc.s != q_seq) { q_finish(); q_seq = mc.s; }   // q of mc.s was staged one step ago
             store(mc, bA);
             if (xr + 2 < n) advance();
             const Meta mn2 = meta_of(xr + 2 < n);
             issue_data(mn1, bA);
-            __syncthreads();
+            q_issue(mn1.s);                                     // q of the next chunk's sequence
+            wave_sync();
             process(meta_nv(mc));
             if (xr + 1 == n || mn1.s != mc.s) flush(mc);
             if (xr + 1 == n) break;
-            __syncthreads();
+            wave_sync();
             mc = mn1;
             mn1 = mn2;
         }
@@ -832,16 +893,17 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
         if (n > 2) advance();
         Meta mn2 = meta_of(n > 2);
         auto step = [&](uint32_t xr, Buf& b) __attribute__((always_inline)) -> bool {
-            if (mc.s != q_seq) { load_q(mc.s); q_seq = mc.s; }
+            if (mc.s != q_seq) { q_finish(); q_seq = mc.s; }   // q of mc.s was staged one step ago
             store(mc, b);
             if (xr + 3 < n) advance();
             const Meta mn3 = meta_of(xr + 3 < n);
             issue_data(mn2, b);
-            __syncthreads();
+            q_issue(mn1.s);                                     // q of the next chunk's sequence
+            wave_sync();
             process(meta_nv(mc));
             if (xr + 1 == n || mn1.s != mc.s) flush(mc);
             if (xr + 1 == n) return false;
-            __syncthreads();
+            wave_sync();
             mc = mn1;
             mn1 = mn2;
             mn2 = mn3;
@@ -857,15 +919,28 @@ __global__ __launch_bounds__(64, (HS4P <= 32) ? 2 : 1) void decode_split_kernel(
     if (j == W - 1) zero_rows(a, lane, mc.s + 1, a.num_seqs, h0, nh);
 }
 
+template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED>
+void launch_split_seg(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st, bool tiled) {
+    // Scalar-addressed segment loads need an exact head size, 16-byte aligned
+    // caches and tile segments of 16 or 32 rows.
+    const uint32_t segr = EXACT && tiled ? c.seg_rows : 0;
+    if (EXACT && segr == 16)
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, EXACT ? 16 : 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
+    else if (EXACT && segr == 32)
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, EXACT ? 32 : 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
+}
+
 template <int HS4P, bool EXACT, int NHS>
 hipError_t launch_split_t(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
                           bool vis, bool tiled) {
     if (vis)
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, true, false>), grid, dim3(64), 0, st, a, c, nbm1);
+        launch_split_seg<HS4P, EXACT, NHS, true, false>(a, c, nbm1, grid, st, tiled);
     else if (EXACT && tiled)
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, false, EXACT>), grid, dim3(64), 0, st, a, c, nbm1);
+        launch_split_seg<HS4P, EXACT, NHS, false, EXACT>(a, c, nbm1, grid, st, tiled);
     else
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, false, false>), grid, dim3(64), 0, st, a, c, nbm1);
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, false, false, 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
     return hipGetLastError();
 }
 
@@ -925,6 +1000,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
     const bool align_ok = reinterpret_cast<uintptr_t>(a.key_cache) % 16 == 0 &&
                           reinterpret_cast<uintptr_t>(a.value_cache) % 16 == 0;
     c.tiled_ok = shape_ok && align_ok;
+    c.q_vec_ok = reinterpret_cast<uintptr_t>(a.q) % 16 == 0 && a.q_stride % 4 == 0;
     c.seg_u4 = c.seg_rows * wpt / 4;
     if (c.seg_u4 == 0) c.seg_u4 = 1;
     c.seg_magic = static_cast<uint32_t>((0x100000000ull + c.seg_u4 - 1) / c.seg_u4);
@@ -932,7 +1008,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
     // (positions are capped by the table); the kernel then only writes zeros.
     const uint32_t nbm1 = a.num_blocks ? a.num_blocks - 1 : 0;
     {
-        const dim3 grid(static_cast<uint32_t>(p.num_waves));
+        const dim3 grid(static_cast<uint32_t>((p.num_waves + kWavesPerGroup - 1) / kWavesPerGroup));
         hipError_t err;
         const bool t = c.tiled_ok != 0;
         if (hs4 == 16) err = launch_split_g<16, true>(a, c, nbm1, grid, stream, vis, t);
