@@ -1,0 +1,937 @@
+// Single-query decode attention over the int8 paged KV cache.
+//
+// What is computed follows the "paged_attn_q8.comp" page: for each (seq s,
+// query head h), out = softmax(scale * q . K^T) . V over the sequence's
+// positions, K and V dequantized on read as code * token_scale, kv head
+// h / (num_heads / num_kv_heads), token t at block_tables[s][t / block_size],
+// offset t % block_size.  As on that page, the per-token K scale multiplies
+// the code dot product and the per-token V scale is folded into the softmax
+// weight.  The visible-list mode (the "attention.rs" page's selective split
+// decode) attends the listed positions instead of 0 .. context_len - 1.
+//
+// MI355X design (not the page's one-workgroup-per-(seq, head) three-pass
+// shader):
+//   * Positions are processed in chunks of 64.  For one row group (kv head,
+//     up to 8 query heads sharing it) the chunks of all sequences form one
+//     sequence of C chunks; a fixed number of persistent wavefronts per row
+//     group each take an equal contiguous range of it (the split-context idea
+//     of the "attention.rs" page, balanced over the whole batch instead of per
+//     sequence), so every wave does the same amount of work and there is no
+//     tail.  A wave that covers a whole sequence writes its output directly;
+//     otherwise it writes softmax partials (running max, sum, unnormalized
+//     output) and a merge kernel combines them.  Wavefronts are numbered kv
+//     head fastest, so the kv-head slices of the same cache blocks are
+//     requested together.  Each K/V byte is read once per row group.
+//   * A chunk of 64 consecutive, 64-aligned positions is a run of whole cache
+//     tiles (or one 64-row slice of a larger tile): it is fetched with
+//     coalesced 16-byte loads into registers, up to two chunks ahead of use,
+//     then written to LDS.  The loads are unconditional (masked slots read a
+//     fixed line), so the compiler's wait counts stay exact across the loop.
+//     Other chunks (visible lists with gaps) are gathered row by row.
+//   * Both contractions run on the int8 matrix cores
+//     (v_mfma_i32_16x16x64_i8), whose operands include the cache's own codes:
+//       q.K^T: each query head's q row is scaled by a power of two and rounded
+//       to an integer below 2^30 in magnitude, written as four balanced
+//       base-256 digits; the 16 MFMA rows are (4 heads x 4 digits), the
+//       columns 16 tokens, k the head dimension.
+//       P.V: the softmax weights of a chunk times the V token scales are
+//       scaled by a power of two and rounded to integers below 2^29, again as
+//       four digits; rows (4 heads x 4 digits), k = 64 tokens, columns 16 head
+//       dimensions.  V codes are transposed to token-major bytes with v_perm.
+//     The int32 digit sums are exact and are combined exactly in f64; q and
+//     the weights keep 30 significant bits, finer than binary32, so the result
+//     carries f32-level rounding error only.
+//   * Online softmax in the exp2 domain (scale folded with log2 e).  Each
+//     MFMA output row group is one head, so the per-head max and sum reduce
+//     over the 16 lanes of a DPP row.
+#pragma once
+#include "decode_split.h"
+
+namespace q8kv {
+namespace {
+
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kDigitBias = 0x80808080u;
+
+__device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Four balanced base-256 digits of a signed integer |n| <= 2^30, one per
+// byte, each read back as a signed int8: sum_k byte_k * 256^k == n.
+__device__ __forceinline__ uint32_t to_digits(int32_t n) {
+    return (static_cast<uint32_t>(n) + kDigitBias) ^ kDigitBias;
+}
+
+// Exact value of sum_k d[k] * 256^k for int32 digit sums |d[k]| < 2^22.
+__device__ __forceinline__ double combine_digits(i32x4 d) {
+    const int32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3];
+    const int32_t lo = d0 + d1 * 256;
+    const int32_t hi = d2 + d3 * 256;
+    return static_cast<double>(hi) * 65536.0 + static_cast<double>(lo);
+}
+
+// v_perm_b32: byte i of the result is byte sel_i of the 8-byte value (a:b),
+// selectors 0-3 picking bytes of b and 4-7 bytes of a.
+__device__ __forceinline__ uint32_t perm(uint32_t a, uint32_t b, uint32_t sel) {
+    return __builtin_amdgcn_perm(a, b, sel);
+}
+
+// 4x4 byte transpose: byte b of y[j] = byte j of x[b].
+__device__ __forceinline__ void transpose4(const uint32_t x[4], uint32_t y[4]) {
+    const uint32_t t01l = perm(x[1], x[0], 0x05010400u);   // x0.0 x1.0 x0.1 x1.1
+    const uint32_t t01h = perm(x[1], x[0], 0x07030602u);   // x0.2 x1.2 x0.3 x1.3
+    const uint32_t t23l = perm(x[3], x[2], 0x05010400u);
+    const uint32_t t23h = perm(x[3], x[2], 0x07030602u);
+    y[0] = perm(t23l, t01l, 0x05040100u);
+    y[1] = perm(t23l, t01l, 0x07060302u);
+    y[2] = perm(t23h, t01h, 0x05040100u);
+    y[3] = perm(t23h, t01h, 0x07060302u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowRor1 = 0x121;
+constexpr int kRowRor2 = 0x122;
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+
+// Reductions over the 16 lanes of a DPP row (rotations within the row).
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dpp_mov<kRowRor1>(v));
+    v = fmaxf(v, dpp_mov<kRowRor2>(v));
+    v = fmaxf(v, dpp_mov<kRowRor4>(v));
+    return fmaxf(v, dpp_mov<kRowRor8>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp_mov<kRowRor1>(v);
+    v += dpp_mov<kRowRor2>(v);
+    v += dpp_mov<kRowRor4>(v);
+    return v + dpp_mov<kRowRor8>(v);
+}
+
+// Exponent e with |x| < 2^e for finite nonzero x (frexp convention).
+__device__ __forceinline__ int exponent_bound(float x) {
+    int e = 0;
+    (void)frexpf(x, &e);
+    return e;
+}
+
+// LDS hand-off between the lanes of one wavefront: LDS operations of a
+// wavefront execute in order, so only compiler reordering must be prevented
+// (the wavefronts of a workgroup never wait for each other).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t t = __shfl_up(v, d, kWave);
+        if (lane >= static_cast<uint32_t>(d)) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), static_cast<int>(l)));
+}
+
+
+// Number of positions sequence s attends.
+template <bool VIS>
+__device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s) {
+    uint32_t n;
+    if (VIS) {
+        n = a.num_visible[s];
+        n = n < a.vis_stride ? n : a.vis_stride;
+    } else {
+        n = a.context_lens[s];
+        n = n < a.max_context_len ? n : a.max_context_len;
+        const uint64_t cap = static_cast<uint64_t>(a.max_num_blocks_per_seq) * a.block_size;
+        if (n > cap) n = static_cast<uint32_t>(cap);   // defensive: never index past a table row
+    }
+    return n;
+}
+
+template <bool VIS>
+__device__ __forceinline__ uint32_t chunks_of(const DecodeArgs& a, uint32_t s) {
+    return (positions_of<VIS>(a, s) + kChunk - 1) / kChunk;
+}
+
+template <bool VIS>
+__device__ __forceinline__ uint32_t position_at(const DecodeArgs& a, uint32_t s, uint32_t idx) {
+    return VIS ? a.visible_pos[static_cast<uint64_t>(s) * a.vis_stride + idx] : idx;
+}
+
+// Device-coherent (agent scope) accesses for data handed between wavefronts
+// that may run on different XCDs: they bypass the non-coherent L2 copies, so
+// no whole-cache write-back or invalidation is needed.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Zero output rows of sequences [s_begin, s_end) for query heads h0 .. h0+nh-1.
+__device__ void zero_rows(const DecodeArgs& a, uint32_t lane, uint32_t s_begin, uint32_t s_end, uint32_t h0,
+                          uint32_t nh) {
+    const uint32_t hs4 = a.head_size / 4;
+    for (uint32_t s = s_begin; s < s_end; ++s)
+        for (uint32_t p = lane; p < nh * hs4; p += kWave) {
+            const uint64_t row = static_cast<uint64_t>(s) * a.num_heads + h0 + p / hs4;
+            *reinterpret_cast<float4*>(a.out + row * a.head_size + 4 * (p % hs4)) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+}
+
+// Chunk sequence of one row group: the chunks of sequence 0, then sequence 1,
+// ...  Wave-uniform results.
+//   chunk_totals: total chunk count C and the chunks of sequences before s.
+template <bool VIS>
+__device__ void chunk_totals(const DecodeArgs& a, uint32_t lane, uint32_t s, uint32_t& total, uint32_t& before) {
+    total = 0;
+    before = 0;
+    for (uint32_t b = 0; b < a.num_seqs; b += kWave) {
+        const uint32_t t = b + lane;
+        const uint32_t nc = t < a.num_seqs ? chunks_of<VIS>(a, t) : 0u;
+        const uint32_t incl = wave_incl_scan(nc, lane);
+        const uint32_t wt = lane_value(incl, kWave - 1);
+        if (s >= b + kWave) before += wt;
+        else if (s > b) before += lane_value(incl, s - b - 1);
+        total += wt;
+    }
+}
+
+//   locate_chunk: the sequence holding chunk x (x < C) and the chunks before it.
+template <bool VIS>
+__device__ void locate_chunk(const DecodeArgs& a, uint32_t lane, uint32_t x, uint32_t& row, uint32_t& before) {
+    uint32_t base = 0;
+    row = a.num_seqs;
+    before = 0;
+    for (uint32_t b = 0; b < a.num_seqs; b += kWave) {
+        const uint32_t t = b + lane;
+        const uint32_t nc = t < a.num_seqs ? chunks_of<VIS>(a, t) : 0u;
+        const uint32_t incl = wave_incl_scan(nc, lane);
+        const uint32_t wt = lane_value(incl, kWave - 1);
+        if (x < base + wt) {
+            const uint64_t m = __ballot(base + incl > x);
+            const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(m));
+            row = b + l;
+            before = base + lane_value(incl - nc, l);
+            return;
+        }
+        base += wt;
+    }
+}
+
+// Wave (of the W covering the C chunks of a row group) whose range holds chunk
+// x: wave j covers [floor(j*C/W), floor((j+1)*C/W)).
+__device__ __forceinline__ uint32_t wave_of_chunk(uint32_t x, uint32_t C, uint32_t W) {
+    return static_cast<uint32_t>(((static_cast<uint64_t>(x) + 1) * W - 1) / C);
+}
+
+// Split-kernel lane roles.  Lane l = 16*g + r.
+//   q.K^T (v_mfma_i32_16x16x64_i8): lane (r, g) supplies MFMA row r = (head
+//   r/4, digit r%4) of the q digits and column r = token 16*tg + r of the
+//   codes, both over the 16 head dimensions 64*kb + 16*g + 0..15, and
+//   receives the digit sums of token 16*tg + r for head g.
+//   P.V: lane (r, g) supplies row r = (head r/4, digit r%4) of the weight
+//   digits and column r of the codes, both over the 16 tokens 4*g + w + 16*b
+//   (w, b = 0..3; byte 4*w + b of the operand), where column r of column
+//   block cw is dimension 4*NCW*r + 4*cw + j of MFMA j; it receives the digit
+//   sums of those dimensions for head g.
+//
+// HS4P: code words per row rounded up to 16, 32, 48 or 64; EXACT: head_size /
+// 4 == HS4P; NHS: sets of 4 query heads per wavefront (1 or 2); VIS: visible
+// list positions; TILED: every chunk is known to be a tile run (dense
+// positions, aligned caches, block_size dividing or a multiple of 64); SEGR:
+// when nonzero (16 or 32, with EXACT), the rows per tile segment, for which
+// each segment of a chunk fills whole 64-lane slots (SEGR*HS4P/256 of them)
+// plus SEGR/4 trailing 16-byte units: every full slot then loads from one
+// segment with a scalar base address and a fixed per-lane offset.
+template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED, int SEGR>
+__global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDepth == 1) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
+    constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
+    constexpr int NCW = HS4P / 16;             // V code words per lane and row
+    constexpr int G = 4 * NHS;
+    constexpr int QD = NKB * 64;               // padded q row length
+    constexpr int WPT_MAX = HS4P + 1;
+    constexpr int NU = (kChunk * WPT_MAX + 4 * kWave - 1) / (4 * kWave);   // 16-byte slots per lane
+    // An exact head size makes a chunk 64*(HS4P+1) words: HS4P/4 full 16-byte
+    // slots per lane plus one 4-byte tail slot per lane.
+    constexpr int NF = EXACT ? HS4P / 4 : NU;
+    constexpr bool FAST = SEGR > 0;
+    static_assert(!FAST || (EXACT && (SEGR * HS4P) % 256 == 0 && SEGR <= kChunk), "segment layout");
+    constexpr int FSEG = FAST ? kChunk / SEGR : 1;          // segments per chunk
+    constexpr int FS = FAST ? SEGR * HS4P / 256 : 0;         // full slots per segment (FSEG * FS == NF)
+    constexpr int FLO = FAST ? SEGR / 4 : 1;                 // trailing 16-byte units per segment
+    constexpr int SEG_U4 = FAST ? SEGR * (HS4P + 1) / 4 : 1; // 16-byte units per segment
+    struct Buf {
+        u32x4 k[NF], v[NF];
+        uint32_t kt, vt;        // EXACT generic layout: one 4-byte tail slot per lane
+        u32x4 k4, v4;           // FAST layout: the segments' trailing units (lanes 0-15)
+    };
+    constexpr int DEPTH = (HS4P <= 32 && NHS == 1) ? kPrefetchDepth : 1;  // chunks loaded ahead
+
+    // Per-wavefront LDS regions: the wavefronts of a workgroup are independent.
+    __shared__ __align__(16) uint32_t sK_[kWavesPerGroup][NU * 4 * kWave];   // also stages q rows at sequence changes
+    __shared__ __align__(16) uint32_t sV_[kWavesPerGroup][NU * 4 * kWave];
+    __shared__ __align__(16) uint32_t sA_[kWavesPerGroup][NHS * 16 * 16];    // [set][head*4+digit][w]: weight digits
+    __shared__ int sEq_[kWavesPerGroup][G];
+    const uint32_t wid = uniform(threadIdx.x / kWave);
+    uint32_t* const sK = sK_[wid];
+    uint32_t* const sV = sV_[wid];
+    uint32_t* const sA = sA_[wid];
+    int* const sEq = sEq_[wid];
+    float* const sQ = reinterpret_cast<float*>(sK);
+
+    const uint32_t lane = threadIdx.x % kWave;
+    const uint32_t r = lane & 15, g = lane >> 4;
+    const uint32_t gw = blockIdx.x * kWavesPerGroup + wid;      // persistent wavefront index
+    if (gw >= c.num_rg * c.waves_per_rg) return;
+    const uint32_t rg = gw % c.num_rg;
+    const uint32_t j = gw / c.num_rg;
+    const uint32_t kvh = rg % a.num_kv_heads;
+    const uint32_t grp = rg / a.num_kv_heads;
+
+    // ---- this wave's chunk range [x0, x1) of the row group's chunk sequence ----
+    // Up to 64 sequences: one load and one scan give the total, the range and
+    // the sequence holding its first chunk.
+    const bool one_window = a.num_seqs <= static_cast<uint32_t>(kWave);
+    uint32_t C, win_np = 0, win_nc = 0, win_incl = 0;
+    if (one_window) {
+        win_np = lane < a.num_seqs ? positions_of<VIS>(a, lane) : 0u;
+        win_nc = (win_np + kChunk - 1) / kChunk;
+        win_incl = wave_incl_scan(win_nc, lane);
+        C = lane_value(win_incl, kWave - 1);
+    } else {
+        uint32_t unused;
+        chunk_totals<VIS>(a, lane, 0, C, unused);
+    }
+    C = uniform(C);
+    const uint32_t W = min(c.waves_per_rg, C);
+    const uint32_t n_rep = a.num_heads / a.num_kv_heads;
+    const uint32_t h0 = kvh * n_rep + grp * G;
+    const uint32_t nh = min(static_cast<uint32_t>(G), n_rep - grp * G);
+    if (j >= W) {
+        if (C == 0 && j == 0) zero_rows(a, lane, 0, a.num_seqs, h0, nh);
+        return;
+    }
+    const uint32_t x0 = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j) * C / W));
+    const uint32_t x1 = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j + 1) * C / W));
+    const uint32_t n = x1 - x0;
+    uint32_t s0, p0c, np0 = 0;
+    if (one_window) {
+        const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(__ballot(win_incl > x0)));
+        s0 = l;
+        p0c = lane_value(win_incl - win_nc, l);
+        np0 = lane_value(win_np, l);
+    } else {
+        locate_chunk<VIS>(a, lane, x0, s0, p0c);
+    }
+    if (uniform(s0) >= a.num_seqs) return;    // unreachable for x0 < C
+
+    const uint32_t hs = a.head_size, hs4 = EXACT ? HS4P : hs / 4, wpt = hs4 + 1;
+    const uint64_t kv_stride = static_cast<uint64_t>(a.num_kv_heads) * a.block_size * wpt;  // words per block
+    const uint64_t kvh_off = static_cast<uint64_t>(kvh) * a.block_size * wpt;
+    const uint32_t chunk_u4 = kChunk * wpt / 4;
+    const uint32_t nseg = kChunk / c.seg_rows;            // tile segments per tiled chunk
+
+    // ---- cursor over the chunk sequence (wave-uniform) ----
+    struct Cursor {
+        uint32_t s, ci, npos, before;    // sequence, chunk index in it, its positions, chunks before it
+    };
+    Cursor cur{uniform(s0), 0, 0, uniform(p0c)};
+    cur.ci = x0 - cur.before;
+    cur.npos = one_window ? uniform(np0) : uniform(positions_of<VIS>(a, cur.s));
+    // Sequences with no positions get zero rows.  Each is written by exactly
+    // one wave of the row group: the one whose range it falls inside, wave 0
+    // for those before the first chunk, the last wave for those after it.
+    auto advance = [&]() __attribute__((always_inline)) {
+        ++cur.ci;
+        if (cur.ci * kChunk >= cur.npos) {
+            cur.before += (cur.npos + kChunk - 1) / kChunk;
+            cur.ci = 0;
+            while (true) {
+                ++cur.s;
+                cur.npos = cur.s >= a.num_seqs ? static_cast<uint32_t>(kChunk)
+                           : one_window ? lane_value(win_np, cur.s)
+                                        : uniform(positions_of<VIS>(a, cur.s));
+                if (cur.npos != 0) break;
+                zero_rows(a, lane, cur.s, cur.s + 1, h0, nh);
+            }
+        }
+    };
+    if (j == 0) zero_rows(a, lane, 0, cur.s, h0, nh);
+
+    // ---- chunk metadata (uniform except the block id of segment `lane`) ----
+    // info: bits 0-6 valid positions (0 for a chunk past the wave's range),
+    // bit 7 tiled chunk, bits 8-31 the number of waves whose ranges share the
+    // sequence (1: it lies wholly in this wave's range); jf: the first of them.
+    struct Meta {
+        uint32_t s, cs, p0, info, jf, id;
+    };
+    auto meta_nv = [](const Meta& m) __attribute__((always_inline)) { return m.info & 0x7Fu; };
+    auto meta_tiled = [](const Meta& m) __attribute__((always_inline)) { return TILED || (m.info & 0x80u) != 0; };
+    auto meta_nrec = [](const Meta& m) __attribute__((always_inline)) { return m.info >> 8; };
+    auto meta_of = [&](bool live) __attribute__((always_inline)) -> Meta {
+        Meta m;
+        m.s = cur.s;
+        m.cs = cur.ci * kChunk;
+        const uint32_t nv = live ? min(static_cast<uint32_t>(kChunk), cur.npos - m.cs) : 0u;
+        m.p0 = VIS ? uniform(position_at<VIS>(a, m.s, m.cs)) : m.cs;
+        uint32_t tiled = 1;
+        if (!TILED) {
+            tiled = c.tiled_ok;
+            if (VIS && tiled && nv > 0) {
+                const uint32_t pl = uniform(position_at<VIS>(a, m.s, m.cs + nv - 1));
+                tiled = (m.p0 % kChunk == 0) && (pl - m.p0 == nv - 1) ? 1u : 0u;
+            }
+        }
+        const uint32_t nc = (cur.npos + kChunk - 1) / kChunk;
+        m.jf = wave_of_chunk(cur.before, C, W);
+        const uint32_t nrec = wave_of_chunk(cur.before + nc - 1, C, W) - m.jf + 1;
+        m.info = nv | (tiled << 7) | (nrec << 8);
+        const uint32_t k = min(lane, nseg - 1);
+        uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(kChunk) ? k : 0u);
+        jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
+        m.id = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
+        return m;
+    };
+
+    // ---- tiled chunk loads: 16-byte slot u = lane + 64*i lies in segment u / seg_u4 ----
+    auto issue_data = [&](const Meta& m, Buf& b) __attribute__((always_inline)) {
+        if (FAST) {
+            // Segment k's tile (block id from lane k) starts at a uniform
+            // address; an invalid segment reads the cache's first bytes.
+            const bool ok = meta_tiled(m);
+            const uint32_t nv = meta_nv(m);
+            const char* kb[FSEG];
+            const char* vb[FSEG];
+#pragma unroll
+            for (int k = 0; k < FSEG; ++k) {
+                uint32_t ph = lane_value(m.id, k);
+                ph = ph < num_blocks_m1 ? ph : num_blocks_m1;
+                const bool valid = ok && static_cast<uint32_t>(k * SEGR) < nv;
+                const uint64_t off = valid ? static_cast<uint64_t>(ph) * kv_stride + kvh_off : 0;
+                kb[k] = reinterpret_cast<const char*>(a.key_cache + off);
+                vb[k] = reinterpret_cast<const char*>(a.value_cache + off);
+            }
+            const uint32_t lb = lane * 16;
+#pragma unroll
+            for (int k = 0; k < FSEG; ++k)
+#pragma unroll
+                for (int f = 0; f < FS; ++f) {
+                    b.k[k * FS + f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb[k] + lb + f * 1024));
+                    b.v[k * FS + f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb[k] + lb + f * 1024));
+                }
+            // Trailing units: lane l < 16 takes unit l % FLO of segment l / FLO.
+            const uint32_t kk = lane / FLO;
+            const char* pk = reinterpret_cast<const char*>(a.key_cache);
+            const char* pv = reinterpret_cast<const char*>(a.value_cache);
+#pragma unroll
+            for (int k = 0; k < FSEG; ++k)
+                if (kk == static_cast<uint32_t>(k)) { pk = kb[k]; pv = vb[k]; }
+            const uint32_t tb = (lane < 16u) ? (FS * 64 + lane % FLO) * 16 : lb;
+            b.k4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pk + tb));
+            b.v4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pv + tb));
+            return;
+        }
+        if (!TILED && !c.tiled_ok) return;     // no tile loads at all (caches not 16-byte aligned, odd block_size)
+        const uint32_t row0 = m.p0 % a.block_size;     // nonzero only when block_size > 64
+        const bool ok = meta_tiled(m);
+        const uint32_t nv = meta_nv(m);
+        const uint64_t base = kvh_off + static_cast<uint64_t>(row0) * wpt;
+        // Recompute the slot geometry per chunk (a few VALU ops) rather than
+        // keeping it live across the loop.
+        uint32_t ln = lane;
+        asm volatile("" : "+v"(ln));
+        // All block-id exchanges first (one LDS round trip), then the loads.
+        // An invalid slot's word offset is masked to 0, so it reads the
+        // cache's first line: branch-free, in bounds, and one cached line.
+        constexpr int NS = NF + (EXACT ? 1 : 0);
+        uint32_t kseg[NS], phys[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const uint32_t u = (i < NF) ? ln + kWave * i : (4 * kWave * NF + ln) >> 2;
+            kseg[i] = __umulhi(u, c.seg_magic);
+            phys[i] = __shfl(m.id, static_cast<int>(min(kseg[i], nseg - 1)), 64);
+        }
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const uint32_t k = kseg[i];
+            const uint32_t ph = phys[i] < num_blocks_m1 ? phys[i] : num_blocks_m1;
+            uint64_t w;
+            bool valid;
+            if (i < NF) {
+                const uint32_t u = ln + kWave * i;
+                valid = ok && (EXACT || u < chunk_u4) && (k * c.seg_rows < nv);
+                w = ph * kv_stride + base + (u - k * c.seg_u4) * 4;
+            } else {
+                const uint32_t wi = 4 * kWave * NF + ln;
+                valid = ok && (k * c.seg_rows < nv);
+                w = ph * kv_stride + base + (wi - 4 * k * c.seg_u4);
+            }
+            w &= 0ull - static_cast<uint64_t>(valid);
+            if (i < NF) {
+                b.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.key_cache + w));
+                b.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.value_cache + w));
+            } else {
+                b.kt = __builtin_nontemporal_load(a.key_cache + w);
+                b.vt = __builtin_nontemporal_load(a.value_cache + w);
+            }
+        }
+    };
+    auto store = [&](const Meta& m, const Buf& b) __attribute__((always_inline)) {
+        if (FAST && meta_tiled(m)) {
+#pragma unroll
+            for (int k = 0; k < FSEG; ++k)
+#pragma unroll
+                for (int f = 0; f < FS; ++f) {
+                    const uint32_t u = k * SEG_U4 + f * 64 + lane;
+                    *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k[k * FS + f];
+                    *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v[k * FS + f];
+                }
+            if (lane < 16u) {
+                const uint32_t u = (lane / FLO) * SEG_U4 + FS * 64 + lane % FLO;
+                *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k4;
+                *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v4;
+            }
+        } else if (meta_tiled(m)) {
+#pragma unroll
+            for (int i = 0; i < NF; ++i) {
+                const uint32_t u = lane + kWave * i;
+                *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k[i];
+                *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v[i];
+            }
+            if (EXACT) {
+                sK[4 * kWave * NF + lane] = b.kt;
+                sV[4 * kWave * NF + lane] = b.vt;
+            }
+        } else {
+            // Row gather: lane i resolves the chunk's i-th position, then the
+            // wave copies the rows one after another.
+            const uint32_t nv = meta_nv(m);
+            const uint32_t pos = position_at<VIS>(a, m.s, m.cs + min(lane, nv - 1));
+            uint32_t jb = pos / a.block_size;
+            jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
+            uint32_t phys = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
+            phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
+            const uint64_t my_row = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size +
+                                     pos % a.block_size) * wpt;
+            for (uint32_t rr = 0; rr < nv; ++rr) {
+                const uint32_t lo = __shfl(static_cast<uint32_t>(my_row), rr, 64);
+                const uint32_t hi = __shfl(static_cast<uint32_t>(my_row >> 32), rr, 64);
+                const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
+                for (uint32_t w = lane; w < wpt; w += kWave) {
+                    sK[rr * wpt + w] = a.key_cache[base + w];
+                    sV[rr * wpt + w] = a.value_cache[base + w];
+                }
+            }
+        }
+    };
+
+    // ---- q digits of the current sequence: MFMA row r = (head r/4, digit r%4) ----
+    i32x4 qa[NHS][NKB];
+    int eq_out[NHS];       // q exponent of this lane's output head 4*hset + g
+    // q rows of the query heads h0 .. h0+nh-1 (padded to G heads of QD
+    // values) staged per lane as QF 16-byte slots: lane l, slot t holds padded
+    // elements 4*(l + 64*t) .. +3.
+    constexpr int QF = G * QD / (4 * kWave);
+    float4 qv[QF];
+    auto q_issue = [&](uint32_t s) __attribute__((always_inline)) {
+        const uint64_t row = static_cast<uint64_t>(s) * a.q_stride;
+#pragma unroll
+        for (int t = 0; t < QF; ++t) {
+            const uint32_t e = 4 * (lane + kWave * t);
+            const uint32_t hi = e / QD, d = e % QD;
+            const bool ok = hi < nh && d < hs;               // d % 4 == 0 and hs % 4 == 0: all four or none
+            const float* src = a.q + (ok ? row + static_cast<uint64_t>(h0 + hi) * hs + d : row);
+            float4 v;
+            if (c.q_vec_ok) {
+                v = *reinterpret_cast<const float4*>(src);
+            } else {
+                v = make_float4(src[0], ok ? src[1] : 0.f, ok ? src[2] : 0.f, ok ? src[3] : 0.f);
+            }
+            qv[t] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto q_finish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < QF; ++t) *reinterpret_cast<float4*>(&sQ[4 * (lane + kWave * t)]) = qv[t];
+        wave_sync();
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) {
+            const uint32_t hq = 4 * hset + r / 4, dig = r % 4;
+            const float* row = &sQ[hq * QD];
+            float amax = 0.0f;
+            for (int d = 0; d < QD; d += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(row + d);
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+            const int eq = amax > 0.0f ? 30 - exponent_bound(amax) : 0;    // |q * 2^eq| < 2^30
+            if (g == 0 && dig == 0) sEq[hq] = eq;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                uint32_t packed[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float4 v = *reinterpret_cast<const float4*>(row + 64 * kb + 16 * g + 4 * w);
+                    const uint32_t b0 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.x, eq)))) >> (8 * dig)) & 0xFFu;
+                    const uint32_t b1 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.y, eq)))) >> (8 * dig)) & 0xFFu;
+                    const uint32_t b2 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.z, eq)))) >> (8 * dig)) & 0xFFu;
+                    const uint32_t b3 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.w, eq)))) >> (8 * dig)) & 0xFFu;
+                    packed[w] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+                }
+                qa[hset][kb] = i32x4{static_cast<int32_t>(packed[0]), static_cast<int32_t>(packed[1]),
+                                     static_cast<int32_t>(packed[2]), static_cast<int32_t>(packed[3])};
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) eq_out[hset] = sEq[4 * hset + g];
+    };
+
+    // Online-softmax state (log2 units) of head 4*hset + g, uniform across the lane's row.
+    float m_run[NHS], l_run[NHS];
+    float acc[NHS][NCW][4];      // dims 4*NCW*r + 4*cw + j of head 4*hset + g
+    auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) {
+            m_run[hset] = -INFINITY;
+            l_run[hset] = 0.0f;
+#pragma unroll
+            for (int cw = 0; cw < NCW; ++cw)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[hset][cw][jj] = 0.0f;
+        }
+    };
+
+    // One chunk from LDS: q.K^T, online softmax, P.V.
+    auto process = [&](uint32_t nv) __attribute__((always_inline)) {
+        // ---- q . K^T ----
+        i32x4 dsum[NHS][4];
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg) {
+            const uint32_t* krow = &sK[(16 * tg + r) * wpt + 4 * g];
+#pragma unroll
+            for (int hset = 0; hset < NHS; ++hset) dsum[hset][tg] = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                i32x4 b;
+                if (EXACT) {
+                    __builtin_memcpy(&b, krow + 16 * kb, 16);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        b[q] = (16 * kb + 4 * g + q < hs4) ? static_cast<int32_t>(krow[16 * kb + q]) : 0;
+                }
+#pragma unroll
+                for (int hset = 0; hset < NHS; ++hset) dsum[hset][tg] = mfma_i8(qa[hset][kb], b, dsum[hset][tg]);
+            }
+        }
+
+        // ---- token scales of rows 16*tg + r ----
+        float ksc[4], vsc[4];
+        bool val[4];
+        float vmax = 0.0f;
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg) {
+            const uint32_t t = 16 * tg + r;
+            val[tg] = t < nv;
+            ksc[tg] = __uint_as_float(sK[t * wpt + hs4]);
+            vsc[tg] = __uint_as_float(sV[t * wpt + hs4]);
+            vmax = val[tg] ? fmaxf(vmax, vsc[tg]) : vmax;     // select: unwritten rows never leak
+        }
+        vmax = row_max(vmax);
+        const int ep = 29 - exponent_bound(vmax);             // weight * 2^ep < 2^29
+
+        // ---- online softmax; weights to integers, digits to LDS ----
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) {
+            float z[4];
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) {
+                const float zq = ldexpf(static_cast<float>(combine_digits(dsum[hset][tg])), -eq_out[hset]);
+                z[tg] = val[tg] ? zq * (ksc[tg] * a.scale_log2) : -INFINITY;
+                cmax = fmaxf(cmax, z[tg]);
+            }
+            const float m_new = fmaxf(m_run[hset], row_max(cmax));
+            const float alpha = exp2f(m_run[hset] - m_new);
+            float psum = 0.0f;
+            uint32_t wd[4];
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg) {
+                const float p = exp2f(z[tg] - m_new);
+                psum += p;
+                const float pv = val[tg] ? p * vsc[tg] : 0.0f;
+                wd[tg] = to_digits(static_cast<int32_t>(rintf(ldexpf(pv, ep))));
+            }
+            l_run[hset] = l_run[hset] * alpha + row_sum(psum);
+            m_run[hset] = m_new;
+            uint32_t td[4];
+            transpose4(wd, td);       // byte tg of td[digit] = digit of token r + 16*tg
+#pragma unroll
+            for (int dg = 0; dg < 4; ++dg) sA[(hset * 16 + 4 * g + dg) * 16 + r] = td[dg];
+#pragma unroll
+            for (int cw = 0; cw < NCW; ++cw)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[hset][cw][jj] *= alpha;
+        }
+        wave_sync();
+
+        // ---- P . V ----
+        i32x4 pa[NHS];
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset)
+            pa[hset] = *reinterpret_cast<const i32x4*>(&sA[(hset * 16 + r) * 16 + 4 * g]);
+        const double pscale = ldexp(1.0, -ep);
+#pragma unroll
+        for (int cw = 0; cw < NCW; ++cw) {
+            uint32_t bj[4][4];      // [byte j][w]: codes of tokens 4g + w + 16*b (byte b)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t x[4], y[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t word = NCW * r + cw;
+                    x[b] = (EXACT || word < hs4) ? sV[(4 * g + w + 16 * b) * wpt + word] : 0u;
+                }
+                transpose4(x, y);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) bj[jj][w] = y[jj];
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const i32x4 b = i32x4{static_cast<int32_t>(bj[jj][0]), static_cast<int32_t>(bj[jj][1]),
+                                      static_cast<int32_t>(bj[jj][2]), static_cast<int32_t>(bj[jj][3])};
+#pragma unroll
+                for (int hset = 0; hset < NHS; ++hset) {
+                    const i32x4 d = mfma_i8(pa[hset], b, i32x4{0, 0, 0, 0});
+                    acc[hset][cw][jj] += static_cast<float>(combine_digits(d) * pscale);
+                }
+            }
+        }
+    };
+
+    // Combine the nrec records of sequence ms (waves jf .. jf+nrec-1) into its
+    // output rows.  Lane items are (head, 4 dims); for each item every
+    // record's (max, sum, 4 dims) is loaded in one batch of independent
+    // loads (8 records at a time), so a typical combine is one memory round
+    // trip.  Running max and rescaling as in the online softmax.
+    auto merge = [&](uint32_t ms, uint32_t jf, uint32_t nrec) __attribute__((always_inline)) {
+        const uint64_t row_sh = static_cast<uint64_t>(ms) * a.num_heads;
+        const uint64_t ml0 = (static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf) * G;   // record 0, head 0
+        for (uint32_t p = lane; p < nh * hs4; p += kWave) {
+            const uint32_t hh = p / hs4, word = p % hs4;
+            float M = -INFINITY, L = 0.0f;
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (uint32_t i0 = 0; i0 < nrec; i0 += 8) {
+                float mi[8], li[8];
+                float4 vi[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t i = min(i0 + k, nrec - 1);
+                    const uint64_t slot = ml0 + static_cast<uint64_t>(i) * G + hh;
+                    const float* pa_ = a.part_acc + slot * hs + 4 * word;
+                    mi[k] = coherent_load(a.part_ml + 2 * slot);
+                    li[k] = coherent_load(a.part_ml + 2 * slot + 1);
+                    vi[k] = make_float4(coherent_load(pa_), coherent_load(pa_ + 1), coherent_load(pa_ + 2),
+                                        coherent_load(pa_ + 3));
+                }
+                float bm = M;
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (i0 + k < nrec) bm = fmaxf(bm, mi[k]);
+                const float sc = exp2f(M - bm);
+                L *= sc; o.x *= sc; o.y *= sc; o.z *= sc; o.w *= sc;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float w = i0 + k < nrec ? exp2f(mi[k] - bm) : 0.0f;
+                    L += w * li[k];
+                    o.x += w * vi[k].x; o.y += w * vi[k].y; o.z += w * vi[k].z; o.w += w * vi[k].w;
+                }
+                M = bm;
+            }
+            const float inv = 1.0f / L;
+            *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) =
+                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        }
+    };
+
+    uint32_t npend = 0, pend_s0 = 0, pend_jf0 = 0, pend_n0 = 0, pend_s1 = 0, pend_jf1 = 0, pend_n1 = 0;
+
+    // ---- end of a sequence's share: final output or a partial record ----
+    // Lane (r, g) holds dims 4*NCW*r + 4*cw + j of head 4*hset + g.  Record id
+    // j + s is unique within the row group: a wave's sequences increase, and a
+    // later wave starts at or after the sequence where the previous one ended.
+    // The last of the sequence's waves to arrive (a counter per (row group,
+    // sequence), which it sets back to zero) later combines all its records.
+    auto flush = [&](const Meta& m) __attribute__((always_inline)) {
+        const uint32_t nrec = meta_nrec(m);
+        const uint64_t row_sh = static_cast<uint64_t>(m.s) * a.num_heads;
+        const uint64_t rec0 = static_cast<uint64_t>(rg) * c.recs_per_rg + m.s;    // record of wave jj: rec0 + jj
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) {
+            const uint32_t hh = 4 * hset + g;
+            if (hh >= nh) continue;
+#pragma unroll
+            for (int cw = 0; cw < NCW; ++cw) {
+                const uint32_t word = NCW * r + cw;
+                if (word >= hs4) continue;
+                float4 v = make_float4(acc[hset][cw][0], acc[hset][cw][1], acc[hset][cw][2], acc[hset][cw][3]);
+                if (nrec == 1) {
+                    const float inv = 1.0f / l_run[hset];
+                    v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
+                    *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) = v;
+                } else {
+                    const uint64_t slot = (rec0 + j) * G + hh;
+                    float* pa_ = a.part_acc + slot * hs + 4 * word;
+                    coherent_store(pa_, v.x);
+                    coherent_store(pa_ + 1, v.y);
+                    coherent_store(pa_ + 2, v.z);
+                    coherent_store(pa_ + 3, v.w);
+                    if (word == 0) {
+                        coherent_store(a.part_ml + 2 * slot, m_run[hset]);
+                        coherent_store(a.part_ml + 2 * slot + 1, l_run[hset]);
+                    }
+                }
+            }
+        }
+        reset();
+        if (nrec == 1) return;
+        // The record was written with device-coherent stores; once they have
+        // completed, count this wave in.  No cache maintenance is needed (a
+        // device-scope fence would write back and invalidate the whole L2).
+        __builtin_amdgcn_s_waitcnt(0);
+        uint32_t prev = 0;
+        if (lane == 0)
+            prev = __hip_atomic_fetch_add(a.counters + static_cast<uint64_t>(rg) * a.num_seqs + m.s, 1u,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = uniform(prev);
+        if (prev != nrec - 1) return;
+        // Last arrival: reset the counter for the next call; the records are
+        // combined after the main loop, when the tile registers are free.  A
+        // sequence shared with other waves extends past one end of this
+        // wave's range, so there are at most two such sequences per wave.
+        if (lane == 0)
+            __hip_atomic_store(a.counters + static_cast<uint64_t>(rg) * a.num_seqs + m.s, 0u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (npend == 0) { pend_s0 = m.s; pend_jf0 = m.jf; pend_n0 = nrec; }
+        else { pend_s1 = m.s; pend_jf1 = m.jf; pend_n1 = nrec; }
+        ++npend;
+    };
+
+    // ---- pipeline over the wave's chunks x0 .. x1-1 ----
+    // Step for chunk x (relative index xr): its data sit in registers `kb/vb`;
+    // the next DEPTH-1 chunks are in flight in the other buffer.  The step
+    // stores chunk x to LDS, reads the block ids of chunk x+DEPTH+1, reuses the
+    // registers for chunk x+DEPTH, and processes chunk x.
+    reset();
+    // Prologue order: block ids of chunk x0, q of its sequence, chunk x0's
+    // tiles, block ids of x0+1; the q digits are formed while tiles arrive.
+    Buf bA;
+    Meta mc = meta_of(true);
+    q_issue(mc.s);
+    issue_data(mc, bA);
+    Meta mn1;
+    if (n > 1) advance();
+    mn1 = meta_of(n > 1);
+    q_finish();
+    uint32_t q_seq = mc.s;
+    if (DEPTH == 1) {
+        for (uint32_t xr = 0;; ++xr) {
+            if (mc.s != q_seq) { q_finish(); q_seq = mc.s; }   // q of mc.s was staged one step ago
+            store(mc, bA);
+            if (xr + 2 < n) advance();
+            const Meta mn2 = meta_of(xr + 2 < n);
+            issue_data(mn1, bA);
+            q_issue(mn1.s);                                     // q of the next chunk's sequence
+            wave_sync();
+            process(meta_nv(mc));
+            if (xr + 1 == n || mn1.s != mc.s) flush(mc);
+            if (xr + 1 == n) break;
+            wave_sync();
+            mc = mn1;
+            mn1 = mn2;
+        }
+    } else {
+        Buf bB;
+        issue_data(mn1, bB);
+        if (n > 2) advance();
+        Meta mn2 = meta_of(n > 2);
+        auto step = [&](uint32_t xr, Buf& b) __attribute__((always_inline)) -> bool {
+            if (mc.s != q_seq) { q_finish(); q_seq = mc.s; }   // q of mc.s was staged one step ago
+            store(mc, b);
+            if (xr + 3 < n) advance();
+            const Meta mn3 = meta_of(xr + 3 < n);
+            issue_data(mn2, b);
+            q_issue(mn1.s);                                     // q of the next chunk's sequence
+            wave_sync();
+            process(meta_nv(mc));
+            if (xr + 1 == n || mn1.s != mc.s) flush(mc);
+            if (xr + 1 == n) return false;
+            wave_sync();
+            mc = mn1;
+            mn1 = mn2;
+            mn2 = mn3;
+            return true;
+        };
+        for (uint32_t xr = 0;; xr += 2) {
+            if (!step(xr, bA)) break;
+            if (!step(xr + 1, bB)) break;
+        }
+    }
+    if (npend > 0) merge(pend_s0, pend_jf0, pend_n0);
+    if (npend > 1) merge(pend_s1, pend_jf1, pend_n1);
+    if (j == W - 1) zero_rows(a, lane, mc.s + 1, a.num_seqs, h0, nh);
+}
+
+template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED>
+void launch_split_seg(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st, bool tiled) {
+    // Scalar-addressed segment loads need an exact head size, 16-byte aligned
+    // caches and tile segments of 16 or 32 rows.
+    const uint32_t segr = EXACT && tiled ? c.seg_rows : 0;
+    if (EXACT && segr == 16)
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, EXACT ? 16 : 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
+    else if (EXACT && segr == 32)
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, EXACT ? 32 : 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
+}
+
+template <int HS4P, bool EXACT, int NHS>
+hipError_t launch_split_t(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
+                          bool vis, bool tiled) {
+    if (vis)
+        launch_split_seg<HS4P, EXACT, NHS, true, false>(a, c, nbm1, grid, st, tiled);
+    else if (EXACT && tiled)
+        launch_split_seg<HS4P, EXACT, NHS, false, EXACT>(a, c, nbm1, grid, st, tiled);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, false, false, 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
+    return hipGetLastError();
+}
+
+template <int HS4P, bool EXACT>
+hipError_t launch_split_g(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
+                          bool vis, bool tiled) {
+    if (c.group == 8) return launch_split_t<HS4P, EXACT, 2>(a, c, nbm1, grid, st, vis, tiled);
+    return launch_split_t<HS4P, EXACT, 1>(a, c, nbm1, grid, st, vis, tiled);
+}
+
+}  // namespace
+}  // namespace q8kv
