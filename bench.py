@@ -247,7 +247,7 @@ def main():
         "cache_write": {"us_mean": round(float(t_write.mean()), 2), "tokens": int(step_slots.size)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "q8_paged_decode (split + merge launches)",
+                     "kernel": "q8_paged_decode (one launch: decode_split_kernel)",
                      "algorithmic_bytes_per_launch": B},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,

@@ -26,7 +26,7 @@ import statistics
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-DECODE_KERNELS = ("decode_split_kernel", "decode_merge_kernel")
+DECODE_KERNELS = ("decode_split_kernel",)
 WRITE_KERNEL = "cache_write_kernel"
 
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d {d}/trace -o bench -f csv "
@@ -104,7 +104,6 @@ def main():
                      min(durs), max(durs), vgpr, agpr, sgpr, lds, scr, tag is not None and len(durs) == n_step))
 
     split_us = mean_of(rows, "decode_split_kernel")
-    merge_us = mean_of(rows, "decode_merge_kernel")
     write_us = mean_of(rows, "cache_write_kernel")
     eff = bench_trace["config"]["effective_kv_bytes"]
     lines = [
@@ -116,8 +115,8 @@ def main():
         "# summarised with: python3 bench_profile.py <that -d directory's parent>",
         "#",
         "# kernel_sources_sha256_16: %s" % digest,
-        "# durations in microseconds per dispatch; step = one launch each of cache_write, decode_split, "
-        "decode_merge",
+        "# durations in microseconds per dispatch; step = one cache_write launch and one decode launch "
+        "(decode_split_kernel, which also combines shared sequences)",
         "",
         "%-52s %9s %4s %5s %9s %9s %9s %9s %5s %5s %5s %6s %6s" % (
             "kernel", "grid", "wg", "calls", "mean_us", "median_us", "min_us", "max_us", "vgpr", "agpr", "sgpr",
@@ -129,10 +128,8 @@ def main():
             "  <- step" if r[13] else ""))
     lines += [
         "",
-        "decode per step (split + merge mean): %.2f us" % (split_us + merge_us),
-        "  decode_split_kernel mean: %.2f us, decode_merge_kernel mean: %.2f us" % (split_us, merge_us),
-        "  effective int8 KV bytes per decode: %d -> %.1f GB/s over split+merge" % (
-            eff, eff / ((split_us + merge_us) * 1e-6) / 1e9),
+        "decode per step (decode_split_kernel mean): %.2f us" % split_us,
+        "  effective int8 KV bytes per decode: %d -> %.1f GB/s" % (eff, eff / (split_us * 1e-6) / 1e9),
         "cache_write (64 tokens) mean: %.2f us" % write_us,
         "bench.py in the same run (HIP events on the launch stream): decode us_mean %.2f, effective %.1f GB/s" % (
             bench_trace["decode"]["us_mean"], bench_trace["decode"]["effective_GBps"]),
@@ -173,7 +170,7 @@ def main():
                          rd, wr)
     dec_bytes = sum(per_kernel[k][2] + per_kernel[k][3] for k in DECODE_KERNELS)
     t = [
-        "# HBM traffic of the decode launches (split + merge), Llama-3-8B-shaped batch",
+        "# HBM traffic of the decode launch, Llama-3-8B-shaped batch",
         "# (S=64 H=32 Hkv=8 head_size=128 block_size=16, context lengths U[512,4096], seed 2)",
         "#",
         "# commands (from any directory on the GPU machine), one counter per run:",
@@ -204,8 +201,6 @@ def main():
         "write_factor: %.6f" % factor["WRITE_SIZE"],
         "split_read_bytes: %.0f" % per_kernel["decode_split_kernel"][2],
         "split_write_bytes: %.0f" % per_kernel["decode_split_kernel"][3],
-        "merge_read_bytes: %.0f" % per_kernel["decode_merge_kernel"][2],
-        "merge_write_bytes: %.0f" % per_kernel["decode_merge_kernel"][3],
         "hbm_bytes_per_step: %.0f" % dec_bytes,
     ]
     with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_traffic.txt"), "w") as f:

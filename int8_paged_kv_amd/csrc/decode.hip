@@ -30,10 +30,14 @@ DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_he
     // Workspace: one arrival counter per (row group, sequence), then the
     // partial records.  A sequence of at most one chunk always lies in a
     // single wave's range, so then no workspace is needed at all.
+    // A record holds the padded head size (code words per row rounded up to
+    // 16, 32, 48 or 64) for every query head of the group.
+    const uint32_t hs4 = head_size / 4;
+    const uint32_t hs4p = hs4 <= 16 ? 16 : hs4 <= 32 ? 32 : hs4 <= 48 ? 48 : 64;
     const uint64_t slots = num_rg * p.recs_per_rg * p.group;
     p.counters_offset = 0;
     p.acc_offset = (num_rg * num_seqs * sizeof(uint32_t) + 255) / 256 * 256;
-    p.ml_offset = p.acc_offset + (slots * head_size * sizeof(float) + 255) / 256 * 256;
+    p.ml_offset = p.acc_offset + (slots * 4 * hs4p * sizeof(float) + 255) / 256 * 256;
     p.bytes = max_positions > static_cast<uint32_t>(kChunk) ? p.ml_offset + slots * 2 * sizeof(float) : 0;
     return p;
 }

@@ -176,14 +176,40 @@ __device__ __forceinline__ uint32_t position_at(const DecodeArgs& a, uint32_t s,
     return VIS ? a.visible_pos[static_cast<uint64_t>(s) * a.vis_stride + idx] : idx;
 }
 
-// Device-coherent (agent scope) accesses for data handed between wavefronts
-// that may run on different XCDs: they bypass the non-coherent L2 copies, so
-// no whole-cache write-back or invalidation is needed.
-__device__ __forceinline__ void coherent_store(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-coherent (agent scope, "sc1") 16- and 8-byte accesses for the
+// partial records handed between wavefronts that may run on different XCDs:
+// they bypass the XCD's non-coherent L2 copies, so no whole-cache write-back
+// or invalidation is needed.  A record is laid out in lane order, so each
+// store or load instruction covers whole contiguous lines.  The loads wait
+// for their own completion inside the same asm block.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void coherent_store4(float* p, f32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
-__device__ __forceinline__ float coherent_load(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void coherent_store2(float* p, f32x2 v) {
+    asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+// Waits for every outstanding vector memory operation of the wavefront.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+// Four records' 16-byte values and (max, sum) pairs, loaded together.
+__device__ __forceinline__ void coherent_load4x4(const float* p0, const float* p1, const float* p2, const float* p3,
+                                                 const float* q0, const float* q1, const float* q2, const float* q3,
+                                                 f32x4& v0, f32x4& v1, f32x4& v2, f32x4& v3,
+                                                 f32x2& w0, f32x2& w1, f32x2& w2, f32x2& w3) {
+    asm volatile(
+        "global_load_dwordx4 %0, %8, off sc1\n\t"
+        "global_load_dwordx4 %1, %9, off sc1\n\t"
+        "global_load_dwordx4 %2, %10, off sc1\n\t"
+        "global_load_dwordx4 %3, %11, off sc1\n\t"
+        "global_load_dwordx2 %4, %12, off sc1\n\t"
+        "global_load_dwordx2 %5, %13, off sc1\n\t"
+        "global_load_dwordx2 %6, %14, off sc1\n\t"
+        "global_load_dwordx2 %7, %15, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+        : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(q0), "v"(q1), "v"(q2), "v"(q3)
+        : "memory");
 }
 
 // Zero output rows of sequences [s_begin, s_end) for query heads h0 .. h0+nh-1.
@@ -267,6 +293,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
     constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
     constexpr int NCW = HS4P / 16;             // V code words per lane and row
     constexpr int G = 4 * NHS;
+    constexpr uint64_t kRecFloats = static_cast<uint64_t>(NHS) * NCW * kWave * 4;   // floats per partial record (= G * 4 * HS4P)
     constexpr int QD = NKB * 64;               // padded q row length
     constexpr int WPT_MAX = HS4P + 1;
     constexpr int NU = (kChunk * WPT_MAX + 4 * kWave - 1) / (4 * kWave);   // 16-byte slots per lane
@@ -729,47 +756,56 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
     };
 
     // Combine the nrec records of sequence ms (waves jf .. jf+nrec-1) into its
-    // output rows.  Lane items are (head, 4 dims); for each item every
-    // record's (max, sum, 4 dims) is loaded in one batch of independent
-    // loads (8 records at a time), so a typical combine is one memory round
-    // trip.  Running max and rescaling as in the online softmax.
+    // output rows.  Each lane combines, for each of its (head, 4 dims) items
+    // in the records' lane-order layout, four records per batch of
+    // independent loads (typically a single memory round trip), with a
+    // running max and rescaling as in the online softmax.
     auto merge = [&](uint32_t ms, uint32_t jf, uint32_t nrec) __attribute__((always_inline)) {
         const uint64_t row_sh = static_cast<uint64_t>(ms) * a.num_heads;
-        const uint64_t ml0 = (static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf) * G;   // record 0, head 0
-        for (uint32_t p = lane; p < nh * hs4; p += kWave) {
-            const uint32_t hh = p / hs4, word = p % hs4;
-            float M = -INFINITY, L = 0.0f;
-            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (uint32_t i0 = 0; i0 < nrec; i0 += 8) {
-                float mi[8], li[8];
-                float4 vi[8];
+        const uint64_t rec0 = static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf;      // record of wave jf
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const uint32_t i = min(i0 + k, nrec - 1);
-                    const uint64_t slot = ml0 + static_cast<uint64_t>(i) * G + hh;
-                    const float* pa_ = a.part_acc + slot * hs + 4 * word;
-                    mi[k] = coherent_load(a.part_ml + 2 * slot);
-                    li[k] = coherent_load(a.part_ml + 2 * slot + 1);
-                    vi[k] = make_float4(coherent_load(pa_), coherent_load(pa_ + 1), coherent_load(pa_ + 2),
-                                        coherent_load(pa_ + 3));
+        for (int hset = 0; hset < NHS; ++hset) {
+            const uint32_t hh = 4 * hset + g;
+#pragma unroll
+            for (int cw = 0; cw < NCW; ++cw) {
+                const uint32_t word = NCW * r + cw;
+                const uint32_t unit = 4 * ((hset * NCW + cw) * kWave + lane);
+                float M = -INFINITY, L = 0.0f;
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+                for (uint32_t i0 = 0; i0 < nrec; i0 += 4) {
+                    const float* pv[4];
+                    const float* pm[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint64_t rec = rec0 + min(i0 + k, nrec - 1);
+                        pv[k] = a.part_acc + rec * kRecFloats + unit;
+                        pm[k] = a.part_ml + 2 * (rec * G + hh);
+                    }
+                    f32x4 v[4];
+                    f32x2 ml[4];
+                    coherent_load4x4(pv[0], pv[1], pv[2], pv[3], pm[0], pm[1], pm[2], pm[3],
+                                     v[0], v[1], v[2], v[3], ml[0], ml[1], ml[2], ml[3]);
+                    float bm = M;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (i0 + k < nrec) bm = fmaxf(bm, ml[k].x);
+                    const float sc = exp2f(M - bm);
+                    L *= sc;
+                    o *= sc;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float w = i0 + k < nrec ? exp2f(ml[k].x - bm) : 0.0f;
+                        L += w * ml[k].y;
+                        o += w * v[k];
+                    }
+                    M = bm;
                 }
-                float bm = M;
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (i0 + k < nrec) bm = fmaxf(bm, mi[k]);
-                const float sc = exp2f(M - bm);
-                L *= sc; o.x *= sc; o.y *= sc; o.z *= sc; o.w *= sc;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float w = i0 + k < nrec ? exp2f(mi[k] - bm) : 0.0f;
-                    L += w * li[k];
-                    o.x += w * vi[k].x; o.y += w * vi[k].y; o.z += w * vi[k].z; o.w += w * vi[k].w;
+                if (hh < nh && word < hs4) {
+                    const float inv = 1.0f / L;
+                    *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) =
+                        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
                 }
-                M = bm;
             }
-            const float inv = 1.0f / L;
-            *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) =
-                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
         }
     };
 
@@ -788,27 +824,21 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
 #pragma unroll
         for (int hset = 0; hset < NHS; ++hset) {
             const uint32_t hh = 4 * hset + g;
-            if (hh >= nh) continue;
 #pragma unroll
             for (int cw = 0; cw < NCW; ++cw) {
                 const uint32_t word = NCW * r + cw;
-                if (word >= hs4) continue;
                 float4 v = make_float4(acc[hset][cw][0], acc[hset][cw][1], acc[hset][cw][2], acc[hset][cw][3]);
                 if (nrec == 1) {
+                    if (hh >= nh || word >= hs4) continue;
                     const float inv = 1.0f / l_run[hset];
                     v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
                     *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) = v;
                 } else {
-                    const uint64_t slot = (rec0 + j) * G + hh;
-                    float* pa_ = a.part_acc + slot * hs + 4 * word;
-                    coherent_store(pa_, v.x);
-                    coherent_store(pa_ + 1, v.y);
-                    coherent_store(pa_ + 2, v.z);
-                    coherent_store(pa_ + 3, v.w);
-                    if (word == 0) {
-                        coherent_store(a.part_ml + 2 * slot, m_run[hset]);
-                        coherent_store(a.part_ml + 2 * slot + 1, l_run[hset]);
-                    }
+                    // record layout: [head set][column word][lane] 16-byte units
+                    float* pa_ = a.part_acc + (rec0 + j) * kRecFloats + 4 * ((hset * NCW + cw) * kWave + lane);
+                    coherent_store4(pa_, f32x4{v.x, v.y, v.z, v.w});
+                    if (cw == 0 && r == 0)
+                        coherent_store2(a.part_ml + 2 * ((rec0 + j) * G + hh), f32x2{m_run[hset], l_run[hset]});
                 }
             }
         }
@@ -817,7 +847,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
         // The record was written with device-coherent stores; once they have
         // completed, count this wave in.  No cache maintenance is needed (a
         // device-scope fence would write back and invalidate the whole L2).
-        __builtin_amdgcn_s_waitcnt(0);
+        wait_vmem();
         uint32_t prev = 0;
         if (lane == 0)
             prev = __hip_atomic_fetch_add(a.counters + static_cast<uint64_t>(rg) * a.num_seqs + m.s, 1u,
