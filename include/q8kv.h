@@ -60,8 +60,9 @@ typedef enum {
  *   key_cache,   u32 device caches [num_blocks, num_kv_heads, block_size,
  *   value_cache  head_size/4 + 1], written at row (slot/block_size, h,
  *                slot%block_size) for every non-pad slot.
- *   slot_mapping u32 [num_tokens]; Q8_PAD_SLOT skips the token entirely
- *                (nothing read, nothing written).
+ *   slot_mapping u32 [num_tokens]; Q8_PAD_SLOT skips the token: nothing is
+ *                written for it (its key/value rows may still be read, so
+ *                they must be addressable).
  *
  * Rounding: every step is one IEEE binary32 operation with round-to-nearest,
  * and the round() of the page is round-half-even.  The output is bit-exact.

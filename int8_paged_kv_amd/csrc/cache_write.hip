@@ -4,7 +4,8 @@
 // head) and for K then V, amax = max|x| (from 0), inv = amax > 0 ? 127/amax : 0,
 // code = clamp(round(x * inv), -127, 127) packed four per u32 word with element
 // 4w+l in byte l, then one word with the bits of amax/127 (1.0 when amax == 0).
-// A pad slot (0xFFFFFFFF) skips the token.  round() is round-half-even here.
+// A pad slot (0xFFFFFFFF) skips the token: nothing is written for it (its
+// source rows may be read).  round() is round-half-even here.
 //
 // MI355X mapping: one wavefront per (token, kv head).  When head_size <= 128
 // the two 32-lane halves quantize K and V side by side; otherwise the whole
@@ -29,12 +30,11 @@ __device__ __forceinline__ uint32_t pack_code(float x, float inv, uint32_t lane_
     return (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8u * lane_byte);
 }
 
-// Packs one vector: lanes [0, width) of the group cooperate; lane w owns word w.
+// Packs one vector already loaded as x (lane w owns word w of it): lanes
+// [0, width) of the group cooperate.
 template <int WIDTH>
-__device__ __forceinline__ void pack_vector(const float* src, uint32_t* dst, uint32_t hs4,
-                                            uint32_t w, bool vec4) {
+__device__ __forceinline__ void pack_vector(float4 x, uint32_t* dst, uint32_t hs4, uint32_t w) {
     const bool active = w < hs4;
-    float4 x = active ? load4(src + 4 * w, vec4) : make_float4(0.f, 0.f, 0.f, 0.f);
     float amax = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
 #pragma unroll
     for (int off = WIDTH / 2; off > 0; off >>= 1)
@@ -58,20 +58,32 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool
     if (pair >= static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads) return;
     const uint32_t t = static_cast<uint32_t>(pair / a.num_kv_heads);
     const uint32_t h = static_cast<uint32_t>(pair % a.num_kv_heads);
+    const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
+    const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
+    const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
+    // The source rows are loaded together with the slot (one memory round
+    // trip instead of two); a pad token's rows may thus be read, but nothing
+    // is written for it.
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    if (HALF) {
+        const uint32_t w = lane & 31;
+        if (w < hs4) x0 = load4((lane >= 32 ? vsrc : ksrc) + 4 * w, vec4);
+    } else {
+        if (lane < hs4) {
+            x0 = load4(ksrc + 4 * lane, vec4);
+            x1 = load4(vsrc + 4 * lane, vec4);
+        }
+    }
     const uint32_t slot = a.slot_mapping[t];
     if (slot == kPadSlot) return;
-    const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
     const uint64_t block = slot / a.block_size, off = slot % a.block_size;
     if (block >= a.num_blocks) return;   // out of contract; skipped rather than written out of bounds
     const uint64_t dst = ((block * a.num_kv_heads + h) * a.block_size + off) * wpt;
-    const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
-    const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
     if (HALF) {
-        const bool is_v = lane >= 32;
-        pack_vector<32>(is_v ? vsrc : ksrc, (is_v ? a.value_cache : a.key_cache) + dst, hs4, lane & 31, vec4);
+        pack_vector<32>(x0, (lane >= 32 ? a.value_cache : a.key_cache) + dst, hs4, lane & 31);
     } else {
-        pack_vector<64>(ksrc, a.key_cache + dst, hs4, lane, vec4);
-        pack_vector<64>(vsrc, a.value_cache + dst, hs4, lane, vec4);
+        pack_vector<64>(x0, a.key_cache + dst, hs4, lane);
+        pack_vector<64>(x1, a.value_cache + dst, hs4, lane);
     }
 }
 
