@@ -263,8 +263,8 @@ __device__ void locate_chunk(const DecodeArgs& a, uint32_t lane, uint32_t x, uin
     }
 }
 
-// Wave (of the W covering the C chunks of a row group) whose range holds chunk
-// x: wave j covers [floor(j*C/W), floor((j+1)*C/W)).
+// Wave (of the W covering the C cost units of a row group) whose range holds
+// unit x: wave j covers [floor(j*C/W), floor((j+1)*C/W)).
 __device__ __forceinline__ uint32_t wave_of_chunk(uint32_t x, uint32_t C, uint32_t W) {
     return static_cast<uint32_t>(((static_cast<uint64_t>(x) + 1) * W - 1) / C);
 }
@@ -335,21 +335,36 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
     const uint32_t grp = rg / a.num_kv_heads;
 
     // ---- this wave's chunk range [x0, x1) of the row group's chunk sequence ----
-    // Up to 64 sequences: one load and one scan give the total, the range and
-    // the sequence holding its first chunk.
+    // The waves split the row group's work into equal contiguous ranges of
+    // cost units.  A chunk costs one unit.  Starting a new sequence inside a
+    // range costs about as much again (closing the previous sequence's piece
+    // and forming the new q), so with at least two units per wave and up to
+    // 64 sequences each non-empty sequence also gets one unit before its first
+    // chunk; otherwise the units are the chunks alone.  Every range then holds
+    // at least one chunk.
+    // Up to 64 sequences: one load and one scan give every sequence's chunk
+    // count and offsets, kept in lane s.
     const bool one_window = a.num_seqs <= static_cast<uint32_t>(kWave);
-    uint32_t C, win_np = 0, win_nc = 0, win_incl = 0;
+    uint32_t C, U, win_np = 0, win_nc = 0, win_incl = 0, win_cinc = 0;
+    bool weighted = false;
     if (one_window) {
         win_np = lane < a.num_seqs ? positions_of<VIS>(a, lane) : 0u;
         win_nc = (win_np + kChunk - 1) / kChunk;
         win_incl = wave_incl_scan(win_nc, lane);
-        C = lane_value(win_incl, kWave - 1);
+        C = uniform(lane_value(win_incl, kWave - 1));
+        const uint64_t ne = __ballot(win_np > 0);
+        const uint32_t sne = static_cast<uint32_t>(__builtin_popcountll(ne));
+        weighted = C + sne >= 2 * c.waves_per_rg;
+        U = weighted ? C + sne : C;
+        const uint64_t upto = lane == kWave - 1 ? ~0ull : (2ull << lane) - 1;
+        win_cinc = win_incl + (weighted ? static_cast<uint32_t>(__builtin_popcountll(ne & upto)) : 0u);
     } else {
         uint32_t unused;
         chunk_totals<VIS>(a, lane, 0, C, unused);
+        C = uniform(C);
+        U = C;
     }
-    C = uniform(C);
-    const uint32_t W = min(c.waves_per_rg, C);
+    const uint32_t W = weighted ? c.waves_per_rg : min(c.waves_per_rg, C);
     const uint32_t n_rep = a.num_heads / a.num_kv_heads;
     const uint32_t h0 = kvh * n_rep + grp * G;
     const uint32_t nh = min(static_cast<uint32_t>(G), n_rep - grp * G);
@@ -357,19 +372,34 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
         if (C == 0 && j == 0) zero_rows(a, lane, 0, a.num_seqs, h0, nh);
         return;
     }
-    const uint32_t x0 = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j) * C / W));
-    const uint32_t x1 = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j + 1) * C / W));
+    // First chunk whose cost index is at least u (u < U), its sequence, the
+    // chunks before that sequence and its positions.  Cost index of chunk i of
+    // sequence s: the units of the sequences before s, plus one when
+    // weighted, plus i.
+    auto chunk_at_cost = [&](uint32_t u, uint32_t& s_out, uint32_t& before_out, uint32_t& np_out) __attribute__((always_inline)) -> uint32_t {
+        if (one_window) {
+            const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(__ballot(win_cinc > u)));
+            s_out = l;
+            before_out = lane_value(win_incl - win_nc, l);
+            np_out = lane_value(win_np, l);
+            const uint32_t cf = lane_value(win_cinc - win_nc, l);     // cost index of its first chunk
+            return before_out + (u > cf ? u - cf : 0u);
+        }
+        locate_chunk<VIS>(a, lane, u, s_out, before_out);
+        np_out = 0;
+        return u;
+    };
+    const uint32_t lo = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j) * U / W));
+    const uint32_t hi = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j + 1) * U / W));
+    uint32_t s0, p0c, np0, s1, p1c, np1;
+    const uint32_t x0 = uniform(chunk_at_cost(lo, s0, p0c, np0));
+    const uint32_t x1 = hi >= U ? C : uniform(chunk_at_cost(hi, s1, p1c, np1));
     const uint32_t n = x1 - x0;
-    uint32_t s0, p0c, np0 = 0;
-    if (one_window) {
-        const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(__ballot(win_incl > x0)));
-        s0 = l;
-        p0c = lane_value(win_incl - win_nc, l);
-        np0 = lane_value(win_np, l);
-    } else {
-        locate_chunk<VIS>(a, lane, x0, s0, p0c);
-    }
-    if (uniform(s0) >= a.num_seqs) return;    // unreachable for x0 < C
+    if (uniform(s0) >= a.num_seqs || n == 0) return;    // unreachable: every range holds a chunk
+    // Cost index of the first chunk of the sequence at cursor state (s, before).
+    auto first_cost = [&](uint32_t s_, uint32_t before_) __attribute__((always_inline)) -> uint32_t {
+        return one_window ? lane_value(win_cinc - win_nc, s_) : before_;
+    };
 
     const uint32_t hs = a.head_size, hs4 = EXACT ? HS4P : hs / 4, wpt = hs4 + 1;
     const uint64_t kv_stride = static_cast<uint64_t>(a.num_kv_heads) * a.block_size * wpt;  // words per block
@@ -402,7 +432,22 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
             }
         }
     };
-    if (j == 0) zero_rows(a, lane, 0, cur.s, h0, nh);
+    // A range that starts a sequence zeroes the empty sequences just before
+    // it (those after the previous non-empty one); empty sequences between two
+    // sequences of one range are zeroed as the cursor passes them, and those
+    // after the last chunk by the last wave.
+    if (cur.ci == 0) {
+        uint32_t first;
+        if (one_window) {
+            const uint64_t below = cur.s >= 64u ? ~0ull : ((1ull << cur.s) - 1);
+            const uint64_t ne = __ballot(win_np > 0) & below;
+            first = ne ? 64u - static_cast<uint32_t>(__builtin_clzll(ne)) : 0u;
+        } else {
+            first = cur.s;
+            while (first > 0 && uniform(positions_of<VIS>(a, first - 1)) == 0) --first;
+        }
+        if (first < cur.s) zero_rows(a, lane, first, cur.s, h0, nh);
+    }
 
     // ---- chunk metadata (uniform except the block id of segment `lane`) ----
     // info: bits 0-6 valid positions (0 for a chunk past the wave's range),
@@ -429,8 +474,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
             }
         }
         const uint32_t nc = (cur.npos + kChunk - 1) / kChunk;
-        m.jf = wave_of_chunk(cur.before, C, W);
-        const uint32_t nrec = wave_of_chunk(cur.before + nc - 1, C, W) - m.jf + 1;
+        const uint32_t cf = first_cost(cur.s, cur.before);
+        m.jf = wave_of_chunk(cf, U, W);
+        const uint32_t nrec = wave_of_chunk(cf + nc - 1, U, W) - m.jf + 1;
         m.info = nv | (tiled << 7) | (nrec << 8);
         const uint32_t k = min(lane, nseg - 1);
         uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(kChunk) ? k : 0u);

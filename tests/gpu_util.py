@@ -19,6 +19,12 @@ def f32_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
 
 
+def nan_out(S: int, H: int, hs: int) -> torch.Tensor:
+    """Output buffer filled with NaN, so a row the decode never writes fails
+    the comparison instead of passing on memory that happens to be zero."""
+    return torch.full((S, H, hs), float("nan"), dtype=torch.float32, device="cuda:0")
+
+
 def u32_host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy().view(np.uint32)
 
@@ -68,6 +74,7 @@ class Filled:
     def decode_gpu(self, **kw):
         from int8_paged_kv_amd import q8_paged_decode
         w = self.w
+        kw.setdefault("out", nan_out(w.num_seqs, w.num_heads, w.head_size))
         out = q8_paged_decode(self.q_d, self.kc_d, self.vc_d, self.bt_d, self.cl_d, w.scale, w.num_kv_heads,
                               w.block_size, max_context_len=w.max_context_len, visible_pos=self.vis_d,
                               num_visible=self.nvis_d, **kw)
@@ -126,6 +133,7 @@ class RandomCase:
     def gpu(self, max_context_len=None, vis=None, nvis=None, **kw):
         from int8_paged_kv_amd import q8_paged_decode
         mcl = int(self.lens.max()) if max_context_len is None else max_context_len
+        kw.setdefault("out", nan_out(self.S, self.H, self.hs))
         out = q8_paged_decode(self.q_d, self.kc_d, self.vc_d, self.bt_d, self.cl_d, self.scale, self.Hkv,
                               self.bs, max_context_len=mcl,
                               visible_pos=None if vis is None else u32_dev(vis),

@@ -66,6 +66,18 @@ def test_wavefront_range_boundaries(oracle_mod, decode_waves, waves):
     assert_close(c.gpu(), c.oracle(oracle_mod), "waves %d" % waves)
 
 
+@pytest.mark.parametrize("waves", [2, 3, 5, 8, 64, 4096])
+def test_empty_sequences_at_range_boundaries(oracle_mod, decode_waves, waves):
+    """Empty sequences between two non-empty ones whose chunks fall in
+    different wavefronts' ranges, at the start, and at the end: every one of
+    them gets zero rows (the output starts as NaN)."""
+    from gpu_util import RandomCase, assert_close
+    lens = [0, 64, 0, 0, 64, 0, 130, 0, 1, 0, 0, 64, 0]
+    decode_waves(waves)
+    c = RandomCase(oracle_mod, 90 + waves, len(lens), 8, 2, 128, 16, lens)
+    assert_close(c.gpu(), c.oracle(oracle_mod), "waves %d" % waves)
+
+
 def test_context_clamp_and_q_stride(oracle_mod):
     from gpu_util import RandomCase, assert_close
     c = RandomCase(oracle_mod, 21, 3, 8, 2, 128, 16, [500, 90, 260], q_pad=24)
