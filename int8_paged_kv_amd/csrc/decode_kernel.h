@@ -66,12 +66,13 @@ __device__ __forceinline__ uint32_t to_digits(int32_t n) {
     return (static_cast<uint32_t>(n) + kDigitBias) ^ kDigitBias;
 }
 
-// Exact value of sum_k d[k] * 256^k for int32 digit sums |d[k]| < 2^22.
-__device__ __forceinline__ double combine_digits(i32x4 d) {
-    const int32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3];
-    const int32_t lo = d0 + d1 * 256;
-    const int32_t hi = d2 + d3 * 256;
-    return static_cast<double>(hi) * 65536.0 + static_cast<double>(lo);
+// sum_k d[k] * 256^k for int32 digit sums |d[k]| < 2^22, rounded to binary32:
+// the two halves are exact int32 values; each conversion and the final fma
+// round once, so the result is within 2^-23 relative of the exact sum.
+__device__ __forceinline__ float combine_digits(i32x4 d) {
+    const int32_t lo = d[0] + d[1] * 256;
+    const int32_t hi = d[2] + d[3] * 256;
+    return fmaf(static_cast<float>(hi), 65536.0f, static_cast<float>(lo));
 }
 
 // v_perm_b32: byte i of the result is byte sel_i of the 8-byte value (a:b),
@@ -289,7 +290,7 @@ __device__ __forceinline__ uint32_t wave_of_chunk(uint32_t x, uint32_t C, uint32
 // plus SEGR/4 trailing 16-byte units: every full slot then loads from one
 // segment with a scalar base address and a fixed per-lane offset.
 template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED, int SEGR>
-__global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDepth == 1) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
+__global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
     constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
     constexpr int NCW = HS4P / 16;             // V code words per lane and row
     constexpr int G = 4 * NHS;
@@ -311,7 +312,6 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
         uint32_t kt, vt;        // EXACT generic layout: one 4-byte tail slot per lane
         u32x4 k4, v4;           // FAST layout: the segments' trailing units (lanes 0-15)
     };
-    constexpr int DEPTH = (HS4P <= 32 && NHS == 1) ? kPrefetchDepth : 1;  // chunks loaded ahead
 
     // Per-wavefront LDS regions: the wavefronts of a workgroup are independent.
     __shared__ __align__(16) uint32_t sK_[kWavesPerGroup][NU * 4 * kWave];   // also stages q rows at sequence changes
@@ -323,7 +323,6 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
     uint32_t* const sV = sV_[wid];
     uint32_t* const sA = sA_[wid];
     int* const sEq = sEq_[wid];
-    float* const sQ = reinterpret_cast<float*>(sK);
 
     const uint32_t lane = threadIdx.x % kWave;
     const uint32_t r = lane & 15, g = lane >> 4;
@@ -410,10 +409,17 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
     // ---- cursor over the chunk sequence (wave-uniform) ----
     struct Cursor {
         uint32_t s, ci, npos, before;    // sequence, chunk index in it, its positions, chunks before it
+        uint32_t jf, nrec;               // first wave sharing the sequence, and their number
     };
-    Cursor cur{uniform(s0), 0, 0, uniform(p0c)};
+    Cursor cur{uniform(s0), 0, 0, uniform(p0c), 0, 0};
     cur.ci = x0 - cur.before;
     cur.npos = one_window ? uniform(np0) : uniform(positions_of<VIS>(a, cur.s));
+    auto share = [&]() __attribute__((always_inline)) {
+        const uint32_t cf = first_cost(cur.s, cur.before);
+        cur.jf = wave_of_chunk(cf, U, W);
+        cur.nrec = wave_of_chunk(cf + (cur.npos + kChunk - 1) / kChunk - 1, U, W) - cur.jf + 1;
+    };
+    share();
     // Sequences with no positions get zero rows.  Each is written by exactly
     // one wave of the row group: the one whose range it falls inside, wave 0
     // for those before the first chunk, the last wave for those after it.
@@ -430,6 +436,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
                 if (cur.npos != 0) break;
                 zero_rows(a, lane, cur.s, cur.s + 1, h0, nh);
             }
+            if (cur.s < a.num_seqs) share();
         }
     };
     // A range that starts a sequence zeroes the empty sequences just before
@@ -473,11 +480,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
                 tiled = (m.p0 % kChunk == 0) && (pl - m.p0 == nv - 1) ? 1u : 0u;
             }
         }
-        const uint32_t nc = (cur.npos + kChunk - 1) / kChunk;
-        const uint32_t cf = first_cost(cur.s, cur.before);
-        m.jf = wave_of_chunk(cf, U, W);
-        const uint32_t nrec = wave_of_chunk(cf + nc - 1, U, W) - m.jf + 1;
-        m.info = nv | (tiled << 7) | (nrec << 8);
+        m.jf = cur.jf;
+        m.info = nv | (tiled << 7) | (cur.nrec << 8);
         const uint32_t k = min(lane, nseg - 1);
         uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(kChunk) ? k : 0u);
         jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
@@ -642,40 +646,60 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
             qv[t] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
+    // Digits of the staged q rows.  Each head's exponent comes from its
+    // largest |q|: the lanes write per-slot maxima to LDS and the 16 lanes of a
+    // head reduce their share.  Then every lane converts its own staged values
+    // once and scatters each value's four digits to the lanes whose MFMA rows
+    // hold them, through LDS in the operand layout [set][k-block][lane][w].
     auto q_finish = [&]() __attribute__((always_inline)) {
+        uint32_t* const sDig = sK;
+        float* const sMax = reinterpret_cast<float*>(sK) + NHS * NKB * 256;
 #pragma unroll
-        for (int t = 0; t < QF; ++t) *reinterpret_cast<float4*>(&sQ[4 * (lane + kWave * t)]) = qv[t];
-        wave_sync();
-#pragma unroll
-        for (int hset = 0; hset < NHS; ++hset) {
-            const uint32_t hq = 4 * hset + r / 4, dig = r % 4;
-            const float* row = &sQ[hq * QD];
-            float amax = 0.0f;
-            for (int d = 0; d < QD; d += 4) {
-                const float4 v = *reinterpret_cast<const float4*>(row + d);
-                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-            }
-            const int eq = amax > 0.0f ? 30 - exponent_bound(amax) : 0;    // |q * 2^eq| < 2^30
-            if (g == 0 && dig == 0) sEq[hq] = eq;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                uint32_t packed[4];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float4 v = *reinterpret_cast<const float4*>(row + 64 * kb + 16 * g + 4 * w);
-                    const uint32_t b0 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.x, eq)))) >> (8 * dig)) & 0xFFu;
-                    const uint32_t b1 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.y, eq)))) >> (8 * dig)) & 0xFFu;
-                    const uint32_t b2 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.z, eq)))) >> (8 * dig)) & 0xFFu;
-                    const uint32_t b3 = (to_digits(static_cast<int32_t>(rintf(ldexpf(v.w, eq)))) >> (8 * dig)) & 0xFFu;
-                    packed[w] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-                }
-                qa[hset][kb] = i32x4{static_cast<int32_t>(packed[0]), static_cast<int32_t>(packed[1]),
-                                     static_cast<int32_t>(packed[2]), static_cast<int32_t>(packed[3])};
-            }
+        for (int t = 0; t < QF; ++t) {
+            const float4 v = qv[t];
+            sMax[lane + kWave * t] = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
         }
         wave_sync();
 #pragma unroll
-        for (int hset = 0; hset < NHS; ++hset) eq_out[hset] = sEq[4 * hset + g];
+        for (int hset = 0; hset < NHS; ++hset) {
+            const uint32_t h = 4 * hset + r / 4;
+            const uint32_t i = 4 * g + r % 4;                 // this lane's share of the head's 16*NKB maxima
+            float m = 0.0f;
+#pragma unroll
+            for (int k = 0; k < NKB; ++k) m = fmaxf(m, sMax[h * 16 * NKB + i * NKB + k]);
+            m = fmaxf(m, __shfl_xor(m, 1, 64));
+            m = fmaxf(m, __shfl_xor(m, 2, 64));
+            m = fmaxf(m, __shfl_xor(m, 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            if (g == 0 && r % 4 == 0) sEq[h] = m > 0.0f ? 30 - exponent_bound(m) : 0;   // |q * 2^eq| < 2^30
+        }
+        wave_sync();
+#pragma unroll
+        for (int t = 0; t < QF; ++t) {
+            const uint32_t f = lane + kWave * t;              // staged float4 index: head f / (16*NKB)
+            const uint32_t hi = f / (16 * NKB), d0 = 4 * (f % (16 * NKB));
+            const int eq = sEq[hi];
+            const float4 v = qv[t];
+            const uint32_t dw[4] = {to_digits(static_cast<int32_t>(rintf(ldexpf(v.x, eq)))),
+                                    to_digits(static_cast<int32_t>(rintf(ldexpf(v.y, eq)))),
+                                    to_digits(static_cast<int32_t>(rintf(ldexpf(v.z, eq)))),
+                                    to_digits(static_cast<int32_t>(rintf(ldexpf(v.w, eq))))};
+            uint32_t pk[4];
+            transpose4(dw, pk);                              // byte e of pk[dig] = digit dig of value e
+            const uint32_t kb = d0 / 64, gq = (d0 % 64) / 16, w = (d0 % 16) / 4;
+            const uint32_t base = (((hi / 4) * NKB + kb) * kWave + 16 * gq + 4 * (hi % 4)) * 4 + w;
+#pragma unroll
+            for (int dg = 0; dg < 4; ++dg) sDig[base + 4 * dg] = pk[dg];
+        }
+        wave_sync();
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                qa[hset][kb] = *reinterpret_cast<const i32x4*>(&sDig[((hset * NKB + kb) * kWave + lane) * 4]);
+            eq_out[hset] = sEq[4 * hset + g];
+        }
+        wave_sync();
     };
 
     // Online-softmax state (log2 units) of head 4*hset + g, uniform across the lane's row.
@@ -739,7 +763,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
             float cmax = -INFINITY;
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) {
-                const float zq = ldexpf(static_cast<float>(combine_digits(dsum[hset][tg])), -eq_out[hset]);
+                const float zq = ldexpf(combine_digits(dsum[hset][tg]), -eq_out[hset]);
                 z[tg] = val[tg] ? zq * (ksc[tg] * a.scale_log2) : -INFINITY;
                 cmax = fmaxf(cmax, z[tg]);
             }
@@ -772,7 +796,6 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
 #pragma unroll
         for (int hset = 0; hset < NHS; ++hset)
             pa[hset] = *reinterpret_cast<const i32x4*>(&sA[(hset * 16 + r) * 16 + 4 * g]);
-        const double pscale = ldexp(1.0, -ep);
 #pragma unroll
         for (int cw = 0; cw < NCW; ++cw) {
             uint32_t bj[4][4];      // [byte j][w]: codes of tokens 4g + w + 16*b (byte b)
@@ -795,7 +818,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
 #pragma unroll
                 for (int hset = 0; hset < NHS; ++hset) {
                     const i32x4 d = mfma_i8(pa[hset], b, i32x4{0, 0, 0, 0});
-                    acc[hset][cw][jj] += static_cast<float>(combine_digits(d) * pscale);
+                    acc[hset][cw][jj] += ldexpf(combine_digits(d), -ep);
                 }
             }
         }
@@ -913,10 +936,10 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
     };
 
     // ---- pipeline over the wave's chunks x0 .. x1-1 ----
-    // Step for chunk x (relative index xr): its data sit in registers `kb/vb`;
-    // the next DEPTH-1 chunks are in flight in the other buffer.  The step
-    // stores chunk x to LDS, reads the block ids of chunk x+DEPTH+1, reuses the
-    // registers for chunk x+DEPTH, and processes chunk x.
+    // Step for chunk x (relative index xr): its tiles sit in registers; the
+    // step stores them to LDS, reads the block ids of chunk x+2, issues the
+    // tile loads of chunk x+1 into the freed registers (and the q rows of its
+    // sequence when that changes), and processes chunk x.
     reset();
     // Prologue order: block ids of chunk x0, q of its sequence, chunk x0's
     // tiles, block ids of x0+1; the q digits are formed while tiles arrive.
@@ -928,49 +951,22 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && kPrefetchDep
     if (n > 1) advance();
     mn1 = meta_of(n > 1);
     q_finish();
-    uint32_t q_seq = mc.s;
-    if (DEPTH == 1) {
-        for (uint32_t xr = 0;; ++xr) {
-            if (mc.s != q_seq) { q_finish(); q_seq = mc.s; }   // q of mc.s was staged one step ago
-            store(mc, bA);
-            if (xr + 2 < n) advance();
-            const Meta mn2 = meta_of(xr + 2 < n);
-            issue_data(mn1, bA);
-            q_issue(mn1.s);                                     // q of the next chunk's sequence
-            wave_sync();
-            process(meta_nv(mc));
-            if (xr + 1 == n || mn1.s != mc.s) flush(mc);
-            if (xr + 1 == n) break;
-            wave_sync();
-            mc = mn1;
-            mn1 = mn2;
-        }
-    } else {
-        Buf bB;
-        issue_data(mn1, bB);
-        if (n > 2) advance();
-        Meta mn2 = meta_of(n > 2);
-        auto step = [&](uint32_t xr, Buf& b) __attribute__((always_inline)) -> bool {
-            if (mc.s != q_seq) { q_finish(); q_seq = mc.s; }   // q of mc.s was staged one step ago
-            store(mc, b);
-            if (xr + 3 < n) advance();
-            const Meta mn3 = meta_of(xr + 3 < n);
-            issue_data(mn2, b);
-            q_issue(mn1.s);                                     // q of the next chunk's sequence
-            wave_sync();
-            process(meta_nv(mc));
-            if (xr + 1 == n || mn1.s != mc.s) flush(mc);
-            if (xr + 1 == n) return false;
-            wave_sync();
-            mc = mn1;
-            mn1 = mn2;
-            mn2 = mn3;
-            return true;
-        };
-        for (uint32_t xr = 0;; xr += 2) {
-            if (!step(xr, bA)) break;
-            if (!step(xr + 1, bB)) break;
-        }
+    uint32_t q_seq_prev = mc.s;
+    for (uint32_t xr = 0;; ++xr) {
+        if (xr > 0 && mc.s != q_seq_prev) q_finish();          // q of mc.s was staged one step ago
+        store(mc, bA);
+        if (xr + 2 < n) advance();
+        const Meta mn2 = meta_of(xr + 2 < n);
+        issue_data(mn1, bA);
+        if (mn1.s != mc.s) q_issue(mn1.s);                    // q of the next chunk's sequence
+        wave_sync();
+        process(meta_nv(mc));
+        if (xr + 1 == n || mn1.s != mc.s) flush(mc);
+        if (xr + 1 == n) break;
+        wave_sync();
+        q_seq_prev = mc.s;
+        mc = mn1;
+        mn1 = mn2;
     }
     if (npend > 0) merge(pend_s0, pend_jf0, pend_n0);
     if (npend > 1) merge(pend_s1, pend_jf1, pend_n1);

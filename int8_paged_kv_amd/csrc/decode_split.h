@@ -4,12 +4,6 @@
 
 namespace q8kv {
 
-// Chunks of K/V loaded ahead of use by the split kernel (1 or 2; 2 needs
-// about 66 more VGPRs at head_size 128, so one wavefront per SIMD).
-#ifndef Q8KV_DECODE_DEPTH
-#define Q8KV_DECODE_DEPTH 1
-#endif
-constexpr int kPrefetchDepth = Q8KV_DECODE_DEPTH;
 // Independent wavefronts packed per workgroup (fewer workgroups to dispatch).
 constexpr uint32_t kWavesPerGroup = 4;
 
