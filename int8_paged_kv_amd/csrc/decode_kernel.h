@@ -191,6 +191,16 @@ __device__ __forceinline__ void coherent_store4(float* p, f32x4 v) {
 __device__ __forceinline__ void coherent_store2(float* p, f32x2 v) {
     asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
+// Byte offset of an LDS location (the value M0 takes for LDS-direct loads).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+// LDS-direct 16-byte load: lane l's 16 bytes at g land at LDS byte lds + 16*l.
+// The compiler does not see these loads: the caller waits for them with
+// wait_vmem() before reading the LDS they fill.
+__device__ __forceinline__ void load_lds16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(g), "s"(lds) : "memory", "m0");
+}
 // Waits for every outstanding vector memory operation of the wavefront.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 // Four records' 16-byte values and (max, sum) pairs, loaded together.
@@ -290,7 +300,7 @@ __device__ __forceinline__ uint32_t wave_of_chunk(uint32_t x, uint32_t C, uint32
 // plus SEGR/4 trailing 16-byte units: every full slot then loads from one
 // segment with a scalar base address and a fixed per-lane offset.
 template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED, int SEGR>
-__global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
+__global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
     constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
     constexpr int NCW = HS4P / 16;             // V code words per lane and row
     constexpr int G = 4 * NHS;
@@ -303,24 +313,33 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void de
     constexpr int NF = EXACT ? HS4P / 4 : NU;
     constexpr bool FAST = SEGR > 0;
     static_assert(!FAST || (EXACT && (SEGR * HS4P) % 256 == 0 && SEGR <= kChunk), "segment layout");
+    // Segment loads go straight to LDS (no register staging), double-buffered:
+    // the next chunk lands in one buffer while the other is processed.  Two
+    // buffers of K and V fit for up to 32 code words per row.
+    constexpr bool DMA = FAST && HS4P <= 32;
+    constexpr int NBUF = DMA ? 2 : 1;
     constexpr int FSEG = FAST ? kChunk / SEGR : 1;          // segments per chunk
     constexpr int FS = FAST ? SEGR * HS4P / 256 : 0;         // full slots per segment (FSEG * FS == NF)
     constexpr int FLO = FAST ? SEGR / 4 : 1;                 // trailing 16-byte units per segment
     constexpr int SEG_U4 = FAST ? SEGR * (HS4P + 1) / 4 : 1; // 16-byte units per segment
     struct Buf {
-        u32x4 k[NF], v[NF];
+        u32x4 k[DMA ? 1 : NF], v[DMA ? 1 : NF];
         uint32_t kt, vt;        // EXACT generic layout: one 4-byte tail slot per lane
         u32x4 k4, v4;           // FAST layout: the segments' trailing units (lanes 0-15)
     };
 
     // Per-wavefront LDS regions: the wavefronts of a workgroup are independent.
-    __shared__ __align__(16) uint32_t sK_[kWavesPerGroup][NU * 4 * kWave];   // also stages q rows at sequence changes
-    __shared__ __align__(16) uint32_t sV_[kWavesPerGroup][NU * 4 * kWave];
+    __shared__ __align__(16) uint32_t sK_[kWavesPerGroup][NBUF][NU * 4 * kWave];   // also q-digit scratch at sequence changes
+    __shared__ __align__(16) uint32_t sV_[kWavesPerGroup][NBUF][NU * 4 * kWave];
     __shared__ __align__(16) uint32_t sA_[kWavesPerGroup][NHS * 16 * 16];    // [set][head*4+digit][w]: weight digits
     __shared__ int sEq_[kWavesPerGroup][G];
     const uint32_t wid = uniform(threadIdx.x / kWave);
-    uint32_t* const sK = sK_[wid];
-    uint32_t* const sV = sV_[wid];
+    // sK/sV: the tiles of the chunk being processed; sKn/sVn: where the next
+    // chunk's segments land (the same buffer without LDS-direct loads).
+    uint32_t* sK = sK_[wid][0];
+    uint32_t* sV = sV_[wid][0];
+    uint32_t* sKn = sK_[wid][NBUF - 1];
+    uint32_t* sVn = sV_[wid][NBUF - 1];
     uint32_t* const sA = sA_[wid];
     int* const sEq = sEq_[wid];
 
@@ -490,7 +509,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void de
     };
 
     // ---- tiled chunk loads: 16-byte slot u = lane + 64*i lies in segment u / seg_u4 ----
-    auto issue_data = [&](const Meta& m, Buf& b) __attribute__((always_inline)) {
+    auto issue_data = [&](const Meta& m, Buf& b, uint32_t* dK, uint32_t* dV) __attribute__((always_inline)) {
         if (FAST) {
             // Segment k's tile (block id from lane k) starts at a uniform
             // address; an invalid segment reads the cache's first bytes.
@@ -508,13 +527,26 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void de
                 vb[k] = reinterpret_cast<const char*>(a.value_cache + off);
             }
             const uint32_t lb = lane * 16;
+            if (DMA && nv == 0) return;   // past the range: nothing is stored from this chunk
+            if (DMA) {
+                const uint32_t lk = lds_offset(dK), lv = lds_offset(dV);
 #pragma unroll
-            for (int k = 0; k < FSEG; ++k)
+                for (int k = 0; k < FSEG; ++k)
 #pragma unroll
-                for (int f = 0; f < FS; ++f) {
-                    b.k[k * FS + f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb[k] + lb + f * 1024));
-                    b.v[k * FS + f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb[k] + lb + f * 1024));
-                }
+                    for (int f = 0; f < FS; ++f) {
+                        const uint32_t o = (k * SEG_U4 + f * 64) * 16;
+                        load_lds16(kb[k] + lb + f * 1024, lk + o);
+                        load_lds16(vb[k] + lb + f * 1024, lv + o);
+                    }
+            } else {
+#pragma unroll
+                for (int k = 0; k < FSEG; ++k)
+#pragma unroll
+                    for (int f = 0; f < FS; ++f) {
+                        b.k[k * FS + f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb[k] + lb + f * 1024));
+                        b.v[k * FS + f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb[k] + lb + f * 1024));
+                    }
+            }
             // Trailing units: lane l < 16 takes unit l % FLO of segment l / FLO.
             const uint32_t kk = lane / FLO;
             const char* pk = reinterpret_cast<const char*>(a.key_cache);
@@ -573,15 +605,18 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void de
         }
     };
     auto store = [&](const Meta& m, const Buf& b) __attribute__((always_inline)) {
+        if (DMA) wait_vmem();           // this chunk's LDS-direct segment loads have landed
         if (FAST && meta_tiled(m)) {
+            if (!DMA) {
 #pragma unroll
-            for (int k = 0; k < FSEG; ++k)
+                for (int k = 0; k < FSEG; ++k)
 #pragma unroll
-                for (int f = 0; f < FS; ++f) {
-                    const uint32_t u = k * SEG_U4 + f * 64 + lane;
-                    *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k[k * FS + f];
-                    *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v[k * FS + f];
-                }
+                    for (int f = 0; f < FS; ++f) {
+                        const uint32_t u = k * SEG_U4 + f * 64 + lane;
+                        *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k[k * FS + f];
+                        *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v[k * FS + f];
+                    }
+            }
             if (lane < 16u) {
                 const uint32_t u = (lane / FLO) * SEG_U4 + FS * 64 + lane % FLO;
                 *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k4;
@@ -652,8 +687,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void de
     // once and scatters each value's four digits to the lanes whose MFMA rows
     // hold them, through LDS in the operand layout [set][k-block][lane][w].
     auto q_finish = [&]() __attribute__((always_inline)) {
-        uint32_t* const sDig = sK;
-        float* const sMax = reinterpret_cast<float*>(sK) + NHS * NKB * 256;
+        uint32_t* const sDig = sKn;       // free: the next chunk's loads (if any) go to the other buffer
+        float* const sMax = reinterpret_cast<float*>(sKn) + NHS * NKB * 256;
 #pragma unroll
         for (int t = 0; t < QF; ++t) {
             const float4 v = qv[t];
@@ -946,7 +981,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void de
     Buf bA;
     Meta mc = meta_of(true);
     q_issue(mc.s);
-    issue_data(mc, bA);
+    issue_data(mc, bA, sK, sV);
     Meta mn1;
     if (n > 1) advance();
     mn1 = meta_of(n > 1);
@@ -957,7 +992,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void de
         store(mc, bA);
         if (xr + 2 < n) advance();
         const Meta mn2 = meta_of(xr + 2 < n);
-        issue_data(mn1, bA);
+        issue_data(mn1, bA, sKn, sVn);
         if (mn1.s != mc.s) q_issue(mn1.s);                    // q of the next chunk's sequence
         wave_sync();
         process(meta_nv(mc));
@@ -967,7 +1002,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, HS4P <= 32 ? 2 : 1) void de
         q_seq_prev = mc.s;
         mc = mn1;
         mn1 = mn2;
+        if (DMA) {
+            uint32_t* t = sK; sK = sKn; sKn = t;
+            t = sV; sV = sVn; sVn = t;
+        }
     }
+    if (DMA) wait_vmem();      // no LDS-direct load may still be landing when the wave ends
     if (npend > 0) merge(pend_s0, pend_jf0, pend_n0);
     if (npend > 1) merge(pend_s1, pend_jf1, pend_n1);
     if (j == W - 1) zero_rows(a, lane, mc.s + 1, a.num_seqs, h0, nh);
