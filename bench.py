@@ -3,8 +3,10 @@
 
 One step = the whole hot path on the Llama-3-8B-shaped batch (64 sequences,
 32 query heads, 8 kv heads, head_size 128, block_size 16, context lengths
-uniform in [512, 4096]): q8_cache_write of the 64 new tokens (one per
-sequence) followed by q8_paged_decode over every sequence's full context.
+uniform in [512, 4096]): the 64 new tokens (one per sequence) quantized and
+packed into the caches, and decode attention over every sequence's full
+context, in one launch of q8_decode_step.  The same step as two launches
+(q8_cache_write, then q8_paged_decode) is timed alongside for reference.
 
 Inputs are resident in HBM before timing.  The step rotates over several
 layer caches (copies of the filled cache at different addresses), as a model's
@@ -44,6 +46,8 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--hot", action="store_true", help="also time back-to-back steps on one cache")
+    p.add_argument("--no-reference", action="store_true",
+                   help="skip timing the two-launch reference (cache write, then decode)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB five times (the known-size "
                         "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -105,7 +109,8 @@ def main():
         sys.exit(2)
 
     import torch
-    from int8_paged_kv_amd import q8_cache_write, q8_paged_decode, q8_paged_decode_workspace_bytes, load_library
+    from int8_paged_kv_amd import (q8_cache_write, q8_decode_step, q8_paged_decode, q8_paged_decode_workspace_bytes,
+                                   load_library)
     from int8_paged_kv_amd import workloads as wl
 
     load_library()
@@ -145,13 +150,18 @@ def main():
         kc, vc = layers[i % len(layers)]
         if ev is not None:
             ev[0].record()
-        q8_cache_write(sk, sv, kc, vc, ss, Hkv, hs, w.block_size)
+        q8_decode_step(q, sk, sv, kc, vc, bt, cl, w.scale, Hkv, w.block_size, mcl, out=out, workspace=ws)
         if ev is not None:
             ev[1].record()
+
+    def step_two_launch(i, ev):
+        kc, vc = layers[i % len(layers)]
+        ev[0].record()
+        q8_cache_write(sk, sv, kc, vc, ss, Hkv, hs, w.block_size)
+        ev[1].record()
         q8_paged_decode(q, kc, vc, bt, cl, w.scale, Hkv, w.block_size, max_context_len=mcl,
                         out=out, workspace=ws)
-        if ev is not None:
-            ev[2].record()
+        ev[2].record()
 
     for i in range(args.warmup):
         step(i)
@@ -165,29 +175,43 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    B = w.effective_kv_bytes()
     # ---- per-launch durations with HIP events on the launch stream ----
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    t_write = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3    # us
-    t_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    t_dec = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3     # us, the one step launch
+    # the same step as two launches, for reference
+    reference = None
+    if not args.no_reference:
+        evs2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step_two_launch(i, evs2[i])
+        torch.cuda.synchronize()
+        t_write = np.array([e[0].elapsed_time(e[1]) for e in evs2]) * 1e3
+        t_dec2 = np.array([e[1].elapsed_time(e[2]) for e in evs2]) * 1e3
+        reference = {"cache_write_us_mean": round(float(t_write.mean()), 2),
+                     "decode_us_mean": round(float(t_dec2.mean()), 2),
+                     "decode_effective_GBps": round(B / (float(t_dec2.mean()) * 1e-6) / 1e9, 1),
+                     "tokens": int(step_slots.size)}
 
     hot = None
     if args.hot:
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         for i in range(args.steps):
             step(0, ev[i])
         torch.cuda.synchronize()
-        th = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+        th = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
         hot = {"decode_us_median": float(np.median(th)),
                "effective_GBps": w.effective_kv_bytes() / (np.median(th) * 1e-6) / 1e9}
 
-    B = w.effective_kv_bytes()
+    # algorithmic bytes of the step's cache write: f32 K and V read, packed rows written
+    Bw = int(step_slots.size) * Hkv * (2 * hs * 4 + 2 * (hs + 4)) + 4 * int(step_slots.size)
     step_s = ms_per_step * 1e-3
     value = B / step_s / 1e9
     dec_mean = float(t_dec.mean())
-    achieved = B / (dec_mean * 1e-6) / 1e9
+    achieved = (B + Bw) / (dec_mean * 1e-6) / 1e9
     digest = kernel_sources_digest()
     traffic = read_traffic(digest)
 
@@ -231,7 +255,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "Llama-3-8B-shaped decode step: 64-token q8 cache write + q8 paged decode, "
+        "config": {"workload": "Llama-3-8B-shaped decode step (one launch): 64-token q8 cache append + q8 paged decode, "
                                "S=64 H=32 Hkv=8 hs=128 bs=16 L~U[512,4096] (seed 2), %d rotated layer caches"
                                % len(layers),
                    "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv, "head_size": hs, "block_size": w.block_size,
@@ -239,16 +263,16 @@ def main():
                    "kv_storage": "int8 codes + f32 per-token scale"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(S * H / step_s, 1),
-        "decode": {"us_mean": round(dec_mean, 2), "us_median": round(float(np.median(t_dec)), 2),
+        "step_launch": {"us_mean": round(dec_mean, 2), "us_median": round(float(np.median(t_dec)), 2),
                    "us_p10": round(float(np.percentile(t_dec, 10)), 2),
                    "us_p90": round(float(np.percentile(t_dec, 90)), 2),
                    "effective_GBps": round(achieved, 1),
                    "seq_heads_per_s": round(S * H / (dec_mean * 1e-6), 1)},
-        "cache_write": {"us_mean": round(float(t_write.mean()), 2), "tokens": int(step_slots.size)},
+        "two_launch_reference": reference,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "q8_paged_decode (one launch: decode_split_kernel)",
-                     "algorithmic_bytes_per_launch": B},
+                     "kernel": "q8_decode_step (one launch: decode_split_kernel, appending the step's tokens)",
+                     "algorithmic_bytes_per_launch": B + Bw},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "hot_single_cache": hot,

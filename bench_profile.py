@@ -30,9 +30,9 @@ DECODE_KERNELS = ("decode_split_kernel",)
 WRITE_KERNEL = "cache_write_kernel"
 
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d {d}/trace -o bench -f csv "
-             "-- python3 /root/repo/bench.py --steps 20 --warmup 5 --no-cpu")
+             "-- python3 /root/repo/bench.py --steps 20 --warmup 5 --no-cpu --no-reference")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {c} -d {d}/pmc_{c} -o bench -f csv "
-           "-- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu")
+           "-- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
 COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} -d {d}/copy_{c} -o copy -f csv "
             "-- python3 /root/repo/bench.py --copy-calibration {mib}")
 
@@ -63,7 +63,7 @@ def step_dispatches(cnt, step_grid_of):
     """Counter values of the decode-step launches: the grid the step uses for each kernel."""
     res = {}
     for (name, grid), vals in cnt.items():
-        for k in DECODE_KERNELS + (WRITE_KERNEL,):
+        for k in DECODE_KERNELS:
             if k in name and grid == step_grid_of.get(k):
                 res[k] = (name, grid, vals)
     return res
@@ -104,7 +104,6 @@ def main():
                      min(durs), max(durs), vgpr, agpr, sgpr, lds, scr, tag is not None and len(durs) == n_step))
 
     split_us = mean_of(rows, "decode_split_kernel")
-    write_us = mean_of(rows, "cache_write_kernel")
     eff = bench_trace["config"]["effective_kv_bytes"]
     lines = [
         "# rocprofv3 kernel trace of the decode step, Llama-3-8B-shaped batch",
@@ -115,8 +114,8 @@ def main():
         "# summarised with: python3 bench_profile.py <that -d directory's parent>",
         "#",
         "# kernel_sources_sha256_16: %s" % digest,
-        "# durations in microseconds per dispatch; step = one cache_write launch and one decode launch "
-        "(decode_split_kernel, which also combines shared sequences)",
+        "# durations in microseconds per dispatch; step = one launch of q8_decode_step (decode_split_kernel: "
+        "appends the 64 new tokens, attends, and combines shared sequences)",
         "",
         "%-52s %9s %4s %5s %9s %9s %9s %9s %5s %5s %5s %6s %6s" % (
             "kernel", "grid", "wg", "calls", "mean_us", "median_us", "min_us", "max_us", "vgpr", "agpr", "sgpr",
@@ -128,11 +127,10 @@ def main():
             "  <- step" if r[13] else ""))
     lines += [
         "",
-        "decode per step (decode_split_kernel mean): %.2f us" % split_us,
-        "  effective int8 KV bytes per decode: %d -> %.1f GB/s" % (eff, eff / (split_us * 1e-6) / 1e9),
-        "cache_write (64 tokens) mean: %.2f us" % write_us,
-        "bench.py in the same run (HIP events on the launch stream): decode us_mean %.2f, effective %.1f GB/s" % (
-            bench_trace["decode"]["us_mean"], bench_trace["decode"]["effective_GBps"]),
+        "step launch (decode_split_kernel mean): %.2f us" % split_us,
+        "  effective int8 KV bytes per step: %d -> %.1f GB/s" % (eff, eff / (split_us * 1e-6) / 1e9),
+        "bench.py in the same run (HIP events on the launch stream): step launch us_mean %.2f, effective %.1f GB/s" % (
+            bench_trace["step_launch"]["us_mean"], bench_trace["step_launch"]["effective_GBps"]),
         "",
         "rocprofv3 --stats table (all dispatches of each kernel, fill phase included):",
     ]
@@ -163,14 +161,14 @@ def main():
         raise SystemExit("counter runs and trace run were taken on different kernel sources: %s vs %s"
                          % (pmc_digest, digest))
     per_kernel = {}
-    for k in DECODE_KERNELS + (WRITE_KERNEL,):
+    for k in DECODE_KERNELS:
         rd = statistics.median(pmc["FETCH_SIZE"][k][2]) * 1024.0 * factor["FETCH_SIZE"]
         wr = statistics.median(pmc["WRITE_SIZE"][k][2]) * 1024.0 * factor["WRITE_SIZE"]
         per_kernel[k] = (statistics.median(pmc["FETCH_SIZE"][k][2]), statistics.median(pmc["WRITE_SIZE"][k][2]),
                          rd, wr)
     dec_bytes = sum(per_kernel[k][2] + per_kernel[k][3] for k in DECODE_KERNELS)
     t = [
-        "# HBM traffic of the decode launch, Llama-3-8B-shaped batch",
+        "# HBM traffic of the step launch (append + decode), Llama-3-8B-shaped batch",
         "# (S=64 H=32 Hkv=8 head_size=128 block_size=16, context lengths U[512,4096], seed 2)",
         "#",
         "# commands (from any directory on the GPU machine), one counter per run:",
@@ -188,13 +186,14 @@ def main():
         "#",
         "# per dispatch (median over the step's launches):",
     ]
-    for k in DECODE_KERNELS + (WRITE_KERNEL,):
+    for k in DECODE_KERNELS:
         fk, wk, rd, wr = per_kernel[k]
         t.append("#   %-20s FETCH_SIZE %10.1f KiB -> %12.0f B read, WRITE_SIZE %9.1f KiB -> %11.0f B written" % (
             k, fk, rd, wk, wr))
     t += [
-        "#   algorithmic int8 KV bytes per decode (codes + scale word of every attended row, K and V): %d" % eff,
-        "#   measured decode traffic / algorithmic = %.4f" % (dec_bytes / eff),
+        "#   algorithmic bytes per step: int8 KV (codes + scale word of every attended row, K and V) %d"
+        " + cache append %d" % (eff, bench_trace["roofline"]["algorithmic_bytes_per_launch"] - eff),
+        "#   measured step traffic / algorithmic = %.4f" % (dec_bytes / bench_trace["roofline"]["algorithmic_bytes_per_launch"]),
         "",
         "kernel_sources_sha256_16: %s" % digest,
         "fetch_factor: %.6f" % factor["FETCH_SIZE"],

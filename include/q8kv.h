@@ -143,6 +143,46 @@ q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
                           float scale, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * q8_decode_step -- one decode step in a single launch: every sequence's new K
+ * and V vector is quantized and packed into the caches at the sequence's last
+ * position, and the batch attends over the caches including it.  The result
+ * (cache words and outputs) is that of q8_cache_write of token s at the slot
+ * of position context_lens[s]-1 of sequence s (its block_tables entry, offset
+ * position % block_size), followed by q8_paged_decode in dense mode; the
+ * packing is the "reshape_and_cache_q8.comp" page's, the attention the
+ * "paged_attn_q8.comp" page's.  One launch instead of two: the wavefront that
+ * attends the last chunk of a sequence quantizes the new rows itself, uses them
+ * in place of the rows the cache still held, and writes them to the caches.
+ *
+ *   key, value    f32 new vectors: element d of kv head h of sequence s at
+ *                 key[s*key_stride + h*head_size + d] (resp. value_stride).
+ *   key_cache,    u32 caches, read and written.
+ *   value_cache
+ *   the rest      as q8_paged_decode in dense mode (visible lists are not
+ *                 supported here), including the workspace
+ *                 (q8_paged_decode_workspace_bytes with max_positions =
+ *                 max_context_len).
+ *
+ * Contract on the contents (not checked): the new position's slot is attended
+ * by no other sequence of the call.  A sequence is appended to only when
+ * 1 <= context_lens[s] <= max_context_len and its table covers position
+ * context_lens[s]-1; otherwise nothing is written for it and it attends the
+ * cache as it is.  Errors: those of q8_paged_decode in dense mode, plus
+ * Q8_ERR_NULL for a NULL key or value and Q8_ERR_SHAPE for a stride below
+ * num_kv_heads*head_size.
+ */
+q8_status q8_decode_step(float* out, const float* q, uint32_t q_stride,
+                         const float* key, uint32_t key_stride,
+                         const float* value, uint32_t value_stride,
+                         uint32_t* key_cache, uint32_t* value_cache,
+                         const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                         const uint32_t* context_lens, uint32_t max_context_len,
+                         uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                         uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                         float scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* hipError_t code behind the calling thread's last Q8_ERR_HIP (0 if none). */
 int q8_last_hip_error(void);
 

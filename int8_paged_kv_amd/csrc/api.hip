@@ -57,25 +57,42 @@ size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
                              max_positions).bytes;
 }
 
-q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
-                          const uint32_t* key_cache, const uint32_t* value_cache,
-                          const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
-                          const uint32_t* context_lens, uint32_t max_context_len,
-                          const uint32_t* visible_pos, const uint32_t* num_visible,
-                          uint32_t vis_stride,
-                          uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
-                          uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
-                          float scale, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+struct AppendArgs {
+    const float* key;
+    const float* value;
+    uint32_t key_stride, value_stride;
+    uint32_t* key_cache;
+    uint32_t* value_cache;
+};
+
+q8_status decode_common(float* out, const float* q, uint32_t q_stride,
+                        const uint32_t* key_cache, const uint32_t* value_cache,
+                        const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                        const uint32_t* context_lens, uint32_t max_context_len,
+                        const uint32_t* visible_pos, const uint32_t* num_visible,
+                        uint32_t vis_stride,
+                        uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                        uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                        float scale, void* workspace, size_t workspace_bytes,
+                        void* stream, const AppendArgs* app) {
     if (!head_size_ok(head_size) || block_size == 0 || num_heads == 0 || num_kv_heads == 0 ||
         num_heads % num_kv_heads != 0)
         return Q8_ERR_SHAPE;
     if (static_cast<uint64_t>(q_stride) < static_cast<uint64_t>(num_heads) * head_size) return Q8_ERR_SHAPE;
     const bool vis = visible_pos != nullptr;
     if (vis && vis_stride == 0) return Q8_ERR_SHAPE;
+    if (app) {
+        const uint64_t row = static_cast<uint64_t>(num_kv_heads) * head_size;
+        if (app->key_stride < row || app->value_stride < row) return Q8_ERR_SHAPE;
+    }
     if (num_seqs == 0) return Q8_OK;
     if (!out || !q || !key_cache || !value_cache || !block_tables) return Q8_ERR_NULL;
     if (vis ? !num_visible : !context_lens) return Q8_ERR_NULL;
+    if (app && (!app->key || !app->value)) return Q8_ERR_NULL;
     const uint32_t max_pos = vis ? vis_stride : max_context_len;
     if (max_pos > 0 && (max_num_blocks_per_seq == 0 || num_blocks == 0)) return Q8_ERR_SHAPE;
     if (!std::isfinite(scale)) return Q8_ERR_SHAPE;
@@ -113,8 +130,55 @@ q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
     a.block_size = block_size;
     a.num_blocks = num_blocks;
     a.scale_log2 = scale * 1.4426950408889634f;
+    if (app) {
+        a.new_key = app->key;
+        a.new_value = app->value;
+        a.new_key_stride = app->key_stride;
+        a.new_value_stride = app->value_stride;
+        a.new_vec4 = reinterpret_cast<uintptr_t>(app->key) % 16 == 0 && reinterpret_cast<uintptr_t>(app->value) % 16 == 0 &&
+                     app->key_stride % 4 == 0 && app->value_stride % 4 == 0 && head_size % 4 == 0;
+        a.key_cache_w = app->key_cache;
+        a.value_cache_w = app->value_cache;
+    }
     const hipError_t e = q8kv::launch_decode(a, p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
+                          const uint32_t* key_cache, const uint32_t* value_cache,
+                          const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                          const uint32_t* context_lens, uint32_t max_context_len,
+                          const uint32_t* visible_pos, const uint32_t* num_visible,
+                          uint32_t vis_stride,
+                          uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                          uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                          float scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    return decode_common(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
+                         context_lens, max_context_len, visible_pos, num_visible, vis_stride, num_seqs,
+                         num_heads, num_kv_heads, head_size, block_size, num_blocks, scale, workspace,
+                         workspace_bytes, stream, nullptr);
+}
+
+q8_status q8_decode_step(float* out, const float* q, uint32_t q_stride,
+                         const float* key, uint32_t key_stride,
+                         const float* value, uint32_t value_stride,
+                         uint32_t* key_cache, uint32_t* value_cache,
+                         const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                         const uint32_t* context_lens, uint32_t max_context_len,
+                         uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                         uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                         float scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    const AppendArgs app{key, value, key_stride, value_stride, key_cache, value_cache};
+    return decode_common(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
+                         context_lens, max_context_len, nullptr, nullptr, 0, num_seqs, num_heads,
+                         num_kv_heads, head_size, block_size, num_blocks, scale, workspace, workspace_bytes,
+                         stream, &app);
 }
 
 int q8_last_hip_error(void) { return g_last_hip_error; }

@@ -1,20 +1,17 @@
 // Quantize + pack new K/V vectors into the int8 paged cache.
 //
-// Follows the "reshape_and_cache_q8.comp" page, main(): for each (token, kv
-// head) and for K then V, amax = max|x| (from 0), inv = amax > 0 ? 127/amax : 0,
-// code = clamp(round(x * inv), -127, 127) packed four per u32 word with element
-// 4w+l in byte l, then one word with the bits of amax/127 (1.0 when amax == 0).
-// A pad slot (0xFFFFFFFF) skips the token: nothing is written for it (its
-// source rows may be read).  round() is round-half-even here.
+// Follows the "reshape_and_cache_q8.comp" page, main(), for each (token, kv
+// head) and for K then V (the quantizer is in q8_pack.h).  A pad slot
+// (0xFFFFFFFF) skips the token: nothing is written for it (its source rows
+// may be read).
 //
 // MI355X mapping: one wavefront per (token, kv head).  When head_size <= 128
 // the two 32-lane halves quantize K and V side by side; otherwise the whole
 // wave does K and then V.  Each lane owns one code word: a 16-byte load of four
 // f32 values, an amax reduction across the lanes of its half (or wave), four
-// IEEE multiplies, v_rndne, clamp and a byte pack.  Every step is a single
-// binary32 operation with round-to-nearest, so the packed words are bit-exact
-// (no FMA contraction applies: there is no add).
+// IEEE multiplies, v_rndne, clamp and a byte pack.
 #include "q8kv_internal.h"
+#include "q8_pack.h"
 
 namespace q8kv {
 namespace {
@@ -22,33 +19,6 @@ namespace {
 __device__ __forceinline__ float4 load4(const float* p, bool vec4) {
     if (vec4) return *reinterpret_cast<const float4*>(p);
     return make_float4(p[0], p[1], p[2], p[3]);
-}
-
-__device__ __forceinline__ uint32_t pack_code(float x, float inv, uint32_t lane_byte) {
-    float r = __builtin_rintf(x * inv);          // nearest, ties to even
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8u * lane_byte);
-}
-
-// Packs one vector already loaded as x (lane w owns word w of it): lanes
-// [0, width) of the group cooperate.
-template <int WIDTH>
-__device__ __forceinline__ void pack_vector(float4 x, uint32_t* dst, uint32_t hs4, uint32_t w) {
-    const bool active = w < hs4;
-    float amax = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
-#pragma unroll
-    for (int off = WIDTH / 2; off > 0; off >>= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, off, WIDTH));
-    const float inv = amax > 0.0f ? __fdiv_rn(127.0f, amax) : 0.0f;
-    if (active) {
-        uint32_t word = pack_code(x.x, inv, 0) | pack_code(x.y, inv, 1) |
-                        pack_code(x.z, inv, 2) | pack_code(x.w, inv, 3);
-        dst[w] = word;
-    }
-    if (w == 0) {
-        const float s = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 1.0f;
-        dst[hs4] = __float_as_uint(s);
-    }
 }
 
 template <bool HALF>

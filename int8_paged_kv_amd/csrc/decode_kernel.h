@@ -46,6 +46,7 @@
 //     over the 16 lanes of a DPP row.
 #pragma once
 #include "decode_split.h"
+#include "q8_pack.h"
 
 namespace q8kv {
 namespace {
@@ -363,10 +364,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     // Up to 64 sequences: one load and one scan give every sequence's chunk
     // count and offsets, kept in lane s.
     const bool one_window = a.num_seqs <= static_cast<uint32_t>(kWave);
-    uint32_t C, U, win_np = 0, win_nc = 0, win_incl = 0, win_cinc = 0;
+    const bool append = !VIS && a.new_key != nullptr;     // decode step: append, then attend
+    uint32_t C, U, win_np = 0, win_nc = 0, win_incl = 0, win_cinc = 0, win_len = 0;
     bool weighted = false;
     if (one_window) {
         win_np = lane < a.num_seqs ? positions_of<VIS>(a, lane) : 0u;
+        if (append && lane < a.num_seqs) win_len = a.context_lens[lane];
         win_nc = (win_np + kChunk - 1) / kChunk;
         win_incl = wave_incl_scan(win_nc, lane);
         C = uniform(lane_value(win_incl, kWave - 1));
@@ -481,6 +484,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     // sequence (1: it lies wholly in this wave's range); jf: the first of them.
     struct Meta {
         uint32_t s, cs, p0, info, jf, id;
+        uint32_t app;            // decode step: the chunk's last row is its sequence's new token
     };
     auto meta_nv = [](const Meta& m) __attribute__((always_inline)) { return m.info & 0x7Fu; };
     auto meta_tiled = [](const Meta& m) __attribute__((always_inline)) { return TILED || (m.info & 0x80u) != 0; };
@@ -501,6 +505,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         }
         m.jf = cur.jf;
         m.info = nv | (tiled << 7) | (cur.nrec << 8);
+        // The new token sits at position context_lens[s]-1, the sequence's last
+        // attended position when it is not clamped.
+        m.app = 0;
+        if (append && nv > 0 && m.cs + nv == cur.npos) {
+            const uint32_t L = one_window ? lane_value(win_len, m.s) : uniform(a.context_lens[m.s]);
+            m.app = L == cur.npos ? 1u : 0u;
+        }
         const uint32_t k = min(lane, nseg - 1);
         uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(kChunk) ? k : 0u);
         jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
@@ -604,6 +615,46 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             }
         }
     };
+    // ---- decode step: the new token's K and V rows, staged one chunk ahead ----
+    // Lane w < head_size/4 holds elements 4w .. 4w+3.  Quantized in the chunk's
+    // step exactly as the cache writer does, they replace the row the tile
+    // loads brought in (the cache still held the old one) and, for the first
+    // query-head group of the kv head, are written to the caches.
+    float4 nkx = make_float4(0.f, 0.f, 0.f, 0.f), nvx = nkx;
+    auto issue_new = [&](const Meta& m) __attribute__((always_inline)) {
+        if (!append || !m.app) return;
+        nkx = make_float4(0.f, 0.f, 0.f, 0.f);
+        nvx = nkx;
+        if (lane < hs4) {
+            const float* pk = a.new_key + static_cast<uint64_t>(m.s) * a.new_key_stride + static_cast<uint64_t>(kvh) * hs + 4 * lane;
+            const float* pv = a.new_value + static_cast<uint64_t>(m.s) * a.new_value_stride + static_cast<uint64_t>(kvh) * hs + 4 * lane;
+            if (a.new_vec4) {
+                nkx = *reinterpret_cast<const float4*>(pk);
+                nvx = *reinterpret_cast<const float4*>(pv);
+            } else {
+                nkx = make_float4(pk[0], pk[1], pk[2], pk[3]);
+                nvx = make_float4(pv[0], pv[1], pv[2], pv[3]);
+            }
+        }
+    };
+    auto store_new = [&](const Meta& m) __attribute__((always_inline)) {
+        if (!append || !m.app) return;
+        uint32_t ks, vs;
+        const uint32_t kw = quantize_word<kWave>(nkx, ks);
+        const uint32_t vw = quantize_word<kWave>(nvx, vs);
+        const uint32_t row = (meta_nv(m) - 1) * wpt;
+        if (lane < hs4) { sK[row + lane] = kw; sV[row + lane] = vw; }
+        if (lane == 0) { sK[row + hs4] = ks; sV[row + hs4] = vs; }
+        if (grp == 0) {
+            const uint32_t pos = m.cs + meta_nv(m) - 1;
+            uint32_t blk = uniform(a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + pos / a.block_size]);
+            blk = blk < num_blocks_m1 ? blk : num_blocks_m1;
+            const uint64_t dst = ((static_cast<uint64_t>(blk) * a.num_kv_heads + kvh) * a.block_size + pos % a.block_size) * wpt;
+            if (lane < hs4) { a.key_cache_w[dst + lane] = kw; a.value_cache_w[dst + lane] = vw; }
+            if (lane == 0) { a.key_cache_w[dst + hs4] = ks; a.value_cache_w[dst + hs4] = vs; }
+        }
+    };
+
     auto store = [&](const Meta& m, const Buf& b) __attribute__((always_inline)) {
         if (DMA) wait_vmem();           // this chunk's LDS-direct segment loads have landed
         if (FAST && meta_tiled(m)) {
@@ -654,6 +705,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
                 }
             }
         }
+        store_new(m);
     };
 
     // ---- q digits of the current sequence: MFMA row r = (head r/4, digit r%4) ----
@@ -982,6 +1034,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     Meta mc = meta_of(true);
     q_issue(mc.s);
     issue_data(mc, bA, sK, sV);
+    issue_new(mc);
     Meta mn1;
     if (n > 1) advance();
     mn1 = meta_of(n > 1);
@@ -993,6 +1046,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         if (xr + 2 < n) advance();
         const Meta mn2 = meta_of(xr + 2 < n);
         issue_data(mn1, bA, sKn, sVn);
+        issue_new(mn1);
         if (mn1.s != mc.s) q_issue(mn1.s);                    // q of the next chunk's sequence
         wave_sync();
         process(meta_nv(mc));

@@ -55,6 +55,15 @@ struct DecodeArgs {
     uint32_t q_stride, max_num_blocks_per_seq, max_context_len, vis_stride;
     uint32_t num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks;
     float scale_log2;        // softmax scale * log2(e)
+    // Decode step (new_key non-null): sequence s's new K and V vectors
+    // (element d of kv head h at new_key[s*new_key_stride + h*head_size + d]),
+    // appended to the caches at position context_lens[s]-1 before it is attended.
+    const float* new_key;
+    const float* new_value;
+    uint32_t new_key_stride, new_value_stride;
+    uint32_t new_vec4;       // the new rows are 16-byte aligned with strides that keep them so
+    uint32_t* key_cache_w;   // key_cache / value_cache, written by the append
+    uint32_t* value_cache_w;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);

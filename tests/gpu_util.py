@@ -45,7 +45,7 @@ def assert_close(got: np.ndarray, want: np.ndarray, what: str = ""):
 class Filled:
     """A workload's caches filled by the HIP writer (device) and the oracle (host)."""
 
-    def __init__(self, w: wl.Workload, oracle, check_write=True):
+    def __init__(self, w: wl.Workload, oracle, check_write=True, with_step=True):
         from int8_paged_kv_amd import q8_cache_write
         self.w = w
         kh, vh = w.empty_caches()
@@ -55,7 +55,7 @@ class Filled:
                            w.num_kv_heads, w.head_size, w.block_size)
             if check_write:
                 oracle.cache_write(k, v, kh, vh, slots, w.num_kv_heads, w.head_size, w.block_size)
-        step = w.step_write()
+        step = w.step_write() if with_step else None
         if step is not None:
             slots, k, v = step
             q8_cache_write(f32_dev(k), f32_dev(v), self.kc_d, self.vc_d, u32_dev(slots),

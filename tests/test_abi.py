@@ -107,3 +107,20 @@ def test_workspace_size_matches_plan(lib):
     assert lib.q8_paged_decode_workspace_bytes(8, 64, 8, 128, 32, 32768) == want(8, 128, 8, 8)
     # n_rep 16: two groups of 8 per kv head
     assert lib.q8_paged_decode_workspace_bytes(2, 32, 2, 64, 16, 500) == want(2, 64, 4, 8)
+
+
+def step_args(**kw):
+    a = dict(out=FAKE, q=FAKE, q_stride=4 * 128, k=FAKE, ks=2 * 128, v=FAKE, vs=2 * 128, kc=FAKE, vc=FAKE,
+             bt=FAKE, max_nb=8, cl=FAKE, mcl=5000, S=2, H=4, Hkv=2, hs=128, bs=16, nb=64, scale=0.1,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "q_stride", "k", "ks", "v", "vs", "kc", "vc", "bt", "max_nb", "cl", "mcl",
+                           "S", "H", "Hkv", "hs", "bs", "nb", "scale", "ws", "wsb", "stream")]
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(k=None), 1), (dict(v=None), 1), (dict(cl=None), 1), (dict(ks=255), 2), (dict(vs=100), 2),
+    (dict(hs=130), 2), (dict(H=5), 2), (dict(wsb=16), 3), (dict(out=ctypes.c_void_p(0x2004)), 5), (dict(S=0), 0),
+])
+def test_decode_step_validation(lib, kw, want):
+    assert lib.q8_decode_step(*step_args(**kw)) == want
