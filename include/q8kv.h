@@ -183,6 +183,36 @@ q8_status q8_decode_step(float* out, const float* q, uint32_t q_stride,
                          float scale, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * q8_paged_decode_rows -- multi-row causal decode: rows_per_seq (nb) query
+ * rows per sequence at its last nb positions, as in chunked prefill or
+ * speculative verification ("attention.rs" page, attention_b: row b of the nb
+ * rows starting at base_pos attends its causal prefix of base_pos + b + 1
+ * positions, with the "paged_attn_q8.comp" page's attention over it).  Here
+ * base_pos = context_lens[s] - nb: row b of sequence s attends positions
+ * 0 .. context_lens[s] - nb + b, clamped to max_context_len (a row whose
+ * prefix is empty gets a zero row).  Every row reads the paged cache
+ * through its sequence's block_tables row.
+ *
+ *   out           f32 [num_seqs * nb, num_heads, head_size], dense, 16-byte
+ *                 aligned; row b of sequence s at index s*nb + b.
+ *   q             f32; element d of head h of row b of sequence s at
+ *                 q[(s*nb + b)*q_stride + h*head_size + d].
+ *   workspace     q8_paged_decode_workspace_bytes(num_seqs * nb, ...).
+ *   the rest      as q8_paged_decode in dense mode.
+ *
+ * nb == 1 is q8_paged_decode.  Errors: those of q8_paged_decode in dense mode,
+ * plus Q8_ERR_SHAPE for nb == 0.
+ */
+q8_status q8_paged_decode_rows(float* out, const float* q, uint32_t q_stride,
+                               const uint32_t* key_cache, const uint32_t* value_cache,
+                               const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                               const uint32_t* context_lens, uint32_t max_context_len, uint32_t rows_per_seq,
+                               uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                               uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* hipError_t code behind the calling thread's last Q8_ERR_HIP (0 if none). */
 int q8_last_hip_error(void);
 

@@ -9,12 +9,15 @@ Two operations behind the C ABI of libq8kv.so (include/q8kv.h):
   lists (the selective decode of the "attention.rs" page).
 * ``q8_decode_step``: both in one launch for the usual decode step (each
   sequence's new token appended at its last position, then attended).
+* ``q8_paged_decode_rows``: multi-row causal decode (several query rows per
+  sequence at its last positions, each over its causal prefix).
 
 The binding loads the library lazily, so ``int8_paged_kv_amd.workloads`` can
 be imported on a machine without the library or a GPU.
 """
 
-__all__ = ["q8_cache_write", "q8_paged_decode", "q8_decode_step", "q8_paged_decode_workspace_bytes",
+__all__ = ["q8_cache_write", "q8_paged_decode", "q8_decode_step", "q8_paged_decode_rows",
+           "q8_paged_decode_workspace_bytes",
            "load_library", "Q8Error", "PAD_SLOT"]
 
 

@@ -49,6 +49,9 @@ def load_library() -> ctypes.CDLL:
         lib.q8_decode_step.argtypes = [P, P, U, P, U, P, U, P, P, P, U, P, U,
                                        U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.q8_decode_step.restype = ctypes.c_int
+        lib.q8_paged_decode_rows.argtypes = [P, P, U, P, P, P, U, P, U, U,
+                                             U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
+        lib.q8_paged_decode_rows.restype = ctypes.c_int
         lib.q8_last_hip_error.argtypes = []
         lib.q8_last_hip_error.restype = ctypes.c_int
         lib.q8_status_string.argtypes = [ctypes.c_int]
@@ -213,5 +216,46 @@ def q8_decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor, key_
                             S, H, num_kv_heads, hs, block_size, num_blocks, float(scale), wp, wb,
                             _stream(stream))
     _check(st, "q8_decode_step")
+    return out
+
+
+def q8_paged_decode_rows(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                         block_size: int, max_context_len: int, rows_per_seq: int,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         num_blocks: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Multi-row causal decode (see include/q8kv.h): q is [S * nb, H, hs] f32
+    (row b of sequence s at s*nb + b); row b attends the first
+    context_lens[s] - nb + b + 1 positions.  Returns out [S * nb, H, hs]."""
+    lib = load_library()
+    if q.dim() != 3 or (q.numel() and not q[0].is_contiguous()):
+        raise ValueError("q must be [S * rows_per_seq, H, head_size] with dense rows")
+    R, H, hs = q.shape
+    nb = int(rows_per_seq)
+    if nb < 1 or R % nb:
+        raise ValueError("q's row count must be a multiple of rows_per_seq")
+    S = R // nb
+    if out is None:
+        out = torch.empty((R, H, hs), dtype=torch.float32, device=q.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (R, H, hs):
+        raise ValueError("out must be a contiguous [S * rows_per_seq, H, head_size] f32 tensor")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [S, max_num_blocks_per_seq]")
+    wpt = hs // 4 + 1
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * wpt)
+    mcl = int(max_context_len)
+    need = lib.q8_paged_decode_workspace_bytes(R, H, num_kv_heads, hs, block_size, mcl)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)   # zero before first use
+    wp = None if workspace is None else workspace.data_ptr()
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.q8_paged_decode_rows(_dev(out, "out", torch.float32), _dev(q, "q", torch.float32), q.stride(0),
+                                  _u32(key_cache, "key_cache"), _u32(value_cache, "value_cache"),
+                                  _u32(block_tables, "block_tables"), block_tables.shape[1],
+                                  _u32(context_lens, "context_lens"), mcl, nb,
+                                  S, H, num_kv_heads, hs, block_size, num_blocks, float(scale), wp, wb,
+                                  _stream(stream))
+    _check(st, "q8_paged_decode_rows")
     return out
 

@@ -78,7 +78,7 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
                         uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
                         uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
                         float scale, void* workspace, size_t workspace_bytes,
-                        void* stream, const AppendArgs* app) {
+                        void* stream, const AppendArgs* app, uint32_t rows_per_seq) {
     if (!head_size_ok(head_size) || block_size == 0 || num_heads == 0 || num_kv_heads == 0 ||
         num_heads % num_kv_heads != 0)
         return Q8_ERR_SHAPE;
@@ -89,6 +89,9 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
         const uint64_t row = static_cast<uint64_t>(num_kv_heads) * head_size;
         if (app->key_stride < row || app->value_stride < row) return Q8_ERR_SHAPE;
     }
+    if (rows_per_seq == 0 || (rows_per_seq > 1 && vis)) return Q8_ERR_SHAPE;
+    if (static_cast<uint64_t>(num_seqs) * rows_per_seq > 0xFFFFFFFFull) return Q8_ERR_UNSUPPORTED;
+    const uint32_t num_rows = num_seqs * rows_per_seq;     // decode rows (one per sequence unless multi-row)
     if (num_seqs == 0) return Q8_OK;
     if (!out || !q || !key_cache || !value_cache || !block_tables) return Q8_ERR_NULL;
     if (vis ? !num_visible : !context_lens) return Q8_ERR_NULL;
@@ -98,9 +101,9 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     if (!std::isfinite(scale)) return Q8_ERR_SHAPE;
     if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return Q8_ERR_UNSUPPORTED;   // rows are written as 16-byte stores
     // Grid limits: one wavefront per workgroup in 1-D grids.
-    const q8kv::DecodePlan p = q8kv::plan_decode(num_seqs, num_heads, num_kv_heads, head_size,
+    const q8kv::DecodePlan p = q8kv::plan_decode(num_rows, num_heads, num_kv_heads, head_size,
                                                  block_size, max_pos);
-    if (p.num_waves > 0x7FFFFFFFull || static_cast<uint64_t>(num_seqs) * num_heads > 0x7FFFFFFFull)
+    if (p.num_waves > 0x7FFFFFFFull || static_cast<uint64_t>(num_rows) * num_heads > 0x7FFFFFFFull)
         return Q8_ERR_UNSUPPORTED;
     if (p.bytes > 0) {
         if (!workspace || workspace_bytes < p.bytes) return Q8_ERR_WORKSPACE;
@@ -123,7 +126,8 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     a.max_num_blocks_per_seq = max_num_blocks_per_seq;
     a.max_context_len = max_context_len;
     a.vis_stride = vis_stride;
-    a.num_seqs = num_seqs;
+    a.num_seqs = num_rows;
+    a.rows_per_seq = rows_per_seq;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
     a.head_size = head_size;
@@ -161,7 +165,21 @@ q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
     return decode_common(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
                          context_lens, max_context_len, visible_pos, num_visible, vis_stride, num_seqs,
                          num_heads, num_kv_heads, head_size, block_size, num_blocks, scale, workspace,
-                         workspace_bytes, stream, nullptr);
+                         workspace_bytes, stream, nullptr, 1);
+}
+
+q8_status q8_paged_decode_rows(float* out, const float* q, uint32_t q_stride,
+                               const uint32_t* key_cache, const uint32_t* value_cache,
+                               const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                               const uint32_t* context_lens, uint32_t max_context_len, uint32_t rows_per_seq,
+                               uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                               uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return decode_common(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
+                         context_lens, max_context_len, nullptr, nullptr, 0, num_seqs, num_heads, num_kv_heads,
+                         head_size, block_size, num_blocks, scale, workspace, workspace_bytes, stream, nullptr,
+                         rows_per_seq);
 }
 
 q8_status q8_decode_step(float* out, const float* q, uint32_t q_stride,
@@ -178,7 +196,7 @@ q8_status q8_decode_step(float* out, const float* q, uint32_t q_stride,
     return decode_common(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
                          context_lens, max_context_len, nullptr, nullptr, 0, num_seqs, num_heads,
                          num_kv_heads, head_size, block_size, num_blocks, scale, workspace, workspace_bytes,
-                         stream, &app);
+                         stream, &app, 1);
 }
 
 int q8_last_hip_error(void) { return g_last_hip_error; }

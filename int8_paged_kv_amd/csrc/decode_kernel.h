@@ -152,7 +152,12 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) {
 }
 
 
-// Number of positions sequence s attends.
+// Block-table row of sequence (or, in multi-row decode, row) s.
+__device__ __forceinline__ uint32_t table_row(const DecodeArgs& a, uint32_t s) {
+    return a.rows_per_seq > 1 ? s / a.rows_per_seq : s;
+}
+
+// Number of positions sequence (or row) s attends.
 template <bool VIS>
 __device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s) {
     uint32_t n;
@@ -160,7 +165,14 @@ __device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s
         n = a.num_visible[s];
         n = n < a.vis_stride ? n : a.vis_stride;
     } else {
-        n = a.context_lens[s];
+        if (a.rows_per_seq > 1) {
+            // causal rows: row b of a sequence of length L attends L - nb + b + 1 positions
+            const uint32_t nb = a.rows_per_seq, b = s % nb;
+            const uint32_t L = a.context_lens[s / nb];
+            n = L + b + 1 > nb ? L + b + 1 - nb : 0u;
+        } else {
+            n = a.context_lens[s];
+        }
         n = n < a.max_context_len ? n : a.max_context_len;
         const uint64_t cap = static_cast<uint64_t>(a.max_num_blocks_per_seq) * a.block_size;
         if (n > cap) n = static_cast<uint32_t>(cap);   // defensive: never index past a table row
@@ -515,7 +527,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         const uint32_t k = min(lane, nseg - 1);
         uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(kChunk) ? k : 0u);
         jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
-        m.id = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
+        m.id = a.block_tables[static_cast<uint64_t>(table_row(a, m.s)) * a.max_num_blocks_per_seq + jb];
         return m;
     };
 
@@ -691,7 +703,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             const uint32_t pos = position_at<VIS>(a, m.s, m.cs + min(lane, nv - 1));
             uint32_t jb = pos / a.block_size;
             jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
-            uint32_t phys = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
+            uint32_t phys = a.block_tables[static_cast<uint64_t>(table_row(a, m.s)) * a.max_num_blocks_per_seq + jb];
             phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
             const uint64_t my_row = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size +
                                      pos % a.block_size) * wpt;

@@ -64,6 +64,10 @@ struct DecodeArgs {
     uint32_t new_vec4;       // the new rows are 16-byte aligned with strides that keep them so
     uint32_t* key_cache_w;   // key_cache / value_cache, written by the append
     uint32_t* value_cache_w;
+    // Multi-row decode (> 1): num_seqs counts rows; row v is row v % rows_per_seq
+    // of sequence v / rows_per_seq (its block-table row), and attends the first
+    // context_lens[seq] - rows_per_seq + (v % rows_per_seq) + 1 positions.
+    uint32_t rows_per_seq;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);

@@ -124,3 +124,19 @@ def step_args(**kw):
 ])
 def test_decode_step_validation(lib, kw, want):
     assert lib.q8_decode_step(*step_args(**kw)) == want
+
+
+def rows_args(**kw):
+    a = dict(out=FAKE, q=FAKE, q_stride=4 * 128, kc=FAKE, vc=FAKE, bt=FAKE, max_nb=8, cl=FAKE, mcl=5000, nb=4,
+             S=2, H=4, Hkv=2, hs=128, bs=16, nblk=64, scale=0.1, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "q_stride", "kc", "vc", "bt", "max_nb", "cl", "mcl", "nb", "S", "H", "Hkv",
+                           "hs", "bs", "nblk", "scale", "ws", "wsb", "stream")]
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(nb=0), 2), (dict(cl=None), 1), (dict(hs=130), 2), (dict(wsb=16), 3), (dict(S=0), 0),
+    (dict(out=ctypes.c_void_p(0x2004)), 5),
+])
+def test_decode_rows_validation(lib, kw, want):
+    assert lib.q8_paged_decode_rows(*rows_args(**kw)) == want
