@@ -109,8 +109,8 @@ def main():
         sys.exit(2)
 
     import torch
-    from int8_paged_kv_amd import (q8_cache_write, q8_decode_step, q8_paged_decode, q8_paged_decode_workspace_bytes,
-                                   load_library)
+    from int8_paged_kv_amd import (q8_cache_write, q8_decode_step, q8_paged_decode, q8_paged_decode_rows,
+                                   q8_paged_decode_workspace_bytes, load_library)
     from int8_paged_kv_amd import workloads as wl
 
     load_library()
@@ -196,6 +196,32 @@ def main():
                      "decode_effective_GBps": round(B / (float(t_dec2.mean()) * 1e-6) / 1e9, 1),
                      "tokens": int(step_slots.size)}
 
+    # ---- multi-row causal decode: 4 verify rows per sequence at its last 4 positions ----
+    multi = None
+    if not args.no_reference:
+        nbr = 4
+        qr = torch.from_numpy(np.random.default_rng(11).standard_normal((S * nbr, H, hs)).astype(np.float32)).to(dev)
+        outr = torch.empty((S * nbr, H, hs), dtype=torch.float32, device=dev)
+        wsr = torch.zeros(max(1, q8_paged_decode_workspace_bytes(S * nbr, H, Hkv, hs, w.block_size, mcl)),
+                          dtype=torch.uint8, device=dev)
+        rows_len = [max(0, min(int(L), mcl) - nbr + b + 1) for L in w.context_lens for b in range(nbr)]
+        Br = int(sum(rows_len)) * Hkv * 2 * (hs + 4)
+        for i in range(3):
+            kc, vc = layers[i % len(layers)]
+            q8_paged_decode_rows(qr, kc, vc, bt, cl, w.scale, Hkv, w.block_size, mcl, nbr, out=outr, workspace=wsr)
+        torch.cuda.synchronize()
+        evr = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+        for i in range(20):
+            kc, vc = layers[i % len(layers)]
+            evr[i][0].record()
+            q8_paged_decode_rows(qr, kc, vc, bt, cl, w.scale, Hkv, w.block_size, mcl, nbr, out=outr, workspace=wsr)
+            evr[i][1].record()
+        torch.cuda.synchronize()
+        tr = np.array([e[0].elapsed_time(e[1]) for e in evr]) * 1e3
+        multi = {"rows_per_seq": nbr, "us_mean": round(float(tr.mean()), 2),
+                 "effective_kv_bytes": Br, "effective_GBps": round(Br / (float(tr.mean()) * 1e-6) / 1e9, 1),
+                 "note": "every row reads its own causal prefix"}
+
     hot = None
     if args.hot:
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -269,6 +295,7 @@ def main():
                    "effective_GBps": round(achieved, 1),
                    "seq_heads_per_s": round(S * H / (dec_mean * 1e-6), 1)},
         "two_launch_reference": reference,
+        "multi_row_decode": multi,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "q8_decode_step (one launch: decode_split_kernel, appending the step's tokens)",
