@@ -202,7 +202,7 @@ def main():
         nbr = 4
         qr = torch.from_numpy(np.random.default_rng(11).standard_normal((S * nbr, H, hs)).astype(np.float32)).to(dev)
         outr = torch.empty((S * nbr, H, hs), dtype=torch.float32, device=dev)
-        wsr = torch.zeros(max(1, q8_paged_decode_workspace_bytes(S * nbr, H, Hkv, hs, w.block_size, mcl)),
+        wsr = torch.zeros(max(1, q8_paged_decode_workspace_bytes(S, H * nbr, Hkv, hs, w.block_size, mcl)),
                           dtype=torch.uint8, device=dev)
         rows_len = [max(0, min(int(L), mcl) - nbr + b + 1) for L in w.context_lens for b in range(nbr)]
         Br = int(sum(rows_len)) * Hkv * 2 * (hs + 4)
@@ -220,7 +220,7 @@ def main():
         tr = np.array([e[0].elapsed_time(e[1]) for e in evr]) * 1e3
         multi = {"rows_per_seq": nbr, "us_mean": round(float(tr.mean()), 2),
                  "effective_kv_bytes": Br, "effective_GBps": round(Br / (float(tr.mean()) * 1e-6) / 1e9, 1),
-                 "note": "every row reads its own causal prefix"}
+                 "note": "bytes counted per row over its own causal prefix; the rows of a sequence share the reads"}
 
     hot = None
     if args.hot:

@@ -191,14 +191,16 @@ q8_status q8_decode_step(float* out, const float* q, uint32_t q_stride,
  * positions, with the "paged_attn_q8.comp" page's attention over it).  Here
  * base_pos = context_lens[s] - nb: row b of sequence s attends positions
  * 0 .. context_lens[s] - nb + b, clamped to max_context_len (a row whose
- * prefix is empty gets a zero row).  Every row reads the paged cache
- * through its sequence's block_tables row.
+ * prefix is empty gets a zero row).  The rows of a sequence share its
+ * block_tables row and its K/V reads: they are processed as extra query
+ * heads of each kv head, each with its own causal limit.
  *
  *   out           f32 [num_seqs * nb, num_heads, head_size], dense, 16-byte
  *                 aligned; row b of sequence s at index s*nb + b.
  *   q             f32; element d of head h of row b of sequence s at
  *                 q[(s*nb + b)*q_stride + h*head_size + d].
- *   workspace     q8_paged_decode_workspace_bytes(num_seqs * nb, ...).
+ *   workspace     q8_paged_decode_workspace_bytes(num_seqs, num_heads * nb,
+ *                 num_kv_heads, head_size, block_size, max_context_len).
  *   the rest      as q8_paged_decode in dense mode.
  *
  * nb == 1 is q8_paged_decode.  Errors: those of q8_paged_decode in dense mode,

@@ -245,7 +245,7 @@ def q8_paged_decode_rows(q: torch.Tensor, key_cache: torch.Tensor, value_cache: 
     if num_blocks is None:
         num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * wpt)
     mcl = int(max_context_len)
-    need = lib.q8_paged_decode_workspace_bytes(R, H, num_kv_heads, hs, block_size, mcl)
+    need = lib.q8_paged_decode_workspace_bytes(S, H * nb, num_kv_heads, hs, block_size, mcl)
     if workspace is None and need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)   # zero before first use
     wp = None if workspace is None else workspace.data_ptr()

@@ -91,7 +91,10 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     }
     if (rows_per_seq == 0 || (rows_per_seq > 1 && vis)) return Q8_ERR_SHAPE;
     if (static_cast<uint64_t>(num_seqs) * rows_per_seq > 0xFFFFFFFFull) return Q8_ERR_UNSUPPORTED;
-    const uint32_t num_rows = num_seqs * rows_per_seq;     // decode rows (one per sequence unless multi-row)
+    // Multi-row decode: a sequence's rows are query heads of its kv heads' groups
+    // (num_heads * rows_per_seq (row, head) pairs), so they share the K/V reads.
+    const uint64_t num_pairs = static_cast<uint64_t>(num_heads) * rows_per_seq;
+    if (num_pairs > 0xFFFFFFFFull) return Q8_ERR_UNSUPPORTED;
     if (num_seqs == 0) return Q8_OK;
     if (!out || !q || !key_cache || !value_cache || !block_tables) return Q8_ERR_NULL;
     if (vis ? !num_visible : !context_lens) return Q8_ERR_NULL;
@@ -101,9 +104,9 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     if (!std::isfinite(scale)) return Q8_ERR_SHAPE;
     if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return Q8_ERR_UNSUPPORTED;   // rows are written as 16-byte stores
     // Grid limits: one wavefront per workgroup in 1-D grids.
-    const q8kv::DecodePlan p = q8kv::plan_decode(num_rows, num_heads, num_kv_heads, head_size,
+    const q8kv::DecodePlan p = q8kv::plan_decode(num_seqs, static_cast<uint32_t>(num_pairs), num_kv_heads, head_size,
                                                  block_size, max_pos);
-    if (p.num_waves > 0x7FFFFFFFull || static_cast<uint64_t>(num_rows) * num_heads > 0x7FFFFFFFull)
+    if (p.num_waves > 0x7FFFFFFFull || static_cast<uint64_t>(num_seqs) * num_pairs > 0x7FFFFFFFull)
         return Q8_ERR_UNSUPPORTED;
     if (p.bytes > 0) {
         if (!workspace || workspace_bytes < p.bytes) return Q8_ERR_WORKSPACE;
@@ -126,7 +129,7 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     a.max_num_blocks_per_seq = max_num_blocks_per_seq;
     a.max_context_len = max_context_len;
     a.vis_stride = vis_stride;
-    a.num_seqs = num_rows;
+    a.num_seqs = num_seqs;
     a.rows_per_seq = rows_per_seq;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;

@@ -152,12 +152,7 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) {
 }
 
 
-// Block-table row of sequence (or, in multi-row decode, row) s.
-__device__ __forceinline__ uint32_t table_row(const DecodeArgs& a, uint32_t s) {
-    return a.rows_per_seq > 1 ? s / a.rows_per_seq : s;
-}
-
-// Number of positions sequence (or row) s attends.
+// Number of positions sequence s attends (in multi-row decode, its last row).
 template <bool VIS>
 __device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s) {
     uint32_t n;
@@ -165,14 +160,7 @@ __device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s
         n = a.num_visible[s];
         n = n < a.vis_stride ? n : a.vis_stride;
     } else {
-        if (a.rows_per_seq > 1) {
-            // causal rows: row b of a sequence of length L attends L - nb + b + 1 positions
-            const uint32_t nb = a.rows_per_seq, b = s % nb;
-            const uint32_t L = a.context_lens[s / nb];
-            n = L + b + 1 > nb ? L + b + 1 - nb : 0u;
-        } else {
-            n = a.context_lens[s];
-        }
+        n = a.context_lens[s];
         n = n < a.max_context_len ? n : a.max_context_len;
         const uint64_t cap = static_cast<uint64_t>(a.max_num_blocks_per_seq) * a.block_size;
         if (n > cap) n = static_cast<uint32_t>(cap);   // defensive: never index past a table row
@@ -236,13 +224,22 @@ __device__ __forceinline__ void coherent_load4x4(const float* p0, const float* p
         : "memory");
 }
 
-// Zero output rows of sequences [s_begin, s_end) for query heads h0 .. h0+nh-1.
-__device__ void zero_rows(const DecodeArgs& a, uint32_t lane, uint32_t s_begin, uint32_t s_end, uint32_t h0,
-                          uint32_t nh) {
+// Query heads of a row group: pairs p = (row p / n_rep, head kvh*n_rep +
+// p % n_rep) of a sequence's rows (one row except in multi-row decode) and the
+// kv head's query heads.  Output row (a row of [rows, num_heads, head_size])
+// of pair p of sequence s.
+__device__ __forceinline__ uint64_t pair_out_row(const DecodeArgs& a, uint32_t s, uint32_t kvh, uint32_t n_rep,
+                                                 uint32_t nrow, uint32_t p) {
+    return (static_cast<uint64_t>(s) * nrow + p / n_rep) * a.num_heads + kvh * n_rep + p % n_rep;
+}
+
+// Zero output rows of sequences [s_begin, s_end) for pairs p0 .. p0+np-1.
+__device__ void zero_rows(const DecodeArgs& a, uint32_t lane, uint32_t s_begin, uint32_t s_end, uint32_t kvh,
+                          uint32_t n_rep, uint32_t nrow, uint32_t p0, uint32_t np) {
     const uint32_t hs4 = a.head_size / 4;
     for (uint32_t s = s_begin; s < s_end; ++s)
-        for (uint32_t p = lane; p < nh * hs4; p += kWave) {
-            const uint64_t row = static_cast<uint64_t>(s) * a.num_heads + h0 + p / hs4;
+        for (uint32_t p = lane; p < np * hs4; p += kWave) {
+            const uint64_t row = pair_out_row(a, s, kvh, n_rep, nrow, p0 + p / hs4);
             *reinterpret_cast<float4*>(a.out + row * a.head_size + 4 * (p % hs4)) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
 }
@@ -381,7 +378,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     bool weighted = false;
     if (one_window) {
         win_np = lane < a.num_seqs ? positions_of<VIS>(a, lane) : 0u;
-        if (append && lane < a.num_seqs) win_len = a.context_lens[lane];
+        if ((append || a.rows_per_seq > 1) && lane < a.num_seqs) win_len = a.context_lens[lane];
         win_nc = (win_np + kChunk - 1) / kChunk;
         win_incl = wave_incl_scan(win_nc, lane);
         C = uniform(lane_value(win_incl, kWave - 1));
@@ -399,10 +396,16 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     }
     const uint32_t W = weighted ? c.waves_per_rg : min(c.waves_per_rg, C);
     const uint32_t n_rep = a.num_heads / a.num_kv_heads;
-    const uint32_t h0 = kvh * n_rep + grp * G;
-    const uint32_t nh = min(static_cast<uint32_t>(G), n_rep - grp * G);
+    // Multi-row decode: the nrow rows of a sequence share its K/V reads; the
+    // row group's query heads are (row, head) pairs h0 .. h0+nh-1.
+    const uint32_t nrow = a.rows_per_seq > 1 ? a.rows_per_seq : 1u;
+    const uint32_t h0 = grp * G;
+    const uint32_t nh = min(static_cast<uint32_t>(G), nrow * n_rep - grp * G);
+    auto zero_seqs = [&](uint32_t s_begin, uint32_t s_end) __attribute__((always_inline)) {
+        zero_rows(a, lane, s_begin, s_end, kvh, n_rep, nrow, h0, nh);
+    };
     if (j >= W) {
-        if (C == 0 && j == 0) zero_rows(a, lane, 0, a.num_seqs, h0, nh);
+        if (C == 0 && j == 0) zero_seqs(0, a.num_seqs);
         return;
     }
     // First chunk whose cost index is at least u (u < U), its sequence, the
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
                            : one_window ? lane_value(win_np, cur.s)
                                         : uniform(positions_of<VIS>(a, cur.s));
                 if (cur.npos != 0) break;
-                zero_rows(a, lane, cur.s, cur.s + 1, h0, nh);
+                zero_seqs(cur.s, cur.s + 1);
             }
             if (cur.s < a.num_seqs) share();
         }
@@ -487,7 +490,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             first = cur.s;
             while (first > 0 && uniform(positions_of<VIS>(a, first - 1)) == 0) --first;
         }
-        if (first < cur.s) zero_rows(a, lane, first, cur.s, h0, nh);
+        if (first < cur.s) zero_seqs(first, cur.s);
     }
 
     // ---- chunk metadata (uniform except the block id of segment `lane`) ----
@@ -497,6 +500,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     struct Meta {
         uint32_t s, cs, p0, info, jf, id;
         uint32_t app;            // decode step: the chunk's last row is its sequence's new token
+        uint32_t lr;             // multi-row decode: context_lens[s] - cs (row b sees lr - (nrow-1-b) of the chunk)
     };
     auto meta_nv = [](const Meta& m) __attribute__((always_inline)) { return m.info & 0x7Fu; };
     auto meta_tiled = [](const Meta& m) __attribute__((always_inline)) { return TILED || (m.info & 0x80u) != 0; };
@@ -519,6 +523,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         m.info = nv | (tiled << 7) | (cur.nrec << 8);
         // The new token sits at position context_lens[s]-1, the sequence's last
         // attended position when it is not clamped.
+        m.lr = 0;
+        if (nrow > 1 && nv > 0) m.lr = (one_window ? lane_value(win_len, m.s) : uniform(a.context_lens[m.s])) - m.cs;
         m.app = 0;
         if (append && nv > 0 && m.cs + nv == cur.npos) {
             const uint32_t L = one_window ? lane_value(win_len, m.s) : uniform(a.context_lens[m.s]);
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         const uint32_t k = min(lane, nseg - 1);
         uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(kChunk) ? k : 0u);
         jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
-        m.id = a.block_tables[static_cast<uint64_t>(table_row(a, m.s)) * a.max_num_blocks_per_seq + jb];
+        m.id = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
         return m;
     };
 
@@ -703,7 +709,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             const uint32_t pos = position_at<VIS>(a, m.s, m.cs + min(lane, nv - 1));
             uint32_t jb = pos / a.block_size;
             jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
-            uint32_t phys = a.block_tables[static_cast<uint64_t>(table_row(a, m.s)) * a.max_num_blocks_per_seq + jb];
+            uint32_t phys = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
             phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
             const uint64_t my_row = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size +
                                      pos % a.block_size) * wpt;
@@ -729,13 +735,16 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     constexpr int QF = G * QD / (4 * kWave);
     float4 qv[QF];
     auto q_issue = [&](uint32_t s) __attribute__((always_inline)) {
-        const uint64_t row = static_cast<uint64_t>(s) * a.q_stride;
+        const uint64_t row = static_cast<uint64_t>(s) * nrow * a.q_stride;
 #pragma unroll
         for (int t = 0; t < QF; ++t) {
             const uint32_t e = 4 * (lane + kWave * t);
             const uint32_t hi = e / QD, d = e % QD;
             const bool ok = hi < nh && d < hs;               // d % 4 == 0 and hs % 4 == 0: all four or none
-            const float* src = a.q + (ok ? row + static_cast<uint64_t>(h0 + hi) * hs + d : row);
+            const uint32_t pq = h0 + hi;                     // pair: row pq / n_rep, head kvh*n_rep + pq % n_rep
+            const float* src = a.q + (ok ? row + static_cast<uint64_t>(pq / n_rep) * a.q_stride +
+                                           static_cast<uint64_t>(kvh * n_rep + pq % n_rep) * hs + d
+                                         : row);
             float4 v;
             if (c.q_vec_ok) {
                 v = *reinterpret_cast<const float4*>(src);
@@ -817,7 +826,17 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     };
 
     // One chunk from LDS: q.K^T, online softmax, P.V.
-    auto process = [&](uint32_t nv) __attribute__((always_inline)) {
+    auto process = [&](const Meta& pm) __attribute__((always_inline)) {
+        const uint32_t nv = meta_nv(pm);
+        // Tokens of the chunk each of the lane's pairs attends: all nv, except in
+        // multi-row decode, where row b of nrow stops nrow-1-b positions early.
+        uint32_t nvh[NHS];
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) {
+            const uint32_t pq = h0 + 4 * hset + g;
+            const uint32_t dl = nrow - 1 - min(pq / n_rep, nrow - 1);
+            nvh[hset] = nrow > 1 ? min(nv, pm.lr > dl ? pm.lr - dl : 0u) : nv;
+        }
         // ---- q . K^T ----
         i32x4 dsum[NHS][4];
 #pragma unroll
@@ -859,22 +878,25 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 #pragma unroll
         for (int hset = 0; hset < NHS; ++hset) {
             float z[4];
+            bool vh[4];
             float cmax = -INFINITY;
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) {
+                vh[tg] = 16 * tg + r < nvh[hset];
                 const float zq = ldexpf(combine_digits(dsum[hset][tg]), -eq_out[hset]);
-                z[tg] = val[tg] ? zq * (ksc[tg] * a.scale_log2) : -INFINITY;
+                z[tg] = vh[tg] ? zq * (ksc[tg] * a.scale_log2) : -INFINITY;
                 cmax = fmaxf(cmax, z[tg]);
             }
             const float m_new = fmaxf(m_run[hset], row_max(cmax));
-            const float alpha = exp2f(m_run[hset] - m_new);
+            // -inf only while a multi-row pair has attended nothing: no NaN from exp2(-inf + inf)
+            const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run[hset] - m_new);
             float psum = 0.0f;
             uint32_t wd[4];
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) {
-                const float p = exp2f(z[tg] - m_new);
+                const float p = vh[tg] ? exp2f(z[tg] - m_new) : 0.0f;
                 psum += p;
-                const float pv = val[tg] ? p * vsc[tg] : 0.0f;
+                const float pv = vh[tg] ? p * vsc[tg] : 0.0f;
                 wd[tg] = to_digits(static_cast<int32_t>(rintf(ldexpf(pv, ep))));
             }
             l_run[hset] = l_run[hset] * alpha + row_sum(psum);
@@ -929,7 +951,6 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     // independent loads (typically a single memory round trip), with a
     // running max and rescaling as in the online softmax.
     auto merge = [&](uint32_t ms, uint32_t jf, uint32_t nrec) __attribute__((always_inline)) {
-        const uint64_t row_sh = static_cast<uint64_t>(ms) * a.num_heads;
         const uint64_t rec0 = static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf;      // record of wave jf
 #pragma unroll
         for (int hset = 0; hset < NHS; ++hset) {
@@ -957,20 +978,22 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
                         if (i0 + k < nrec) bm = fmaxf(bm, ml[k].x);
-                    const float sc = exp2f(M - bm);
+                    // A record whose row attended nothing (multi-row decode) has
+                    // max -inf and sum 0: it gets weight 0, never exp2(nan).
+                    const float sc = bm == -INFINITY ? 1.0f : exp2f(M - bm);
                     L *= sc;
                     o *= sc;
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const float w = i0 + k < nrec ? exp2f(ml[k].x - bm) : 0.0f;
+                        const float w = (i0 + k < nrec && ml[k].x != -INFINITY) ? exp2f(ml[k].x - bm) : 0.0f;
                         L += w * ml[k].y;
                         o += w * v[k];
                     }
                     M = bm;
                 }
                 if (hh < nh && word < hs4) {
-                    const float inv = 1.0f / L;
-                    *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) =
+                    const float inv = L > 0.0f ? 1.0f / L : 0.0f;      // an empty prefix gives a zero row
+                    *reinterpret_cast<float4*>(a.out + pair_out_row(a, ms, kvh, n_rep, nrow, h0 + hh) * hs + 4 * word) =
                         make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
                 }
             }
@@ -987,7 +1010,6 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     // sequence), which it sets back to zero) later combines all its records.
     auto flush = [&](const Meta& m) __attribute__((always_inline)) {
         const uint32_t nrec = meta_nrec(m);
-        const uint64_t row_sh = static_cast<uint64_t>(m.s) * a.num_heads;
         const uint64_t rec0 = static_cast<uint64_t>(rg) * c.recs_per_rg + m.s;    // record of wave jj: rec0 + jj
 #pragma unroll
         for (int hset = 0; hset < NHS; ++hset) {
@@ -998,9 +1020,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
                 float4 v = make_float4(acc[hset][cw][0], acc[hset][cw][1], acc[hset][cw][2], acc[hset][cw][3]);
                 if (nrec == 1) {
                     if (hh >= nh || word >= hs4) continue;
-                    const float inv = 1.0f / l_run[hset];
+                    const float inv = l_run[hset] > 0.0f ? 1.0f / l_run[hset] : 0.0f;   // empty prefix: zero row
                     v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
-                    *reinterpret_cast<float4*>(a.out + (row_sh + h0 + hh) * hs + 4 * word) = v;
+                    *reinterpret_cast<float4*>(a.out + pair_out_row(a, m.s, kvh, n_rep, nrow, h0 + hh) * hs + 4 * word) = v;
                 } else {
                     // record layout: [head set][column word][lane] 16-byte units
                     float* pa_ = a.part_acc + (rec0 + j) * kRecFloats + 4 * ((hset * NCW + cw) * kWave + lane);
@@ -1061,7 +1083,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         issue_new(mn1);
         if (mn1.s != mc.s) q_issue(mn1.s);                    // q of the next chunk's sequence
         wave_sync();
-        process(meta_nv(mc));
+        process(mc);
         if (xr + 1 == n || mn1.s != mc.s) flush(mc);
         if (xr + 1 == n) break;
         wave_sync();
@@ -1076,7 +1098,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     if (DMA) wait_vmem();      // no LDS-direct load may still be landing when the wave ends
     if (npend > 0) merge(pend_s0, pend_jf0, pend_n0);
     if (npend > 1) merge(pend_s1, pend_jf1, pend_n1);
-    if (j == W - 1) zero_rows(a, lane, mc.s + 1, a.num_seqs, h0, nh);
+    if (j == W - 1) zero_seqs(mc.s + 1, a.num_seqs);
 }
 
 template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED>
