@@ -43,6 +43,11 @@ def poison_cache(num_blocks_total: int, num_kv_heads: int, block_size: int, head
     return c
 
 
+def poison_cache_f32(num_blocks_total: int, num_kv_heads: int, block_size: int, head_size: int) -> np.ndarray:
+    """An f32 cache [num_blocks_total, Hkv, bs, hs] with every element NaN."""
+    return np.full((num_blocks_total, num_kv_heads, block_size, head_size), np.nan, dtype=np.float32)
+
+
 @dataclasses.dataclass
 class Workload:
     name: str

@@ -57,6 +57,13 @@ def _load():
         lib.q8o_paged_decode.restype = ctypes.c_int
         lib.q8o_paged_decode_units.argtypes = [P, P, U] + dec
         lib.q8o_paged_decode_units.restype = ctypes.c_int
+        lib.q8o_f32_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U]
+        lib.q8o_f32_cache_write.restype = ctypes.c_int
+        f32dec = [P, U, P, P, P, U, P, U, U, U, U, U, U, U, ctypes.c_float, ctypes.c_int]
+        lib.q8o_f32_paged_decode.argtypes = [P] + f32dec
+        lib.q8o_f32_paged_decode.restype = ctypes.c_int
+        lib.q8o_f32_paged_decode_units.argtypes = [P, P, U] + f32dec
+        lib.q8o_f32_paged_decode_units.restype = ctypes.c_int
         lib.q8o_max_threads.argtypes = []
         lib.q8o_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -177,4 +184,66 @@ def paged_decode_units(units, q, key_cache, value_cache, block_tables, context_l
                                           _ptr(cl), mcl, _ptr(vp), _ptr(nv), vstr, S, H,
                                           num_kv_heads, hs, block_size, nb, float(scale), nthreads),
            "paged_decode_units")
+    return out
+
+
+# ---- f32 cache baseline: layout [num_blocks, num_kv_heads, block_size, head_size] f32 ----
+
+def f32_cache_write(key, value, key_cache, value_cache, slot_mapping, num_kv_heads, head_size,
+                    block_size, num_blocks=None, key_stride=None, value_stride=None):
+    """Copy K and V rows into the f32 caches at their slots, in place (numpy f32 arrays)."""
+    key = _c(key, np.float32)
+    value = _c(value, np.float32)
+    slot_mapping = _c(slot_mapping, np.uint32)
+    for c in (key_cache, value_cache):
+        if c.dtype != np.float32 or not c.flags.c_contiguous:
+            raise ValueError("f32 caches must be contiguous float32 arrays")
+    T = slot_mapping.shape[0]
+    ks = key_stride if key_stride is not None else (key.size // T if T else num_kv_heads * head_size)
+    vs = value_stride if value_stride is not None else (value.size // T if T else num_kv_heads * head_size)
+    nb = num_blocks if num_blocks is not None else key_cache.size // (num_kv_heads * block_size * head_size)
+    _check(_load().q8o_f32_cache_write(_ptr(key), ks, _ptr(value), vs, _ptr(key_cache), _ptr(value_cache),
+                                       _ptr(slot_mapping), T, num_kv_heads, head_size, block_size, nb),
+           "f32_cache_write")
+
+
+def _f32_common(q, key_cache, block_tables, context_lens, max_context_len, num_kv_heads, block_size,
+                num_blocks):
+    q = _c(q, np.float32)
+    S, H, hs = q.shape
+    bt = _c(block_tables, np.uint32)
+    cl = _c(context_lens, np.uint32)
+    for c in (key_cache,):
+        if c.dtype != np.float32 or not c.flags.c_contiguous:
+            raise ValueError("f32 caches must be contiguous float32 arrays")
+    nb = num_blocks if num_blocks is not None else key_cache.size // (num_kv_heads * block_size * hs)
+    if max_context_len is None:
+        max_context_len = int(cl.max()) if cl.size else 0
+    return q, S, H, hs, bt, cl, nb, max_context_len
+
+
+def f32_paged_decode(q, key_cache, value_cache, block_tables, context_lens, scale, num_kv_heads,
+                     block_size, max_context_len=None, num_blocks=None, nthreads=0) -> np.ndarray:
+    """Decode every (seq, head) over an f32 paged cache; result [S, H, hs] f32."""
+    q, S, H, hs, bt, cl, nb, mcl = _f32_common(q, key_cache, block_tables, context_lens,
+                                               max_context_len, num_kv_heads, block_size, num_blocks)
+    out = np.zeros((S, H, hs), dtype=np.float32)
+    _check(_load().q8o_f32_paged_decode(_ptr(out), _ptr(q), H * hs, _ptr(key_cache), _ptr(value_cache),
+                                        _ptr(bt), bt.shape[-1], _ptr(cl), mcl, S, H, num_kv_heads, hs,
+                                        block_size, nb, float(scale), nthreads), "f32_paged_decode")
+    return out
+
+
+def f32_paged_decode_units(units, q, key_cache, value_cache, block_tables, context_lens, scale,
+                           num_kv_heads, block_size, max_context_len=None, num_blocks=None,
+                           nthreads=0) -> np.ndarray:
+    """Decode only the listed (seq, head) pairs over an f32 cache; result [len(units), hs] f32."""
+    q, S, H, hs, bt, cl, nb, mcl = _f32_common(q, key_cache, block_tables, context_lens,
+                                               max_context_len, num_kv_heads, block_size, num_blocks)
+    u = _c(np.asarray(units).reshape(-1, 2), np.uint32)
+    out = np.zeros((u.shape[0], hs), dtype=np.float32)
+    _check(_load().q8o_f32_paged_decode_units(_ptr(out), _ptr(u), u.shape[0], _ptr(q), H * hs,
+                                              _ptr(key_cache), _ptr(value_cache), _ptr(bt), bt.shape[-1],
+                                              _ptr(cl), mcl, S, H, num_kv_heads, hs, block_size, nb,
+                                              float(scale), nthreads), "f32_paged_decode_units")
     return out

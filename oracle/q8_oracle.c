@@ -41,6 +41,15 @@
  *   per-row split decode that binds the row's visible token list): the row
  *   attends exactly the listed logical positions; context_lens is unused.
  *
+ *   f32 cache baseline (the "paged_attn_q8.comp" page's header: the int8 decode
+ *   keeps the math and structure of the f32 decode, whose cache holds 4 bytes
+ *   per element; the "reshape_and_cache_q8.comp" page's header: pad slots are
+ *   skipped as in the f32 writer).  The pages do not print the f32 layout; it
+ *   is read as the quantized layout with each token vector stored as head_size
+ *   f32 values: [num_blocks, num_kv_heads, block_size, head_size] f32.  The
+ *   writer copies rows; the decode is the definition above with
+ *   k_hat, v_hat the stored f32 values (exact in binary64).
+ *
  * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fopenmp -fPIC
  * -shared.  On x86-64 (SSE, FLT_EVAL_METHOD == 0) every float operation above
  * rounds to binary32 once.  OpenMP only spreads independent (seq, head) units
@@ -152,6 +161,7 @@ int q8o_cache_write(const float* key, uint32_t key_stride,
 typedef struct {
     const float* q; uint32_t q_stride;
     const uint32_t* key_cache; const uint32_t* value_cache;
+    const float* key_cache_f32; const float* value_cache_f32;   /* f32 baseline when non-NULL */
     const uint32_t* block_tables; uint32_t max_num_blocks_per_seq;
     const uint32_t* context_lens; uint32_t max_context_len;
     const uint32_t* visible_pos; const uint32_t* num_visible; uint32_t vis_stride;
@@ -159,13 +169,29 @@ typedef struct {
     double scale;
 } decode_args;
 
+/* The K (or V) vector of kv head kvh at (physical block, offset), in binary64. */
+static void load_row(const decode_args* a, int value, uint32_t phys, uint32_t off, uint32_t kvh,
+                     double* out)
+{
+    const uint32_t hs = a->head_size;
+    if (a->key_cache_f32) {
+        const float* c = value ? a->value_cache_f32 : a->key_cache_f32;
+        const float* row = c + (((uint64_t)phys * a->num_kv_heads + kvh) * a->block_size + off) * hs;
+        for (uint32_t d = 0; d < hs; ++d) out[d] = (double)row[d];
+    } else {
+        const uint32_t* c = value ? a->value_cache : a->key_cache;
+        q8o_dequantize_row(c + row_offset(phys, off, kvh, a->num_kv_heads, a->block_size, hs / 4 + 1),
+                           hs, out);
+    }
+}
+
 /*
  * One (seq, head) unit.  out_row gets head_size floats; work holds 2*head_size
  * doubles plus one double per attended position.
  */
 static int decode_unit(const decode_args* a, uint32_t s, uint32_t h, float* out_row)
 {
-    const uint32_t hs = a->head_size, wpt = hs / 4 + 1;
+    const uint32_t hs = a->head_size;
     const uint32_t kvh = h / (a->num_heads / a->num_kv_heads);
     uint32_t n;
     const uint32_t* pos = NULL;
@@ -196,9 +222,7 @@ static int decode_unit(const decode_args* a, uint32_t s, uint32_t h, float* out_
         if (j >= a->max_num_blocks_per_seq) { free(z); return Q8O_ERR_RANGE; }
         uint32_t phys = bt[j];
         if (phys >= a->num_blocks) { free(z); return Q8O_ERR_RANGE; }
-        const uint32_t* krow = a->key_cache +
-            row_offset(phys, t % a->block_size, kvh, a->num_kv_heads, a->block_size, wpt);
-        q8o_dequantize_row(krow, hs, k_hat);
+        load_row(a, 0, phys, t % a->block_size, kvh, k_hat);
         double dot = 0.0;
         for (uint32_t d = 0; d < hs; ++d) dot += (double)qv[d] * k_hat[d];
         z[i] = a->scale * dot;
@@ -211,11 +235,9 @@ static int decode_unit(const decode_args* a, uint32_t s, uint32_t h, float* out_
     for (uint32_t i = 0; i < n; ++i) {
         uint32_t t = pos ? pos[i] : i;
         uint32_t phys = bt[t / a->block_size];
-        const uint32_t* vrow = a->value_cache +
-            row_offset(phys, t % a->block_size, kvh, a->num_kv_heads, a->block_size, wpt);
         double w = exp(z[i] - zmax);
         denom += w;
-        q8o_dequantize_row(vrow, hs, k_hat);     /* reuse buffer for v_hat */
+        load_row(a, 1, phys, t % a->block_size, kvh, k_hat);     /* reuse buffer for v_hat */
         for (uint32_t d = 0; d < hs; ++d) o[d] += w * k_hat[d];
     }
     for (uint32_t d = 0; d < hs; ++d) out_row[d] = (float)(o[d] / denom);
@@ -230,6 +252,44 @@ static int check_decode_shape(const decode_args* a)
         return Q8O_ERR_SHAPE;
     if ((uint64_t)a->q_stride < (uint64_t)a->num_heads * a->head_size) return Q8O_ERR_SHAPE;
     return Q8O_OK;
+}
+
+static int run_units(const decode_args* a, float* out, const uint32_t* units, uint32_t num_units,
+                     int nthreads)
+{
+    int rc = check_decode_shape(a);
+    if (rc != Q8O_OK) return rc;
+    for (uint32_t i = 0; i < num_units; ++i)
+        if (units[2 * i] >= a->num_seqs || units[2 * i + 1] >= a->num_heads) return Q8O_ERR_RANGE;
+    int err = Q8O_OK;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < (int64_t)num_units; ++i) {
+        int r = decode_unit(a, units[2 * i], units[2 * i + 1], out + (uint64_t)i * a->head_size);
+        if (r != Q8O_OK) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+            err = r;
+        }
+    }
+    (void)nthreads;
+    return err;
+}
+
+/* Every (seq, head) of the batch as a unit list, in row-major output order. */
+static uint32_t* all_units(uint32_t num_seqs, uint32_t num_heads, uint64_t* nu)
+{
+    *nu = (uint64_t)num_seqs * num_heads;
+    uint32_t* units = (uint32_t*)malloc(sizeof(uint32_t) * 2 * (*nu ? *nu : 1));
+    if (!units) return NULL;
+    for (uint64_t i = 0; i < *nu; ++i) {
+        units[2 * i] = (uint32_t)(i / num_heads);
+        units[2 * i + 1] = (uint32_t)(i % num_heads);
+    }
+    return units;
 }
 
 /*
@@ -248,30 +308,11 @@ int q8o_paged_decode_units(float* out, const uint32_t* units, uint32_t num_units
                            uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
                            float scale, int nthreads)
 {
-    decode_args a = { q, q_stride, key_cache, value_cache, block_tables,
+    decode_args a = { q, q_stride, key_cache, value_cache, NULL, NULL, block_tables,
                       max_num_blocks_per_seq, context_lens, max_context_len,
                       visible_pos, num_visible, vis_stride, num_seqs, num_heads,
                       num_kv_heads, head_size, block_size, num_blocks, (double)scale };
-    int rc = check_decode_shape(&a);
-    if (rc != Q8O_OK) return rc;
-    for (uint32_t i = 0; i < num_units; ++i)
-        if (units[2 * i] >= num_seqs || units[2 * i + 1] >= num_heads) return Q8O_ERR_RANGE;
-    int err = Q8O_OK;
-#ifdef _OPENMP
-    if (nthreads <= 0) nthreads = omp_get_max_threads();
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
-#endif
-    for (int64_t i = 0; i < (int64_t)num_units; ++i) {
-        int r = decode_unit(&a, units[2 * i], units[2 * i + 1], out + (uint64_t)i * head_size);
-        if (r != Q8O_OK) {
-#ifdef _OPENMP
-#pragma omp critical
-#endif
-            err = r;
-        }
-    }
-    (void)nthreads;
-    return err;
+    return run_units(&a, out, units, num_units, nthreads);
 }
 
 /* Decode every (seq, head): out is [num_seqs, num_heads, head_size] dense f32. */
@@ -285,19 +326,82 @@ int q8o_paged_decode(float* out, const float* q, uint32_t q_stride,
                      uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
                      float scale, int nthreads)
 {
-    uint64_t nu = (uint64_t)num_seqs * num_heads;
-    uint32_t* units = (uint32_t*)malloc(sizeof(uint32_t) * 2 * (nu ? nu : 1));
+    uint64_t nu;
+    uint32_t* units = all_units(num_seqs, num_heads, &nu);
     if (!units) return Q8O_ERR_NOMEM;
-    for (uint64_t i = 0; i < nu; ++i) {
-        units[2 * i] = (uint32_t)(i / num_heads);
-        units[2 * i + 1] = (uint32_t)(i % num_heads);
-    }
     int rc = q8o_paged_decode_units(out, units, (uint32_t)nu, q, q_stride, key_cache,
                                     value_cache, block_tables, max_num_blocks_per_seq,
                                     context_lens, max_context_len, visible_pos,
                                     num_visible, vis_stride, num_seqs, num_heads,
                                     num_kv_heads, head_size, block_size, num_blocks,
                                     scale, nthreads);
+    free(units);
+    return rc;
+}
+
+/* f32 baseline writer: row t, kv head h is copied to its slot; pads are skipped. */
+int q8o_f32_cache_write(const float* key, uint32_t key_stride,
+                        const float* value, uint32_t value_stride,
+                        float* key_cache, float* value_cache,
+                        const uint32_t* slot_mapping, uint32_t num_tokens,
+                        uint32_t num_kv_heads, uint32_t head_size,
+                        uint32_t block_size, uint32_t num_blocks)
+{
+    if (head_size == 0 || block_size == 0 || num_kv_heads == 0) return Q8O_ERR_SHAPE;
+    if ((uint64_t)key_stride < (uint64_t)num_kv_heads * head_size ||
+        (uint64_t)value_stride < (uint64_t)num_kv_heads * head_size)
+        return Q8O_ERR_SHAPE;
+    for (uint32_t t = 0; t < num_tokens; ++t) {
+        uint32_t slot = slot_mapping[t];
+        if (slot == Q8O_PAD_SLOT) continue;
+        uint64_t block = slot / block_size, off = slot % block_size;
+        if (block >= num_blocks) return Q8O_ERR_RANGE;
+        for (uint32_t h = 0; h < num_kv_heads; ++h) {
+            uint64_t dst = ((block * num_kv_heads + h) * block_size + off) * head_size;
+            memcpy(key_cache + dst, key + (uint64_t)t * key_stride + (uint64_t)h * head_size,
+                   sizeof(float) * head_size);
+            memcpy(value_cache + dst, value + (uint64_t)t * value_stride + (uint64_t)h * head_size,
+                   sizeof(float) * head_size);
+        }
+    }
+    return Q8O_OK;
+}
+
+/* f32 baseline decode of selected units (dense mode only); as q8o_paged_decode_units. */
+int q8o_f32_paged_decode_units(float* out, const uint32_t* units, uint32_t num_units,
+                               const float* q, uint32_t q_stride,
+                               const float* key_cache, const float* value_cache,
+                               const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                               const uint32_t* context_lens, uint32_t max_context_len,
+                               uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                               uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                               float scale, int nthreads)
+{
+    if (!key_cache || !value_cache) return Q8O_ERR_SHAPE;
+    decode_args a = { q, q_stride, NULL, NULL, key_cache, value_cache, block_tables,
+                      max_num_blocks_per_seq, context_lens, max_context_len,
+                      NULL, NULL, 0, num_seqs, num_heads,
+                      num_kv_heads, head_size, block_size, num_blocks, (double)scale };
+    return run_units(&a, out, units, num_units, nthreads);
+}
+
+/* f32 baseline decode of every (seq, head): out is [num_seqs, num_heads, head_size]. */
+int q8o_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
+                         const float* key_cache, const float* value_cache,
+                         const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                         const uint32_t* context_lens, uint32_t max_context_len,
+                         uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                         uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                         float scale, int nthreads)
+{
+    uint64_t nu;
+    uint32_t* units = all_units(num_seqs, num_heads, &nu);
+    if (!units) return Q8O_ERR_NOMEM;
+    int rc = q8o_f32_paged_decode_units(out, units, (uint32_t)nu, q, q_stride, key_cache,
+                                        value_cache, block_tables, max_num_blocks_per_seq,
+                                        context_lens, max_context_len, num_seqs, num_heads,
+                                        num_kv_heads, head_size, block_size, num_blocks,
+                                        scale, nthreads);
     free(units);
     return rc;
 }
