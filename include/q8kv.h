@@ -215,6 +215,80 @@ q8_status q8_paged_decode_rows(float* out, const float* q, uint32_t q_stride,
                                float scale, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/*
+ * f32 paged-cache baseline.  The "paged_attn_q8.comp" page's header says the
+ * int8 decode keeps the math and workgroup structure of an f32 paged decode
+ * whose cache holds 4 bytes per element, and the "reshape_and_cache_q8.comp"
+ * page's header says its pad-slot rule mirrors the f32 writer.  The pages do
+ * not print the f32 layout; here it is the int8 layout with one f32 per
+ * element: an f32 buffer [num_blocks, num_kv_heads, block_size, head_size]
+ * for K and one for V.  These calls exist so that the int8 cache can be
+ * measured against the f32 one on the same batch.
+ *
+ * q8_f32_cache_write -- copy the new K and V vectors of num_tokens tokens
+ * into the f32 paged caches at their slots (block slot / block_size, offset
+ * slot % block_size); a slot equal to Q8_PAD_SLOT skips the token.
+ *
+ *   key, value   f32 device arrays, as for q8_cache_write.
+ *   key_cache,   f32 device caches in the layout above, 16-byte aligned.
+ *   value_cache
+ *   slot_mapping u32 [num_tokens].
+ *
+ * Errors: Q8_ERR_NULL for a NULL pointer when num_tokens > 0; Q8_ERR_SHAPE
+ * when head_size is 0, not a multiple of 4 or above 256, block_size,
+ * num_kv_heads or num_blocks is 0, or a stride is below num_kv_heads *
+ * head_size; Q8_ERR_UNSUPPORTED when a cache is not 16-byte aligned.
+ * num_tokens == 0 enqueues nothing.
+ */
+q8_status q8_f32_cache_write(const float* key, uint32_t key_stride,
+                             const float* value, uint32_t value_stride,
+                             float* key_cache, float* value_cache,
+                             const uint32_t* slot_mapping, uint32_t num_tokens,
+                             uint32_t num_kv_heads, uint32_t head_size,
+                             uint32_t block_size, uint32_t num_blocks, void* stream);
+
+/* Workspace bytes q8_f32_paged_decode needs for these sizes (0 when the
+ * head counts are inconsistent). */
+size_t q8_f32_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
+                                           uint32_t num_kv_heads, uint32_t head_size);
+
+/*
+ * q8_f32_paged_decode -- single-query decode over the f32 paged caches: for
+ * each (seq s, head h), out = softmax(scale * q . K^T) . V over positions
+ * 0 .. min(context_lens[s], max_context_len) - 1 of kv head
+ * h / (num_heads / num_kv_heads), position t at block_tables[s][t /
+ * block_size], offset t % block_size (the "paged_attn_q8.comp" page's math
+ * with the f32 elements it replaces).
+ *
+ *   out           f32 [num_seqs, num_heads, head_size], dense, 16-byte aligned.
+ *   q             f32, 16-byte aligned, q_stride a multiple of 4; element d
+ *                 of head h of seq s at q[s*q_stride + h*head_size + d].
+ *   key_cache,    f32 caches in the layout above, 16-byte aligned.
+ *   value_cache
+ *   block_tables, context_lens, max_context_len, scale: as q8_paged_decode.
+ *   workspace     q8_f32_paged_decode_workspace_bytes() bytes, 16-byte
+ *                 aligned, ZERO-FILLED before its first use; each completed
+ *                 call leaves it ready for the next (as for q8_paged_decode).
+ *
+ * An empty position set gives a zero output row.  Errors: Q8_ERR_NULL for a
+ * NULL required pointer; Q8_ERR_SHAPE when head_size is not a multiple of 4
+ * or above 256, block_size, num_heads or num_kv_heads is 0, num_heads %
+ * num_kv_heads != 0, q_stride < num_heads*head_size, or
+ * max_num_blocks_per_seq or num_blocks is 0 while positions are possible;
+ * Q8_ERR_WORKSPACE when the workspace is too small or misaligned;
+ * Q8_ERR_UNSUPPORTED when head_size is not 16, 32, 64, 128 or 256, a pointer
+ * above is not 16-byte aligned, q_stride is not a multiple of 4, or
+ * max_context_len >= 2^31.  num_seqs == 0 enqueues nothing.
+ */
+q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
+                              const float* key_cache, const float* value_cache,
+                              const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                              const uint32_t* context_lens, uint32_t max_context_len,
+                              uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                              uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                              float scale, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* hipError_t code behind the calling thread's last Q8_ERR_HIP (0 if none). */
 int q8_last_hip_error(void);
 

@@ -1,6 +1,6 @@
 """int8 paged KV cache for AMD MI355X (gfx950).
 
-Two operations behind the C ABI of libq8kv.so (include/q8kv.h):
+Operations behind the C ABI of libq8kv.so (include/q8kv.h):
 
 * ``q8_cache_write``: symmetric per-token int8 quantize + pack of new K/V
   vectors into the paged cache (the "reshape_and_cache_q8.comp" page).
@@ -11,13 +11,16 @@ Two operations behind the C ABI of libq8kv.so (include/q8kv.h):
   sequence's new token appended at its last position, then attended).
 * ``q8_paged_decode_rows``: multi-row causal decode (several query rows per
   sequence at its last positions, each over its causal prefix).
+* ``q8_f32_cache_write`` / ``q8_f32_paged_decode``: the same write and decode
+  over an f32 paged cache, the baseline the int8 cache is measured against.
 
 The binding loads the library lazily, so ``int8_paged_kv_amd.workloads`` can
 be imported on a machine without the library or a GPU.
 """
 
 __all__ = ["q8_cache_write", "q8_paged_decode", "q8_decode_step", "q8_paged_decode_rows",
-           "q8_paged_decode_workspace_bytes",
+           "q8_paged_decode_workspace_bytes", "q8_f32_cache_write", "q8_f32_paged_decode",
+           "q8_f32_paged_decode_workspace_bytes",
            "load_library", "Q8Error", "PAD_SLOT"]
 
 

@@ -52,6 +52,13 @@ def load_library() -> ctypes.CDLL:
         lib.q8_paged_decode_rows.argtypes = [P, P, U, P, P, P, U, P, U, U,
                                              U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.q8_paged_decode_rows.restype = ctypes.c_int
+        lib.q8_f32_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U, P]
+        lib.q8_f32_cache_write.restype = ctypes.c_int
+        lib.q8_f32_paged_decode_workspace_bytes.argtypes = [U, U, U, U]
+        lib.q8_f32_paged_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.q8_f32_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U,
+                                            U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
+        lib.q8_f32_paged_decode.restype = ctypes.c_int
         lib.q8_last_hip_error.argtypes = []
         lib.q8_last_hip_error.restype = ctypes.c_int
         lib.q8_status_string.argtypes = [ctypes.c_int]
@@ -259,3 +266,59 @@ def q8_paged_decode_rows(q: torch.Tensor, key_cache: torch.Tensor, value_cache: 
     _check(st, "q8_paged_decode_rows")
     return out
 
+
+def q8_f32_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, slot_mapping: torch.Tensor, num_kv_heads: int,
+                       head_size: int, block_size: int, num_blocks: Optional[int] = None, stream=None) -> None:
+    """Copy K/V rows into the f32 paged caches [num_blocks, Hkv, block_size, head_size] (baseline)."""
+    lib = load_library()
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * head_size)
+    st = lib.q8_f32_cache_write(kp, ks, vp, vs, _dev(key_cache, "key_cache", torch.float32),
+                                _dev(value_cache, "value_cache", torch.float32),
+                                _u32(slot_mapping, "slot_mapping"), slot_mapping.numel(), num_kv_heads,
+                                head_size, block_size, num_blocks, _stream(stream))
+    _check(st, "q8_f32_cache_write")
+
+
+def q8_f32_paged_decode_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int) -> int:
+    return int(load_library().q8_f32_paged_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size))
+
+
+def q8_f32_paged_decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                        num_kv_heads: int, block_size: int, max_context_len: Optional[int] = None,
+                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        num_blocks: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Single-query decode over the f32 paged caches (baseline); q is [S, H, hs] with dense heads.
+
+    A caller-provided workspace must have been zero-filled before its first
+    use; every completed call leaves it ready for the next.
+    """
+    lib = load_library()
+    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [num_seqs, num_heads, head_size] with dense heads")
+    S, H, hs = q.shape
+    if out is None:
+        out = torch.empty((S, H, hs), dtype=torch.float32, device=q.device)
+    if not out.is_contiguous() or tuple(out.shape) != (S, H, hs):
+        raise ValueError("out must be a dense [num_seqs, num_heads, head_size] tensor")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if context_lens.numel() else 0
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * hs)
+    need = lib.q8_f32_paged_decode_workspace_bytes(S, H, num_kv_heads, hs)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)   # zero before first use
+    wp = workspace.data_ptr()
+    wb = workspace.numel() * workspace.element_size()
+    st = lib.q8_f32_paged_decode(_dev(out, "out", torch.float32), _dev(q, "q", torch.float32), q.stride(0),
+                                 _dev(key_cache, "key_cache", torch.float32),
+                                 _dev(value_cache, "value_cache", torch.float32),
+                                 _u32(block_tables, "block_tables"), block_tables.shape[-1],
+                                 _u32(context_lens, "context_lens"), max_context_len, S, H, num_kv_heads, hs,
+                                 block_size, num_blocks, float(scale), wp, wb, _stream(stream))
+    _check(st, "q8_f32_paged_decode")
+    return out

@@ -202,6 +202,99 @@ q8_status q8_decode_step(float* out, const float* q, uint32_t q_stride,
                          stream, &app, 1);
 }
 
+q8_status q8_f32_cache_write(const float* key, uint32_t key_stride,
+                             const float* value, uint32_t value_stride,
+                             float* key_cache, float* value_cache,
+                             const uint32_t* slot_mapping, uint32_t num_tokens,
+                             uint32_t num_kv_heads, uint32_t head_size,
+                             uint32_t block_size, uint32_t num_blocks, void* stream) {
+    if (!head_size_ok(head_size) || block_size == 0 || num_kv_heads == 0 || num_blocks == 0) return Q8_ERR_SHAPE;
+    const uint64_t row = static_cast<uint64_t>(num_kv_heads) * head_size;
+    if (key_stride < row || value_stride < row) return Q8_ERR_SHAPE;
+    if (num_tokens == 0) return Q8_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping) return Q8_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(key_cache) % 16 != 0 || reinterpret_cast<uintptr_t>(value_cache) % 16 != 0)
+        return Q8_ERR_UNSUPPORTED;
+    if (static_cast<uint64_t>(num_tokens) * row / 4 > 0xFFFFFFFFull * 256) return Q8_ERR_UNSUPPORTED;
+    q8kv::F32CacheWriteArgs a{};
+    a.key = key;
+    a.value = value;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.slot_mapping = slot_mapping;
+    a.key_stride = key_stride;
+    a.value_stride = value_stride;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.head_size = head_size;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    const hipError_t e = q8kv::launch_f32_cache_write(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+size_t q8_f32_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
+                                           uint32_t num_kv_heads, uint32_t head_size) {
+    if (num_kv_heads == 0 || num_heads == 0 || num_heads % num_kv_heads != 0) return 0;
+    return q8kv::plan_f32_decode(num_seqs, num_heads, num_kv_heads, head_size).bytes;
+}
+
+q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
+                              const float* key_cache, const float* value_cache,
+                              const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                              const uint32_t* context_lens, uint32_t max_context_len,
+                              uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                              uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                              float scale, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    if (!head_size_ok(head_size) || block_size == 0 || num_heads == 0 || num_kv_heads == 0 ||
+        num_heads % num_kv_heads != 0)
+        return Q8_ERR_SHAPE;
+    if (static_cast<uint64_t>(q_stride) < static_cast<uint64_t>(num_heads) * head_size) return Q8_ERR_SHAPE;
+    if (!std::isfinite(scale)) return Q8_ERR_SHAPE;
+    if (max_context_len > 0 && (max_num_blocks_per_seq == 0 || num_blocks == 0)) return Q8_ERR_SHAPE;
+    if (head_size != 16 && head_size != 32 && head_size != 64 && head_size != 128 && head_size != 256)
+        return Q8_ERR_UNSUPPORTED;
+    if (max_context_len >= 0x80000000u || q_stride % 4 != 0) return Q8_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return Q8_OK;
+    if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens) return Q8_ERR_NULL;
+    for (const void* p : {static_cast<const void*>(out), static_cast<const void*>(q),
+                          static_cast<const void*>(key_cache), static_cast<const void*>(value_cache)})
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return Q8_ERR_UNSUPPORTED;
+    const q8kv::F32DecodePlan p = q8kv::plan_f32_decode(num_seqs, num_heads, num_kv_heads, head_size);
+    if (p.num_waves > 0x7FFFFFFFull) return Q8_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < p.bytes || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return Q8_ERR_WORKSPACE;
+    q8kv::F32DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    char* ws = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(ws + p.counters_offset);
+    a.part_acc = reinterpret_cast<float*>(ws + p.acc_offset);
+    a.part_ml = reinterpret_cast<float*>(ws + p.ml_offset);
+    a.q_stride = q_stride;
+    a.max_num_blocks_per_seq = max_num_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_size = head_size;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    a.group = p.group;
+    a.num_groups = p.num_groups;
+    a.waves_per_rg = p.waves_per_rg;
+    a.recs_per_rg = p.recs_per_rg;
+    a.inv_block_size = 1.0f / static_cast<float>(block_size);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const hipError_t e = q8kv::launch_f32_decode(a, p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
 int q8_last_hip_error(void) { return g_last_hip_error; }
 
 const char* q8_status_string(q8_status status) {

@@ -12,22 +12,23 @@
 // MI355X design (not the page's one-workgroup-per-(seq, head) three-pass
 // shader):
 //   * Positions are processed in chunks of 64.  For one row group (kv head,
-//     up to 8 query heads sharing it) the chunks of all sequences form one
-//     sequence of C chunks; a fixed number of persistent wavefronts per row
-//     group each take an equal contiguous range of it (the split-context idea
-//     of the "attention.rs" page, balanced over the whole batch instead of per
-//     sequence), so every wave does the same amount of work and there is no
-//     tail.  A wave that covers a whole sequence writes its output directly;
-//     otherwise it writes softmax partials (running max, sum, unnormalized
-//     output) and a merge kernel combines them.  Wavefronts are numbered kv
-//     head fastest, so the kv-head slices of the same cache blocks are
+//     up to 8 of its query heads; in multi-row decode, up to 8 (row, head)
+//     pairs) the chunks of all sequences form one sequence of C chunks, and a
+//     fixed number of persistent wavefronts per row group each take an equal
+//     contiguous range of it, weighted by cost (each nonempty sequence adds
+//     one unit for its fixed work).  This is the split-context idea of the
+//     "attention.rs" page, balanced over the whole batch instead of per
+//     sequence.  A wave that covers a whole sequence writes its output
+//     directly; otherwise it writes a softmax partial (running max, sum,
+//     unnormalized output) with device-coherent stores, and the last wave to
+//     arrive for that sequence combines the partials.  Wavefronts are numbered
+//     kv head fastest, so the kv-head slices of the same cache blocks are
 //     requested together.  Each K/V byte is read once per row group.
 //   * A chunk of 64 consecutive, 64-aligned positions is a run of whole cache
-//     tiles (or one 64-row slice of a larger tile): it is fetched with
-//     coalesced 16-byte loads into registers, up to two chunks ahead of use,
-//     then written to LDS.  The loads are unconditional (masked slots read a
-//     fixed line), so the compiler's wait counts stay exact across the loop.
-//     Other chunks (visible lists with gaps) are gathered row by row.
+//     tiles (or one 64-row slice of a larger tile), fetched one chunk ahead
+//     with coalesced 16-byte loads: at head sizes up to 128 straight into one
+//     of two LDS buffers (LDS-direct loads), otherwise into registers and
+//     then LDS.  Visible lists with gaps are gathered row by row.
 //   * Both contractions run on the int8 matrix cores
 //     (v_mfma_i32_16x16x64_i8), whose operands include the cache's own codes:
 //       q.K^T: each query head's q row is scaled by a power of two and rounded
@@ -38,15 +39,16 @@
 //       scaled by a power of two and rounded to integers below 2^29, again as
 //       four digits; rows (4 heads x 4 digits), k = 64 tokens, columns 16 head
 //       dimensions.  V codes are transposed to token-major bytes with v_perm.
-//     The int32 digit sums are exact and are combined exactly in f64; q and
-//     the weights keep 30 significant bits, finer than binary32, so the result
-//     carries f32-level rounding error only.
+//     The int32 digit sums are exact; they are combined in binary32 with a
+//     single rounding per step, so q and the weights keep about 30
+//     significant bits and the result carries f32-level rounding error only.
 //   * Online softmax in the exp2 domain (scale folded with log2 e).  Each
 //     MFMA output row group is one head, so the per-head max and sum reduce
 //     over the 16 lanes of a DPP row.
 #pragma once
 #include "decode_split.h"
 #include "q8_pack.h"
+#include "wave_ops.h"
 
 namespace q8kv {
 namespace {
@@ -94,63 +96,12 @@ __device__ __forceinline__ void transpose4(const uint32_t x[4], uint32_t y[4]) {
     y[3] = perm(t23h, t01h, 0x07060302u);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kRowRor1 = 0x121;
-constexpr int kRowRor2 = 0x122;
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;
-
-// Reductions over the 16 lanes of a DPP row (rotations within the row).
-__device__ __forceinline__ float row_max(float v) {
-    v = fmaxf(v, dpp_mov<kRowRor1>(v));
-    v = fmaxf(v, dpp_mov<kRowRor2>(v));
-    v = fmaxf(v, dpp_mov<kRowRor4>(v));
-    return fmaxf(v, dpp_mov<kRowRor8>(v));
-}
-__device__ __forceinline__ float row_sum(float v) {
-    v += dpp_mov<kRowRor1>(v);
-    v += dpp_mov<kRowRor2>(v);
-    v += dpp_mov<kRowRor4>(v);
-    return v + dpp_mov<kRowRor8>(v);
-}
-
 // Exponent e with |x| < 2^e for finite nonzero x (frexp convention).
 __device__ __forceinline__ int exponent_bound(float x) {
     int e = 0;
     (void)frexpf(x, &e);
     return e;
 }
-
-// LDS hand-off between the lanes of one wavefront: LDS operations of a
-// wavefront execute in order, so only compiler reordering must be prevented
-// (the wavefronts of a workgroup never wait for each other).
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ uint32_t uniform(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
-}
-
-// Inclusive prefix sum over the 64 lanes of the wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t t = __shfl_up(v, d, kWave);
-        if (lane >= static_cast<uint32_t>(d)) v += t;
-    }
-    return v;
-}
-
-__device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t l) {
-    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), static_cast<int>(l)));
-}
-
 
 // Number of positions sequence s attends (in multi-row decode, its last row).
 template <bool VIS>

@@ -72,4 +72,50 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
 
+// ---- f32 paged-cache baseline: cache [num_blocks, num_kv_heads, block_size, head_size] f32 ----
+
+constexpr uint32_t kF32DecodeWaves = 2048;   // persistent waves: 8 per CU (2 workgroups of 4)
+
+struct F32CacheWriteArgs {
+    const float* key;
+    const float* value;
+    float* key_cache;
+    float* value_cache;
+    const uint32_t* slot_mapping;
+    uint32_t key_stride, value_stride;
+    uint32_t num_tokens, num_kv_heads, head_size, block_size, num_blocks;
+};
+
+hipError_t launch_f32_cache_write(const F32CacheWriteArgs& a, hipStream_t stream);
+
+// Row groups are (kv head, group of `group` query heads); each has
+// waves_per_rg persistent waves over its chunk list and recs_per_rg partial
+// record slots.
+struct F32DecodePlan {
+    uint32_t group, num_groups, waves_per_rg, recs_per_rg;
+    uint64_t num_waves;
+    size_t counters_offset, ml_offset, acc_offset, bytes;
+};
+
+F32DecodePlan plan_f32_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads, uint32_t head_size);
+
+struct F32DecodeArgs {
+    float* out;
+    const float* q;
+    const float* key_cache;
+    const float* value_cache;
+    const uint32_t* block_tables;
+    const uint32_t* context_lens;
+    uint32_t* counters;      // [row group, seq]: arrivals of a sequence's waves; zero between calls
+    float* part_ml;          // [row group, record, head in group, 2]: running max (log2 units), sum
+    float* part_acc;         // [row group, record, head in group, head_size]: unnormalized output
+    uint32_t q_stride, max_num_blocks_per_seq, max_context_len;
+    uint32_t num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks;
+    uint32_t group, num_groups, waves_per_rg, recs_per_rg;
+    float inv_block_size;    // 1 / block_size in binary32
+    float scale_log2;        // softmax scale * log2(e)
+};
+
+hipError_t launch_f32_decode(const F32DecodeArgs& a, const F32DecodePlan& p, hipStream_t stream);
+
 }  // namespace q8kv

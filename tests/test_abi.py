@@ -140,3 +140,52 @@ def rows_args(**kw):
 ])
 def test_decode_rows_validation(lib, kw, want):
     assert lib.q8_paged_decode_rows(*rows_args(**kw)) == want
+
+
+def f32_args(**kw):
+    a = dict(out=FAKE, q=FAKE, q_stride=4 * 128, kc=FAKE, vc=FAKE, bt=FAKE, max_nb=8, cl=FAKE, mcl=5000,
+             S=2, H=4, Hkv=2, hs=128, bs=16, nb=64, scale=0.1, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "q_stride", "kc", "vc", "bt", "max_nb", "cl", "mcl", "S", "H", "Hkv",
+                           "hs", "bs", "nb", "scale", "ws", "wsb", "stream")]
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(hs=130), 2), (dict(hs=512), 2), (dict(H=5), 2), (dict(bs=0), 2), (dict(q_stride=511), 2),
+    (dict(scale=float("inf")), 2), (dict(max_nb=0), 2), (dict(hs=96, q_stride=4 * 96), 5),
+    (dict(q_stride=514), 5), (dict(mcl=1 << 31), 5), (dict(out=None), 1), (dict(cl=None), 1),
+    (dict(q=ctypes.c_void_p(0x1008)), 5), (dict(kc=ctypes.c_void_p(0x1004)), 5), (dict(ws=None), 3),
+    (dict(wsb=16), 3), (dict(S=0), 0),
+])
+def test_f32_decode_validation(lib, kw, want):
+    assert lib.q8_f32_paged_decode(*f32_args(**kw)) == want
+
+
+def test_f32_workspace_size_matches_plan(lib):
+    # 2048 persistent waves over the row groups (kv head, group of 4, 2 or 1
+    # query heads); (waves per group + S - 1) records of (head_size + 2)
+    # floats per head, after one arrival counter per (row group, sequence).
+    def want(S, hs, rg, group):
+        recs = 2048 // rg + S - 1
+        slots = rg * recs * group
+        r256 = lambda b: (b + 255) // 256 * 256
+        return r256(rg * S * 4) + r256(slots * hs * 4) + slots * 2 * 4
+    assert lib.q8_f32_paged_decode_workspace_bytes(64, 32, 8, 128) == want(64, 128, 8, 4)
+    assert lib.q8_f32_paged_decode_workspace_bytes(3, 12, 2, 64) == want(3, 64, 6, 2)     # n_rep 6: 3 groups of 2
+    assert lib.q8_f32_paged_decode_workspace_bytes(5, 6, 2, 32) == want(5, 32, 6, 1)      # n_rep 3: single heads
+    assert lib.q8_f32_paged_decode_workspace_bytes(2, 4, 3, 128) == 0                     # inconsistent heads
+
+
+@pytest.mark.parametrize("hs,bs,hkv,stride,nb,want", [
+    (0, 16, 2, 256, 8, 2), (6, 16, 2, 256, 8, 2), (260, 16, 1, 260, 8, 2), (128, 0, 2, 256, 8, 2),
+    (128, 16, 0, 256, 8, 2), (128, 16, 2, 255, 8, 2), (128, 16, 2, 256, 0, 2),
+])
+def test_f32_cache_write_shape_errors(lib, hs, bs, hkv, stride, nb, want):
+    assert lib.q8_f32_cache_write(FAKE, stride, FAKE, stride, FAKE, FAKE, FAKE, 4, hkv, hs, bs, nb, None) == want
+
+
+def test_f32_cache_write_null_empty_and_alignment(lib):
+    assert lib.q8_f32_cache_write(None, 256, FAKE, 256, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    assert lib.q8_f32_cache_write(None, 256, None, 256, None, None, None, 0, 2, 128, 16, 8, None) == 0
+    assert lib.q8_f32_cache_write(FAKE, 256, FAKE, 256, ctypes.c_void_p(0x1004), FAKE, FAKE, 4, 2, 128, 16, 8,
+                                  None) == 5
