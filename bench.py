@@ -40,8 +40,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q8_paged_decode_llama_traffic.txt
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--layers", type=int, default=8, help="layer caches rotated over (MALL defeat)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -110,7 +110,8 @@ def main():
 
     import torch
     from int8_paged_kv_amd import (q8_cache_write, q8_decode_step, q8_paged_decode, q8_paged_decode_rows,
-                                   q8_paged_decode_workspace_bytes, load_library)
+                                   q8_paged_decode_workspace_bytes, q8_f32_cache_write, q8_f32_paged_decode,
+                                   q8_f32_paged_decode_workspace_bytes, load_library)
     from int8_paged_kv_amd import workloads as wl
 
     load_library()
@@ -222,6 +223,55 @@ def main():
                  "effective_kv_bytes": Br, "effective_GBps": round(Br / (float(tr.mean()) * 1e-6) / 1e9, 1),
                  "note": "bytes counted per row over its own causal prefix; the rows of a sequence share the reads"}
 
+    # ---- the same step over an f32 paged cache (4 bytes per element, no scale word) ----
+    f32ref = None
+    if not args.no_reference:
+        nbt = w.num_blocks + 1          # the workload's caches carry one reserved block
+        f32_layers = []
+        for li in range(2):             # 2.6 GB per layer: a step's 1.27 GB of f32 KV already exceeds the MALL
+            kf = torch.full((nbt, Hkv, w.block_size, hs), float("nan"), dtype=torch.float32, device=dev)
+            vf = torch.full_like(kf, float("nan"))
+            f32_layers.append((kf, vf))
+        for slots, k, v in fill_host:
+            sl, kd, vd = u32(slots), f32(k), f32(v)
+            for kf, vf in f32_layers:
+                q8_f32_cache_write(kd, vd, kf, vf, sl, Hkv, hs, w.block_size)
+        wsf = torch.zeros(max(16, q8_f32_paged_decode_workspace_bytes(S, H, Hkv, hs)), dtype=torch.uint8, device=dev)
+        outf = torch.empty((S, H, hs), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+        def f32_step(i, ev=None):
+            kf, vf = f32_layers[i % len(f32_layers)]
+            if ev is not None:
+                ev[0].record()
+            q8_f32_cache_write(sk, sv, kf, vf, ss, Hkv, hs, w.block_size)
+            if ev is not None:
+                ev[1].record()
+            q8_f32_paged_decode(q, kf, vf, bt, cl, w.scale, Hkv, w.block_size, max_context_len=mcl,
+                                out=outf, workspace=wsf)
+            if ev is not None:
+                ev[2].record()
+
+        for i in range(5):
+            f32_step(i)
+        torch.cuda.synchronize()
+        nf = min(100, max(20, args.steps // 4))
+        evf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nf)]
+        for i in range(nf):
+            f32_step(i, evf[i])
+        torch.cuda.synchronize()
+        tfw = np.array([e[0].elapsed_time(e[1]) for e in evf]) * 1e3
+        tfd = np.array([e[1].elapsed_time(e[2]) for e in evf]) * 1e3
+        Bf = int(w.attended_counts().sum()) * Hkv * 2 * hs * 4
+        f32ref = {"cache_write_us_mean": round(float(tfw.mean()), 2),
+                  "decode_us_mean": round(float(tfd.mean()), 2),
+                  "f32_kv_bytes": Bf,
+                  "decode_f32_kv_GBps": round(Bf / (float(tfd.mean()) * 1e-6) / 1e9, 1),
+                  "int8_step_speedup": round(float(tfw.mean() + tfd.mean()) / float(t_dec.mean()), 3),
+                  "note": "q8_f32_cache_write + q8_f32_paged_decode of the same step over an f32 cache "
+                          "[num_blocks, Hkv, bs, hs]; speedup = f32 step time / int8 one-launch step time"}
+        del f32_layers
+
     hot = None
     if args.hot:
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -296,6 +346,7 @@ def main():
                    "seq_heads_per_s": round(S * H / (dec_mean * 1e-6), 1)},
         "two_launch_reference": reference,
         "multi_row_decode": multi,
+        "f32_cache_reference": f32ref,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "q8_decode_step (one launch: decode_split_kernel, appending the step's tokens)",
