@@ -64,6 +64,17 @@ def _load():
         lib.q8o_f32_paged_decode.restype = ctypes.c_int
         lib.q8o_f32_paged_decode_units.argtypes = [P, P, U] + f32dec
         lib.q8o_f32_paged_decode_units.restype = ctypes.c_int
+        F = ctypes.c_float
+        lib.q8o_rope_table.argtypes = [P, U, U, F]
+        lib.q8o_rope_table.restype = ctypes.c_int
+        lib.q8o_norm_rope_row.argtypes = [P, U, P, P, U, F, P]
+        lib.q8o_norm_rope_row.restype = ctypes.c_int
+        lib.q8o_norm_rope_row_f64.argtypes = [P, U, P, U, U, ctypes.c_double, ctypes.c_double, P]
+        lib.q8o_norm_rope_row_f64.restype = ctypes.c_int
+        lib.q8o_norm_rope.argtypes = [P, U, P, U, U, U, U, U, P, P, P, U, U, F]
+        lib.q8o_norm_rope.restype = ctypes.c_int
+        lib.q8o_norm_rope_cache_write.argtypes = [P, U, P, U, P, P, P, P, P, P, U, U, F, U, U, U, U, U]
+        lib.q8o_norm_rope_cache_write.restype = ctypes.c_int
         lib.q8o_max_threads.argtypes = []
         lib.q8o_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -247,3 +258,73 @@ def f32_paged_decode_units(units, q, key_cache, value_cache, block_tables, conte
                                               _ptr(cl), mcl, S, H, num_kv_heads, hs, block_size, nb,
                                               float(scale), nthreads), "f32_paged_decode_units")
     return out
+
+
+# ---------------------------------------------------------------- norm + rotary ----
+
+def rope_table(num_positions: int, rot: int, theta: float) -> np.ndarray:
+    """[num_positions, rot] f32: cos then sin of p * theta^(-2i/rot), i < rot/2."""
+    t = np.zeros((num_positions, max(rot, 1)), dtype=np.float32)
+    _check(_load().q8o_rope_table(_ptr(t), num_positions, rot, float(theta)), "rope_table")
+    return t[:, :rot] if rot else t[:, :0]
+
+
+def norm_rope_row(x, weight, cs_row, rot: int, eps: float) -> np.ndarray:
+    """One head vector through RMSNorm (weight) and the rotary step (table row cs_row)."""
+    x = _c(x, np.float32)
+    w = _c(weight, np.float32)
+    cs = _c(cs_row if rot else np.zeros(1, np.float32), np.float32)
+    y = np.zeros(x.shape[-1], dtype=np.float32)
+    _check(_load().q8o_norm_rope_row(_ptr(x), x.shape[-1], _ptr(w), _ptr(cs), rot, float(eps), _ptr(y)),
+           "norm_rope_row")
+    return y
+
+
+def norm_rope_row_f64(x, weight, pos: int, rot: int, theta: float, eps: float) -> np.ndarray:
+    """The same definition in binary64 throughout, angles straight from theta."""
+    x = _c(x, np.float32)
+    w = _c(weight, np.float32)
+    y = np.zeros(x.shape[-1], dtype=np.float64)
+    _check(_load().q8o_norm_rope_row_f64(_ptr(x), x.shape[-1], _ptr(w), int(pos), rot, float(theta),
+                                         float(eps), _ptr(y)), "norm_rope_row_f64")
+    return y
+
+
+def norm_rope(x, positions, weight, table, rot: int, eps: float, num_heads: int, head_size: int,
+              x_stride=None, head_stride=None) -> np.ndarray:
+    """Rows of heads: head h of row t at x.flat[t*x_stride + h*head_stride]; returns
+    [num_rows, num_heads, head_size] f32."""
+    x = _c(x, np.float32)
+    positions = _c(positions, np.uint32)
+    T = positions.shape[0]
+    hst = head_size if head_stride is None else head_stride
+    xs = x_stride if x_stride is not None else (x.size // T if T else num_heads * hst)
+    table = _c(table if rot else np.zeros((1, 1), np.float32), np.float32)
+    out = np.zeros((T, num_heads, head_size), dtype=np.float32)
+    _check(_load().q8o_norm_rope(_ptr(out), num_heads * head_size, _ptr(x), xs, hst, T, num_heads, head_size,
+                                 _ptr(positions), _ptr(_c(weight, np.float32)), _ptr(table), rot,
+                                 table.shape[0] if rot else 0, float(eps)), "norm_rope")
+    return out
+
+
+def norm_rope_cache_write(key, value, key_cache, value_cache, slot_mapping, positions, weight, table, rot: int,
+                          eps: float, num_kv_heads, head_size, block_size, num_blocks=None,
+                          key_stride=None, value_stride=None):
+    """cache_write with K rows first taken through norm_rope_row at positions[t] (in place)."""
+    key = _c(key, np.float32)
+    value = _c(value, np.float32)
+    slot_mapping = _c(slot_mapping, np.uint32)
+    positions = _c(positions, np.uint32)
+    for c in (key_cache, value_cache):
+        if c.dtype != np.uint32 or not c.flags.c_contiguous:
+            raise ValueError("caches must be contiguous uint32 arrays")
+    T = slot_mapping.shape[0]
+    ks = key_stride if key_stride is not None else (key.size // T if T else num_kv_heads * head_size)
+    vs = value_stride if value_stride is not None else (value.size // T if T else num_kv_heads * head_size)
+    wpt = head_size // 4 + 1
+    nb = num_blocks if num_blocks is not None else key_cache.size // (num_kv_heads * block_size * wpt)
+    table = _c(table if rot else np.zeros((1, 1), np.float32), np.float32)
+    _check(_load().q8o_norm_rope_cache_write(_ptr(key), ks, _ptr(value), vs, _ptr(key_cache), _ptr(value_cache),
+                                             _ptr(slot_mapping), _ptr(positions), _ptr(_c(weight, np.float32)),
+                                             _ptr(table), rot, table.shape[0] if rot else 0, float(eps), T,
+                                             num_kv_heads, head_size, block_size, nb), "norm_rope_cache_write")

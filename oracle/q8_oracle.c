@@ -50,6 +50,26 @@
  *   writer copies rows; the decode is the definition above with
  *   k_hat, v_hat the stored f32 values (exact in binary64).
  *
+ *   Norm + rotary step ahead of the cache write (the "attention.rs" page: the
+ *   q/k norm-and-rope dispatches before the q8 append, with a learned per-head
+ *   norm weight, rot = head_dim * partial_rotary_factor rotated elements, the
+ *   model's rope theta and rms eps, and row b at position base_pos + b).  The
+ *   page does not print the kernel body; the reading taken is the usual
+ *   per-head RMSNorm followed by a rotate-half rotary embedding of the first
+ *   rot elements:
+ *     r     = 1 / sqrt(mean_d x_d^2 + eps)
+ *     n_d   = x_d * r * w_d
+ *     for i < rot/2, with a = n_i, b = n_{i+rot/2}, phi = pos * theta^(-2i/rot):
+ *       y_i = a cos(phi) - b sin(phi),   y_{i+rot/2} = b cos(phi) + a sin(phi)
+ *     y_d = n_d for d >= rot.
+ *   The result feeds the quantizer, whose codes are decided in binary32, so
+ *   the rounding points are fixed: mean_d x_d^2 + eps, the square root and the
+ *   reciprocal in binary64, r rounded to binary32; x*r and then *w, each one
+ *   binary32 product; cos and sin in binary64, rounded to binary32 (a table
+ *   per position); each rotated element as binary32 products and one binary32
+ *   sum.  q8o_norm_rope_row_f64 is the same definition in binary64 throughout
+ *   (angles straight from theta), the reference the pins check against.
+ *
  * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fopenmp -fPIC
  * -shared.  On x86-64 (SSE, FLT_EVAL_METHOD == 0) every float operation above
  * rounds to binary32 once.  OpenMP only spreads independent (seq, head) units
@@ -403,6 +423,140 @@ int q8o_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
                                         num_kv_heads, head_size, block_size, num_blocks,
                                         scale, nthreads);
     free(units);
+    return rc;
+}
+
+/* ---------------------------------------------------- norm + rotary ---- */
+
+static int rope_shape_ok(uint32_t head_size, uint32_t rot)
+{
+    return head_size > 0 && head_size % 4 == 0 && rot % 2 == 0 && rot <= head_size;
+}
+
+/* Rotary table, one row of rot floats per position p < num_positions:
+ * row[i] = cos(p * theta^(-2i/rot)), row[rot/2 + i] = sin(...), i < rot/2,
+ * each evaluated in binary64 and rounded to binary32. */
+int q8o_rope_table(float* table, uint32_t num_positions, uint32_t rot, float theta)
+{
+    if (rot % 2 != 0 || !(theta > 0.0f)) return Q8O_ERR_SHAPE;
+    uint32_t half = rot / 2;
+    for (uint32_t p = 0; p < num_positions; ++p)
+        for (uint32_t i = 0; i < half; ++i) {
+            double inv_freq = pow((double)theta, -(2.0 * i) / (double)rot);
+            double phi = (double)p * inv_freq;
+            table[(uint64_t)p * rot + i] = (float)cos(phi);
+            table[(uint64_t)p * rot + half + i] = (float)sin(phi);
+        }
+    return Q8O_OK;
+}
+
+/* One head vector x[0..head_size) at the rounding points stated above; cs is
+ * the rotary table row of the vector's position (unused when rot == 0). */
+int q8o_norm_rope_row(const float* x, uint32_t head_size, const float* weight, const float* cs,
+                      uint32_t rot, float eps, float* y)
+{
+    if (!rope_shape_ok(head_size, rot)) return Q8O_ERR_SHAPE;
+    double ss = 0.0;
+    for (uint32_t d = 0; d < head_size; ++d) {
+        if (!isfinite(x[d])) return Q8O_ERR_INPUT;
+        ss += (double)x[d] * (double)x[d];
+    }
+    float r = (float)(1.0 / sqrt(ss / (double)head_size + (double)eps));
+    for (uint32_t d = 0; d < head_size; ++d) {
+        float t = x[d] * r;
+        y[d] = t * weight[d];
+    }
+    uint32_t half = rot / 2;
+    for (uint32_t i = 0; i < half; ++i) {
+        float a = y[i], b = y[i + half];
+        float c = cs[i], sn = cs[half + i];
+        float ac = a * c, bs = b * sn, bc = b * c, as = a * sn;
+        y[i] = ac - bs;
+        y[i + half] = bc + as;
+    }
+    return Q8O_OK;
+}
+
+/* The same definition in binary64, with the angle taken straight from theta. */
+int q8o_norm_rope_row_f64(const float* x, uint32_t head_size, const float* weight, uint32_t pos,
+                          uint32_t rot, double theta, double eps, double* y)
+{
+    if (!rope_shape_ok(head_size, rot)) return Q8O_ERR_SHAPE;
+    double ss = 0.0;
+    for (uint32_t d = 0; d < head_size; ++d) ss += (double)x[d] * (double)x[d];
+    double r = 1.0 / sqrt(ss / (double)head_size + eps);
+    for (uint32_t d = 0; d < head_size; ++d) y[d] = (double)x[d] * r * (double)weight[d];
+    uint32_t half = rot / 2;
+    for (uint32_t i = 0; i < half; ++i) {
+        double phi = (double)pos * pow(theta, -(2.0 * i) / (double)rot);
+        double a = y[i], b = y[i + half];
+        y[i] = a * cos(phi) - b * sin(phi);
+        y[i + half] = b * cos(phi) + a * sin(phi);
+    }
+    return Q8O_OK;
+}
+
+/* Rows of f32 head vectors: head h of row t at x[t*x_stride + h*head_stride],
+ * written to out[t*out_stride + h*head_size]; row t at positions[t]. */
+int q8o_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t x_stride, uint32_t head_stride,
+                  uint32_t num_rows, uint32_t num_heads, uint32_t head_size, const uint32_t* positions,
+                  const float* weight, const float* table, uint32_t rot, uint32_t num_positions, float eps)
+{
+    if (!rope_shape_ok(head_size, rot) || head_stride < head_size ||
+        (uint64_t)out_stride < (uint64_t)num_heads * head_size)
+        return Q8O_ERR_SHAPE;
+    for (uint32_t t = 0; t < num_rows; ++t) {
+        uint32_t p = positions[t];
+        if (rot > 0 && p >= num_positions) return Q8O_ERR_RANGE;
+        for (uint32_t h = 0; h < num_heads; ++h) {
+            int rc = q8o_norm_rope_row(x + (uint64_t)t * x_stride + (uint64_t)h * head_stride, head_size,
+                                       weight, table + (uint64_t)p * rot, rot, eps,
+                                       out + (uint64_t)t * out_stride + (uint64_t)h * head_size);
+            if (rc != Q8O_OK) return rc;
+        }
+    }
+    return Q8O_OK;
+}
+
+/* Cache write with the norm + rotary step on K: for each non-pad token, each
+ * kv head's K vector becomes q8o_norm_rope_row of it (at positions[t]) and is
+ * then packed as q8o_cache_write packs it; V is packed unchanged. */
+int q8o_norm_rope_cache_write(const float* key, uint32_t key_stride,
+                              const float* value, uint32_t value_stride,
+                              uint32_t* key_cache, uint32_t* value_cache,
+                              const uint32_t* slot_mapping, const uint32_t* positions,
+                              const float* weight, const float* table, uint32_t rot,
+                              uint32_t num_positions, float eps, uint32_t num_tokens,
+                              uint32_t num_kv_heads, uint32_t head_size,
+                              uint32_t block_size, uint32_t num_blocks)
+{
+    if (head_size == 0 || head_size % 4 != 0 || block_size == 0 || num_kv_heads == 0 ||
+        !rope_shape_ok(head_size, rot))
+        return Q8O_ERR_SHAPE;
+    if ((uint64_t)key_stride < (uint64_t)num_kv_heads * head_size ||
+        (uint64_t)value_stride < (uint64_t)num_kv_heads * head_size)
+        return Q8O_ERR_SHAPE;
+    uint32_t wpt = head_size / 4 + 1;
+    float* y = (float*)malloc(sizeof(float) * head_size);
+    if (!y) return Q8O_ERR_NOMEM;
+    int rc = Q8O_OK;
+    for (uint32_t t = 0; t < num_tokens && rc == Q8O_OK; ++t) {
+        uint32_t slot = slot_mapping[t];
+        if (slot == Q8O_PAD_SLOT) continue;
+        uint64_t block = slot / block_size, off = slot % block_size;
+        uint32_t p = positions[t];
+        if (block >= num_blocks || (rot > 0 && p >= num_positions)) { rc = Q8O_ERR_RANGE; break; }
+        for (uint32_t h = 0; h < num_kv_heads && rc == Q8O_OK; ++h) {
+            uint64_t dst = row_offset(block, off, h, num_kv_heads, block_size, wpt);
+            rc = q8o_norm_rope_row(key + (uint64_t)t * key_stride + (uint64_t)h * head_size, head_size,
+                                   weight, table + (uint64_t)p * rot, rot, eps, y);
+            if (rc == Q8O_OK) rc = q8o_quantize_row(y, head_size, key_cache + dst);
+            if (rc == Q8O_OK)
+                rc = q8o_quantize_row(value + (uint64_t)t * value_stride + (uint64_t)h * head_size,
+                                      head_size, value_cache + dst);
+        }
+    }
+    free(y);
     return rc;
 }
 
