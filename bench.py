@@ -111,7 +111,8 @@ def main():
     import torch
     from int8_paged_kv_amd import (q8_cache_write, q8_decode_step, q8_paged_decode, q8_paged_decode_rows,
                                    q8_paged_decode_workspace_bytes, q8_f32_cache_write, q8_f32_paged_decode,
-                                   q8_f32_paged_decode_workspace_bytes, load_library)
+                                   q8_f32_paged_decode_workspace_bytes, q8_rope_table, q8_norm_rope,
+                                   q8_norm_rope_cache_write, load_library)
     from int8_paged_kv_amd import workloads as wl
 
     load_library()
@@ -272,6 +273,83 @@ def main():
                           "[num_blocks, Hkv, bs, hs]; speedup = f32 step time / int8 one-launch step time"}
         del f32_layers
 
+    # ---- per-head RMSNorm + partial rotary step ahead of the write (rot = head_size/2) ----
+    normrope = None
+    if not args.no_reference:
+        rot, P = hs // 2, 8192
+        g = np.random.default_rng(12)
+        table = q8_rope_table(P, rot, 10000.0, device=dev)
+        kn = f32((1.0 + 0.1 * g.standard_normal(hs)).astype(np.float32))
+        qn = f32((1.0 + 0.1 * g.standard_normal(hs)).astype(np.float32))
+        step_pos = u32(np.minimum(np.asarray(w.context_lens, dtype=np.int64), mcl) - 1)
+        qnr = torch.empty_like(q)
+        outn = torch.empty_like(out)      # the main step's output stays for the parity check
+        q2 = q.view(S, H * hs)
+
+        def nr_step(i, ev=None):
+            kc, vc = layers[i % len(layers)]
+            if ev is not None:
+                ev[0].record()
+            q8_norm_rope(q2, step_pos, qn, table, rot, 1e-6, H, hs, out=qnr)
+            if ev is not None:
+                ev[1].record()
+            q8_norm_rope_cache_write(sk, sv, kc, vc, ss, step_pos, kn, table, rot, 1e-6, Hkv, hs, w.block_size)
+            if ev is not None:
+                ev[2].record()
+            q8_paged_decode(qnr, kc, vc, bt, cl, w.scale, Hkv, w.block_size, max_context_len=mcl, out=outn,
+                            workspace=ws)
+            if ev is not None:
+                ev[3].record()
+
+        for i in range(5):
+            nr_step(i)
+        torch.cuda.synchronize()
+        nn_ = 100
+        evn = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nn_)]
+        for i in range(nn_):
+            nr_step(i, evn[i])
+        torch.cuda.synchronize()
+        tq = np.array([e[0].elapsed_time(e[1]) for e in evn]) * 1e3
+        tw = np.array([e[1].elapsed_time(e[2]) for e in evn]) * 1e3
+        td = np.array([e[2].elapsed_time(e[3]) for e in evn]) * 1e3
+        # bulk: 16384 tokens at scattered slots of a separate cache, fused vs plain writer
+        Tb = 16384
+        nbb = Tb // w.block_size + 64
+        kb_ = torch.zeros(((nbb + 1) * Hkv * w.block_size * (hs // 4 + 1),), dtype=torch.int32, device=dev)
+        vb_ = torch.zeros_like(kb_)
+        bk = f32(g.standard_normal((Tb, Hkv, hs)).astype(np.float32))
+        bv = f32(g.standard_normal((Tb, Hkv, hs)).astype(np.float32))
+        bslots = u32(g.choice(nbb * w.block_size, size=Tb, replace=False).astype(np.uint32))
+        bpos = u32(g.integers(0, P, Tb).astype(np.uint32))
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(30)]
+        for i in range(35):
+            e = evb[i - 5] if i >= 5 else None
+            if e is not None:
+                e[0].record()
+            q8_norm_rope_cache_write(bk, bv, kb_, vb_, bslots, bpos, kn, table, rot, 1e-6, Hkv, hs, w.block_size)
+            if e is not None:
+                e[1].record()
+            q8_cache_write(bk, bv, kb_, vb_, bslots, Hkv, hs, w.block_size)
+            if e is not None:
+                e[2].record()
+        torch.cuda.synchronize()
+        tbf = np.array([e[0].elapsed_time(e[1]) for e in evb]) * 1e3
+        tbp = np.array([e[1].elapsed_time(e[2]) for e in evb]) * 1e3
+        Bb = Tb * Hkv * (2 * hs * 4 + 2 * (hs + 4)) + 4 * Tb       # f32 K/V read, packed rows written, slots
+        normrope = {"rot": rot, "theta": 10000.0,
+                    "q_norm_rope_us_mean": round(float(tq.mean()), 2),
+                    "norm_rope_cache_write_us_mean": round(float(tw.mean()), 2),
+                    "decode_us_mean": round(float(td.mean()), 2),
+                    "bulk_tokens": Tb,
+                    "bulk_norm_rope_cache_write_us_mean": round(float(tbf.mean()), 2),
+                    "bulk_plain_cache_write_us_mean": round(float(tbp.mean()), 2),
+                    "bulk_algorithmic_bytes": Bb,
+                    "bulk_norm_rope_GBps": round(Bb / (float(tbf.mean()) * 1e-6) / 1e9, 1),
+                    "bulk_norm_rope_frac_hbm_peak": round(Bb / (float(tbf.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "note": "the step with q8_norm_rope on q rows and q8_norm_rope_cache_write for the new K/V "
+                            "(three launches), then a 16384-token bulk write; positions L-1 for the step"}
+        del kb_, vb_
+
     hot = None
     if args.hot:
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -347,6 +425,7 @@ def main():
         "two_launch_reference": reference,
         "multi_row_decode": multi,
         "f32_cache_reference": f32ref,
+        "norm_rope_step": normrope,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "q8_decode_step (one launch: decode_split_kernel, appending the step's tokens)",

@@ -289,6 +289,69 @@ q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
                               float scale, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Per-head RMSNorm + partial rotary embedding.  The "attention.rs" page
+ * normalizes q and k per head with a learned weight (rms eps) and rotates
+ * the first rot = head_dim * partial_rotary_factor elements at the row's
+ * position (rope theta) before the q8 append (its q/k norm-and-rope
+ * dispatches); the kernel body is not printed.  Computed here, per head
+ * vector x of head_size elements at position pos:
+ *   r   = 1 / sqrt(mean_d x_d^2 + eps)          (binary64, rounded to f32)
+ *   n_d = (x_d * r) * w_d                        (binary32 products)
+ *   for i < rot/2, a = n_i, b = n_{i+rot/2}, c/s = table[pos][i], table[pos][rot/2 + i]:
+ *     y_i = a*c - b*s,   y_{i+rot/2} = b*c + a*s (binary32, never fused)
+ *   y_d = n_d for d >= rot.
+ * rot must be 0 or a multiple of 8 not above head_size.  Inputs must be
+ * finite; a zero vector with eps == 0 is outside the contract.
+ *
+ * q8_rope_table -- fill the rotary table: table[p*rot + i] =
+ * cos(p * theta^(-2i/rot)) and table[p*rot + rot/2 + i] = sin(p *
+ * theta^(-2i/rot)) for p < num_positions, i < rot/2, each evaluated in
+ * binary64 and rounded to f32.  table: caller-owned device f32 array of
+ * num_positions*rot elements.  Q8_ERR_SHAPE when rot is odd or theta is not
+ * positive and finite; Q8_ERR_NULL for a NULL table with rot*num_positions > 0.
+ */
+q8_status q8_rope_table(float* table, uint32_t num_positions, uint32_t rot, float theta, void* stream);
+
+/*
+ * q8_norm_rope -- the step above on rows of heads (the q side): head h of row
+ * t is read at x[t*x_stride + h*head_stride + d] and written to
+ * out[t*out_stride + h*head_size + d], at position positions[t].
+ *   weight     device f32 [head_size], shared by the heads.
+ *   table      device f32 [num_positions, rot] from q8_rope_table (unused and
+ *              may be NULL when rot == 0, as may positions).
+ * positions[t] < num_positions is a caller contract (out-of-range values are
+ * clamped, not reported).  out must not overlap x unless out == x with
+ * matching strides (in place).  Errors: Q8_ERR_NULL; Q8_ERR_SHAPE when
+ * head_size is not a multiple of 4 or above 256, rot is not a multiple of 8
+ * or exceeds head_size, head_stride < head_size, x_stride or out_stride is
+ * too small for num_heads heads, eps is negative or not finite, or rot > 0
+ * with num_positions == 0.  num_rows == 0 enqueues nothing.
+ */
+q8_status q8_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t x_stride,
+                       uint32_t head_stride, uint32_t num_rows, uint32_t num_heads, uint32_t head_size,
+                       const uint32_t* positions, const float* weight, const float* table,
+                       uint32_t rot, uint32_t num_positions, float eps, void* stream);
+
+/*
+ * q8_norm_rope_cache_write -- q8_cache_write with the step above applied to
+ * the K vectors first: for each token whose slot is not Q8_PAD_SLOT, each kv
+ * head's K vector becomes its normalized, rotated self at positions[t]
+ * (weight: the K norm weight) and is packed as q8_cache_write packs it; V is
+ * packed unchanged.  The arguments shared with q8_cache_write mean the same;
+ * weight, table, rot, num_positions and eps are as for q8_norm_rope.  A pad
+ * token's position is not read.  Errors: those of q8_cache_write plus the
+ * shape rules of q8_norm_rope.
+ */
+q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
+                                   const float* value, uint32_t value_stride,
+                                   uint32_t* key_cache, uint32_t* value_cache,
+                                   const uint32_t* slot_mapping, const uint32_t* positions,
+                                   const float* weight, const float* table, uint32_t rot,
+                                   uint32_t num_positions, float eps, uint32_t num_tokens,
+                                   uint32_t num_kv_heads, uint32_t head_size,
+                                   uint32_t block_size, uint32_t num_blocks, void* stream);
+
 /* hipError_t code behind the calling thread's last Q8_ERR_HIP (0 if none). */
 int q8_last_hip_error(void);
 

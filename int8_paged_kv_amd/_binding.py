@@ -59,6 +59,13 @@ def load_library() -> ctypes.CDLL:
         lib.q8_f32_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U,
                                             U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.q8_f32_paged_decode.restype = ctypes.c_int
+        F = ctypes.c_float
+        lib.q8_rope_table.argtypes = [P, U, U, F, P]
+        lib.q8_rope_table.restype = ctypes.c_int
+        lib.q8_norm_rope.argtypes = [P, U, P, U, U, U, U, U, P, P, P, U, U, F, P]
+        lib.q8_norm_rope.restype = ctypes.c_int
+        lib.q8_norm_rope_cache_write.argtypes = [P, U, P, U, P, P, P, P, P, P, U, U, F, U, U, U, U, U, P]
+        lib.q8_norm_rope_cache_write.restype = ctypes.c_int
         lib.q8_last_hip_error.argtypes = []
         lib.q8_last_hip_error.restype = ctypes.c_int
         lib.q8_status_string.argtypes = [ctypes.c_int]
@@ -322,3 +329,63 @@ def q8_f32_paged_decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: t
                                  block_size, num_blocks, float(scale), wp, wb, _stream(stream))
     _check(st, "q8_f32_paged_decode")
     return out
+
+
+def q8_rope_table(num_positions: int, rot: int, theta: float, device=None, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Rotary table [num_positions, rot] f32: cos, then sin, of p * theta^(-2i/rot), i < rot/2."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty((num_positions, rot), dtype=torch.float32, device=device or "cuda")
+    if not out.is_contiguous() or out.numel() != num_positions * rot:
+        raise ValueError("out must be a dense [num_positions, rot] tensor")
+    ptr = _dev(out, "table", torch.float32) if out.numel() else None
+    _check(lib.q8_rope_table(ptr, num_positions, rot, float(theta), _stream(stream)), "q8_rope_table")
+    return out
+
+
+def q8_norm_rope(x: torch.Tensor, positions: Optional[torch.Tensor], weight: torch.Tensor,
+                 table: Optional[torch.Tensor], rot: int, eps: float, num_heads: int, head_size: int,
+                 head_stride: Optional[int] = None, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Per-head RMSNorm + partial rotary step on rows of heads (x is [T, ...] with dense rows;
+    head h of row t starts at element h*head_stride of the row).  Returns [T, num_heads, head_size]."""
+    lib = load_library()
+    T = x.shape[0]
+    xp, xs = _rows(x, "x")
+    hst = head_size if head_stride is None else head_stride
+    if out is None:
+        out = torch.empty((T, num_heads, head_size), dtype=torch.float32, device=x.device)
+    if tuple(out.shape) != (T, num_heads, head_size) or not out.is_contiguous():
+        raise ValueError("out must be a dense [T, num_heads, head_size] tensor")
+    num_positions = table.shape[0] if (table is not None and rot) else 0
+    st = lib.q8_norm_rope(_dev(out, "out", torch.float32), num_heads * head_size, xp, xs, hst, T, num_heads,
+                          head_size, _u32(positions, "positions") if positions is not None else None,
+                          _dev(weight, "weight", torch.float32),
+                          _dev(table, "table", torch.float32) if (table is not None and rot) else None,
+                          rot, num_positions, float(eps), _stream(stream))
+    _check(st, "q8_norm_rope")
+    return out
+
+
+def q8_norm_rope_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                             value_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                             positions: Optional[torch.Tensor], weight: torch.Tensor,
+                             table: Optional[torch.Tensor], rot: int, eps: float, num_kv_heads: int,
+                             head_size: int, block_size: int, num_blocks: Optional[int] = None,
+                             stream=None) -> None:
+    """q8_cache_write with K normalized and rotated at positions[t] first (see include/q8kv.h)."""
+    lib = load_library()
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    wpt = head_size // 4 + 1
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * wpt)
+    num_positions = table.shape[0] if (table is not None and rot) else 0
+    st = lib.q8_norm_rope_cache_write(kp, ks, vp, vs, _u32(key_cache, "key_cache"), _u32(value_cache, "value_cache"),
+                                      _u32(slot_mapping, "slot_mapping"),
+                                      _u32(positions, "positions") if positions is not None else None,
+                                      _dev(weight, "weight", torch.float32),
+                                      _dev(table, "table", torch.float32) if (table is not None and rot) else None,
+                                      rot, num_positions, float(eps), slot_mapping.numel(), num_kv_heads,
+                                      head_size, block_size, num_blocks, _stream(stream))
+    _check(st, "q8_norm_rope_cache_write")

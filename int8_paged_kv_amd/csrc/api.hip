@@ -295,6 +295,95 @@ q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
+q8_status q8_rope_table(float* table, uint32_t num_positions, uint32_t rot, float theta, void* stream) {
+    if (rot % 2 != 0 || !(theta > 0.0f) || !std::isfinite(theta)) return Q8_ERR_SHAPE;
+    if (rot == 0 || num_positions == 0) return Q8_OK;
+    if (!table) return Q8_ERR_NULL;
+    if (static_cast<uint64_t>(num_positions) * (rot / 2) > 0xFFFFFFFFull * 256) return Q8_ERR_UNSUPPORTED;
+    const hipError_t e = q8kv::launch_rope_table(table, num_positions, rot, static_cast<double>(theta),
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+namespace {
+bool rope_shape_ok(uint32_t head_size, uint32_t rot, uint32_t num_positions, float eps) {
+    return head_size_ok(head_size) && rot % 8 == 0 && rot <= head_size && eps >= 0.0f && std::isfinite(eps) &&
+           (rot == 0 || num_positions > 0);
+}
+}  // namespace
+
+q8_status q8_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t x_stride,
+                       uint32_t head_stride, uint32_t num_rows, uint32_t num_heads, uint32_t head_size,
+                       const uint32_t* positions, const float* weight, const float* table,
+                       uint32_t rot, uint32_t num_positions, float eps, void* stream) {
+    if (!rope_shape_ok(head_size, rot, num_positions, eps) || head_stride < head_size) return Q8_ERR_SHAPE;
+    if (num_heads > 0) {
+        const uint64_t span = static_cast<uint64_t>(num_heads - 1) * head_stride + head_size;
+        if (x_stride < span || out_stride < static_cast<uint64_t>(num_heads) * head_size) return Q8_ERR_SHAPE;
+    }
+    if (num_rows == 0 || num_heads == 0) return Q8_OK;
+    if (!out || !x || !weight || (rot > 0 && (!table || !positions))) return Q8_ERR_NULL;
+    if (static_cast<uint64_t>(num_rows) * num_heads > 0xFFFFFFFFull * 4) return Q8_ERR_UNSUPPORTED;
+    q8kv::NormRopeArgs a{};
+    a.out = out;
+    a.x = x;
+    a.positions = positions;
+    a.weight = weight;
+    a.table = table;
+    a.x_stride = x_stride;
+    a.head_stride = head_stride;
+    a.out_stride = out_stride;
+    a.num_rows = num_rows;
+    a.num_heads = num_heads;
+    a.head_size = head_size;
+    a.rot = rot;
+    a.num_positions = num_positions;
+    a.eps = eps;
+    const hipError_t e = q8kv::launch_norm_rope(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
+                                   const float* value, uint32_t value_stride,
+                                   uint32_t* key_cache, uint32_t* value_cache,
+                                   const uint32_t* slot_mapping, const uint32_t* positions,
+                                   const float* weight, const float* table, uint32_t rot,
+                                   uint32_t num_positions, float eps, uint32_t num_tokens,
+                                   uint32_t num_kv_heads, uint32_t head_size,
+                                   uint32_t block_size, uint32_t num_blocks, void* stream) {
+    if (!rope_shape_ok(head_size, rot, num_positions, eps) || block_size == 0 || num_kv_heads == 0)
+        return Q8_ERR_SHAPE;
+    const uint64_t row = static_cast<uint64_t>(num_kv_heads) * head_size;
+    if (key_stride < row || value_stride < row) return Q8_ERR_SHAPE;
+    if (num_tokens == 0) return Q8_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping || !weight ||
+        (rot > 0 && (!table || !positions)))
+        return Q8_ERR_NULL;
+    if (num_blocks == 0) return Q8_ERR_SHAPE;
+    if (static_cast<uint64_t>(num_tokens) * num_kv_heads > 0xFFFFFFFFull * 4) return Q8_ERR_UNSUPPORTED;
+    q8kv::NormRopeCacheWriteArgs a{};
+    a.key = key;
+    a.value = value;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.slot_mapping = slot_mapping;
+    a.positions = positions;
+    a.weight = weight;
+    a.table = table;
+    a.key_stride = key_stride;
+    a.value_stride = value_stride;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.head_size = head_size;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    a.rot = rot;
+    a.num_positions = num_positions;
+    a.eps = eps;
+    const hipError_t e = q8kv::launch_norm_rope_cache_write(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
 int q8_last_hip_error(void) { return g_last_hip_error; }
 
 const char* q8_status_string(q8_status status) {

@@ -23,6 +23,37 @@ struct CacheWriteArgs {
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
 
+// ---- per-head RMSNorm + partial rotary embedding (q rows; fused into the K write) ----
+
+struct NormRopeArgs {
+    float* out;                  // [num_rows, num_heads, head_size] rows of out_stride floats
+    const float* x;              // head h of row t at x[t*x_stride + h*head_stride]
+    const uint32_t* positions;   // [num_rows]
+    const float* weight;         // [head_size] norm weight
+    const float* table;          // [num_positions, rot] rotary cos | sin
+    uint32_t x_stride, head_stride, out_stride;
+    uint32_t num_rows, num_heads, head_size, rot, num_positions;
+    float eps;
+};
+
+struct NormRopeCacheWriteArgs {
+    const float* key;
+    const float* value;
+    uint32_t* key_cache;
+    uint32_t* value_cache;
+    const uint32_t* slot_mapping;
+    const uint32_t* positions;   // [num_tokens]; not read for pad tokens
+    const float* weight;         // [head_size] K norm weight
+    const float* table;          // [num_positions, rot]
+    uint32_t key_stride, value_stride;
+    uint32_t num_tokens, num_kv_heads, head_size, block_size, num_blocks, rot, num_positions;
+    float eps;
+};
+
+hipError_t launch_rope_table(float* table, uint32_t num_positions, uint32_t rot, double theta, hipStream_t stream);
+hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t stream);
+hipError_t launch_norm_rope_cache_write(const NormRopeCacheWriteArgs& a, hipStream_t stream);
+
 // Decode plan shared by the workspace query and the decode call.  For each
 // row group (kv head, group of query heads sharing it) waves_per_rg
 // persistent wavefronts split the batch's 64-position chunks evenly; a

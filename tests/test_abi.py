@@ -189,3 +189,58 @@ def test_f32_cache_write_null_empty_and_alignment(lib):
     assert lib.q8_f32_cache_write(None, 256, None, 256, None, None, None, 0, 2, 128, 16, 8, None) == 0
     assert lib.q8_f32_cache_write(FAKE, 256, FAKE, 256, ctypes.c_void_p(0x1004), FAKE, FAKE, 4, 2, 128, 16, 8,
                                   None) == 5
+
+
+# ---- per-head RMSNorm + partial rotary step ----
+
+def test_rope_table_validation(lib):
+    assert lib.q8_rope_table(FAKE, 16, 7, ctypes.c_float(10000.0), None) == 2      # odd rot
+    assert lib.q8_rope_table(FAKE, 16, 8, ctypes.c_float(0.0), None) == 2          # theta not positive
+    assert lib.q8_rope_table(FAKE, 16, 8, ctypes.c_float(float("inf")), None) == 2
+    assert lib.q8_rope_table(None, 16, 8, ctypes.c_float(10000.0), None) == 1      # NULL table
+    assert lib.q8_rope_table(None, 0, 8, ctypes.c_float(10000.0), None) == 0       # nothing to fill
+    assert lib.q8_rope_table(None, 16, 0, ctypes.c_float(10000.0), None) == 0
+
+
+@pytest.mark.parametrize("hs,rot,hstride,xstride,ostride,npos,eps,want", [
+    (128, 64, 128, 4096, 4096, 16, 1e-6, 0),      # valid, but num_rows == 0 below: nothing enqueued
+    (130, 64, 130, 4160, 4160, 16, 1e-6, 2),      # head_size not a multiple of 4
+    (128, 60, 128, 4096, 4096, 16, 1e-6, 2),      # rot not a multiple of 8
+    (64, 72, 64, 2048, 2048, 16, 1e-6, 2),        # rot above head_size
+    (128, 64, 120, 4096, 4096, 16, 1e-6, 2),      # head_stride < head_size
+    (128, 64, 128, 4000, 4096, 16, 1e-6, 2),      # x_stride too small for 32 heads
+    (128, 64, 128, 4096, 4000, 16, 1e-6, 2),      # out_stride too small
+    (128, 64, 128, 4096, 4096, 0, 1e-6, 2),       # rot > 0 without a table
+    (128, 64, 128, 4096, 4096, 16, -1.0, 2),      # negative eps
+])
+def test_norm_rope_validation(lib, hs, rot, hstride, xstride, ostride, npos, eps, want):
+    assert lib.q8_norm_rope(FAKE, ostride, FAKE, xstride, hstride, 0, 32, hs, FAKE, FAKE, FAKE, rot, npos,
+                            ctypes.c_float(eps), None) == want
+
+
+def test_norm_rope_nulls(lib):
+    args = lambda out, x, pos, w, tab: (out, 4096, x, 4096, 128, 4, 32, 128, pos, w, tab, 64, 16,
+                                        ctypes.c_float(1e-6), None)
+    assert lib.q8_norm_rope(*args(None, FAKE, FAKE, FAKE, FAKE)) == 1
+    assert lib.q8_norm_rope(*args(FAKE, FAKE, None, FAKE, FAKE)) == 1        # rot > 0 needs positions
+    assert lib.q8_norm_rope(*args(FAKE, FAKE, FAKE, FAKE, None)) == 1        # and the table
+    assert lib.q8_norm_rope(*args(FAKE, FAKE, FAKE, None, FAKE)) == 1
+
+
+@pytest.mark.parametrize("hs,bs,hkv,stride,nb,rot,npos,want", [
+    (0, 16, 2, 256, 8, 0, 0, 2), (128, 0, 2, 256, 8, 64, 16, 2), (128, 16, 0, 256, 8, 64, 16, 2),
+    (128, 16, 2, 255, 8, 64, 16, 2), (128, 16, 2, 256, 0, 64, 16, 2), (128, 16, 2, 256, 8, 12, 16, 2),
+    (128, 16, 2, 256, 8, 64, 0, 2),
+])
+def test_norm_rope_cache_write_validation(lib, hs, bs, hkv, stride, nb, rot, npos, want):
+    assert lib.q8_norm_rope_cache_write(FAKE, stride, FAKE, stride, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, rot, npos,
+                                        ctypes.c_float(1e-6), 4, hkv, hs, bs, nb, None) == want
+
+
+def test_norm_rope_cache_write_nulls_and_empty(lib):
+    assert lib.q8_norm_rope_cache_write(FAKE, 256, FAKE, 256, FAKE, FAKE, FAKE, None, FAKE, FAKE, 64, 16,
+                                        ctypes.c_float(1e-6), 4, 2, 128, 16, 8, None) == 1
+    assert lib.q8_norm_rope_cache_write(FAKE, 256, FAKE, 256, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 16,
+                                        ctypes.c_float(1e-6), 4, 2, 128, 16, 8, None) == 1
+    assert lib.q8_norm_rope_cache_write(None, 256, None, 256, None, None, None, None, None, None, 64, 16,
+                                        ctypes.c_float(1e-6), 0, 2, 128, 16, 8, None) == 0
