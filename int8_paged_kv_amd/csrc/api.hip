@@ -339,6 +339,7 @@ q8_status q8_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t
     a.rot = rot;
     a.num_positions = num_positions;
     a.eps = eps;
+    a.params_vec4 = reinterpret_cast<uintptr_t>(weight) % 16 == 0 && reinterpret_cast<uintptr_t>(table) % 16 == 0;
     const hipError_t e = q8kv::launch_norm_rope(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
@@ -380,6 +381,7 @@ q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
     a.rot = rot;
     a.num_positions = num_positions;
     a.eps = eps;
+    a.params_vec4 = reinterpret_cast<uintptr_t>(weight) % 16 == 0 && reinterpret_cast<uintptr_t>(table) % 16 == 0;
     const hipError_t e = q8kv::launch_norm_rope_cache_write(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }

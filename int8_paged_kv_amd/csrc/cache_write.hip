@@ -5,9 +5,10 @@
 // (0xFFFFFFFF) skips the token: nothing is written for it (its source rows
 // may be read).
 //
-// MI355X mapping: one wavefront per (token, kv head).  When head_size <= 128
-// the two 32-lane halves quantize K and V side by side; otherwise the whole
-// wave does K and then V.  Each lane owns one code word: a 16-byte load of four
+// MI355X mapping: one wavefront per (token, kv head), or in large writes per
+// group of consecutive ones whose loads are all in flight together.  When
+// head_size <= 128 the two 32-lane halves quantize K and V side by side;
+// otherwise the whole wave does K and then V.  Each lane owns one code word: a 16-byte load of four
 // f32 values, an amax reduction across the lanes of its half (or wave), four
 // IEEE multiplies, v_rndne, clamp and a byte pack.
 #include "q8kv_internal.h"
@@ -21,39 +22,53 @@ __device__ __forceinline__ float4 load4(const float* p, bool vec4) {
     return make_float4(p[0], p[1], p[2], p[3]);
 }
 
-template <bool HALF>
+// NP consecutive (token, kv head) pairs per wave: every pair's rows and slot
+// are loaded before any is packed, so a wave keeps NP rows in flight (large
+// writes); NP = 1 for small ones, where the grid is short anyway.
+template <bool HALF, int NP>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool vec4) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint64_t pair = static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (pair >= static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads) return;
-    const uint32_t t = static_cast<uint32_t>(pair / a.num_kv_heads);
-    const uint32_t h = static_cast<uint32_t>(pair % a.num_kv_heads);
+    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave) * NP;
+    const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
+    if (first >= pairs) return;
     const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
-    const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
-    const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
-    // The source rows are loaded together with the slot (one memory round
-    // trip instead of two); a pad token's rows may thus be read, but nothing
-    // is written for it.
-    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-    if (HALF) {
-        const uint32_t w = lane & 31;
-        if (w < hs4) x0 = load4((lane >= 32 ? vsrc : ksrc) + 4 * w, vec4);
-    } else {
-        if (lane < hs4) {
-            x0 = load4(ksrc + 4 * lane, vec4);
-            x1 = load4(vsrc + 4 * lane, vec4);
+    // The source rows are loaded together with the slots (one memory round
+    // trip); a pad token's rows may thus be read, but nothing is written for it.
+    float4 x0[NP], x1[NP];
+    uint32_t slot[NP], head[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        x0[i] = x1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        slot[i] = kPadSlot;
+        head[i] = 0;
+        const uint64_t pair = first + i;
+        if (pair >= pairs) continue;                 // wave-uniform
+        const uint32_t t = static_cast<uint32_t>(pair / a.num_kv_heads);
+        const uint32_t h = static_cast<uint32_t>(pair % a.num_kv_heads);
+        head[i] = h;
+        const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
+        const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
+        if (HALF) {
+            const uint32_t w = lane & 31;
+            if (w < hs4) x0[i] = load4((lane >= 32 ? vsrc : ksrc) + 4 * w, vec4);
+        } else if (lane < hs4) {
+            x0[i] = load4(ksrc + 4 * lane, vec4);
+            x1[i] = load4(vsrc + 4 * lane, vec4);
         }
+        slot[i] = a.slot_mapping[t];
     }
-    const uint32_t slot = a.slot_mapping[t];
-    if (slot == kPadSlot) return;
-    const uint64_t block = slot / a.block_size, off = slot % a.block_size;
-    if (block >= a.num_blocks) return;   // out of contract; skipped rather than written out of bounds
-    const uint64_t dst = ((block * a.num_kv_heads + h) * a.block_size + off) * wpt;
-    if (HALF) {
-        pack_vector<32>(x0, (lane >= 32 ? a.value_cache : a.key_cache) + dst, hs4, lane & 31);
-    } else {
-        pack_vector<64>(x0, a.key_cache + dst, hs4, lane);
-        pack_vector<64>(x1, a.value_cache + dst, hs4, lane);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        if (slot[i] == kPadSlot) continue;
+        const uint64_t block = slot[i] / a.block_size, off = slot[i] % a.block_size;
+        if (block >= a.num_blocks) continue;         // out of contract; skipped rather than written out of bounds
+        const uint64_t dst = ((block * a.num_kv_heads + head[i]) * a.block_size + off) * wpt;
+        if (HALF) {
+            pack_vector<32>(x0[i], (lane >= 32 ? a.value_cache : a.key_cache) + dst, hs4, lane & 31);
+        } else {
+            pack_vector<64>(x0[i], a.key_cache + dst, hs4, lane);
+            pack_vector<64>(x1[i], a.value_cache + dst, hs4, lane);
+        }
     }
 }
 
@@ -61,14 +76,19 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
     const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
-    const uint64_t blocks = (pairs + 3) / 4;
     const bool vec4 = (reinterpret_cast<uintptr_t>(a.key) % 16 == 0) &&
                       (reinterpret_cast<uintptr_t>(a.value) % 16 == 0) &&
                       a.key_stride % 4 == 0 && a.value_stride % 4 == 0;
-    if (a.head_size / 4 <= 32)
-        hipLaunchKernelGGL(cache_write_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, a, vec4);
-    else
-        hipLaunchKernelGGL(cache_write_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, a, vec4);
+    const bool half = a.head_size / 4 <= 32;
+    if (pairs >= kWriteBatchMinPairs) {
+        const dim3 grid(static_cast<uint32_t>((pairs + 4 * kWritePairsPerWave - 1) / (4 * kWritePairsPerWave)));
+        if (half) hipLaunchKernelGGL((cache_write_kernel<true, kWritePairsPerWave>), grid, dim3(256), 0, stream, a, vec4);
+        else hipLaunchKernelGGL((cache_write_kernel<false, kWritePairsPerWave>), grid, dim3(256), 0, stream, a, vec4);
+    } else {
+        const dim3 grid(static_cast<uint32_t>((pairs + 3) / 4));
+        if (half) hipLaunchKernelGGL((cache_write_kernel<true, 1>), grid, dim3(256), 0, stream, a, vec4);
+        else hipLaunchKernelGGL((cache_write_kernel<false, 1>), grid, dim3(256), 0, stream, a, vec4);
+    }
     return hipGetLastError();
 }
 

@@ -22,9 +22,11 @@
 // as in the cache writer.  The sum of squares is a binary64 xor-shuffle
 // reduction over those lanes; the partner of rotated element i (i + rot/2, or
 // i - rot/2) sits in lane w +- rot/8 (rot a multiple of 8), fetched with one
-// shuffle.  The fused writer runs one wavefront per (token, kv head): for
-// head sizes up to 128 lanes 0-31 take K through the norm and the rotation and
-// lanes 32-63 pack V beside them, otherwise the wave does K and then V.
+// shuffle.  The fused writer runs one wavefront per (token, kv head), or in
+// large writes per group of consecutive ones whose loads are all in flight
+// together: for head sizes up to 128 lanes 0-31 take K through the norm and
+// the rotation and lanes 32-63 pack V beside them, otherwise the wave does K
+// and then V.
 #include "q8kv_internal.h"
 #include "q8_pack.h"
 
@@ -41,7 +43,7 @@ __device__ __forceinline__ float4 load4(const float* p, bool vec4) {
 // vector.  cs is the rotary table row of the vector's position.
 template <int WIDTH>
 __device__ __forceinline__ float4 norm_rope4(float4 x, uint32_t w, uint32_t head_size, const float* weight,
-                                             const float* cs, uint32_t rot, float eps) {
+                                             const float* cs, uint32_t rot, float eps, bool pvec4) {
 #pragma clang fp contract(off)
     double ss = static_cast<double>(x.x) * x.x + static_cast<double>(x.y) * x.y +
                 static_cast<double>(x.z) * x.z + static_cast<double>(x.w) * x.w;
@@ -50,7 +52,7 @@ __device__ __forceinline__ float4 norm_rope4(float4 x, uint32_t w, uint32_t head
     const float r = static_cast<float>(1.0 / sqrt(ss / static_cast<double>(head_size) + static_cast<double>(eps)));
     const uint32_t hs4 = head_size / 4;
     float4 wt = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (w < hs4) wt = make_float4(weight[4 * w], weight[4 * w + 1], weight[4 * w + 2], weight[4 * w + 3]);
+    if (w < hs4) wt = load4(weight + 4 * w, pvec4);
     float4 n;
     n.x = (x.x * r) * wt.x;
     n.y = (x.y * r) * wt.y;
@@ -68,8 +70,9 @@ __device__ __forceinline__ float4 norm_rope4(float4 x, uint32_t w, uint32_t head
     if (!first && !second) return n;
     const uint32_t i0 = 4 * (first ? w : w - h8);
     const uint32_t half = rot / 2;
-    const float c[4] = {cs[i0], cs[i0 + 1], cs[i0 + 2], cs[i0 + 3]};
-    const float s[4] = {cs[half + i0], cs[half + i0 + 1], cs[half + i0 + 2], cs[half + i0 + 3]};
+    const float4 c4 = load4(cs + i0, pvec4), s4 = load4(cs + half + i0, pvec4);
+    const float c[4] = {c4.x, c4.y, c4.z, c4.w};
+    const float s[4] = {s4.x, s4.y, s4.z, s4.w};
     const float nn[4] = {n.x, n.y, n.z, n.w}, pp[4] = {p.x, p.y, p.z, p.w};
     float y[4];
 #pragma unroll
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a, bool vec
     if (live && w < hs4)
         x = load4(a.x + static_cast<uint64_t>(t) * a.x_stride + static_cast<uint64_t>(h) * a.head_stride + 4 * w, vec4);
     const float* cs = live ? table_row(a.table, a.positions, t, a.rot, a.num_positions) : a.table;
-    const float4 y = norm_rope4<WIDTH>(x, w, a.head_size, a.weight, cs, a.rot, a.eps);
+    const float4 y = norm_rope4<WIDTH>(x, w, a.head_size, a.weight, cs, a.rot, a.eps, a.params_vec4);
     if (live && w < hs4) {
         float* o = a.out + static_cast<uint64_t>(t) * a.out_stride + static_cast<uint64_t>(h) * a.head_size + 4 * w;
         if (vec4) *reinterpret_cast<float4*>(o) = y;
@@ -128,39 +131,61 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a, bool vec
     }
 }
 
-// Cache write with the norm + rotary step on K (one wave per (token, kv head)).
-template <bool HALF>
+// Cache write with the norm + rotary step on K: one wave per NP consecutive
+// (token, kv head) pairs, every pair's rows and slot loaded before any is
+// processed (NP > 1 for large writes, to keep several rows in flight).
+template <bool HALF, int NP>
 __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCacheWriteArgs a, bool vec4) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint64_t pair = static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (pair >= static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads) return;
-    const uint32_t t = static_cast<uint32_t>(pair / a.num_kv_heads);
-    const uint32_t h = static_cast<uint32_t>(pair % a.num_kv_heads);
-    const uint32_t slot = a.slot_mapping[t];
-    if (slot == kPadSlot) return;                        // pads: no read of the rows or the position
-    const uint64_t block = slot / a.block_size, off = slot % a.block_size;
-    if (block >= a.num_blocks) return;                   // out of contract; skipped rather than written out of bounds
+    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave) * NP;
+    const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
+    if (first >= pairs) return;
     const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
-    const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
-    const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
-    const float* cs = table_row(a.table, a.positions, t, a.rot, a.num_positions);
-    const uint64_t dst = ((block * a.num_kv_heads + h) * a.block_size + off) * wpt;
-    if (HALF) {
-        const uint32_t w = lane & 31;
-        const bool is_v = lane >= 32;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (w < hs4) x = load4((is_v ? vsrc : ksrc) + 4 * w, vec4);
-        const float4 y = norm_rope4<32>(x, w, a.head_size, a.weight, cs, a.rot, a.eps);
-        pack_vector<32>(is_v ? x : y, (is_v ? a.value_cache : a.key_cache) + dst, hs4, w);
-    } else {
-        float4 xk = make_float4(0.f, 0.f, 0.f, 0.f), xv = xk;
-        if (lane < hs4) {
-            xk = load4(ksrc + 4 * lane, vec4);
-            xv = load4(vsrc + 4 * lane, vec4);
+    float4 xk[NP], xv[NP];
+    uint32_t slot[NP], head[NP], posn[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        xk[i] = xv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        slot[i] = kPadSlot;
+        head[i] = posn[i] = 0;
+        const uint64_t pair = first + i;
+        if (pair >= pairs) continue;                     // wave-uniform
+        const uint32_t t = static_cast<uint32_t>(pair / a.num_kv_heads);
+        const uint32_t h = static_cast<uint32_t>(pair % a.num_kv_heads);
+        head[i] = h;
+        // A pad token's rows and position may be read (loaded with the slot),
+        // but nothing is written for it.
+        const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
+        const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
+        if (HALF) {
+            const uint32_t w = lane & 31;
+            if (w < hs4) xk[i] = load4((lane >= 32 ? vsrc : ksrc) + 4 * w, vec4);
+        } else if (lane < hs4) {
+            xk[i] = load4(ksrc + 4 * lane, vec4);
+            xv[i] = load4(vsrc + 4 * lane, vec4);
         }
-        const float4 y = norm_rope4<64>(xk, lane, a.head_size, a.weight, cs, a.rot, a.eps);
-        pack_vector<64>(y, a.key_cache + dst, hs4, lane);
-        pack_vector<64>(xv, a.value_cache + dst, hs4, lane);
+        slot[i] = a.slot_mapping[t];
+        if (a.rot > 0) posn[i] = a.positions[t];
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        if (slot[i] == kPadSlot) continue;
+        const uint64_t block = slot[i] / a.block_size, off = slot[i] % a.block_size;
+        if (block >= a.num_blocks) continue;             // out of contract; skipped rather than written out of bounds
+        // positions[t] < num_positions is a caller contract: clamped rather than read out of bounds
+        const uint32_t p = posn[i] < a.num_positions ? posn[i] : a.num_positions - 1;
+        const float* cs = a.rot > 0 ? a.table + static_cast<uint64_t>(p) * a.rot : a.table;
+        const uint64_t dst = ((block * a.num_kv_heads + head[i]) * a.block_size + off) * wpt;
+        if (HALF) {
+            const uint32_t w = lane & 31;
+            const bool is_v = lane >= 32;
+            const float4 y = norm_rope4<32>(xk[i], w, a.head_size, a.weight, cs, a.rot, a.eps, a.params_vec4);
+            pack_vector<32>(is_v ? xk[i] : y, (is_v ? a.value_cache : a.key_cache) + dst, hs4, w);
+        } else {
+            const float4 y = norm_rope4<64>(xk[i], lane, a.head_size, a.weight, cs, a.rot, a.eps, a.params_vec4);
+            pack_vector<64>(y, a.key_cache + dst, hs4, lane);
+            pack_vector<64>(xv[i], a.value_cache + dst, hs4, lane);
+        }
     }
 }
 
@@ -192,11 +217,16 @@ hipError_t launch_norm_rope_cache_write(const NormRopeCacheWriteArgs& a, hipStre
     const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
     const bool vec4 = reinterpret_cast<uintptr_t>(a.key) % 16 == 0 && reinterpret_cast<uintptr_t>(a.value) % 16 == 0 &&
                       a.key_stride % 4 == 0 && a.value_stride % 4 == 0;
-    const dim3 grid(static_cast<uint32_t>((pairs + 3) / 4));
-    if (a.head_size / 4 <= 32)
-        hipLaunchKernelGGL(norm_rope_cache_write_kernel<true>, grid, dim3(256), 0, stream, a, vec4);
-    else
-        hipLaunchKernelGGL(norm_rope_cache_write_kernel<false>, grid, dim3(256), 0, stream, a, vec4);
+    const bool half = a.head_size / 4 <= 32;
+    if (pairs >= kWriteBatchMinPairs) {
+        const dim3 grid(static_cast<uint32_t>((pairs + 4 * kWritePairsPerWave - 1) / (4 * kWritePairsPerWave)));
+        if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, kWritePairsPerWave>), grid, dim3(256), 0, stream, a, vec4);
+        else hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, kWritePairsPerWave>), grid, dim3(256), 0, stream, a, vec4);
+    } else {
+        const dim3 grid(static_cast<uint32_t>((pairs + 3) / 4));
+        if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, 1>), grid, dim3(256), 0, stream, a, vec4);
+        else hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, 1>), grid, dim3(256), 0, stream, a, vec4);
+    }
     return hipGetLastError();
 }
 

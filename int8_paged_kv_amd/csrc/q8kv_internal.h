@@ -10,6 +10,10 @@ constexpr uint32_t kPadSlot = 0xFFFFFFFFu;
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kChunk = 64;         // decode positions per chunk
 constexpr uint32_t kDecodeWaves = 1024;   // persistent decode wavefronts: 4 per CU of an MI355X
+// Cache writers: from this many (token, kv head) pairs on, each wave takes
+// kWritePairsPerWave consecutive pairs with all their loads in flight.
+constexpr uint64_t kWriteBatchMinPairs = 32768;
+constexpr int kWritePairsPerWave = 4;
 
 struct CacheWriteArgs {
     const float* key;
@@ -34,6 +38,7 @@ struct NormRopeArgs {
     uint32_t x_stride, head_stride, out_stride;
     uint32_t num_rows, num_heads, head_size, rot, num_positions;
     float eps;
+    bool params_vec4;            // weight and table 16-byte aligned (rot % 8 == 0 keeps table rows so)
 };
 
 struct NormRopeCacheWriteArgs {
@@ -48,6 +53,7 @@ struct NormRopeCacheWriteArgs {
     uint32_t key_stride, value_stride;
     uint32_t num_tokens, num_kv_heads, head_size, block_size, num_blocks, rot, num_positions;
     float eps;
+    bool params_vec4;            // weight and table 16-byte aligned
 };
 
 hipError_t launch_rope_table(float* table, uint32_t num_positions, uint32_t rot, double theta, hipStream_t stream);

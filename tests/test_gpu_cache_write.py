@@ -98,3 +98,20 @@ def test_mha256_4096_token_write(oracle_mod):
     t, h = zk[0]
     row = kh[s2[t] // w.block_size, h, s2[t] % w.block_size]
     assert row[-1] == 0x3F800000 and not row[:-1].any()
+
+
+@pytest.mark.parametrize("T,hkv,hs", [(4103, 8, 128), (2053, 16, 256), (8191, 4, 64)])
+def test_large_ragged_writes(oracle_mod, T, hkv, hs):
+    """Writes of >= 32768 (token, kv head) pairs take several consecutive pairs
+    per wave; pair counts that leave the last wave partly filled, with pads."""
+    g = np.random.default_rng(T + hkv)
+    bs = 16
+    nb = T // bs + 8
+    key = g.standard_normal((T, hkv, hs)).astype(np.float32)
+    val = g.standard_normal((T, hkv, hs)).astype(np.float32)
+    slots = g.choice(nb * bs, size=T, replace=False).astype(np.uint32)
+    slots[g.choice(T, size=T // 10, replace=False)] = wl.PAD_SLOT
+    slots[-1] = wl.PAD_SLOT
+    k, v, kh, vh = run_write(oracle_mod, key, val, slots, nb, hkv, hs, bs)
+    assert_words_equal(k, kh, "key cache")
+    assert_words_equal(v, vh, "value cache")

@@ -149,7 +149,7 @@ def test_norm_rope_cache_write(oracle_mod, hs, rot, hkv, theta, stride_pad):
     slots = g.choice(nb * bs, size=T, replace=False).astype(np.uint32)
     slots[[0, 9, 30]] = wl.PAD_SLOT
     pos = g.integers(0, P, T).astype(np.uint32)
-    pos[9] = 0xFFFFFFFF                                   # a pad token's position is not read
+    pos[9] = 0xFFFFFFFF                                   # a pad token's position is not used
     kh, vh = wl.poison_cache(nb, hkv, bs, hs), wl.poison_cache(nb, hkv, bs, hs)
     kd, vd = u32_dev(kh), u32_dev(vh)
     tab_d = gpu_table(P, rot, theta) if rot else None
@@ -228,3 +228,56 @@ def test_norm_rope_then_decode_matches_oracle(oracle_mod):
     assert np.array_equal(u32_host(vd), vh) and np.array_equal(u32_host(kd), kh)
     ref = oracle_mod.paged_decode(qh, kh, vh, w_.block_tables, w_.context_lens, w_.scale, hkv, bs)
     assert_close(out.cpu().numpy(), ref, "decode after norm + rotary")
+
+
+@pytest.mark.parametrize("T,hkv,hs,rot", [(4103, 8, 128, 64), (2053, 16, 256, 128)])
+def test_norm_rope_cache_write_large_ragged(oracle_mod, T, hkv, hs, rot):
+    """>= 32768 pairs (several consecutive pairs per wave), a partly filled last
+    wave, pads among them."""
+    from int8_paged_kv_amd import q8_norm_rope_cache_write
+    f32_dev, u32_dev, u32_host = dev()
+    g = np.random.default_rng(T)
+    bs, P = 16, 8192
+    nb = T // bs + 8
+    key = g.standard_normal((T, hkv, hs)).astype(np.float32)
+    val = g.standard_normal((T, hkv, hs)).astype(np.float32)
+    w = (1.0 + 0.1 * g.standard_normal(hs)).astype(np.float32)
+    slots = g.choice(nb * bs, size=T, replace=False).astype(np.uint32)
+    slots[g.choice(T, size=T // 10, replace=False)] = wl.PAD_SLOT
+    slots[-1] = wl.PAD_SLOT
+    pos = g.integers(0, P, T).astype(np.uint32)
+    kh, vh = wl.poison_cache(nb, hkv, bs, hs), wl.poison_cache(nb, hkv, bs, hs)
+    kd, vd = u32_dev(kh), u32_dev(vh)
+    tab_d = gpu_table(P, rot, 10000.0)
+    q8_norm_rope_cache_write(f32_dev(key), f32_dev(val), kd, vd, u32_dev(slots), u32_dev(pos), f32_dev(w), tab_d,
+                             rot, 1e-6, hkv, hs, bs)
+    torch.cuda.synchronize()
+    tab_h = oracle_mod.rope_table(P, rot, 10000.0)
+    oracle_mod.norm_rope_cache_write(key, val, kh, vh, slots, pos, w, tab_h, rot, 1e-6, hkv, hs, bs)
+    assert np.array_equal(u32_host(vd), vh)
+    n = compare_k_rows(oracle_mod, u32_host(kd), kh, key, slots, pos, w, tab_h, rot, hkv, hs, bs)
+    assert n <= 4
+
+
+def test_norm_rope_cache_write_unaligned_weight_and_rows(oracle_mod):
+    """Weight and K/V rows 4 bytes off 16-byte alignment (element loads)."""
+    from int8_paged_kv_amd import q8_norm_rope_cache_write
+    f32_dev, u32_dev, u32_host = dev()
+    g = np.random.default_rng(21)
+    T, hkv, hs, bs, nb, rot, P = 29, 2, 128, 16, 8, 64, 512
+    wx = (1.0 + 0.1 * g.standard_normal(hs + 1)).astype(np.float32)
+    kx = g.standard_normal(T * hkv * hs + 1).astype(np.float32)
+    vx = g.standard_normal(T * hkv * hs + 1).astype(np.float32)
+    slots = g.choice(nb * bs, size=T, replace=False).astype(np.uint32)
+    pos = g.integers(0, P, T).astype(np.uint32)
+    kh, vh = wl.poison_cache(nb, hkv, bs, hs), wl.poison_cache(nb, hkv, bs, hs)
+    kd, vd = u32_dev(kh), u32_dev(vh)
+    tab_d = gpu_table(P, rot, 10000.0)
+    q8_norm_rope_cache_write(f32_dev(kx)[1:].view(T, hkv * hs), f32_dev(vx)[1:].view(T, hkv * hs), kd, vd,
+                             u32_dev(slots), u32_dev(pos), f32_dev(wx)[1:], tab_d, rot, 1e-6, hkv, hs, bs)
+    torch.cuda.synchronize()
+    tab_h = oracle_mod.rope_table(P, rot, 10000.0)
+    key, val, w = kx[1:].reshape(T, hkv, hs), vx[1:].reshape(T, hkv, hs), wx[1:]
+    oracle_mod.norm_rope_cache_write(key, val, kh, vh, slots, pos, w, tab_h, rot, 1e-6, hkv, hs, bs)
+    assert np.array_equal(u32_host(vd), vh)
+    assert compare_k_rows(oracle_mod, u32_host(kd), kh, key, slots, pos, w, tab_h, rot, hkv, hs, bs) <= 2
