@@ -71,11 +71,17 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes_per_launch": n * 4, "launches": 5}), flush=True)
 
 
+# The files the decode-step kernel (decode_split_kernel) and its launch are
+# built from; the committed HBM-traffic figures hold while these are unchanged.
+DECODE_SOURCES = ("decode_kernel.h", "decode_split.h", "decode.hip", "decode_hs16.hip", "decode_hs32.hip",
+                  "decode_hs48.hip", "decode_hs64.hip", "q8_pack.h", "wave_ops.h", "q8kv_internal.h")
+
+
 def kernel_sources_digest() -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int8_paged_kv_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in DECODE_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]

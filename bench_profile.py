@@ -12,8 +12,12 @@ Expected layout of DIR (what the commands printed in each summary write):
   DIR/pmc_FETCH_SIZE.log, DIR/pmc_WRITE_SIZE.log, DIR/copy_FETCH_SIZE.log
       stdout of those runs (bench's JSON line carries the kernel-source digest)
 
-Writes profiles/q8_paged_decode_llama_kernel_trace.txt and
-profiles/q8_paged_decode_llama_traffic.txt; the latter is what bench.py reads
+Optionally DIR/trace_all/ and DIR/trace_all.log: the same trace of a run with
+the reference legs (every kernel the bench times).
+
+Writes profiles/q8_paged_decode_llama_kernel_trace.txt,
+profiles/q8_paged_decode_llama_traffic.txt and, with trace_all,
+profiles/llama_step_all_kernels_trace.txt; the latter is what bench.py reads
 for roofline.traffic while the kernel sources still match its digest.
 """
 from __future__ import annotations
@@ -33,6 +37,8 @@ TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats 
              "-- python3 /root/repo/bench.py --steps 20 --warmup 5 --no-cpu --no-reference")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {c} -d {d}/pmc_{c} -o bench -f csv "
            "-- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
+TRACE_ALL_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d {d}/trace_all -o bench -f csv "
+                 "-- python3 /root/repo/bench.py --steps 20 --warmup 5 --no-cpu")
 COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} -d {d}/copy_{c} -o copy -f csv "
             "-- python3 /root/repo/bench.py --copy-calibration {mib}")
 
@@ -140,6 +146,39 @@ def main():
                 short(r["Name"])[:52], r["Calls"], r["AverageNs"], r["MinNs"], r["MaxNs"]))
     with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
+
+    # ---- optional: every kernel of a run with the reference legs ----
+    all_dir = os.path.join(d, "trace_all")
+    if os.path.exists(os.path.join(all_dir, "bench_kernel_trace.csv")):
+        per = defaultdict(list)
+        with open(os.path.join(all_dir, "bench_kernel_trace.csv")) as f:
+            for r in csv.DictReader(f):
+                grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                per[(r["Kernel_Name"], grid, int(r["VGPR_Count"]), int(r["LDS_Block_Size"]))].append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        allj = last_json(os.path.join(d, "trace_all.log"))
+        out = [
+            "# rocprofv3 kernel trace of every kernel the bench runs, Llama-3-8B-shaped batch",
+            "# (step, two-launch reference, 4-row decode, f32-cache step, norm + rotary step, 16384-token bulk writes)",
+            "#",
+            "# command (from any directory on the GPU machine):",
+            "#   " + TRACE_ALL_CMD.format(d=args.cmd_dir),
+            "# summarised with: python3 bench_profile.py <that -d directory's parent>",
+            "#",
+            "# durations in microseconds per dispatch, grouped by kernel and grid",
+            "",
+            "%-60s %9s %5s %9s %9s %9s %5s %6s" % ("kernel", "grid", "calls", "mean_us", "median_us", "max_us",
+                                                  "vgpr", "lds"),
+        ]
+        for (name, grid, vgpr, lds), durs in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            nm = name.replace("void ", "").replace("q8kv::(anonymous namespace)::", "").split("(")[0]
+            out.append("%-60s %9d %5d %9.2f %9.2f %9.2f %5d %6d" % (
+                nm[:60], grid, len(durs), statistics.mean(durs), statistics.median(durs), max(durs), vgpr, lds))
+        out += ["", "bench.py line of the same run (reference legs):"]
+        for k in ("two_launch_reference", "multi_row_decode", "f32_cache_reference", "norm_rope_step"):
+            out.append("  %s: %s" % (k, json.dumps(allj.get(k))))
+        with open(os.path.join(ROOT, "profiles", "llama_step_all_kernels_trace.txt"), "w") as f:
+            f.write("\n".join(out) + "\n")
 
     # ---- HBM traffic from FETCH_SIZE / WRITE_SIZE, calibrated by the copy ----
     mib = args.copy_mib
