@@ -75,6 +75,8 @@ def _load():
         lib.q8o_norm_rope.restype = ctypes.c_int
         lib.q8o_norm_rope_cache_write.argtypes = [P, U, P, U, P, P, P, P, P, P, U, U, F, U, U, U, U, U]
         lib.q8o_norm_rope_cache_write.restype = ctypes.c_int
+        lib.q8o_index_select.argtypes = [P, U, P, U, U, U, P, U, P]
+        lib.q8o_index_select.restype = ctypes.c_int
         lib.q8o_max_threads.argtypes = []
         lib.q8o_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -328,3 +330,19 @@ def norm_rope_cache_write(key, value, key_cache, value_cache, slot_mapping, posi
                                              _ptr(slot_mapping), _ptr(positions), _ptr(_c(weight, np.float32)),
                                              _ptr(table), rot, table.shape[0] if rot else 0, float(eps), T,
                                              num_kv_heads, head_size, block_size, nb), "norm_rope_cache_write")
+
+
+# ---------------------------------------------------------------- block select ----
+
+def index_select(scores, row_lens, ratio: int, k: int, vis_stride: int):
+    """Visible lists from block scores: returns (visible_pos u32 [rows, vis_stride]
+    (unused tail entries 0), num_visible u32 [rows])."""
+    scores = _c(scores, np.float32)
+    row_lens = _c(row_lens, np.uint32)
+    R = row_lens.shape[0]
+    stride = scores.shape[-1] if scores.ndim > 1 else scores.size
+    vis = np.zeros((R, vis_stride), dtype=np.uint32)
+    nv = np.zeros(R, dtype=np.uint32)
+    _check(_load().q8o_index_select(_ptr(scores), stride, _ptr(row_lens), R, ratio, k, _ptr(vis), vis_stride,
+                                    _ptr(nv)), "index_select")
+    return vis, nv

@@ -70,6 +70,17 @@
  *   sum.  q8o_norm_rope_row_f64 is the same definition in binary64 throughout
  *   (angles straight from theta), the reference the pins check against.
  *
+ *   Block selection into a visible list (the "attention.rs" page: each row b
+ *   of a step has t_len = base_pos + b + 1 positions and blocks = t_len /
+ *   ratio complete blocks; with kblk = budget / ratio, a row is selective when
+ *   blocks > kblk and then attends kblk*ratio + (t_len - blocks*ratio)
+ *   positions, else all t_len; the indexer's select pass turns block scores
+ *   into that list, vis_stride = budget + ratio apart).  The select kernel is
+ *   not printed; the reading taken: the kblk complete blocks of highest score
+ *   (ties to the lower block index), their positions in ascending order, then
+ *   the trailing incomplete block's positions.  When blocks <= kblk every
+ *   complete block is taken, which is the dense list 0 .. t_len-1.
+ *
  * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fopenmp -fPIC
  * -shared.  On x86-64 (SSE, FLT_EVAL_METHOD == 0) every float operation above
  * rounds to binary32 once.  OpenMP only spreads independent (seq, head) units
@@ -558,6 +569,40 @@ int q8o_norm_rope_cache_write(const float* key, uint32_t key_stride,
     }
     free(y);
     return rc;
+}
+
+/* ------------------------------------------------------- block select ---- */
+
+/* Row r: scores[r*score_stride + j] for its complete blocks j < row_lens[r] /
+ * ratio.  Writes visible_pos[r*vis_stride + i], i < num_visible[r]. */
+int q8o_index_select(const float* scores, uint32_t score_stride, const uint32_t* row_lens,
+                     uint32_t num_rows, uint32_t ratio, uint32_t k,
+                     uint32_t* visible_pos, uint32_t vis_stride, uint32_t* num_visible)
+{
+    if (ratio == 0) return Q8O_ERR_SHAPE;
+    if ((uint64_t)k * ratio + ratio > vis_stride) return Q8O_ERR_SHAPE;   /* the longest list must fit */
+    for (uint32_t r = 0; r < num_rows; ++r) {
+        uint32_t t_len = row_lens[r];
+        uint32_t blocks = t_len / ratio;
+        if (blocks > score_stride) return Q8O_ERR_RANGE;
+        const float* sc = scores + (uint64_t)r * score_stride;
+        for (uint32_t j = 0; j < blocks; ++j)
+            if (!isfinite(sc[j])) return Q8O_ERR_INPUT;
+        uint32_t n = 0;
+        uint32_t* out = visible_pos + (uint64_t)r * vis_stride;
+        /* block j is selected when fewer than k blocks come before it in the
+         * order (score descending, index ascending) */
+        for (uint32_t j = 0; j < blocks; ++j) {
+            uint32_t ahead = 0;
+            for (uint32_t i = 0; i < blocks && ahead < k; ++i)
+                if (sc[i] > sc[j] || (sc[i] == sc[j] && i < j)) ++ahead;
+            if (ahead < k)
+                for (uint32_t p = 0; p < ratio; ++p) out[n++] = j * ratio + p;
+        }
+        for (uint32_t p = blocks * ratio; p < t_len; ++p) out[n++] = p;
+        num_visible[r] = n;
+    }
+    return Q8O_OK;
 }
 
 int q8o_max_threads(void)
