@@ -118,7 +118,7 @@ def main():
     from int8_paged_kv_amd import (q8_cache_write, q8_decode_step, q8_paged_decode, q8_paged_decode_rows,
                                    q8_paged_decode_workspace_bytes, q8_f32_cache_write, q8_f32_paged_decode,
                                    q8_f32_paged_decode_workspace_bytes, q8_rope_table, q8_norm_rope,
-                                   q8_norm_rope_cache_write, load_library)
+                                   q8_norm_rope_cache_write, q8_index_select, load_library)
     from int8_paged_kv_amd import workloads as wl
 
     load_library()
@@ -356,6 +356,65 @@ def main():
                             "(three launches), then a 16384-token bulk write; positions L-1 for the step"}
         del kb_, vb_
 
+    # ---- selected-token step: block scores -> visible lists -> visible-list decode ----
+    selected = None
+    if not args.no_reference:
+        ws_ = wl.selected()
+        ratio_, k_ = 64, 32
+        kh5, vh5 = ws_.empty_caches()
+        kc5, vc5 = u32(kh5), u32(vh5)
+        del kh5, vh5
+        for slots, k, v in ws_.fill_chunks():
+            q8_cache_write(f32(k), f32(v), kc5, vc5, u32(slots), ws_.num_kv_heads, ws_.head_size, ws_.block_size)
+        g5 = np.random.default_rng(13)
+        nblk5 = int(ws_.context_lens.max()) // ratio_
+        sc5 = (g5.random((ws_.num_seqs, nblk5)) * 0.5).astype(np.float32)
+        for s_ in range(ws_.num_seqs):
+            n_ = int(ws_.num_visible[s_])
+            sc5[s_, np.unique(ws_.visible_pos[s_, :n_] // ratio_)[:k_]] = 1.0 + g5.random(k_).astype(np.float32)
+        sc5d, cl5 = f32(sc5), u32(ws_.context_lens)
+        vstride = ws_.visible_pos.shape[1]
+        vis5 = torch.zeros((ws_.num_seqs, vstride), dtype=torch.int32, device=dev)
+        nv5 = torch.zeros((ws_.num_seqs,), dtype=torch.int32, device=dev)
+        q5, bt5 = f32(ws_.q()), u32(ws_.block_tables)
+        out5 = torch.empty((ws_.num_seqs, ws_.num_heads, ws_.head_size), dtype=torch.float32, device=dev)
+        ws5 = torch.zeros(max(1, q8_paged_decode_workspace_bytes(ws_.num_seqs, ws_.num_heads, ws_.num_kv_heads,
+                                                                 ws_.head_size, ws_.block_size, vstride)),
+                          dtype=torch.uint8, device=dev)
+
+        def sel_step(ev=None):
+            if ev is not None:
+                ev[0].record()
+            q8_index_select(sc5d, cl5, ratio_, k_, vstride, visible_pos=vis5, num_visible=nv5)
+            if ev is not None:
+                ev[1].record()
+            q8_paged_decode(q5, kc5, vc5, bt5, cl5, ws_.scale, ws_.num_kv_heads, ws_.block_size,
+                            visible_pos=vis5, num_visible=nv5, out=out5, workspace=ws5)
+            if ev is not None:
+                ev[2].record()
+
+        for _ in range(5):
+            sel_step()
+        torch.cuda.synchronize()
+        ev5 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(100)]
+        for e in ev5:
+            sel_step(e)
+        torch.cuda.synchronize()
+        ts_ = np.array([e[0].elapsed_time(e[1]) for e in ev5]) * 1e3
+        td_ = np.array([e[1].elapsed_time(e[2]) for e in ev5]) * 1e3
+        B5 = ws_.effective_kv_bytes()
+        selected = {"workload": "selected-token decode S=16 H=32 Hkv=4 hs=128 bs=16, 65536-token capacity, "
+                                "32 of 1023 64-token blocks + tail per sequence (seed 5)",
+                    "index_select_us_mean": round(float(ts_.mean()), 2),
+                    "decode_us_mean": round(float(td_.mean()), 2),
+                    "effective_kv_bytes": B5,
+                    "decode_effective_GBps": round(B5 / (float(td_.mean()) * 1e-6) / 1e9, 1),
+                    "lists_match_workload": bool(np.array_equal(nv5.cpu().numpy().view(np.uint32),
+                                                                ws_.num_visible)),
+                    "note": "q8_index_select over one score per complete block (16 rows x 1023), then "
+                            "q8_paged_decode over the lists; scores rank each sequence's workload blocks first"}
+        del kc5, vc5
+
     hot = None
     if args.hot:
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -432,6 +491,7 @@ def main():
         "multi_row_decode": multi,
         "f32_cache_reference": f32ref,
         "norm_rope_step": normrope,
+        "selected_step": selected,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "q8_decode_step (one launch: decode_split_kernel, appending the step's tokens)",

@@ -352,6 +352,33 @@ q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
                                    uint32_t num_kv_heads, uint32_t head_size,
                                    uint32_t block_size, uint32_t num_blocks, void* stream);
 
+/*
+ * q8_index_select -- block selection into a visible list.  The
+ * "attention.rs" page's per-row decode gives row r t_len = row_lens[r]
+ * positions and blocks = t_len / ratio complete blocks; with k = kblk
+ * (budget / ratio) a row is selective when blocks > k and then attends
+ * k*ratio + (t_len - blocks*ratio) positions, else all t_len, from a list
+ * the indexer's select pass builds out of block scores (vis_stride = budget
+ * + ratio apart).  The select kernel is not printed; computed here: the k
+ * complete blocks of highest score (ties to the lower block index), their
+ * positions ascending, then the trailing incomplete block's positions; with
+ * blocks <= k, every position 0 .. t_len-1.  The lists feed q8_paged_decode's
+ * visible-position mode directly.
+ *   scores        device f32; row r's block j at scores[r*score_stride + j],
+ *                 finite, read for j < blocks only.
+ *   row_lens      device u32 [num_rows]: t_len per row; t_len / ratio <=
+ *                 score_stride is a caller contract (clamped, not reported).
+ *   visible_pos   device u32; row r's list at visible_pos[r*vis_stride + i],
+ *                 i < num_visible[r]; entries past it are left untouched.
+ *   num_visible   device u32 [num_rows].
+ * Errors: Q8_ERR_NULL; Q8_ERR_SHAPE when ratio == 0 or (k + 1)*ratio >
+ * vis_stride (the longest list must fit); Q8_ERR_UNSUPPORTED when
+ * score_stride > 16384.  num_rows == 0 enqueues nothing.
+ */
+q8_status q8_index_select(const float* scores, uint32_t score_stride, const uint32_t* row_lens,
+                          uint32_t num_rows, uint32_t ratio, uint32_t k, uint32_t* visible_pos,
+                          uint32_t vis_stride, uint32_t* num_visible, void* stream);
+
 /* hipError_t code behind the calling thread's last Q8_ERR_HIP (0 if none). */
 int q8_last_hip_error(void);
 

@@ -66,6 +66,8 @@ def load_library() -> ctypes.CDLL:
         lib.q8_norm_rope.restype = ctypes.c_int
         lib.q8_norm_rope_cache_write.argtypes = [P, U, P, U, P, P, P, P, P, P, U, U, F, U, U, U, U, U, P]
         lib.q8_norm_rope_cache_write.restype = ctypes.c_int
+        lib.q8_index_select.argtypes = [P, U, P, U, U, U, P, U, P, P]
+        lib.q8_index_select.restype = ctypes.c_int
         lib.q8_last_hip_error.argtypes = []
         lib.q8_last_hip_error.restype = ctypes.c_int
         lib.q8_status_string.argtypes = [ctypes.c_int]
@@ -389,3 +391,23 @@ def q8_norm_rope_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: 
                                       rot, num_positions, float(eps), slot_mapping.numel(), num_kv_heads,
                                       head_size, block_size, num_blocks, _stream(stream))
     _check(st, "q8_norm_rope_cache_write")
+
+
+def q8_index_select(scores: torch.Tensor, row_lens: torch.Tensor, ratio: int, k: int, vis_stride: int,
+                    visible_pos: Optional[torch.Tensor] = None, num_visible: Optional[torch.Tensor] = None,
+                    stream=None):
+    """Visible lists from block scores [rows, max_blocks] (see include/q8kv.h).
+    Returns (visible_pos [rows, vis_stride], num_visible [rows]) as int32 tensors of u32 bits."""
+    lib = load_library()
+    if scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be [rows, max_blocks] with dense rows")
+    R = scores.shape[0]
+    if visible_pos is None:
+        visible_pos = torch.zeros((R, vis_stride), dtype=torch.int32, device=scores.device)
+    if num_visible is None:
+        num_visible = torch.zeros((R,), dtype=torch.int32, device=scores.device)
+    st = lib.q8_index_select(_dev(scores, "scores", torch.float32), scores.stride(0), _u32(row_lens, "row_lens"), R,
+                             ratio, k, _u32(visible_pos, "visible_pos"), vis_stride, _u32(num_visible, "num_visible"),
+                             _stream(stream))
+    _check(st, "q8_index_select")
+    return visible_pos, num_visible

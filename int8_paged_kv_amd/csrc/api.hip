@@ -386,6 +386,28 @@ q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
+q8_status q8_index_select(const float* scores, uint32_t score_stride, const uint32_t* row_lens,
+                          uint32_t num_rows, uint32_t ratio, uint32_t k, uint32_t* visible_pos,
+                          uint32_t vis_stride, uint32_t* num_visible, void* stream) {
+    if (ratio == 0 || (static_cast<uint64_t>(k) + 1) * ratio > vis_stride) return Q8_ERR_SHAPE;
+    if (score_stride > q8kv::kSelectMaxBlocks) return Q8_ERR_UNSUPPORTED;
+    if (num_rows == 0) return Q8_OK;
+    if (!scores || !row_lens || !visible_pos || !num_visible) return Q8_ERR_NULL;
+    if (num_rows > 0x7FFFFFFFu) return Q8_ERR_UNSUPPORTED;
+    q8kv::IndexSelectArgs a{};
+    a.scores = scores;
+    a.row_lens = row_lens;
+    a.visible_pos = visible_pos;
+    a.num_visible = num_visible;
+    a.score_stride = score_stride;
+    a.num_rows = num_rows;
+    a.ratio = ratio;
+    a.k = k;
+    a.vis_stride = vis_stride;
+    const hipError_t e = q8kv::launch_index_select(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
 int q8_last_hip_error(void) { return g_last_hip_error; }
 
 const char* q8_status_string(q8_status status) {

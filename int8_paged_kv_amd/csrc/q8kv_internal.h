@@ -56,6 +56,20 @@ struct NormRopeCacheWriteArgs {
     bool params_vec4;            // weight and table 16-byte aligned
 };
 
+// ---- block selection into a visible list ----
+
+constexpr uint32_t kSelectMaxBlocks = 16384;   // scores per row held in LDS
+
+struct IndexSelectArgs {
+    const float* scores;         // row r's block j at scores[r*score_stride + j]
+    const uint32_t* row_lens;    // [num_rows] t_len
+    uint32_t* visible_pos;       // row r's list at visible_pos[r*vis_stride]
+    uint32_t* num_visible;       // [num_rows]
+    uint32_t score_stride, num_rows, ratio, k, vis_stride;
+};
+
+hipError_t launch_index_select(const IndexSelectArgs& a, hipStream_t stream);
+
 hipError_t launch_rope_table(float* table, uint32_t num_positions, uint32_t rot, double theta, hipStream_t stream);
 hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t stream);
 hipError_t launch_norm_rope_cache_write(const NormRopeCacheWriteArgs& a, hipStream_t stream);

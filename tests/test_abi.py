@@ -244,3 +244,12 @@ def test_norm_rope_cache_write_nulls_and_empty(lib):
                                         ctypes.c_float(1e-6), 4, 2, 128, 16, 8, None) == 1
     assert lib.q8_norm_rope_cache_write(None, 256, None, 256, None, None, None, None, None, None, 64, 16,
                                         ctypes.c_float(1e-6), 0, 2, 128, 16, 8, None) == 0
+
+
+def test_index_select_validation(lib):
+    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 0, 2, FAKE, 128, FAKE, None) == 2          # ratio 0
+    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 64, 32, FAKE, 2111, FAKE, None) == 2       # (k+1)*ratio > vis_stride
+    assert lib.q8_index_select(FAKE, 16385, FAKE, 4, 64, 32, FAKE, 2112, FAKE, None) == 5    # too many blocks per row
+    assert lib.q8_index_select(None, 64, FAKE, 4, 64, 32, FAKE, 2112, FAKE, None) == 1
+    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 64, 32, FAKE, 2112, None, None) == 1
+    assert lib.q8_index_select(None, 64, None, 0, 64, 32, None, 2112, None, None) == 0       # no rows

@@ -1,0 +1,84 @@
+"""GPU parity of q8_index_select against the oracle: visible lists and counts are
+index work, so they must be identical, entry by entry (ties resolved to the
+lower block index on both sides); entries past a row's count stay untouched.
+The selected-token workload's lists are then rebuilt from block scores and fed
+to the visible-list decode."""
+import numpy as np
+import pytest
+
+from int8_paged_kv_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SENTINEL = 0xDEADBEEF
+
+
+def run_select(oracle_mod, scores, lens, ratio, k, vis_stride):
+    from int8_paged_kv_amd import q8_index_select
+    from gpu_util import f32_dev, u32_dev, u32_host
+    R = lens.shape[0]
+    vis_d = u32_dev(np.full((R, vis_stride), SENTINEL, np.uint32))
+    nv_d = u32_dev(np.full(R, SENTINEL, np.uint32))
+    q8_index_select(f32_dev(scores), u32_dev(lens), ratio, k, vis_stride, visible_pos=vis_d, num_visible=nv_d)
+    torch.cuda.synchronize()
+    vis, nv = u32_host(vis_d), u32_host(nv_d)
+    want_vis, want_nv = oracle_mod.index_select(scores, lens, ratio, k, vis_stride)
+    assert np.array_equal(nv, want_nv), "visible counts differ"
+    for r in range(R):
+        n = int(want_nv[r])
+        assert np.array_equal(vis[r, :n], want_vis[r, :n]), "row %d: visible lists differ" % r
+        assert np.all(vis[r, n:] == SENTINEL), "row %d: entries past the count were written" % r
+    return vis, nv
+
+
+@pytest.mark.parametrize("ratio,k,max_blocks,kind", [
+    (64, 32, 1024, "normal"),
+    (64, 32, 1024, "ties"),
+    (16, 5, 300, "ties"),
+    (4, 1, 50, "ties"),
+    (1, 3, 16384, "normal"),       # the largest row the kernel holds
+    (1, 200, 16384, "ties"),
+    (8, 0, 40, "normal"),          # selective rows keep only their tail
+    (32, 7, 64, "zeros"),          # every score +-0: ties decided by index alone
+])
+def test_matches_oracle(oracle_mod, ratio, k, max_blocks, kind):
+    g = np.random.default_rng(ratio * 1000 + k + max_blocks)
+    R = 24
+    if kind == "normal":
+        scores = g.standard_normal((R, max_blocks)).astype(np.float32)
+    elif kind == "ties":
+        scores = g.integers(-2, 3, (R, max_blocks)).astype(np.float32)
+    else:
+        scores = np.where(g.random((R, max_blocks)) < 0.5, -0.0, 0.0).astype(np.float32)
+    top = max_blocks * ratio + ratio - 1
+    lens = g.integers(0, top + 1, R).astype(np.uint32)
+    lens[:6] = [0, ratio - 1, k * ratio, k * ratio + ratio - 1, (k + 1) * ratio, top]   # edges of the dense case
+    run_select(oracle_mod, scores, lens, ratio, k, k * ratio + ratio)
+
+
+def test_rebuilds_selected_workload_and_decodes(oracle_mod):
+    """Scores that rank each sequence's 32 visible blocks first reproduce the
+    selected-token workload's lists; the decode over them matches the oracle."""
+    from gpu_util import Filled, assert_close, u32_dev
+    from int8_paged_kv_amd import q8_paged_decode
+    w = wl.selected()
+    ratio, k = 64, 32
+    vis_stride = w.visible_pos.shape[1]
+    g = np.random.default_rng(55)
+    nblocks = int(w.context_lens.max()) // ratio
+    scores = (g.random((w.num_seqs, nblocks)) * 0.5).astype(np.float32)
+    for s in range(w.num_seqs):
+        n = int(w.num_visible[s])
+        blocks = np.unique(w.visible_pos[s, :n] // ratio)[:k]
+        scores[s, blocks] = 1.0 + g.random(k).astype(np.float32)
+    vis, nv = run_select(oracle_mod, scores, w.context_lens.astype(np.uint32), ratio, k, vis_stride)
+    for s in range(w.num_seqs):
+        n = int(w.num_visible[s])
+        assert nv[s] == n and np.array_equal(vis[s, :n], w.visible_pos[s, :n])
+    f = Filled(w, oracle_mod)
+    out = q8_paged_decode(f.q_d, f.kc_d, f.vc_d, u32_dev(w.block_tables), u32_dev(w.context_lens), w.scale,
+                          w.num_kv_heads, w.block_size, visible_pos=u32_dev(vis), num_visible=u32_dev(nv))
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), f.decode_oracle(oracle_mod), "decode over the selected lists")
