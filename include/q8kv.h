@@ -110,7 +110,9 @@ size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
  *   num_visible,  selective decode over the row's visible token list): when
  *   vis_stride    visible_pos != NULL, seq s attends exactly the positions
  *                 visible_pos[s*vis_stride + i], i < num_visible[s]
- *                 (num_visible[s] <= vis_stride; positions distinct);
+ *                 (num_visible[s] <= vis_stride; positions ascending and
+ *                 distinct: 64 listed positions from a multiple of 64 to 63
+ *                 above it are read as one tile run);
  *                 context_lens and max_context_len are then unused.
  *   scale         f32 softmax scale applied to q.k.
  *   workspace     device memory of at least q8_paged_decode_workspace_bytes()

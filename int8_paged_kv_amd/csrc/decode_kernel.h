@@ -155,24 +155,20 @@ __device__ __forceinline__ void load_lds16(const void* g, uint32_t lds) {
 }
 // Waits for every outstanding vector memory operation of the wavefront.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
-// Four records' 16-byte values and (max, sum) pairs, loaded together.
-__device__ __forceinline__ void coherent_load4x4(const float* p0, const float* p1, const float* p2, const float* p3,
-                                                 const float* q0, const float* q1, const float* q2, const float* q3,
-                                                 f32x4& v0, f32x4& v1, f32x4& v2, f32x4& v3,
-                                                 f32x2& w0, f32x2& w1, f32x2& w2, f32x2& w3) {
-    asm volatile(
-        "global_load_dwordx4 %0, %8, off sc1\n\t"
-        "global_load_dwordx4 %1, %9, off sc1\n\t"
-        "global_load_dwordx4 %2, %10, off sc1\n\t"
-        "global_load_dwordx4 %3, %11, off sc1\n\t"
-        "global_load_dwordx2 %4, %12, off sc1\n\t"
-        "global_load_dwordx2 %5, %13, off sc1\n\t"
-        "global_load_dwordx2 %6, %14, off sc1\n\t"
-        "global_load_dwordx2 %7, %15, off sc1\n\t"
-        "s_waitcnt vmcnt(0)"
-        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
-        : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(q0), "v"(q1), "v"(q2), "v"(q3)
-        : "memory");
+// Device-coherent loads the compiler tracks (relaxed agent-scope atomic
+// loads of 8 bytes compile to sc1 loads): a 16-byte unit as two halves, and an
+// 8-byte (max, sum) pair.
+__device__ __forceinline__ f32x4 coherent_load4(const float* p) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4{__uint_as_float(static_cast<uint32_t>(lo)), __uint_as_float(static_cast<uint32_t>(lo >> 32)),
+                 __uint_as_float(static_cast<uint32_t>(hi)), __uint_as_float(static_cast<uint32_t>(hi >> 32))};
+}
+__device__ __forceinline__ f32x2 coherent_load2(const float* p) {
+    const uint64_t x = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return f32x2{__uint_as_float(static_cast<uint32_t>(x)), __uint_as_float(static_cast<uint32_t>(x >> 32))};
 }
 
 // Query heads of a row group: pairs p = (row p / n_rep, head kvh*n_rep +
@@ -456,19 +452,41 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     auto meta_nv = [](const Meta& m) __attribute__((always_inline)) { return m.info & 0x7Fu; };
     auto meta_tiled = [](const Meta& m) __attribute__((always_inline)) { return TILED || (m.info & 0x80u) != 0; };
     auto meta_nrec = [](const Meta& m) __attribute__((always_inline)) { return m.info >> 8; };
+    // Visible lists: the first and last listed position of 64 consecutive
+    // chunks of one sequence, lane l holding chunk vc_c0 + l, loaded in one
+    // round trip when the cursor leaves the cached span; a chunk's bounds are
+    // then read from a lane instead of two dependent loads per chunk.
+    uint32_t vc_s = ~0u, vc_c0 = 0, vc_first = 0, vc_last = 0;
+    auto vis_bounds = [&](uint32_t s_, uint32_t ci, uint32_t npos, uint32_t& p0, uint32_t& pl)
+        __attribute__((always_inline)) {
+        if (s_ != vc_s || ci < vc_c0 || ci - vc_c0 >= static_cast<uint32_t>(kWave)) {
+            vc_s = s_;
+            vc_c0 = ci;
+            const uint32_t cl = ci + lane;
+            const uint64_t row = static_cast<uint64_t>(s_) * a.vis_stride;
+            const bool in = static_cast<uint64_t>(cl) * kChunk < npos;
+            const uint32_t f = in ? cl * kChunk : 0u;
+            const uint32_t l = in ? min(cl * kChunk + kChunk - 1, npos - 1) : 0u;
+            vc_first = a.visible_pos[row + f];
+            vc_last = a.visible_pos[row + l];
+        }
+        p0 = lane_value(vc_first, ci - vc_c0);
+        pl = lane_value(vc_last, ci - vc_c0);
+    };
     auto meta_of = [&](bool live) __attribute__((always_inline)) -> Meta {
         Meta m;
         m.s = cur.s;
         m.cs = cur.ci * kChunk;
         const uint32_t nv = live ? min(static_cast<uint32_t>(kChunk), cur.npos - m.cs) : 0u;
-        m.p0 = VIS ? uniform(position_at<VIS>(a, m.s, m.cs)) : m.cs;
+        uint32_t pl = 0;
+        if (VIS) vis_bounds(m.s, cur.ci, cur.npos, m.p0, pl);
+        else m.p0 = m.cs;
         uint32_t tiled = 1;
         if (!TILED) {
             tiled = c.tiled_ok;
-            if (VIS && tiled && nv > 0) {
-                const uint32_t pl = uniform(position_at<VIS>(a, m.s, m.cs + nv - 1));
-                tiled = (m.p0 % kChunk == 0) && (pl - m.p0 == nv - 1) ? 1u : 0u;
-            }
+            // ascending distinct positions from a 64-aligned p0 to p0 + nv - 1
+            // are exactly the tile rows p0 .. p0 + nv - 1
+            if (VIS && tiled && nv > 0) tiled = (m.p0 % kChunk == 0) && (pl - m.p0 == nv - 1) ? 1u : 0u;
         }
         m.jf = cur.jf;
         m.info = nv | (tiled << 7) | (cur.nrec << 8);
@@ -898,54 +916,70 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 
     // Combine the nrec records of sequence ms (waves jf .. jf+nrec-1) into its
     // output rows.  Each lane combines, for each of its (head, 4 dims) items
-    // in the records' lane-order layout, four records per batch of
-    // independent loads (typically a single memory round trip), with a
-    // running max and rescaling as in the online softmax.
+    // in the records' lane-order layout, four records per batch with a running
+    // max and rescaling as in the online softmax.  A batch's loads for all the
+    // lane's items are issued together (device-coherent 8-byte loads the
+    // compiler tracks), so a batch costs one memory round trip whatever the
+    // number of items.
     auto merge = [&](uint32_t ms, uint32_t jf, uint32_t nrec) __attribute__((always_inline)) {
         const uint64_t rec0 = static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf;      // record of wave jf
+        float M[NHS], L[NHS];
+        f32x4 o[NHS][NCW];
+#pragma unroll
+        for (int hset = 0; hset < NHS; ++hset) {
+            M[hset] = -INFINITY;
+            L[hset] = 0.0f;
+#pragma unroll
+            for (int cw = 0; cw < NCW; ++cw) o[hset][cw] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (uint32_t i0 = 0; i0 < nrec; i0 += 4) {
+            f32x4 v[4][NHS][NCW];
+            f32x2 ml[4][NHS];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint64_t rec = rec0 + min(i0 + k, nrec - 1);
+#pragma unroll
+                for (int hset = 0; hset < NHS; ++hset) {
+                    ml[k][hset] = coherent_load2(a.part_ml + 2 * (rec * G + 4 * hset + g));
+#pragma unroll
+                    for (int cw = 0; cw < NCW; ++cw)
+                        v[k][hset][cw] = coherent_load4(a.part_acc + rec * kRecFloats +
+                                                        4 * ((hset * NCW + cw) * kWave + lane));
+                }
+            }
+#pragma unroll
+            for (int hset = 0; hset < NHS; ++hset) {
+                float bm = M[hset];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (i0 + k < nrec) bm = fmaxf(bm, ml[k][hset].x);
+                // A record whose row attended nothing (multi-row decode) has
+                // max -inf and sum 0: it gets weight 0, never exp2(nan).
+                const float sc = bm == -INFINITY ? 1.0f : exp2f(M[hset] - bm);
+                L[hset] *= sc;
+#pragma unroll
+                for (int cw = 0; cw < NCW; ++cw) o[hset][cw] *= sc;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float w = (i0 + k < nrec && ml[k][hset].x != -INFINITY) ? exp2f(ml[k][hset].x - bm) : 0.0f;
+                    L[hset] += w * ml[k][hset].y;
+#pragma unroll
+                    for (int cw = 0; cw < NCW; ++cw) o[hset][cw] += w * v[k][hset][cw];
+                }
+                M[hset] = bm;
+            }
+        }
 #pragma unroll
         for (int hset = 0; hset < NHS; ++hset) {
             const uint32_t hh = 4 * hset + g;
+            const float inv = L[hset] > 0.0f ? 1.0f / L[hset] : 0.0f;      // an empty prefix gives a zero row
 #pragma unroll
             for (int cw = 0; cw < NCW; ++cw) {
                 const uint32_t word = NCW * r + cw;
-                const uint32_t unit = 4 * ((hset * NCW + cw) * kWave + lane);
-                float M = -INFINITY, L = 0.0f;
-                f32x4 o = {0.f, 0.f, 0.f, 0.f};
-                for (uint32_t i0 = 0; i0 < nrec; i0 += 4) {
-                    const float* pv[4];
-                    const float* pm[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint64_t rec = rec0 + min(i0 + k, nrec - 1);
-                        pv[k] = a.part_acc + rec * kRecFloats + unit;
-                        pm[k] = a.part_ml + 2 * (rec * G + hh);
-                    }
-                    f32x4 v[4];
-                    f32x2 ml[4];
-                    coherent_load4x4(pv[0], pv[1], pv[2], pv[3], pm[0], pm[1], pm[2], pm[3],
-                                     v[0], v[1], v[2], v[3], ml[0], ml[1], ml[2], ml[3]);
-                    float bm = M;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (i0 + k < nrec) bm = fmaxf(bm, ml[k].x);
-                    // A record whose row attended nothing (multi-row decode) has
-                    // max -inf and sum 0: it gets weight 0, never exp2(nan).
-                    const float sc = bm == -INFINITY ? 1.0f : exp2f(M - bm);
-                    L *= sc;
-                    o *= sc;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float w = (i0 + k < nrec && ml[k].x != -INFINITY) ? exp2f(ml[k].x - bm) : 0.0f;
-                        L += w * ml[k].y;
-                        o += w * v[k];
-                    }
-                    M = bm;
-                }
                 if (hh < nh && word < hs4) {
-                    const float inv = L > 0.0f ? 1.0f / L : 0.0f;      // an empty prefix gives a zero row
+                    const f32x4 x = o[hset][cw];
                     *reinterpret_cast<float4*>(a.out + pair_out_row(a, ms, kvh, n_rep, nrow, h0 + hh) * hs + 4 * word) =
-                        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+                        make_float4(x.x * inv, x.y * inv, x.z * inv, x.w * inv);
                 }
             }
         }
