@@ -916,12 +916,15 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 
     // Combine the nrec records of sequence ms (waves jf .. jf+nrec-1) into its
     // output rows.  Each lane combines, for each of its (head, 4 dims) items
-    // in the records' lane-order layout, four records per batch with a running
-    // max and rescaling as in the online softmax.  A batch's loads for all the
+    // in the records' lane-order layout, a batch of records at a time (as many
+    // as 16 of the lane's 16-byte values allow, 2 to 8) with a running max and
+    // rescaling as in the online softmax.  A batch's loads for all the
     // lane's items are issued together (device-coherent 8-byte loads the
     // compiler tracks), so a batch costs one memory round trip whatever the
     // number of items.
     auto merge = [&](uint32_t ms, uint32_t jf, uint32_t nrec) __attribute__((always_inline)) {
+        // records per batch: MB * NHS * NCW 16-byte values in registers
+        constexpr int MB = NHS * NCW <= 2 ? 8 : (NHS * NCW <= 4 ? 4 : 2);
         const uint64_t rec0 = static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf;      // record of wave jf
         float M[NHS], L[NHS];
         f32x4 o[NHS][NCW];
@@ -932,11 +935,11 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 #pragma unroll
             for (int cw = 0; cw < NCW; ++cw) o[hset][cw] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        for (uint32_t i0 = 0; i0 < nrec; i0 += 4) {
-            f32x4 v[4][NHS][NCW];
-            f32x2 ml[4][NHS];
+        for (uint32_t i0 = 0; i0 < nrec; i0 += MB) {
+            f32x4 v[MB][NHS][NCW];
+            f32x2 ml[MB][NHS];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < MB; ++k) {
                 const uint64_t rec = rec0 + min(i0 + k, nrec - 1);
 #pragma unroll
                 for (int hset = 0; hset < NHS; ++hset) {
@@ -951,7 +954,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             for (int hset = 0; hset < NHS; ++hset) {
                 float bm = M[hset];
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
+                for (int k = 0; k < MB; ++k)
                     if (i0 + k < nrec) bm = fmaxf(bm, ml[k][hset].x);
                 // A record whose row attended nothing (multi-row decode) has
                 // max -inf and sum 0: it gets weight 0, never exp2(nan).
@@ -960,7 +963,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 #pragma unroll
                 for (int cw = 0; cw < NCW; ++cw) o[hset][cw] *= sc;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
+                for (int k = 0; k < MB; ++k) {
                     const float w = (i0 + k < nrec && ml[k][hset].x != -INFINITY) ? exp2f(ml[k][hset].x - bm) : 0.0f;
                     L[hset] += w * ml[k][hset].y;
 #pragma unroll
