@@ -916,15 +916,15 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 
     // Combine the nrec records of sequence ms (waves jf .. jf+nrec-1) into its
     // output rows.  Each lane combines, for each of its (head, 4 dims) items
-    // in the records' lane-order layout, a batch of records at a time (as many
-    // as 16 of the lane's 16-byte values allow, 2 to 8) with a running max and
-    // rescaling as in the online softmax.  A batch's loads for all the
+    // in the records' lane-order layout, a batch of records at a time (8 when
+    // the lane holds up to four 16-byte values per record, else 4) with a
+    // running max and rescaling as in the online softmax.  A batch's loads for all the
     // lane's items are issued together (device-coherent 8-byte loads the
     // compiler tracks), so a batch costs one memory round trip whatever the
     // number of items.
     auto merge = [&](uint32_t ms, uint32_t jf, uint32_t nrec) __attribute__((always_inline)) {
         // records per batch: MB * NHS * NCW 16-byte values in registers
-        constexpr int MB = NHS * NCW <= 2 ? 8 : (NHS * NCW <= 4 ? 4 : 2);
+        constexpr int MB = NHS * NCW <= 4 ? 8 : 4;
         const uint64_t rec0 = static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf;      // record of wave jf
         float M[NHS], L[NHS];
         f32x4 o[NHS][NCW];
