@@ -38,26 +38,42 @@ __device__ __forceinline__ float4 load4(const float* p, bool vec4) {
     return make_float4(p[0], p[1], p[2], p[3]);
 }
 
+// Per-lane operands of the step that do not depend on the vector: its four
+// weights and, for lanes holding rotated elements, four cos and four sin
+// values from the table row of the vector's position (rot/8 lanes hold the
+// first elements a of the pairs, the next rot/8 the second elements b).
+struct RopeLane {
+    float4 wt, c, s;
+};
+__device__ __forceinline__ float4 load_weight4(const float* weight, uint32_t w, uint32_t hs4, bool pvec4) {
+    return w < hs4 ? load4(weight + 4 * w, pvec4) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+__device__ __forceinline__ void load_cs4(const float* cs, uint32_t w, uint32_t rot, bool pvec4, float4& c, float4& s) {
+    const uint32_t h8 = rot / 8;
+    c = s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (w >= 2 * h8) return;
+    const uint32_t i0 = 4 * (w < h8 ? w : w - h8);
+    c = load4(cs + i0, pvec4);
+    s = load4(cs + rot / 2 + i0, pvec4);
+}
+
 // Lane w of a group of WIDTH lanes holds elements 4w .. 4w+3 of x (zeros for
 // w >= head_size/4); returns the same elements of the normalized and rotated
-// vector.  cs is the rotary table row of the vector's position.
+// vector.
 template <int WIDTH>
-__device__ __forceinline__ float4 norm_rope4(float4 x, uint32_t w, uint32_t head_size, const float* weight,
-                                             const float* cs, uint32_t rot, float eps, bool pvec4) {
+__device__ __forceinline__ float4 norm_rope4(float4 x, uint32_t w, uint32_t head_size, const RopeLane& op,
+                                             uint32_t rot, float eps) {
 #pragma clang fp contract(off)
     double ss = static_cast<double>(x.x) * x.x + static_cast<double>(x.y) * x.y +
                 static_cast<double>(x.z) * x.z + static_cast<double>(x.w) * x.w;
 #pragma unroll
     for (int off = WIDTH / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, WIDTH);
     const float r = static_cast<float>(1.0 / sqrt(ss / static_cast<double>(head_size) + static_cast<double>(eps)));
-    const uint32_t hs4 = head_size / 4;
-    float4 wt = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (w < hs4) wt = load4(weight + 4 * w, pvec4);
     float4 n;
-    n.x = (x.x * r) * wt.x;
-    n.y = (x.y * r) * wt.y;
-    n.z = (x.z * r) * wt.z;
-    n.w = (x.w * r) * wt.w;
+    n.x = (x.x * r) * op.wt.x;
+    n.y = (x.y * r) * op.wt.y;
+    n.z = (x.z * r) * op.wt.z;
+    n.w = (x.w * r) * op.wt.w;
     // Rotated lanes: the first rot/8 lanes hold the a's, the next rot/8 the b's.
     const uint32_t h8 = rot / 8;
     const bool first = w < h8, second = !first && w < 2 * h8;
@@ -68,11 +84,8 @@ __device__ __forceinline__ float4 norm_rope4(float4 x, uint32_t w, uint32_t head
     p.z = __shfl(n.z, static_cast<int>(src), WIDTH);
     p.w = __shfl(n.w, static_cast<int>(src), WIDTH);
     if (!first && !second) return n;
-    const uint32_t i0 = 4 * (first ? w : w - h8);
-    const uint32_t half = rot / 2;
-    const float4 c4 = load4(cs + i0, pvec4), s4 = load4(cs + half + i0, pvec4);
-    const float c[4] = {c4.x, c4.y, c4.z, c4.w};
-    const float s[4] = {s4.x, s4.y, s4.z, s4.w};
+    const float c[4] = {op.c.x, op.c.y, op.c.z, op.c.w};
+    const float s[4] = {op.s.x, op.s.y, op.s.z, op.s.w};
     const float nn[4] = {n.x, n.y, n.z, n.w}, pp[4] = {p.x, p.y, p.z, p.w};
     float y[4];
 #pragma unroll
@@ -122,8 +135,11 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a, bool vec
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live && w < hs4)
         x = load4(a.x + static_cast<uint64_t>(t) * a.x_stride + static_cast<uint64_t>(h) * a.head_stride + 4 * w, vec4);
+    RopeLane op;
+    op.wt = load_weight4(a.weight, w, hs4, a.params_vec4);
     const float* cs = live ? table_row(a.table, a.positions, t, a.rot, a.num_positions) : a.table;
-    const float4 y = norm_rope4<WIDTH>(x, w, a.head_size, a.weight, cs, a.rot, a.eps, a.params_vec4);
+    load_cs4(cs, w, a.rot, a.params_vec4, op.c, op.s);
+    const float4 y = norm_rope4<WIDTH>(x, w, a.head_size, op, a.rot, a.eps);
     if (live && w < hs4) {
         float* o = a.out + static_cast<uint64_t>(t) * a.out_stride + static_cast<uint64_t>(h) * a.head_size + 4 * w;
         if (vec4) *reinterpret_cast<float4*>(o) = y;
@@ -167,22 +183,32 @@ __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCach
         slot[i] = a.slot_mapping[t];
         if (a.rot > 0) posn[i] = a.positions[t];
     }
+    // The table rows of every pair's position, loaded together (one round
+    // trip after the rows), and the norm weight once per wave.
+    const uint32_t w = HALF ? (lane & 31) : lane;
+    RopeLane op[NP];
+    const float4 wt = load_weight4(a.weight, w, hs4, a.params_vec4);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        op[i].wt = wt;
+        op[i].c = op[i].s = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (slot[i] == kPadSlot || a.rot == 0) continue;
+        // positions[t] < num_positions is a caller contract: clamped rather than read out of bounds
+        const uint32_t p = posn[i] < a.num_positions ? posn[i] : a.num_positions - 1;
+        load_cs4(a.table + static_cast<uint64_t>(p) * a.rot, w, a.rot, a.params_vec4, op[i].c, op[i].s);
+    }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         if (slot[i] == kPadSlot) continue;
         const uint64_t block = slot[i] / a.block_size, off = slot[i] % a.block_size;
         if (block >= a.num_blocks) continue;             // out of contract; skipped rather than written out of bounds
-        // positions[t] < num_positions is a caller contract: clamped rather than read out of bounds
-        const uint32_t p = posn[i] < a.num_positions ? posn[i] : a.num_positions - 1;
-        const float* cs = a.rot > 0 ? a.table + static_cast<uint64_t>(p) * a.rot : a.table;
         const uint64_t dst = ((block * a.num_kv_heads + head[i]) * a.block_size + off) * wpt;
         if (HALF) {
-            const uint32_t w = lane & 31;
             const bool is_v = lane >= 32;
-            const float4 y = norm_rope4<32>(xk[i], w, a.head_size, a.weight, cs, a.rot, a.eps, a.params_vec4);
+            const float4 y = norm_rope4<32>(xk[i], w, a.head_size, op[i], a.rot, a.eps);
             pack_vector<32>(is_v ? xk[i] : y, (is_v ? a.value_cache : a.key_cache) + dst, hs4, w);
         } else {
-            const float4 y = norm_rope4<64>(xk[i], lane, a.head_size, a.weight, cs, a.rot, a.eps, a.params_vec4);
+            const float4 y = norm_rope4<64>(xk[i], lane, a.head_size, op[i], a.rot, a.eps);
             pack_vector<64>(y, a.key_cache + dst, hs4, lane);
             pack_vector<64>(xv[i], a.value_cache + dst, hs4, lane);
         }
@@ -219,9 +245,11 @@ hipError_t launch_norm_rope_cache_write(const NormRopeCacheWriteArgs& a, hipStre
                       a.key_stride % 4 == 0 && a.value_stride % 4 == 0;
     const bool half = a.head_size / 4 <= 32;
     if (pairs >= kWriteBatchMinPairs) {
-        const dim3 grid(static_cast<uint32_t>((pairs + 4 * kWritePairsPerWave - 1) / (4 * kWritePairsPerWave)));
-        if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, kWritePairsPerWave>), grid, dim3(256), 0, stream, a, vec4);
-        else hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, kWritePairsPerWave>), grid, dim3(256), 0, stream, a, vec4);
+        // Two pairs per wave: the step's registers for four would cut occupancy from 8 waves per SIMD to 5.
+        constexpr int NP = 2;
+        const dim3 grid(static_cast<uint32_t>((pairs + 4 * NP - 1) / (4 * NP)));
+        if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, NP>), grid, dim3(256), 0, stream, a, vec4);
+        else hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, NP>), grid, dim3(256), 0, stream, a, vec4);
     } else {
         const dim3 grid(static_cast<uint32_t>((pairs + 3) / 4));
         if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, 1>), grid, dim3(256), 0, stream, a, vec4);
