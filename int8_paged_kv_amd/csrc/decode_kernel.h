@@ -15,8 +15,8 @@
 //     up to 8 of its query heads; in multi-row decode, up to 8 (row, head)
 //     pairs) the chunks of all sequences form one sequence of C chunks, and a
 //     fixed number of persistent wavefronts per row group each take an equal
-//     contiguous range of it, weighted by cost (each nonempty sequence adds
-//     one unit for its fixed work).  This is the split-context idea of the
+//     contiguous range of it, weighted by cost (a chunk 4 units, the fixed
+//     work of each nonempty sequence 7).  This is the split-context idea of the
 //     "attention.rs" page, balanced over the whole batch instead of per
 //     sequence.  A wave that covers a whole sequence writes its output
 //     directly; otherwise it writes a softmax partial (running max, sum,
@@ -58,6 +58,13 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kDigitBias = 0x80808080u;
+
+// Cost units that split a row group's work evenly among its waves (per-wave
+// stamps on the Llama-shaped batch: a chunk costs about 2.6 us of wave time, a
+// sequence's start about 1.8 times that: its q digits, the output or partial
+// record of the previous sequence, the counter round trip).
+constexpr uint32_t kCostChunk = 4;
+constexpr uint32_t kCostSeq = 7;
 
 __device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
@@ -290,6 +297,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     __shared__ __align__(16) uint32_t sV_[kWavesPerGroup][NBUF][NU * 4 * kWave];
     __shared__ __align__(16) uint32_t sA_[kWavesPerGroup][NHS * 16 * 16];    // [set][head*4+digit][w]: weight digits
     __shared__ int sEq_[kWavesPerGroup][G];
+    // q-digit scratch of its own (LDS-direct loads, one set of 4 heads: it fits
+    // the budget there), so that a sequence change can form the new q digits
+    // while the next chunk's loads are already in flight; elsewhere the next
+    // chunk's buffer serves, before those loads are issued.
+    constexpr bool QSCR = DMA && NHS == 1;
+    constexpr int QSCR_WORDS = NHS * NKB * 256 + (G * QD / (4 * kWave)) * kWave;
+    __shared__ __align__(16) uint32_t sQs_[kWavesPerGroup][QSCR ? QSCR_WORDS : 1];
     const uint32_t wid = uniform(threadIdx.x / kWave);
     // sK/sV: the tiles of the chunk being processed; sKn/sVn: where the next
     // chunk's segments land (the same buffer without LDS-direct loads).
@@ -311,18 +325,19 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 
     // ---- this wave's chunk range [x0, x1) of the row group's chunk sequence ----
     // The waves split the row group's work into equal contiguous ranges of
-    // cost units.  A chunk costs one unit.  Starting a new sequence inside a
-    // range costs about as much again (closing the previous sequence's piece
-    // and forming the new q), so with at least two units per wave and up to
-    // 64 sequences each non-empty sequence also gets one unit before its first
-    // chunk; otherwise the units are the chunks alone.  Every range then holds
-    // at least one chunk.
+    // cost units.  A chunk costs kCostChunk units; starting a new sequence
+    // inside a range (closing the previous sequence's piece, forming the new
+    // q) costs kCostSeq more, measured.  With up to 64 sequences and at least
+    // kCostChunk + kCostSeq units per wave (the widest gap between two chunks'
+    // cost indices) the units are weighted so; otherwise they are the chunks
+    // alone.  Every range then holds at least one chunk.
     // Up to 64 sequences: one load and one scan give every sequence's chunk
     // count and offsets, kept in lane s.
     const bool one_window = a.num_seqs <= static_cast<uint32_t>(kWave);
     const bool append = !VIS && a.new_key != nullptr;     // decode step: append, then attend
     uint32_t C, U, win_np = 0, win_nc = 0, win_incl = 0, win_cinc = 0, win_len = 0;
     bool weighted = false;
+    uint32_t ua = 1;      // cost units of a chunk (kCostChunk when weighted)
     if (one_window) {
         win_np = lane < a.num_seqs ? positions_of<VIS>(a, lane) : 0u;
         if ((append || a.rows_per_seq > 1) && lane < a.num_seqs) win_len = a.context_lens[lane];
@@ -331,10 +346,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         C = uniform(lane_value(win_incl, kWave - 1));
         const uint64_t ne = __ballot(win_np > 0);
         const uint32_t sne = static_cast<uint32_t>(__builtin_popcountll(ne));
-        weighted = C + sne >= 2 * c.waves_per_rg;
-        U = weighted ? C + sne : C;
+        const uint64_t uw = static_cast<uint64_t>(kCostChunk) * C + static_cast<uint64_t>(kCostSeq) * sne;
+        weighted = uw >= static_cast<uint64_t>(kCostChunk + kCostSeq) * c.waves_per_rg && uw < (1ull << 31);
+        ua = weighted ? kCostChunk : 1u;
+        U = weighted ? static_cast<uint32_t>(uw) : C;
         const uint64_t upto = lane == kWave - 1 ? ~0ull : (2ull << lane) - 1;
-        win_cinc = win_incl + (weighted ? static_cast<uint32_t>(__builtin_popcountll(ne & upto)) : 0u);
+        win_cinc = ua * win_incl + (weighted ? kCostSeq * static_cast<uint32_t>(__builtin_popcountll(ne & upto)) : 0u);
     } else {
         uint32_t unused;
         chunk_totals<VIS>(a, lane, 0, C, unused);
@@ -355,18 +372,20 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         if (C == 0 && j == 0) zero_seqs(0, a.num_seqs);
         return;
     }
-    // First chunk whose cost index is at least u (u < U), its sequence, the
-    // chunks before that sequence and its positions.  Cost index of chunk i of
-    // sequence s: the units of the sequences before s, plus one when
-    // weighted, plus i.
+    // First chunk whose cost index is at least u (u < U, and when weighted
+    // u <= U - kCostChunk - kCostSeq, as every range bound is), its sequence,
+    // the chunks before that sequence and its positions.  Cost index of chunk
+    // i of sequence s: the units of the sequences before s, plus kCostSeq when
+    // weighted, plus ua*i.  Its sequence is the first whose last chunk's cost
+    // index (its cumulative units minus ua) reaches u.
     auto chunk_at_cost = [&](uint32_t u, uint32_t& s_out, uint32_t& before_out, uint32_t& np_out) __attribute__((always_inline)) -> uint32_t {
         if (one_window) {
-            const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(__ballot(win_cinc > u)));
+            const uint32_t l = static_cast<uint32_t>(__builtin_ctzll(__ballot(win_cinc > u + ua - 1)));
             s_out = l;
             before_out = lane_value(win_incl - win_nc, l);
             np_out = lane_value(win_np, l);
-            const uint32_t cf = lane_value(win_cinc - win_nc, l);     // cost index of its first chunk
-            return before_out + (u > cf ? u - cf : 0u);
+            const uint32_t cf = lane_value(win_cinc - ua * win_nc, l);     // cost index of its first chunk
+            return before_out + (u > cf ? (u - cf + ua - 1) / ua : 0u);
         }
         locate_chunk<VIS>(a, lane, u, s_out, before_out);
         np_out = 0;
@@ -381,7 +400,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     if (uniform(s0) >= a.num_seqs || n == 0) return;    // unreachable: every range holds a chunk
     // Cost index of the first chunk of the sequence at cursor state (s, before).
     auto first_cost = [&](uint32_t s_, uint32_t before_) __attribute__((always_inline)) -> uint32_t {
-        return one_window ? lane_value(win_cinc - win_nc, s_) : before_;
+        return one_window ? lane_value(win_cinc - ua * win_nc, s_) : before_;
     };
 
     const uint32_t hs = a.head_size, hs4 = EXACT ? HS4P : hs / 4, wpt = hs4 + 1;
@@ -401,7 +420,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     auto share = [&]() __attribute__((always_inline)) {
         const uint32_t cf = first_cost(cur.s, cur.before);
         cur.jf = wave_of_chunk(cf, U, W);
-        cur.nrec = wave_of_chunk(cf + (cur.npos + kChunk - 1) / kChunk - 1, U, W) - cur.jf + 1;
+        cur.nrec = wave_of_chunk(cf + ua * ((cur.npos + kChunk - 1) / kChunk - 1), U, W) - cur.jf + 1;
     };
     share();
     // Sequences with no positions get zero rows.  Each is written by exactly
@@ -729,8 +748,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     // once and scatters each value's four digits to the lanes whose MFMA rows
     // hold them, through LDS in the operand layout [set][k-block][lane][w].
     auto q_finish = [&]() __attribute__((always_inline)) {
-        uint32_t* const sDig = sKn;       // free: the next chunk's loads (if any) go to the other buffer
-        float* const sMax = reinterpret_cast<float*>(sKn) + NHS * NKB * 256;
+        uint32_t* const scratch = QSCR ? sQs_[wid] : sKn;   // sKn: no loads are landing in it yet
+        uint32_t* const sDig = scratch;
+        float* const sMax = reinterpret_cast<float*>(scratch) + NHS * NKB * 256;
 #pragma unroll
         for (int t = 0; t < QF; ++t) {
             const float4 v = qv[t];
@@ -1063,12 +1083,24 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     q_finish();
     uint32_t q_seq_prev = mc.s;
     for (uint32_t xr = 0;; ++xr) {
-        if (xr > 0 && mc.s != q_seq_prev) q_finish();          // q of mc.s was staged one step ago
+        // q of mc.s was staged one step ago; its digits are formed before the
+        // next sequence's q rows are staged into the same registers.
+        const bool new_q = xr > 0 && mc.s != q_seq_prev;
+        if (!QSCR && new_q) q_finish();
         store(mc, bA);
+        if (QSCR && new_q) {
+            // The staged q rows have landed (store waited for every load).  Use
+            // them here so that the compiler's wait for them sits here, before
+            // the next chunk's LDS-direct loads it does not count; placed at
+            // q_finish it would also wait for those.
+#pragma unroll
+            for (int t = 0; t < QF; ++t) asm volatile("" : : "v"(qv[t].x), "v"(qv[t].y), "v"(qv[t].z), "v"(qv[t].w));
+        }
         if (xr + 2 < n) advance();
         const Meta mn2 = meta_of(xr + 2 < n);
         issue_data(mn1, bA, sKn, sVn);
         issue_new(mn1);
+        if (QSCR && new_q) q_finish();                        // with the next chunk's loads in flight
         if (mn1.s != mc.s) q_issue(mn1.s);                    // q of the next chunk's sequence
         wave_sync();
         process(mc);
