@@ -159,7 +159,8 @@ def main():
         allj = last_json(os.path.join(d, "trace_all.log"))
         out = [
             "# rocprofv3 kernel trace of every kernel the bench runs, Llama-3-8B-shaped batch",
-            "# (step, two-launch reference, 4-row decode, f32-cache step, norm + rotary step, 16384-token bulk writes)",
+            "# (step, two-launch reference, 4-row decode, f32-cache step, norm + rotary step, 16384-token bulk",
+            "# writes, selected-token step: block selection + visible-list decode)",
             "#",
             "# command (from any directory on the GPU machine):",
             "#   " + TRACE_ALL_CMD.format(d=args.cmd_dir),
@@ -175,7 +176,8 @@ def main():
             out.append("%-60s %9d %5d %9.2f %9.2f %9.2f %5d %6d" % (
                 nm[:60], grid, len(durs), statistics.mean(durs), statistics.median(durs), max(durs), vgpr, lds))
         out += ["", "bench.py line of the same run (reference legs):"]
-        for k in ("two_launch_reference", "multi_row_decode", "f32_cache_reference", "norm_rope_step"):
+        for k in ("two_launch_reference", "multi_row_decode", "f32_cache_reference", "norm_rope_step",
+                  "selected_step"):
             out.append("  %s: %s" % (k, json.dumps(allj.get(k))))
         with open(os.path.join(ROOT, "profiles", "llama_step_all_kernels_trace.txt"), "w") as f:
             f.write("\n".join(out) + "\n")
