@@ -54,11 +54,14 @@ def test_shapes_and_paths(oracle_mod, S, H, Hkv, hs, bs, lens):
     assert_close(c.gpu(), c.oracle(oracle_mod), "shape %s" % ((S, H, Hkv, hs, bs, lens),))
 
 
-@pytest.mark.parametrize("waves", [1, 7, 64, 333, 4096])
+@pytest.mark.parametrize("waves", [1, 7, 64, 84, 86, 88, 333, 4096])
 def test_wavefront_range_boundaries(oracle_mod, decode_waves, waves):
     """Chunk ranges of the persistent wavefronts: one wave for everything,
     waves spanning several sequences (and empty ones), sequences split over
-    many waves, and one chunk per wave."""
+    many waves, and one chunk per wave.  These lengths make 100 chunks in 11
+    non-empty sequences per row group (2 row groups), 477 weighted cost units:
+    84 and 86 waves leave 11.4 and 11.1 units per wave (weighted split), 88
+    leave 10.8 (chunks alone)."""
     from gpu_util import RandomCase, assert_close
     lens = [0, 63, 64, 65, 255, 256, 257, 0, 1023, 1024, 1025, 2049, 1]
     decode_waves(waves)
