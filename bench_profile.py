@@ -39,6 +39,8 @@ PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc
            "-- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
 TRACE_ALL_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d {d}/trace_all -o bench -f csv "
                  "-- python3 /root/repo/bench.py --steps 20 --warmup 5 --no-cpu")
+L2_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum "
+          "-d {d}/pmc_L2 -o bench -f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
 COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} -d {d}/copy_{c} -o copy -f csv "
             "-- python3 /root/repo/bench.py --copy-calibration {mib}")
 
@@ -62,6 +64,15 @@ def counters(path: str):
     with open(path) as f:
         for r in csv.DictReader(f):
             out[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return out
+
+
+def counters_by_name(path: str):
+    """{(kernel, grid, counter): [value per dispatch]}"""
+    out = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out[(r["Kernel_Name"], int(r["Grid_Size"]), r["Counter_Name"])].append(float(r["Counter_Value"]))
     return out
 
 
@@ -231,6 +242,27 @@ def main():
         fk, wk, rd, wr = per_kernel[k]
         t.append("#   %-20s FETCH_SIZE %10.1f KiB -> %12.0f B read, WRITE_SIZE %9.1f KiB -> %11.0f B written" % (
             k, fk, rd, wk, wr))
+    l2_line, l2_key = [], []
+    l2_csv = os.path.join(d, "pmc_L2", "bench_counter_collection.csv")
+    if os.path.exists(l2_csv):
+        if last_json(os.path.join(d, "pmc_L2.log"))["kernel_sources_sha256_16"] != digest:
+            raise SystemExit("L2 counter run was taken on different kernel sources")
+        cb = counters_by_name(l2_csv)
+        hit = [v for (name, grid, c), vs in cb.items()
+               if "decode_split_kernel" in name and grid == step_grid.get("decode_split_kernel") and c.startswith("TCC_HIT")
+               for v in vs]
+        miss = [v for (name, grid, c), vs in cb.items()
+                if "decode_split_kernel" in name and grid == step_grid.get("decode_split_kernel") and c.startswith("TCC_MISS")
+                for v in vs]
+        if hit and miss:
+            h, m = statistics.median(hit), statistics.median(miss)
+            l2_line = ["#", "# L2 (TCC) requests of the step launch, median per dispatch (command:",
+                       "#   " + L2_CMD.format(d=args.cmd_dir) + "):",
+                       "#   hits %.0f, misses %.0f -> hit rate %.4f (K/V tiles are read once per row group and"
+                       " loaded nontemporal;" % (h, m, h / (h + m)),
+                       "#   the hits are the shared q rows, block tables, lengths and the re-read partial records)"]
+            l2_key = ["l2_hit_rate: %.4f" % (h / (h + m))]
+    t += l2_line
     t += [
         "#   algorithmic bytes per step: int8 KV (codes + scale word of every attended row, K and V) %d"
         " + cache append %d" % (eff, bench_trace["roofline"]["algorithmic_bytes_per_launch"] - eff),
@@ -242,7 +274,7 @@ def main():
         "split_read_bytes: %.0f" % per_kernel["decode_split_kernel"][2],
         "split_write_bytes: %.0f" % per_kernel["decode_split_kernel"][3],
         "hbm_bytes_per_step: %.0f" % dec_bytes,
-    ]
+    ] + l2_key
     with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_traffic.txt"), "w") as f:
         f.write("\n".join(t) + "\n")
     print("wrote profiles/q8_paged_decode_llama_kernel_trace.txt and profiles/q8_paged_decode_llama_traffic.txt")
