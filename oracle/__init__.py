@@ -75,7 +75,7 @@ def _load():
         lib.q8o_norm_rope.restype = ctypes.c_int
         lib.q8o_norm_rope_cache_write.argtypes = [P, U, P, U, P, P, P, P, P, P, U, U, F, U, U, U, U, U]
         lib.q8o_norm_rope_cache_write.restype = ctypes.c_int
-        lib.q8o_index_select.argtypes = [P, U, P, U, U, U, P, U, P]
+        lib.q8o_index_select.argtypes = [P, U, P, U, U, U, P, U, P, P, U]
         lib.q8o_index_select.restype = ctypes.c_int
         lib.q8o_max_threads.argtypes = []
         lib.q8o_max_threads.restype = ctypes.c_int
@@ -334,15 +334,18 @@ def norm_rope_cache_write(key, value, key_cache, value_cache, slot_mapping, posi
 
 # ---------------------------------------------------------------- block select ----
 
-def index_select(scores, row_lens, ratio: int, k: int, vis_stride: int):
+def index_select(scores, row_lens, ratio: int, k: int, vis_stride: int, mask_stride: int = 0):
     """Visible lists from block scores: returns (visible_pos u32 [rows, vis_stride]
-    (unused tail entries 0), num_visible u32 [rows])."""
+    (unused tail entries 0), num_visible u32 [rows]); with mask_stride > 0 also
+    the block bitmask u32 [rows, mask_stride] (bit j of a row: the list holds a
+    position of block j)."""
     scores = _c(scores, np.float32)
     row_lens = _c(row_lens, np.uint32)
     R = row_lens.shape[0]
     stride = scores.shape[-1] if scores.ndim > 1 else scores.size
     vis = np.zeros((R, vis_stride), dtype=np.uint32)
     nv = np.zeros(R, dtype=np.uint32)
+    mask = np.zeros((R, mask_stride), dtype=np.uint32) if mask_stride else None
     _check(_load().q8o_index_select(_ptr(scores), stride, _ptr(row_lens), R, ratio, k, _ptr(vis), vis_stride,
-                                    _ptr(nv)), "index_select")
-    return vis, nv
+                                    _ptr(nv), _ptr(mask), mask_stride), "index_select")
+    return (vis, nv, mask) if mask_stride else (vis, nv)

@@ -79,7 +79,11 @@
  *   not printed; the reading taken: the kblk complete blocks of highest score
  *   (ties to the lower block index), their positions in ascending order, then
  *   the trailing incomplete block's positions.  When blocks <= kblk every
- *   complete block is taken, which is the dense list 0 .. t_len-1.
+ *   complete block is taken, which is the dense list 0 .. t_len-1.  The pass
+ *   also emits a per-row bitmask of ceil(max_blocks/32) words (max_blocks =
+ *   max_t/ratio + 1, so the trailing block has a bit); its meaning is not
+ *   printed either: bit j (word j/32, bit j%32) is set exactly when the list
+ *   holds a position of block j.
  *
  * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fopenmp -fPIC
  * -shared.  On x86-64 (SSE, FLT_EVAL_METHOD == 0) every float operation above
@@ -575,9 +579,11 @@ int q8o_norm_rope_cache_write(const float* key, uint32_t key_stride,
 
 /* Row r: scores[r*score_stride + j] for its complete blocks j < row_lens[r] /
  * ratio.  Writes visible_pos[r*vis_stride + i], i < num_visible[r]. */
+/* visible_mask may be NULL; otherwise mask_stride words per row, all written. */
 int q8o_index_select(const float* scores, uint32_t score_stride, const uint32_t* row_lens,
                      uint32_t num_rows, uint32_t ratio, uint32_t k,
-                     uint32_t* visible_pos, uint32_t vis_stride, uint32_t* num_visible)
+                     uint32_t* visible_pos, uint32_t vis_stride, uint32_t* num_visible,
+                     uint32_t* visible_mask, uint32_t mask_stride)
 {
     if (ratio == 0) return Q8O_ERR_SHAPE;
     if ((uint64_t)k * ratio + ratio > vis_stride) return Q8O_ERR_SHAPE;   /* the longest list must fit */
@@ -601,6 +607,15 @@ int q8o_index_select(const float* scores, uint32_t score_stride, const uint32_t*
         }
         for (uint32_t p = blocks * ratio; p < t_len; ++p) out[n++] = p;
         num_visible[r] = n;
+        if (visible_mask) {
+            uint32_t* m = visible_mask + (uint64_t)r * mask_stride;
+            memset(m, 0, (size_t)mask_stride * sizeof(uint32_t));
+            for (uint32_t e = 0; e < n; ++e) {
+                uint32_t b = out[e] / ratio;
+                if (b / 32 >= mask_stride) return Q8O_ERR_RANGE;   /* a touched block has no bit */
+                m[b / 32] |= 1u << (b % 32);
+            }
+        }
     }
     return Q8O_OK;
 }

@@ -82,3 +82,46 @@ def test_out_of_contract_rejected():
         oracle.index_select(np.array([[1, np.nan, 2]], np.float32), np.array([12]), 4, 1, 8)
     with pytest.raises(Exception):
         oracle.index_select(np.zeros((1, 2), np.float32), np.array([12]), 4, 1, 8)     # 3 blocks, 2 scores
+
+
+def brute_mask(scores, t_len, ratio, k, words):
+    """Bit j set for each kept complete block j and for the trailing block."""
+    blocks = t_len // ratio
+    keep = sorted(range(blocks), key=lambda j: (-float(scores[j]), j))[:k]
+    bits = set(keep) | ({blocks} if t_len % ratio else set())
+    m = [0] * words
+    for j in bits:
+        m[j // 32] |= 1 << (j % 32)
+    return m
+
+
+def test_mask_hand_example():
+    # blocks 2 and 3 kept, positions 20..21 of block 5 as the tail: bits 2, 3, 5
+    _, _, m = oracle.index_select(np.array([[3, 1, 5, 5, 0]], np.float32), np.array([22]), 4, 2, 12, mask_stride=2)
+    assert m[0].tolist() == [0b101100, 0]
+    # dense row (3 complete blocks <= k = 4) with a tail: blocks 0..3
+    _, _, m = oracle.index_select(np.zeros((1, 4), np.float32), np.array([13]), 4, 4, 20, mask_stride=1)
+    assert m[0].tolist() == [0b1111]
+    # empty row: no bits, every word still written
+    _, _, m = oracle.index_select(np.zeros((1, 4), np.float32), np.array([0]), 4, 1, 8, mask_stride=3)
+    assert m[0].tolist() == [0, 0, 0]
+
+
+@pytest.mark.parametrize("ratio,k,max_blocks", [(1, 40, 127), (4, 2, 13), (64, 32, 100)])
+def test_mask_brute_force_across_words(ratio, k, max_blocks):
+    g = np.random.default_rng(ratio * 7 + k)
+    R = 30
+    words = (max_blocks + 1 + 31) // 32
+    scores = g.integers(-3, 4, (R, max_blocks)).astype(np.float32)
+    lens = g.integers(0, max_blocks * ratio + ratio, R).astype(np.uint32)
+    _, nv, m = oracle.index_select(scores, lens, ratio, k, k * ratio + ratio, mask_stride=words)
+    for r in range(R):
+        assert m[r].tolist() == brute_mask(scores[r], int(lens[r]), ratio, k, words)
+        # popcount * ratio covers the list: whole blocks plus at most one partial one
+        pc = sum(bin(int(w)).count("1") for w in m[r])
+        assert pc == -(-int(nv[r]) // ratio)
+
+
+def test_mask_too_narrow_rejected():
+    with pytest.raises(Exception):    # the tail block 32 needs a second word
+        oracle.index_select(np.zeros((1, 40), np.float32), np.array([32 * 4 + 1]), 4, 40, 164, mask_stride=1)
