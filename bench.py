@@ -376,6 +376,8 @@ def main():
         vstride = ws_.visible_pos.shape[1]
         vis5 = torch.zeros((ws_.num_seqs, vstride), dtype=torch.int32, device=dev)
         nv5 = torch.zeros((ws_.num_seqs,), dtype=torch.int32, device=dev)
+        mstride5 = (nblk5 + 1 + 31) // 32
+        mask5 = torch.zeros((ws_.num_seqs, mstride5), dtype=torch.int32, device=dev)
         q5, bt5 = f32(ws_.q()), u32(ws_.block_tables)
         out5 = torch.empty((ws_.num_seqs, ws_.num_heads, ws_.head_size), dtype=torch.float32, device=dev)
         ws5 = torch.zeros(max(1, q8_paged_decode_workspace_bytes(ws_.num_seqs, ws_.num_heads, ws_.num_kv_heads,
@@ -385,7 +387,8 @@ def main():
         def sel_step(ev=None):
             if ev is not None:
                 ev[0].record()
-            q8_index_select(sc5d, cl5, ratio_, k_, vstride, visible_pos=vis5, num_visible=nv5)
+            q8_index_select(sc5d, cl5, ratio_, k_, vstride, visible_pos=vis5, num_visible=nv5,
+                            mask_stride=mstride5, visible_mask=mask5)
             if ev is not None:
                 ev[1].record()
             q8_paged_decode(q5, kc5, vc5, bt5, cl5, ws_.scale, ws_.num_kv_heads, ws_.block_size,
@@ -411,7 +414,8 @@ def main():
                     "decode_effective_GBps": round(B5 / (float(td_.mean()) * 1e-6) / 1e9, 1),
                     "lists_match_workload": bool(np.array_equal(nv5.cpu().numpy().view(np.uint32),
                                                                 ws_.num_visible)),
-                    "note": "q8_index_select over one score per complete block (16 rows x 1023), then "
+                    "note": "q8_index_select over one score per complete block (16 rows x 1023, lists and block "
+                            "bitmasks), then "
                             "q8_paged_decode over the lists; scores rank each sequence's workload blocks first"}
         del kc5, vc5
 

@@ -365,7 +365,10 @@ q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
  * complete blocks of highest score (ties to the lower block index), their
  * positions ascending, then the trailing incomplete block's positions; with
  * blocks <= k, every position 0 .. t_len-1.  The lists feed q8_paged_decode's
- * visible-position mode directly.
+ * visible-position mode directly.  The pass also emits the per-row block
+ * bitmask the page sizes as ceil(max_blocks/32) words; its meaning is not
+ * printed either: bit j (word j/32, bit j%32) is set exactly when the list
+ * holds a position of block j.
  *   scores        device f32; row r's block j at scores[r*score_stride + j],
  *                 finite, read for j < blocks only.
  *   row_lens      device u32 [num_rows]: t_len per row; t_len / ratio <=
@@ -373,13 +376,21 @@ q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
  *   visible_pos   device u32; row r's list at visible_pos[r*vis_stride + i],
  *                 i < num_visible[r]; entries past it are left untouched.
  *   num_visible   device u32 [num_rows].
- * Errors: Q8_ERR_NULL; Q8_ERR_SHAPE when ratio == 0 or (k + 1)*ratio >
- * vis_stride (the longest list must fit); Q8_ERR_UNSUPPORTED when
- * score_stride > 16384.  num_rows == 0 enqueues nothing.
+ *   visible_mask  device u32 or NULL (no mask); row r's bits at
+ *                 visible_mask[r*mask_stride + w], all mask_stride words
+ *                 written (0 where no block is touched).
+ *   mask_stride   words per mask row, >= ceil((score_stride + 1) / 32): a bit
+ *                 for every complete block and the trailing one.  Ignored
+ *                 when visible_mask is NULL.
+ * Errors: Q8_ERR_NULL; Q8_ERR_SHAPE when ratio == 0, (k + 1)*ratio >
+ * vis_stride (the longest list must fit) or the mask rows are too narrow;
+ * Q8_ERR_UNSUPPORTED when score_stride > 16384.  num_rows == 0 enqueues
+ * nothing.
  */
 q8_status q8_index_select(const float* scores, uint32_t score_stride, const uint32_t* row_lens,
                           uint32_t num_rows, uint32_t ratio, uint32_t k, uint32_t* visible_pos,
-                          uint32_t vis_stride, uint32_t* num_visible, void* stream);
+                          uint32_t vis_stride, uint32_t* num_visible, uint32_t* visible_mask,
+                          uint32_t mask_stride, void* stream);
 
 /* hipError_t code behind the calling thread's last Q8_ERR_HIP (0 if none). */
 int q8_last_hip_error(void);

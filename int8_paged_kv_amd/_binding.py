@@ -66,7 +66,7 @@ def load_library() -> ctypes.CDLL:
         lib.q8_norm_rope.restype = ctypes.c_int
         lib.q8_norm_rope_cache_write.argtypes = [P, U, P, U, P, P, P, P, P, P, U, U, F, U, U, U, U, U, P]
         lib.q8_norm_rope_cache_write.restype = ctypes.c_int
-        lib.q8_index_select.argtypes = [P, U, P, U, U, U, P, U, P, P]
+        lib.q8_index_select.argtypes = [P, U, P, U, U, U, P, U, P, P, U, P]
         lib.q8_index_select.restype = ctypes.c_int
         lib.q8_last_hip_error.argtypes = []
         lib.q8_last_hip_error.restype = ctypes.c_int
@@ -395,9 +395,10 @@ def q8_norm_rope_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: 
 
 def q8_index_select(scores: torch.Tensor, row_lens: torch.Tensor, ratio: int, k: int, vis_stride: int,
                     visible_pos: Optional[torch.Tensor] = None, num_visible: Optional[torch.Tensor] = None,
-                    stream=None):
+                    mask_stride: int = 0, visible_mask: Optional[torch.Tensor] = None, stream=None):
     """Visible lists from block scores [rows, max_blocks] (see include/q8kv.h).
-    Returns (visible_pos [rows, vis_stride], num_visible [rows]) as int32 tensors of u32 bits."""
+    Returns (visible_pos [rows, vis_stride], num_visible [rows]) as int32 tensors of u32 bits;
+    with mask_stride > 0 also the block bitmask [rows, mask_stride] as a third element."""
     lib = load_library()
     if scores.dim() != 2 or scores.stride(1) != 1:
         raise ValueError("scores must be [rows, max_blocks] with dense rows")
@@ -406,8 +407,13 @@ def q8_index_select(scores: torch.Tensor, row_lens: torch.Tensor, ratio: int, k:
         visible_pos = torch.zeros((R, vis_stride), dtype=torch.int32, device=scores.device)
     if num_visible is None:
         num_visible = torch.zeros((R,), dtype=torch.int32, device=scores.device)
+    if mask_stride and visible_mask is None:
+        visible_mask = torch.zeros((R, mask_stride), dtype=torch.int32, device=scores.device)
+    if visible_mask is not None and (not mask_stride or tuple(visible_mask.shape) != (R, mask_stride)
+                                     or not visible_mask.is_contiguous()):
+        raise ValueError("visible_mask must be a contiguous [rows, mask_stride] tensor")
     st = lib.q8_index_select(_dev(scores, "scores", torch.float32), scores.stride(0), _u32(row_lens, "row_lens"), R,
                              ratio, k, _u32(visible_pos, "visible_pos"), vis_stride, _u32(num_visible, "num_visible"),
-                             _stream(stream))
+                             _u32(visible_mask, "visible_mask"), mask_stride, _stream(stream))
     _check(st, "q8_index_select")
-    return visible_pos, num_visible
+    return (visible_pos, num_visible, visible_mask) if mask_stride else (visible_pos, num_visible)

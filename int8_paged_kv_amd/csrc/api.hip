@@ -388,8 +388,12 @@ q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
 
 q8_status q8_index_select(const float* scores, uint32_t score_stride, const uint32_t* row_lens,
                           uint32_t num_rows, uint32_t ratio, uint32_t k, uint32_t* visible_pos,
-                          uint32_t vis_stride, uint32_t* num_visible, void* stream) {
+                          uint32_t vis_stride, uint32_t* num_visible, uint32_t* visible_mask,
+                          uint32_t mask_stride, void* stream) {
     if (ratio == 0 || (static_cast<uint64_t>(k) + 1) * ratio > vis_stride) return Q8_ERR_SHAPE;
+    // a bit for each block a row can touch: score_stride complete ones and a trailing one
+    if (visible_mask && static_cast<uint64_t>(mask_stride) * 32 < static_cast<uint64_t>(score_stride) + 1)
+        return Q8_ERR_SHAPE;
     if (score_stride > q8kv::kSelectMaxBlocks) return Q8_ERR_UNSUPPORTED;
     if (num_rows == 0) return Q8_OK;
     if (!scores || !row_lens || !visible_pos || !num_visible) return Q8_ERR_NULL;
@@ -404,6 +408,8 @@ q8_status q8_index_select(const float* scores, uint32_t score_stride, const uint
     a.ratio = ratio;
     a.k = k;
     a.vis_stride = vis_stride;
+    a.visible_mask = visible_mask;
+    a.mask_stride = visible_mask ? mask_stride : 0;
     const hipError_t e = q8kv::launch_index_select(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }

@@ -16,6 +16,14 @@
 // equal to T to take.  Two block scans in index order then mark the taken
 // ties (the lowest-indexed ones) and give each selected block its slot; all
 // threads write the list.  O(blocks) per row whatever the scores.
+//
+// The optional block bitmask (bit j: the list holds a position of block j)
+// comes from the same pass: in the selective case each wave's ballot over its
+// 64 blocks of a scan chunk is two mask words (chunks start at multiples of
+// 256 blocks, so words never straddle waves), the trailing block's bit joins
+// the ballot of the lane that holds its index, and words past the last chunk
+// are written by a final sweep; the dense and tail-only cases have closed
+// forms per word.
 #include "q8kv_internal.h"
 #include "wave_ops.h"
 
@@ -73,14 +81,28 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(IndexSelectAr
     const uint32_t head = k * a.ratio;
     uint32_t tail = t_len - blocks * a.ratio;
     tail = tail < a.vis_stride - head ? tail : a.vis_stride - head;
+    uint32_t* const bits_out = a.visible_mask ? a.visible_mask + static_cast<uint64_t>(r) * a.mask_stride : nullptr;
+    // mask word w when the only touched block (if any) is the trailing one
+    const auto tail_word = [&](uint32_t w) -> uint32_t {
+        return (tail != 0 && w == blocks / 32) ? 1u << (blocks % 32) : 0u;
+    };
     if (blocks > k && k == 0) {                                   // selective, no blocks kept: the tail only
         for (uint32_t e = tid; e < tail; e += kSelThreads) out[e] = blocks * a.ratio + e;
+        if (bits_out)
+            for (uint32_t w = tid; w < a.mask_stride; w += kSelThreads) bits_out[w] = tail_word(w);
         if (tid == 0) a.num_visible[r] = tail;
         return;
     }
     if (blocks <= k) {                                            // every position
         const uint32_t n = t_len < a.vis_stride ? t_len : a.vis_stride;
         for (uint32_t p = tid; p < n; p += kSelThreads) out[p] = p;
+        if (bits_out) {
+            const uint32_t nblk = n / a.ratio + (n % a.ratio != 0);   // blocks 0 .. nblk-1 touched
+            for (uint32_t w = tid; w < a.mask_stride; w += kSelThreads) {
+                const uint32_t lo = w * 32;
+                bits_out[w] = nblk >= lo + 32 ? ~0u : (nblk > lo ? (1u << (nblk - lo)) - 1u : 0u);
+            }
+        }
         if (tid == 0) a.num_visible[r] = n;
         return;
     }
@@ -136,8 +158,17 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(IndexSelectAr
         const uint32_t sel = (j < blocks && (key > T || (eq && eq_before < need))) ? 1u : 0u;
         const uint32_t slot = sel_run + block_excl_scan(sel, tmp, sel_tot);
         if (sel) chosen[slot] = j;
+        if (bits_out) {
+            const uint64_t bits = __ballot(sel || (j == blocks && tail != 0));
+            const uint32_t w = (j - lane) / 32 + lane;            // this wave's two words; lanes 0 and 1 write
+            if (lane < 2 && w < a.mask_stride) bits_out[w] = static_cast<uint32_t>(bits >> (32 * lane));
+        }
         eq_run += eq_tot;
         sel_run += sel_tot;
+    }
+    if (bits_out) {                                               // words past the last scan chunk
+        const uint32_t done = (blocks + kSelThreads - 1) / kSelThreads * (kSelThreads / 32);
+        for (uint32_t w = done + tid; w < a.mask_stride; w += kSelThreads) bits_out[w] = tail_word(w);
     }
     __syncthreads();
 

@@ -65,7 +65,8 @@ struct IndexSelectArgs {
     const uint32_t* row_lens;    // [num_rows] t_len
     uint32_t* visible_pos;       // row r's list at visible_pos[r*vis_stride]
     uint32_t* num_visible;       // [num_rows]
-    uint32_t score_stride, num_rows, ratio, k, vis_stride;
+    uint32_t* visible_mask;      // row r's block bits at visible_mask[r*mask_stride], or null
+    uint32_t score_stride, num_rows, ratio, k, vis_stride, mask_stride;
 };
 
 hipError_t launch_index_select(const IndexSelectArgs& a, hipStream_t stream);

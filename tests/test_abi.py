@@ -247,9 +247,11 @@ def test_norm_rope_cache_write_nulls_and_empty(lib):
 
 
 def test_index_select_validation(lib):
-    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 0, 2, FAKE, 128, FAKE, None) == 2          # ratio 0
-    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 64, 32, FAKE, 2111, FAKE, None) == 2       # (k+1)*ratio > vis_stride
-    assert lib.q8_index_select(FAKE, 16385, FAKE, 4, 64, 32, FAKE, 2112, FAKE, None) == 5    # too many blocks per row
-    assert lib.q8_index_select(None, 64, FAKE, 4, 64, 32, FAKE, 2112, FAKE, None) == 1
-    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 64, 32, FAKE, 2112, None, None) == 1
-    assert lib.q8_index_select(None, 64, None, 0, 64, 32, None, 2112, None, None) == 0       # no rows
+    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 0, 2, FAKE, 128, FAKE, None, 0, None) == 2          # ratio 0
+    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 64, 32, FAKE, 2111, FAKE, None, 0, None) == 2       # (k+1)*ratio > vis_stride
+    assert lib.q8_index_select(FAKE, 16385, FAKE, 4, 64, 32, FAKE, 2112, FAKE, None, 0, None) == 5    # too many blocks per row
+    assert lib.q8_index_select(None, 64, FAKE, 4, 64, 32, FAKE, 2112, FAKE, None, 0, None) == 1
+    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 64, 32, FAKE, 2112, None, None, 0, None) == 1
+    assert lib.q8_index_select(None, 64, None, 0, 64, 32, None, 2112, None, None, 0, None) == 0       # no rows
+    assert lib.q8_index_select(FAKE, 64, FAKE, 4, 64, 32, FAKE, 2112, FAKE, FAKE, 2, None) == 2   # 65 blocks need 3 words
+    assert lib.q8_index_select(FAKE, 63, FAKE, 0, 64, 32, FAKE, 2112, FAKE, FAKE, 2, None) == 0   # 64 blocks fit in 2

@@ -15,21 +15,30 @@ torch = pytest.importorskip("torch")
 SENTINEL = 0xDEADBEEF
 
 
-def run_select(oracle_mod, scores, lens, ratio, k, vis_stride):
+def run_select(oracle_mod, scores, lens, ratio, k, vis_stride, mask_stride=0):
+    """With mask_stride > 0 the block bitmask is requested too; every mask word
+    is written, so the sentinel must be gone from all of them."""
     from int8_paged_kv_amd import q8_index_select
     from gpu_util import f32_dev, u32_dev, u32_host
     R = lens.shape[0]
     vis_d = u32_dev(np.full((R, vis_stride), SENTINEL, np.uint32))
     nv_d = u32_dev(np.full(R, SENTINEL, np.uint32))
-    q8_index_select(f32_dev(scores), u32_dev(lens), ratio, k, vis_stride, visible_pos=vis_d, num_visible=nv_d)
+    mask_d = u32_dev(np.full((R, mask_stride), SENTINEL, np.uint32)) if mask_stride else None
+    q8_index_select(f32_dev(scores), u32_dev(lens), ratio, k, vis_stride, visible_pos=vis_d, num_visible=nv_d,
+                    mask_stride=mask_stride, visible_mask=mask_d)
     torch.cuda.synchronize()
     vis, nv = u32_host(vis_d), u32_host(nv_d)
-    want_vis, want_nv = oracle_mod.index_select(scores, lens, ratio, k, vis_stride)
+    want = oracle_mod.index_select(scores, lens, ratio, k, vis_stride, mask_stride=mask_stride)
+    want_vis, want_nv = want[0], want[1]
     assert np.array_equal(nv, want_nv), "visible counts differ"
     for r in range(R):
         n = int(want_nv[r])
         assert np.array_equal(vis[r, :n], want_vis[r, :n]), "row %d: visible lists differ" % r
         assert np.all(vis[r, n:] == SENTINEL), "row %d: entries past the count were written" % r
+    if mask_stride:
+        mask = u32_host(mask_d)
+        bad = np.nonzero(np.any(mask != want[2], axis=1))[0]
+        assert bad.size == 0, "block bitmasks differ in rows %s" % bad[:8].tolist()
     return vis, nv
 
 
@@ -56,6 +65,22 @@ def test_matches_oracle(oracle_mod, ratio, k, max_blocks, kind):
     lens = g.integers(0, top + 1, R).astype(np.uint32)
     lens[:6] = [0, ratio - 1, k * ratio, k * ratio + ratio - 1, (k + 1) * ratio, top]   # edges of the dense case
     run_select(oracle_mod, scores, lens, ratio, k, k * ratio + ratio)
+    # the bitmask too, one spare word past the widest row
+    run_select(oracle_mod, scores, lens, ratio, k, k * ratio + ratio, (max_blocks + 1 + 31) // 32 + 1)
+
+
+@pytest.mark.parametrize("max_blocks", [255, 256, 257, 511, 512])
+def test_mask_at_chunk_edges(oracle_mod, max_blocks):
+    """Rows whose trailing block is the first block past a 256-block scan chunk,
+    the last one inside it, or a word edge; every row selective."""
+    g = np.random.default_rng(max_blocks)
+    ratio, k = 4, 9
+    R = 16
+    scores = g.standard_normal((R, max_blocks)).astype(np.float32)
+    lens = np.array([b * ratio + t for b in (max_blocks, max_blocks - 1, 256, 255, 224, 32, 31, 40)
+                     for t in (0, 3) if b <= max_blocks], np.uint32)[:R]
+    lens = np.resize(lens, R).astype(np.uint32)
+    run_select(oracle_mod, scores, lens, ratio, k, k * ratio + ratio, (max_blocks + 1 + 31) // 32)
 
 
 def test_rebuilds_selected_workload_and_decodes(oracle_mod):
