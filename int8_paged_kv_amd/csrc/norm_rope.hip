@@ -19,16 +19,17 @@
 // two binary32 products and one binary32 sum or difference, never fused.
 //
 // MI355X mapping: a vector is held by head_size/4 lanes, four elements each,
-// as in the cache writer.  The sum of squares is a binary64 xor-shuffle
-// reduction over those lanes; the partner of rotated element i (i + rot/2, or
-// i - rot/2) sits in lane w +- rot/8 (rot a multiple of 8), fetched with one
-// shuffle.  The fused writer runs one wavefront per (token, kv head), or in
+// as in the cache writer.  The sum of squares is a binary64 tree reduction
+// over those lanes (DPP and swizzle steps); the partner of rotated element i
+// (i + rot/2, or i - rot/2) sits in lane w +- rot/8 (rot a multiple of 8),
+// fetched with one permute.  The fused writer runs one wavefront per (token, kv head), or in
 // large writes per group of consecutive ones whose loads are all in flight
 // together: for head sizes up to 128 lanes 0-31 take K through the norm and
 // the rotation and lanes 32-63 pack V beside them, otherwise the wave does K
 // and then V.
 #include "q8kv_internal.h"
 #include "q8_pack.h"
+#include "wave_ops.h"
 
 namespace q8kv {
 namespace {
@@ -57,18 +58,31 @@ __device__ __forceinline__ void load_cs4(const float* cs, uint32_t w, uint32_t r
     s = load4(cs + rot / 2 + i0, pvec4);
 }
 
+// The mean of a sum over head_size elements, as the binary64 quotient.  A
+// power-of-two head size divides exactly by multiplying with its reciprocal
+// (2^-k, built from its exponent bits), which spares the division sequence.
+struct RowMean {
+    uint32_t head_size;
+    bool pow2;
+    double inv;
+    __device__ __forceinline__ explicit RowMean(uint32_t hs) : head_size(hs), pow2((hs & (hs - 1)) == 0), inv(0.0) {
+        if (pow2) inv = __longlong_as_double(static_cast<long long>(1023 - __builtin_ctz(hs)) << 52);
+    }
+    __device__ __forceinline__ double operator()(double ss) const {
+        return pow2 ? ss * inv : ss / static_cast<double>(head_size);
+    }
+};
+
 // Lane w of a group of WIDTH lanes holds elements 4w .. 4w+3 of x (zeros for
 // w >= head_size/4); returns the same elements of the normalized and rotated
 // vector.
 template <int WIDTH>
-__device__ __forceinline__ float4 norm_rope4(float4 x, uint32_t w, uint32_t head_size, const RopeLane& op,
+__device__ __forceinline__ float4 norm_rope4(float4 x, uint32_t w, const RowMean& mean, const RopeLane& op,
                                              uint32_t rot, float eps) {
 #pragma clang fp contract(off)
-    double ss = static_cast<double>(x.x) * x.x + static_cast<double>(x.y) * x.y +
-                static_cast<double>(x.z) * x.z + static_cast<double>(x.w) * x.w;
-#pragma unroll
-    for (int off = WIDTH / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, WIDTH);
-    const float r = static_cast<float>(1.0 / sqrt(ss / static_cast<double>(head_size) + static_cast<double>(eps)));
+    const double ss = group_sum<WIDTH>(static_cast<double>(x.x) * x.x + static_cast<double>(x.y) * x.y +
+                                       static_cast<double>(x.z) * x.z + static_cast<double>(x.w) * x.w);
+    const float r = static_cast<float>(1.0 / sqrt(mean(ss) + static_cast<double>(eps)));
     float4 n;
     n.x = (x.x * r) * op.wt.x;
     n.y = (x.y * r) * op.wt.y;
@@ -78,11 +92,13 @@ __device__ __forceinline__ float4 norm_rope4(float4 x, uint32_t w, uint32_t head
     const uint32_t h8 = rot / 8;
     const bool first = w < h8, second = !first && w < 2 * h8;
     const uint32_t src = first ? w + h8 : (second ? w - h8 : w);
+    // byte address of the partner lane in the wave (the same for every vector of the wave)
+    const int addr = static_cast<int>(((__lane_id() & ~static_cast<uint32_t>(WIDTH - 1)) + src) << 2);
     float4 p;
-    p.x = __shfl(n.x, static_cast<int>(src), WIDTH);
-    p.y = __shfl(n.y, static_cast<int>(src), WIDTH);
-    p.z = __shfl(n.z, static_cast<int>(src), WIDTH);
-    p.w = __shfl(n.w, static_cast<int>(src), WIDTH);
+    p.x = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(n.x)));
+    p.y = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(n.y)));
+    p.z = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(n.z)));
+    p.w = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(n.w)));
     if (!first && !second) return n;
     const float c[4] = {op.c.x, op.c.y, op.c.z, op.c.w};
     const float s[4] = {op.s.x, op.s.y, op.s.z, op.s.w};
@@ -139,7 +155,7 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a, bool vec
     op.wt = load_weight4(a.weight, w, hs4, a.params_vec4);
     const float* cs = live ? table_row(a.table, a.positions, t, a.rot, a.num_positions) : a.table;
     load_cs4(cs, w, a.rot, a.params_vec4, op.c, op.s);
-    const float4 y = norm_rope4<WIDTH>(x, w, a.head_size, op, a.rot, a.eps);
+    const float4 y = norm_rope4<WIDTH>(x, w, RowMean(a.head_size), op, a.rot, a.eps);
     if (live && w < hs4) {
         float* o = a.out + static_cast<uint64_t>(t) * a.out_stride + static_cast<uint64_t>(h) * a.head_size + 4 * w;
         if (vec4) *reinterpret_cast<float4*>(o) = y;
@@ -149,26 +165,35 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a, bool vec
 
 // Cache write with the norm + rotary step on K: one wave per NP consecutive
 // (token, kv head) pairs, every pair's rows and slot loaded before any is
-// processed (NP > 1 for large writes, to keep several rows in flight).
-template <bool HALF, int NP>
+// processed (NP > 1 for large writes, to keep several rows in flight).  With
+// SAME_T the NP pairs are heads of one token (NP divides num_kv_heads): one
+// slot, one position and one table row serve them all.
+template <bool HALF, int NP, bool SAME_T>
 __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCacheWriteArgs a, bool vec4) {
+    static_assert(SAME_T || NP <= 2, "without SAME_T a wave's pairs may span two tokens at most");
+    constexpr int NT = SAME_T ? 1 : NP;                  // tokens per wave
     const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave) * NP;
+    // Wave-uniform pair indices: the slot and position of a pair are then
+    // scalar loads, counted apart from the rows' vector loads, so the table
+    // rows can be requested while the rows are still in flight.
+    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + uniform(threadIdx.x / kWave)) * NP;
     const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
     if (first >= pairs) return;
+    // One division per wave; the wave's later pairs step through the heads.
+    const uint32_t t0 = static_cast<uint32_t>(first / a.num_kv_heads);
+    const uint32_t h0 = static_cast<uint32_t>(first - static_cast<uint64_t>(t0) * a.num_kv_heads);
     const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
     float4 xk[NP], xv[NP];
-    uint32_t slot[NP], head[NP], posn[NP];
+    uint32_t head[NP], slot[NT], posn[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) slot[i] = kPadSlot, posn[i] = 0;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         xk[i] = xv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        slot[i] = kPadSlot;
-        head[i] = posn[i] = 0;
-        const uint64_t pair = first + i;
-        if (pair >= pairs) continue;                     // wave-uniform
-        const uint32_t t = static_cast<uint32_t>(pair / a.num_kv_heads);
-        const uint32_t h = static_cast<uint32_t>(pair % a.num_kv_heads);
+        uint32_t t = t0, h = h0 + i;
+        if (!SAME_T && h >= a.num_kv_heads) h -= a.num_kv_heads, ++t;
         head[i] = h;
+        if (first + i >= pairs) continue;                // wave-uniform
         // A pad token's rows and position may be read (loaded with the slot),
         // but nothing is written for it.
         const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
@@ -180,16 +205,18 @@ __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCach
             xk[i] = load4(ksrc + 4 * lane, vec4);
             xv[i] = load4(vsrc + 4 * lane, vec4);
         }
-        slot[i] = a.slot_mapping[t];
-        if (a.rot > 0) posn[i] = a.positions[t];
+        if (!SAME_T || i == 0) {
+            slot[SAME_T ? 0 : i] = a.slot_mapping[t];
+            if (a.rot > 0) posn[SAME_T ? 0 : i] = a.positions[t];
+        }
     }
-    // The table rows of every pair's position, loaded together (one round
-    // trip after the rows), and the norm weight once per wave.
+    // The table rows of the positions, requested as soon as the positions are
+    // in (before the rows), and the norm weight once per wave.
     const uint32_t w = HALF ? (lane & 31) : lane;
-    RopeLane op[NP];
+    RopeLane op[NT];
     const float4 wt = load_weight4(a.weight, w, hs4, a.params_vec4);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
+    for (int i = 0; i < NT; ++i) {
         op[i].wt = wt;
         op[i].c = op[i].s = make_float4(0.f, 0.f, 0.f, 0.f);
         if (slot[i] == kPadSlot || a.rot == 0) continue;
@@ -197,18 +224,26 @@ __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCach
         const uint32_t p = posn[i] < a.num_positions ? posn[i] : a.num_positions - 1;
         load_cs4(a.table + static_cast<uint64_t>(p) * a.rot, w, a.rot, a.params_vec4, op[i].c, op[i].s);
     }
+    // Cache row of each token: block and offset in it (slots are 32-bit).
+    uint32_t blk[NT], off[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        blk[i] = slot[i] / a.block_size;
+        off[i] = slot[i] - blk[i] * a.block_size;
+    }
+    const RowMean mean(a.head_size);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-        if (slot[i] == kPadSlot) continue;
-        const uint64_t block = slot[i] / a.block_size, off = slot[i] % a.block_size;
-        if (block >= a.num_blocks) continue;             // out of contract; skipped rather than written out of bounds
-        const uint64_t dst = ((block * a.num_kv_heads + head[i]) * a.block_size + off) * wpt;
+        const int ti = SAME_T ? 0 : i;
+        if (first + i >= pairs || slot[ti] == kPadSlot) continue;
+        if (blk[ti] >= a.num_blocks) continue;           // out of contract; skipped rather than written out of bounds
+        const uint64_t dst = ((static_cast<uint64_t>(blk[ti]) * a.num_kv_heads + head[i]) * a.block_size + off[ti]) * wpt;
         if (HALF) {
             const bool is_v = lane >= 32;
-            const float4 y = norm_rope4<32>(xk[i], w, a.head_size, op[i], a.rot, a.eps);
+            const float4 y = norm_rope4<32>(xk[i], w, mean, op[ti], a.rot, a.eps);
             pack_vector<32>(is_v ? xk[i] : y, (is_v ? a.value_cache : a.key_cache) + dst, hs4, w);
         } else {
-            const float4 y = norm_rope4<64>(xk[i], lane, a.head_size, op[i], a.rot, a.eps);
+            const float4 y = norm_rope4<64>(xk[i], lane, mean, op[ti], a.rot, a.eps);
             pack_vector<64>(y, a.key_cache + dst, hs4, lane);
             pack_vector<64>(xv[i], a.value_cache + dst, hs4, lane);
         }
@@ -244,16 +279,23 @@ hipError_t launch_norm_rope_cache_write(const NormRopeCacheWriteArgs& a, hipStre
     const bool vec4 = reinterpret_cast<uintptr_t>(a.key) % 16 == 0 && reinterpret_cast<uintptr_t>(a.value) % 16 == 0 &&
                       a.key_stride % 4 == 0 && a.value_stride % 4 == 0;
     const bool half = a.head_size / 4 <= 32;
-    if (pairs >= kWriteBatchMinPairs) {
-        // Two pairs per wave: the step's registers for four would cut occupancy from 8 waves per SIMD to 5.
-        constexpr int NP = 2;
-        const dim3 grid(static_cast<uint32_t>((pairs + 4 * NP - 1) / (4 * NP)));
-        if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, NP>), grid, dim3(256), 0, stream, a, vec4);
-        else hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, NP>), grid, dim3(256), 0, stream, a, vec4);
+    const uint32_t grid_1 = static_cast<uint32_t>((pairs + 3) / 4);      // one pair per wave
+    if (pairs >= kWriteBatchMinPairs && half && a.num_kv_heads % 4 == 0) {
+        // Four heads of one token per wave, sharing the slot, position and table row.
+        const dim3 grid(static_cast<uint32_t>((pairs + 15) / 16));
+        hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, 4, true>), grid, dim3(256), 0, stream, a, vec4);
+    } else if (pairs >= kWriteBatchMinPairs) {
+        // Two pairs per wave: for head sizes above 128 the registers for four
+        // would cut occupancy below 8 waves per SIMD.
+        const dim3 grid(static_cast<uint32_t>((pairs + 7) / 8));
+        const bool same_t = a.num_kv_heads % 2 == 0;
+        if (half && same_t) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, 2, true>), grid, dim3(256), 0, stream, a, vec4);
+        else if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, 2, false>), grid, dim3(256), 0, stream, a, vec4);
+        else if (same_t) hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, 2, true>), grid, dim3(256), 0, stream, a, vec4);
+        else hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, 2, false>), grid, dim3(256), 0, stream, a, vec4);
     } else {
-        const dim3 grid(static_cast<uint32_t>((pairs + 3) / 4));
-        if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, 1>), grid, dim3(256), 0, stream, a, vec4);
-        else hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, 1>), grid, dim3(256), 0, stream, a, vec4);
+        if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, 1, true>), dim3(grid_1), dim3(256), 0, stream, a, vec4);
+        else hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, 1, true>), dim3(grid_1), dim3(256), 0, stream, a, vec4);
     }
     return hipGetLastError();
 }

@@ -10,6 +10,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "lane_reduce.h"
 
 namespace q8kv {
 
@@ -22,12 +23,10 @@ __device__ __forceinline__ uint32_t pack_code(float x, float inv, uint32_t lane_
 // Lane w of a group of WIDTH lanes holds elements 4w .. 4w+3 of the vector in
 // x (zeros for w >= head_size/4).  Returns the lane's code word and sets
 // scale_bits, the bits of the vector's scale word (the same in every lane).
+// Every lane of the wave must be active.
 template <int WIDTH>
 __device__ __forceinline__ uint32_t quantize_word(float4 x, uint32_t& scale_bits) {
-    float amax = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
-#pragma unroll
-    for (int off = WIDTH / 2; off > 0; off >>= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, off, WIDTH));
+    const float amax = group_max<WIDTH>(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
     const float inv = amax > 0.0f ? __fdiv_rn(127.0f, amax) : 0.0f;
     scale_bits = __float_as_uint(amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 1.0f);
     return pack_code(x.x, inv, 0) | pack_code(x.y, inv, 1) | pack_code(x.z, inv, 2) | pack_code(x.w, inv, 3);

@@ -47,7 +47,7 @@ struct NormRopeCacheWriteArgs {
     uint32_t* key_cache;
     uint32_t* value_cache;
     const uint32_t* slot_mapping;
-    const uint32_t* positions;   // [num_tokens]; not read for pad tokens
+    const uint32_t* positions;   // [num_tokens]; may be read for pad tokens, never used for them
     const float* weight;         // [head_size] K norm weight
     const float* table;          // [num_positions, rot]
     uint32_t key_stride, value_stride;

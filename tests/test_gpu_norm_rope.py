@@ -230,10 +230,16 @@ def test_norm_rope_then_decode_matches_oracle(oracle_mod):
     assert_close(out.cpu().numpy(), ref, "decode after norm + rotary")
 
 
-@pytest.mark.parametrize("T,hkv,hs,rot", [(4103, 8, 128, 64), (2053, 16, 256, 128)])
+@pytest.mark.parametrize("T,hkv,hs,rot", [
+    (4103, 8, 128, 64),      # four heads of a token per wave
+    (2053, 16, 256, 128),    # two heads of a token per wave, head size above 128
+    (16411, 2, 64, 32),      # two heads of a token per wave
+    (10939, 3, 128, 64),     # pairs straddle tokens; the last wave holds one pair
+    (10923, 3, 256, 128),    # the same above head size 128
+])
 def test_norm_rope_cache_write_large_ragged(oracle_mod, T, hkv, hs, rot):
     """>= 32768 pairs (several consecutive pairs per wave), a partly filled last
-    wave, pads among them."""
+    wave or workgroup, pads among them."""
     from int8_paged_kv_amd import q8_norm_rope_cache_write
     f32_dev, u32_dev, u32_host = dev()
     g = np.random.default_rng(T)
