@@ -13,6 +13,7 @@
 // IEEE multiplies, v_rndne, clamp and a byte pack.
 #include "q8kv_internal.h"
 #include "q8_pack.h"
+#include "wave_ops.h"
 
 namespace q8kv {
 namespace {
@@ -28,7 +29,9 @@ __device__ __forceinline__ float4 load4(const float* p, bool vec4) {
 template <bool HALF, int NP>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool vec4) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave) * NP;
+    // Wave-uniform pair indices (slots become scalar loads); one division per
+    // wave, the later pairs step through the heads.
+    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + uniform(threadIdx.x / kWave)) * NP;
     const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
     if (first >= pairs) return;
     const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
@@ -36,16 +39,15 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool
     // trip); a pad token's rows may thus be read, but nothing is written for it.
     float4 x0[NP], x1[NP];
     uint32_t slot[NP], head[NP];
+    uint32_t t = static_cast<uint32_t>(first / a.num_kv_heads);
+    uint32_t h = static_cast<uint32_t>(first - static_cast<uint64_t>(t) * a.num_kv_heads);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         x0[i] = x1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         slot[i] = kPadSlot;
-        head[i] = 0;
-        const uint64_t pair = first + i;
-        if (pair >= pairs) continue;                 // wave-uniform
-        const uint32_t t = static_cast<uint32_t>(pair / a.num_kv_heads);
-        const uint32_t h = static_cast<uint32_t>(pair % a.num_kv_heads);
+        if (i > 0 && ++h == a.num_kv_heads) h = 0, ++t;
         head[i] = h;
+        if (first + i >= pairs) continue;            // wave-uniform
         const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
         const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
         if (HALF) {
@@ -60,9 +62,9 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         if (slot[i] == kPadSlot) continue;
-        const uint64_t block = slot[i] / a.block_size, off = slot[i] % a.block_size;
+        const uint32_t block = slot[i] / a.block_size, off = slot[i] - block * a.block_size;
         if (block >= a.num_blocks) continue;         // out of contract; skipped rather than written out of bounds
-        const uint64_t dst = ((block * a.num_kv_heads + head[i]) * a.block_size + off) * wpt;
+        const uint64_t dst = ((static_cast<uint64_t>(block) * a.num_kv_heads + head[i]) * a.block_size + off) * wpt;
         if (HALF) {
             pack_vector<32>(x0[i], (lane >= 32 ? a.value_cache : a.key_cache) + dst, hs4, lane & 31);
         } else {

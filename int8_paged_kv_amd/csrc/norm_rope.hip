@@ -172,6 +172,10 @@ template <bool HALF, int NP, bool SAME_T>
 __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCacheWriteArgs a, bool vec4) {
     static_assert(SAME_T || NP <= 2, "without SAME_T a wave's pairs may span two tokens at most");
     constexpr int NT = SAME_T ? 1 : NP;                  // tokens per wave
+    // Two heads of one token side by side: lanes 0-31 hold head 2j's K (then
+    // V) and lanes 32-63 head 2j+1's, so the norm runs once per two K vectors
+    // instead of once per K vector beside an idle V half.
+    constexpr bool PAIRED = HALF && SAME_T && NP % 2 == 0;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     // Wave-uniform pair indices: the slot and position of a pair are then
     // scalar loads, counted apart from the rows' vector loads, so the table
@@ -198,7 +202,9 @@ __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCach
         // but nothing is written for it.
         const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
         const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
-        if (HALF) {
+        if (PAIRED) {
+            // rows loaded below, two heads per instruction
+        } else if (HALF) {
             const uint32_t w = lane & 31;
             if (w < hs4) xk[i] = load4((lane >= 32 ? vsrc : ksrc) + 4 * w, vec4);
         } else if (lane < hs4) {
@@ -208,6 +214,15 @@ __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCach
         if (!SAME_T || i == 0) {
             slot[SAME_T ? 0 : i] = a.slot_mapping[t];
             if (a.rot > 0) posn[SAME_T ? 0 : i] = a.positions[t];
+        }
+    }
+    if (PAIRED && (lane & 31) < hs4) {
+        // register set j: head h0+2j in lanes 0-31, h0+2j+1 in lanes 32-63; K in xk, V in xv
+#pragma unroll
+        for (int j = 0; j < NP / 2; ++j) {
+            const uint64_t hj = h0 + 2 * j + (lane >> 5);
+            xk[j] = load4(a.key + static_cast<uint64_t>(t0) * a.key_stride + hj * a.head_size + 4 * (lane & 31), vec4);
+            xv[j] = load4(a.value + static_cast<uint64_t>(t0) * a.value_stride + hj * a.head_size + 4 * (lane & 31), vec4);
         }
     }
     // The table rows of the positions, requested as soon as the positions are
@@ -232,6 +247,19 @@ __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCach
         off[i] = slot[i] - blk[i] * a.block_size;
     }
     const RowMean mean(a.head_size);
+    if (PAIRED) {
+        // every pair of the wave is in range (pairs is a multiple of NP) and shares slot[0]
+        if (slot[0] == kPadSlot || blk[0] >= a.num_blocks) return;
+        const uint32_t hv = head[0] + (lane >> 5);     // this half's head in pair group 0
+#pragma unroll
+        for (int j = 0; j < NP / 2; ++j) {
+            const uint64_t dst = ((static_cast<uint64_t>(blk[0]) * a.num_kv_heads + hv + 2 * j) * a.block_size + off[0]) * wpt;
+            const float4 y = norm_rope4<32>(xk[j], w, mean, op[0], a.rot, a.eps);
+            pack_vector<32>(y, a.key_cache + dst, hs4, w);
+            pack_vector<32>(xv[j], a.value_cache + dst, hs4, w);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         const int ti = SAME_T ? 0 : i;
