@@ -74,7 +74,8 @@ def copy_calibration(mib: int) -> None:
 # The files the decode-step kernel (decode_split_kernel) and its launch are
 # built from; the committed HBM-traffic figures hold while these are unchanged.
 DECODE_SOURCES = ("decode_kernel.h", "decode_split.h", "decode.hip", "decode_hs16.hip", "decode_hs32.hip",
-                  "decode_hs48.hip", "decode_hs64.hip", "q8_pack.h", "wave_ops.h", "q8kv_internal.h")
+                  "decode_hs48.hip", "decode_hs64.hip", "q8_pack.h", "lane_reduce.h", "wave_ops.h",
+                  "q8kv_internal.h")
 
 
 def kernel_sources_digest() -> str:
