@@ -9,7 +9,7 @@
 // index, their positions in ascending order, then the trailing incomplete
 // block's positions; with blocks <= kblk that is every position.
 //
-// MI355X mapping: one 256-thread workgroup per row.  The row's scores go to
+// MI355X mapping: one 1024-thread workgroup per row.  The row's scores go to
 // LDS as order-preserving 32-bit keys (signed zeros merged).  A radix select
 // over 4 digits of 8 bits (an LDS histogram per digit, its bins suffix-summed
 // by one wave) finds the kblk-th largest key T and how many of the blocks
@@ -20,7 +20,7 @@
 // The optional block bitmask (bit j: the list holds a position of block j)
 // comes from the same pass: in the selective case each wave's ballot over its
 // 64 blocks of a scan chunk is two mask words (chunks start at multiples of
-// 256 blocks, so words never straddle waves), the trailing block's bit joins
+// 1024 blocks, so words never straddle waves), the trailing block's bit joins
 // the ballot of the lane that holds its index, and words past the last chunk
 // are written by a final sweep; the dense and tail-only cases have closed
 // forms per word.
@@ -30,7 +30,7 @@
 namespace q8kv {
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;      // a row of up to 1024 blocks in one pass
 constexpr int kSelWaves = kSelThreads / kWave;
 
 // Larger key <=> larger score; -0 and +0 map to the same key.
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(IndexSelectAr
     __shared__ uint32_t pick[2];          // digit chosen in this pass, keys still needed after it
     // Indices of the selected blocks, in ascending order.  They share the key
     // array: slot s of block j satisfies s <= j, every key of the current
-    // 256-block chunk is read before the chunk's scans, and later chunks'
+    // scan chunk is read before the chunk's scans, and later chunks'
     // keys lie above every slot written so far.
     uint32_t* const chosen = keys;
     const uint32_t tid = threadIdx.x, lane = tid % kWave;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(IndexSelectAr
     // ---- radix select: T = the k-th largest key, need = how many keys == T to take ----
     uint32_t prefix = 0, mask = 0, need = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;
+        if (tid < 256) hist[tid] = 0;
         __syncthreads();
         for (uint32_t j = tid; j < blocks; j += kSelThreads) {
             const uint32_t key = keys[j];

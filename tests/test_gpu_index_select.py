@@ -69,15 +69,15 @@ def test_matches_oracle(oracle_mod, ratio, k, max_blocks, kind):
     run_select(oracle_mod, scores, lens, ratio, k, k * ratio + ratio, (max_blocks + 1 + 31) // 32 + 1)
 
 
-@pytest.mark.parametrize("max_blocks", [255, 256, 257, 511, 512])
+@pytest.mark.parametrize("max_blocks", [255, 256, 257, 1023, 1024, 1025, 2049])
 def test_mask_at_chunk_edges(oracle_mod, max_blocks):
-    """Rows whose trailing block is the first block past a 256-block scan chunk,
-    the last one inside it, or a word edge; every row selective."""
+    """Rows whose trailing block is the first block past a scan chunk (1024
+    blocks), the last one inside it, or a word or wave edge; every row selective."""
     g = np.random.default_rng(max_blocks)
     ratio, k = 4, 9
-    R = 16
+    R = 20
     scores = g.standard_normal((R, max_blocks)).astype(np.float32)
-    lens = np.array([b * ratio + t for b in (max_blocks, max_blocks - 1, 256, 255, 224, 32, 31, 40)
+    lens = np.array([b * ratio + t for b in (max_blocks, max_blocks - 1, 2048, 1024, 1023, 256, 255, 224, 32, 31, 40)
                      for t in (0, 3) if b <= max_blocks], np.uint32)[:R]
     lens = np.resize(lens, R).astype(np.uint32)
     run_select(oracle_mod, scores, lens, ratio, k, k * ratio + ratio, (max_blocks + 1 + 31) // 32)
