@@ -320,8 +320,13 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     if (gw >= c.num_rg * c.waves_per_rg) return;
     const uint32_t rg = gw % c.num_rg;
     const uint32_t j = gw / c.num_rg;
-    const uint32_t kvh = rg % a.num_kv_heads;
-    const uint32_t grp = rg / a.num_kv_heads;
+    // The row groups of one kv head are adjacent: with several (multi-row
+    // decode, or more query heads than a group holds), their waves for the
+    // same range j share a workgroup, hence a CU and an L2, and read the same
+    // tiles at about the same time.
+    const uint32_t ngrp = c.num_rg / a.num_kv_heads;
+    const uint32_t kvh = rg / ngrp;
+    const uint32_t grp = rg % ngrp;
 
     // ---- this wave's chunk range [x0, x1) of the row group's chunk sequence ----
     // The waves split the row group's work into equal contiguous ranges of
