@@ -41,6 +41,8 @@ TRACE_ALL_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --st
                  "-- python3 /root/repo/bench.py --steps 20 --warmup 5 --no-cpu")
 L2_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum "
           "-d {d}/pmc_L2 -o bench -f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
+PMC_ALL_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {c} -d {d}/pmc_all_{c} -o bench "
+               "-f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu")
 COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} -d {d}/copy_{c} -o copy -f csv "
             "-- python3 /root/repo/bench.py --copy-calibration {mib}")
 
@@ -277,6 +279,67 @@ def main():
     ] + l2_key
     with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_traffic.txt"), "w") as f:
         f.write("\n".join(t) + "\n")
+
+    # ---- optional: HBM traffic of every kernel of a run with the reference legs ----
+    fa = os.path.join(d, "pmc_all_FETCH_SIZE", "bench_counter_collection.csv")
+    wa = os.path.join(d, "pmc_all_WRITE_SIZE", "bench_counter_collection.csv")
+    if os.path.exists(fa) and os.path.exists(wa):
+        jf = last_json(os.path.join(d, "pmc_all_FETCH_SIZE.log"))
+        if {jf["kernel_sources_sha256_16"], last_json(os.path.join(d, "pmc_all_WRITE_SIZE.log"))[
+                "kernel_sources_sha256_16"]} != {digest}:
+            raise SystemExit("all-legs counter runs were taken on different kernel sources")
+        cf, cw = counters(fa), counters(wa)
+        durs = {}
+        if os.path.exists(os.path.join(all_dir, "bench_kernel_trace.csv")):
+            acc = defaultdict(list)
+            with open(os.path.join(all_dir, "bench_kernel_trace.csv")) as f:
+                for r in csv.DictReader(f):
+                    grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                    acc[(r["Kernel_Name"], grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            durs = {k: statistics.median(v) for k, v in acc.items()}
+        out = [
+            "# HBM traffic of every kernel the bench runs (step, two-launch reference, 4-row decode, f32-cache",
+            "# step, norm + rotary step and 16384-token bulk writes, selected-token step), median per dispatch",
+            "# of each (kernel, grid), calibrated by the plain copy as in q8_paged_decode_llama_traffic.txt",
+            "# (FETCH_SIZE x %.4f, WRITE_SIZE x %.4f)" % (factor["FETCH_SIZE"], factor["WRITE_SIZE"]),
+            "#",
+            "# commands (from any directory on the GPU machine), one counter per run:",
+            "#   " + PMC_ALL_CMD.format(c="FETCH_SIZE", d=args.cmd_dir),
+            "#   " + PMC_ALL_CMD.format(c="WRITE_SIZE", d=args.cmd_dir),
+            "# durations: median of the same (kernel, grid) in llama_step_all_kernels_trace.txt's run",
+            "# summarised with: python3 bench_profile.py <that -d directory's parent>",
+            "#",
+            "# kernel_sources_sha256_16: %s" % digest,
+            "",
+            "%-52s %9s %5s %14s %13s %9s %9s" % ("kernel", "grid", "calls", "read_B", "written_B", "median_us",
+                                                 "HBM_GBps"),
+        ]
+        for key in sorted(cf, key=lambda k: -statistics.median(cf[k]) * len(cf[k])):
+            if key not in cw:
+                continue
+            rd = statistics.median(cf[key]) * 1024.0 * factor["FETCH_SIZE"]
+            wr = statistics.median(cw[key]) * 1024.0 * factor["WRITE_SIZE"]
+            if rd + wr < 1e6:
+                continue
+            us = durs.get(key)
+            nm = key[0].replace("void ", "").replace("q8kv::(anonymous namespace)::", "").split("(")[0]
+            out.append("%-52s %9d %5d %14.0f %13.0f %9s %9s" % (
+                nm[:52], key[1], len(cf[key]), rd, wr, "%.2f" % us if us else "-",
+                "%.0f" % ((rd + wr) / (us * 1e-6) / 1e9) if us else "-"))
+        mr, f32, nr, sel = (jf.get(k) or {} for k in ("multi_row_decode", "f32_cache_reference", "norm_rope_step",
+                                                        "selected_step"))
+        out += [
+            "",
+            "algorithmic bytes of the reference legs (bench.py line of the FETCH_SIZE run):",
+            "  step decode: %d (int8 KV of every attended row, K and V)" % eff,
+            "  4-row decode: the same prefixes, read once when the rows of a sequence share the reads: %d;"
+            " counted per row: %s" % (eff, mr.get("effective_kv_bytes")),
+            "  f32-cache decode: %s" % f32.get("f32_kv_bytes"),
+            "  bulk writes (16384 tokens): %s" % nr.get("bulk_algorithmic_bytes"),
+            "  selected-token decode: %s" % sel.get("effective_kv_bytes"),
+        ]
+        with open(os.path.join(ROOT, "profiles", "llama_step_all_kernels_traffic.txt"), "w") as f:
+            f.write("\n".join(out) + "\n")
     print("wrote profiles/q8_paged_decode_llama_kernel_trace.txt and profiles/q8_paged_decode_llama_traffic.txt")
 
 
