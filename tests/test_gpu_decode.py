@@ -35,7 +35,7 @@ def test_tiny_workload(oracle_mod):
     (2, 8, 8, 128, 16, [100, 33]),              # MHA (n_rep 1)
     (2, 4, 2, 128, 16, [300, 64]),              # n_rep 2
     (2, 6, 2, 128, 16, [129, 70]),              # n_rep 3
-    (2, 10, 2, 128, 16, [90, 200]),             # n_rep 5: two head groups of 4 + 1
+    (2, 10, 2, 128, 16, [90, 200]),             # n_rep 5: one group of 8, three slots unused
     (2, 16, 2, 128, 32, [333, 65]),             # n_rep 8
     (2, 32, 2, 64, 16, [150, 40]),              # n_rep 16: two groups of 8
     (2, 4, 1, 4, 16, [50, 3]),                  # head_size 4
