@@ -72,3 +72,27 @@ def test_rows_match_single_row_decodes(oracle_mod):
         single = q8_paged_decode(qd[b::nb].contiguous(), c.kc_d, c.vc_d, c.bt_d, u32_dev(lens_b), c.scale, 2, 16,
                                  max_context_len=700)
         assert_close(multi[b::nb], single.cpu().numpy(), "row %d" % b)
+
+
+def test_rows_full_size_llama(oracle_mod):
+    """The Llama-shaped batch with 4 rows per sequence in the launch
+    configuration the bench times (16 (row, head) pairs per kv head: two row
+    groups side by side): every row against the oracle over its prefix."""
+    from int8_paged_kv_amd import q8_paged_decode_rows, q8_paged_decode_workspace_bytes
+    from int8_paged_kv_amd import workloads as wl
+    from gpu_util import Filled, assert_close, f32_dev, nan_out
+    w = wl.get("llama")
+    f = Filled(w, oracle_mod)
+    nb = 4
+    S, H, Hkv, hs, mcl = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size, w.max_context_len
+    q = np.random.default_rng(11).standard_normal((S * nb, H, hs)).astype(np.float32)
+    ws = torch.zeros(max(1, q8_paged_decode_workspace_bytes(S, H * nb, Hkv, hs, w.block_size, mcl)),
+                     dtype=torch.uint8, device="cuda:0")
+    out = q8_paged_decode_rows(f32_dev(q), f.kc_d, f.vc_d, f.bt_d, f.cl_d, w.scale, Hkv, w.block_size, mcl, nb,
+                               out=nan_out(S * nb, H, hs), workspace=ws)
+    torch.cuda.synchronize()
+    rows_bt = np.repeat(w.block_tables, nb, axis=0)
+    rows_len = np.array([max(0, int(L) - nb + b + 1) for L in w.context_lens for b in range(nb)], dtype=np.uint32)
+    want = oracle_mod.paged_decode(q, f.kc_h, f.vc_h, rows_bt, rows_len, w.scale, Hkv, w.block_size,
+                                   max_context_len=mcl)
+    assert_close(out.cpu().numpy(), want, "4-row decode of the Llama-shaped batch")
