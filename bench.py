@@ -119,7 +119,8 @@ def main():
     from int8_paged_kv_amd import (q8_cache_write, q8_decode_step, q8_paged_decode, q8_paged_decode_rows,
                                    q8_paged_decode_workspace_bytes, q8_f32_cache_write, q8_f32_paged_decode,
                                    q8_f32_paged_decode_workspace_bytes, q8_rope_table, q8_norm_rope,
-                                   q8_norm_rope_cache_write, q8_index_select, load_library)
+                                   q8_norm_rope_cache_write, q8_norm_rope_qk_cache_write, q8_index_select,
+                                   load_library)
     from int8_paged_kv_amd import workloads as wl
 
     load_library()
@@ -319,6 +320,31 @@ def main():
         tq = np.array([e[0].elapsed_time(e[1]) for e in evn]) * 1e3
         tw = np.array([e[1].elapsed_time(e[2]) for e in evn]) * 1e3
         td = np.array([e[2].elapsed_time(e[3]) for e in evn]) * 1e3
+
+        # the same step with q rows and the K/V write in one launch (two launches in all)
+        def nr_step2(i, ev=None):
+            kc, vc = layers[i % len(layers)]
+            if ev is not None:
+                ev[0].record()
+            q8_norm_rope_qk_cache_write(q2, step_pos, qn, H, sk, sv, kc, vc, ss, step_pos, kn, table, rot, 1e-6,
+                                        Hkv, hs, w.block_size, q_out=qnr)
+            if ev is not None:
+                ev[1].record()
+            q8_paged_decode(qnr, kc, vc, bt, cl, w.scale, Hkv, w.block_size, max_context_len=mcl, out=outn,
+                            workspace=ws)
+            if ev is not None:
+                ev[2].record()
+
+        for i in range(5):
+            nr_step2(i)
+        torch.cuda.synchronize()
+        evn2 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nn_)]
+        for i in range(nn_):
+            nr_step2(i, evn2[i])
+        torch.cuda.synchronize()
+        tqk = np.array([e[0].elapsed_time(e[1]) for e in evn2]) * 1e3
+        t2 = np.array([e[0].elapsed_time(e[2]) for e in evn2]) * 1e3
+        t3 = np.array([e[0].elapsed_time(e[3]) for e in evn]) * 1e3
         # bulk: 16384 tokens at scattered slots of a separate cache, fused vs plain writer
         Tb = 16384
         nbb = Tb // w.block_size + 64
@@ -347,6 +373,9 @@ def main():
                     "q_norm_rope_us_mean": round(float(tq.mean()), 2),
                     "norm_rope_cache_write_us_mean": round(float(tw.mean()), 2),
                     "decode_us_mean": round(float(td.mean()), 2),
+                    "three_launch_step_us_mean": round(float(t3.mean()), 2),
+                    "qk_norm_rope_cache_write_us_mean": round(float(tqk.mean()), 2),
+                    "two_launch_step_us_mean": round(float(t2.mean()), 2),
                     "bulk_tokens": Tb,
                     "bulk_norm_rope_cache_write_us_mean": round(float(tbf.mean()), 2),
                     "bulk_plain_cache_write_us_mean": round(float(tbp.mean()), 2),
@@ -354,7 +383,8 @@ def main():
                     "bulk_norm_rope_GBps": round(Bb / (float(tbf.mean()) * 1e-6) / 1e9, 1),
                     "bulk_norm_rope_frac_hbm_peak": round(Bb / (float(tbf.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "note": "the step with q8_norm_rope on q rows and q8_norm_rope_cache_write for the new K/V "
-                            "(three launches), then a 16384-token bulk write; positions L-1 for the step"}
+                            "(three launches with the decode), the same with q8_norm_rope_qk_cache_write (two "
+                            "launches), then a 16384-token bulk write; positions L-1 for the step"}
         del kb_, vb_
 
     # ---- selected-token step: block scores -> visible lists -> visible-list decode ----

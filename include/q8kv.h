@@ -355,6 +355,33 @@ q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
                                    uint32_t block_size, uint32_t num_blocks, void* stream);
 
 /*
+ * q8_norm_rope_qk_cache_write -- q8_norm_rope on query rows and
+ * q8_norm_rope_cache_write on the new K/V rows of the same step, in one launch.
+ * The "attention.rs" page normalizes and rotates q and k together in one
+ * dispatch (its qk_norm_rope_b) ahead of the q8 append; here that dispatch
+ * also quantizes and packs K and V into the cache.  The result is exactly that
+ * of q8_norm_rope(q_out, q_out_stride, q, q_stride, q_head_stride, num_q_rows,
+ * num_heads, head_size, q_positions, q_weight, table, rot, num_positions, eps)
+ * followed by q8_norm_rope_cache_write(key, ..., k_weight, table, ...): the
+ * arguments mean the same as there, head_size, table, rot, num_positions and
+ * eps are shared, and q_weight / k_weight are the q and K norm weights.  q_out
+ * must not overlap key, value or the caches (q and q_out may be the same
+ * rows).  Writes of at least 32768 (token, kv head) pairs take a second launch
+ * (the bulk writer).  Errors: those of the two calls; either side may be empty
+ * (num_q_rows or num_heads 0, num_tokens 0).
+ */
+q8_status q8_norm_rope_qk_cache_write(float* q_out, uint32_t q_out_stride, const float* q, uint32_t q_stride,
+                                      uint32_t q_head_stride, uint32_t num_q_rows, uint32_t num_heads,
+                                      const uint32_t* q_positions, const float* q_weight,
+                                      const float* key, uint32_t key_stride, const float* value,
+                                      uint32_t value_stride, uint32_t* key_cache, uint32_t* value_cache,
+                                      const uint32_t* slot_mapping, const uint32_t* positions,
+                                      const float* k_weight, const float* table, uint32_t rot,
+                                      uint32_t num_positions, float eps, uint32_t num_tokens,
+                                      uint32_t num_kv_heads, uint32_t head_size, uint32_t block_size,
+                                      uint32_t num_blocks, void* stream);
+
+/*
  * q8_index_select -- block selection into a visible list.  The
  * "attention.rs" page's per-row decode gives row r t_len = row_lens[r]
  * positions and blocks = t_len / ratio complete blocks; with k = kblk

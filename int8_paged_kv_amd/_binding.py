@@ -66,6 +66,9 @@ def load_library() -> ctypes.CDLL:
         lib.q8_norm_rope.restype = ctypes.c_int
         lib.q8_norm_rope_cache_write.argtypes = [P, U, P, U, P, P, P, P, P, P, U, U, F, U, U, U, U, U, P]
         lib.q8_norm_rope_cache_write.restype = ctypes.c_int
+        lib.q8_norm_rope_qk_cache_write.argtypes = [P, U, P, U, U, U, U, P, P, P, U, P, U, P, P, P, P, P, P, U, U,
+                                                    F, U, U, U, U, U, P]
+        lib.q8_norm_rope_qk_cache_write.restype = ctypes.c_int
         lib.q8_index_select.argtypes = [P, U, P, U, U, U, P, U, P, P, U, P]
         lib.q8_index_select.restype = ctypes.c_int
         lib.q8_last_hip_error.argtypes = []
@@ -115,6 +118,8 @@ def _rows(x: torch.Tensor, name: str):
     """(pointer, row stride) of a [T, ...] f32 tensor whose rows are dense."""
     if x.dim() < 2 or (x.numel() and not x[0].is_contiguous()):
         raise ValueError("%s must be [T, num_kv_heads, head_size] with dense rows" % name)
+    if x.shape[0] == 0:       # no rows: torch's row stride is arbitrary then; report the dense one
+        return _dev(x, name, torch.float32), int(torch.Size(x.shape[1:]).numel())
     return _dev(x, name, torch.float32), x.stride(0)
 
 
@@ -391,6 +396,42 @@ def q8_norm_rope_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: 
                                       rot, num_positions, float(eps), slot_mapping.numel(), num_kv_heads,
                                       head_size, block_size, num_blocks, _stream(stream))
     _check(st, "q8_norm_rope_cache_write")
+
+
+def q8_norm_rope_qk_cache_write(q: torch.Tensor, q_positions: Optional[torch.Tensor], q_weight: torch.Tensor,
+                                num_heads: int, key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                                value_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                                positions: Optional[torch.Tensor], k_weight: torch.Tensor,
+                                table: Optional[torch.Tensor], rot: int, eps: float, num_kv_heads: int,
+                                head_size: int, block_size: int, num_blocks: Optional[int] = None,
+                                q_head_stride: Optional[int] = None, q_out: Optional[torch.Tensor] = None,
+                                stream=None) -> torch.Tensor:
+    """q8_norm_rope on q rows and q8_norm_rope_cache_write on the new K/V rows in one launch
+    (see include/q8kv.h).  Returns q_out [T_q, num_heads, head_size]."""
+    lib = load_library()
+    Tq = q.shape[0]
+    qp, qs = _rows(q, "q")
+    hst = head_size if q_head_stride is None else q_head_stride
+    if q_out is None:
+        q_out = torch.empty((Tq, num_heads, head_size), dtype=torch.float32, device=q.device)
+    if tuple(q_out.shape) != (Tq, num_heads, head_size) or not q_out.is_contiguous():
+        raise ValueError("q_out must be a dense [T, num_heads, head_size] tensor")
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    wpt = head_size // 4 + 1
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * wpt)
+    num_positions = table.shape[0] if (table is not None and rot) else 0
+    tab = _dev(table, "table", torch.float32) if (table is not None and rot) else None
+    st = lib.q8_norm_rope_qk_cache_write(
+        _dev(q_out, "q_out", torch.float32), num_heads * head_size, qp, qs, hst, Tq, num_heads,
+        _u32(q_positions, "q_positions") if q_positions is not None else None, _dev(q_weight, "q_weight", torch.float32),
+        kp, ks, vp, vs, _u32(key_cache, "key_cache"), _u32(value_cache, "value_cache"),
+        _u32(slot_mapping, "slot_mapping"), _u32(positions, "positions") if positions is not None else None,
+        _dev(k_weight, "k_weight", torch.float32), tab, rot, num_positions, float(eps), slot_mapping.numel(),
+        num_kv_heads, head_size, block_size, num_blocks, _stream(stream))
+    _check(st, "q8_norm_rope_qk_cache_write")
+    return q_out
 
 
 def q8_index_select(scores: torch.Tensor, row_lens: torch.Tensor, ratio: int, k: int, vis_stride: int,

@@ -312,10 +312,16 @@ bool rope_shape_ok(uint32_t head_size, uint32_t rot, uint32_t num_positions, flo
 }
 }  // namespace
 
-q8_status q8_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t x_stride,
-                       uint32_t head_stride, uint32_t num_rows, uint32_t num_heads, uint32_t head_size,
-                       const uint32_t* positions, const float* weight, const float* table,
-                       uint32_t rot, uint32_t num_positions, float eps, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and argument block of q8_norm_rope; *empty when nothing is to be done.
+q8_status norm_rope_args(q8kv::NormRopeArgs& a, bool* empty, float* out, uint32_t out_stride, const float* x,
+                         uint32_t x_stride, uint32_t head_stride, uint32_t num_rows, uint32_t num_heads,
+                         uint32_t head_size, const uint32_t* positions, const float* weight, const float* table,
+                         uint32_t rot, uint32_t num_positions, float eps) {
+    *empty = true;
     if (!rope_shape_ok(head_size, rot, num_positions, eps) || head_stride < head_size) return Q8_ERR_SHAPE;
     if (num_heads > 0) {
         const uint64_t span = static_cast<uint64_t>(num_heads - 1) * head_stride + head_size;
@@ -324,7 +330,6 @@ q8_status q8_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t
     if (num_rows == 0 || num_heads == 0) return Q8_OK;
     if (!out || !x || !weight || (rot > 0 && (!table || !positions))) return Q8_ERR_NULL;
     if (static_cast<uint64_t>(num_rows) * num_heads > 0xFFFFFFFFull * 4) return Q8_ERR_UNSUPPORTED;
-    q8kv::NormRopeArgs a{};
     a.out = out;
     a.x = x;
     a.positions = positions;
@@ -340,18 +345,18 @@ q8_status q8_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t
     a.num_positions = num_positions;
     a.eps = eps;
     a.params_vec4 = reinterpret_cast<uintptr_t>(weight) % 16 == 0 && reinterpret_cast<uintptr_t>(table) % 16 == 0;
-    const hipError_t e = q8kv::launch_norm_rope(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? Q8_OK : hip_fail(e);
+    *empty = false;
+    return Q8_OK;
 }
 
-q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
-                                   const float* value, uint32_t value_stride,
-                                   uint32_t* key_cache, uint32_t* value_cache,
-                                   const uint32_t* slot_mapping, const uint32_t* positions,
-                                   const float* weight, const float* table, uint32_t rot,
-                                   uint32_t num_positions, float eps, uint32_t num_tokens,
-                                   uint32_t num_kv_heads, uint32_t head_size,
-                                   uint32_t block_size, uint32_t num_blocks, void* stream) {
+// Validation and argument block of q8_norm_rope_cache_write.
+q8_status norm_rope_write_args(q8kv::NormRopeCacheWriteArgs& a, bool* empty, const float* key, uint32_t key_stride,
+                               const float* value, uint32_t value_stride, uint32_t* key_cache,
+                               uint32_t* value_cache, const uint32_t* slot_mapping, const uint32_t* positions,
+                               const float* weight, const float* table, uint32_t rot, uint32_t num_positions,
+                               float eps, uint32_t num_tokens, uint32_t num_kv_heads, uint32_t head_size,
+                               uint32_t block_size, uint32_t num_blocks) {
+    *empty = true;
     if (!rope_shape_ok(head_size, rot, num_positions, eps) || block_size == 0 || num_kv_heads == 0)
         return Q8_ERR_SHAPE;
     const uint64_t row = static_cast<uint64_t>(num_kv_heads) * head_size;
@@ -362,7 +367,6 @@ q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
         return Q8_ERR_NULL;
     if (num_blocks == 0) return Q8_ERR_SHAPE;
     if (static_cast<uint64_t>(num_tokens) * num_kv_heads > 0xFFFFFFFFull * 4) return Q8_ERR_UNSUPPORTED;
-    q8kv::NormRopeCacheWriteArgs a{};
     a.key = key;
     a.value = value;
     a.key_cache = key_cache;
@@ -382,7 +386,66 @@ q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
     a.num_positions = num_positions;
     a.eps = eps;
     a.params_vec4 = reinterpret_cast<uintptr_t>(weight) % 16 == 0 && reinterpret_cast<uintptr_t>(table) % 16 == 0;
+    *empty = false;
+    return Q8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+q8_status q8_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t x_stride,
+                       uint32_t head_stride, uint32_t num_rows, uint32_t num_heads, uint32_t head_size,
+                       const uint32_t* positions, const float* weight, const float* table,
+                       uint32_t rot, uint32_t num_positions, float eps, void* stream) {
+    q8kv::NormRopeArgs a{};
+    bool empty;
+    const q8_status st = norm_rope_args(a, &empty, out, out_stride, x, x_stride, head_stride, num_rows, num_heads,
+                                        head_size, positions, weight, table, rot, num_positions, eps);
+    if (st != Q8_OK || empty) return st;
+    const hipError_t e = q8kv::launch_norm_rope(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
+                                   const float* value, uint32_t value_stride,
+                                   uint32_t* key_cache, uint32_t* value_cache,
+                                   const uint32_t* slot_mapping, const uint32_t* positions,
+                                   const float* weight, const float* table, uint32_t rot,
+                                   uint32_t num_positions, float eps, uint32_t num_tokens,
+                                   uint32_t num_kv_heads, uint32_t head_size,
+                                   uint32_t block_size, uint32_t num_blocks, void* stream) {
+    q8kv::NormRopeCacheWriteArgs a{};
+    bool empty;
+    const q8_status st = norm_rope_write_args(a, &empty, key, key_stride, value, value_stride, key_cache, value_cache,
+                                              slot_mapping, positions, weight, table, rot, num_positions, eps,
+                                              num_tokens, num_kv_heads, head_size, block_size, num_blocks);
+    if (st != Q8_OK || empty) return st;
     const hipError_t e = q8kv::launch_norm_rope_cache_write(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+q8_status q8_norm_rope_qk_cache_write(float* q_out, uint32_t q_out_stride, const float* q, uint32_t q_stride,
+                                      uint32_t q_head_stride, uint32_t num_q_rows, uint32_t num_heads,
+                                      const uint32_t* q_positions, const float* q_weight,
+                                      const float* key, uint32_t key_stride, const float* value,
+                                      uint32_t value_stride, uint32_t* key_cache, uint32_t* value_cache,
+                                      const uint32_t* slot_mapping, const uint32_t* positions,
+                                      const float* k_weight, const float* table, uint32_t rot,
+                                      uint32_t num_positions, float eps, uint32_t num_tokens,
+                                      uint32_t num_kv_heads, uint32_t head_size, uint32_t block_size,
+                                      uint32_t num_blocks, void* stream) {
+    q8kv::NormRopeArgs qa{};
+    q8kv::NormRopeCacheWriteArgs ka{};
+    bool q_empty, k_empty;
+    q8_status st = norm_rope_args(qa, &q_empty, q_out, q_out_stride, q, q_stride, q_head_stride, num_q_rows, num_heads,
+                                  head_size, q_positions, q_weight, table, rot, num_positions, eps);
+    if (st != Q8_OK) return st;
+    st = norm_rope_write_args(ka, &k_empty, key, key_stride, value, value_stride, key_cache, value_cache, slot_mapping,
+                              positions, k_weight, table, rot, num_positions, eps, num_tokens, num_kv_heads,
+                              head_size, block_size, num_blocks);
+    if (st != Q8_OK || (q_empty && k_empty)) return st;
+    const hipError_t e = q8kv::launch_norm_rope_qk_cache_write(qa, ka, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 

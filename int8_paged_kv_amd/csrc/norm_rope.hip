@@ -133,13 +133,14 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float* table, uint32_t 
     table[static_cast<uint64_t>(p) * rot + half + i] = static_cast<float>(sin(phi));
 }
 
-// Rows of f32 heads, WIDTH lanes per (row, head).
+// Rows of f32 heads, WIDTH lanes per (row, head); block: the workgroup's
+// index among those doing rows.
 template <int WIDTH>
-__global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a, bool vec4) {
+__device__ __forceinline__ void norm_rope_rows(const NormRopeArgs& a, bool vec4, uint32_t block) {
     constexpr int PER_WAVE = kWave / WIDTH;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t w = lane % WIDTH;
-    const uint64_t unit = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave) * PER_WAVE +
+    const uint64_t unit = (static_cast<uint64_t>(block) * (blockDim.x / kWave) + threadIdx.x / kWave) * PER_WAVE +
                           lane / WIDTH;
     const uint64_t units = static_cast<uint64_t>(a.num_rows) * a.num_heads;
     // Whole waves return together or not at all (the reductions shuffle across the group).
@@ -163,13 +164,18 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a, bool vec
     }
 }
 
+template <int WIDTH>
+__global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a, bool vec4) {
+    norm_rope_rows<WIDTH>(a, vec4, blockIdx.x);
+}
+
 // Cache write with the norm + rotary step on K: one wave per NP consecutive
 // (token, kv head) pairs, every pair's rows and slot loaded before any is
 // processed (NP > 1 for large writes, to keep several rows in flight).  With
 // SAME_T the NP pairs are heads of one token (NP divides num_kv_heads): one
 // slot, one position and one table row serve them all.
 template <bool HALF, int NP, bool SAME_T>
-__global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCacheWriteArgs a, bool vec4) {
+__device__ __forceinline__ void norm_rope_write_pairs(const NormRopeCacheWriteArgs& a, bool vec4, uint32_t block) {
     static_assert(SAME_T || NP <= 2, "without SAME_T a wave's pairs may span two tokens at most");
     constexpr int NT = SAME_T ? 1 : NP;                  // tokens per wave
     // Two heads of one token side by side: lanes 0-31 hold head 2j's K (then
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCach
     // Wave-uniform pair indices: the slot and position of a pair are then
     // scalar loads, counted apart from the rows' vector loads, so the table
     // rows can be requested while the rows are still in flight.
-    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + uniform(threadIdx.x / kWave)) * NP;
+    const uint64_t first = (static_cast<uint64_t>(block) * (blockDim.x / kWave) + uniform(threadIdx.x / kWave)) * NP;
     const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
     if (first >= pairs) return;
     // One division per wave; the wave's later pairs step through the heads.
@@ -278,6 +284,22 @@ __global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCach
     }
 }
 
+template <bool HALF, int NP, bool SAME_T>
+__global__ __launch_bounds__(256) void norm_rope_cache_write_kernel(NormRopeCacheWriteArgs a, bool vec4) {
+    norm_rope_write_pairs<HALF, NP, SAME_T>(a, vec4, blockIdx.x);
+}
+
+// q rows and the new K/V rows of a step in one launch: workgroups below
+// q_blocks take q (row, head) units, the others one (token, kv head) pair per
+// wave.  SMALL: head size up to 128 (32 lanes per q head, K and V side by
+// side in the writer).
+template <bool SMALL>
+__global__ __launch_bounds__(256) void norm_rope_qk_write_kernel(NormRopeArgs q, NormRopeCacheWriteArgs k,
+                                                                 uint32_t q_blocks, bool q_vec4, bool k_vec4) {
+    if (blockIdx.x < q_blocks) norm_rope_rows<SMALL ? 32 : 64>(q, q_vec4, blockIdx.x);
+    else norm_rope_write_pairs<SMALL, 1, true>(k, k_vec4, blockIdx.x - q_blocks);
+}
+
 }  // namespace
 
 hipError_t launch_rope_table(float* table, uint32_t num_positions, uint32_t rot, double theta, hipStream_t stream) {
@@ -287,25 +309,36 @@ hipError_t launch_rope_table(float* table, uint32_t num_positions, uint32_t rot,
     return hipGetLastError();
 }
 
-hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t stream) {
-    const bool vec4 = reinterpret_cast<uintptr_t>(a.x) % 16 == 0 && reinterpret_cast<uintptr_t>(a.out) % 16 == 0 &&
-                      a.x_stride % 4 == 0 && a.head_stride % 4 == 0 && a.out_stride % 4 == 0;
+namespace {
+bool rows_vec4(const NormRopeArgs& a) {
+    return reinterpret_cast<uintptr_t>(a.x) % 16 == 0 && reinterpret_cast<uintptr_t>(a.out) % 16 == 0 &&
+           a.x_stride % 4 == 0 && a.head_stride % 4 == 0 && a.out_stride % 4 == 0;
+}
+bool pairs_vec4(const NormRopeCacheWriteArgs& a) {
+    return reinterpret_cast<uintptr_t>(a.key) % 16 == 0 && reinterpret_cast<uintptr_t>(a.value) % 16 == 0 &&
+           a.key_stride % 4 == 0 && a.value_stride % 4 == 0;
+}
+// workgroups of 4 waves for the q rows: two (row, head) units per wave at
+// head sizes up to 128, one above
+uint32_t rows_blocks(const NormRopeArgs& a) {
     const uint64_t units = static_cast<uint64_t>(a.num_rows) * a.num_heads;
-    if (a.head_size / 4 <= 32) {
-        const uint64_t waves = (units + 1) / 2;
-        hipLaunchKernelGGL(norm_rope_kernel<32>, dim3(static_cast<uint32_t>((waves + 3) / 4)), dim3(256), 0, stream, a,
-                           vec4);
-    } else {
-        hipLaunchKernelGGL(norm_rope_kernel<64>, dim3(static_cast<uint32_t>((units + 3) / 4)), dim3(256), 0, stream, a,
-                           vec4);
-    }
+    const uint64_t waves = a.head_size / 4 <= 32 ? (units + 1) / 2 : units;
+    return static_cast<uint32_t>((waves + 3) / 4);
+}
+}  // namespace
+
+hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t stream) {
+    const bool vec4 = rows_vec4(a);
+    if (a.head_size / 4 <= 32)
+        hipLaunchKernelGGL(norm_rope_kernel<32>, dim3(rows_blocks(a)), dim3(256), 0, stream, a, vec4);
+    else
+        hipLaunchKernelGGL(norm_rope_kernel<64>, dim3(rows_blocks(a)), dim3(256), 0, stream, a, vec4);
     return hipGetLastError();
 }
 
 hipError_t launch_norm_rope_cache_write(const NormRopeCacheWriteArgs& a, hipStream_t stream) {
     const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
-    const bool vec4 = reinterpret_cast<uintptr_t>(a.key) % 16 == 0 && reinterpret_cast<uintptr_t>(a.value) % 16 == 0 &&
-                      a.key_stride % 4 == 0 && a.value_stride % 4 == 0;
+    const bool vec4 = pairs_vec4(a);
     const bool half = a.head_size / 4 <= 32;
     const uint32_t grid_1 = static_cast<uint32_t>((pairs + 3) / 4);      // one pair per wave
     if (pairs >= kWriteBatchMinPairs && half && a.num_kv_heads % 4 == 0) {
@@ -325,6 +358,29 @@ hipError_t launch_norm_rope_cache_write(const NormRopeCacheWriteArgs& a, hipStre
         if (half) hipLaunchKernelGGL((norm_rope_cache_write_kernel<true, 1, true>), dim3(grid_1), dim3(256), 0, stream, a, vec4);
         else hipLaunchKernelGGL((norm_rope_cache_write_kernel<false, 1, true>), dim3(grid_1), dim3(256), 0, stream, a, vec4);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_rope_qk_cache_write(const NormRopeArgs& q, const NormRopeCacheWriteArgs& k,
+                                           hipStream_t stream) {
+    const uint64_t pairs = static_cast<uint64_t>(k.num_tokens) * k.num_kv_heads;
+    const bool no_q = q.num_rows == 0 || q.num_heads == 0;
+    if (pairs >= kWriteBatchMinPairs || no_q || pairs == 0) {
+        // a bulk write keeps its batched kernel; an empty side needs no combined launch
+        if (!no_q) {
+            const hipError_t e = launch_norm_rope(q, stream);
+            if (e != hipSuccess) return e;
+        }
+        return pairs ? launch_norm_rope_cache_write(k, stream) : hipSuccess;
+    }
+    const uint32_t qb = rows_blocks(q);
+    const dim3 grid(qb + static_cast<uint32_t>((pairs + 3) / 4));
+    if (q.head_size / 4 <= 32)
+        hipLaunchKernelGGL(norm_rope_qk_write_kernel<true>, grid, dim3(256), 0, stream, q, k, qb, rows_vec4(q),
+                           pairs_vec4(k));
+    else
+        hipLaunchKernelGGL(norm_rope_qk_write_kernel<false>, grid, dim3(256), 0, stream, q, k, qb, rows_vec4(q),
+                           pairs_vec4(k));
     return hipGetLastError();
 }
 

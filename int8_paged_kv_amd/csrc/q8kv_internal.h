@@ -74,6 +74,8 @@ hipError_t launch_index_select(const IndexSelectArgs& a, hipStream_t stream);
 hipError_t launch_rope_table(float* table, uint32_t num_positions, uint32_t rot, double theta, hipStream_t stream);
 hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t stream);
 hipError_t launch_norm_rope_cache_write(const NormRopeCacheWriteArgs& a, hipStream_t stream);
+// q rows and the K/V write in one launch (two for a bulk write)
+hipError_t launch_norm_rope_qk_cache_write(const NormRopeArgs& q, const NormRopeCacheWriteArgs& k, hipStream_t stream);
 
 // Decode plan shared by the workspace query and the decode call.  For each
 // row group (kv head, group of query heads sharing it) waves_per_rg

@@ -246,6 +246,28 @@ def test_norm_rope_cache_write_nulls_and_empty(lib):
                                         ctypes.c_float(1e-6), 0, 2, 128, 16, 8, None) == 0
 
 
+def qk_call(lib, q_out=FAKE, q_head_stride=128, q_rows=4, heads=32, q_pos=FAKE, q_w=FAKE, key=FAKE, k_pos=FAKE,
+            k_w=FAKE, table=FAKE, rot=64, npos=16, tokens=4, hkv=2, hs=128, bs=16, nb=8):
+    return lib.q8_norm_rope_qk_cache_write(q_out, heads * hs, FAKE, heads * q_head_stride, q_head_stride, q_rows,
+                                           heads, q_pos, q_w, key, hkv * hs, FAKE, hkv * hs, FAKE, FAKE, FAKE, k_pos,
+                                           k_w, table, rot, npos, ctypes.c_float(1e-6), tokens, hkv, hs, bs, nb, None)
+
+
+def test_norm_rope_qk_cache_write_validation(lib):
+    """The union of q8_norm_rope's and q8_norm_rope_cache_write's rules; either side may be empty."""
+    assert qk_call(lib, q_out=None, q_pos=None, q_w=None, key=None, k_pos=None, k_w=None, table=None,
+                   q_rows=0, tokens=0) == 0                                  # both sides empty
+    assert qk_call(lib, q_head_stride=127) == 2                             # q heads overlap
+    assert qk_call(lib, rot=12) == 2                                        # rot not a multiple of 8
+    assert qk_call(lib, bs=0, q_rows=0) == 2                                # the write's shape, q empty
+    assert qk_call(lib, nb=0) == 2
+    assert qk_call(lib, q_out=None) == 1
+    assert qk_call(lib, q_pos=None) == 1                                    # rot > 0: q positions needed
+    assert qk_call(lib, key=None) == 1
+    assert qk_call(lib, k_w=None) == 1
+    assert qk_call(lib, table=None, q_rows=0) == 1                          # the table, for the write alone
+
+
 def test_index_select_validation(lib):
     assert lib.q8_index_select(FAKE, 64, FAKE, 4, 0, 2, FAKE, 128, FAKE, None, 0, None) == 2          # ratio 0
     assert lib.q8_index_select(FAKE, 64, FAKE, 4, 64, 32, FAKE, 2111, FAKE, None, 0, None) == 2       # (k+1)*ratio > vis_stride

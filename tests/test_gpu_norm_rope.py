@@ -287,3 +287,52 @@ def test_norm_rope_cache_write_unaligned_weight_and_rows(oracle_mod):
     oracle_mod.norm_rope_cache_write(key, val, kh, vh, slots, pos, w, tab_h, rot, 1e-6, hkv, hs, bs)
     assert np.array_equal(u32_host(vd), vh)
     assert compare_k_rows(oracle_mod, u32_host(kd), kh, key, slots, pos, w, tab_h, rot, hkv, hs, bs) <= 2
+
+
+@pytest.mark.parametrize("Tq,H,T,hkv,hs,rot", [
+    (64, 32, 64, 8, 128, 64),        # the decode step's shape: 64 sequences, one new token each
+    (5, 4, 7, 2, 256, 128),          # head size above 128
+    (0, 4, 9, 2, 64, 32),            # no q rows: the write alone
+    (6, 3, 0, 2, 64, 32),            # no new tokens: the q rows alone
+    (3, 8, 4200, 8, 128, 64),        # a bulk write: q rows, then the batched writer
+])
+def test_norm_rope_qk_cache_write(oracle_mod, Tq, H, T, hkv, hs, rot):
+    """q rows and the K/V write in one launch: bit-identical to q8_norm_rope
+    followed by q8_norm_rope_cache_write, and against the oracle."""
+    from int8_paged_kv_amd import q8_norm_rope, q8_norm_rope_cache_write, q8_norm_rope_qk_cache_write
+    f32_dev, u32_dev, u32_host = dev()
+    g = np.random.default_rng(Tq * 31 + T + hs)
+    bs, P = 16, 8192
+    nb = T // bs + 4
+    q = (g.standard_normal((Tq, H * hs)) * 3).astype(np.float32)
+    qpos = g.integers(0, P, Tq).astype(np.uint32)
+    key = (g.standard_normal((T, hkv * hs)) * g.uniform(0.05, 30, (T, 1))).astype(np.float32)
+    val = g.standard_normal((T, hkv * hs)).astype(np.float32)
+    qw = (1.0 + 0.1 * g.standard_normal(hs)).astype(np.float32)
+    kw = (1.0 + 0.1 * g.standard_normal(hs)).astype(np.float32)
+    slots = g.choice(nb * bs, size=T, replace=False).astype(np.uint32)
+    if T > 3:
+        slots[[1, T // 2]] = wl.PAD_SLOT
+    kpos = g.integers(0, P, T).astype(np.uint32)
+    tab_d = gpu_table(P, rot, 10000.0)
+    kh, vh = wl.poison_cache(nb, hkv, bs, hs), wl.poison_cache(nb, hkv, bs, hs)
+    kd1, vd1 = u32_dev(kh), u32_dev(vh)
+    qo1 = q8_norm_rope_qk_cache_write(f32_dev(q), u32_dev(qpos), f32_dev(qw), H, f32_dev(key), f32_dev(val), kd1, vd1,
+                                      u32_dev(slots), u32_dev(kpos), f32_dev(kw), tab_d, rot, 1e-6, hkv, hs, bs)
+    kd2, vd2 = u32_dev(kh), u32_dev(vh)
+    qo2 = q8_norm_rope(f32_dev(q), u32_dev(qpos), f32_dev(qw), tab_d, rot, 1e-6, H, hs)
+    q8_norm_rope_cache_write(f32_dev(key), f32_dev(val), kd2, vd2, u32_dev(slots), u32_dev(kpos), f32_dev(kw), tab_d,
+                             rot, 1e-6, hkv, hs, bs)
+    torch.cuda.synchronize()
+    q1, q2 = qo1.cpu().numpy(), qo2.cpu().numpy()
+    assert np.array_equal(q1.view(np.uint32), q2.view(np.uint32)), "q rows differ from the separate call"
+    assert np.array_equal(u32_host(kd1), u32_host(kd2)) and np.array_equal(u32_host(vd1), u32_host(vd2)), \
+        "caches differ from the separate call"
+    tab_h = oracle_mod.rope_table(P, rot, 10000.0)
+    if Tq:
+        check_rows_close(q1, oracle_mod.norm_rope(q, qpos, qw, tab_h, rot, 1e-6, H, hs))
+    oracle_mod.norm_rope_cache_write(key, val, kh, vh, slots, kpos, kw, tab_h, rot, 1e-6, hkv, hs, bs)
+    assert np.array_equal(u32_host(vd1), vh)
+    n = compare_k_rows(oracle_mod, u32_host(kd1), kh, key.reshape(T, hkv, hs), slots, kpos, kw, tab_h, rot, hkv, hs,
+                       bs)
+    assert n <= max(2, T * hkv // 10000)
