@@ -1,6 +1,7 @@
 """Randomized GPU parity sweep against the oracle: decode (dense and
-visible-list), the one-launch step, multi-row decode and the cache writer
-(bit-exact; small and batched sizes, pads) over random head
+visible-list), the one-launch step, multi-row decode, the cache writer
+(bit-exact; small and batched sizes, pads), block selection (lists, counts
+and bitmasks bit-exact) and the q + K/V norm and rotary launch, over random head
 sizes, block sizes, GQA ratios, batch sizes on both sides of the 64-sequence
 window, length mixes (empty, one token, block and chunk edges, long), clamps
 and forced wavefront counts.  Every case is drawn from a fixed seed and named
@@ -15,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-N_CASES = 96
+N_CASES = 128
 HEAD_SIZES = [16, 32, 48, 64, 68, 96, 128, 192, 256]
 BLOCK_SIZES = [1, 4, 5, 8, 16, 32, 64, 128]
 KV_HEADS = [1, 2, 3, 4, 8]
@@ -25,7 +26,7 @@ WAVES = [None, None, 1, 7, 64, 333, 2048]
 
 def draw(i):
     g = np.random.default_rng(900 + i)
-    kind = ["decode", "decode", "visible", "step", "rows", "write"][i % 6]
+    kind = ["decode", "decode", "visible", "step", "rows", "write", "select", "normrope"][i % 8]
     hs = int(g.choice(HEAD_SIZES))
     bs = int(g.choice(BLOCK_SIZES))
     hkv = int(g.choice(KV_HEADS))
@@ -76,6 +77,24 @@ def run_write_case(oracle_mod, p):
     assert np.array_equal(u32_host(vd), vh), "value cache words differ (T=%d)" % T
 
 
+def run_select_case(oracle_mod, p):
+    """q8_index_select over random rows: lists, counts and bitmasks bit-exact."""
+    from test_gpu_index_select import run_select
+    g = np.random.default_rng(p["seed"] + 4)
+    ratio = int(g.choice([1, 4, 16, 64]))
+    k = int(g.integers(0, 41))
+    max_blocks = int(g.integers(1, 3001))
+    R = int(g.integers(1, 41))
+    if g.random() < 0.5:
+        scores = g.integers(-3, 4, (R, max_blocks)).astype(np.float32)       # many ties
+    else:
+        scores = g.standard_normal((R, max_blocks)).astype(np.float32)
+    lens = g.integers(0, max_blocks * ratio + ratio, R).astype(np.uint32)
+    vis_stride = k * ratio + ratio + int(g.integers(0, 5))
+    mask_stride = (max_blocks + 1 + 31) // 32 + int(g.integers(0, 3))
+    run_select(oracle_mod, scores, lens, ratio, k, vis_stride, mask_stride)
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(oracle_mod, i):
     p = draw(i)
@@ -85,6 +104,15 @@ def test_random_case(oracle_mod, i):
     try:
         if p["kind"] == "write":
             run_write_case(oracle_mod, p)
+        elif p["kind"] == "select":
+            run_select_case(oracle_mod, p)
+        elif p["kind"] == "normrope":
+            from test_gpu_norm_rope import test_norm_rope_qk_cache_write as run_qk
+            g = np.random.default_rng(p["seed"] + 5)
+            hs = int(g.choice([32, 64, 96, 128, 192, 256]))
+            rot = 8 * int(g.integers(0, hs // 8 + 1))
+            run_qk(oracle_mod, int(g.choice([0, 1, 9, 64])), int(g.integers(1, 9)), int(g.choice([0, 3, 64, 700])),
+                   p["Hkv"], hs, rot)
         elif p["kind"] == "step":
             from test_gpu_step import run_step_case
             run_step_case(oracle_mod, p["seed"], p["S"], p["H"], p["Hkv"], p["hs"], p["bs"], p["lens"], mcl=p["mcl"])
