@@ -1,7 +1,8 @@
 """Randomized GPU parity sweep against the oracle: decode (dense and
 visible-list), the one-launch step, multi-row decode, the cache writer
 (bit-exact; small and batched sizes, pads), block selection (lists, counts
-and bitmasks bit-exact) and the q + K/V norm and rotary launch, over random head
+and bitmasks bit-exact), the q + K/V norm and rotary launch and the f32-cache
+decode, over random head
 sizes, block sizes, GQA ratios, batch sizes on both sides of the 64-sequence
 window, length mixes (empty, one token, block and chunk edges, long), clamps
 and forced wavefront counts.  Every case is drawn from a fixed seed and named
@@ -16,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-N_CASES = 128
+N_CASES = 144
 HEAD_SIZES = [16, 32, 48, 64, 68, 96, 128, 192, 256]
 BLOCK_SIZES = [1, 4, 5, 8, 16, 32, 64, 128]
 KV_HEADS = [1, 2, 3, 4, 8]
@@ -26,7 +27,7 @@ WAVES = [None, None, 1, 7, 64, 333, 2048]
 
 def draw(i):
     g = np.random.default_rng(900 + i)
-    kind = ["decode", "decode", "visible", "step", "rows", "write", "select", "normrope"][i % 8]
+    kind = ["decode", "decode", "visible", "step", "rows", "write", "select", "normrope", "f32"][i % 9]
     hs = int(g.choice(HEAD_SIZES))
     bs = int(g.choice(BLOCK_SIZES))
     hkv = int(g.choice(KV_HEADS))
@@ -104,6 +105,14 @@ def test_random_case(oracle_mod, i):
     try:
         if p["kind"] == "write":
             run_write_case(oracle_mod, p)
+        elif p["kind"] == "f32":
+            from test_gpu_f32 import F32Gpu
+            from gpu_util import assert_close
+            hs = {16: 16, 32: 32, 48: 64, 64: 64, 68: 64, 96: 128, 128: 128, 192: 256, 256: 256}[p["hs"]]
+            if p["waves"] is not None:
+                os.environ["Q8KV_F32_DECODE_WAVES"] = str(p["waves"])
+            c = F32Gpu(oracle_mod, p["seed"], p["S"], p["H"], p["Hkv"], hs, p["bs"], p["lens"])
+            assert_close(c.gpu(max_context_len=p["mcl"]), c.oracle(oracle_mod, max_context_len=p["mcl"]), name)
         elif p["kind"] == "select":
             run_select_case(oracle_mod, p)
         elif p["kind"] == "normrope":
@@ -143,3 +152,4 @@ def test_random_case(oracle_mod, i):
         raise AssertionError("%s: %s" % (name, e)) from None
     finally:
         os.environ.pop("Q8KV_DECODE_WAVES", None)
+        os.environ.pop("Q8KV_F32_DECODE_WAVES", None)
