@@ -43,6 +43,12 @@ L2_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc 
           "-d {d}/pmc_L2 -o bench -f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
 PMC_ALL_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {c} -d {d}/pmc_all_{c} -o bench "
                "-f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu")
+SQ_PASSES = (("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM",
+              "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
+             ("SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA",
+              "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM", "SQ_WAVES"))
+SQ_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {cs} -d {d}/pmc_sq{i} -o bench "
+          "-f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
 COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} -d {d}/copy_{c} -o copy -f csv "
             "-- python3 /root/repo/bench.py --copy-calibration {mib}")
 
@@ -279,6 +285,42 @@ def main():
     ] + l2_key
     with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_traffic.txt"), "w") as f:
         f.write("\n".join(t) + "\n")
+
+    # ---- optional: SQ instruction and wait counters of the step launch ----
+    sq_csv = [os.path.join(d, "pmc_sq%d" % i, "bench_counter_collection.csv") for i in (1, 2)]
+    if all(os.path.exists(x) for x in sq_csv):
+        vals = {}
+        for i, x in enumerate(sq_csv, 1):
+            if last_json(os.path.join(d, "pmc_sq%d.log" % i))["kernel_sources_sha256_16"] != digest:
+                raise SystemExit("SQ counter runs were taken on different kernel sources")
+            for (name, grid, c), vs in counters_by_name(x).items():
+                if "decode_split_kernel" in name and grid == step_grid.get("decode_split_kernel"):
+                    vals[c] = statistics.median(vs)
+        q = [
+            "# SQ counters of the step launch (append + decode), Llama-3-8B-shaped batch, median per dispatch",
+            "# (S=64 H=32 Hkv=8 head_size=128 block_size=16, context lengths U[512,4096], seed 2)",
+            "#",
+            "# commands (from any directory on the GPU machine), eight SQ counters per run:",
+        ] + ["#   " + SQ_CMD.format(cs=" ".join(cs), d=args.cmd_dir, i=i) for i, cs in enumerate(SQ_PASSES, 1)] + [
+            "# summarised with: python3 bench_profile.py <that -d directory's parent>",
+            "#",
+            "# kernel_sources_sha256_16: %s" % digest,
+            "",
+        ]
+        for c in [c for cs in SQ_PASSES for c in cs]:
+            if c in vals:
+                q.append("%-28s %16.0f" % (c, vals[c]))
+        wc = vals.get("SQ_WAVE_CYCLES")
+        if wc:
+            q += ["", "fractions of wave cycles (SQ_WAVE_CYCLES):"]
+            for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM",
+                      "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA"):
+                if c in vals:
+                    q.append("  %-26s %.3f" % (c, vals[c] / wc))
+        if vals.get("SQ_BUSY_CYCLES") and vals.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+            q.append("  MFMA busy / SQ busy cycles  %.3f" % (vals["SQ_VALU_MFMA_BUSY_CYCLES"] / vals["SQ_BUSY_CYCLES"]))
+        with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_sq_counters.txt"), "w") as f:
+            f.write("\n".join(q) + "\n")
 
     # ---- optional: HBM traffic of every kernel of a run with the reference legs ----
     fa = os.path.join(d, "pmc_all_FETCH_SIZE", "bench_counter_collection.csv")
