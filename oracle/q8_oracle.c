@@ -521,11 +521,13 @@ int q8o_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t x_st
         (uint64_t)out_stride < (uint64_t)num_heads * head_size)
         return Q8O_ERR_SHAPE;
     for (uint32_t t = 0; t < num_rows; ++t) {
-        uint32_t p = positions[t];
+        /* without rotation, positions and table may be NULL and are not read */
+        uint32_t p = rot > 0 ? positions[t] : 0;
         if (rot > 0 && p >= num_positions) return Q8O_ERR_RANGE;
+        const float* cs = rot > 0 ? table + (uint64_t)p * rot : NULL;
         for (uint32_t h = 0; h < num_heads; ++h) {
             int rc = q8o_norm_rope_row(x + (uint64_t)t * x_stride + (uint64_t)h * head_stride, head_size,
-                                       weight, table + (uint64_t)p * rot, rot, eps,
+                                       weight, cs, rot, eps,
                                        out + (uint64_t)t * out_stride + (uint64_t)h * head_size);
             if (rc != Q8O_OK) return rc;
         }
@@ -559,12 +561,12 @@ int q8o_norm_rope_cache_write(const float* key, uint32_t key_stride,
         uint32_t slot = slot_mapping[t];
         if (slot == Q8O_PAD_SLOT) continue;
         uint64_t block = slot / block_size, off = slot % block_size;
-        uint32_t p = positions[t];
+        uint32_t p = rot > 0 ? positions[t] : 0;    /* not read without rotation */
         if (block >= num_blocks || (rot > 0 && p >= num_positions)) { rc = Q8O_ERR_RANGE; break; }
         for (uint32_t h = 0; h < num_kv_heads && rc == Q8O_OK; ++h) {
             uint64_t dst = row_offset(block, off, h, num_kv_heads, block_size, wpt);
             rc = q8o_norm_rope_row(key + (uint64_t)t * key_stride + (uint64_t)h * head_size, head_size,
-                                   weight, table + (uint64_t)p * rot, rot, eps, y);
+                                   weight, rot > 0 ? table + (uint64_t)p * rot : NULL, rot, eps, y);
             if (rc == Q8O_OK) rc = q8o_quantize_row(y, head_size, key_cache + dst);
             if (rc == Q8O_OK)
                 rc = q8o_quantize_row(value + (uint64_t)t * value_stride + (uint64_t)h * head_size,
