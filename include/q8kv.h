@@ -13,7 +13,8 @@
  *
  * Conventions for every entry point:
  *   - Array pointers are DEVICE pointers owned by the caller.  The library
- *     keeps no per-call state and allocates no memory.
+ *     keeps no per-call state and allocates no memory (the one exception to
+ *     the first: q8_paged_decode_noalloc's scratch array, below).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work; they never synchronize.  They are reentrant.
  *   - Shapes are validated on the host before anything is enqueued; on any
@@ -144,6 +145,42 @@ q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
                           uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
                           float scale, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * q8_paged_decode_noalloc -- q8_paged_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The partial records
+ * and arrival counters live in a fixed device array of
+ * Q8_NOALLOC_SCRATCH_BYTES inside the library; each GPU the library runs on
+ * holds its own copy until the process ends.  The call allocates nothing:
+ * the first call on a device looks up the array's address
+ * (hipGetSymbolAddress) and clears it with a fill kernel on `stream`.
+ *
+ *   All arguments mean what they mean for q8_paged_decode (dense or
+ *   visible-list mode); the results are the same as those of q8_paged_decode
+ *   with its own workspace.
+ *
+ * Every call on one GPU shares that GPU's array, and each call leaves it ready
+ * for the next: calls on one GPU must not overlap (the same stream, or
+ * streams ordered by the caller); overlapping calls race on the array and
+ * give undefined results.  After a failed or aborted launch the array's
+ * counters may be left nonzero and later results are undefined.
+ * Errors: those of q8_paged_decode, except that Q8_ERR_WORKSPACE means these
+ * sizes need more than Q8_NOALLOC_SCRATCH_BYTES of scratch
+ * (q8_paged_decode_workspace_bytes gives the need); Q8_ERR_HIP when the
+ * array's address cannot be found; Q8_ERR_UNSUPPORTED on a device ordinal
+ * of 64 or more.
+ */
+#define Q8_NOALLOC_SCRATCH_BYTES (32u << 20)
+q8_status q8_paged_decode_noalloc(float* out, const float* q, uint32_t q_stride,
+                                  const uint32_t* key_cache, const uint32_t* value_cache,
+                                  const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                                  const uint32_t* context_lens, uint32_t max_context_len,
+                                  const uint32_t* visible_pos, const uint32_t* num_visible,
+                                  uint32_t vis_stride,
+                                  uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                                  uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                                  float scale, void* stream);
 
 /*
  * q8_decode_step -- one decode step in a single launch: every sequence's new K

@@ -7,6 +7,8 @@ Operations behind the C ABI of libq8kv.so (include/q8kv.h):
 * ``q8_paged_decode``: single-query decode attention over that cache (the
   "paged_attn_q8.comp" page), optionally over per-sequence visible-position
   lists (the selective decode of the "attention.rs" page).
+* ``q8_paged_decode_noalloc``: the same decode with the library's own
+  scratch array in place of a workspace, for callers that cannot allocate.
 * ``q8_decode_step``: both in one launch for the usual decode step (each
   sequence's new token appended at its last position, then attended).
 * ``q8_paged_decode_rows``: multi-row causal decode (several query rows per
@@ -25,7 +27,7 @@ The binding loads the library lazily, so ``int8_paged_kv_amd.workloads`` can
 be imported on a machine without the library or a GPU.
 """
 
-__all__ = ["q8_cache_write", "q8_paged_decode", "q8_decode_step", "q8_paged_decode_rows",
+__all__ = ["q8_cache_write", "q8_paged_decode", "q8_paged_decode_noalloc", "q8_decode_step", "q8_paged_decode_rows",
            "q8_paged_decode_workspace_bytes", "q8_f32_cache_write", "q8_f32_paged_decode",
            "q8_f32_paged_decode_workspace_bytes", "q8_rope_table", "q8_norm_rope", "q8_norm_rope_cache_write",
            "q8_norm_rope_qk_cache_write", "q8_index_select",

@@ -46,6 +46,9 @@ def load_library() -> ctypes.CDLL:
         lib.q8_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U, P, P, U,
                                         U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.q8_paged_decode.restype = ctypes.c_int
+        lib.q8_paged_decode_noalloc.argtypes = [P, P, U, P, P, P, U, P, U, P, P, U,
+                                                U, U, U, U, U, U, ctypes.c_float, P]
+        lib.q8_paged_decode_noalloc.restype = ctypes.c_int
         lib.q8_decode_step.argtypes = [P, P, U, P, U, P, U, P, P, P, U, P, U,
                                        U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
         lib.q8_decode_step.restype = ctypes.c_int
@@ -196,6 +199,47 @@ def q8_paged_decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch
                              S, H, num_kv_heads, hs, block_size, num_blocks, float(scale), wp, wb,
                              _stream(stream))
     _check(st, "q8_paged_decode")
+    return out
+
+
+def q8_paged_decode_noalloc(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: Optional[torch.Tensor], scale: float,
+                            num_kv_heads: int, block_size: int, max_context_len: Optional[int] = None,
+                            visible_pos: Optional[torch.Tensor] = None, num_visible: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None, num_blocks: Optional[int] = None,
+                            stream=None) -> torch.Tensor:
+    """q8_paged_decode with the library's own scratch array instead of a
+    workspace (see include/q8kv.h): nothing is allocated when `out` is given.
+    Calls on one GPU must not overlap."""
+    lib = load_library()
+    if q.dim() != 3 or (q.numel() and not q[0].is_contiguous()):
+        raise ValueError("q must be [S, H, head_size] with dense rows")
+    S, H, hs = q.shape
+    if out is None:
+        out = torch.empty((S, H, hs), dtype=torch.float32, device=q.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (S, H, hs):
+        raise ValueError("out must be a contiguous [S, H, head_size] f32 tensor")
+    vis = visible_pos is not None
+    if vis:
+        if visible_pos.dim() != 2:
+            raise ValueError("visible_pos must be [S, vis_stride]")
+        vis_stride, mcl = visible_pos.shape[1], 0
+    else:
+        if max_context_len is None:
+            raise ValueError("max_context_len is required in dense mode")
+        vis_stride, mcl = 0, int(max_context_len)
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [S, max_num_blocks_per_seq]")
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * (hs // 4 + 1))
+    st = lib.q8_paged_decode_noalloc(_dev(out, "out", torch.float32), _dev(q, "q", torch.float32), q.stride(0),
+                                     _u32(key_cache, "key_cache"), _u32(value_cache, "value_cache"),
+                                     _u32(block_tables, "block_tables"), block_tables.shape[1],
+                                     _u32(context_lens, "context_lens"), mcl,
+                                     _u32(visible_pos, "visible_pos"), _u32(num_visible, "num_visible"),
+                                     vis_stride, S, H, num_kv_heads, hs, block_size, num_blocks, float(scale),
+                                     _stream(stream))
+    _check(st, "q8_paged_decode_noalloc")
     return out
 
 

@@ -4,6 +4,7 @@
 #include "q8kv_internal.h"
 
 #include <cmath>
+#include <mutex>
 
 namespace {
 
@@ -59,6 +60,55 @@ size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
 
 }  // extern "C"
 
+// ---- scratch of the decode entry point that allocates nothing ----
+// A fixed device array holds that entry point's partial records and arrival
+// counters.  Each GPU the library runs on has its own copy at its own
+// address, found once per device with hipGetSymbolAddress; host code uses
+// only that address, never the array's name.  All calls on one GPU share it.
+namespace {
+constexpr size_t kScratchBytes = Q8_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+__global__ void zero_scratch_kernel(uint4* p, size_t n) {
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];   // device address of `scratch`, per device, once set up
+
+// The scratch address on the current device.  The first call on a device
+// looks the address up and clears the whole array (the arrival counters must
+// start at zero; every completed decode leaves them at zero again) with a
+// fill kernel on the caller's stream, ordered before the caller's decode.
+q8_status scratch_of_current_device(void** out, hipStream_t stream) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxScratchDevices) return Q8_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        hipLaunchKernelGGL(zero_scratch_kernel, dim3(1024), dim3(256), 0, stream, static_cast<uint4*>(ptr),
+                           kScratchBytes / sizeof(uint4));
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return Q8_OK;
+}
+
+}  // namespace
+
 namespace {
 
 struct AppendArgs {
@@ -78,7 +128,8 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
                         uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
                         uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
                         float scale, void* workspace, size_t workspace_bytes,
-                        void* stream, const AppendArgs* app, uint32_t rows_per_seq) {
+                        void* stream, const AppendArgs* app, uint32_t rows_per_seq,
+                        bool static_scratch = false) {
     if (!head_size_ok(head_size) || block_size == 0 || num_heads == 0 || num_kv_heads == 0 ||
         num_heads % num_kv_heads != 0)
         return Q8_ERR_SHAPE;
@@ -108,6 +159,13 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
                                                  block_size, max_pos);
     if (p.num_waves > 0x7FFFFFFFull || static_cast<uint64_t>(num_seqs) * num_pairs > 0x7FFFFFFFull)
         return Q8_ERR_UNSUPPORTED;
+    if (p.bytes > 0 && static_scratch) {
+        // The library's own scratch array instead of a caller workspace.
+        if (p.bytes > kScratchBytes) return Q8_ERR_WORKSPACE;
+        const q8_status st = scratch_of_current_device(&workspace, static_cast<hipStream_t>(stream));
+        if (st != Q8_OK) return st;
+        workspace_bytes = kScratchBytes;
+    }
     if (p.bytes > 0) {
         if (!workspace || workspace_bytes < p.bytes) return Q8_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return Q8_ERR_WORKSPACE;
@@ -169,6 +227,21 @@ q8_status q8_paged_decode(float* out, const float* q, uint32_t q_stride,
                          context_lens, max_context_len, visible_pos, num_visible, vis_stride, num_seqs,
                          num_heads, num_kv_heads, head_size, block_size, num_blocks, scale, workspace,
                          workspace_bytes, stream, nullptr, 1);
+}
+
+q8_status q8_paged_decode_noalloc(float* out, const float* q, uint32_t q_stride,
+                                  const uint32_t* key_cache, const uint32_t* value_cache,
+                                  const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                                  const uint32_t* context_lens, uint32_t max_context_len,
+                                  const uint32_t* visible_pos, const uint32_t* num_visible,
+                                  uint32_t vis_stride,
+                                  uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                                  uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                                  float scale, void* stream) {
+    return decode_common(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
+                         context_lens, max_context_len, visible_pos, num_visible, vis_stride, num_seqs,
+                         num_heads, num_kv_heads, head_size, block_size, num_blocks, scale, nullptr, 0, stream,
+                         nullptr, 1, true);
 }
 
 q8_status q8_paged_decode_rows(float* out, const float* q, uint32_t q_stride,

@@ -277,3 +277,25 @@ def test_index_select_validation(lib):
     assert lib.q8_index_select(None, 64, None, 0, 64, 32, None, 2112, None, None, 0, None) == 0       # no rows
     assert lib.q8_index_select(FAKE, 64, FAKE, 4, 64, 32, FAKE, 2112, FAKE, FAKE, 2, None) == 2   # 65 blocks need 3 words
     assert lib.q8_index_select(FAKE, 63, FAKE, 0, 64, 32, FAKE, 2112, FAKE, FAKE, 2, None) == 0   # 64 blocks fit in 2
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """The no-alloc decode refuses shapes whose partial records exceed its
+    fixed scratch array before touching the device; smaller shapes than the
+    limit pass validation identically to q8_paged_decode's."""
+    a = decode_args(S=100000, H=16, Hkv=16, hs=256, q_stride=16 * 256, mcl=5000)
+    need = lib.q8_paged_decode_workspace_bytes(100000, 16, 16, 256, 16, 5000)
+    assert need > (32 << 20)
+    del a[19:21]        # no workspace arguments
+    assert lib.q8_paged_decode_noalloc(*a) == 3
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(hs=6), 2), (dict(H=3, Hkv=2), 2), (dict(q_stride=100), 2), (dict(q=None), 1),
+    (dict(vis=FAKE, nvis=FAKE, vis_stride=0), 2),
+])
+def test_noalloc_validation_matches_decode(lib, kw, want):
+    a = decode_args(**kw)
+    assert lib.q8_paged_decode(*a) == want
+    del a[19:21]
+    assert lib.q8_paged_decode_noalloc(*a) == want
