@@ -71,11 +71,12 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes_per_launch": n * 4, "launches": 5}), flush=True)
 
 
-# The files the decode-step kernel (decode_split_kernel) and its launch are
-# built from; the committed HBM-traffic figures hold while these are unchanged.
+# The files the decode kernel (decode_split_kernel), the cache writer and their
+# launches are built from; the committed HBM-traffic figures hold while these
+# are unchanged.
 DECODE_SOURCES = ("decode_kernel.h", "decode_split.h", "decode.hip", "decode_hs16.hip", "decode_hs32.hip",
                   "decode_hs48.hip", "decode_hs64.hip", "q8_pack.h", "lane_reduce.h", "wave_ops.h",
-                  "q8kv_internal.h")
+                  "q8kv_internal.h", "cache_write.hip")
 
 
 def kernel_sources_digest() -> str:
@@ -101,6 +102,283 @@ def read_traffic(digest: str):
         if kv.get("kernel_sources_sha256_16") != digest:
             return None
         return float(kv["hbm_bytes_per_step"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_threads() -> int:
+    """Threads of the all-cores CPU leg: the host's cores, capped at the
+    OMP_NUM_THREADS the machine sets for this process (its CPU share)."""
+    return max(1, min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(oracle, w, qh, kh, vh, mcl, seconds):
+    """The oracle's decode (binary64 plain definition) on the host, on all
+    cores of this process's share and on one thread, over bounded samples of
+    the same workload; rates in effective KV bytes per second, so they compare
+    with the GPU line directly."""
+    Hkv, hs, bs = w.num_kv_heads, w.head_size, w.block_size
+    n_all = cpu_threads()
+
+    def run(seqs, nthreads, budget):
+        q = qh[seqs]
+        bt, cl = w.block_tables[seqs], w.context_lens[seqs]
+        B = int(np.minimum(cl, mcl).sum()) * Hkv * 2 * (hs + 4)
+        reps, t = 0, 0.0
+        while t < budget or reps == 0:
+            c0 = time.perf_counter()
+            oracle.paged_decode(q, kh, vh, bt, cl, w.scale, Hkv, bs, max_context_len=mcl, nthreads=nthreads)
+            t += time.perf_counter() - c0
+            reps += 1
+        return B * reps / t / 1e9, reps, t, B
+
+    all_seqs = np.arange(w.num_seqs)
+    v_all, r_all, t_all, _ = run(all_seqs, n_all, seconds)
+    few = all_seqs[:4]            # one thread: the first 4 sequences of the batch
+    v_one, r_one, t_one, b_one = run(few, 1, seconds / 2)
+    return {"value": round(v_all, 3), "unit": "GB/s", "cores": n_all, "kind": "oracle",
+            "sample": "the full decode step (all %d (seq,head) rows of the Llama-shaped batch) repeated %d times "
+                      "in %.1f s" % (w.num_seqs * w.num_heads, r_all, t_all),
+            "single_thread": {"value": round(v_one, 3), "unit": "GB/s", "cores": 1,
+                              "sample": "sequences 0-3 of the batch (%d effective KV bytes) repeated %d times in "
+                                        "%.1f s" % (b_one, r_one, t_one)},
+            "host": {"os_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+                     "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}}
+
+
+def _timed(fn, n, dev_sync=True):
+    """Mean duration of n back-to-back launches (fn(i) enqueues launch i),
+    from HIP events around them on the current stream, in microseconds."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def _fill_device(w, kc, vc, gen, chunk=65536):
+    """Fill the caches with the workload's rows: its slots, K/V drawn N(0,1) on
+    the device from `gen` (the timing does not depend on the values), with its
+    outlier channels scaled x20."""
+    import torch
+    from int8_paged_kv_amd import q8_cache_write
+    dev = kc.device
+    slots = w.fill_slots()
+    ok = None if w.outlier_k is None else torch.from_numpy(w.outlier_k).to(dev)
+    ov = None if w.outlier_v is None else torch.from_numpy(w.outlier_v).to(dev)
+    for st in range(0, slots.shape[0], chunk):
+        sl = slots[st:st + chunk]
+        T = sl.shape[0]
+        k = torch.randn((T, w.num_kv_heads, w.head_size), generator=gen, device=dev, dtype=torch.float32)
+        v = torch.randn((T, w.num_kv_heads, w.head_size), generator=gen, device=dev, dtype=torch.float32)
+        if ok is not None:
+            k[:, ok] *= 20.0
+        if ov is not None:
+            v[:, ov] *= 20.0
+        sld = torch.from_numpy(sl.view(np.int32)).to(dev)
+        q8_cache_write(k, v, kc, vc, sld, w.num_kv_heads, w.head_size, w.block_size)
+        del k, v
+
+
+def bench_long_context(dev):
+    """Long-context decode: S=8 H=64 Hkv=8 hs=128 bs=32, 32768 positions each,
+    fragmented tables (seed 3); two cache copies rotated (1.1 GB of K/V each)."""
+    import torch
+    from int8_paged_kv_amd import q8_paged_decode, q8_paged_decode_workspace_bytes
+    from int8_paged_kv_amd import workloads as wl
+    w = wl.long_context()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    copies = []
+    for _ in range(2):
+        kh, vh = w.empty_caches()
+        kc = torch.from_numpy(kh.view(np.int32)).to(dev)
+        vc = torch.from_numpy(vh.view(np.int32)).to(dev)
+        del kh, vh
+        _fill_device(w, kc, vc, gen)
+        copies.append((kc, vc))
+    q = torch.from_numpy(w.q()).to(dev)
+    bt = torch.from_numpy(w.block_tables.view(np.int32)).to(dev)
+    cl = torch.from_numpy(w.context_lens.view(np.int32)).to(dev)
+    ws = torch.zeros(max(1, q8_paged_decode_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size,
+                                                            w.block_size, w.max_context_len)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((w.num_seqs, w.num_heads, w.head_size), dtype=torch.float32, device=dev)
+
+    def run(i):
+        kc, vc = copies[i % 2]
+        q8_paged_decode(q, kc, vc, bt, cl, w.scale, w.num_kv_heads, w.block_size,
+                        max_context_len=w.max_context_len, out=out, workspace=ws)
+
+    for i in range(6):
+        run(i)
+    us = _timed(run, 40)
+    B = w.effective_kv_bytes()
+    del copies
+    return {"workload": w.description + " (seed 3)", "us_mean": round(us, 2), "effective_kv_bytes": B,
+            "effective_GBps": round(B / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(B / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "seq_heads_per_s": round(w.num_seqs * w.num_heads / (us * 1e-6), 1),
+            "traffic": read_leg_traffic("long_context"),
+            "note": "q8_paged_decode, back-to-back launches over two rotated cache copies; K/V values drawn on "
+                    "the device (same shapes, distribution and outlier channels; the full-size parity test "
+                    "uses the host generator)"}
+
+
+def bench_mha256(dev):
+    """MHA head_size 256 (seed 4): the decode (S=128, H=Hkv=16, bs=16,
+    L~U[1024,2048], 1.68 GB of K/V) and the 4096-token write with 10% pad
+    slots and 0.5% all-zero vectors."""
+    import torch
+    from int8_paged_kv_amd import q8_cache_write, q8_paged_decode, q8_paged_decode_workspace_bytes
+    from int8_paged_kv_amd import workloads as wl
+    w = wl.mha256()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    kh, vh = w.empty_caches()
+    kc = torch.from_numpy(kh.view(np.int32)).to(dev)
+    vc = torch.from_numpy(vh.view(np.int32)).to(dev)
+    del kh, vh
+    _fill_device(w, kc, vc, gen)
+    q = torch.from_numpy(w.q()).to(dev)
+    bt = torch.from_numpy(w.block_tables.view(np.int32)).to(dev)
+    cl = torch.from_numpy(w.context_lens.view(np.int32)).to(dev)
+    ws = torch.zeros(max(1, q8_paged_decode_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size,
+                                                            w.block_size, w.max_context_len)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((w.num_seqs, w.num_heads, w.head_size), dtype=torch.float32, device=dev)
+
+    def run(i):
+        q8_paged_decode(q, kc, vc, bt, cl, w.scale, w.num_kv_heads, w.block_size,
+                        max_context_len=w.max_context_len, out=out, workspace=ws)
+
+    for i in range(4):
+        run(i)
+    us = _timed(run, 20)
+    B = w.effective_kv_bytes()
+    dec = {"workload": w.description + " (seed 4)", "us_mean": round(us, 2), "effective_kv_bytes": B,
+           "effective_GBps": round(B / (us * 1e-6) / 1e9, 1),
+           "frac_hbm_peak": round(B / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "seq_heads_per_s": round(w.num_seqs * w.num_heads / (us * 1e-6), 1),
+           "traffic": read_leg_traffic("mha256_decode"),
+           "note": "q8_paged_decode, back-to-back launches (1.68 GB of K/V per launch, far above the 256 MB "
+                   "Infinity Cache); K/V values drawn on the device"}
+    # the padded bulk write: four copies of its inputs rotated, so they come from HBM
+    slots, k, v = wl.mha256_write(w)
+    T = slots.shape[0]
+    sl = torch.from_numpy(slots.view(np.int32)).to(dev)
+    ins = [(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)) for _ in range(4)]
+
+    def write(i):
+        kk, vv = ins[i % 4]
+        q8_cache_write(kk, vv, kc, vc, sl, w.num_kv_heads, w.head_size, w.block_size)
+
+    for i in range(4):
+        write(i)
+    usw = _timed(write, 40)
+    n_real = int(np.count_nonzero(slots != wl.PAD_SLOT))
+    Bw = n_real * w.num_kv_heads * (2 * w.head_size * 4 + 2 * (w.head_size + 4)) + 4 * T
+    wr = {"workload": "4096-token write, MHA head_size 256, 10% pad slots, 0.5% zero vectors (seed 4)",
+          "us_mean": round(usw, 2), "tokens": T, "pad_tokens": T - n_real, "algorithmic_bytes": Bw,
+          "GBps": round(Bw / (usw * 1e-6) / 1e9, 1), "frac_hbm_peak": round(Bw / (usw * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+          "traffic": read_leg_traffic("mha256_write"),
+          "note": "q8_cache_write; algorithmic bytes = f32 K and V of the non-pad tokens read, their packed rows "
+                  "written, and the slots"}
+    del kc, vc, ins
+    return dec, wr
+
+
+def bench_ceiling(dev, w, layers, bt):
+    """The practical HBM ceiling beside the 8 TB/s peak: a streaming read of
+    2 GiB, and the Llama step's own K/V tiles (every (block, kv head) run of
+    16 rows the batch attends, in the decode's order) read without any
+    arithmetic by the measurement kernels of libq8kv_bench.so."""
+    import ctypes
+    import torch
+    from int8_paged_kv_amd import build as pkg_build
+    if not os.path.exists(pkg_build.BENCH_LIB):
+        return None
+    lib = ctypes.CDLL(pkg_build.BENCH_LIB)
+    lib.q8b_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32,
+                                    ctypes.c_void_p]
+    lib.q8b_tile_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
+                                    ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    grid = 2048
+    sink = torch.zeros(grid * 4, dtype=torch.int32, device=dev)
+    nbytes = 2 << 30
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(2)]
+
+    def sread(i):
+        rc = lib.q8b_stream_read(bufs[i % 2].data_ptr(), nbytes, sink.data_ptr(), grid, stream)
+        if rc:
+            raise RuntimeError("q8b_stream_read: hipError %d" % rc)
+
+    for i in range(4):
+        sread(i)
+    us_s = _timed(sread, 20)
+    del bufs
+    # tiles of the Llama batch: (sequence, block, kv head), kv head fastest
+    wpt = w.head_size // 4 + 1
+    tile_u4 = w.block_size * wpt // 4
+    offs = []
+    for s_, L in enumerate(w.context_lens):
+        for j in range(-(-int(L) // w.block_size)):
+            phys = int(w.block_tables[s_, j])
+            for h in range(w.num_kv_heads):
+                offs.append((phys * w.num_kv_heads + h) * tile_u4)
+    tiles = torch.from_numpy(np.asarray(offs, dtype=np.int64)).to(dev)
+    nt = len(offs)
+
+    def gather(i):
+        kc, vc = layers[i % len(layers)]
+        rc = lib.q8b_tile_gather(kc.data_ptr(), vc.data_ptr(), tiles.data_ptr(), nt, tile_u4, sink.data_ptr(),
+                                 grid // 4 * 2, stream)
+        if rc:
+            raise RuntimeError("q8b_tile_gather: hipError %d" % rc)
+
+    for i in range(4):
+        gather(i)
+    us_g = _timed(gather, 40)
+    Bt = nt * tile_u4 * 16 * 2
+    return {"stream_read_GBps": round(nbytes / (us_s * 1e-6) / 1e9, 1), "stream_read_bytes": nbytes,
+            "stream_read_us": round(us_s, 2),
+            "tile_gather_GBps": round(Bt / (us_g * 1e-6) / 1e9, 1), "tile_gather_bytes": Bt,
+            "tile_gather_us": round(us_g, 2), "tile_gather_waves": grid // 4 * 2 * 4,
+            "note": "libq8kv_bench.so: 16-byte nontemporal loads folded into one word per wave; the tile gather "
+                    "reads the Llama step's %d K and V tiles of %d bytes (whole tiles, partial last blocks "
+                    "included) from the same rotated layer caches the step reads, with no arithmetic"
+                    % (nt, tile_u4 * 16)}
+
+
+def read_leg_traffic(leg: str):
+    """HBM bytes per launch of a bench leg's kernel from the committed all-kernel
+    counter summary, or None when absent or taken on different kernel sources."""
+    try:
+        kv = {}
+        with open(os.path.join(ROOT, "profiles", "bench_legs_traffic.txt")) as f:
+            for line in f:
+                if ":" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_sources_sha256_16") != kernel_sources_digest():
+            return None
+        return float(kv[leg + "_hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -177,16 +455,23 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps, wall clock ----
+    # ---- timed region: exactly K steps, wall clock, and HIP events on the
+    # launch stream around the same K launches (their mean is the kernel's
+    # average launch duration, back to back, as rocprofv3 sees it) ----
+    ev_region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t0 = time.perf_counter()
+    ev_region[0].record()
     for i in range(args.steps):
         step(i)
+    ev_region[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    region_us = ev_region[0].elapsed_time(ev_region[1]) * 1e3 / args.steps
 
     B = w.effective_kv_bytes()
-    # ---- per-launch durations with HIP events on the launch stream ----
+    # ---- per-launch durations with HIP events around each launch (their
+    # spread; each also holds the launch's own dispatch latency) ----
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
@@ -228,9 +513,15 @@ def main():
             evr[i][1].record()
         torch.cuda.synchronize()
         tr = np.array([e[0].elapsed_time(e[1]) for e in evr]) * 1e3
+        Bd = B     # distinct K/V bytes: each sequence's longest row reads its whole context once
         multi = {"rows_per_seq": nbr, "us_mean": round(float(tr.mean()), 2),
-                 "effective_kv_bytes": Br, "effective_GBps": round(Br / (float(tr.mean()) * 1e-6) / 1e9, 1),
-                 "note": "bytes counted per row over its own causal prefix; the rows of a sequence share the reads"}
+                 "distinct_kv_bytes": Bd, "distinct_GBps": round(Bd / (float(tr.mean()) * 1e-6) / 1e9, 1),
+                 "frac_hbm_peak": round(Bd / (float(tr.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                 "per_row_kv_bytes": Br,
+                 "per_row_rate_GBps": round(Br / (float(tr.mean()) * 1e-6) / 1e9, 1),
+                 "note": "the roofline figure is distinct_GBps: the K/V rows each sequence holds, read once "
+                         "for all its rows; per_row_rate counts every row's prefix separately (the rows share "
+                         "the reads), so it is not a bandwidth"}
 
     # ---- the same step over an f32 paged cache (4 bytes per element, no scale word) ----
     f32ref = None
@@ -460,12 +751,20 @@ def main():
         hot = {"decode_us_median": float(np.median(th)),
                "effective_GBps": w.effective_kv_bytes() / (np.median(th) * 1e-6) / 1e9}
 
+    # ---- the other configurations' decodes and the padded bulk write, and the
+    # practical HBM ceiling of the decode's access pattern ----
+    long_leg = mha_legs = ceiling = None
+    if not args.no_reference:
+        long_leg = bench_long_context(dev)
+        mha_legs = bench_mha256(dev)
+        ceiling = bench_ceiling(dev, w, layers, bt)
+
     # algorithmic bytes of the step's cache write: f32 K and V read, packed rows written
     Bw = int(step_slots.size) * Hkv * (2 * hs * 4 + 2 * (hs + 4)) + 4 * int(step_slots.size)
     step_s = ms_per_step * 1e-3
     value = B / step_s / 1e9
     dec_mean = float(t_dec.mean())
-    achieved = (B + Bw) / (dec_mean * 1e-6) / 1e9
+    achieved = (B + Bw) / (region_us * 1e-6) / 1e9
     digest = kernel_sources_digest()
     traffic = read_traffic(digest)
 
@@ -478,23 +777,14 @@ def main():
         for slots, k, v in fill_host:
             oracle.cache_write(k, v, kh, vh, slots, Hkv, hs, w.block_size)
         oracle.cache_write(step_k, step_v, kh, vh, step_slots, Hkv, hs, w.block_size)
-        nthreads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16") or 16))
         qh = w.q()
-        reps, t_cpu = 0, 0.0
-        ref = None
-        while t_cpu < args.cpu_seconds or reps == 0:
-            c0 = time.perf_counter()
-            ref = oracle.paged_decode(qh, kh, vh, w.block_tables, w.context_lens, w.scale, Hkv, w.block_size,
-                                      max_context_len=mcl, nthreads=nthreads)
-            t_cpu += time.perf_counter() - c0
-            reps += 1
-        cpu = {"value": B * reps / t_cpu / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-               "sample": "the full decode step (all 2048 (seq,head) rows, binary64 plain definition) "
-                         "repeated %d times in %.1f s" % (reps, t_cpu)}
+        ref = oracle.paged_decode(qh, kh, vh, w.block_tables, w.context_lens, w.scale, Hkv, w.block_size,
+                                  max_context_len=mcl, nthreads=cpu_threads())
         got = out.cpu().numpy()
         err = np.abs(got.astype(np.float64) - ref)
         parity = {"max_abs_err": float(err.max()),
                   "within_1e-4": bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))}
+        cpu = cpu_baseline(oracle, w, qh, kh, vh, mcl, args.cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -517,20 +807,32 @@ def main():
                    "kv_storage": "int8 codes + f32 per-token scale"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(S * H / step_s, 1),
-        "step_launch": {"us_mean": round(dec_mean, 2), "us_median": round(float(np.median(t_dec)), 2),
-                   "us_p10": round(float(np.percentile(t_dec, 10)), 2),
-                   "us_p90": round(float(np.percentile(t_dec, 90)), 2),
-                   "effective_GBps": round(achieved, 1),
-                   "seq_heads_per_s": round(S * H / (dec_mean * 1e-6), 1)},
+        "step_launch": {"us_mean_back_to_back": round(region_us, 2),
+                        "effective_GBps": round(B / (region_us * 1e-6) / 1e9, 1),
+                        "seq_heads_per_s": round(S * H / (region_us * 1e-6), 1),
+                        "note": "HIP events on the launch stream around the timed region's K launches; "
+                                "per_launch_events: an event pair around each launch (each also holds that "
+                                "launch's dispatch latency)",
+                        "per_launch_events": {"us_mean": round(dec_mean, 2),
+                                              "us_median": round(float(np.median(t_dec)), 2),
+                                              "us_p10": round(float(np.percentile(t_dec, 10)), 2),
+                                              "us_p90": round(float(np.percentile(t_dec, 90)), 2)}},
         "two_launch_reference": reference,
         "multi_row_decode": multi,
         "f32_cache_reference": f32ref,
         "norm_rope_step": normrope,
         "selected_step": selected,
+        "long_context": long_leg,
+        "mha256_decode": None if mha_legs is None else mha_legs[0],
+        "mha256_write": None if mha_legs is None else mha_legs[1],
+        "practical_ceiling": ceiling,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "q8_decode_step (one launch: decode_split_kernel, appending the step's tokens)",
-                     "algorithmic_bytes_per_launch": B + Bw},
+                     "algorithmic_bytes_per_launch": B + Bw,
+                     "launch_us": round(region_us, 2),
+                     "launch_us_source": "HIP events around the timed region's launches on the launch stream, "
+                                         "divided by their number"},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "hot_single_cache": hot,

@@ -25,6 +25,15 @@
  *     num_blocks, block-table rows holding valid ids for every block a
  *     sequence uses, finite inputs.  Breaking it is undefined behaviour.
  *   - head_size must be a multiple of 4 and at most 256 (the pages' maximum).
+ *   - Two environment variables, meant for tests, force the number of
+ *     persistent wavefronts the decodes split the batch over (otherwise:
+ *     as many as the device keeps resident for the kernel, at most 2048 for
+ *     the int8 decodes, and 2048 for the f32 decode): Q8KV_DECODE_WAVES (int8
+ *     decodes and the decode step) and Q8KV_F32_DECODE_WAVES (f32 decode),
+ *     each an integer from 1 to 2^20, read by every call.  The workspace
+ *     query reads the same variable, so a workspace sized under one setting
+ *     must be used under it.  Results do not depend on the setting beyond
+ *     f32 rounding.
  */
 #ifndef Q8KV_H
 #define Q8KV_H
@@ -62,8 +71,8 @@ typedef enum {
  *   value_cache  head_size/4 + 1], written at row (slot/block_size, h,
  *                slot%block_size) for every non-pad slot.
  *   slot_mapping u32 [num_tokens]; Q8_PAD_SLOT skips the token: nothing is
- *                written for it (its key/value rows may still be read, so
- *                they must be addressable).
+ *                read or written for it (as on the page, its key/value rows
+ *                are not touched).
  *
  * Rounding: every step is one IEEE binary32 operation with round-to-nearest,
  * and the round() of the page is round-half-even.  The output is bit-exact.
@@ -87,7 +96,7 @@ q8_status q8_cache_write(const float* key, uint32_t key_stride,
  * the split-context decode with a combine step follows the "attention.rs"
  * page.  max_positions is max_context_len in dense mode and vis_stride in
  * visible-list mode.  Returns 0 when no workspace is needed (every sequence
- * has at most 64 positions).  Pure host arithmetic; needs no GPU.
+ * has at most 32 positions).  Pure host arithmetic; needs no GPU.
  */
 size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
                                        uint32_t num_kv_heads, uint32_t head_size,

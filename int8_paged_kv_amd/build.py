@@ -16,6 +16,8 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libq8kv.so")
+# measurement kernels of the benchmark (the practical HBM ceiling), a library of their own
+BENCH_LIB = os.path.join(PKG, "libq8kv_bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -26,8 +28,8 @@ FLAGS = [
 ]
 
 
-def sources():
-    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+def sources(sub: str = "csrc"):
+    return sorted(glob.glob(os.path.join(PKG, sub, "*.hip")))
 
 
 def _run(cmd):
@@ -37,12 +39,18 @@ def _run(cmd):
 
 
 def build(verbose: bool = False, jobs: int = 0) -> str:
+    _build_lib(sources("csrc"), LIB, verbose, jobs)
+    _build_lib(sources("csrc_bench"), BENCH_LIB, verbose, jobs)
+    return LIB
+
+
+def _build_lib(srcs, lib_path: str, verbose: bool, jobs: int) -> None:
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
-    jobs = jobs or max(1, min(len(sources()), os.cpu_count() or 1, 16))
+    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 16))
     with tempfile.TemporaryDirectory(prefix="q8kv_build_") as tmpdir:
         cmds = []
         objs = []
-        for src in sources():
+        for src in srcs:
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
             objs.append(obj)
             cmds.append([HIPCC] + FLAGS + inc + ["-c", src, "-o", obj])
@@ -56,15 +64,14 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
                 raise RuntimeError("hipcc failed: %s\n%s" % (" ".join(c), out))
             if out.strip() and verbose:
                 print(out)
-        tmp = LIB + ".tmp%d" % os.getpid()
+        tmp = lib_path + ".tmp%d" % os.getpid()
         link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
         if verbose:
             print(" ".join(link), flush=True)
         rc, out = _run(link)
         if rc != 0:
             raise RuntimeError("hipcc link failed:\n" + out)
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, lib_path)
 
 
 if __name__ == "__main__":

@@ -55,7 +55,7 @@ size_t q8_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
                                        uint32_t block_size, uint32_t max_positions) {
     if (num_kv_heads == 0 || num_heads % num_kv_heads != 0) return 0;
     return q8kv::plan_decode(num_seqs, num_heads, num_kv_heads, head_size, block_size,
-                             max_positions).bytes;
+                             max_positions, q8kv::decode_wave_bound()).bytes;
 }
 
 }  // extern "C"
@@ -155,8 +155,9 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     if (!std::isfinite(scale)) return Q8_ERR_SHAPE;
     if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return Q8_ERR_UNSUPPORTED;   // rows are written as 16-byte stores
     // Grid limits: one wavefront per workgroup in 1-D grids.
+    // Workspace need at the wave bound; a launch uses at most that many waves.
     const q8kv::DecodePlan p = q8kv::plan_decode(num_seqs, static_cast<uint32_t>(num_pairs), num_kv_heads, head_size,
-                                                 block_size, max_pos);
+                                                 block_size, max_pos, q8kv::decode_wave_bound());
     if (p.num_waves > 0x7FFFFFFFull || static_cast<uint64_t>(num_seqs) * num_pairs > 0x7FFFFFFFull)
         return Q8_ERR_UNSUPPORTED;
     if (p.bytes > 0 && static_scratch) {
@@ -179,10 +180,7 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     a.context_lens = context_lens;
     a.visible_pos = visible_pos;
     a.num_visible = num_visible;
-    char* ws = static_cast<char*>(workspace);
-    a.counters = p.bytes ? reinterpret_cast<uint32_t*>(ws + p.counters_offset) : nullptr;
-    a.part_acc = p.bytes ? reinterpret_cast<float*>(ws + p.acc_offset) : nullptr;
-    a.part_ml = p.bytes ? reinterpret_cast<float*>(ws + p.ml_offset) : nullptr;
+    a.workspace = p.bytes ? workspace : nullptr;
     a.q_stride = q_stride;
     a.max_num_blocks_per_seq = max_num_blocks_per_seq;
     a.max_context_len = max_context_len;
@@ -205,7 +203,7 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
         a.key_cache_w = app->key_cache;
         a.value_cache_w = app->value_cache;
     }
-    const hipError_t e = q8kv::launch_decode(a, p, static_cast<hipStream_t>(stream));
+    const hipError_t e = q8kv::launch_decode(a, max_pos, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 

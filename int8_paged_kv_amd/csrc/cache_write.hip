@@ -2,8 +2,7 @@
 //
 // Follows the "reshape_and_cache_q8.comp" page, main(), for each (token, kv
 // head) and for K then V (the quantizer is in q8_pack.h).  A pad slot
-// (0xFFFFFFFF) skips the token: nothing is written for it (its source rows
-// may be read).
+// (0xFFFFFFFF) skips the token: nothing is read or written for it.
 //
 // MI355X mapping: one wavefront per (token, kv head), or in large writes per
 // group of consecutive ones whose loads are all in flight together.  When
@@ -23,9 +22,9 @@ __device__ __forceinline__ float4 load4(const float* p, bool vec4) {
     return make_float4(p[0], p[1], p[2], p[3]);
 }
 
-// NP consecutive (token, kv head) pairs per wave: every pair's rows and slot
-// are loaded before any is packed, so a wave keeps NP rows in flight (large
-// writes); NP = 1 for small ones, where the grid is short anyway.
+// NP consecutive (token, kv head) pairs per wave: every pair's slot, then every
+// non-pad pair's rows, are loaded before any is packed, so a wave keeps NP rows
+// in flight (large writes); NP = 1 for small ones, where the grid is short anyway.
 template <bool HALF, int NP>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool vec4) {
     const uint32_t lane = threadIdx.x & (kWave - 1);
@@ -35,19 +34,26 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool
     const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
     if (first >= pairs) return;
     const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
-    // The source rows are loaded together with the slots (one memory round
-    // trip); a pad token's rows may thus be read, but nothing is written for it.
+    // The slots come first (scalar loads of the wave's tokens); then only the
+    // rows of non-pad tokens are loaded, all of them before any is packed.
     float4 x0[NP], x1[NP];
-    uint32_t slot[NP], head[NP];
+    uint32_t slot[NP], head[NP], tok[NP];
     uint32_t t = static_cast<uint32_t>(first / a.num_kv_heads);
     uint32_t h = static_cast<uint32_t>(first - static_cast<uint64_t>(t) * a.num_kv_heads);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-        x0[i] = x1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         slot[i] = kPadSlot;
         if (i > 0 && ++h == a.num_kv_heads) h = 0, ++t;
         head[i] = h;
-        if (first + i >= pairs) continue;            // wave-uniform
+        tok[i] = t;
+        if (first + i < pairs) slot[i] = a.slot_mapping[t];     // wave-uniform
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        x0[i] = x1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (slot[i] == kPadSlot) continue;           // wave-uniform: nothing is read for a pad token
+        t = tok[i];
+        h = head[i];
         const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
         const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
         if (HALF) {
@@ -57,7 +63,6 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool
             x0[i] = load4(ksrc + 4 * lane, vec4);
             x1[i] = load4(vsrc + 4 * lane, vec4);
         }
-        slot[i] = a.slot_mapping[t];
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {

@@ -1,26 +1,38 @@
 // Decode planning and dispatch: the split plan shared by the workspace query
-// and the launch, and the choice of split-kernel instantiation.  The kernel
-// itself (and what it computes) is in decode_kernel.h.
+// and the launch, the choice of split-kernel instantiation, and the number of
+// persistent wavefronts the device keeps resident for it.  The kernel itself
+// (and what it computes) is in decode_kernel.h.
 #include <stdlib.h>
+
+#include <mutex>
 
 #include "decode_split.h"
 
 namespace q8kv {
 
+uint64_t decode_wave_override() {
+    // Q8KV_DECODE_WAVES (documented in q8kv.h) forces the persistent wave
+    // count; tests use it to move the boundaries between wave ranges.
+    if (const char* e = getenv("Q8KV_DECODE_WAVES")) {
+        const long v = atol(e);
+        if (v >= 1 && v <= (1L << 20)) return static_cast<uint64_t>(v);
+    }
+    return 0;
+}
+
+uint64_t decode_wave_bound() {
+    const uint64_t o = decode_wave_override();
+    return o ? o : kMaxDecodeWaves;
+}
+
 DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
-                       uint32_t head_size, uint32_t block_size, uint32_t max_positions) {
+                       uint32_t head_size, uint32_t block_size, uint32_t max_positions, uint64_t target) {
     DecodePlan p{};
     const uint32_t n_rep = num_kv_heads ? num_heads / num_kv_heads : 1;
     p.group = n_rep > 4 ? 8 : 4;
     p.num_groups = (n_rep + p.group - 1) / p.group;
     (void)block_size;
-    // Persistent wavefronts: 4 per compute unit of an MI355X (256 CUs),
-    // shared evenly by the row groups.
-    uint64_t target = kDecodeWaves;
-    if (const char* e = getenv("Q8KV_DECODE_WAVES")) {
-        const long v = atol(e);
-        if (v >= 1 && v <= (1L << 20)) target = static_cast<uint64_t>(v);
-    }
+    // The persistent wavefronts are shared evenly by the row groups.
     const uint64_t num_rg = static_cast<uint64_t>(num_kv_heads) * p.num_groups;
     uint64_t per = num_rg ? target / num_rg : 1;
     if (per < 1) per = 1;
@@ -31,30 +43,74 @@ DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_he
     // partial records.  A sequence of at most one chunk always lies in a
     // single wave's range, so then no workspace is needed at all.
     // A record holds the padded head size (code words per row rounded up to
-    // 16, 32, 48 or 64) for every query head of the group.
+    // 16, 32, 48 or 64) for every query head of the group.  The need grows
+    // with the wave count, so a workspace sized for the bound serves every
+    // launch below it.
     const uint32_t hs4 = head_size / 4;
     const uint32_t hs4p = hs4 <= 16 ? 16 : hs4 <= 32 ? 32 : hs4 <= 48 ? 48 : 64;
     const uint64_t slots = num_rg * p.recs_per_rg * p.group;
     p.counters_offset = 0;
     p.acc_offset = (num_rg * num_seqs * sizeof(uint32_t) + 255) / 256 * 256;
     p.ml_offset = p.acc_offset + (slots * 4 * hs4p * sizeof(float) + 255) / 256 * 256;
-    p.bytes = max_positions > static_cast<uint32_t>(kChunk) ? p.ml_offset + slots * 2 * sizeof(float) : 0;
+    // (a chunk holds 32 or 64 positions: the smaller bounds when one suffices)
+    p.bytes = max_positions > 32u ? p.ml_offset + slots * 2 * sizeof(float) : 0;
     return p;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+namespace {
+
+// Workgroups of one kernel resident per compute unit (LDS, registers and
+// its waves-per-EU bound decide it), and the device's compute units; both
+// cached per (kernel, device).
+struct Residency {
+    const void* fn;
+    int device;
+    uint32_t waves;     // resident wavefronts on the whole device
+    uint32_t per_cu;    // resident workgroups per compute unit
+};
+std::mutex g_res_mu;
+Residency g_res[64];
+int g_res_n = 0;
+
+hipError_t resident_waves(const void* fn, uint32_t* waves, uint32_t* per_cu) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_res_mu);
+    for (int i = 0; i < g_res_n; ++i)
+        if (g_res[i].fn == fn && g_res[i].device == dev) {
+            *waves = g_res[i].waves;
+            *per_cu = g_res[i].per_cu;
+            return hipSuccess;
+        }
+    int blocks = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kWave * kWavesPerGroup, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (blocks < 1) blocks = 1;
+    if (cus < 1) cus = 1;
+    const uint64_t w = static_cast<uint64_t>(blocks) * kWavesPerGroup * static_cast<uint64_t>(cus);
+    *waves = static_cast<uint32_t>(w < kMaxDecodeWaves ? w : kMaxDecodeWaves);
+    *per_cu = static_cast<uint32_t>(blocks);
+    if (g_res_n < 64) g_res[g_res_n++] = Residency{fn, dev, *waves, *per_cu};
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_t stream) {
     const bool vis = a.visible_pos != nullptr;
     const uint32_t hs4 = a.head_size / 4;
     const uint32_t wpt = hs4 + 1;
+    // Query heads per kv head: (row, head) pairs in multi-row decode.
+    const uint32_t num_pairs = a.num_heads * (a.rows_per_seq > 1 ? a.rows_per_seq : 1u);
+    const uint32_t group = num_pairs / a.num_kv_heads > 4 ? 8 : 4;
+    const uint32_t hs4p = hs4 <= 16 ? 16 : hs4 <= 32 ? 32 : hs4 <= 48 ? 48 : 64;
+    const uint32_t ch = static_cast<uint32_t>(decode_chunk(static_cast<int>(hs4p), group == 8 ? 2 : 1));
     SplitConsts c{};
-    c.waves_per_rg = p.waves_per_rg;
-    c.num_rg = a.num_kv_heads * p.num_groups;
-    c.group = p.group;
-    c.num_groups = p.num_groups;
-    c.recs_per_rg = p.recs_per_rg;
-    c.seg_rows = a.block_size < static_cast<uint32_t>(kChunk) ? a.block_size : kChunk;
-    const bool shape_ok = a.block_size % 4 == 0 &&
-                          (kChunk % a.block_size == 0 || a.block_size % kChunk == 0);
+    c.seg_rows = a.block_size < ch ? a.block_size : ch;
+    const bool shape_ok = a.block_size % 4 == 0 && (ch % a.block_size == 0 || a.block_size % ch == 0);
     const bool align_ok = reinterpret_cast<uintptr_t>(a.key_cache) % 16 == 0 &&
                           reinterpret_cast<uintptr_t>(a.value_cache) % 16 == 0;
     c.tiled_ok = shape_ok && align_ok;
@@ -62,19 +118,48 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s
     c.seg_u4 = c.seg_rows * wpt / 4;
     if (c.seg_u4 == 0) c.seg_u4 = 1;
     c.seg_magic = static_cast<uint32_t>((0x100000000ull + c.seg_u4 - 1) / c.seg_u4);
+    const bool t = c.tiled_ok != 0;
+    // Segment layouts need whole tiles per segment: blocks no longer than a chunk.
+    const uint32_t seg_whole = a.block_size <= ch ? c.seg_rows : 0u;
+    const void* fn;
+    if (hs4 <= 16) fn = split_kernel_hs16(vis, t, hs4 == 16, group, seg_whole);
+    else if (hs4 <= 32) fn = split_kernel_hs32(vis, t, hs4 == 32, group, seg_whole);
+    else if (hs4 <= 48) fn = split_kernel_hs48(vis, t, hs4 == 48, group, seg_whole);
+    else fn = split_kernel_hs64(vis, t, hs4 == 64, group, seg_whole);
+    // As many persistent wavefronts as the device keeps resident for this
+    // kernel, at most the bound the workspace was sized for.
+    uint64_t target = decode_wave_override();
+    uint32_t per_cu = 1;
+    if (!target) {
+        uint32_t w = 0;
+        const hipError_t e = resident_waves(fn, &w, &per_cu);
+        if (e != hipSuccess) return e;
+        target = w;
+    }
+    const DecodePlan p = plan_decode(a.num_seqs, num_pairs, a.num_kv_heads, a.head_size, a.block_size,
+                                     max_positions, target);
+    c.waves_per_rg = p.waves_per_rg;
+    c.num_rg = a.num_kv_heads * p.num_groups;
+    c.group = p.group;
+    c.num_groups = p.num_groups;
+    c.recs_per_rg = p.recs_per_rg;
+    // Two resident workgroups per CU with the whole grid resident: the second
+    // half of the grid is each CU's second workgroup (smaller shares).
+    c.young_from = per_cu == 2 && !decode_wave_override() ? p.waves_per_rg / 2 : p.waves_per_rg;
+    DecodeArgs ka = a;
+    if (p.bytes) {
+        char* ws = static_cast<char*>(a.workspace);
+        ka.counters = reinterpret_cast<uint32_t*>(ws + p.counters_offset);
+        ka.part_acc = reinterpret_cast<float*>(ws + p.acc_offset);
+        ka.part_ml = reinterpret_cast<float*>(ws + p.ml_offset);
+    }
     // With no block table or no blocks every sequence attends nothing
     // (positions are capped by the table); the kernel then only writes zeros.
-    const uint32_t nbm1 = a.num_blocks ? a.num_blocks - 1 : 0;
-    {
-        const dim3 grid(static_cast<uint32_t>((p.num_waves + kWavesPerGroup - 1) / kWavesPerGroup));
-        hipError_t err;
-        const bool t = c.tiled_ok != 0;
-        if (hs4 <= 16) err = launch_split_hs16(a, c, nbm1, grid, stream, vis, t, hs4 == 16);
-        else if (hs4 <= 32) err = launch_split_hs32(a, c, nbm1, grid, stream, vis, t, hs4 == 32);
-        else if (hs4 <= 48) err = launch_split_hs48(a, c, nbm1, grid, stream, vis, t, hs4 == 48);
-        else err = launch_split_hs64(a, c, nbm1, grid, stream, vis, t, hs4 == 64);
-        if (err != hipSuccess) return err;
-    }
+    uint32_t nbm1 = a.num_blocks ? a.num_blocks - 1 : 0;
+    void* args[] = {&ka, &c, &nbm1};
+    const dim3 grid(static_cast<uint32_t>((p.num_waves + kWavesPerGroup - 1) / kWavesPerGroup));
+    const hipError_t e = hipLaunchKernel(fn, grid, dim3(kWave * kWavesPerGroup), args, 0, stream);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -4,10 +4,9 @@
 
 namespace q8kv {
 
-hipError_t launch_split_hs32(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
-                             bool vis, bool tiled, bool exact) {
-    return exact ? launch_split_g<32, true>(a, c, nbm1, grid, st, vis, tiled)
-                 : launch_split_g<32, false>(a, c, nbm1, grid, st, vis, tiled);
+const void* split_kernel_hs32(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows) {
+    return exact ? split_kernel_g<32, true>(vis, tiled, group, seg_rows)
+                 : split_kernel_g<32, false>(vis, tiled, group, seg_rows);
 }
 
 }  // namespace q8kv

@@ -59,12 +59,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kDigitBias = 0x80808080u;
 
-// Cost units that split a row group's work evenly among its waves (per-wave
-// stamps on the Llama-shaped batch: a chunk costs about 2.6 us of wave time, a
-// sequence's start about 1.8 times that: its q digits, the output or partial
-// record of the previous sequence, the counter round trip).
+// Cost units that split a row group's work evenly among its waves: a chunk,
+// and a sequence's start (its q digits, the output or partial record of the
+// previous sequence, the append of the step's new row).  Per-wave stamps on
+// the Llama-shaped batch: with 64-position chunks a start costs about 1.8
+// chunks of wave time, with 32-position chunks about one chunk.
 constexpr uint32_t kCostChunk = 4;
-constexpr uint32_t kCostSeq = 7;
+constexpr uint32_t cost_seq(int ch) { return ch == 64 ? 7u : 4u; }
 
 __device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
@@ -126,9 +127,9 @@ __device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s
     return n;
 }
 
-template <bool VIS>
+template <bool VIS, int CH>
 __device__ __forceinline__ uint32_t chunks_of(const DecodeArgs& a, uint32_t s) {
-    return (positions_of<VIS>(a, s) + kChunk - 1) / kChunk;
+    return (positions_of<VIS>(a, s) + CH - 1) / CH;
 }
 
 template <bool VIS>
@@ -201,13 +202,13 @@ __device__ void zero_rows(const DecodeArgs& a, uint32_t lane, uint32_t s_begin, 
 // Chunk sequence of one row group: the chunks of sequence 0, then sequence 1,
 // ...  Wave-uniform results.
 //   chunk_totals: total chunk count C and the chunks of sequences before s.
-template <bool VIS>
+template <bool VIS, int CH>
 __device__ void chunk_totals(const DecodeArgs& a, uint32_t lane, uint32_t s, uint32_t& total, uint32_t& before) {
     total = 0;
     before = 0;
     for (uint32_t b = 0; b < a.num_seqs; b += kWave) {
         const uint32_t t = b + lane;
-        const uint32_t nc = t < a.num_seqs ? chunks_of<VIS>(a, t) : 0u;
+        const uint32_t nc = t < a.num_seqs ? chunks_of<VIS, CH>(a, t) : 0u;
         const uint32_t incl = wave_incl_scan(nc, lane);
         const uint32_t wt = lane_value(incl, kWave - 1);
         if (s >= b + kWave) before += wt;
@@ -217,14 +218,14 @@ __device__ void chunk_totals(const DecodeArgs& a, uint32_t lane, uint32_t s, uin
 }
 
 //   locate_chunk: the sequence holding chunk x (x < C) and the chunks before it.
-template <bool VIS>
+template <bool VIS, int CH>
 __device__ void locate_chunk(const DecodeArgs& a, uint32_t lane, uint32_t x, uint32_t& row, uint32_t& before) {
     uint32_t base = 0;
     row = a.num_seqs;
     before = 0;
     for (uint32_t b = 0; b < a.num_seqs; b += kWave) {
         const uint32_t t = b + lane;
-        const uint32_t nc = t < a.num_seqs ? chunks_of<VIS>(a, t) : 0u;
+        const uint32_t nc = t < a.num_seqs ? chunks_of<VIS, CH>(a, t) : 0u;
         const uint32_t incl = wave_incl_scan(nc, lane);
         const uint32_t wt = lane_value(incl, kWave - 1);
         if (x < base + wt) {
@@ -238,11 +239,31 @@ __device__ void locate_chunk(const DecodeArgs& a, uint32_t lane, uint32_t x, uin
     }
 }
 
-// Wave (of the W covering the C cost units of a row group) whose range holds
-// unit x: wave j covers [floor(j*C/W), floor((j+1)*C/W)).
-__device__ __forceinline__ uint32_t wave_of_chunk(uint32_t x, uint32_t C, uint32_t W) {
-    return static_cast<uint32_t>(((static_cast<uint64_t>(x) + 1) * W - 1) / C);
-}
+// Shares of a row group's U cost units among its W waves.  Waves j < H weigh
+// kShareOld and the others kShareYoung: with two workgroups per compute unit,
+// the second half of the grid is the second workgroup on each CU, whose
+// waves start behind the first ones (their first loads queue behind those
+// waves' tile loads) and are issued second on their SIMDs; per-wave stamps
+// show them finishing about 7% later on equal shares.  Wave j covers units
+// [floor(P(j)*U/T), floor(P(j+1)*U/T)) with P(j) = kShareOld*min(j, H) +
+// kShareYoung*max(j - H, 0) and T = P(W); H >= W gives equal shares.
+constexpr uint32_t kShareOld = 23, kShareYoung = 21;
+struct Shares {
+    uint32_t W, H, U;
+    uint64_t T;
+    __device__ __forceinline__ uint64_t P(uint32_t j) const {
+        return static_cast<uint64_t>(kShareOld) * min(j, H) + static_cast<uint64_t>(kShareYoung) * (j > H ? j - H : 0u);
+    }
+    __device__ __forceinline__ uint32_t bound(uint32_t j) const { return static_cast<uint32_t>(P(j) * U / T); }
+    // the wave whose range holds unit x: the largest j with bound(j) <= x
+    __device__ __forceinline__ uint32_t wave_of(uint32_t x) const {
+        const uint64_t A = (static_cast<uint64_t>(x) + 1) * T;
+        const uint64_t oldU = static_cast<uint64_t>(kShareOld) * H * U;
+        const uint64_t j = A <= oldU ? (A - 1) / (static_cast<uint64_t>(kShareOld) * U)
+                                     : H + (A - oldU - 1) / (static_cast<uint64_t>(kShareYoung) * U);
+        return static_cast<uint32_t>(j < W - 1 ? j : W - 1);
+    }
+};
 
 // Split-kernel lane roles.  Lane l = 16*g + r.
 //   q.K^T (v_mfma_i32_16x16x64_i8): lane (r, g) supplies MFMA row r = (head
@@ -263,46 +284,54 @@ __device__ __forceinline__ uint32_t wave_of_chunk(uint32_t x, uint32_t C, uint32
 // each segment of a chunk fills whole 64-lane slots (SEGR*HS4P/256 of them)
 // plus SEGR/4 trailing 16-byte units: every full slot then loads from one
 // segment with a scalar base address and a fixed per-lane offset.
-template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED, int SEGR>
-__global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
+template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED, int SEGR, int CH>
+__global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 || CH == 32)) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
     constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
     constexpr int NCW = HS4P / 16;             // V code words per lane and row
     constexpr int G = 4 * NHS;
     constexpr uint64_t kRecFloats = static_cast<uint64_t>(NHS) * NCW * kWave * 4;   // floats per partial record (= G * 4 * HS4P)
     constexpr int QD = NKB * 64;               // padded q row length
     constexpr int WPT_MAX = HS4P + 1;
-    constexpr int NU = (kChunk * WPT_MAX + 4 * kWave - 1) / (4 * kWave);   // 16-byte slots per lane
-    // An exact head size makes a chunk 64*(HS4P+1) words: HS4P/4 full 16-byte
-    // slots per lane plus one 4-byte tail slot per lane.
-    constexpr int NF = EXACT ? HS4P / 4 : NU;
+    constexpr int NTG = CH / 16;               // 16-token column groups of a chunk
+    constexpr uint32_t kCostSeq = cost_seq(CH);
+    static_assert(CH == 32 || CH == 64, "chunk size");
+    constexpr int NU = (CH * WPT_MAX + 4 * kWave - 1) / (4 * kWave);   // 16-byte slots per lane
+    // An exact head size makes a chunk CH*(HS4P+1) words: CH*HS4P/256 full
+    // 16-byte slots per lane plus a 4-byte tail slot in CH lanes.
+    constexpr int NF = EXACT ? CH * HS4P / 256 : NU;
     constexpr bool FAST = SEGR > 0;
-    static_assert(!FAST || (EXACT && (SEGR * HS4P) % 256 == 0 && SEGR <= kChunk), "segment layout");
+    static_assert(!FAST || (EXACT && (SEGR * HS4P) % 256 == 0 && SEGR <= CH), "segment layout");
+    static_assert(!EXACT || (CH * HS4P) % 256 == 0, "exact layout");
     // Segment loads go straight to LDS (no register staging), double-buffered:
     // the next chunk lands in one buffer while the other is processed.  Two
     // buffers of K and V fit for up to 32 code words per row.
     constexpr bool DMA = FAST && HS4P <= 32;
     constexpr int NBUF = DMA ? 2 : 1;
-    constexpr int FSEG = FAST ? kChunk / SEGR : 1;          // segments per chunk
+    constexpr int FSEG = FAST ? CH / SEGR : 1;              // segments per chunk
     constexpr int FS = FAST ? SEGR * HS4P / 256 : 0;         // full slots per segment (FSEG * FS == NF)
     constexpr int FLO = FAST ? SEGR / 4 : 1;                 // trailing 16-byte units per segment
     constexpr int SEG_U4 = FAST ? SEGR * (HS4P + 1) / 4 : 1; // 16-byte units per segment
+    constexpr uint32_t NTAIL = FAST ? FSEG * FLO : 0;         // lanes holding the segments' trailing units (CH/4)
     struct Buf {
         u32x4 k[DMA ? 1 : NF], v[DMA ? 1 : NF];
         uint32_t kt, vt;        // EXACT generic layout: one 4-byte tail slot per lane
-        u32x4 k4, v4;           // FAST layout: the segments' trailing units (lanes 0-15)
+        u32x4 k4, v4;           // FAST layout: the segments' trailing units (lanes below NTAIL)
     };
 
     // Per-wavefront LDS regions: the wavefronts of a workgroup are independent.
-    __shared__ __align__(16) uint32_t sK_[kWavesPerGroup][NBUF][NU * 4 * kWave];   // also q-digit scratch at sequence changes
-    __shared__ __align__(16) uint32_t sV_[kWavesPerGroup][NBUF][NU * 4 * kWave];
-    __shared__ __align__(16) uint32_t sA_[kWavesPerGroup][NHS * 16 * 16];    // [set][head*4+digit][w]: weight digits
+    // Segment layouts fill a chunk's CH*(HS4P+1) words exactly; the others
+    // use whole 64-lane slots.
+    constexpr int BUFW = FAST ? CH * (HS4P + 1) : NU * 4 * kWave;
+    __shared__ __align__(16) uint32_t sK_[kWavesPerGroup][NBUF][BUFW];   // also q-digit scratch at sequence changes
+    __shared__ __align__(16) uint32_t sV_[kWavesPerGroup][NBUF][BUFW];
+    __shared__ __align__(16) uint32_t sA_[kWavesPerGroup][NHS * 16 * 16];    // [set][head*4+digit][w]: weight digits; q maxima
     __shared__ int sEq_[kWavesPerGroup][G];
     // q-digit scratch of its own (LDS-direct loads, one set of 4 heads: it fits
     // the budget there), so that a sequence change can form the new q digits
     // while the next chunk's loads are already in flight; elsewhere the next
     // chunk's buffer serves, before those loads are issued.
     constexpr bool QSCR = DMA && NHS == 1;
-    constexpr int QSCR_WORDS = NHS * NKB * 256 + (G * QD / (4 * kWave)) * kWave;
+    constexpr int QSCR_WORDS = NHS * NKB * 256;      // digits; the per-slot maxima go to sA
     __shared__ __align__(16) uint32_t sQs_[kWavesPerGroup][QSCR ? QSCR_WORDS : 1];
     const uint32_t wid = uniform(threadIdx.x / kWave);
     // sK/sV: the tiles of the chunk being processed; sKn/sVn: where the next
@@ -346,24 +375,32 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     if (one_window) {
         win_np = lane < a.num_seqs ? positions_of<VIS>(a, lane) : 0u;
         if ((append || a.rows_per_seq > 1) && lane < a.num_seqs) win_len = a.context_lens[lane];
-        win_nc = (win_np + kChunk - 1) / kChunk;
+        win_nc = (win_np + CH - 1) / CH;
         win_incl = wave_incl_scan(win_nc, lane);
         C = uniform(lane_value(win_incl, kWave - 1));
         const uint64_t ne = __ballot(win_np > 0);
         const uint32_t sne = static_cast<uint32_t>(__builtin_popcountll(ne));
         const uint64_t uw = static_cast<uint64_t>(kCostChunk) * C + static_cast<uint64_t>(kCostSeq) * sne;
-        weighted = uw >= static_cast<uint64_t>(kCostChunk + kCostSeq) * c.waves_per_rg && uw < (1ull << 31);
+        // every share, the smallest included, must span the widest gap
+        // between two chunks' cost indices
+        const Shares sh{c.waves_per_rg, min(c.young_from, c.waves_per_rg), 1u, 0u};
+        weighted = uw * kShareYoung >= static_cast<uint64_t>(kCostChunk + kCostSeq) * sh.P(c.waves_per_rg) &&
+                   uw < (1ull << 31);
         ua = weighted ? kCostChunk : 1u;
         U = weighted ? static_cast<uint32_t>(uw) : C;
         const uint64_t upto = lane == kWave - 1 ? ~0ull : (2ull << lane) - 1;
         win_cinc = ua * win_incl + (weighted ? kCostSeq * static_cast<uint32_t>(__builtin_popcountll(ne & upto)) : 0u);
     } else {
         uint32_t unused;
-        chunk_totals<VIS>(a, lane, 0, C, unused);
+        chunk_totals<VIS, CH>(a, lane, 0, C, unused);
         C = uniform(C);
         U = C;
     }
     const uint32_t W = weighted ? c.waves_per_rg : min(c.waves_per_rg, C);
+    // unequal shares only with cost weighting (the chunk-count split needs a
+    // chunk in every share)
+    Shares shares{W, weighted ? min(c.young_from, W) : W, U, 0u};
+    shares.T = shares.P(W);
     const uint32_t n_rep = a.num_heads / a.num_kv_heads;
     // Multi-row decode: the nrow rows of a sequence share its K/V reads; the
     // row group's query heads are (row, head) pairs h0 .. h0+nh-1.
@@ -392,12 +429,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             const uint32_t cf = lane_value(win_cinc - ua * win_nc, l);     // cost index of its first chunk
             return before_out + (u > cf ? (u - cf + ua - 1) / ua : 0u);
         }
-        locate_chunk<VIS>(a, lane, u, s_out, before_out);
+        locate_chunk<VIS, CH>(a, lane, u, s_out, before_out);
         np_out = 0;
         return u;
     };
-    const uint32_t lo = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j) * U / W));
-    const uint32_t hi = uniform(static_cast<uint32_t>(static_cast<uint64_t>(j + 1) * U / W));
+    const uint32_t lo = uniform(shares.bound(j));
+    const uint32_t hi = uniform(shares.bound(j + 1));
     uint32_t s0, p0c, np0, s1, p1c, np1;
     const uint32_t x0 = uniform(chunk_at_cost(lo, s0, p0c, np0));
     const uint32_t x1 = hi >= U ? C : uniform(chunk_at_cost(hi, s1, p1c, np1));
@@ -411,8 +448,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     const uint32_t hs = a.head_size, hs4 = EXACT ? HS4P : hs / 4, wpt = hs4 + 1;
     const uint64_t kv_stride = static_cast<uint64_t>(a.num_kv_heads) * a.block_size * wpt;  // words per block
     const uint64_t kvh_off = static_cast<uint64_t>(kvh) * a.block_size * wpt;
-    const uint32_t chunk_u4 = kChunk * wpt / 4;
-    const uint32_t nseg = kChunk / c.seg_rows;            // tile segments per tiled chunk
+    const uint32_t chunk_u4 = CH * wpt / 4;
+    const uint32_t nseg = CH / c.seg_rows;            // tile segments per tiled chunk
 
     // ---- cursor over the chunk sequence (wave-uniform) ----
     struct Cursor {
@@ -424,8 +461,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     cur.npos = one_window ? uniform(np0) : uniform(positions_of<VIS>(a, cur.s));
     auto share = [&]() __attribute__((always_inline)) {
         const uint32_t cf = first_cost(cur.s, cur.before);
-        cur.jf = wave_of_chunk(cf, U, W);
-        cur.nrec = wave_of_chunk(cf + ua * ((cur.npos + kChunk - 1) / kChunk - 1), U, W) - cur.jf + 1;
+        cur.jf = shares.wave_of(cf);
+        cur.nrec = shares.wave_of(cf + ua * ((cur.npos + CH - 1) / CH - 1)) - cur.jf + 1;
     };
     share();
     // Sequences with no positions get zero rows.  Each is written by exactly
@@ -433,12 +470,12 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     // for those before the first chunk, the last wave for those after it.
     auto advance = [&]() __attribute__((always_inline)) {
         ++cur.ci;
-        if (cur.ci * kChunk >= cur.npos) {
-            cur.before += (cur.npos + kChunk - 1) / kChunk;
+        if (cur.ci * CH >= cur.npos) {
+            cur.before += (cur.npos + CH - 1) / CH;
             cur.ci = 0;
             while (true) {
                 ++cur.s;
-                cur.npos = cur.s >= a.num_seqs ? static_cast<uint32_t>(kChunk)
+                cur.npos = cur.s >= a.num_seqs ? static_cast<uint32_t>(CH)
                            : one_window ? lane_value(win_np, cur.s)
                                         : uniform(positions_of<VIS>(a, cur.s));
                 if (cur.npos != 0) break;
@@ -488,9 +525,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             vc_c0 = ci;
             const uint32_t cl = ci + lane;
             const uint64_t row = static_cast<uint64_t>(s_) * a.vis_stride;
-            const bool in = static_cast<uint64_t>(cl) * kChunk < npos;
-            const uint32_t f = in ? cl * kChunk : 0u;
-            const uint32_t l = in ? min(cl * kChunk + kChunk - 1, npos - 1) : 0u;
+            const bool in = static_cast<uint64_t>(cl) * CH < npos;
+            const uint32_t f = in ? cl * CH : 0u;
+            const uint32_t l = in ? min(cl * CH + CH - 1, npos - 1) : 0u;
             vc_first = a.visible_pos[row + f];
             vc_last = a.visible_pos[row + l];
         }
@@ -500,8 +537,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     auto meta_of = [&](bool live) __attribute__((always_inline)) -> Meta {
         Meta m;
         m.s = cur.s;
-        m.cs = cur.ci * kChunk;
-        const uint32_t nv = live ? min(static_cast<uint32_t>(kChunk), cur.npos - m.cs) : 0u;
+        m.cs = cur.ci * CH;
+        const uint32_t nv = live ? min(static_cast<uint32_t>(CH), cur.npos - m.cs) : 0u;
         uint32_t pl = 0;
         if (VIS) vis_bounds(m.s, cur.ci, cur.npos, m.p0, pl);
         else m.p0 = m.cs;
@@ -510,7 +547,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             tiled = c.tiled_ok;
             // ascending distinct positions from a 64-aligned p0 to p0 + nv - 1
             // are exactly the tile rows p0 .. p0 + nv - 1
-            if (VIS && tiled && nv > 0) tiled = (m.p0 % kChunk == 0) && (pl - m.p0 == nv - 1) ? 1u : 0u;
+            if (VIS && tiled && nv > 0) tiled = (m.p0 % CH == 0) && (pl - m.p0 == nv - 1) ? 1u : 0u;
         }
         m.jf = cur.jf;
         m.info = nv | (tiled << 7) | (cur.nrec << 8);
@@ -524,7 +561,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             m.app = L == cur.npos ? 1u : 0u;
         }
         const uint32_t k = min(lane, nseg - 1);
-        uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(kChunk) ? k : 0u);
+        uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(CH) ? k : 0u);
         jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
         m.id = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
         return m;
@@ -569,14 +606,14 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
                         b.v[k * FS + f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb[k] + lb + f * 1024));
                     }
             }
-            // Trailing units: lane l < 16 takes unit l % FLO of segment l / FLO.
+            // Trailing units: lane l < NTAIL takes unit l % FLO of segment l / FLO.
             const uint32_t kk = lane / FLO;
             const char* pk = reinterpret_cast<const char*>(a.key_cache);
             const char* pv = reinterpret_cast<const char*>(a.value_cache);
 #pragma unroll
             for (int k = 0; k < FSEG; ++k)
                 if (kk == static_cast<uint32_t>(k)) { pk = kb[k]; pv = vb[k]; }
-            const uint32_t tb = (lane < 16u) ? (FS * 64 + lane % FLO) * 16 : lb;
+            const uint32_t tb = (lane < NTAIL) ? (FS * 64 + lane % FLO) * 16 : lb;
             b.k4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pk + tb));
             b.v4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pv + tb));
             return;
@@ -658,8 +695,10 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         if (lane == 0) { sK[row + hs4] = ks; sV[row + hs4] = vs; }
         if (grp == 0) {
             const uint32_t pos = m.cs + meta_nv(m) - 1;
-            uint32_t blk = uniform(a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + pos / a.block_size]);
-            blk = blk < num_blocks_m1 ? blk : num_blocks_m1;
+            const uint32_t blk = uniform(a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + pos / a.block_size]);
+            // An out-of-range block id breaks the caller contract: nothing is
+            // written for it (a clamped id would overwrite another block's row).
+            if (blk > num_blocks_m1) return;
             const uint64_t dst = ((static_cast<uint64_t>(blk) * a.num_kv_heads + kvh) * a.block_size + pos % a.block_size) * wpt;
             if (lane < hs4) { a.key_cache_w[dst + lane] = kw; a.value_cache_w[dst + lane] = vw; }
             if (lane == 0) { a.key_cache_w[dst + hs4] = ks; a.value_cache_w[dst + hs4] = vs; }
@@ -679,7 +718,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
                         *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v[k * FS + f];
                     }
             }
-            if (lane < 16u) {
+            if (lane < NTAIL) {
                 const uint32_t u = (lane / FLO) * SEG_U4 + FS * 64 + lane % FLO;
                 *reinterpret_cast<u32x4*>(&sK[4 * u]) = b.k4;
                 *reinterpret_cast<u32x4*>(&sV[4 * u]) = b.v4;
@@ -726,6 +765,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     // values) staged per lane as QF 16-byte slots: lane l, slot t holds padded
     // elements 4*(l + 64*t) .. +3.
     constexpr int QF = G * QD / (4 * kWave);
+    static_assert(QSCR ? QF * kWave <= NHS * 16 * 16 : NHS * NKB * 256 + QF * kWave <= BUFW, "q scratch");
     float4 qv[QF];
     auto q_issue = [&](uint32_t s) __attribute__((always_inline)) {
         const uint64_t row = static_cast<uint64_t>(s) * nrow * a.q_stride;
@@ -755,7 +795,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
     auto q_finish = [&]() __attribute__((always_inline)) {
         uint32_t* const scratch = QSCR ? sQs_[wid] : sKn;   // sKn: no loads are landing in it yet
         uint32_t* const sDig = scratch;
-        float* const sMax = reinterpret_cast<float*>(scratch) + NHS * NKB * 256;
+        // per-slot maxima: in sA (not in use outside a chunk's processing)
+        // when the digits have a scratch of their own
+        float* const sMax = QSCR ? reinterpret_cast<float*>(sA) : reinterpret_cast<float*>(scratch) + NHS * NKB * 256;
 #pragma unroll
         for (int t = 0; t < QF; ++t) {
             const float4 v = qv[t];
@@ -831,10 +873,10 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             const uint32_t dl = nrow - 1 - min(pq / n_rep, nrow - 1);
             nvh[hset] = nrow > 1 ? min(nv, pm.lr > dl ? pm.lr - dl : 0u) : nv;
         }
-        // ---- q . K^T ----
+        // ---- q . K^T (NTG groups of 16 tokens) ----
         i32x4 dsum[NHS][4];
 #pragma unroll
-        for (int tg = 0; tg < 4; ++tg) {
+        for (int tg = 0; tg < NTG; ++tg) {
             const uint32_t* krow = &sK[(16 * tg + r) * wpt + 4 * g];
 #pragma unroll
             for (int hset = 0; hset < NHS; ++hset) dsum[hset][tg] = i32x4{0, 0, 0, 0};
@@ -858,7 +900,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
         bool val[4];
         float vmax = 0.0f;
 #pragma unroll
-        for (int tg = 0; tg < 4; ++tg) {
+        for (int tg = 0; tg < NTG; ++tg) {
             const uint32_t t = 16 * tg + r;
             val[tg] = t < nv;
             ksc[tg] = __uint_as_float(sK[t * wpt + hs4]);
@@ -875,7 +917,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             bool vh[4];
             float cmax = -INFINITY;
 #pragma unroll
-            for (int tg = 0; tg < 4; ++tg) {
+            for (int tg = 0; tg < NTG; ++tg) {
                 vh[tg] = 16 * tg + r < nvh[hset];
                 const float zq = ldexpf(combine_digits(dsum[hset][tg]), -eq_out[hset]);
                 z[tg] = vh[tg] ? zq * (ksc[tg] * a.scale_log2) : -INFINITY;
@@ -885,9 +927,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
             // -inf only while a multi-row pair has attended nothing: no NaN from exp2(-inf + inf)
             const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run[hset] - m_new);
             float psum = 0.0f;
-            uint32_t wd[4];
+            uint32_t wd[4] = {0u, 0u, 0u, 0u};      // groups past the chunk (CH = 32): weight 0
 #pragma unroll
-            for (int tg = 0; tg < 4; ++tg) {
+            for (int tg = 0; tg < NTG; ++tg) {
                 const float p = vh[tg] ? exp2f(z[tg] - m_new) : 0.0f;
                 psum += p;
                 const float pv = vh[tg] ? p * vsc[tg] : 0.0f;
@@ -920,7 +962,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const uint32_t word = NCW * r + cw;
-                    x[b] = (EXACT || word < hs4) ? sV[(4 * g + w + 16 * b) * wpt + word] : 0u;
+                    x[b] = (b < NTG && (EXACT || word < hs4)) ? sV[(4 * g + w + 16 * b) * wpt + word] : 0u;
                 }
                 transpose4(x, y);
 #pragma unroll
@@ -1127,35 +1169,30 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && SEGR == 0) ?
 }
 
 template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED>
-void launch_split_seg(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st, bool tiled) {
+const void* split_kernel_seg(bool tiled, uint32_t seg_rows) {
+    constexpr int CH = decode_chunk(HS4P, NHS);
     // Scalar-addressed segment loads need an exact head size, 16-byte aligned
     // caches and tile segments of 16 or 32 rows.
-    const uint32_t segr = EXACT && tiled ? c.seg_rows : 0;
+    const uint32_t segr = EXACT && tiled ? seg_rows : 0;
     if (EXACT && segr == 16)
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, EXACT ? 16 : 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
-    else if (EXACT && segr == 32)
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, EXACT ? 32 : 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
-    else
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
+        return reinterpret_cast<const void*>(&decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, EXACT ? 16 : 0, CH>);
+    if (EXACT && segr == 32)
+        return reinterpret_cast<const void*>(&decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, EXACT ? 32 : 0, CH>);
+    return reinterpret_cast<const void*>(&decode_split_kernel<HS4P, EXACT, NHS, VIS, TILED, 0, CH>);
 }
 
 template <int HS4P, bool EXACT, int NHS>
-hipError_t launch_split_t(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
-                          bool vis, bool tiled) {
-    if (vis)
-        launch_split_seg<HS4P, EXACT, NHS, true, false>(a, c, nbm1, grid, st, tiled);
-    else if (EXACT && tiled)
-        launch_split_seg<HS4P, EXACT, NHS, false, EXACT>(a, c, nbm1, grid, st, tiled);
-    else
-        hipLaunchKernelGGL((decode_split_kernel<HS4P, EXACT, NHS, false, false, 0>), grid, dim3(kWave * kWavesPerGroup), 0, st, a, c, nbm1);
-    return hipGetLastError();
+const void* split_kernel_t(bool vis, bool tiled, uint32_t seg_rows) {
+    if (vis) return split_kernel_seg<HS4P, EXACT, NHS, true, false>(tiled, seg_rows);
+    if (EXACT && tiled) return split_kernel_seg<HS4P, EXACT, NHS, false, EXACT>(tiled, seg_rows);
+    return reinterpret_cast<const void*>(
+        &decode_split_kernel<HS4P, EXACT, NHS, false, false, 0, decode_chunk(HS4P, NHS)>);
 }
 
 template <int HS4P, bool EXACT>
-hipError_t launch_split_g(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
-                          bool vis, bool tiled) {
-    if (c.group == 8) return launch_split_t<HS4P, EXACT, 2>(a, c, nbm1, grid, st, vis, tiled);
-    return launch_split_t<HS4P, EXACT, 1>(a, c, nbm1, grid, st, vis, tiled);
+const void* split_kernel_g(bool vis, bool tiled, uint32_t group, uint32_t seg_rows) {
+    if (group == 8) return split_kernel_t<HS4P, EXACT, 2>(vis, tiled, seg_rows);
+    return split_kernel_t<HS4P, EXACT, 1>(vis, tiled, seg_rows);
 }
 
 }  // namespace

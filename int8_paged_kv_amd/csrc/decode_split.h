@@ -7,6 +7,13 @@ namespace q8kv {
 // Independent wavefronts packed per workgroup (fewer workgroups to dispatch).
 constexpr uint32_t kWavesPerGroup = 4;
 
+// Positions per chunk of a split-kernel instantiation: 32 for up to 32 code
+// words per row with one set of 4 query heads (two chunks in flight per
+// wave fit in a quarter of the CU's LDS, so two workgroups share a CU), else
+// 64.  hs4p: code words per row rounded up to 16, 32, 48 or 64; nhs: sets of
+// 4 query heads per wavefront.
+constexpr int decode_chunk(int hs4p, int nhs) { return hs4p <= 32 && nhs == 1 ? 32 : 64; }
+
 struct SplitConsts {
     uint32_t waves_per_rg;  // persistent wavefronts per row group (before capping by the chunk count)
     uint32_t num_rg;        // row groups: num_kv_heads * num_groups
@@ -14,20 +21,20 @@ struct SplitConsts {
     uint32_t recs_per_rg;   // partial records per row group: waves_per_rg + num_seqs - 1
     uint32_t seg_u4;        // 16-byte units per tile segment in a chunk
     uint32_t seg_magic;     // ceil(2^32 / seg_u4): u / seg_u4 == mulhi(u, magic) for u < 2^16
-    uint32_t seg_rows;      // rows per segment = min(block_size, 64)
+    uint32_t seg_rows;      // rows per segment = min(block_size, chunk positions)
     uint32_t tiled_ok;      // segment copies are legal (alignment, block_size shape)
     uint32_t q_vec_ok;      // q rows of every sequence are 16-byte aligned
+    uint32_t young_from;    // first wave (of a row group) in the grid's second workgroup per CU; >= waves: none
 };
 
-// One translation unit per padded head size (code words per row rounded up
-// to 16, 32, 48 or 64); `exact` when head_size / 4 equals that size.
-hipError_t launch_split_hs16(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
-                             bool vis, bool tiled, bool exact);
-hipError_t launch_split_hs32(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
-                             bool vis, bool tiled, bool exact);
-hipError_t launch_split_hs48(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
-                             bool vis, bool tiled, bool exact);
-hipError_t launch_split_hs64(const DecodeArgs& a, const SplitConsts& c, uint32_t nbm1, dim3 grid, hipStream_t st,
-                             bool vis, bool tiled, bool exact);
+// The split-kernel instantiation for these arguments: one translation unit
+// per padded head size (code words per row rounded up to 16, 32, 48 or 64);
+// `exact` when head_size / 4 equals that size; seg_rows: the block size when
+// a block is a whole tile segment of a chunk (at most the chunk's positions),
+// else 0.  Launched with (DecodeArgs, SplitConsts, uint32_t num_blocks_m1).
+const void* split_kernel_hs16(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
+const void* split_kernel_hs32(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
+const void* split_kernel_hs48(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
+const void* split_kernel_hs64(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
 
 }  // namespace q8kv

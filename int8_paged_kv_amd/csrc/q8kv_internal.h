@@ -8,8 +8,10 @@ namespace q8kv {
 
 constexpr uint32_t kPadSlot = 0xFFFFFFFFu;
 constexpr int kWave = 64;          // CDNA wavefront width
-constexpr int kChunk = 64;         // decode positions per chunk
-constexpr uint32_t kDecodeWaves = 1024;   // persistent decode wavefronts: 4 per CU of an MI355X
+// Bound on the persistent decode wavefronts (8 per CU of a 256-CU MI355X);
+// a launch takes as many as the device keeps resident for its kernel, up to
+// this bound, which also sizes the workspace.
+constexpr uint32_t kMaxDecodeWaves = 2048;
 // Cache writers: from this many (token, kv head) pairs on, each wave takes
 // kWritePairsPerWave consecutive pairs with all their loads in flight.
 constexpr uint64_t kWriteBatchMinPairs = 32768;
@@ -91,8 +93,13 @@ struct DecodePlan {
     size_t counters_offset, ml_offset, acc_offset, bytes;
 };
 
+// target: persistent wavefronts to spread over the row groups.
 DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
-                       uint32_t head_size, uint32_t block_size, uint32_t max_positions);
+                       uint32_t head_size, uint32_t block_size, uint32_t max_positions, uint64_t target);
+// The wave count a workspace must be sized for (kMaxDecodeWaves, or the
+// Q8KV_DECODE_WAVES override), and the override alone (0 when unset).
+uint64_t decode_wave_bound();
+uint64_t decode_wave_override();
 
 struct DecodeArgs {
     float* out;
@@ -103,6 +110,8 @@ struct DecodeArgs {
     const uint32_t* context_lens;
     const uint32_t* visible_pos;
     const uint32_t* num_visible;
+    void* workspace;         // caller workspace, sized for decode_wave_bound() waves (null when none is needed)
+    // Set at launch from the plan, inside the workspace:
     uint32_t* counters;      // [row group, seq]: arrivals of a sequence's waves; zero between calls
     float* part_ml;          // [row group, record, head in group, 2]: running max (log2 units), sum
     float* part_acc;         // [row group, record, head in group, head_size]: unnormalized output
@@ -124,7 +133,8 @@ struct DecodeArgs {
     uint32_t rows_per_seq;
 };
 
-hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
+// max_positions: max_context_len in dense mode, vis_stride with visible lists.
+hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_t stream);
 
 // ---- f32 paged-cache baseline: cache [num_blocks, num_kv_heads, block_size, head_size] f32 ----
 

@@ -90,15 +90,16 @@ def test_decode_validation(lib, kw, want):
 
 
 def test_workspace_size_matches_plan(lib):
-    # At most one 64-position chunk per sequence: every sequence lies in one
-    # wavefront's range, no partials.
-    assert lib.q8_paged_decode_workspace_bytes(2, 4, 2, 128, 16, 64) == 0
+    # At most 32 positions per sequence (a chunk holds 32 or 64): every
+    # sequence lies in one wavefront's range, no partials.
+    assert lib.q8_paged_decode_workspace_bytes(2, 4, 2, 128, 16, 32) == 0
+    assert lib.q8_paged_decode_workspace_bytes(2, 4, 2, 128, 16, 33) > 0
     # Otherwise: per row group (kv head, group of 4 or 8 query heads),
     # (waves per group + S - 1) records of (head_size + 2) floats per head.
     # Layout: arrival counters (one u32 per row group and sequence), then the
     # records' outputs, then their (max, sum) pairs, each 256-byte aligned.
     def want(S, hs, rg, group):
-        recs = 1024 // rg + S - 1
+        recs = 2048 // rg + S - 1
         slots = rg * recs * group
         r256 = lambda b: (b + 255) // 256 * 256
         return r256(rg * S * 4) + r256(slots * hs * 4) + slots * 2 * 4
