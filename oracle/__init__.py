@@ -293,17 +293,22 @@ def norm_rope_row_f64(x, weight, pos: int, rot: int, theta: float, eps: float) -
 
 
 def norm_rope(x, positions, weight, table, rot: int, eps: float, num_heads: int, head_size: int,
-              x_stride=None, head_stride=None) -> np.ndarray:
-    """Rows of heads: head h of row t at x.flat[t*x_stride + h*head_stride]; returns
-    [num_rows, num_heads, head_size] f32."""
+              x_stride=None, head_stride=None, out_stride=None, out=None) -> np.ndarray:
+    """Rows of heads: head h of row t at x.flat[t*x_stride + h*head_stride], written
+    to out.flat[t*out_stride + h*head_size]; returns [num_rows, num_heads,
+    head_size] f32 (or, with out_stride and out given, out itself, written in place)."""
     x = _c(x, np.float32)
     positions = _c(positions, np.uint32)
     T = positions.shape[0]
     hst = head_size if head_stride is None else head_stride
     xs = x_stride if x_stride is not None else (x.size // T if T else num_heads * hst)
     table = _c(table if rot else np.zeros((1, 1), np.float32), np.float32)
-    out = np.zeros((T, num_heads, head_size), dtype=np.float32)
-    _check(_load().q8o_norm_rope(_ptr(out), num_heads * head_size, _ptr(x), xs, hst, T, num_heads, head_size,
+    os_ = num_heads * head_size if out_stride is None else out_stride
+    if out is None:
+        out = np.zeros((T, num_heads, head_size) if out_stride is None else (T, os_), dtype=np.float32)
+    if out.dtype != np.float32 or not out.flags.c_contiguous or out.size < T * os_:
+        raise ValueError("out must be a contiguous f32 array of num_rows * out_stride elements")
+    _check(_load().q8o_norm_rope(_ptr(out), os_, _ptr(x), xs, hst, T, num_heads, head_size,
                                  _ptr(positions), _ptr(_c(weight, np.float32)), _ptr(table), rot,
                                  table.shape[0] if rot else 0, float(eps)), "norm_rope")
     return out

@@ -13,8 +13,13 @@ with frequencies theta^(-2i/rot)) is pinned here by:
   norm and scale invariance, and the relative-position property of rotations;
 * the binary32 pipeline (the one the quantizer sees) against the binary64
   definition, element by element;
-* the fused writer against the quantizer applied to the pipeline's rows, pad
-  slots untouched, and out-of-contract shapes and positions rejected.
+* the rows-of-heads function's indexing (row, head and output strides, the
+  q/gate interleave of head stride 2*head_size, each row's table row) against
+  numpy slicing of the same arrays and the binary64 definition at each row's
+  position;
+* the fused writer against the quantizer applied to the pipeline's rows (also
+  with padded key/value row strides), pad slots untouched, and out-of-contract
+  shapes and positions rejected.
 """
 import math
 
@@ -167,6 +172,75 @@ def test_writer_composes_norm_rope_and_quantizer():
             written[blk, h, off] = True
     assert np.array_equal(kc[~written], kc0[~written]) and np.array_equal(vc[~written], vc0[~written])
     assert kc.shape[-1] == wpt
+
+
+@pytest.mark.parametrize("hs,rot,H,head_stride,pad_x,pad_out", [
+    (128, 64, 4, 256, 12, 8),       # q and gate interleaved per head: head stride 2*head_size
+    (64, 32, 3, 64, 4, 0),
+    (32, 8, 5, 40, 0, 4),
+    (256, 0, 2, 300, 7, 16),        # no rotation: positions and table unused
+])
+def test_rows_of_heads_indexing(hs, rot, H, head_stride, pad_x, pad_out):
+    """Each output head is the row function of exactly the input slice numpy
+    takes at (row * x_stride + head * head_stride), with the table row of that
+    row's position, written at (row * out_stride + head * head_size); the
+    padding between output rows is left alone.  A swapped stride, a head read
+    at head_size instead of head_stride, or a wrong table row fails here."""
+    g = np.random.default_rng(hs + rot + H)
+    T, P, theta, eps = 9, 700, 10000.0, 1e-6
+    xs = (H - 1) * head_stride + hs + pad_x
+    os_ = H * hs + pad_out
+    x = (g.standard_normal(T * xs) * 2.5).astype(np.float32)
+    w = (1.0 + 0.1 * g.standard_normal(hs)).astype(np.float32)
+    pos = g.permutation(P)[:T].astype(np.uint32)            # distinct, shuffled positions
+    tab = oracle.rope_table(P, rot, theta) if rot else None
+    out = np.full((T, os_), 1234.5, np.float32)
+    oracle.norm_rope(x, pos, w, tab, rot, eps, H, hs, x_stride=xs, head_stride=head_stride, out_stride=os_,
+                     out=out)
+    for t in range(T):
+        p = int(pos[t])
+        for h in range(H):
+            xi = x[t * xs + h * head_stride: t * xs + h * head_stride + hs]
+            want = oracle.norm_rope_row(xi, w, tab[p] if rot else None, rot, eps)
+            got = out[t, h * hs:(h + 1) * hs]
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (t, h)
+            # and the position's angle, taken straight from theta, not from a table row
+            y64 = oracle.norm_rope_row_f64(xi, w, p, rot, theta, eps)
+            assert np.max(np.abs(got - y64)) <= 8 * 2.0 ** -24 * np.max(np.abs(y64)) + 1e-30, (t, h)
+        assert np.all(out[t, H * hs:] == np.float32(1234.5)), "padding between output rows written"
+
+
+def test_writer_row_strides():
+    """The fused writer with key and value rows of different padded strides:
+    each non-pad (token, kv head) is the quantizer of the row function of the
+    slice at token * stride + head * head_size."""
+    g = np.random.default_rng(16)
+    T, Hkv, hs, bs, nb, rot, P = 23, 3, 64, 8, 12, 32, 300
+    ks, vs = Hkv * hs + 20, Hkv * hs + 4
+    key = g.standard_normal(T * ks).astype(np.float32)
+    val = g.standard_normal(T * vs).astype(np.float32)
+    tab = oracle.rope_table(P, rot, 500.0)
+    wt = (1.0 + 0.1 * g.standard_normal(hs)).astype(np.float32)
+    slots = g.choice(nb * bs, size=T, replace=False).astype(np.uint32)
+    slots[[2, 11]] = oracle.PAD_SLOT
+    pos = g.integers(0, P, T).astype(np.uint32)
+    kc, vc = wl.poison_cache(nb, Hkv, bs, hs), wl.poison_cache(nb, Hkv, bs, hs)
+    kc0, vc0 = kc.copy(), vc.copy()
+    oracle.norm_rope_cache_write(key, val, kc, vc, slots, pos, wt, tab, rot, 1e-6, Hkv, hs, bs,
+                                 key_stride=ks, value_stride=vs)
+    written = np.zeros(kc.shape[:3], dtype=bool)
+    for t in range(T):
+        if slots[t] == oracle.PAD_SLOT:
+            continue
+        blk, off = divmod(int(slots[t]), bs)
+        for h in range(Hkv):
+            kx = key[t * ks + h * hs: t * ks + (h + 1) * hs]
+            vx = val[t * vs + h * hs: t * vs + (h + 1) * hs]
+            assert np.array_equal(kc[blk, h, off], oracle.quantize_row(oracle.norm_rope_row(kx, wt, tab[pos[t]],
+                                                                                            rot, 1e-6)))
+            assert np.array_equal(vc[blk, h, off], oracle.quantize_row(vx))
+            written[blk, h, off] = True
+    assert np.array_equal(kc[~written], kc0[~written]) and np.array_equal(vc[~written], vc0[~written])
 
 
 def test_out_of_contract_rejected():
