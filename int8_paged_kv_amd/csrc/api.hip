@@ -158,7 +158,8 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     // Workspace need at the wave bound; a launch uses at most that many waves.
     const q8kv::DecodePlan p = q8kv::plan_decode(num_seqs, static_cast<uint32_t>(num_pairs), num_kv_heads, head_size,
                                                  block_size, max_pos, q8kv::decode_wave_bound());
-    if (p.num_waves > 0x7FFFFFFFull || static_cast<uint64_t>(num_seqs) * num_pairs > 0x7FFFFFFFull)
+    if (p.num_waves > 0x7FFFFFFFull || static_cast<uint64_t>(num_seqs) * num_pairs > 0x7FFFFFFFull ||
+        p.recs_per_rg > 0x7FFFFFFFull)
         return Q8_ERR_UNSUPPORTED;
     if (p.bytes > 0 && static_scratch) {
         // The library's own scratch array instead of a caller workspace.
@@ -333,7 +334,7 @@ q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
                           static_cast<const void*>(key_cache), static_cast<const void*>(value_cache)})
         if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return Q8_ERR_UNSUPPORTED;
     const q8kv::F32DecodePlan p = q8kv::plan_f32_decode(num_seqs, num_heads, num_kv_heads, head_size);
-    if (p.num_waves > 0x7FFFFFFFull) return Q8_ERR_UNSUPPORTED;
+    if (p.num_waves > 0x7FFFFFFFull || p.recs_per_rg > 0x7FFFFFFFull) return Q8_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < p.bytes || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
         return Q8_ERR_WORKSPACE;
     q8kv::F32DecodeArgs a{};
@@ -359,7 +360,7 @@ q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
     a.group = p.group;
     a.num_groups = p.num_groups;
     a.waves_per_rg = p.waves_per_rg;
-    a.recs_per_rg = p.recs_per_rg;
+    a.recs_per_rg = static_cast<uint32_t>(p.recs_per_rg);
     a.inv_block_size = 1.0f / static_cast<float>(block_size);
     a.scale_log2 = scale * 1.4426950408889634f;
     const hipError_t e = q8kv::launch_f32_decode(a, p, static_cast<hipStream_t>(stream));

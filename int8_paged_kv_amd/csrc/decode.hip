@@ -38,7 +38,7 @@ DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_he
     if (per < 1) per = 1;
     p.waves_per_rg = static_cast<uint32_t>(per);
     p.num_waves = num_rg * per;
-    p.recs_per_rg = p.waves_per_rg + (num_seqs ? num_seqs - 1 : 0);
+    p.recs_per_rg = static_cast<uint64_t>(p.waves_per_rg) + (num_seqs ? num_seqs - 1 : 0);
     // Workspace: one arrival counter per (row group, sequence), then the
     // partial records.  A sequence of at most one chunk always lies in a
     // single wave's range, so then no workspace is needed at all.
@@ -142,7 +142,7 @@ hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_
     c.num_rg = a.num_kv_heads * p.num_groups;
     c.group = p.group;
     c.num_groups = p.num_groups;
-    c.recs_per_rg = p.recs_per_rg;
+    c.recs_per_rg = static_cast<uint32_t>(p.recs_per_rg);     // the call's shapes were checked to fit
     // Two resident workgroups per CU with the whole grid resident: the second
     // half of the grid is each CU's second workgroup (smaller shares).
     c.young_from = per_cu == 2 && !decode_wave_override() ? p.waves_per_rg / 2 : p.waves_per_rg;

@@ -507,7 +507,7 @@ F32DecodePlan plan_f32_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t nu
     }
     const uint64_t num_rg = static_cast<uint64_t>(num_kv_heads) * p.num_groups;
     p.waves_per_rg = static_cast<uint32_t>(num_rg >= target ? 1 : target / num_rg);
-    p.recs_per_rg = p.waves_per_rg + (num_seqs ? num_seqs - 1 : 0);
+    p.recs_per_rg = static_cast<uint64_t>(p.waves_per_rg) + (num_seqs ? num_seqs - 1 : 0);
     p.num_waves = num_rg * p.waves_per_rg;
     auto r256 = [](size_t b) { return (b + 255) / 256 * 256; };
     const size_t slots = static_cast<size_t>(num_rg) * p.recs_per_rg * p.group;

@@ -88,7 +88,7 @@ struct DecodePlan {
     uint32_t group;          // query heads handled together per kv head (4 or 8)
     uint32_t num_groups;     // ceil(n_rep / group)
     uint32_t waves_per_rg;   // persistent wavefronts per row group
-    uint32_t recs_per_rg;    // partial record slots per row group: waves_per_rg + num_seqs - 1
+    uint64_t recs_per_rg;    // partial record slots per row group: waves_per_rg + num_seqs - 1 (64-bit: no wrap)
     uint64_t num_waves;      // grid: row groups * waves_per_rg
     size_t counters_offset, ml_offset, acc_offset, bytes;
 };
@@ -156,7 +156,8 @@ hipError_t launch_f32_cache_write(const F32CacheWriteArgs& a, hipStream_t stream
 // waves_per_rg persistent waves over its chunk list and recs_per_rg partial
 // record slots.
 struct F32DecodePlan {
-    uint32_t group, num_groups, waves_per_rg, recs_per_rg;
+    uint32_t group, num_groups, waves_per_rg;
+    uint64_t recs_per_rg;    // 64-bit: no wrap for extreme sequence counts
     uint64_t num_waves;
     size_t counters_offset, ml_offset, acc_offset, bytes;
 };
