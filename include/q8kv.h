@@ -468,6 +468,33 @@ q8_status q8_index_select(const float* scores, uint32_t score_stride, const uint
 /* hipError_t code behind the calling thread's last Q8_ERR_HIP (0 if none). */
 int q8_last_hip_error(void);
 
+/*
+ * Content checks (libq8kv_debug.so, the library built with Q8_DEBUG_BOUNDS).
+ * The release library trusts the contents of the device arrays as the
+ * pages' shaders do; the debug build also checks them on the device and
+ * records every failed check as a bit of a flag word per GPU, while still
+ * computing as the release build does (reads clamped into the cache, writes
+ * past it skipped):
+ *   Q8_BOUNDS_SLOT     q8_cache_write: a slot past num_blocks*block_size that
+ *                      is not Q8_PAD_SLOT (nothing is written for it)
+ *   Q8_BOUNDS_BLOCK    decode / decode step: a block id at or past num_blocks
+ *                      for an attended position or the appended row
+ *   Q8_BOUNDS_TABLE    decode: positions of a sequence past its block-table
+ *                      row (context_lens beyond max_num_blocks_per_seq*block_size,
+ *                      or a visible position whose block is past the row)
+ *   Q8_BOUNDS_VISIBLE  visible lists: num_visible past vis_stride, or listed
+ *                      positions of a chunk not ascending and distinct
+ * q8_bounds_flags -- wait for the device (hipDeviceSynchronize), store the
+ * current device's flag word in *flags and, when clear != 0, reset it.  In the
+ * release library it stores 0 and returns Q8_ERR_UNSUPPORTED.  Q8_ERR_NULL for
+ * a NULL flags pointer; Q8_ERR_HIP when the device calls fail.
+ */
+#define Q8_BOUNDS_SLOT 1u
+#define Q8_BOUNDS_BLOCK 2u
+#define Q8_BOUNDS_TABLE 4u
+#define Q8_BOUNDS_VISIBLE 8u
+q8_status q8_bounds_flags(uint32_t* flags, int clear);
+
 /* Static, human-readable name of a status code. */
 const char* q8_status_string(q8_status status);
 

@@ -31,7 +31,7 @@ __all__ = ["q8_cache_write", "q8_paged_decode", "q8_paged_decode_noalloc", "q8_d
            "q8_paged_decode_workspace_bytes", "q8_f32_cache_write", "q8_f32_paged_decode",
            "q8_f32_paged_decode_workspace_bytes", "q8_rope_table", "q8_norm_rope", "q8_norm_rope_cache_write",
            "q8_norm_rope_qk_cache_write", "q8_index_select",
-           "load_library", "Q8Error", "PAD_SLOT"]
+           "load_library", "load_debug_library", "use_library", "bounds_flags", "Q8Error", "PAD_SLOT"]
 
 
 def __getattr__(name):

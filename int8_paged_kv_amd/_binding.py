@@ -28,6 +28,8 @@ class Q8Error(RuntimeError):
         self.status = status
 
 
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8kv_debug.so")
+
 _lib = None
 
 
@@ -35,51 +37,83 @@ def load_library() -> ctypes.CDLL:
     """Load libq8kv.so (built by int8_paged_kv_amd/build.py); raise if it is absent."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError("libq8kv.so is not built (%s); run int8_paged_kv_amd/build.py" % LIB_PATH)
-        lib = ctypes.CDLL(LIB_PATH)
-        P, U = ctypes.c_void_p, ctypes.c_uint32
-        lib.q8_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U, P]
-        lib.q8_cache_write.restype = ctypes.c_int
-        lib.q8_paged_decode_workspace_bytes.argtypes = [U, U, U, U, U, U]
-        lib.q8_paged_decode_workspace_bytes.restype = ctypes.c_size_t
-        lib.q8_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U, P, P, U,
-                                        U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
-        lib.q8_paged_decode.restype = ctypes.c_int
-        lib.q8_paged_decode_noalloc.argtypes = [P, P, U, P, P, P, U, P, U, P, P, U,
-                                                U, U, U, U, U, U, ctypes.c_float, P]
-        lib.q8_paged_decode_noalloc.restype = ctypes.c_int
-        lib.q8_decode_step.argtypes = [P, P, U, P, U, P, U, P, P, P, U, P, U,
-                                       U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
-        lib.q8_decode_step.restype = ctypes.c_int
-        lib.q8_paged_decode_rows.argtypes = [P, P, U, P, P, P, U, P, U, U,
-                                             U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
-        lib.q8_paged_decode_rows.restype = ctypes.c_int
-        lib.q8_f32_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U, P]
-        lib.q8_f32_cache_write.restype = ctypes.c_int
-        lib.q8_f32_paged_decode_workspace_bytes.argtypes = [U, U, U, U]
-        lib.q8_f32_paged_decode_workspace_bytes.restype = ctypes.c_size_t
-        lib.q8_f32_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U,
-                                            U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
-        lib.q8_f32_paged_decode.restype = ctypes.c_int
-        F = ctypes.c_float
-        lib.q8_rope_table.argtypes = [P, U, U, F, P]
-        lib.q8_rope_table.restype = ctypes.c_int
-        lib.q8_norm_rope.argtypes = [P, U, P, U, U, U, U, U, P, P, P, U, U, F, P]
-        lib.q8_norm_rope.restype = ctypes.c_int
-        lib.q8_norm_rope_cache_write.argtypes = [P, U, P, U, P, P, P, P, P, P, U, U, F, U, U, U, U, U, P]
-        lib.q8_norm_rope_cache_write.restype = ctypes.c_int
-        lib.q8_norm_rope_qk_cache_write.argtypes = [P, U, P, U, U, U, U, P, P, P, U, P, U, P, P, P, P, P, P, U, U,
-                                                    F, U, U, U, U, U, P]
-        lib.q8_norm_rope_qk_cache_write.restype = ctypes.c_int
-        lib.q8_index_select.argtypes = [P, U, P, U, U, U, P, U, P, P, U, P]
-        lib.q8_index_select.restype = ctypes.c_int
-        lib.q8_last_hip_error.argtypes = []
-        lib.q8_last_hip_error.restype = ctypes.c_int
-        lib.q8_status_string.argtypes = [ctypes.c_int]
-        lib.q8_status_string.restype = ctypes.c_char_p
-        _lib = lib
+        _lib = _open(LIB_PATH)
     return _lib
+
+
+def load_debug_library() -> ctypes.CDLL:
+    """Load libq8kv_debug.so, the build with device-side content checks
+    (q8_bounds_flags reads them back).  It is not the one the other calls here
+    use; use_library() swaps it in."""
+    return _open(DEBUG_LIB_PATH)
+
+
+def use_library(lib: Optional[ctypes.CDLL]) -> Optional[ctypes.CDLL]:
+    """Make `lib` the library every call of this binding goes to (None: the
+    release library on next use); returns the previous one."""
+    global _lib
+    prev, _lib = _lib, lib
+    return prev
+
+
+def bounds_flags(clear: bool = True) -> int:
+    """The current device's flag word of failed content checks (debug build;
+    see include/q8kv.h), after waiting for the device."""
+    lib = load_library()
+    f = ctypes.c_uint32(0)
+    st = lib.q8_bounds_flags(ctypes.byref(f), 1 if clear else 0)
+    _check(st, "q8_bounds_flags")
+    return int(f.value)
+
+
+def _open(path: str) -> ctypes.CDLL:
+    """Open one build of the library and declare its entry points."""
+    if not os.path.exists(path):
+        raise ImportError("%s is not built; run int8_paged_kv_amd/build.py" % path)
+    lib = ctypes.CDLL(path)
+    P, U = ctypes.c_void_p, ctypes.c_uint32
+    lib.q8_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U, P]
+    lib.q8_cache_write.restype = ctypes.c_int
+    lib.q8_paged_decode_workspace_bytes.argtypes = [U, U, U, U, U, U]
+    lib.q8_paged_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.q8_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U, P, P, U,
+                                    U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
+    lib.q8_paged_decode.restype = ctypes.c_int
+    lib.q8_paged_decode_noalloc.argtypes = [P, P, U, P, P, P, U, P, U, P, P, U,
+                                            U, U, U, U, U, U, ctypes.c_float, P]
+    lib.q8_paged_decode_noalloc.restype = ctypes.c_int
+    lib.q8_decode_step.argtypes = [P, P, U, P, U, P, U, P, P, P, U, P, U,
+                                   U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
+    lib.q8_decode_step.restype = ctypes.c_int
+    lib.q8_paged_decode_rows.argtypes = [P, P, U, P, P, P, U, P, U, U,
+                                         U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
+    lib.q8_paged_decode_rows.restype = ctypes.c_int
+    lib.q8_f32_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U, P]
+    lib.q8_f32_cache_write.restype = ctypes.c_int
+    lib.q8_f32_paged_decode_workspace_bytes.argtypes = [U, U, U, U]
+    lib.q8_f32_paged_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.q8_f32_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U,
+                                        U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
+    lib.q8_f32_paged_decode.restype = ctypes.c_int
+    F = ctypes.c_float
+    lib.q8_rope_table.argtypes = [P, U, U, F, P]
+    lib.q8_rope_table.restype = ctypes.c_int
+    lib.q8_norm_rope.argtypes = [P, U, P, U, U, U, U, U, P, P, P, U, U, F, P]
+    lib.q8_norm_rope.restype = ctypes.c_int
+    lib.q8_norm_rope_cache_write.argtypes = [P, U, P, U, P, P, P, P, P, P, U, U, F, U, U, U, U, U, P]
+    lib.q8_norm_rope_cache_write.restype = ctypes.c_int
+    lib.q8_norm_rope_qk_cache_write.argtypes = [P, U, P, U, U, U, U, P, P, P, U, P, U, P, P, P, P, P, P, U, U,
+                                                F, U, U, U, U, U, P]
+    lib.q8_norm_rope_qk_cache_write.restype = ctypes.c_int
+    lib.q8_index_select.argtypes = [P, U, P, U, U, U, P, U, P, P, U, P]
+    lib.q8_index_select.restype = ctypes.c_int
+    lib.q8_last_hip_error.argtypes = []
+    lib.q8_last_hip_error.restype = ctypes.c_int
+    lib.q8_status_string.argtypes = [ctypes.c_int]
+    lib.q8_status_string.restype = ctypes.c_char_p
+    lib.q8_bounds_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+    lib.q8_bounds_flags.restype = ctypes.c_int
+    return lib
 
 
 def _check(status: int, what: str):

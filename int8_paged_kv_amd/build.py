@@ -18,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libq8kv.so")
 # measurement kernels of the benchmark (the practical HBM ceiling), a library of their own
 BENCH_LIB = os.path.join(PKG, "libq8kv_bench.so")
+# the same sources with the device-side content checks (Q8_DEBUG_BOUNDS)
+DEBUG_LIB = os.path.join(PKG, "libq8kv_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -40,11 +42,12 @@ def _run(cmd):
 
 def build(verbose: bool = False, jobs: int = 0) -> str:
     _build_lib(sources("csrc"), LIB, verbose, jobs)
+    _build_lib(sources("csrc"), DEBUG_LIB, verbose, jobs, ["-DQ8_DEBUG_BOUNDS"])
     _build_lib(sources("csrc_bench"), BENCH_LIB, verbose, jobs)
     return LIB
 
 
-def _build_lib(srcs, lib_path: str, verbose: bool, jobs: int) -> None:
+def _build_lib(srcs, lib_path: str, verbose: bool, jobs: int, defines=()) -> None:
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
     jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 16))
     with tempfile.TemporaryDirectory(prefix="q8kv_build_") as tmpdir:
@@ -53,7 +56,7 @@ def _build_lib(srcs, lib_path: str, verbose: bool, jobs: int) -> None:
         for src in srcs:
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
             objs.append(obj)
-            cmds.append([HIPCC] + FLAGS + inc + ["-c", src, "-o", obj])
+            cmds.append([HIPCC] + FLAGS + list(defines) + inc + ["-c", src, "-o", obj])
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)

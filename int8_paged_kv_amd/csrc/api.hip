@@ -15,6 +15,36 @@ q8_status hip_fail(hipError_t e) {
     return Q8_ERR_HIP;
 }
 
+}  // namespace
+
+// ---- content checks of the Q8_DEBUG_BOUNDS build ----
+// One device word per GPU collects the bits of failed checks (bounds.h);
+// kernels receive its address, looked up once per device.
+static __device__ __align__(4) uint32_t bounds_word;
+
+namespace {
+
+constexpr int kMaxBoundsDevices = 64;
+std::mutex g_bounds_mu;
+uint32_t* g_bounds_ptr[kMaxBoundsDevices];
+
+// Address of the current device's flag word (debug builds), else null.
+uint32_t* bounds_flags_ptr() {
+#ifdef Q8_DEBUG_BOUNDS
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxBoundsDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_bounds_mu);
+    if (!g_bounds_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(bounds_word)) != hipSuccess) return nullptr;
+        g_bounds_ptr[dev] = static_cast<uint32_t*>(p);
+    }
+    return g_bounds_ptr[dev];
+#else
+    return nullptr;
+#endif
+}
+
 bool head_size_ok(uint32_t hs) { return hs != 0 && hs % 4 == 0 && hs <= Q8_MAX_HEAD_SIZE; }
 
 }  // namespace
@@ -46,6 +76,7 @@ q8_status q8_cache_write(const float* key, uint32_t key_stride,
     a.head_size = head_size;
     a.block_size = block_size;
     a.num_blocks = num_blocks;
+    a.bounds_flags = bounds_flags_ptr();
     const hipError_t e = q8kv::launch_cache_write(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
@@ -194,6 +225,7 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     a.block_size = block_size;
     a.num_blocks = num_blocks;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.bounds_flags = bounds_flags_ptr();
     if (app) {
         a.new_key = app->key;
         a.new_value = app->value;
@@ -550,6 +582,22 @@ q8_status q8_index_select(const float* scores, uint32_t score_stride, const uint
 }
 
 int q8_last_hip_error(void) { return g_last_hip_error; }
+
+q8_status q8_bounds_flags(uint32_t* flags, int clear) {
+    if (!flags) return Q8_ERR_NULL;
+    *flags = 0;
+#ifdef Q8_DEBUG_BOUNDS
+    uint32_t* p = bounds_flags_ptr();
+    if (!p) return hip_fail(hipErrorInvalidSymbol);
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(flags, p, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) e = hipMemset(p, 0, sizeof(uint32_t));
+    return e == hipSuccess ? Q8_OK : hip_fail(e);
+#else
+    (void)clear;
+    return Q8_ERR_UNSUPPORTED;
+#endif
+}
 
 const char* q8_status_string(q8_status status) {
     switch (status) {

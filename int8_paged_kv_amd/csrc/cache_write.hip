@@ -11,6 +11,7 @@
 // f32 values, an amax reduction across the lanes of its half (or wave), four
 // IEEE multiplies, v_rndne, clamp and a byte pack.
 #include "q8kv_internal.h"
+#include "bounds.h"
 #include "q8_pack.h"
 #include "wave_ops.h"
 
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool
     for (int i = 0; i < NP; ++i) {
         if (slot[i] == kPadSlot) continue;
         const uint32_t block = slot[i] / a.block_size, off = slot[i] - block * a.block_size;
+        bounds_report(a.bounds_flags, block >= a.num_blocks, kBoundSlot);
         if (block >= a.num_blocks) continue;         // out of contract; skipped rather than written out of bounds
         const uint64_t dst = ((static_cast<uint64_t>(block) * a.num_kv_heads + head[i]) * a.block_size + off) * wpt;
         if (HALF) {

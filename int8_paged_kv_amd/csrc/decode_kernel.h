@@ -46,6 +46,7 @@
 //     MFMA output row group is one head, so the per-head max and sum reduce
 //     over the 16 lanes of a DPP row.
 #pragma once
+#include "bounds.h"
 #include "decode_split.h"
 #include "q8_pack.h"
 #include "wave_ops.h"
@@ -117,11 +118,13 @@ __device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s
     uint32_t n;
     if (VIS) {
         n = a.num_visible[s];
+        bounds_report(a.bounds_flags, n > a.vis_stride, kBoundVisible);
         n = n < a.vis_stride ? n : a.vis_stride;
     } else {
         n = a.context_lens[s];
         n = n < a.max_context_len ? n : a.max_context_len;
         const uint64_t cap = static_cast<uint64_t>(a.max_num_blocks_per_seq) * a.block_size;
+        bounds_report(a.bounds_flags, n > cap, kBoundTable);
         if (n > cap) n = static_cast<uint32_t>(cap);   // defensive: never index past a table row
     }
     return n;
@@ -562,8 +565,19 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
         }
         const uint32_t k = min(lane, nseg - 1);
         uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(CH) ? k : 0u);
+        // a segment holding attended positions (its first row below nv)
+        const bool used = lane < nseg && k * c.seg_rows < nv;
+        bounds_report(a.bounds_flags, used && jb >= a.max_num_blocks_per_seq, kBoundTable);
         jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
         m.id = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
+#ifdef Q8_DEBUG_BOUNDS
+        bounds_report(a.bounds_flags, used && (tiled != 0) && m.id > num_blocks_m1, kBoundBlock);
+        if (VIS && nv > 0 && tiled) {
+            // a tile run must be exactly the listed positions p0 .. p0 + nv - 1
+            const uint32_t pl_ = position_at<VIS>(a, m.s, m.cs + min(lane, nv - 1));
+            bounds_report(a.bounds_flags, lane < nv && pl_ != m.p0 + lane, kBoundVisible);
+        }
+#endif
         return m;
     };
 
@@ -698,6 +712,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             const uint32_t blk = uniform(a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + pos / a.block_size]);
             // An out-of-range block id breaks the caller contract: nothing is
             // written for it (a clamped id would overwrite another block's row).
+            bounds_report(a.bounds_flags, lane == 0 && blk > num_blocks_m1, kBoundBlock);
             if (blk > num_blocks_m1) return;
             const uint64_t dst = ((static_cast<uint64_t>(blk) * a.num_kv_heads + kvh) * a.block_size + pos % a.block_size) * wpt;
             if (lane < hs4) { a.key_cache_w[dst + lane] = kw; a.value_cache_w[dst + lane] = vw; }
@@ -740,8 +755,15 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             const uint32_t nv = meta_nv(m);
             const uint32_t pos = position_at<VIS>(a, m.s, m.cs + min(lane, nv - 1));
             uint32_t jb = pos / a.block_size;
+            bounds_report(a.bounds_flags, lane < nv && jb >= a.max_num_blocks_per_seq, kBoundTable);
+#ifdef Q8_DEBUG_BOUNDS
+            // listed positions ascending and distinct within the chunk
+            const uint32_t prev = __shfl(pos, lane > 0 ? lane - 1 : 0, 64);
+            bounds_report(a.bounds_flags, lane > 0 && lane < nv && pos <= prev, kBoundVisible);
+#endif
             jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
             uint32_t phys = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
+            bounds_report(a.bounds_flags, lane < nv && phys > num_blocks_m1, kBoundBlock);
             phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
             const uint64_t my_row = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size +
                                      pos % a.block_size) * wpt;

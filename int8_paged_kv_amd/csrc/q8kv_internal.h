@@ -25,6 +25,7 @@ struct CacheWriteArgs {
     const uint32_t* slot_mapping;
     uint32_t key_stride, value_stride;
     uint32_t num_tokens, num_kv_heads, head_size, block_size, num_blocks;
+    uint32_t* bounds_flags;  // Q8_DEBUG_BOUNDS builds: device flag word of failed content checks
 };
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
@@ -131,6 +132,7 @@ struct DecodeArgs {
     // of sequence v / rows_per_seq (its block-table row), and attends the first
     // context_lens[seq] - rows_per_seq + (v % rows_per_seq) + 1 positions.
     uint32_t rows_per_seq;
+    uint32_t* bounds_flags;  // Q8_DEBUG_BOUNDS builds: device flag word of failed content checks
 };
 
 // max_positions: max_context_len in dense mode, vis_stride with visible lists.

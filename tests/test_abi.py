@@ -300,3 +300,17 @@ def test_noalloc_validation_matches_decode(lib, kw, want):
     assert lib.q8_paged_decode(*a) == want
     del a[19:21]
     assert lib.q8_paged_decode_noalloc(*a) == want
+
+
+def test_bounds_flags_release_and_debug(lib):
+    """The release library has no content checks (Q8_ERR_UNSUPPORTED, flags 0);
+    the debug build exports every declared symbol as well."""
+    f = ctypes.c_uint32(7)
+    assert lib.q8_bounds_flags(ctypes.byref(f), 0) == 5 and f.value == 0
+    assert lib.q8_bounds_flags(None, 0) == 1
+    from int8_paged_kv_amd import _binding
+    if not os.path.exists(_binding.DEBUG_LIB_PATH):
+        pytest.skip("libq8kv_debug.so not built")
+    dbg = _binding.load_debug_library()
+    for name in declared_functions():
+        assert hasattr(dbg, name), name
