@@ -29,7 +29,7 @@ DecodePlan plan_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_he
                        uint32_t head_size, uint32_t block_size, uint32_t max_positions, uint64_t target) {
     DecodePlan p{};
     const uint32_t n_rep = num_kv_heads ? num_heads / num_kv_heads : 1;
-    p.group = n_rep > 4 ? 8 : 4;
+    p.group = decode_group(n_rep);
     p.num_groups = (n_rep + p.group - 1) / p.group;
     (void)block_size;
     // The persistent wavefronts are shared evenly by the row groups.
@@ -105,9 +105,9 @@ hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_
     const uint32_t wpt = hs4 + 1;
     // Query heads per kv head: (row, head) pairs in multi-row decode.
     const uint32_t num_pairs = a.num_heads * (a.rows_per_seq > 1 ? a.rows_per_seq : 1u);
-    const uint32_t group = num_pairs / a.num_kv_heads > 4 ? 8 : 4;
+    const uint32_t group = decode_group(num_pairs / a.num_kv_heads);
     const uint32_t hs4p = hs4 <= 16 ? 16 : hs4 <= 32 ? 32 : hs4 <= 48 ? 48 : 64;
-    const uint32_t ch = static_cast<uint32_t>(decode_chunk(static_cast<int>(hs4p), group == 8 ? 2 : 1));
+    const uint32_t ch = static_cast<uint32_t>(decode_chunk(static_cast<int>(hs4p), static_cast<int>(group / 4)));
     SplitConsts c{};
     c.seg_rows = a.block_size < ch ? a.block_size : ch;
     const bool shape_ok = a.block_size % 4 == 0 && (ch % a.block_size == 0 || a.block_size % ch == 0);

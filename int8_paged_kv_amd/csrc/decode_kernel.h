@@ -11,12 +11,12 @@
 //
 // MI355X design (not the page's one-workgroup-per-(seq, head) three-pass
 // shader):
-//   * Positions are processed in chunks of 64.  For one row group (kv head,
-//     up to 8 of its query heads; in multi-row decode, up to 8 (row, head)
-//     pairs) the chunks of all sequences form one sequence of C chunks, and a
+//   * Positions are processed in chunks of 32 or 64.  For one row group (kv
+//     head, up to 16 of its query heads; in multi-row decode, up to 16 (row,
+//     head) pairs) the chunks of all sequences form one sequence of C chunks, and a
 //     fixed number of persistent wavefronts per row group each take an equal
-//     contiguous range of it, weighted by cost (a chunk 4 units, the fixed
-//     work of each nonempty sequence 7).  This is the split-context idea of the
+//     contiguous range of it, weighted by cost (a chunk, plus the fixed work
+//     of each nonempty sequence).  This is the split-context idea of the
 //     "attention.rs" page, balanced over the whole batch instead of per
 //     sequence.  A wave that covers a whole sequence writes its output
 //     directly; otherwise it writes a softmax partial (running max, sum,
@@ -280,7 +280,7 @@ struct Shares {
 //   sums of those dimensions for head g.
 //
 // HS4P: code words per row rounded up to 16, 32, 48 or 64; EXACT: head_size /
-// 4 == HS4P; NHS: sets of 4 query heads per wavefront (1 or 2); VIS: visible
+// 4 == HS4P; NHS: sets of 4 query heads per wavefront (1, 2 or 4); VIS: visible
 // list positions; TILED: every chunk is known to be a tile run (dense
 // positions, aligned caches, block_size dividing or a multiple of 64); SEGR:
 // when nonzero (16 or 32, with EXACT), the rows per tile segment, for which
@@ -787,7 +787,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     // values) staged per lane as QF 16-byte slots: lane l, slot t holds padded
     // elements 4*(l + 64*t) .. +3.
     constexpr int QF = G * QD / (4 * kWave);
-    static_assert(QSCR ? QF * kWave <= NHS * 16 * 16 : NHS * NKB * 256 + QF * kWave <= BUFW, "q scratch");
+    static_assert(QF * kWave <= NHS * 16 * 16 && (QSCR || NHS * NKB * 256 <= BUFW), "q scratch");
     float4 qv[QF];
     auto q_issue = [&](uint32_t s) __attribute__((always_inline)) {
         const uint64_t row = static_cast<uint64_t>(s) * nrow * a.q_stride;
@@ -818,8 +818,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
         uint32_t* const scratch = QSCR ? sQs_[wid] : sKn;   // sKn: no loads are landing in it yet
         uint32_t* const sDig = scratch;
         // per-slot maxima: in sA (not in use outside a chunk's processing)
-        // when the digits have a scratch of their own
-        float* const sMax = QSCR ? reinterpret_cast<float*>(sA) : reinterpret_cast<float*>(scratch) + NHS * NKB * 256;
+        float* const sMax = reinterpret_cast<float*>(sA);
 #pragma unroll
         for (int t = 0; t < QF; ++t) {
             const float4 v = qv[t];
@@ -1013,7 +1012,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     // number of items.
     auto merge = [&](uint32_t ms, uint32_t jf, uint32_t nrec) __attribute__((always_inline)) {
         // records per batch: MB * NHS * NCW 16-byte values in registers
-        constexpr int MB = NHS * NCW <= 4 ? 8 : 4;
+        constexpr int MB = NHS * NCW <= 4 ? 8 : NHS * NCW <= 8 ? 4 : 2;
         const uint64_t rec0 = static_cast<uint64_t>(rg) * c.recs_per_rg + ms + jf;      // record of wave jf
         float M[NHS], L[NHS];
         f32x4 o[NHS][NCW];
@@ -1213,6 +1212,7 @@ const void* split_kernel_t(bool vis, bool tiled, uint32_t seg_rows) {
 
 template <int HS4P, bool EXACT>
 const void* split_kernel_g(bool vis, bool tiled, uint32_t group, uint32_t seg_rows) {
+    if (group == 16) return split_kernel_t<HS4P, EXACT, 4>(vis, tiled, seg_rows);
     if (group == 8) return split_kernel_t<HS4P, EXACT, 2>(vis, tiled, seg_rows);
     return split_kernel_t<HS4P, EXACT, 1>(vis, tiled, seg_rows);
 }

@@ -14,6 +14,11 @@ constexpr uint32_t kWavesPerGroup = 4;
 // 4 query heads per wavefront.
 constexpr int decode_chunk(int hs4p, int nhs) { return hs4p <= 32 && nhs == 1 ? 32 : 64; }
 
+// Query heads (or, in multi-row decode, (row, head) pairs) of one kv head
+// handled together by a wavefront, so that each K/V byte is read once for
+// them: 4, 8 or 16 (n_rep above 16 takes several groups of 16).
+constexpr uint32_t decode_group(uint32_t n_rep) { return n_rep > 8 ? 16u : n_rep > 4 ? 8u : 4u; }
+
 struct SplitConsts {
     uint32_t waves_per_rg;  // persistent wavefronts per row group (before capping by the chunk count)
     uint32_t num_rg;        // row groups: num_kv_heads * num_groups

@@ -94,7 +94,7 @@ def test_workspace_size_matches_plan(lib):
     # sequence lies in one wavefront's range, no partials.
     assert lib.q8_paged_decode_workspace_bytes(2, 4, 2, 128, 16, 32) == 0
     assert lib.q8_paged_decode_workspace_bytes(2, 4, 2, 128, 16, 33) > 0
-    # Otherwise: per row group (kv head, group of 4 or 8 query heads),
+    # Otherwise: per row group (kv head, group of 4, 8 or 16 query heads),
     # (waves per group + S - 1) records of (head_size + 2) floats per head.
     # Layout: arrival counters (one u32 per row group and sequence), then the
     # records' outputs, then their (max, sum) pairs, each 256-byte aligned.
@@ -106,8 +106,9 @@ def test_workspace_size_matches_plan(lib):
     assert lib.q8_paged_decode_workspace_bytes(64, 32, 8, 128, 16, 4096) == want(64, 128, 8, 4)
     # n_rep 8 uses groups of 8 query heads
     assert lib.q8_paged_decode_workspace_bytes(8, 64, 8, 128, 32, 32768) == want(8, 128, 8, 8)
-    # n_rep 16: two groups of 8 per kv head
-    assert lib.q8_paged_decode_workspace_bytes(2, 32, 2, 64, 16, 500) == want(2, 64, 4, 8)
+    # n_rep 16: one group of 16 per kv head; n_rep 32: two groups of 16
+    assert lib.q8_paged_decode_workspace_bytes(2, 32, 2, 64, 16, 500) == want(2, 64, 2, 16)
+    assert lib.q8_paged_decode_workspace_bytes(2, 64, 2, 64, 16, 500) == want(2, 64, 4, 16)
 
 
 def step_args(**kw):
