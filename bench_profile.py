@@ -34,21 +34,21 @@ DECODE_KERNELS = ("decode_split_kernel",)
 WRITE_KERNEL = "cache_write_kernel"
 
 TRACE_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d {d}/trace -o bench -f csv "
-             "-- python3 /root/repo/bench.py --steps 20 --warmup 5 --no-cpu --no-reference")
+             "-- python3 /root/repo/bench.py --steps 200 --warmup 20 --no-cpu --no-reference --no-hot")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {c} -d {d}/pmc_{c} -o bench -f csv "
-           "-- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
+           "-- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference --prime-s 0 --no-hot")
 TRACE_ALL_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d {d}/trace_all -o bench -f csv "
-                 "-- python3 /root/repo/bench.py --steps 20 --warmup 5 --no-cpu")
+                 "-- python3 /root/repo/bench.py --steps 200 --warmup 20 --no-cpu --no-hot")
 L2_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum "
-          "-d {d}/pmc_L2 -o bench -f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
+          "-d {d}/pmc_L2 -o bench -f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference --prime-s 0 --no-hot")
 PMC_ALL_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {c} -d {d}/pmc_all_{c} -o bench "
-               "-f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu")
+               "-f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --prime-s 0 --no-hot")
 SQ_PASSES = (("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM",
               "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
              ("SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA",
               "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM", "SQ_WAVES"))
 SQ_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {cs} -d {d}/pmc_sq{i} -o bench "
-          "-f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference")
+          "-f csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-cpu --no-reference --prime-s 0 --no-hot")
 COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} -d {d}/copy_{c} -o copy -f csv "
             "-- python3 /root/repo/bench.py --copy-calibration {mib}")
 
@@ -115,18 +115,22 @@ def main():
                    int(r["Scratch_Size"]))].append(dur)
     bench_trace = last_json(os.path.join(d, "trace.log"))
     digest = bench_trace["kernel_sources_sha256_16"]
-    # The step's launches are the ones with as many dispatches as the step count
-    # (warmup + timed + event-timed steps); fill-phase launches use other grids.
-    n_step = 2 * bench_trace["steps"] + bench_trace["warmup"]
+    # The step's launches: the decode kernel's (kernel, grid) with the most
+    # dispatches (warmup, timed and event-timed steps); fill-phase launches
+    # are the cache writer's.
     step_grid = {}
+    best = {}
+    for key, durs in trace.items():
+        for k in DECODE_KERNELS:
+            if k in key[0] and len(durs) > best.get(k, 0):
+                best[k] = len(durs)
+                step_grid[k] = key[1]
     rows = []
     for key, durs in sorted(trace.items(), key=lambda kv: -sum(kv[1])):
         name, grid, wg, vgpr, agpr, sgpr, lds, scr = key
-        tag = next((k for k in DECODE_KERNELS + (WRITE_KERNEL,) if k in name), None)
-        if tag and len(durs) == n_step:
-            step_grid[tag] = grid
+        is_step = any(k in name and grid == step_grid.get(k) for k in DECODE_KERNELS)
         rows.append((short(name), grid, wg, len(durs), statistics.mean(durs), statistics.median(durs),
-                     min(durs), max(durs), vgpr, agpr, sgpr, lds, scr, tag is not None and len(durs) == n_step))
+                     min(durs), max(durs), vgpr, agpr, sgpr, lds, scr, is_step))
 
     split_us = mean_of(rows, "decode_split_kernel")
     eff = bench_trace["config"]["effective_kv_bytes"]
@@ -154,8 +158,9 @@ def main():
         "",
         "step launch (decode_split_kernel mean): %.2f us" % split_us,
         "  effective int8 KV bytes per step: %d -> %.1f GB/s" % (eff, eff / (split_us * 1e-6) / 1e9),
-        "bench.py in the same run (HIP events on the launch stream): step launch us_mean %.2f, effective %.1f GB/s" % (
-            bench_trace["step_launch"]["us_mean"], bench_trace["step_launch"]["effective_GBps"]),
+        "bench.py in the same run (HIP events on the launch stream around the timed launches): %.2f us per "
+        "launch, effective %.1f GB/s" % (bench_trace["step_launch"]["us_mean_back_to_back"],
+                                         bench_trace["step_launch"]["effective_GBps"]),
         "",
         "rocprofv3 --stats table (all dispatches of each kernel, fill phase included):",
     ]
@@ -179,7 +184,9 @@ def main():
         out = [
             "# rocprofv3 kernel trace of every kernel the bench runs, Llama-3-8B-shaped batch",
             "# (step, two-launch reference, 4-row decode, f32-cache step, norm + rotary step, 16384-token bulk",
-            "# writes, selected-token step: block selection + visible-list decode)",
+            "# writes, selected-token step: block selection + visible-list decode, long-context decode,",
+            "# MHA head_size=256 decode and its 4096-token padded write, and the measurement kernels of the",
+            "# practical HBM ceiling)",
             "#",
             "# command (from any directory on the GPU machine):",
             "#   " + TRACE_ALL_CMD.format(d=args.cmd_dir),
@@ -196,7 +203,7 @@ def main():
                 nm[:60], grid, len(durs), statistics.mean(durs), statistics.median(durs), max(durs), vgpr, lds))
         out += ["", "bench.py line of the same run (reference legs):"]
         for k in ("two_launch_reference", "multi_row_decode", "f32_cache_reference", "norm_rope_step",
-                  "selected_step"):
+                  "selected_step", "long_context", "mha256_decode", "mha256_write", "practical_ceiling"):
             out.append("  %s: %s" % (k, json.dumps(allj.get(k))))
         with open(os.path.join(ROOT, "profiles", "llama_step_all_kernels_trace.txt"), "w") as f:
             f.write("\n".join(out) + "\n")
@@ -317,8 +324,11 @@ def main():
                       "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA"):
                 if c in vals:
                     q.append("  %-26s %.3f" % (c, vals[c] / wc))
-        if vals.get("SQ_BUSY_CYCLES") and vals.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
-            q.append("  MFMA busy / SQ busy cycles  %.3f" % (vals["SQ_VALU_MFMA_BUSY_CYCLES"] / vals["SQ_BUSY_CYCLES"]))
+        if vals.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None and split_us:
+            # summed over the 256 CUs; the step's cycles from the trace's mean at the 2.4 GHz peak clock
+            per_cu = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / 256
+            q += ["", "MFMA busy cycles per CU %.0f over a %.2f us step (%.0f cycles at 2.4 GHz): %.3f"
+                  % (per_cu, split_us, split_us * 2400, per_cu / (split_us * 2400))]
         with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_sq_counters.txt"), "w") as f:
             f.write("\n".join(q) + "\n")
 
@@ -341,7 +351,8 @@ def main():
             durs = {k: statistics.median(v) for k, v in acc.items()}
         out = [
             "# HBM traffic of every kernel the bench runs (step, two-launch reference, 4-row decode, f32-cache",
-            "# step, norm + rotary step and 16384-token bulk writes, selected-token step), median per dispatch",
+            "# step, norm + rotary step and 16384-token bulk writes, selected-token step, long-context and",
+            "# MHA-256 decodes, the padded 4096-token write, ceiling kernels), median per dispatch",
             "# of each (kernel, grid), calibrated by the plain copy as in q8_paged_decode_llama_traffic.txt",
             "# (FETCH_SIZE x %.4f, WRITE_SIZE x %.4f)" % (factor["FETCH_SIZE"], factor["WRITE_SIZE"]),
             "#",
@@ -368,20 +379,48 @@ def main():
             out.append("%-52s %9d %5d %14.0f %13.0f %9s %9s" % (
                 nm[:52], key[1], len(cf[key]), rd, wr, "%.2f" % us if us else "-",
                 "%.0f" % ((rd + wr) / (us * 1e-6) / 1e9) if us else "-"))
-        mr, f32, nr, sel = (jf.get(k) or {} for k in ("multi_row_decode", "f32_cache_reference", "norm_rope_step",
-                                                        "selected_step"))
+        mr, f32, nr, sel, lg, md, mw = (jf.get(k) or {} for k in (
+            "multi_row_decode", "f32_cache_reference", "norm_rope_step", "selected_step", "long_context",
+            "mha256_decode", "mha256_write"))
         out += [
             "",
             "algorithmic bytes of the reference legs (bench.py line of the FETCH_SIZE run):",
             "  step decode: %d (int8 KV of every attended row, K and V)" % eff,
             "  4-row decode: the same prefixes, read once when the rows of a sequence share the reads: %d;"
-            " counted per row: %s" % (eff, mr.get("effective_kv_bytes")),
+            " counted per row: %s" % (eff, mr.get("per_row_kv_bytes")),
             "  f32-cache decode: %s" % f32.get("f32_kv_bytes"),
             "  bulk writes (16384 tokens): %s" % nr.get("bulk_algorithmic_bytes"),
             "  selected-token decode: %s" % sel.get("effective_kv_bytes"),
+            "  long-context decode: %s" % lg.get("effective_kv_bytes"),
+            "  MHA head_size=256 decode: %s" % md.get("effective_kv_bytes"),
+            "  MHA head_size=256 4096-token write: %s" % mw.get("algorithmic_bytes"),
         ]
         with open(os.path.join(ROOT, "profiles", "llama_step_all_kernels_traffic.txt"), "w") as f:
             f.write("\n".join(out) + "\n")
+        # the legs' kernels: the (kernel, grid) of the leg's instantiation launched most often
+        legs = {"long_context": "decode_split_kernel<32, true, 2, false, true, 32, 64>",
+                "mha256_decode": "decode_split_kernel<64, true, 1, false, true, 16, 64>",
+                "mha256_write": "cache_write_kernel<false, 4>"}
+        lt = [
+            "# HBM bytes per launch of the long-context decode, the MHA head_size=256 decode and its padded",
+            "# 4096-token write (bench.py legs long_context, mha256_decode, mha256_write), from the runs of",
+            "# llama_step_all_kernels_traffic.txt; bench.py reads these while the sources match the digest.",
+            "# Each leg's kernel is its instantiation's (kernel, grid) with the most dispatches.",
+            "",
+            "kernel_sources_sha256_16: %s" % digest,
+        ]
+        for leg, sig in legs.items():
+            cands = [k for k in cf if sig in k[0] and k in cw]
+            if not cands:
+                continue
+            key = max(cands, key=lambda k: len(cf[k]))
+            rd = statistics.median(cf[key]) * 1024.0 * factor["FETCH_SIZE"]
+            wr = statistics.median(cw[key]) * 1024.0 * factor["WRITE_SIZE"]
+            lt += ["# %s: %s grid %d, %d dispatches: read %.0f B, written %.0f B" % (
+                leg, sig, key[1], len(cf[key]), rd, wr),
+                   "%s_hbm_bytes_per_launch: %.0f" % (leg, rd + wr)]
+        with open(os.path.join(ROOT, "profiles", "bench_legs_traffic.txt"), "w") as f:
+            f.write("\n".join(lt) + "\n")
     print("wrote profiles/q8_paged_decode_llama_kernel_trace.txt and profiles/q8_paged_decode_llama_traffic.txt")
 
 
