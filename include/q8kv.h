@@ -55,7 +55,7 @@ typedef enum {
     Q8_ERR_SHAPE = 2,        /* sizes or strides violate the limits listed per call */
     Q8_ERR_WORKSPACE = 3,    /* workspace too small or not 16-byte aligned */
     Q8_ERR_HIP = 4,          /* a HIP launch failed; see q8_last_hip_error() */
-    Q8_ERR_UNSUPPORTED = 5   /* a valid combination this build does not handle */
+    Q8_ERR_UNSUPPORTED = 5   /* a valid combination the library does not handle */
 } q8_status;
 
 /*

@@ -14,13 +14,13 @@
  *   head_size/4 code words, four int8 codes per word with element 4w+l in byte
  *   l (little-endian lane), followed by one word holding the f32 scale's bits.
  *
- *   Quantize + pack ("reshape_and_cache_q8.comp" page, main(): the KEY block
- *   "amax reduce -> scale -> pack" and the identical VALUE block).  Binary32,
+ *   Quantize + pack ("reshape_and_cache_q8.comp" page, main(), its KEY block
+ *   and the VALUE block that repeats it for V).  Binary32,
  *   one IEEE operation per step, as the page's shader states them:
  *     amax = max_d |x_d| (starting from 0)
  *     inv  = amax > 0 ? 127/amax : 0
  *     code = clamp(round(x_d * inv), -127, 127), ties to even (the page leaves
- *            the tie rule to the implementation; this build fixes even)
+ *            the tie rule to the implementation; ties go to even here)
  *     scale word = bits(amax > 0 ? amax/127 : 1.0)
  *   A slot equal to 0xFFFFFFFF is a pad: nothing is read or written.
  *
