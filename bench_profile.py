@@ -53,10 +53,15 @@ COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc
             "-- python3 /root/repo/bench.py --copy-calibration {mib}")
 
 
+def kname(name: str) -> str:
+    """A kernel's name without its return type, namespaces and parameter list."""
+    return name.replace("void ", "").replace("q8kv::", "").replace("(anonymous namespace)::", "").split("(")[0]
+
+
 def short(name: str) -> str:
     for k in DECODE_KERNELS + (WRITE_KERNEL, "copyBuffer"):
         if k in name:
-            return name.replace("void ", "").replace("q8kv::(anonymous namespace)::", "").split("(")[0]
+            return kname(name)
     return name[:60]
 
 
@@ -198,7 +203,7 @@ def main():
                                                   "vgpr", "lds"),
         ]
         for (name, grid, vgpr, lds), durs in sorted(per.items(), key=lambda kv: -sum(kv[1])):
-            nm = name.replace("void ", "").replace("q8kv::(anonymous namespace)::", "").split("(")[0]
+            nm = kname(name)
             out.append("%-60s %9d %5d %9.2f %9.2f %9.2f %5d %6d" % (
                 nm[:60], grid, len(durs), statistics.mean(durs), statistics.median(durs), max(durs), vgpr, lds))
         out += ["", "bench.py line of the same run (reference legs):"]
@@ -375,7 +380,7 @@ def main():
             if rd + wr < 1e6:
                 continue
             us = durs.get(key)
-            nm = key[0].replace("void ", "").replace("q8kv::(anonymous namespace)::", "").split("(")[0]
+            nm = kname(key[0])
             out.append("%-52s %9d %5d %14.0f %13.0f %9s %9s" % (
                 nm[:52], key[1], len(cf[key]), rd, wr, "%.2f" % us if us else "-",
                 "%.0f" % ((rd + wr) / (us * 1e-6) / 1e9) if us else "-"))

@@ -387,9 +387,9 @@ q8_status q8_norm_rope(float* out, uint32_t out_stride, const float* x, uint32_t
  * head's K vector becomes its normalized, rotated self at positions[t]
  * (weight: the K norm weight) and is packed as q8_cache_write packs it; V is
  * packed unchanged.  The arguments shared with q8_cache_write mean the same;
- * weight, table, rot, num_positions and eps are as for q8_norm_rope.  A pad
- * token's position (like its rows) may be read but is not used.  Errors: those of q8_cache_write plus the
- * shape rules of q8_norm_rope.
+ * weight, table, rot, num_positions and eps are as for q8_norm_rope.  Nothing
+ * is read or written for a pad token (rows, position).  Errors: those of
+ * q8_cache_write plus the shape rules of q8_norm_rope.
  */
 q8_status q8_norm_rope_cache_write(const float* key, uint32_t key_stride,
                                    const float* value, uint32_t value_stride,

@@ -194,18 +194,25 @@ __device__ __forceinline__ void norm_rope_write_pairs(const NormRopeCacheWriteAr
     const uint32_t h0 = static_cast<uint32_t>(first - static_cast<uint64_t>(t0) * a.num_kv_heads);
     const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
     float4 xk[NP], xv[NP];
-    uint32_t head[NP], slot[NT], posn[NT];
+    uint32_t head[NP], tok[NP], slot[NT], posn[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) slot[i] = kPadSlot, posn[i] = 0;
+    // The slots come first (wave-uniform scalar loads); a pad token's rows and
+    // position are then not read at all, and nothing is written for it.
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-        xk[i] = xv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         uint32_t t = t0, h = h0 + i;
         if (!SAME_T && h >= a.num_kv_heads) h -= a.num_kv_heads, ++t;
         head[i] = h;
-        if (first + i >= pairs) continue;                // wave-uniform
-        // A pad token's rows and position may be read (loaded with the slot),
-        // but nothing is written for it.
+        tok[i] = t;
+        if (first + i < pairs && (!SAME_T || i == 0)) slot[SAME_T ? 0 : i] = a.slot_mapping[t];
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        xk[i] = xv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int ti = SAME_T ? 0 : i;
+        if (first + i >= pairs || slot[ti] == kPadSlot) continue;    // wave-uniform
+        const uint32_t t = tok[i], h = head[i];
         const float* ksrc = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size;
         const float* vsrc = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size;
         if (PAIRED) {
@@ -217,12 +224,9 @@ __device__ __forceinline__ void norm_rope_write_pairs(const NormRopeCacheWriteAr
             xk[i] = load4(ksrc + 4 * lane, vec4);
             xv[i] = load4(vsrc + 4 * lane, vec4);
         }
-        if (!SAME_T || i == 0) {
-            slot[SAME_T ? 0 : i] = a.slot_mapping[t];
-            if (a.rot > 0) posn[SAME_T ? 0 : i] = a.positions[t];
-        }
+        if ((!SAME_T || i == 0) && a.rot > 0) posn[ti] = a.positions[t];
     }
-    if (PAIRED && (lane & 31) < hs4) {
+    if (PAIRED && slot[0] != kPadSlot && (lane & 31) < hs4) {
         // register set j: head h0+2j in lanes 0-31, h0+2j+1 in lanes 32-63; K in xk, V in xv
 #pragma unroll
         for (int j = 0; j < NP / 2; ++j) {
