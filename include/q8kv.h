@@ -78,8 +78,10 @@ typedef enum {
  * and the round() of the page is round-half-even.  The output is bit-exact.
  * Errors: Q8_ERR_NULL for a NULL array with num_tokens > 0; Q8_ERR_SHAPE when
  * head_size is 0, not a multiple of 4 or above 256, when block_size or
- * num_kv_heads is 0, or when a stride is below num_kv_heads*head_size.
- * num_tokens == 0 returns Q8_OK and enqueues nothing.
+ * num_kv_heads is 0, when a stride is below num_kv_heads*head_size, or when
+ * the launch would need more than 2^31 - 1 workgroups (one per 16 tokens of a
+ * kv head once num_tokens*num_kv_heads reaches 32768, one per four (token,
+ * kv head) pairs below).  num_tokens == 0 returns Q8_OK and enqueues nothing.
  */
 q8_status q8_cache_write(const float* key, uint32_t key_stride,
                          const float* value, uint32_t value_stride,

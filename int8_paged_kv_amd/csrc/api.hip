@@ -63,6 +63,7 @@ q8_status q8_cache_write(const float* key, uint32_t key_stride,
     if (num_tokens == 0) return Q8_OK;
     if (!key || !value || !key_cache || !value_cache || !slot_mapping) return Q8_ERR_NULL;
     if (num_blocks == 0) return Q8_ERR_SHAPE;
+    if (q8kv::cache_write_blocks(num_tokens, num_kv_heads) > q8kv::kMaxGridBlocks) return Q8_ERR_SHAPE;
     q8kv::CacheWriteArgs a{};
     a.key = key;
     a.value = value;

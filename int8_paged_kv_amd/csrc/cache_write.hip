@@ -4,12 +4,17 @@
 // head) and for K then V (the quantizer is in q8_pack.h).  A pad slot
 // (0xFFFFFFFF) skips the token: nothing is read or written for it.
 //
-// MI355X mapping: one wavefront per (token, kv head), or in large writes per
-// group of consecutive ones whose loads are all in flight together.  When
-// head_size <= 128 the two 32-lane halves quantize K and V side by side;
-// otherwise the whole wave does K and then V.  Each lane owns one code word: a 16-byte load of four
-// f32 values, an amax reduction across the lanes of its half (or wave), four
-// IEEE multiplies, v_rndne, clamp and a byte pack.
+// MI355X mapping: one wavefront per (token, kv head) in small writes.  In
+// large ones a workgroup takes 16 consecutive tokens of one kv head, four per
+// wave with all their loads in flight together: when those tokens fill a block
+// in order (a prefill), the workgroup writes that block's whole tile for the
+// head from one compute unit, so its L2 assembles full lines before they go
+// to memory (rows written from different XCDs leave partial lines, which cost
+// the memory a read-modify-write each).  When head_size <= 128 the two 32-lane
+// halves quantize K and V side by side; otherwise the whole wave does K and
+// then V.  Each lane owns one code word: a 16-byte load of four f32 values,
+// an amax reduction across the lanes of its half (or wave), four IEEE
+// multiplies, v_rndne, clamp and a byte pack.
 #include "q8kv_internal.h"
 #include "bounds.h"
 #include "q8_pack.h"
@@ -23,32 +28,50 @@ __device__ __forceinline__ float4 load4(const float* p, bool vec4) {
     return make_float4(p[0], p[1], p[2], p[3]);
 }
 
-// NP consecutive (token, kv head) pairs per wave: every pair's slot, then every
-// non-pad pair's rows, are loaded before any is packed, so a wave keeps NP rows
-// in flight (large writes); NP = 1 for small ones, where the grid is short anyway.
-template <bool HALF, int NP>
+// NP (token, kv head) pairs per wave.  TILES: workgroup b takes tokens
+// 16*(b / num_kv_heads) .. +15 of kv head b % num_kv_heads, wave w the NP = 4
+// consecutive tokens from 16*(b / num_kv_heads) + 4*w.  Otherwise a wave takes
+// NP consecutive pairs of the (token, kv head) order.  Every pair's slot, then
+// every non-pad pair's rows, are loaded before any is packed, so a wave keeps
+// NP rows in flight.
+template <bool HALF, int NP, bool TILES>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteArgs a, bool vec4) {
+    static_assert(!TILES || NP * 4 == 16, "a workgroup of four waves covers 16 tokens");
     const uint32_t lane = threadIdx.x & (kWave - 1);
-    // Wave-uniform pair indices (slots become scalar loads); one division per
-    // wave, the later pairs step through the heads.
-    const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + uniform(threadIdx.x / kWave)) * NP;
-    const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
-    if (first >= pairs) return;
+    const uint32_t wave = uniform(threadIdx.x / kWave);
     const uint32_t hs4 = a.head_size / 4, wpt = hs4 + 1;
     // The slots come first (scalar loads of the wave's tokens); then only the
     // rows of non-pad tokens are loaded, all of them before any is packed.
     float4 x0[NP], x1[NP];
     uint32_t slot[NP], head[NP], tok[NP];
-    uint32_t t = static_cast<uint32_t>(first / a.num_kv_heads);
-    uint32_t h = static_cast<uint32_t>(first - static_cast<uint64_t>(t) * a.num_kv_heads);
+    if (TILES) {
+        const uint32_t h = blockIdx.x % a.num_kv_heads;
+        const uint64_t t0 = static_cast<uint64_t>(blockIdx.x / a.num_kv_heads) * 16 + wave * NP;
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        slot[i] = kPadSlot;
-        if (i > 0 && ++h == a.num_kv_heads) h = 0, ++t;
-        head[i] = h;
-        tok[i] = t;
-        if (first + i < pairs) slot[i] = a.slot_mapping[t];     // wave-uniform
+        for (int i = 0; i < NP; ++i) {
+            slot[i] = kPadSlot;
+            head[i] = h;
+            tok[i] = static_cast<uint32_t>(t0 + i);
+            if (t0 + i < a.num_tokens) slot[i] = a.slot_mapping[t0 + i];     // wave-uniform
+        }
+    } else {
+        // Wave-uniform pair indices (slots become scalar loads); one division
+        // per wave, the later pairs step through the heads.
+        const uint64_t first = (static_cast<uint64_t>(blockIdx.x) * (blockDim.x / kWave) + wave) * NP;
+        const uint64_t pairs = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads;
+        if (first >= pairs) return;
+        uint32_t t = static_cast<uint32_t>(first / a.num_kv_heads);
+        uint32_t h = static_cast<uint32_t>(first - static_cast<uint64_t>(t) * a.num_kv_heads);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            slot[i] = kPadSlot;
+            if (i > 0 && ++h == a.num_kv_heads) h = 0, ++t;
+            head[i] = h;
+            tok[i] = t;
+            if (first + i < pairs) slot[i] = a.slot_mapping[t];     // wave-uniform
+        }
     }
+    uint32_t t, h;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         x0[i] = x1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -89,14 +112,15 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
                       (reinterpret_cast<uintptr_t>(a.value) % 16 == 0) &&
                       a.key_stride % 4 == 0 && a.value_stride % 4 == 0;
     const bool half = a.head_size / 4 <= 32;
+    const uint64_t blocks = cache_write_blocks(a.num_tokens, a.num_kv_heads);
+    if (blocks == 0 || blocks > kMaxGridBlocks) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<uint32_t>(blocks));
     if (pairs >= kWriteBatchMinPairs) {
-        const dim3 grid(static_cast<uint32_t>((pairs + 4 * kWritePairsPerWave - 1) / (4 * kWritePairsPerWave)));
-        if (half) hipLaunchKernelGGL((cache_write_kernel<true, kWritePairsPerWave>), grid, dim3(256), 0, stream, a, vec4);
-        else hipLaunchKernelGGL((cache_write_kernel<false, kWritePairsPerWave>), grid, dim3(256), 0, stream, a, vec4);
+        if (half) hipLaunchKernelGGL((cache_write_kernel<true, kWritePairsPerWave, true>), grid, dim3(256), 0, stream, a, vec4);
+        else hipLaunchKernelGGL((cache_write_kernel<false, kWritePairsPerWave, true>), grid, dim3(256), 0, stream, a, vec4);
     } else {
-        const dim3 grid(static_cast<uint32_t>((pairs + 3) / 4));
-        if (half) hipLaunchKernelGGL((cache_write_kernel<true, 1>), grid, dim3(256), 0, stream, a, vec4);
-        else hipLaunchKernelGGL((cache_write_kernel<false, 1>), grid, dim3(256), 0, stream, a, vec4);
+        if (half) hipLaunchKernelGGL((cache_write_kernel<true, 1, false>), grid, dim3(256), 0, stream, a, vec4);
+        else hipLaunchKernelGGL((cache_write_kernel<false, 1, false>), grid, dim3(256), 0, stream, a, vec4);
     }
     return hipGetLastError();
 }

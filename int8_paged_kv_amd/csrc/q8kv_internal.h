@@ -16,6 +16,15 @@ constexpr uint32_t kMaxDecodeWaves = 2048;
 // kWritePairsPerWave consecutive pairs with all their loads in flight.
 constexpr uint64_t kWriteBatchMinPairs = 32768;
 constexpr int kWritePairsPerWave = 4;
+// Largest one-dimensional grid (workgroups) a launch may ask for.
+constexpr uint64_t kMaxGridBlocks = 0x7FFFFFFFull;
+// Workgroups of a q8_cache_write launch: one per four (token, kv head) pairs
+// in small writes, one per 16 tokens of a kv head in batched ones.
+inline uint64_t cache_write_blocks(uint32_t num_tokens, uint32_t num_kv_heads) {
+    const uint64_t pairs = static_cast<uint64_t>(num_tokens) * num_kv_heads;
+    if (pairs >= kWriteBatchMinPairs) return (static_cast<uint64_t>(num_tokens) + 15) / 16 * num_kv_heads;
+    return (pairs + 3) / 4;
+}
 
 struct CacheWriteArgs {
     const float* key;

@@ -138,6 +138,7 @@ static void writer_and_step_validation() {
     EXPECT(q8_cache_write(nullptr, 256, k, 256, c, c, sl, 4, 2, 128, 16, 8, nullptr) == Q8_ERR_NULL);
     EXPECT(q8_cache_write(nullptr, 256, nullptr, 256, nullptr, nullptr, nullptr, 0, 2, 128, 16, 8, nullptr) == Q8_OK);
     EXPECT(q8_cache_write(k, 256, k, 256, c, c, sl, 4, 2, 128, 16, 0, nullptr) == Q8_ERR_SHAPE);
+    EXPECT(q8_cache_write(k, 1024, k, 1024, c, c, sl, 0xFFFFFFFFu, 8, 128, 16, 8, nullptr) == Q8_ERR_SHAPE);
     EXPECT(q8_f32_cache_write(k, 256, k, 256, reinterpret_cast<float*>(fake(0x3004)), reinterpret_cast<float*>(c), sl, 4,
                               2, 128, 16, 8, nullptr) == Q8_ERR_UNSUPPORTED);
     // norm + rotary

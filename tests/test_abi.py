@@ -64,6 +64,13 @@ def test_cache_write_shape_errors(lib, hs, bs, hkv, stride, want):
     assert lib.q8_cache_write(FAKE, stride, FAKE, stride, FAKE, FAKE, FAKE, 4, hkv, hs, bs, 8, None) == want
 
 
+def test_cache_write_grid_limit(lib):
+    # a batched write takes one workgroup per 16 tokens of a kv head: 2^28 * 8
+    # of them is past the 2^31 - 1 a launch may ask for
+    assert lib.q8_cache_write(FAKE, 1024, FAKE, 1024, FAKE, FAKE, FAKE, 0xFFFFFFFF, 8, 128, 16, 8, None) == 2
+    assert lib.q8_cache_write(FAKE, 2048, FAKE, 2048, FAKE, FAKE, FAKE, 1 << 31, 16, 128, 16, 8, None) == 2
+
+
 def test_cache_write_null_and_empty(lib):
     assert lib.q8_cache_write(None, 256, FAKE, 256, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
     assert lib.q8_cache_write(None, 256, None, 256, None, None, None, 0, 2, 128, 16, 8, None) == 0
