@@ -286,9 +286,11 @@ q8_status q8_paged_decode_rows(float* out, const float* q, uint32_t q_stride,
  *
  * Errors: Q8_ERR_NULL for a NULL pointer when num_tokens > 0; Q8_ERR_SHAPE
  * when head_size is 0, not a multiple of 4 or above 256, block_size,
- * num_kv_heads or num_blocks is 0, or a stride is below num_kv_heads *
- * head_size; Q8_ERR_UNSUPPORTED when a cache is not 16-byte aligned.
- * num_tokens == 0 enqueues nothing.
+ * num_kv_heads or num_blocks is 0, a stride is below num_kv_heads *
+ * head_size, or the launch would need more than 2^31 - 1 workgroups (one
+ * thread per 16 bytes of the new rows, 256 per workgroup);
+ * Q8_ERR_UNSUPPORTED when a cache is not 16-byte aligned.  num_tokens == 0
+ * enqueues nothing.
  */
 q8_status q8_f32_cache_write(const float* key, uint32_t key_stride,
                              const float* value, uint32_t value_stride,

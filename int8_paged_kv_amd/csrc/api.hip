@@ -318,6 +318,9 @@ q8_status q8_f32_cache_write(const float* key, uint32_t key_stride,
     if (key_stride < row || value_stride < row) return Q8_ERR_SHAPE;
     if (num_tokens == 0) return Q8_OK;
     if (!key || !value || !key_cache || !value_cache || !slot_mapping) return Q8_ERR_NULL;
+    // one thread per 16-byte piece of a (token, kv head) row, 256 per workgroup
+    if ((static_cast<uint64_t>(num_tokens) * num_kv_heads * (head_size / 4) + 255) / 256 > q8kv::kMaxGridBlocks)
+        return Q8_ERR_SHAPE;
     if (reinterpret_cast<uintptr_t>(key_cache) % 16 != 0 || reinterpret_cast<uintptr_t>(value_cache) % 16 != 0)
         return Q8_ERR_UNSUPPORTED;
     if (static_cast<uint64_t>(num_tokens) * row / 4 > 0xFFFFFFFFull * 256) return Q8_ERR_UNSUPPORTED;
@@ -404,7 +407,8 @@ q8_status q8_rope_table(float* table, uint32_t num_positions, uint32_t rot, floa
     if (rot % 2 != 0 || !(theta > 0.0f) || !std::isfinite(theta)) return Q8_ERR_SHAPE;
     if (rot == 0 || num_positions == 0) return Q8_OK;
     if (!table) return Q8_ERR_NULL;
-    if (static_cast<uint64_t>(num_positions) * (rot / 2) > 0xFFFFFFFFull * 256) return Q8_ERR_UNSUPPORTED;
+    // one thread per (position, pair), 256 per workgroup
+    if ((static_cast<uint64_t>(num_positions) * (rot / 2) + 255) / 256 > q8kv::kMaxGridBlocks) return Q8_ERR_UNSUPPORTED;
     const hipError_t e = q8kv::launch_rope_table(table, num_positions, rot, static_cast<double>(theta),
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
@@ -434,7 +438,8 @@ q8_status norm_rope_args(q8kv::NormRopeArgs& a, bool* empty, float* out, uint32_
     }
     if (num_rows == 0 || num_heads == 0) return Q8_OK;
     if (!out || !x || !weight || (rot > 0 && (!table || !positions))) return Q8_ERR_NULL;
-    if (static_cast<uint64_t>(num_rows) * num_heads > 0xFFFFFFFFull * 4) return Q8_ERR_UNSUPPORTED;
+    // at most one (row, head) unit per wave, four waves per workgroup
+    if (static_cast<uint64_t>(num_rows) * num_heads > q8kv::kMaxGridBlocks * 4) return Q8_ERR_UNSUPPORTED;
     a.out = out;
     a.x = x;
     a.positions = positions;
@@ -471,7 +476,8 @@ q8_status norm_rope_write_args(q8kv::NormRopeCacheWriteArgs& a, bool* empty, con
         (rot > 0 && (!table || !positions)))
         return Q8_ERR_NULL;
     if (num_blocks == 0) return Q8_ERR_SHAPE;
-    if (static_cast<uint64_t>(num_tokens) * num_kv_heads > 0xFFFFFFFFull * 4) return Q8_ERR_UNSUPPORTED;
+    // at most one (token, kv head) pair per wave, four waves per workgroup
+    if (static_cast<uint64_t>(num_tokens) * num_kv_heads > q8kv::kMaxGridBlocks * 4) return Q8_ERR_UNSUPPORTED;
     a.key = key;
     a.value = value;
     a.key_cache = key_cache;

@@ -369,8 +369,10 @@ hipError_t launch_norm_rope_qk_cache_write(const NormRopeArgs& q, const NormRope
                                            hipStream_t stream) {
     const uint64_t pairs = static_cast<uint64_t>(k.num_tokens) * k.num_kv_heads;
     const bool no_q = q.num_rows == 0 || q.num_heads == 0;
-    if (pairs >= kWriteBatchMinPairs || no_q || pairs == 0) {
-        // a bulk write keeps its batched kernel; an empty side needs no combined launch
+    if (pairs >= kWriteBatchMinPairs || no_q || pairs == 0 ||
+        (no_q ? 0u : rows_blocks(q)) + (pairs + 3) / 4 > kMaxGridBlocks) {
+        // a bulk write keeps its batched kernel; an empty side needs no combined
+        // launch; nor does a combination whose grid would pass the launch limit
         if (!no_q) {
             const hipError_t e = launch_norm_rope(q, stream);
             if (e != hipSuccess) return e;
