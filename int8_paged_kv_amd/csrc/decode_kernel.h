@@ -64,9 +64,10 @@ constexpr uint32_t kDigitBias = 0x80808080u;
 // and a sequence's start (its q digits, the output or partial record of the
 // previous sequence, the append of the step's new row).  Per-wave stamps on
 // the Llama-shaped batch: with 64-position chunks a start costs about 1.8
-// chunks of wave time, with 32-position chunks about one chunk.
+// chunks of wave time; with 32-position chunks a weight of 1.5 chunks gave
+// the shortest launch (weights of 1 to 2 chunks timed).
 constexpr uint32_t kCostChunk = 4;
-constexpr uint32_t cost_seq(int ch) { return ch == 64 ? 7u : 4u; }
+constexpr uint32_t cost_seq(int ch) { return ch == 64 ? 7u : 6u; }
 
 __device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
