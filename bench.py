@@ -79,11 +79,20 @@ def copy_calibration(mib: int) -> None:
 
 
 # The files the decode kernel (decode_split_kernel), the cache writer and their
-# launches are built from; the committed HBM-traffic figures hold while these
-# are unchanged.
+# launches are built from; the committed HBM-traffic figures hold while their
+# code is unchanged (comments and layout do not count).
 DECODE_SOURCES = ("decode_kernel.h", "decode_split.h", "decode.hip", "decode_hs16.hip", "decode_hs32.hip",
                   "decode_hs48.hip", "decode_hs64.hip", "q8_pack.h", "lane_reduce.h", "wave_ops.h",
-                  "q8kv_internal.h", "cache_write.hip")
+                  "q8kv_internal.h", "bounds.h", "cache_write.hip")
+
+
+def code_only(text: str) -> str:
+    """C++ source with its comments removed and whitespace collapsed (the
+    sources hold no string literal with comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def kernel_sources_digest() -> str:
@@ -91,8 +100,8 @@ def kernel_sources_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int8_paged_kv_amd", "csrc")
     for f in DECODE_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,11 +24,13 @@
 //     arrive for that sequence combines the partials.  Wavefronts are numbered
 //     kv head fastest, so the kv-head slices of the same cache blocks are
 //     requested together.  Each K/V byte is read once per row group.
-//   * A chunk of 64 consecutive, 64-aligned positions is a run of whole cache
-//     tiles (or one 64-row slice of a larger tile), fetched one chunk ahead
-//     with coalesced 16-byte loads: at head sizes up to 128 straight into one
-//     of two LDS buffers (LDS-direct loads), otherwise into registers and
-//     then LDS.  Visible lists with gaps are gathered row by row.
+//   * A chunk of CH (32 or 64) consecutive, CH-aligned positions is a run of
+//     whole cache tiles (or one CH-row slice of a larger tile), fetched one
+//     chunk ahead with coalesced 16-byte loads: at head sizes up to 128
+//     straight into one of two LDS buffers (LDS-direct loads), otherwise into
+//     registers and then LDS.  Visible lists with gaps are gathered row by
+//     row.  32-position chunks (one set of 4 query heads, up to 128
+//     dimensions) let two workgroups share a compute unit.
 //   * Both contractions run on the int8 matrix cores
 //     (v_mfma_i32_16x16x64_i8), whose operands include the cache's own codes:
 //       q.K^T: each query head's q row is scaled by a power of two and rounded
@@ -37,8 +39,9 @@
 //       columns 16 tokens, k the head dimension.
 //       P.V: the softmax weights of a chunk times the V token scales are
 //       scaled by a power of two and rounded to integers below 2^29, again as
-//       four digits; rows (4 heads x 4 digits), k = 64 tokens, columns 16 head
-//       dimensions.  V codes are transposed to token-major bytes with v_perm.
+//       four digits; rows (4 heads x 4 digits), k = 64 tokens (a 32-position
+//       chunk fills half with zero weights), columns 16 head dimensions.  V
+//       codes are transposed to token-major bytes with v_perm.
 //     The int32 digit sums are exact; they are combined in binary32 with a
 //     single rounding per step, so q and the weights keep about 30
 //     significant bits and the result carries f32-level rounding error only.

@@ -91,11 +91,11 @@ hipError_t launch_norm_rope_qk_cache_write(const NormRopeArgs& q, const NormRope
 
 // Decode plan shared by the workspace query and the decode call.  For each
 // row group (kv head, group of query heads sharing it) waves_per_rg
-// persistent wavefronts split the batch's 64-position chunks evenly; a
-// sequence covered by more than one wavefront leaves one partial record per
-// wavefront.
+// persistent wavefronts split the batch's chunks (32 or 64 positions) by
+// cost; a sequence covered by more than one wavefront leaves one partial
+// record per wavefront.
 struct DecodePlan {
-    uint32_t group;          // query heads handled together per kv head (4 or 8)
+    uint32_t group;          // query heads handled together per kv head (4, 8 or 16)
     uint32_t num_groups;     // ceil(n_rep / group)
     uint32_t waves_per_rg;   // persistent wavefronts per row group
     uint64_t recs_per_rg;    // partial record slots per row group: waves_per_rg + num_seqs - 1 (64-bit: no wrap)
