@@ -713,7 +713,15 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
         if (lane == 0) { sK[row + hs4] = ks; sV[row + hs4] = vs; }
         if (grp == 0) {
             const uint32_t pos = m.cs + meta_nv(m) - 1;
-            const uint32_t blk = uniform(a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + pos / a.block_size]);
+            // When blocks and chunks nest (a block size dividing the chunk, or
+            // a multiple of it), the row's block id is the one its chunk's
+            // segment was read with (lane k of m.id holds segment k's): no new
+            // load.  Otherwise it is read from the table.
+            const uint32_t bs = a.block_size;
+            const bool nested = bs <= static_cast<uint32_t>(CH) ? CH % bs == 0 : bs % CH == 0;
+            const uint32_t blk = nested ? lane_value(m.id, bs <= static_cast<uint32_t>(CH) ? (meta_nv(m) - 1) / bs : 0u)
+                                        : uniform(a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq +
+                                                                 pos / bs]);
             // An out-of-range block id breaks the caller contract: nothing is
             // written for it (a clamped id would overwrite another block's row).
             bounds_report(a.bounds_flags, lane == 0 && blk > num_blocks_m1, kBoundBlock);
