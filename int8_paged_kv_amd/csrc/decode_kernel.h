@@ -1163,6 +1163,14 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     q_finish();
     uint32_t q_seq_prev = mc.s;
     for (uint32_t xr = 0;; ++xr) {
+        // Issue priority by the chunks left: of the waves sharing a SIMD, the
+        // one with more work left issues first, so they tend to finish
+        // together (the arbiter otherwise favours the older wave, and the
+        // latest waves of a launch were the younger workgroups').
+        if (n - xr > 12) __builtin_amdgcn_s_setprio(3);
+        else if (n - xr > 6) __builtin_amdgcn_s_setprio(2);
+        else if (n - xr > 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         // q of mc.s was staged one step ago; its digits are formed before the
         // next sequence's q rows are staged into the same registers.
         const bool new_q = xr > 0 && mc.s != q_seq_prev;
