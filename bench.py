@@ -83,7 +83,7 @@ def copy_calibration(mib: int) -> None:
 # code is unchanged (comments and layout do not count).
 DECODE_SOURCES = ("decode_kernel.h", "decode_split.h", "decode.hip", "decode_hs16.hip", "decode_hs32.hip",
                   "decode_hs48.hip", "decode_hs64.hip", "q8_pack.h", "lane_reduce.h", "wave_ops.h",
-                  "q8kv_internal.h", "bounds.h", "cache_write.hip")
+                  "q8kv_internal.h", "bounds.h", "cache_write.hip", "norm_rope_ops.h", "decode_nr.hip")
 
 
 def code_only(text: str) -> str:
@@ -413,8 +413,8 @@ def main():
     from int8_paged_kv_amd import (q8_cache_write, q8_decode_step, q8_paged_decode, q8_paged_decode_rows,
                                    q8_paged_decode_workspace_bytes, q8_f32_cache_write, q8_f32_paged_decode,
                                    q8_f32_paged_decode_workspace_bytes, q8_rope_table, q8_norm_rope,
-                                   q8_norm_rope_cache_write, q8_norm_rope_qk_cache_write, q8_index_select,
-                                   load_library)
+                                   q8_norm_rope_cache_write, q8_norm_rope_qk_cache_write,
+                                   q8_norm_rope_decode_step, q8_index_select, load_library)
     from int8_paged_kv_amd import workloads as wl
 
     load_library()
@@ -661,6 +661,28 @@ def main():
         tqk = np.array([e[0].elapsed_time(e[1]) for e in evn2]) * 1e3
         t2 = np.array([e[0].elapsed_time(e[2]) for e in evn2]) * 1e3
         t3 = np.array([e[0].elapsed_time(e[3]) for e in evn]) * 1e3
+
+        # the whole step in one launch (q8_norm_rope_decode_step), against the
+        # plain one-launch step and the two-launch form, each timed over
+        # back-to-back steps on the cycled layers (HIP events at the ends only)
+        def nr_fused(i):
+            kc, vc = layers[i % len(layers)]
+            q8_norm_rope_decode_step(q, sk, sv, kc, vc, bt, cl, w.scale, Hkv, w.block_size, mcl, qn, kn, table,
+                                     rot, 1e-6, out=outn, workspace=ws)
+
+        nb_ = max(100, args.steps)
+        for i in range(10):
+            nr_fused(i)
+        t_fused = _timed(nr_fused, nb_)
+        t_two = _timed(nr_step2, nb_)
+        t_plain = _timed(lambda i: step(i), nb_)
+        # the fused step's output against the two-launch form's, bit for bit
+        # (same layer, the same rows appended)
+        nr_fused(0)
+        fused_out = outn.clone()
+        nr_step2(0)
+        torch.cuda.synchronize()
+        fused_equal = bool(torch.equal(fused_out.view(torch.int32), outn.view(torch.int32)))
         # bulk: 16384 tokens at scattered slots of a separate cache, fused vs plain writer
         Tb = 16384
         nbb = Tb // w.block_size + 64
@@ -692,6 +714,10 @@ def main():
                     "three_launch_step_us_mean": round(float(t3.mean()), 2),
                     "qk_norm_rope_cache_write_us_mean": round(float(tqk.mean()), 2),
                     "two_launch_step_us_mean": round(float(t2.mean()), 2),
+                    "fused_step_us": round(t_fused, 2),
+                    "two_launch_step_us_back_to_back": round(t_two, 2),
+                    "plain_step_us_back_to_back": round(t_plain, 2),
+                    "fused_step_equals_two_launch_bitwise": fused_equal,
                     "bulk_tokens": Tb,
                     "bulk_norm_rope_cache_write_us_mean": round(float(tbf.mean()), 2),
                     "bulk_plain_cache_write_us_mean": round(float(tbp.mean()), 2),
@@ -700,7 +726,9 @@ def main():
                     "bulk_norm_rope_frac_hbm_peak": round(Bb / (float(tbf.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "note": "the step with q8_norm_rope on q rows and q8_norm_rope_cache_write for the new K/V "
                             "(three launches with the decode), the same with q8_norm_rope_qk_cache_write (two "
-                            "launches), then a 16384-token bulk write; positions L-1 for the step"}
+                            "launches), each launch bracketed by events; then q8_norm_rope_decode_step (one launch), "
+                            "the two-launch form and the plain q8_decode_step timed over back-to-back steps "
+                            "(events at the ends); then a 16384-token bulk write; positions L-1 for the step"}
         del kb_, vb_
 
     # ---- selected-token step: block scores -> visible lists -> visible-list decode ----

@@ -432,6 +432,51 @@ q8_status q8_norm_rope_qk_cache_write(float* q_out, uint32_t q_out_stride, const
                                       uint32_t num_blocks, void* stream);
 
 /*
+ * q8_norm_rope_decode_step -- q8_decode_step with the per-head RMSNorm +
+ * partial rotary step above applied to the query rows and to the new K rows,
+ * in the same single launch.  The "attention.rs" page normalizes and rotates q
+ * and k ahead of the q8 append and the decode (its qk_norm_rope_b dispatch);
+ * here the wavefront that stages a sequence's q rows normalizes and rotates
+ * them, and the one that appends its new K row does the same to it before
+ * quantizing.  The result (outputs and cache words) is exactly that of
+ *   q8_norm_rope(q', .., q, .., positions, q_weight, table, rot, num_positions, eps)
+ *   q8_norm_rope_cache_write(key, .., value, .., slots, positions, k_weight, ...)
+ *   q8_paged_decode(out, q', ...)                       (dense mode)
+ * with positions[s] = context_lens[s] - 1 and slots[s] the slot of that
+ * position (its block_tables entry, offset position % block_size), for the
+ * sequences q8_decode_step appends to (the others are not written, and their
+ * q rows are still rotated at context_lens[s] - 1).
+ *
+ *   q             f32 query rows before the step, laid out as for q8_decode_step.
+ *   q_weight,     device f32 [head_size]: the q and K norm weights.
+ *   k_weight
+ *   table, rot,   as for q8_norm_rope (table unused and may be NULL when
+ *   num_positions, rot == 0); a position past the table is clamped to its
+ *   eps           last row, as there.
+ *   the rest      as q8_decode_step, including the workspace.
+ *
+ * Errors: those of q8_decode_step; Q8_ERR_SHAPE under the shape rules of
+ * q8_norm_rope; Q8_ERR_NULL for a NULL weight, or a NULL table with rot > 0
+ * (num_seqs > 0); Q8_ERR_UNSUPPORTED unless head_size is 128, num_heads /
+ * num_kv_heads is at most 8, both caches are 16-byte aligned and block_size
+ * is a multiple of 4 that divides, or is a multiple of, the positions per
+ * chunk (32 when num_heads / num_kv_heads <= 4, else 64).  Other shapes take
+ * q8_norm_rope_qk_cache_write followed by q8_paged_decode.
+ */
+q8_status q8_norm_rope_decode_step(float* out, const float* q, uint32_t q_stride,
+                                   const float* key, uint32_t key_stride,
+                                   const float* value, uint32_t value_stride,
+                                   uint32_t* key_cache, uint32_t* value_cache,
+                                   const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                                   const uint32_t* context_lens, uint32_t max_context_len,
+                                   const float* q_weight, const float* k_weight, const float* table,
+                                   uint32_t rot, uint32_t num_positions, float eps,
+                                   uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                                   uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                                   float scale, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * q8_index_select -- block selection into a visible list.  The
  * "attention.rs" page's per-row decode gives row r t_len = row_lens[r]
  * positions and blocks = t_len / ratio complete blocks; with k = kblk

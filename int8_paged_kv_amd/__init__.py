@@ -18,7 +18,8 @@ Operations behind the C ABI of libq8kv.so (include/q8kv.h):
 * ``q8_rope_table``, ``q8_norm_rope``, ``q8_norm_rope_cache_write``: per-head
   RMSNorm + partial rotary embedding of q rows, and fused ahead of the K
   quantizer in the cache write (the q/k norm-and-rope step of "attention.rs");
-  ``q8_norm_rope_qk_cache_write`` does the q rows and the K/V write in one launch.
+  ``q8_norm_rope_qk_cache_write`` does the q rows and the K/V write in one launch,
+  ``q8_norm_rope_decode_step`` the whole step (norm + rotary, append, decode).
 * ``q8_index_select``: block scores to visible-position lists (the top
   kblk blocks plus the trailing partial block), the input of the visible-list
   decode.
@@ -30,7 +31,7 @@ be imported on a machine without the library or a GPU.
 __all__ = ["q8_cache_write", "q8_paged_decode", "q8_paged_decode_noalloc", "q8_decode_step", "q8_paged_decode_rows",
            "q8_paged_decode_workspace_bytes", "q8_f32_cache_write", "q8_f32_paged_decode",
            "q8_f32_paged_decode_workspace_bytes", "q8_rope_table", "q8_norm_rope", "q8_norm_rope_cache_write",
-           "q8_norm_rope_qk_cache_write", "q8_index_select",
+           "q8_norm_rope_qk_cache_write", "q8_norm_rope_decode_step", "q8_index_select",
            "load_library", "load_debug_library", "use_library", "bounds_flags", "Q8Error", "PAD_SLOT"]
 
 

@@ -105,6 +105,9 @@ def _open(path: str) -> ctypes.CDLL:
     lib.q8_norm_rope_qk_cache_write.argtypes = [P, U, P, U, U, U, U, P, P, P, U, P, U, P, P, P, P, P, P, U, U,
                                                 F, U, U, U, U, U, P]
     lib.q8_norm_rope_qk_cache_write.restype = ctypes.c_int
+    lib.q8_norm_rope_decode_step.argtypes = [P, P, U, P, U, P, U, P, P, P, U, P, U, P, P, P, U, U, F,
+                                             U, U, U, U, U, U, F, P, ctypes.c_size_t, P]
+    lib.q8_norm_rope_decode_step.restype = ctypes.c_int
     lib.q8_index_select.argtypes = [P, U, P, U, U, U, P, U, P, P, U, P]
     lib.q8_index_select.restype = ctypes.c_int
     lib.q8_last_hip_error.argtypes = []
@@ -315,6 +318,52 @@ def q8_decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor, key_
                             S, H, num_kv_heads, hs, block_size, num_blocks, float(scale), wp, wb,
                             _stream(stream))
     _check(st, "q8_decode_step")
+    return out
+
+
+def q8_norm_rope_decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                             value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                             scale: float, num_kv_heads: int, block_size: int, max_context_len: int,
+                             q_weight: torch.Tensor, k_weight: torch.Tensor, table: Optional[torch.Tensor], rot: int,
+                             eps: float, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                             num_blocks: Optional[int] = None, stream=None) -> torch.Tensor:
+    """q8_decode_step with the per-head RMSNorm + partial rotary step applied to q
+    and to the new K rows at position context_lens[s]-1, in the same launch (see
+    include/q8kv.h).  q is the un-normalized [S, H, head_size] f32; table is
+    q8_rope_table's [num_positions, rot] (None when rot == 0)."""
+    lib = load_library()
+    if q.dim() != 3 or (q.numel() and not q[0].is_contiguous()):
+        raise ValueError("q must be [S, H, head_size] with dense rows")
+    S, H, hs = q.shape
+    if out is None:
+        out = torch.empty((S, H, hs), dtype=torch.float32, device=q.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (S, H, hs):
+        raise ValueError("out must be a contiguous [S, H, head_size] f32 tensor")
+    kp, kst = _rows(key, "key")
+    vp, vst = _rows(value, "value")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [S, max_num_blocks_per_seq]")
+    wpt = hs // 4 + 1
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * wpt)
+    mcl = int(max_context_len)
+    need = lib.q8_paged_decode_workspace_bytes(S, H, num_kv_heads, hs, block_size, mcl)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)   # zero before first use
+    wp = None if workspace is None else workspace.data_ptr()
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    num_positions = table.shape[0] if (table is not None and rot) else 0
+    tab = _dev(table, "table", torch.float32) if (table is not None and rot) else None
+    st = lib.q8_norm_rope_decode_step(_dev(out, "out", torch.float32), _dev(q, "q", torch.float32), q.stride(0),
+                                      kp, kst, vp, vst,
+                                      _u32(key_cache, "key_cache"), _u32(value_cache, "value_cache"),
+                                      _u32(block_tables, "block_tables"), block_tables.shape[1],
+                                      _u32(context_lens, "context_lens"), mcl,
+                                      _dev(q_weight, "q_weight", torch.float32),
+                                      _dev(k_weight, "k_weight", torch.float32), tab, int(rot), num_positions,
+                                      float(eps), S, H, num_kv_heads, hs, block_size, num_blocks, float(scale), wp,
+                                      wb, _stream(stream))
+    _check(st, "q8_norm_rope_decode_step")
     return out
 
 

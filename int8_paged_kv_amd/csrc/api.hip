@@ -46,6 +46,11 @@ uint32_t* bounds_flags_ptr() {
 }
 
 bool head_size_ok(uint32_t hs) { return hs != 0 && hs % 4 == 0 && hs <= Q8_MAX_HEAD_SIZE; }
+// Shape rules of the norm + rotary step.
+bool rope_shape_ok(uint32_t head_size, uint32_t rot, uint32_t num_positions, float eps) {
+    return head_size_ok(head_size) && rot % 8 == 0 && rot <= head_size && eps >= 0.0f && std::isfinite(eps) &&
+           (rot == 0 || num_positions > 0);
+}
 
 }  // namespace
 
@@ -151,6 +156,15 @@ struct AppendArgs {
     uint32_t* value_cache;
 };
 
+// The norm + rotary step's parameters of a decode step that applies it.
+struct NormRopeStepArgs {
+    const float* q_weight;
+    const float* k_weight;
+    const float* table;
+    uint32_t rot, num_positions;
+    float eps;
+};
+
 q8_status decode_common(float* out, const float* q, uint32_t q_stride,
                         const uint32_t* key_cache, const uint32_t* value_cache,
                         const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
@@ -161,7 +175,7 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
                         uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
                         float scale, void* workspace, size_t workspace_bytes,
                         void* stream, const AppendArgs* app, uint32_t rows_per_seq,
-                        bool static_scratch = false) {
+                        bool static_scratch = false, const NormRopeStepArgs* nr = nullptr) {
     if (!head_size_ok(head_size) || block_size == 0 || num_heads == 0 || num_kv_heads == 0 ||
         num_heads % num_kv_heads != 0)
         return Q8_ERR_SHAPE;
@@ -182,6 +196,8 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     if (!out || !q || !key_cache || !value_cache || !block_tables) return Q8_ERR_NULL;
     if (vis ? !num_visible : !context_lens) return Q8_ERR_NULL;
     if (app && (!app->key || !app->value)) return Q8_ERR_NULL;
+    if (nr && !q8kv::norm_rope_decode_supported(head_size, num_heads, num_kv_heads, block_size, key_cache, value_cache))
+        return Q8_ERR_UNSUPPORTED;
     const uint32_t max_pos = vis ? vis_stride : max_context_len;
     if (max_pos > 0 && (max_num_blocks_per_seq == 0 || num_blocks == 0)) return Q8_ERR_SHAPE;
     if (!std::isfinite(scale)) return Q8_ERR_SHAPE;
@@ -236,6 +252,17 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
                      app->key_stride % 4 == 0 && app->value_stride % 4 == 0 && head_size % 4 == 0;
         a.key_cache_w = app->key_cache;
         a.value_cache_w = app->value_cache;
+    }
+    if (nr) {
+        a.nr_q_weight = nr->q_weight;
+        a.nr_k_weight = nr->k_weight;
+        a.nr_table = nr->table;
+        a.nr_rot = nr->rot;
+        a.nr_num_positions = nr->num_positions;
+        a.nr_eps = nr->eps;
+        a.nr_params_vec4 = reinterpret_cast<uintptr_t>(nr->q_weight) % 16 == 0 &&
+                           reinterpret_cast<uintptr_t>(nr->k_weight) % 16 == 0 &&
+                           reinterpret_cast<uintptr_t>(nr->table) % 16 == 0;
     }
     const hipError_t e = q8kv::launch_decode(a, max_pos, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
@@ -305,6 +332,28 @@ q8_status q8_decode_step(float* out, const float* q, uint32_t q_stride,
                          context_lens, max_context_len, nullptr, nullptr, 0, num_seqs, num_heads,
                          num_kv_heads, head_size, block_size, num_blocks, scale, workspace, workspace_bytes,
                          stream, &app, 1);
+}
+
+q8_status q8_norm_rope_decode_step(float* out, const float* q, uint32_t q_stride,
+                                   const float* key, uint32_t key_stride,
+                                   const float* value, uint32_t value_stride,
+                                   uint32_t* key_cache, uint32_t* value_cache,
+                                   const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                                   const uint32_t* context_lens, uint32_t max_context_len,
+                                   const float* q_weight, const float* k_weight, const float* table,
+                                   uint32_t rot, uint32_t num_positions, float eps,
+                                   uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                                   uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                                   float scale, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    if (!rope_shape_ok(head_size, rot, num_positions, eps)) return Q8_ERR_SHAPE;
+    if (num_seqs > 0 && (!q_weight || !k_weight || (rot > 0 && !table))) return Q8_ERR_NULL;
+    const AppendArgs app{key, value, key_stride, value_stride, key_cache, value_cache};
+    const NormRopeStepArgs nr{q_weight, k_weight, table, rot, num_positions, eps};
+    return decode_common(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
+                         context_lens, max_context_len, nullptr, nullptr, 0, num_seqs, num_heads,
+                         num_kv_heads, head_size, block_size, num_blocks, scale, workspace, workspace_bytes,
+                         stream, &app, 1, false, &nr);
 }
 
 q8_status q8_f32_cache_write(const float* key, uint32_t key_stride,
@@ -413,13 +462,6 @@ q8_status q8_rope_table(float* table, uint32_t num_positions, uint32_t rot, floa
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
-
-namespace {
-bool rope_shape_ok(uint32_t head_size, uint32_t rot, uint32_t num_positions, float eps) {
-    return head_size_ok(head_size) && rot % 8 == 0 && rot <= head_size && eps >= 0.0f && std::isfinite(eps) &&
-           (rot == 0 || num_positions > 0);
-}
-}  // namespace
 
 }  // extern "C"
 

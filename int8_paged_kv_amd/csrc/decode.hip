@@ -97,7 +97,28 @@ hipError_t resident_waves(const void* fn, uint32_t* waves, uint32_t* per_cu) {
     return hipSuccess;
 }
 
+// Chunks of `ch` positions can be copied as tile runs: block_size nests with
+// the chunk and both caches are 16-byte aligned.
+bool tiles_ok(const DecodeArgs& a, uint32_t ch) {
+    const bool shape_ok = a.block_size % 4 == 0 && (ch % a.block_size == 0 || a.block_size % ch == 0);
+    const bool align_ok = reinterpret_cast<uintptr_t>(a.key_cache) % 16 == 0 &&
+                          reinterpret_cast<uintptr_t>(a.value_cache) % 16 == 0;
+    return shape_ok && align_ok;
+}
+
 }  // namespace
+
+bool norm_rope_decode_supported(uint32_t head_size, uint32_t num_heads, uint32_t num_kv_heads, uint32_t block_size,
+                                const uint32_t* key_cache, const uint32_t* value_cache) {
+    if (head_size != 128 || num_kv_heads == 0) return false;
+    const uint32_t group = decode_group(num_heads / num_kv_heads);
+    if (group > 8) return false;
+    DecodeArgs a{};
+    a.block_size = block_size;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    return tiles_ok(a, static_cast<uint32_t>(decode_chunk(32, static_cast<int>(group / 4))));
+}
 
 hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_t stream) {
     const bool vis = a.visible_pos != nullptr;
@@ -110,10 +131,7 @@ hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_
     const uint32_t ch = static_cast<uint32_t>(decode_chunk(static_cast<int>(hs4p), static_cast<int>(group / 4)));
     SplitConsts c{};
     c.seg_rows = a.block_size < ch ? a.block_size : ch;
-    const bool shape_ok = a.block_size % 4 == 0 && (ch % a.block_size == 0 || a.block_size % ch == 0);
-    const bool align_ok = reinterpret_cast<uintptr_t>(a.key_cache) % 16 == 0 &&
-                          reinterpret_cast<uintptr_t>(a.value_cache) % 16 == 0;
-    c.tiled_ok = shape_ok && align_ok;
+    c.tiled_ok = tiles_ok(a, ch);
     c.q_vec_ok = reinterpret_cast<uintptr_t>(a.q) % 16 == 0 && a.q_stride % 4 == 0;
     c.seg_u4 = c.seg_rows * wpt / 4;
     if (c.seg_u4 == 0) c.seg_u4 = 1;
@@ -126,6 +144,11 @@ hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_
     else if (hs4 <= 32) fn = split_kernel_hs32(vis, t, hs4 == 32, group, seg_whole);
     else if (hs4 <= 48) fn = split_kernel_hs48(vis, t, hs4 == 48, group, seg_whole);
     else fn = split_kernel_hs64(vis, t, hs4 == 64, group, seg_whole);
+    if (a.nr_q_weight) {
+        // the norm + rotary step exists for the shapes norm_rope_decode_supported accepts
+        fn = !vis && t && hs4 == 32 && a.rows_per_seq <= 1 ? split_kernel_nr_hs32(group, seg_whole) : nullptr;
+        if (!fn) return hipErrorInvalidValue;
+    }
     // As many persistent wavefronts as the device keeps resident for this
     // kernel, at most the bound the workspace was sized for.
     uint64_t target = decode_wave_override();

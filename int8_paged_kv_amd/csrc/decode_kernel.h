@@ -51,6 +51,7 @@
 #pragma once
 #include "bounds.h"
 #include "decode_split.h"
+#include "norm_rope_ops.h"
 #include "q8_pack.h"
 #include "wave_ops.h"
 
@@ -290,8 +291,12 @@ struct Shares {
 // when nonzero (16 or 32, with EXACT), the rows per tile segment, for which
 // each segment of a chunk fills whole 64-lane slots (SEGR*HS4P/256 of them)
 // plus SEGR/4 trailing 16-byte units: every full slot then loads from one
-// segment with a scalar base address and a fixed per-lane offset.
-template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED, int SEGR, int CH>
+// segment with a scalar base address and a fixed per-lane offset.  NR: the
+// decode step with the per-head RMSNorm + partial rotary step (head_size 128,
+// dense positions): q rows and the new K row are normalized and rotated at the
+// sequence's last position as they are staged, as the standalone norm + rotary
+// kernels do it.
+template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED, int SEGR, int CH, bool NR = false>
 __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 || CH == 32)) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
     constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
     constexpr int NCW = HS4P / 16;             // V code words per lane and row
@@ -302,6 +307,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     constexpr int NTG = CH / 16;               // 16-token column groups of a chunk
     constexpr uint32_t kCostSeq = cost_seq(CH);
     static_assert(CH == 32 || CH == 64, "chunk size");
+    static_assert(!NR || (HS4P == 32 && EXACT && !VIS), "norm + rotary step: 32 lanes per q head, dense positions");
     constexpr int NU = (CH * WPT_MAX + 4 * kWave - 1) / (4 * kWave);   // 16-byte slots per lane
     // An exact head size makes a chunk CH*(HS4P+1) words: CH*HS4P/256 full
     // 16-byte slots per lane plus a 4-byte tail slot in CH lanes.
@@ -687,10 +693,25 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     // loads brought in (the cache still held the old one) and, for the first
     // query-head group of the kv head, are written to the caches.
     float4 nkx = make_float4(0.f, 0.f, 0.f, 0.f), nvx = nkx;
+    // Norm + rotary step: the table row of a position (clamped to the table),
+    // and for the new K row lane w's weights and cos/sin (64-lane group, w =
+    // lane), staged with it.
+    auto nr_row = [&](uint32_t pos) __attribute__((always_inline)) -> const float* {
+        if (a.nr_rot == 0) return a.nr_table;
+        const uint32_t p = pos < a.nr_num_positions ? pos : a.nr_num_positions - 1;
+        return a.nr_table + static_cast<uint64_t>(p) * a.nr_rot;
+    };
+    RopeLane nk_op{};
     auto issue_new = [&](const Meta& m) __attribute__((always_inline)) {
         if (!append || !m.app) return;
         nkx = make_float4(0.f, 0.f, 0.f, 0.f);
         nvx = nkx;
+        if constexpr (NR) {
+            // the appended row's position: the chunk's last (context_lens[s] - 1)
+            const float* cs = nr_row(m.cs + meta_nv(m) - 1);
+            nk_op.wt = load_weight4(a.nr_k_weight, lane, hs4, a.nr_params_vec4 != 0);
+            load_cs4(cs, lane, a.nr_rot, a.nr_params_vec4 != 0, nk_op.c, nk_op.s);
+        }
         if (lane < hs4) {
             const float* pk = a.new_key + static_cast<uint64_t>(m.s) * a.new_key_stride + static_cast<uint64_t>(kvh) * hs + 4 * lane;
             const float* pv = a.new_value + static_cast<uint64_t>(m.s) * a.new_value_stride + static_cast<uint64_t>(kvh) * hs + 4 * lane;
@@ -705,6 +726,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     };
     auto store_new = [&](const Meta& m) __attribute__((always_inline)) {
         if (!append || !m.app) return;
+        // lanes at and above head_size/4 hold zeros and weight 0: they add
+        // nothing to the sum of squares and stay 0
+        if constexpr (NR) nkx = norm_rope4<kWave>(nkx, lane, RowMean(hs), nk_op, a.nr_rot, a.nr_eps);
         uint32_t ks, vs;
         const uint32_t kw = quantize_word<kWave>(nkx, ks);
         const uint32_t vw = quantize_word<kWave>(nvx, vs);
@@ -801,8 +825,20 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     constexpr int QF = G * QD / (4 * kWave);
     static_assert(QF * kWave <= NHS * 16 * 16 && (QSCR || NHS * NKB * 256 <= BUFW), "q scratch");
     float4 qv[QF];
+    // Norm + rotary step on the staged q rows: lane w = lane % 32 of each
+    // 32-lane half holds elements 4w .. 4w+3 of one head (QD == 128), so one
+    // set of weights and cos/sin per lane serves every slot.
+    RopeLane q_op{};
     auto q_issue = [&](uint32_t s) __attribute__((always_inline)) {
         const uint64_t row = static_cast<uint64_t>(s) * nrow * a.q_stride;
+        if constexpr (NR) {
+            // position context_lens[s] - 1 (a staged sequence has positions, so
+            // context_lens[s] >= 1)
+            const uint32_t L = one_window ? lane_value(win_len, s) : uniform(a.context_lens[s]);
+            const uint32_t w = lane % 32u;
+            q_op.wt = load_weight4(a.nr_q_weight, w, hs4, a.nr_params_vec4 != 0);
+            load_cs4(nr_row(L - 1), w, a.nr_rot, a.nr_params_vec4 != 0, q_op.c, q_op.s);
+        }
 #pragma unroll
         for (int t = 0; t < QF; ++t) {
             const uint32_t e = 4 * (lane + kWave * t);
@@ -827,6 +863,16 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     // once and scatters each value's four digits to the lanes whose MFMA rows
     // hold them, through LDS in the operand layout [set][k-block][lane][w].
     auto q_finish = [&]() __attribute__((always_inline)) {
+        if constexpr (NR) {
+            // slots of heads past nh stay zero (they are padding, not vectors)
+            const RowMean mean(hs);
+#pragma unroll
+            for (int t = 0; t < QF; ++t) {
+                const uint32_t hi = 4 * (lane + kWave * t) / QD;
+                const float4 y = norm_rope4<32>(qv[t], lane % 32u, mean, q_op, a.nr_rot, a.nr_eps);
+                qv[t] = hi < nh ? y : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
         uint32_t* const scratch = QSCR ? sQs_[wid] : sKn;   // sKn: no loads are landing in it yet
         uint32_t* const sDig = scratch;
         // per-slot maxima: in sA (not in use outside a chunk's processing)
@@ -1183,6 +1229,11 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             // q_finish it would also wait for those.
 #pragma unroll
             for (int t = 0; t < QF; ++t) asm volatile("" : : "v"(qv[t].x), "v"(qv[t].y), "v"(qv[t].z), "v"(qv[t].w));
+            if constexpr (NR) {
+                asm volatile("" : : "v"(q_op.wt.x), "v"(q_op.wt.y), "v"(q_op.wt.z), "v"(q_op.wt.w));
+                asm volatile("" : : "v"(q_op.c.x), "v"(q_op.c.y), "v"(q_op.c.z), "v"(q_op.c.w));
+                asm volatile("" : : "v"(q_op.s.x), "v"(q_op.s.y), "v"(q_op.s.z), "v"(q_op.s.w));
+            }
         }
         if (xr + 2 < n) advance();
         const Meta mn2 = meta_of(xr + 2 < n);
@@ -1235,6 +1286,18 @@ const void* split_kernel_g(bool vis, bool tiled, uint32_t group, uint32_t seg_ro
     if (group == 16) return split_kernel_t<HS4P, EXACT, 4>(vis, tiled, seg_rows);
     if (group == 8) return split_kernel_t<HS4P, EXACT, 2>(vis, tiled, seg_rows);
     return split_kernel_t<HS4P, EXACT, 1>(vis, tiled, seg_rows);
+}
+
+// The norm + rotary decode step (head_size 128, dense, tiled chunks) for sets
+// of NHS query heads.
+template <int NHS>
+const void* split_kernel_nr(uint32_t seg_rows) {
+    constexpr int CH = decode_chunk(32, NHS);
+    if (seg_rows == 16)
+        return reinterpret_cast<const void*>(&decode_split_kernel<32, true, NHS, false, true, 16, CH, true>);
+    if (seg_rows == 32)
+        return reinterpret_cast<const void*>(&decode_split_kernel<32, true, NHS, false, true, 32, CH, true>);
+    return reinterpret_cast<const void*>(&decode_split_kernel<32, true, NHS, false, true, 0, CH, true>);
 }
 
 }  // namespace

@@ -41,5 +41,8 @@ const void* split_kernel_hs16(bool vis, bool tiled, bool exact, uint32_t group, 
 const void* split_kernel_hs32(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
 const void* split_kernel_hs48(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
 const void* split_kernel_hs64(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
+// The norm + rotary decode step's instantiation (head_size 128, dense
+// positions, tiled chunks) for query-head groups of 4 or 8; null otherwise.
+const void* split_kernel_nr_hs32(uint32_t group, uint32_t seg_rows);
 
 }  // namespace q8kv

@@ -137,6 +137,15 @@ struct DecodeArgs {
     uint32_t new_vec4;       // the new rows are 16-byte aligned with strides that keep them so
     uint32_t* key_cache_w;   // key_cache / value_cache, written by the append
     uint32_t* value_cache_w;
+    // Decode step with the per-head RMSNorm + partial rotary step (nr_q_weight
+    // non-null): sequence s's q rows and new K row are normalized and rotated
+    // at position context_lens[s] - 1 before use (norm_rope_ops.h).
+    const float* nr_q_weight;    // [head_size]
+    const float* nr_k_weight;    // [head_size]
+    const float* nr_table;       // [nr_num_positions, nr_rot]: cos | sin per position
+    uint32_t nr_rot, nr_num_positions;
+    float nr_eps;
+    uint32_t nr_params_vec4;     // weights and table 16-byte aligned
     // Multi-row decode (> 1): num_seqs counts rows; row v is row v % rows_per_seq
     // of sequence v / rows_per_seq (its block-table row), and attends the first
     // context_lens[seq] - rows_per_seq + (v % rows_per_seq) + 1 positions.
@@ -146,6 +155,12 @@ struct DecodeArgs {
 
 // max_positions: max_context_len in dense mode, vis_stride with visible lists.
 hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_t stream);
+// Whether the decode step with the norm + rotary step (dense, one row per
+// sequence) has a kernel for these shapes: head_size 128, at most 8 query
+// heads per kv head, caches 16-byte aligned and block_size nesting with the
+// chunk.
+bool norm_rope_decode_supported(uint32_t head_size, uint32_t num_heads, uint32_t num_kv_heads, uint32_t block_size,
+                                const uint32_t* key_cache, const uint32_t* value_cache);
 
 // ---- f32 paged-cache baseline: cache [num_blocks, num_kv_heads, block_size, head_size] f32 ----
 

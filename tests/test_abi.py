@@ -135,6 +135,34 @@ def test_decode_step_validation(lib, kw, want):
     assert lib.q8_decode_step(*step_args(**kw)) == want
 
 
+def nr_step_args(**kw):
+    a = dict(out=FAKE, q=FAKE, q_stride=4 * 128, k=FAKE, ks=2 * 128, v=FAKE, vs=2 * 128, kc=FAKE, vc=FAKE,
+             bt=FAKE, max_nb=8, cl=FAKE, mcl=5000, qw=FAKE, kw=FAKE, tab=FAKE, rot=64, npos=8192, eps=1e-6,
+             S=2, H=4, Hkv=2, hs=128, bs=16, nb=64, scale=0.1, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "q_stride", "k", "ks", "v", "vs", "kc", "vc", "bt", "max_nb", "cl", "mcl",
+                           "qw", "kw", "tab", "rot", "npos", "eps",
+                           "S", "H", "Hkv", "hs", "bs", "nb", "scale", "ws", "wsb", "stream")]
+
+
+@pytest.mark.parametrize("kw,want", [
+    # the norm + rotary step's shape rules and operands
+    (dict(rot=12), 2), (dict(rot=136), 2), (dict(eps=-1.0), 2), (dict(eps=float("inf")), 2), (dict(npos=0), 2),
+    (dict(qw=None), 1), (dict(kw=None), 1), (dict(tab=None), 1),
+    # those of the decode step
+    (dict(k=None), 1), (dict(cl=None), 1), (dict(ks=255), 2), (dict(hs=130), 2), (dict(H=5), 2),
+    (dict(wsb=16), 3), (dict(out=ctypes.c_void_p(0x2004)), 5), (dict(S=0), 0), (dict(S=0, qw=None), 0),
+    # shapes without a fused kernel: head_size other than 128, more than 8
+    # query heads per kv head, misaligned caches, block sizes not nesting with
+    # the chunk (32 positions for up to 4 query heads per kv head, else 64)
+    (dict(hs=64, rot=32, q_stride=4 * 64, ks=128, vs=128), 5), (dict(H=32, q_stride=32 * 128), 5),
+    (dict(kc=ctypes.c_void_p(0x1004)), 5), (dict(vc=ctypes.c_void_p(0x1008)), 5), (dict(bs=48), 5),
+    (dict(bs=6), 5), (dict(H=16, q_stride=16 * 128, bs=48), 5),
+])
+def test_norm_rope_decode_step_validation(lib, kw, want):
+    assert lib.q8_norm_rope_decode_step(*nr_step_args(**kw)) == want
+
+
 def rows_args(**kw):
     a = dict(out=FAKE, q=FAKE, q_stride=4 * 128, kc=FAKE, vc=FAKE, bt=FAKE, max_nb=8, cl=FAKE, mcl=5000, nb=4,
              S=2, H=4, Hkv=2, hs=128, bs=16, nblk=64, scale=0.1, ws=FAKE, wsb=1 << 30, stream=None)
