@@ -151,13 +151,13 @@ def main():
         "# durations in microseconds per dispatch; step = one launch of q8_decode_step (decode_split_kernel: "
         "appends the 64 new tokens, attends, and combines shared sequences)",
         "",
-        "%-52s %9s %4s %5s %9s %9s %9s %9s %5s %5s %5s %6s %6s" % (
+        "%-62s %9s %4s %5s %9s %9s %9s %9s %5s %5s %5s %6s %6s" % (
             "kernel", "grid", "wg", "calls", "mean_us", "median_us", "min_us", "max_us", "vgpr", "agpr", "sgpr",
             "lds", "scratch"),
     ]
     for r in rows:
-        lines.append("%-52s %9d %4d %5d %9.2f %9.2f %9.2f %9.2f %5d %5d %5d %6d %6d%s" % (
-            r[0][:52], r[1], r[2], r[3], r[4], r[5], r[6], r[7], r[8], r[9], r[10], r[11], r[12],
+        lines.append("%-62s %9d %4d %5d %9.2f %9.2f %9.2f %9.2f %5d %5d %5d %6d %6d%s" % (
+            r[0][:62], r[1], r[2], r[3], r[4], r[5], r[6], r[7], r[8], r[9], r[10], r[11], r[12],
             "  <- step" if r[13] else ""))
     lines += [
         "",
@@ -171,8 +171,8 @@ def main():
     ]
     with open(os.path.join(d, "trace", "bench_kernel_stats.csv")) as f:
         for r in csv.DictReader(f):
-            lines.append("  %-52s calls %4s avg_ns %12s min_ns %9s max_ns %9s" % (
-                short(r["Name"])[:52], r["Calls"], r["AverageNs"], r["MinNs"], r["MaxNs"]))
+            lines.append("  %-62s calls %4s avg_ns %12s min_ns %9s max_ns %9s" % (
+                short(r["Name"])[:62], r["Calls"], r["AverageNs"], r["MinNs"], r["MaxNs"]))
     with open(os.path.join(ROOT, "profiles", "q8_paged_decode_llama_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -369,7 +369,7 @@ def main():
             "#",
             "# kernel_sources_sha256_16: %s" % digest,
             "",
-            "%-52s %9s %5s %14s %13s %9s %9s" % ("kernel", "grid", "calls", "read_B", "written_B", "median_us",
+            "%-62s %9s %5s %14s %13s %9s %9s" % ("kernel", "grid", "calls", "read_B", "written_B", "median_us",
                                                  "HBM_GBps"),
         ]
         for key in sorted(cf, key=lambda k: -statistics.median(cf[k]) * len(cf[k])):
@@ -381,8 +381,8 @@ def main():
                 continue
             us = durs.get(key)
             nm = kname(key[0])
-            out.append("%-52s %9d %5d %14.0f %13.0f %9s %9s" % (
-                nm[:52], key[1], len(cf[key]), rd, wr, "%.2f" % us if us else "-",
+            out.append("%-62s %9d %5d %14.0f %13.0f %9s %9s" % (
+                nm[:62], key[1], len(cf[key]), rd, wr, "%.2f" % us if us else "-",
                 "%.0f" % ((rd + wr) / (us * 1e-6) / 1e9) if us else "-"))
         mr, f32, nr, sel, lg, md, mw = (jf.get(k) or {} for k in (
             "multi_row_decode", "f32_cache_reference", "norm_rope_step", "selected_step", "long_context",
@@ -403,9 +403,9 @@ def main():
         with open(os.path.join(ROOT, "profiles", "llama_step_all_kernels_traffic.txt"), "w") as f:
             f.write("\n".join(out) + "\n")
         # the legs' kernels: the (kernel, grid) of the leg's instantiation launched most often
-        legs = {"long_context": "decode_split_kernel<32, true, 2, false, true, 32, 64>",
-                "mha256_decode": "decode_split_kernel<64, true, 1, false, true, 16, 64>",
-                "mha256_write": "cache_write_kernel<false, 4>"}
+        legs = {"long_context": "decode_split_kernel<32, true, 2, false, true, 32, 64, false>",
+                "mha256_decode": "decode_split_kernel<64, true, 1, false, true, 16, 64, false>",
+                "mha256_write": "cache_write_kernel<false, 4, true>"}
         lt = [
             "# HBM bytes per launch of the long-context decode, the MHA head_size=256 decode and its padded",
             "# 4096-token write (bench.py legs long_context, mha256_decode, mha256_write), from the runs of",
