@@ -83,7 +83,8 @@ def copy_calibration(mib: int) -> None:
 # code is unchanged (comments and layout do not count).
 DECODE_SOURCES = ("decode_kernel.h", "decode_split.h", "decode.hip", "decode_hs16.hip", "decode_hs32.hip",
                   "decode_hs48.hip", "decode_hs64.hip", "q8_pack.h", "lane_reduce.h", "wave_ops.h",
-                  "q8kv_internal.h", "bounds.h", "cache_write.hip", "norm_rope_ops.h", "decode_nr.hip")
+                  "q8kv_internal.h", "bounds.h", "cache_write.hip", "norm_rope_ops.h", "decode_nr16.hip",
+                  "decode_nr32.hip", "decode_nr64.hip")
 
 
 def code_only(text: str) -> str:

@@ -435,19 +435,26 @@ q8_status q8_norm_rope_qk_cache_write(float* q_out, uint32_t q_out_stride, const
  * q8_norm_rope_decode_step -- q8_decode_step with the per-head RMSNorm +
  * partial rotary step above applied to the query rows and to the new K rows,
  * in the same single launch.  The "attention.rs" page normalizes and rotates q
- * and k ahead of the q8 append and the decode (its qk_norm_rope_b dispatch);
- * here the wavefront that stages a sequence's q rows normalizes and rotates
- * them, and the one that appends its new K row does the same to it before
- * quantizing.  The result (outputs and cache words) is exactly that of
- *   q8_norm_rope(q', .., q, .., positions, q_weight, table, rot, num_positions, eps)
+ * and k ahead of the q8 append and the decode (its qk_norm_rope_b dispatch),
+ * and its decode reads q heads 2*head_dim apart (q and the output gate
+ * interleaved per head); here the wavefront that stages a sequence's q rows
+ * normalizes and rotates them, and the one that appends its new K row does
+ * the same to it before quantizing.  The result (outputs and cache words) is
+ * exactly that of
+ *   q8_norm_rope(q', .., q, q_stride, q_head_stride, .., positions, q_weight, table, rot, num_positions, eps)
  *   q8_norm_rope_cache_write(key, .., value, .., slots, positions, k_weight, ...)
  *   q8_paged_decode(out, q', ...)                       (dense mode)
  * with positions[s] = context_lens[s] - 1 and slots[s] the slot of that
  * position (its block_tables entry, offset position % block_size), for the
  * sequences q8_decode_step appends to (the others are not written, and their
- * q rows are still rotated at context_lens[s] - 1).
+ * q rows are still rotated at context_lens[s] - 1).  q itself is not written.
  *
- *   q             f32 query rows before the step, laid out as for q8_decode_step.
+ *   q             f32 query rows before the step: head h of sequence s at
+ *                 q[s*q_stride + h*q_head_stride + d].
+ *   q_head_stride elements between the heads of a row: head_size for packed
+ *                 heads (0 means the same), 2*head_size for the q/gate
+ *                 interleave; at least head_size, and q_stride at least
+ *                 (num_heads-1)*q_head_stride + head_size.
  *   q_weight,     device f32 [head_size]: the q and K norm weights.
  *   k_weight
  *   table, rot,   as for q8_norm_rope (table unused and may be NULL when
@@ -456,14 +463,15 @@ q8_status q8_norm_rope_qk_cache_write(float* q_out, uint32_t q_out_stride, const
  *   the rest      as q8_decode_step, including the workspace.
  *
  * Errors: those of q8_decode_step; Q8_ERR_SHAPE under the shape rules of
- * q8_norm_rope; Q8_ERR_NULL for a NULL weight, or a NULL table with rot > 0
- * (num_seqs > 0); Q8_ERR_UNSUPPORTED unless head_size is 128, num_heads /
- * num_kv_heads is at most 8, both caches are 16-byte aligned and block_size
- * is a multiple of 4 that divides, or is a multiple of, the positions per
- * chunk (32 when num_heads / num_kv_heads <= 4, else 64).  Other shapes take
- * q8_norm_rope_qk_cache_write followed by q8_paged_decode.
+ * q8_norm_rope or for a q_head_stride below head_size; Q8_ERR_NULL for a NULL
+ * weight, or a NULL table with rot > 0 (num_seqs > 0); Q8_ERR_UNSUPPORTED
+ * unless head_size is 64, 128 or 256, both caches are 16-byte aligned and
+ * block_size is a multiple of 4 that divides, or is a multiple of, the
+ * positions per chunk (32 for head_size <= 128 with num_heads / num_kv_heads
+ * <= 4, else 64).  Other shapes take q8_norm_rope_qk_cache_write followed by
+ * q8_paged_decode.
  */
-q8_status q8_norm_rope_decode_step(float* out, const float* q, uint32_t q_stride,
+q8_status q8_norm_rope_decode_step(float* out, const float* q, uint32_t q_stride, uint32_t q_head_stride,
                                    const float* key, uint32_t key_stride,
                                    const float* value, uint32_t value_stride,
                                    uint32_t* key_cache, uint32_t* value_cache,

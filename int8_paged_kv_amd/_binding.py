@@ -105,7 +105,7 @@ def _open(path: str) -> ctypes.CDLL:
     lib.q8_norm_rope_qk_cache_write.argtypes = [P, U, P, U, U, U, U, P, P, P, U, P, U, P, P, P, P, P, P, U, U,
                                                 F, U, U, U, U, U, P]
     lib.q8_norm_rope_qk_cache_write.restype = ctypes.c_int
-    lib.q8_norm_rope_decode_step.argtypes = [P, P, U, P, U, P, U, P, P, P, U, P, U, P, P, P, U, U, F,
+    lib.q8_norm_rope_decode_step.argtypes = [P, P, U, U, P, U, P, U, P, P, P, U, P, U, P, P, P, U, U, F,
                                              U, U, U, U, U, U, F, P, ctypes.c_size_t, P]
     lib.q8_norm_rope_decode_step.restype = ctypes.c_int
     lib.q8_index_select.argtypes = [P, U, P, U, U, U, P, U, P, P, U, P]
@@ -329,11 +329,13 @@ def q8_norm_rope_decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Te
                              num_blocks: Optional[int] = None, stream=None) -> torch.Tensor:
     """q8_decode_step with the per-head RMSNorm + partial rotary step applied to q
     and to the new K rows at position context_lens[s]-1, in the same launch (see
-    include/q8kv.h).  q is the un-normalized [S, H, head_size] f32; table is
+    include/q8kv.h).  q is the un-normalized [S, H, head_size] f32 with unit
+    element stride; its head stride may exceed head_size (a q/gate interleave,
+    e.g. x[:, :, :head_size] of an [S, H, 2*head_size] tensor).  table is
     q8_rope_table's [num_positions, rot] (None when rot == 0)."""
     lib = load_library()
-    if q.dim() != 3 or (q.numel() and not q[0].is_contiguous()):
-        raise ValueError("q must be [S, H, head_size] with dense rows")
+    if q.dim() != 3 or (q.numel() and q.stride(2) != 1):
+        raise ValueError("q must be [S, H, head_size] with unit element stride")
     S, H, hs = q.shape
     if out is None:
         out = torch.empty((S, H, hs), dtype=torch.float32, device=q.device)
@@ -355,7 +357,7 @@ def q8_norm_rope_decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Te
     num_positions = table.shape[0] if (table is not None and rot) else 0
     tab = _dev(table, "table", torch.float32) if (table is not None and rot) else None
     st = lib.q8_norm_rope_decode_step(_dev(out, "out", torch.float32), _dev(q, "q", torch.float32), q.stride(0),
-                                      kp, kst, vp, vst,
+                                      q.stride(1), kp, kst, vp, vst,
                                       _u32(key_cache, "key_cache"), _u32(value_cache, "value_cache"),
                                       _u32(block_tables, "block_tables"), block_tables.shape[1],
                                       _u32(context_lens, "context_lens"), mcl,

@@ -175,11 +175,16 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
                         uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
                         float scale, void* workspace, size_t workspace_bytes,
                         void* stream, const AppendArgs* app, uint32_t rows_per_seq,
-                        bool static_scratch = false, const NormRopeStepArgs* nr = nullptr) {
+                        bool static_scratch = false, const NormRopeStepArgs* nr = nullptr,
+                        uint32_t q_head_stride = 0) {
     if (!head_size_ok(head_size) || block_size == 0 || num_heads == 0 || num_kv_heads == 0 ||
         num_heads % num_kv_heads != 0)
         return Q8_ERR_SHAPE;
-    if (static_cast<uint64_t>(q_stride) < static_cast<uint64_t>(num_heads) * head_size) return Q8_ERR_SHAPE;
+    // head h of a q row at h * q_head_stride (0: packed heads, head_size apart)
+    if (q_head_stride == 0) q_head_stride = head_size;
+    if (q_head_stride < head_size) return Q8_ERR_SHAPE;
+    if (static_cast<uint64_t>(q_stride) < static_cast<uint64_t>(num_heads - 1) * q_head_stride + head_size)
+        return Q8_ERR_SHAPE;
     const bool vis = visible_pos != nullptr;
     if (vis && vis_stride == 0) return Q8_ERR_SHAPE;
     if (app) {
@@ -231,6 +236,7 @@ q8_status decode_common(float* out, const float* q, uint32_t q_stride,
     a.num_visible = num_visible;
     a.workspace = p.bytes ? workspace : nullptr;
     a.q_stride = q_stride;
+    a.q_head_stride = q_head_stride;
     a.max_num_blocks_per_seq = max_num_blocks_per_seq;
     a.max_context_len = max_context_len;
     a.vis_stride = vis_stride;
@@ -334,7 +340,7 @@ q8_status q8_decode_step(float* out, const float* q, uint32_t q_stride,
                          stream, &app, 1);
 }
 
-q8_status q8_norm_rope_decode_step(float* out, const float* q, uint32_t q_stride,
+q8_status q8_norm_rope_decode_step(float* out, const float* q, uint32_t q_stride, uint32_t q_head_stride,
                                    const float* key, uint32_t key_stride,
                                    const float* value, uint32_t value_stride,
                                    uint32_t* key_cache, uint32_t* value_cache,
@@ -353,7 +359,7 @@ q8_status q8_norm_rope_decode_step(float* out, const float* q, uint32_t q_stride
     return decode_common(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
                          context_lens, max_context_len, nullptr, nullptr, 0, num_seqs, num_heads,
                          num_kv_heads, head_size, block_size, num_blocks, scale, workspace, workspace_bytes,
-                         stream, &app, 1, false, &nr);
+                         stream, &app, 1, false, &nr, q_head_stride);
 }
 
 q8_status q8_f32_cache_write(const float* key, uint32_t key_stride,

@@ -110,14 +110,14 @@ bool tiles_ok(const DecodeArgs& a, uint32_t ch) {
 
 bool norm_rope_decode_supported(uint32_t head_size, uint32_t num_heads, uint32_t num_kv_heads, uint32_t block_size,
                                 const uint32_t* key_cache, const uint32_t* value_cache) {
-    if (head_size != 128 || num_kv_heads == 0) return false;
+    if ((head_size != 64 && head_size != 128 && head_size != 256) || num_kv_heads == 0) return false;
     const uint32_t group = decode_group(num_heads / num_kv_heads);
-    if (group > 8) return false;
+    if (head_size == 256 && group == 16) return false;    // no instantiation (register pressure)
     DecodeArgs a{};
     a.block_size = block_size;
     a.key_cache = key_cache;
     a.value_cache = value_cache;
-    return tiles_ok(a, static_cast<uint32_t>(decode_chunk(32, static_cast<int>(group / 4))));
+    return tiles_ok(a, static_cast<uint32_t>(decode_chunk(static_cast<int>(head_size / 4), static_cast<int>(group / 4))));
 }
 
 hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_t stream) {
@@ -132,7 +132,7 @@ hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_
     SplitConsts c{};
     c.seg_rows = a.block_size < ch ? a.block_size : ch;
     c.tiled_ok = tiles_ok(a, ch);
-    c.q_vec_ok = reinterpret_cast<uintptr_t>(a.q) % 16 == 0 && a.q_stride % 4 == 0;
+    c.q_vec_ok = reinterpret_cast<uintptr_t>(a.q) % 16 == 0 && a.q_stride % 4 == 0 && a.q_head_stride % 4 == 0;
     c.seg_u4 = c.seg_rows * wpt / 4;
     if (c.seg_u4 == 0) c.seg_u4 = 1;
     c.seg_magic = static_cast<uint32_t>((0x100000000ull + c.seg_u4 - 1) / c.seg_u4);
@@ -146,7 +146,12 @@ hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_
     else fn = split_kernel_hs64(vis, t, hs4 == 64, group, seg_whole);
     if (a.nr_q_weight) {
         // the norm + rotary step exists for the shapes norm_rope_decode_supported accepts
-        fn = !vis && t && hs4 == 32 && a.rows_per_seq <= 1 ? split_kernel_nr_hs32(group, seg_whole) : nullptr;
+        fn = nullptr;
+        if (!vis && t && a.rows_per_seq <= 1) {
+            if (hs4 == 16) fn = split_kernel_nr_hs16(group, seg_whole);
+            else if (hs4 == 32) fn = split_kernel_nr_hs32(group, seg_whole);
+            else if (hs4 == 64) fn = split_kernel_nr_hs64(group, seg_whole);
+        }
         if (!fn) return hipErrorInvalidValue;
     }
     // As many persistent wavefronts as the device keeps resident for this

@@ -292,10 +292,10 @@ struct Shares {
 // each segment of a chunk fills whole 64-lane slots (SEGR*HS4P/256 of them)
 // plus SEGR/4 trailing 16-byte units: every full slot then loads from one
 // segment with a scalar base address and a fixed per-lane offset.  NR: the
-// decode step with the per-head RMSNorm + partial rotary step (head_size 128,
-// dense positions): q rows and the new K row are normalized and rotated at the
-// sequence's last position as they are staged, as the standalone norm + rotary
-// kernels do it.
+// decode step with the per-head RMSNorm + partial rotary step (head_size 64,
+// 128 or 256, dense positions): q rows and the new K row are normalized and
+// rotated at the sequence's last position as they are staged, as the
+// standalone norm + rotary kernels do it.
 template <int HS4P, bool EXACT, int NHS, bool VIS, bool TILED, int SEGR, int CH, bool NR = false>
 __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 || CH == 32)) ? 2 : 1) void decode_split_kernel(DecodeArgs a, SplitConsts c, uint32_t num_blocks_m1) {
     constexpr int NKB = HS4P / 16;             // 64-dimension k-blocks of q.K^T
@@ -307,7 +307,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     constexpr int NTG = CH / 16;               // 16-token column groups of a chunk
     constexpr uint32_t kCostSeq = cost_seq(CH);
     static_assert(CH == 32 || CH == 64, "chunk size");
-    static_assert(!NR || (HS4P == 32 && EXACT && !VIS), "norm + rotary step: 32 lanes per q head, dense positions");
+    static_assert(!NR || ((HS4P == 16 || HS4P == 32 || HS4P == 64) && EXACT && !VIS),
+                  "norm + rotary step: 16, 32 or 64 lanes per q head, dense positions");
     constexpr int NU = (CH * WPT_MAX + 4 * kWave - 1) / (4 * kWave);   // 16-byte slots per lane
     // An exact head size makes a chunk CH*(HS4P+1) words: CH*HS4P/256 full
     // 16-byte slots per lane plus a 4-byte tail slot in CH lanes.
@@ -693,25 +694,22 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     // loads brought in (the cache still held the old one) and, for the first
     // query-head group of the kv head, are written to the caches.
     float4 nkx = make_float4(0.f, 0.f, 0.f, 0.f), nvx = nkx;
-    // Norm + rotary step: the table row of a position (clamped to the table),
-    // and for the new K row lane w's weights and cos/sin (64-lane group, w =
-    // lane), staged with it.
+    // Norm + rotary step: the table row of a position (clamped to the table);
+    // the staged q rows' weights and cos/sin (q_op, at the position of their
+    // sequence's last row); the new K row's weights for lane w = lane (64-lane
+    // group), staged with it.
     auto nr_row = [&](uint32_t pos) __attribute__((always_inline)) -> const float* {
         if (a.nr_rot == 0) return a.nr_table;
         const uint32_t p = pos < a.nr_num_positions ? pos : a.nr_num_positions - 1;
         return a.nr_table + static_cast<uint64_t>(p) * a.nr_rot;
     };
-    RopeLane nk_op{};
+    RopeLane q_op{};
+    float4 nk_wt = make_float4(0.f, 0.f, 0.f, 0.f);
     auto issue_new = [&](const Meta& m) __attribute__((always_inline)) {
         if (!append || !m.app) return;
         nkx = make_float4(0.f, 0.f, 0.f, 0.f);
         nvx = nkx;
-        if constexpr (NR) {
-            // the appended row's position: the chunk's last (context_lens[s] - 1)
-            const float* cs = nr_row(m.cs + meta_nv(m) - 1);
-            nk_op.wt = load_weight4(a.nr_k_weight, lane, hs4, a.nr_params_vec4 != 0);
-            load_cs4(cs, lane, a.nr_rot, a.nr_params_vec4 != 0, nk_op.c, nk_op.s);
-        }
+        if constexpr (NR) nk_wt = load_weight4(a.nr_k_weight, lane, hs4, a.nr_params_vec4 != 0);
         if (lane < hs4) {
             const float* pk = a.new_key + static_cast<uint64_t>(m.s) * a.new_key_stride + static_cast<uint64_t>(kvh) * hs + 4 * lane;
             const float* pv = a.new_value + static_cast<uint64_t>(m.s) * a.new_value_stride + static_cast<uint64_t>(kvh) * hs + 4 * lane;
@@ -726,9 +724,14 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     };
     auto store_new = [&](const Meta& m) __attribute__((always_inline)) {
         if (!append || !m.app) return;
-        // lanes at and above head_size/4 hold zeros and weight 0: they add
-        // nothing to the sum of squares and stay 0
-        if constexpr (NR) nkx = norm_rope4<kWave>(nkx, lane, RowMean(hs), nk_op, a.nr_rot, a.nr_eps);
+        // The appended row sits at the q rows' position, context_lens[s] - 1,
+        // and the staged q rows are still this sequence's (the next
+        // sequence's are staged after this store), so their cos/sin serve:
+        // rotated lanes lie below 2 * (rot / 8) <= HS4P, where the q lane
+        // w = lane % HS4P equals lane.  Lanes at and above head_size/4 hold
+        // zeros and weight 0: they add nothing to the sum of squares and stay 0.
+        if constexpr (NR)
+            nkx = norm_rope4<kWave>(nkx, lane, RowMean(hs), RopeLane{nk_wt, q_op.c, q_op.s}, a.nr_rot, a.nr_eps);
         uint32_t ks, vs;
         const uint32_t kw = quantize_word<kWave>(nkx, ks);
         const uint32_t vw = quantize_word<kWave>(nvx, vs);
@@ -825,17 +828,17 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     constexpr int QF = G * QD / (4 * kWave);
     static_assert(QF * kWave <= NHS * 16 * 16 && (QSCR || NHS * NKB * 256 <= BUFW), "q scratch");
     float4 qv[QF];
-    // Norm + rotary step on the staged q rows: lane w = lane % 32 of each
-    // 32-lane half holds elements 4w .. 4w+3 of one head (QD == 128), so one
-    // set of weights and cos/sin per lane serves every slot.
-    RopeLane q_op{};
+    // Norm + rotary step on the staged q rows: an exact head fills HS4P lanes
+    // of a slot (QD == 4 * HS4P), lane w = lane % HS4P holding its elements
+    // 4w .. 4w+3, so one set of weights and cos/sin per lane (q_op, staged
+    // with the rows) serves every slot.
     auto q_issue = [&](uint32_t s) __attribute__((always_inline)) {
         const uint64_t row = static_cast<uint64_t>(s) * nrow * a.q_stride;
         if constexpr (NR) {
             // position context_lens[s] - 1 (a staged sequence has positions, so
             // context_lens[s] >= 1)
             const uint32_t L = one_window ? lane_value(win_len, s) : uniform(a.context_lens[s]);
-            const uint32_t w = lane % 32u;
+            const uint32_t w = lane % static_cast<uint32_t>(HS4P);
             q_op.wt = load_weight4(a.nr_q_weight, w, hs4, a.nr_params_vec4 != 0);
             load_cs4(nr_row(L - 1), w, a.nr_rot, a.nr_params_vec4 != 0, q_op.c, q_op.s);
         }
@@ -846,7 +849,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             const bool ok = hi < nh && d < hs;               // d % 4 == 0 and hs % 4 == 0: all four or none
             const uint32_t pq = h0 + hi;                     // pair: row pq / n_rep, head kvh*n_rep + pq % n_rep
             const float* src = a.q + (ok ? row + static_cast<uint64_t>(pq / n_rep) * a.q_stride +
-                                           static_cast<uint64_t>(kvh * n_rep + pq % n_rep) * hs + d
+                                           static_cast<uint64_t>(kvh * n_rep + pq % n_rep) * a.q_head_stride + d
                                          : row);
             float4 v;
             if (c.q_vec_ok) {
@@ -869,7 +872,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
 #pragma unroll
             for (int t = 0; t < QF; ++t) {
                 const uint32_t hi = 4 * (lane + kWave * t) / QD;
-                const float4 y = norm_rope4<32>(qv[t], lane % 32u, mean, q_op, a.nr_rot, a.nr_eps);
+                const float4 y = norm_rope4<HS4P>(qv[t], lane % static_cast<uint32_t>(HS4P), mean, q_op, a.nr_rot,
+                                                  a.nr_eps);
                 qv[t] = hi < nh ? y : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
@@ -1288,16 +1292,27 @@ const void* split_kernel_g(bool vis, bool tiled, uint32_t group, uint32_t seg_ro
     return split_kernel_t<HS4P, EXACT, 1>(vis, tiled, seg_rows);
 }
 
-// The norm + rotary decode step (head_size 128, dense, tiled chunks) for sets
-// of NHS query heads.
-template <int NHS>
-const void* split_kernel_nr(uint32_t seg_rows) {
-    constexpr int CH = decode_chunk(32, NHS);
+// The norm + rotary decode step (exact head sizes of HS4P code words, dense,
+// tiled chunks) for sets of NHS query heads.
+template <int HS4P, int NHS>
+const void* split_kernel_nr_seg(uint32_t seg_rows) {
+    constexpr int CH = decode_chunk(HS4P, NHS);
     if (seg_rows == 16)
-        return reinterpret_cast<const void*>(&decode_split_kernel<32, true, NHS, false, true, 16, CH, true>);
+        return reinterpret_cast<const void*>(&decode_split_kernel<HS4P, true, NHS, false, true, 16, CH, true>);
     if (seg_rows == 32)
-        return reinterpret_cast<const void*>(&decode_split_kernel<32, true, NHS, false, true, 32, CH, true>);
-    return reinterpret_cast<const void*>(&decode_split_kernel<32, true, NHS, false, true, 0, CH, true>);
+        return reinterpret_cast<const void*>(&decode_split_kernel<HS4P, true, NHS, false, true, 32, CH, true>);
+    return reinterpret_cast<const void*>(&decode_split_kernel<HS4P, true, NHS, false, true, 0, CH, true>);
+}
+
+template <int HS4P>
+const void* split_kernel_nr(uint32_t group, uint32_t seg_rows) {
+    if (group == 16) {
+        // none for 16 heads at head_size 256: the plain kernel already spills there
+        if constexpr (HS4P == 64) return nullptr;
+        else return split_kernel_nr_seg<HS4P, 4>(seg_rows);
+    }
+    if (group == 8) return split_kernel_nr_seg<HS4P, 2>(seg_rows);
+    return split_kernel_nr_seg<HS4P, 1>(seg_rows);
 }
 
 }  // namespace

@@ -41,8 +41,11 @@ const void* split_kernel_hs16(bool vis, bool tiled, bool exact, uint32_t group, 
 const void* split_kernel_hs32(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
 const void* split_kernel_hs48(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
 const void* split_kernel_hs64(bool vis, bool tiled, bool exact, uint32_t group, uint32_t seg_rows);
-// The norm + rotary decode step's instantiation (head_size 128, dense
-// positions, tiled chunks) for query-head groups of 4 or 8; null otherwise.
+// The norm + rotary decode step's instantiation (head_size 64, 128 or 256:
+// 16, 32 or 64 code words per row; dense positions, tiled chunks) for
+// query-head groups of 4, 8 or 16 (not 16 at head_size 256: null).
+const void* split_kernel_nr_hs16(uint32_t group, uint32_t seg_rows);
 const void* split_kernel_nr_hs32(uint32_t group, uint32_t seg_rows);
+const void* split_kernel_nr_hs64(uint32_t group, uint32_t seg_rows);
 
 }  // namespace q8kv

@@ -1,10 +1,11 @@
-// Reductions over aligned groups of 32 or 64 lanes of a wavefront, with the
-// result in every lane of the group, bit-identical across them.
+// Reductions over aligned groups of 16, 32 or 64 lanes of a wavefront, with
+// the result in every lane of the group, bit-identical across them.
 //
 // The steps pair lanes 1 and 2 apart (DPP quad permutations), the mirrored
-// halves of each 8 and each 16 lanes (DPP row mirrors), lanes 16 apart (a
-// swizzle inside 32 lanes) and, for 64-lane groups, the two 32-lane halves
-// (lanes 0 and 32 read out).  Before every step the lanes on each side of a
+// halves of each 8 and each 16 lanes (DPP row mirrors), then, for 32- and
+// 64-lane groups, lanes 16 apart (a swizzle inside 32 lanes) and, for 64-lane
+// groups, the two 32-lane halves (lanes 0 and 32 read out).  A 16-lane group
+// therefore sums in the same order as the first half of a 32-lane one.  Before every step the lanes on each side of a
 // pairing already hold one identical value, so a commutative operation leaves
 // all lanes agreeing.  DPP and swizzle patterns are immediates: no lane index
 // arithmetic as with a general shuffle.  All lanes of the wave must be active.
@@ -56,12 +57,12 @@ __device__ __forceinline__ double read_lane(double v, int l) {
 
 template <int WIDTH, typename T, typename Op>
 __device__ __forceinline__ T group_reduce(T v, Op op) {
-    static_assert(WIDTH == 32 || WIDTH == 64, "groups of 32 or 64 lanes");
+    static_assert(WIDTH == 16 || WIDTH == 32 || WIDTH == 64, "groups of 16, 32 or 64 lanes");
     v = op(v, dpp<kDppXor1>(v));
     v = op(v, dpp<kDppXor2>(v));
     v = op(v, dpp<kDppHalfMirror>(v));
     v = op(v, dpp<kDppMirror>(v));
-    v = op(v, swz16(v));
+    if (WIDTH >= 32) v = op(v, swz16(v));
     if (WIDTH == 64) v = op(read_lane(v, 0), read_lane(v, 32));
     return v;
 }

@@ -126,6 +126,7 @@ struct DecodeArgs {
     float* part_ml;          // [row group, record, head in group, 2]: running max (log2 units), sum
     float* part_acc;         // [row group, record, head in group, head_size]: unnormalized output
     uint32_t q_stride, max_num_blocks_per_seq, max_context_len, vis_stride;
+    uint32_t q_head_stride;  // head h of a q row at h * q_head_stride (head_size unless the caller interleaves heads)
     uint32_t num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks;
     float scale_log2;        // softmax scale * log2(e)
     // Decode step (new_key non-null): sequence s's new K and V vectors
@@ -156,9 +157,9 @@ struct DecodeArgs {
 // max_positions: max_context_len in dense mode, vis_stride with visible lists.
 hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_t stream);
 // Whether the decode step with the norm + rotary step (dense, one row per
-// sequence) has a kernel for these shapes: head_size 128, at most 8 query
-// heads per kv head, caches 16-byte aligned and block_size nesting with the
-// chunk.
+// sequence) has a kernel for these shapes: head_size 64, 128 or 256 (at 256,
+// at most 8 query heads per kv head), caches 16-byte aligned and block_size
+// nesting with the chunk.
 bool norm_rope_decode_supported(uint32_t head_size, uint32_t num_heads, uint32_t num_kv_heads, uint32_t block_size,
                                 const uint32_t* key_cache, const uint32_t* value_cache);
 

@@ -34,7 +34,9 @@ const void* split_kernel_hs16(bool, bool, bool, uint32_t, uint32_t) { return nul
 const void* split_kernel_hs32(bool, bool, bool, uint32_t, uint32_t) { return nullptr; }
 const void* split_kernel_hs48(bool, bool, bool, uint32_t, uint32_t) { return nullptr; }
 const void* split_kernel_hs64(bool, bool, bool, uint32_t, uint32_t) { return nullptr; }
+const void* split_kernel_nr_hs16(uint32_t, uint32_t) { return nullptr; }
 const void* split_kernel_nr_hs32(uint32_t, uint32_t) { return nullptr; }
+const void* split_kernel_nr_hs64(uint32_t, uint32_t) { return nullptr; }
 }  // namespace q8kv
 
 static int failures = 0;
@@ -161,21 +163,25 @@ static void writer_and_step_validation() {
                                        4, 2, 128, 16, 8, nullptr) == Q8_ERR_SHAPE);
     // the decode step with the norm + rotary step
     void* ws = fake(0x4000);
-    EXPECT(q8_norm_rope_decode_step(o, k, 512, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 12, 100, 1e-6f, 2, 4, 2, 128,
+    EXPECT(q8_norm_rope_decode_step(o, k, 512, 0, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 12, 100, 1e-6f, 2, 4, 2, 128,
                                     16, 64, 0.1f, ws, 1u << 30, nullptr) == Q8_ERR_SHAPE);
-    EXPECT(q8_norm_rope_decode_step(o, k, 512, k, 256, k, 256, c, c, sl, 8, sl, 100, nullptr, w, w, 64, 100, 1e-6f, 2, 4, 2,
+    EXPECT(q8_norm_rope_decode_step(o, k, 512, 0, k, 256, k, 256, c, c, sl, 8, sl, 100, nullptr, w, w, 64, 100, 1e-6f, 2, 4, 2,
                                     128, 16, 64, 0.1f, ws, 1u << 30, nullptr) == Q8_ERR_NULL);
-    EXPECT(q8_norm_rope_decode_step(o, k, 256, k, 128, k, 128, c, c, sl, 8, sl, 100, w, w, w, 32, 100, 1e-6f, 2, 4, 2, 64,
+    EXPECT(q8_norm_rope_decode_step(o, k, 384, 0, k, 192, k, 192, c, c, sl, 8, sl, 100, w, w, w, 32, 100, 1e-6f, 2, 4, 2, 96,
                                     16, 64, 0.1f, ws, 1u << 30, nullptr) == Q8_ERR_UNSUPPORTED);
-    EXPECT(q8_norm_rope_decode_step(o, k, 512, k, 256, k, 256, reinterpret_cast<uint32_t*>(fake(0x3004)), c, sl, 8, sl,
+    EXPECT(q8_norm_rope_decode_step(o, k, 512, 100, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 64, 100, 1e-6f, 2, 4, 2,
+                                    128, 16, 64, 0.1f, ws, 1u << 30, nullptr) == Q8_ERR_SHAPE);
+    EXPECT(q8_norm_rope_decode_step(o, k, 0xFFFFFFFFu, 0x7FFFFFFFu, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 64, 100,
+                                    1e-6f, 2, 4, 2, 128, 16, 64, 0.1f, ws, 1u << 30, nullptr) == Q8_ERR_SHAPE);
+    EXPECT(q8_norm_rope_decode_step(o, k, 512, 0, k, 256, k, 256, reinterpret_cast<uint32_t*>(fake(0x3004)), c, sl, 8, sl,
                                     100, w, w, w, 64, 100, 1e-6f, 2, 4, 2, 128, 16, 64, 0.1f, ws, 1u << 30,
                                     nullptr) == Q8_ERR_UNSUPPORTED);
-    EXPECT(q8_norm_rope_decode_step(o, k, 512, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 64, 100, 1e-6f, 2, 4, 2, 128,
+    EXPECT(q8_norm_rope_decode_step(o, k, 512, 0, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 64, 100, 1e-6f, 2, 4, 2, 128,
                                     48, 64, 0.1f, ws, 1u << 30, nullptr) == Q8_ERR_UNSUPPORTED);
-    EXPECT(q8_norm_rope_decode_step(o, k, 512, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 64, 100, 1e-6f, 2, 4, 2, 128,
+    EXPECT(q8_norm_rope_decode_step(o, k, 512, 0, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 64, 100, 1e-6f, 2, 4, 2, 128,
                                     16, 64, 0.1f, ws, 16, nullptr) == Q8_ERR_WORKSPACE);
     // a supported shape reaches the launch (no kernel in this build: a HIP error)
-    EXPECT(q8_norm_rope_decode_step(o, k, 512, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 64, 100, 1e-6f, 2, 4, 2, 128,
+    EXPECT(q8_norm_rope_decode_step(o, k, 512, 0, k, 256, k, 256, c, c, sl, 8, sl, 100, w, w, w, 64, 100, 1e-6f, 2, 4, 2, 128,
                                     16, 64, 0.1f, ws, 1u << 30, nullptr) == Q8_ERR_HIP);
     // block selection
     EXPECT(q8_index_select(k, 100, sl, 4, 0, 8, c, 1000, c, nullptr, 0, nullptr) == Q8_ERR_SHAPE);

@@ -136,11 +136,11 @@ def test_decode_step_validation(lib, kw, want):
 
 
 def nr_step_args(**kw):
-    a = dict(out=FAKE, q=FAKE, q_stride=4 * 128, k=FAKE, ks=2 * 128, v=FAKE, vs=2 * 128, kc=FAKE, vc=FAKE,
+    a = dict(out=FAKE, q=FAKE, q_stride=4 * 128, qhs=0, k=FAKE, ks=2 * 128, v=FAKE, vs=2 * 128, kc=FAKE, vc=FAKE,
              bt=FAKE, max_nb=8, cl=FAKE, mcl=5000, qw=FAKE, kw=FAKE, tab=FAKE, rot=64, npos=8192, eps=1e-6,
              S=2, H=4, Hkv=2, hs=128, bs=16, nb=64, scale=0.1, ws=FAKE, wsb=1 << 30, stream=None)
     a.update(kw)
-    return [a[k] for k in ("out", "q", "q_stride", "k", "ks", "v", "vs", "kc", "vc", "bt", "max_nb", "cl", "mcl",
+    return [a[k] for k in ("out", "q", "q_stride", "qhs", "k", "ks", "v", "vs", "kc", "vc", "bt", "max_nb", "cl", "mcl",
                            "qw", "kw", "tab", "rot", "npos", "eps",
                            "S", "H", "Hkv", "hs", "bs", "nb", "scale", "ws", "wsb", "stream")]
 
@@ -152,12 +152,15 @@ def nr_step_args(**kw):
     # those of the decode step
     (dict(k=None), 1), (dict(cl=None), 1), (dict(ks=255), 2), (dict(hs=130), 2), (dict(H=5), 2),
     (dict(wsb=16), 3), (dict(out=ctypes.c_void_p(0x2004)), 5), (dict(S=0), 0), (dict(S=0, qw=None), 0),
-    # shapes without a fused kernel: head_size other than 128, more than 8
-    # query heads per kv head, misaligned caches, block sizes not nesting with
-    # the chunk (32 positions for up to 4 query heads per kv head, else 64)
-    (dict(hs=64, rot=32, q_stride=4 * 64, ks=128, vs=128), 5), (dict(H=32, q_stride=32 * 128), 5),
+    # q head stride: below head_size, or a row too short for its heads
+    (dict(qhs=100), 2), (dict(qhs=256, q_stride=4 * 256 - 129), 2), (dict(qhs=256, q_stride=4 * 256 - 128, wsb=16), 3),
+    # shapes without a fused kernel: head sizes other than 64, 128 and 256,
+    # misaligned caches, block sizes not nesting with the chunk (32 positions
+    # at head_size <= 128 with up to 4 query heads per kv head, else 64)
+    (dict(hs=96, rot=32, q_stride=4 * 96, ks=192, vs=192), 5), (dict(hs=32, rot=32, q_stride=4 * 32, ks=64, vs=64), 5),
     (dict(kc=ctypes.c_void_p(0x1004)), 5), (dict(vc=ctypes.c_void_p(0x1008)), 5), (dict(bs=48), 5),
-    (dict(bs=6), 5), (dict(H=16, q_stride=16 * 128, bs=48), 5),
+    (dict(bs=6), 5), (dict(H=16, q_stride=16 * 128, bs=48), 5), (dict(H=32, q_stride=32 * 128, bs=96), 5),
+    (dict(hs=256, q_stride=4 * 256, ks=512, vs=512, bs=96), 5),
 ])
 def test_norm_rope_decode_step_validation(lib, kw, want):
     assert lib.q8_norm_rope_decode_step(*nr_step_args(**kw)) == want
