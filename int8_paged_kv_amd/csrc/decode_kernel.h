@@ -169,6 +169,12 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 __device__ __forceinline__ void load_lds16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(g), "s"(lds) : "memory", "m0");
 }
+// A load through the scalar data cache from a wave-uniform address of data no
+// kernel writes during the launch (read only: nothing is stored that way).
+__device__ __forceinline__ uint32_t scalar_load(const uint32_t* p) {
+    typedef const __attribute__((address_space(4))) uint32_t* ConstPtr;
+    return *(ConstPtr)p;     // (a C-style cast: the only one that changes address space)
+}
 // Waits for every outstanding vector memory operation of the wavefront.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 // Device-coherent loads the compiler tracks (relaxed agent-scope atomic
@@ -548,7 +554,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
         p0 = lane_value(vc_first, ci - vc_c0);
         pl = lane_value(vc_last, ci - vc_c0);
     };
-    auto meta_of = [&](bool live) __attribute__((always_inline)) -> Meta {
+    auto meta_of = [&](bool live, bool first = false) __attribute__((always_inline)) -> Meta {
         Meta m;
         m.s = cur.s;
         m.cs = cur.ci * CH;
@@ -580,7 +586,18 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
         const bool used = lane < nseg && k * c.seg_rows < nv;
         bounds_report(a.bounds_flags, used && jb >= a.max_num_blocks_per_seq, kBoundTable);
         jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
-        m.id = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
+        if (first && nseg <= 2) {
+            // The first chunk's (at most two) block ids as scalar loads: they
+            // skip the vector-memory queue, where the tile loads the CU's
+            // other waves have already issued sit ahead of them.
+            const uint64_t row = static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq;
+            const uint32_t j0 = uniform(lane_value(jb, 0)), j1 = uniform(lane_value(jb, 1));
+            const uint32_t id0 = scalar_load(a.block_tables + row + j0);
+            const uint32_t id1 = scalar_load(a.block_tables + row + j1);
+            m.id = lane == 0 ? id0 : id1;
+        } else {
+            m.id = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
+        }
 #ifdef Q8_DEBUG_BOUNDS
         bounds_report(a.bounds_flags, used && (tiled != 0) && m.id > num_blocks_m1, kBoundBlock);
         if (VIS && nv > 0 && tiled) {
@@ -1200,11 +1217,11 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     // tile loads of chunk x+1 into the freed registers (and the q rows of its
     // sequence when that changes), and processes chunk x.
     reset();
-    // Prologue order: block ids of chunk x0, q of its sequence, chunk x0's
-    // tiles, block ids of x0+1; the q digits are formed while tiles arrive.
+    // Prologue order: q of the first sequence, block ids of chunk x0, chunk
+    // x0's tiles, block ids of x0+1; the q digits are formed while tiles arrive.
     Buf bA;
-    Meta mc = meta_of(true);
-    q_issue(mc.s);
+    q_issue(cur.s);                       // q first: the first chunk's block-id wait below would delay it
+    Meta mc = meta_of(true, true);
     issue_data(mc, bA, sK, sV);
     issue_new(mc);
     Meta mn1;
