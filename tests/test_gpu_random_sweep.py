@@ -1,8 +1,8 @@
 """Randomized GPU parity sweep against the oracle: decode (dense and
 visible-list), the one-launch step, multi-row decode, the cache writer
 (bit-exact; small and batched sizes, pads), block selection (lists, counts
-and bitmasks bit-exact), the q + K/V norm and rotary launch and the f32-cache
-decode, over random head
+and bitmasks bit-exact), the q + K/V norm and rotary launch, the decode step
+with the norm and rotary step inside it, and the f32-cache decode, over random head
 sizes, block sizes, GQA ratios, batch sizes on both sides of the 64-sequence
 window, length mixes (empty, one token, block and chunk edges, long), clamps
 and forced wavefront counts.  Every case is drawn from a fixed seed and named
@@ -153,3 +153,46 @@ def test_random_case(oracle_mod, i):
     finally:
         os.environ.pop("Q8KV_DECODE_WAVES", None)
         os.environ.pop("Q8KV_F32_DECODE_WAVES", None)
+
+
+N_NR_CASES = 24
+
+
+def draw_nr(i):
+    """A random decode step with the norm + rotary step (its supported shapes)."""
+    g = np.random.default_rng(5000 + i)
+    hs = int(g.choice([64, 128, 256]))
+    bs = int(g.choice([4, 8, 16, 32, 64, 128]))
+    hkv = int(g.choice(KV_HEADS))
+    n_rep = int(g.choice([r for r in N_REPS if hs < 256 or r <= 8]))
+    while hkv * n_rep > 64:
+        n_rep = max(1, n_rep // 2)
+    S = int(g.choice([1, 2, 5, 17, 63, 64, 65, 80]))
+    edges = [0, 1, bs - 1 if bs > 1 else 1, bs, bs + 1, 31, 32, 33, 63, 64, 65, 129]
+    budget = 30000 // max(1, S)
+    lens = [0 if r < 0.1 else int(g.choice(edges)) if r < 0.4 else int(g.integers(1, max(2, min(2000, budget))))
+            for r in g.random(S)]
+    mcl = int(g.integers(1, max(lens))) if g.random() < 0.25 and max(lens) > 2 else None
+    P = int(g.choice([8192, max(2, max(lens) // 2)]))           # sometimes positions past the table
+    return dict(hs=hs, bs=bs, Hkv=hkv, H=hkv * n_rep, S=S, lens=lens, mcl=mcl, P=P,
+                rot=8 * int(g.integers(0, hs // 8 + 1)), eps=float(g.choice([0.0, 1e-6, 1e-5])),
+                layout=str(g.choice(["packed", "packed", "interleave", "offset"])),
+                misaligned=bool(g.random() < 0.3), waves=WAVES[int(g.integers(len(WAVES)))], seed=6000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_NR_CASES))
+def test_random_norm_rope_step_case(oracle_mod, i):
+    """q8_norm_rope_decode_step: bit-exact against q8_norm_rope + q8_decode_step,
+    and against the oracle's norm_rope -> norm_rope_cache_write -> paged_decode."""
+    from test_gpu_norm_rope_step import run_case
+    p = draw_nr(i)
+    name = "nr case %d: %s" % (i, {k: (v if k != "lens" else v[:12]) for k, v in p.items()})
+    if p["waves"] is not None:
+        os.environ["Q8KV_DECODE_WAVES"] = str(p["waves"])
+    try:
+        run_case(oracle_mod, p["seed"], p["S"], p["H"], p["Hkv"], p["bs"], p["lens"], p["rot"], hs=p["hs"],
+                 mcl=p["mcl"], P=p["P"], eps=p["eps"], q_layout=p["layout"], misaligned_params=p["misaligned"])
+    except AssertionError as e:
+        raise AssertionError("%s: %s" % (name, e)) from None
+    finally:
+        os.environ.pop("Q8KV_DECODE_WAVES", None)
