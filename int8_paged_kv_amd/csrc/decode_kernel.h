@@ -117,9 +117,10 @@ __device__ __forceinline__ int exponent_bound(float x) {
     return e;
 }
 
-// Number of positions sequence s attends (in multi-row decode, its last row).
+// Number of positions sequence s attends (in multi-row decode, its last row);
+// in dense mode *len (when given) receives context_lens[s] itself.
 template <bool VIS>
-__device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s) {
+__device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s, uint32_t* len = nullptr) {
     uint32_t n;
     if (VIS) {
         n = a.num_visible[s];
@@ -127,6 +128,7 @@ __device__ __forceinline__ uint32_t positions_of(const DecodeArgs& a, uint32_t s
         n = n < a.vis_stride ? n : a.vis_stride;
     } else {
         n = a.context_lens[s];
+        if (len) *len = n;
         n = n < a.max_context_len ? n : a.max_context_len;
         const uint64_t cap = static_cast<uint64_t>(a.max_num_blocks_per_seq) * a.block_size;
         bounds_report(a.bounds_flags, n > cap, kBoundTable);
@@ -475,10 +477,29 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     struct Cursor {
         uint32_t s, ci, npos, before;    // sequence, chunk index in it, its positions, chunks before it
         uint32_t jf, nrec;               // first wave sharing the sequence, and their number
+        uint32_t len;                    // norm + rotary step without one window: context_lens[s]
     };
-    Cursor cur{uniform(s0), 0, 0, uniform(p0c), 0, 0};
+    Cursor cur{uniform(s0), 0, 0, uniform(p0c), 0, 0, 0};
     cur.ci = x0 - cur.before;
-    cur.npos = one_window ? uniform(np0) : uniform(positions_of<VIS>(a, cur.s));
+    // Positions of the cursor's sequence (with one load window, from a lane).
+    // The norm + rotary step also keeps the context length from the same
+    // read, so its q position, append test and multi-row limits need no read
+    // of their own (each would stall the wave on its round trip); the other
+    // instantiations read it where they need it (one register fewer across
+    // the loop, measurably faster at the headline shape).
+    auto load_seq = [&](uint32_t s_) __attribute__((always_inline)) {
+        if (one_window) {
+            cur.npos = lane_value(win_np, s_);
+        } else if constexpr (NR) {
+            uint32_t raw = 0;
+            cur.npos = uniform(positions_of<VIS>(a, s_, &raw));
+            cur.len = uniform(raw);
+        } else {
+            cur.npos = uniform(positions_of<VIS>(a, s_));
+        }
+    };
+    if (one_window) cur.npos = uniform(np0);
+    else load_seq(cur.s);
     auto share = [&]() __attribute__((always_inline)) {
         const uint32_t cf = first_cost(cur.s, cur.before);
         cur.jf = shares.wave_of(cf);
@@ -495,9 +516,14 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             cur.ci = 0;
             while (true) {
                 ++cur.s;
-                cur.npos = cur.s >= a.num_seqs ? static_cast<uint32_t>(CH)
-                           : one_window ? lane_value(win_np, cur.s)
-                                        : uniform(positions_of<VIS>(a, cur.s));
+                if constexpr (NR) {
+                    if (cur.s >= a.num_seqs) cur.npos = static_cast<uint32_t>(CH);
+                    else load_seq(cur.s);
+                } else {
+                    cur.npos = cur.s >= a.num_seqs ? static_cast<uint32_t>(CH)
+                               : one_window ? lane_value(win_np, cur.s)
+                                            : uniform(positions_of<VIS>(a, cur.s));
+                }
                 if (cur.npos != 0) break;
                 zero_seqs(cur.s, cur.s + 1);
             }
@@ -529,6 +555,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
         uint32_t s, cs, p0, info, jf, id;
         uint32_t app;            // decode step: the chunk's last row is its sequence's new token
         uint32_t lr;             // multi-row decode: context_lens[s] - cs (row b sees lr - (nrow-1-b) of the chunk)
+        uint32_t len;            // norm + rotary step: context_lens[s]
     };
     auto meta_nv = [](const Meta& m) __attribute__((always_inline)) { return m.info & 0x7Fu; };
     auto meta_tiled = [](const Meta& m) __attribute__((always_inline)) { return TILED || (m.info & 0x80u) != 0; };
@@ -574,11 +601,15 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
         // The new token sits at position context_lens[s]-1, the sequence's last
         // attended position when it is not clamped.
         m.lr = 0;
-        if (nrow > 1 && nv > 0) m.lr = (one_window ? lane_value(win_len, m.s) : uniform(a.context_lens[m.s])) - m.cs;
+        auto seq_len = [&]() __attribute__((always_inline)) -> uint32_t {
+            if (one_window) return lane_value(win_len, m.s);
+            return NR ? cur.len : uniform(a.context_lens[m.s]);
+        };
+        if constexpr (NR) m.len = seq_len();
+        if (nrow > 1 && nv > 0) m.lr = seq_len() - m.cs;
         m.app = 0;
         if (append && nv > 0 && m.cs + nv == cur.npos) {
-            const uint32_t L = one_window ? lane_value(win_len, m.s) : uniform(a.context_lens[m.s]);
-            m.app = L == cur.npos ? 1u : 0u;
+            m.app = seq_len() == cur.npos ? 1u : 0u;
         }
         const uint32_t k = min(lane, nseg - 1);
         uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(CH) ? k : 0u);
@@ -849,12 +880,11 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     // of a slot (QD == 4 * HS4P), lane w = lane % HS4P holding its elements
     // 4w .. 4w+3, so one set of weights and cos/sin per lane (q_op, staged
     // with the rows) serves every slot.
-    auto q_issue = [&](uint32_t s) __attribute__((always_inline)) {
+    auto q_issue = [&](uint32_t s, uint32_t L) __attribute__((always_inline)) {
         const uint64_t row = static_cast<uint64_t>(s) * nrow * a.q_stride;
         if constexpr (NR) {
-            // position context_lens[s] - 1 (a staged sequence has positions, so
-            // context_lens[s] >= 1)
-            const uint32_t L = one_window ? lane_value(win_len, s) : uniform(a.context_lens[s]);
+            // position L - 1, L = context_lens[s] (a staged sequence has
+            // positions, so L >= 1)
             const uint32_t w = lane % static_cast<uint32_t>(HS4P);
             q_op.wt = load_weight4(a.nr_q_weight, w, hs4, a.nr_params_vec4 != 0);
             load_cs4(nr_row(L - 1), w, a.nr_rot, a.nr_params_vec4 != 0, q_op.c, q_op.s);
@@ -1220,7 +1250,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     // Prologue order: q of the first sequence, block ids of chunk x0, chunk
     // x0's tiles, block ids of x0+1; the q digits are formed while tiles arrive.
     Buf bA;
-    q_issue(cur.s);                       // q first: the first chunk's block-id wait below would delay it
+    q_issue(cur.s, one_window ? lane_value(win_len, cur.s) : cur.len);   // q first: the first chunk's block-id wait below would delay it
     Meta mc = meta_of(true, true);
     issue_data(mc, bA, sK, sV);
     issue_new(mc);
@@ -1261,7 +1291,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
         issue_data(mn1, bA, sKn, sVn);
         issue_new(mn1);
         if (QSCR && new_q) q_finish();                        // with the next chunk's loads in flight
-        if (mn1.s != mc.s) q_issue(mn1.s);                    // q of the next chunk's sequence
+        if (mn1.s != mc.s) q_issue(mn1.s, mn1.len);                    // q of the next chunk's sequence
         wave_sync();
         process(mc);
         if (xr + 1 == n || mn1.s != mc.s) flush(mc);
