@@ -468,10 +468,14 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
     };
 
     const uint32_t hs = a.head_size, hs4 = EXACT ? HS4P : hs / 4, wpt = hs4 + 1;
-    const uint64_t kv_stride = static_cast<uint64_t>(a.num_kv_heads) * a.block_size * wpt;  // words per block
-    const uint64_t kvh_off = static_cast<uint64_t>(kvh) * a.block_size * wpt;
+    // In segment layouts a block is exactly one tile segment (block_size ==
+    // SEGR), so its size and the segment rows are compile-time constants.
+    const uint32_t bsz = FAST ? static_cast<uint32_t>(SEGR) : a.block_size;
+    const uint32_t segr = FAST ? static_cast<uint32_t>(SEGR) : c.seg_rows;
+    const uint64_t kv_stride = static_cast<uint64_t>(a.num_kv_heads) * bsz * wpt;  // words per block
+    const uint64_t kvh_off = static_cast<uint64_t>(kvh) * bsz * wpt;
     const uint32_t chunk_u4 = CH * wpt / 4;
-    const uint32_t nseg = CH / c.seg_rows;            // tile segments per tiled chunk
+    const uint32_t nseg = CH / segr;                  // tile segments per tiled chunk
 
     // ---- cursor over the chunk sequence (wave-uniform) ----
     struct Cursor {
@@ -612,9 +616,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             m.app = seq_len() == cur.npos ? 1u : 0u;
         }
         const uint32_t k = min(lane, nseg - 1);
-        uint32_t jb = m.p0 / a.block_size + (a.block_size <= static_cast<uint32_t>(CH) ? k : 0u);
+        uint32_t jb = m.p0 / bsz + (bsz <= static_cast<uint32_t>(CH) ? k : 0u);
         // a segment holding attended positions (its first row below nv)
-        const bool used = lane < nseg && k * c.seg_rows < nv;
+        const bool used = lane < nseg && k * segr < nv;
         bounds_report(a.bounds_flags, used && jb >= a.max_num_blocks_per_seq, kBoundTable);
         jb = jb < a.max_num_blocks_per_seq ? jb : a.max_num_blocks_per_seq - 1;
         if (first && nseg <= 2) {
@@ -692,7 +696,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             return;
         }
         if (!TILED && !c.tiled_ok) return;     // no tile loads at all (caches not 16-byte aligned, odd block_size)
-        const uint32_t row0 = m.p0 % a.block_size;     // nonzero only when block_size > 64
+        const uint32_t row0 = m.p0 % bsz;              // nonzero only when block_size > 64
         const bool ok = meta_tiled(m);
         const uint32_t nv = meta_nv(m);
         const uint64_t base = kvh_off + static_cast<uint64_t>(row0) * wpt;
@@ -719,11 +723,11 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             bool valid;
             if (i < NF) {
                 const uint32_t u = ln + kWave * i;
-                valid = ok && (EXACT || u < chunk_u4) && (k * c.seg_rows < nv);
+                valid = ok && (EXACT || u < chunk_u4) && (k * segr < nv);
                 w = ph * kv_stride + base + (u - k * c.seg_u4) * 4;
             } else {
                 const uint32_t wi = 4 * kWave * NF + ln;
-                valid = ok && (k * c.seg_rows < nv);
+                valid = ok && (k * segr < nv);
                 w = ph * kv_stride + base + (wi - 4 * k * c.seg_u4);
             }
             w &= 0ull - static_cast<uint64_t>(valid);
@@ -792,7 +796,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             // a multiple of it), the row's block id is the one its chunk's
             // segment was read with (lane k of m.id holds segment k's): no new
             // load.  Otherwise it is read from the table.
-            const uint32_t bs = a.block_size;
+            const uint32_t bs = bsz;
             const bool nested = bs <= static_cast<uint32_t>(CH) ? CH % bs == 0 : bs % CH == 0;
             const uint32_t blk = nested ? lane_value(m.id, bs <= static_cast<uint32_t>(CH) ? (meta_nv(m) - 1) / bs : 0u)
                                         : uniform(a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq +
@@ -801,7 +805,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             // written for it (a clamped id would overwrite another block's row).
             bounds_report(a.bounds_flags, lane == 0 && blk > num_blocks_m1, kBoundBlock);
             if (blk > num_blocks_m1) return;
-            const uint64_t dst = ((static_cast<uint64_t>(blk) * a.num_kv_heads + kvh) * a.block_size + pos % a.block_size) * wpt;
+            const uint64_t dst = ((static_cast<uint64_t>(blk) * a.num_kv_heads + kvh) * bsz + pos % bsz) * wpt;
             if (lane < hs4) { a.key_cache_w[dst + lane] = kw; a.value_cache_w[dst + lane] = vw; }
             if (lane == 0) { a.key_cache_w[dst + hs4] = ks; a.value_cache_w[dst + hs4] = vs; }
         }
@@ -841,7 +845,7 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             // wave copies the rows one after another.
             const uint32_t nv = meta_nv(m);
             const uint32_t pos = position_at<VIS>(a, m.s, m.cs + min(lane, nv - 1));
-            uint32_t jb = pos / a.block_size;
+            uint32_t jb = pos / bsz;
             bounds_report(a.bounds_flags, lane < nv && jb >= a.max_num_blocks_per_seq, kBoundTable);
 #ifdef Q8_DEBUG_BOUNDS
             // listed positions ascending and distinct within the chunk
@@ -852,8 +856,8 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
             uint32_t phys = a.block_tables[static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq + jb];
             bounds_report(a.bounds_flags, lane < nv && phys > num_blocks_m1, kBoundBlock);
             phys = phys < num_blocks_m1 ? phys : num_blocks_m1;
-            const uint64_t my_row = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * a.block_size +
-                                     pos % a.block_size) * wpt;
+            const uint64_t my_row = ((static_cast<uint64_t>(phys) * a.num_kv_heads + kvh) * bsz +
+                                     pos % bsz) * wpt;
             for (uint32_t rr = 0; rr < nv; ++rr) {
                 const uint32_t lo = __shfl(static_cast<uint32_t>(my_row), rr, 64);
                 const uint32_t hi = __shfl(static_cast<uint32_t>(my_row >> 32), rr, 64);
