@@ -684,6 +684,8 @@ def main():
         nr_step2(0)
         torch.cuda.synchronize()
         fused_equal = bool(torch.equal(fused_out.view(torch.int32), outn.view(torch.int32)))
+        # the headline step's algorithmic bytes: int8 KV read, plus the append (f32 K/V in, packed rows out, slots)
+        B_nr = B + S * Hkv * (2 * hs * 4 + 2 * (hs + 4)) + 4 * S
         # bulk: 16384 tokens at scattered slots of a separate cache, fused vs plain writer
         Tb = 16384
         nbb = Tb // w.block_size + 64
@@ -716,6 +718,8 @@ def main():
                     "qk_norm_rope_cache_write_us_mean": round(float(tqk.mean()), 2),
                     "two_launch_step_us_mean": round(float(t2.mean()), 2),
                     "fused_step_us": round(t_fused, 2),
+                    "fused_step_GBps": round(B_nr / (t_fused * 1e-6) / 1e9, 1),
+                    "fused_step_frac_hbm_peak": round(B_nr / (t_fused * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "two_launch_step_us_back_to_back": round(t_two, 2),
                     "plain_step_us_back_to_back": round(t_plain, 2),
                     "fused_step_equals_two_launch_bitwise": fused_equal,
