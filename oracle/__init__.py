@@ -64,6 +64,16 @@ def _load():
         lib.q8o_f32_paged_decode.restype = ctypes.c_int
         lib.q8o_f32_paged_decode_units.argtypes = [P, P, U] + f32dec
         lib.q8o_f32_paged_decode_units.restype = ctypes.c_int
+        lib.q8o_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.q8o_f32_to_bf16.restype = ctypes.c_uint16
+        lib.q8o_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.q8o_bf16_to_f32.restype = ctypes.c_float
+        lib.q8o_bf16_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U]
+        lib.q8o_bf16_cache_write.restype = ctypes.c_int
+        lib.q8o_bf16_paged_decode.argtypes = [P] + f32dec
+        lib.q8o_bf16_paged_decode.restype = ctypes.c_int
+        lib.q8o_bf16_paged_decode_units.argtypes = [P, P, U] + f32dec
+        lib.q8o_bf16_paged_decode_units.restype = ctypes.c_int
         F = ctypes.c_float
         lib.q8o_rope_table.argtypes = [P, U, U, F]
         lib.q8o_rope_table.restype = ctypes.c_int
@@ -259,6 +269,80 @@ def f32_paged_decode_units(units, q, key_cache, value_cache, block_tables, conte
                                               _ptr(key_cache), _ptr(value_cache), _ptr(bt), bt.shape[-1],
                                               _ptr(cl), mcl, S, H, num_kv_heads, hs, block_size, nb,
                                               float(scale), nthreads), "f32_paged_decode_units")
+    return out
+
+
+# ---------------------------------------------------------------- bf16 baseline ----
+
+def f32_to_bf16(x) -> np.ndarray:
+    """Round f32 values to bfloat16 (nearest, ties to even); returns their uint16 encodings."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = _load().q8o_f32_to_bf16
+    return np.array([f(float(v)) for v in x.reshape(-1)], dtype=np.uint16).reshape(x.shape)
+
+
+def bf16_to_f32(b) -> np.ndarray:
+    """bfloat16 encodings (uint16) read as f32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_cache_write(key, value, key_cache, value_cache, slot_mapping, num_kv_heads, head_size,
+                     block_size, num_blocks=None, key_stride=None, value_stride=None):
+    """Round K and V rows to bfloat16 into the bf16 caches at their slots, in place (uint16 arrays)."""
+    key = _c(key, np.float32)
+    value = _c(value, np.float32)
+    slot_mapping = _c(slot_mapping, np.uint32)
+    for c in (key_cache, value_cache):
+        if c.dtype != np.uint16 or not c.flags.c_contiguous:
+            raise ValueError("bf16 caches must be contiguous uint16 arrays")
+    T = slot_mapping.shape[0]
+    ks = key_stride if key_stride is not None else (key.size // T if T else num_kv_heads * head_size)
+    vs = value_stride if value_stride is not None else (value.size // T if T else num_kv_heads * head_size)
+    nb = num_blocks if num_blocks is not None else key_cache.size // (num_kv_heads * block_size * head_size)
+    _check(_load().q8o_bf16_cache_write(_ptr(key), ks, _ptr(value), vs, _ptr(key_cache), _ptr(value_cache),
+                                        _ptr(slot_mapping), T, num_kv_heads, head_size, block_size, nb),
+           "bf16_cache_write")
+
+
+def _bf16_common(q, key_cache, block_tables, context_lens, max_context_len, num_kv_heads, block_size,
+                 num_blocks):
+    q = _c(q, np.float32)
+    S, H, hs = q.shape
+    bt = _c(block_tables, np.uint32)
+    cl = _c(context_lens, np.uint32)
+    if key_cache.dtype != np.uint16 or not key_cache.flags.c_contiguous:
+        raise ValueError("bf16 caches must be contiguous uint16 arrays")
+    nb = num_blocks if num_blocks is not None else key_cache.size // (num_kv_heads * block_size * hs)
+    if max_context_len is None:
+        max_context_len = int(cl.max()) if cl.size else 0
+    return q, S, H, hs, bt, cl, nb, max_context_len
+
+
+def bf16_paged_decode(q, key_cache, value_cache, block_tables, context_lens, scale, num_kv_heads,
+                      block_size, max_context_len=None, num_blocks=None, nthreads=0) -> np.ndarray:
+    """Decode every (seq, head) over a bf16 paged cache; result [S, H, hs] f32."""
+    q, S, H, hs, bt, cl, nb, mcl = _bf16_common(q, key_cache, block_tables, context_lens,
+                                                max_context_len, num_kv_heads, block_size, num_blocks)
+    out = np.zeros((S, H, hs), dtype=np.float32)
+    _check(_load().q8o_bf16_paged_decode(_ptr(out), _ptr(q), H * hs, _ptr(key_cache), _ptr(value_cache),
+                                         _ptr(bt), bt.shape[-1], _ptr(cl), mcl, S, H, num_kv_heads, hs,
+                                         block_size, nb, float(scale), nthreads), "bf16_paged_decode")
+    return out
+
+
+def bf16_paged_decode_units(units, q, key_cache, value_cache, block_tables, context_lens, scale,
+                            num_kv_heads, block_size, max_context_len=None, num_blocks=None,
+                            nthreads=0) -> np.ndarray:
+    """Decode only the listed (seq, head) pairs over a bf16 cache; result [len(units), hs] f32."""
+    q, S, H, hs, bt, cl, nb, mcl = _bf16_common(q, key_cache, block_tables, context_lens,
+                                                max_context_len, num_kv_heads, block_size, num_blocks)
+    u = _c(np.asarray(units).reshape(-1, 2), np.uint32)
+    out = np.zeros((u.shape[0], hs), dtype=np.float32)
+    _check(_load().q8o_bf16_paged_decode_units(_ptr(out), _ptr(u), u.shape[0], _ptr(q), H * hs,
+                                               _ptr(key_cache), _ptr(value_cache), _ptr(bt), bt.shape[-1],
+                                               _ptr(cl), mcl, S, H, num_kv_heads, hs, block_size, nb,
+                                               float(scale), nthreads), "bf16_paged_decode_units")
     return out
 
 

@@ -50,6 +50,14 @@
  *   writer copies rows; the decode is the definition above with
  *   k_hat, v_hat the stored f32 values (exact in binary64).
  *
+ *   bf16 cache baseline (not on the pages: the half-width cache most serving
+ *   stacks keep, measured beside the f32 one).  The same layout with each
+ *   element stored as bfloat16, the upper half of a binary32 encoding: the
+ *   writer rounds each f32 input to the nearest bfloat16 value, ties to the
+ *   one with an even last significand bit (IEEE 754 round-to-nearest-even at
+ *   8 significand bits); the decode is the definition above with k_hat, v_hat
+ *   the stored bfloat16 values (exact in binary64).
+ *
  *   Norm + rotary step ahead of the cache write (the "attention.rs" page: the
  *   q/k norm-and-rope dispatches before the q8 append, with a learned per-head
  *   norm weight, rot = head_dim * partial_rotary_factor rotated elements, the
@@ -112,6 +120,26 @@ enum {
 
 static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* A bfloat16 value read as binary32 (its 16 bits are the upper half). */
+float q8o_bf16_to_f32(uint16_t b) { return bits_to_f32((uint32_t)b << 16); }
+
+/*
+ * The bfloat16 nearest to finite x, ties to even: bfloat16 keeps a binary32
+ * value's sign, exponent and top 7 fraction bits, so the candidates are the
+ * truncation t (x's upper 16 bits) and the next value away from zero, t + 1.
+ * The dropped 16 bits r decide: below half an ulp (0x8000) keep t, above it
+ * take t + 1, exactly half keep whichever of the two has an even last bit.
+ * (t + 1 past the largest finite magnitude is infinity, as rounding gives.)
+ */
+uint16_t q8o_f32_to_bf16(float x)
+{
+    const uint32_t u = f32_to_bits(x);
+    const uint32_t t = u >> 16, r = u & 0xFFFFu;
+    if (r < 0x8000u) return (uint16_t)t;
+    if (r > 0x8000u) return (uint16_t)(t + 1u);
+    return (uint16_t)((t & 1u) ? t + 1u : t);
+}
 
 /* One token vector x[0..head_size) -> head_size/4 code words + 1 scale word. */
 int q8o_quantize_row(const float* x, uint32_t head_size, uint32_t* row)
@@ -197,6 +225,7 @@ typedef struct {
     const float* q; uint32_t q_stride;
     const uint32_t* key_cache; const uint32_t* value_cache;
     const float* key_cache_f32; const float* value_cache_f32;   /* f32 baseline when non-NULL */
+    const uint16_t* key_cache_bf16; const uint16_t* value_cache_bf16;   /* bf16 baseline when non-NULL */
     const uint32_t* block_tables; uint32_t max_num_blocks_per_seq;
     const uint32_t* context_lens; uint32_t max_context_len;
     const uint32_t* visible_pos; const uint32_t* num_visible; uint32_t vis_stride;
@@ -213,6 +242,10 @@ static void load_row(const decode_args* a, int value, uint32_t phys, uint32_t of
         const float* c = value ? a->value_cache_f32 : a->key_cache_f32;
         const float* row = c + (((uint64_t)phys * a->num_kv_heads + kvh) * a->block_size + off) * hs;
         for (uint32_t d = 0; d < hs; ++d) out[d] = (double)row[d];
+    } else if (a->key_cache_bf16) {
+        const uint16_t* c = value ? a->value_cache_bf16 : a->key_cache_bf16;
+        const uint16_t* row = c + (((uint64_t)phys * a->num_kv_heads + kvh) * a->block_size + off) * hs;
+        for (uint32_t d = 0; d < hs; ++d) out[d] = (double)q8o_bf16_to_f32(row[d]);
     } else {
         const uint32_t* c = value ? a->value_cache : a->key_cache;
         q8o_dequantize_row(c + row_offset(phys, off, kvh, a->num_kv_heads, a->block_size, hs / 4 + 1),
@@ -343,7 +376,7 @@ int q8o_paged_decode_units(float* out, const uint32_t* units, uint32_t num_units
                            uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
                            float scale, int nthreads)
 {
-    decode_args a = { q, q_stride, key_cache, value_cache, NULL, NULL, block_tables,
+    decode_args a = { q, q_stride, key_cache, value_cache, NULL, NULL, NULL, NULL, block_tables,
                       max_num_blocks_per_seq, context_lens, max_context_len,
                       visible_pos, num_visible, vis_stride, num_seqs, num_heads,
                       num_kv_heads, head_size, block_size, num_blocks, (double)scale };
@@ -413,7 +446,7 @@ int q8o_f32_paged_decode_units(float* out, const uint32_t* units, uint32_t num_u
                                float scale, int nthreads)
 {
     if (!key_cache || !value_cache) return Q8O_ERR_SHAPE;
-    decode_args a = { q, q_stride, NULL, NULL, key_cache, value_cache, block_tables,
+    decode_args a = { q, q_stride, NULL, NULL, key_cache, value_cache, NULL, NULL, block_tables,
                       max_num_blocks_per_seq, context_lens, max_context_len,
                       NULL, NULL, 0, num_seqs, num_heads,
                       num_kv_heads, head_size, block_size, num_blocks, (double)scale };
@@ -437,6 +470,76 @@ int q8o_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
                                         context_lens, max_context_len, num_seqs, num_heads,
                                         num_kv_heads, head_size, block_size, num_blocks,
                                         scale, nthreads);
+    free(units);
+    return rc;
+}
+
+/* bf16 baseline writer: each element of row t, kv head h rounded to bfloat16
+ * (q8o_f32_to_bf16) at its slot; pads are skipped. */
+int q8o_bf16_cache_write(const float* key, uint32_t key_stride,
+                         const float* value, uint32_t value_stride,
+                         uint16_t* key_cache, uint16_t* value_cache,
+                         const uint32_t* slot_mapping, uint32_t num_tokens,
+                         uint32_t num_kv_heads, uint32_t head_size,
+                         uint32_t block_size, uint32_t num_blocks)
+{
+    if (head_size == 0 || block_size == 0 || num_kv_heads == 0) return Q8O_ERR_SHAPE;
+    if ((uint64_t)key_stride < (uint64_t)num_kv_heads * head_size ||
+        (uint64_t)value_stride < (uint64_t)num_kv_heads * head_size)
+        return Q8O_ERR_SHAPE;
+    for (uint32_t t = 0; t < num_tokens; ++t) {
+        uint32_t slot = slot_mapping[t];
+        if (slot == Q8O_PAD_SLOT) continue;
+        uint64_t block = slot / block_size, off = slot % block_size;
+        if (block >= num_blocks) return Q8O_ERR_RANGE;
+        for (uint32_t h = 0; h < num_kv_heads; ++h) {
+            uint64_t dst = ((block * num_kv_heads + h) * block_size + off) * head_size;
+            const float* k = key + (uint64_t)t * key_stride + (uint64_t)h * head_size;
+            const float* v = value + (uint64_t)t * value_stride + (uint64_t)h * head_size;
+            for (uint32_t d = 0; d < head_size; ++d) {
+                key_cache[dst + d] = q8o_f32_to_bf16(k[d]);
+                value_cache[dst + d] = q8o_f32_to_bf16(v[d]);
+            }
+        }
+    }
+    return Q8O_OK;
+}
+
+/* bf16 baseline decode of selected units (dense mode only); as q8o_paged_decode_units. */
+int q8o_bf16_paged_decode_units(float* out, const uint32_t* units, uint32_t num_units,
+                                const float* q, uint32_t q_stride,
+                                const uint16_t* key_cache, const uint16_t* value_cache,
+                                const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                                const uint32_t* context_lens, uint32_t max_context_len,
+                                uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                                uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                                float scale, int nthreads)
+{
+    if (!key_cache || !value_cache) return Q8O_ERR_SHAPE;
+    decode_args a = { q, q_stride, NULL, NULL, NULL, NULL, key_cache, value_cache, block_tables,
+                      max_num_blocks_per_seq, context_lens, max_context_len,
+                      NULL, NULL, 0, num_seqs, num_heads,
+                      num_kv_heads, head_size, block_size, num_blocks, (double)scale };
+    return run_units(&a, out, units, num_units, nthreads);
+}
+
+/* bf16 baseline decode of every (seq, head): out is [num_seqs, num_heads, head_size]. */
+int q8o_bf16_paged_decode(float* out, const float* q, uint32_t q_stride,
+                          const uint16_t* key_cache, const uint16_t* value_cache,
+                          const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                          const uint32_t* context_lens, uint32_t max_context_len,
+                          uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                          uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                          float scale, int nthreads)
+{
+    uint64_t nu;
+    uint32_t* units = all_units(num_seqs, num_heads, &nu);
+    if (!units) return Q8O_ERR_NOMEM;
+    int rc = q8o_bf16_paged_decode_units(out, units, (uint32_t)nu, q, q_stride, key_cache,
+                                         value_cache, block_tables, max_num_blocks_per_seq,
+                                         context_lens, max_context_len, num_seqs, num_heads,
+                                         num_kv_heads, head_size, block_size, num_blocks,
+                                         scale, nthreads);
     free(units);
     return rc;
 }

@@ -39,7 +39,7 @@ static int quant_cases(void)
     return 0;
 }
 
-/* an int8 and an f32 cache over the same random rows, decoded densely, clamped and through visible lists */
+/* int8, f32 and bf16 caches over the same random rows, decoded densely, clamped and through visible lists */
 static int decode_cases(uint32_t bs)
 {
     const uint32_t S = 3, H = 6, Hkv = 3, hs = 12, wpt = hs / 4 + 1;
@@ -53,7 +53,9 @@ static int decode_cases(uint32_t bs)
     const size_t words = (size_t)nb * Hkv * bs * wpt, floats = (size_t)nb * Hkv * bs * hs;
     uint32_t* kc = xalloc(words * 4); uint32_t* vc = xalloc(words * 4);
     float* kf = xalloc(floats * 4); float* vf = xalloc(floats * 4);
+    uint16_t* kb = xalloc(floats * 2); uint16_t* vb = xalloc(floats * 2);
     memset(kc, 0, words * 4); memset(vc, 0, words * 4); memset(kf, 0, floats * 4); memset(vf, 0, floats * 4);
+    memset(kb, 0, floats * 2); memset(vb, 0, floats * 2);
     for (uint32_t s = 0; s < S; ++s) {
         const uint32_t L = lens[s];
         if (!L) continue;
@@ -63,6 +65,7 @@ static int decode_cases(uint32_t bs)
         slots[L - 1] = L > 1 ? slots[L - 1] : slots[0];
         CHECK(q8o_cache_write(k, Hkv * hs, v, Hkv * hs, kc, vc, slots, L, Hkv, hs, bs, nb));
         CHECK(q8o_f32_cache_write(k, Hkv * hs, v, Hkv * hs, kf, vf, slots, L, Hkv, hs, bs, nb));
+        CHECK(q8o_bf16_cache_write(k, Hkv * hs, v, Hkv * hs, kb, vb, slots, L, Hkv, hs, bs, nb));
         free(k); free(v); free(slots);
     }
     {   /* a pad token among the writes */
@@ -78,6 +81,7 @@ static int decode_cases(uint32_t bs)
     CHECK(q8o_paged_decode(out, q, H * hs, kc, vc, bt, max_nb, lens, 4, NULL, NULL, 0, S, H, Hkv, hs, bs, nb,
                            0.25f, 2));
     CHECK(q8o_f32_paged_decode(out, q, H * hs, kf, vf, bt, max_nb, lens, 15, S, H, Hkv, hs, bs, nb, 0.25f, 1));
+    CHECK(q8o_bf16_paged_decode(out, q, H * hs, kb, vb, bt, max_nb, lens, 15, S, H, Hkv, hs, bs, nb, 0.25f, 2));
     {
         const uint32_t vs = 15;
         uint32_t* vis = xalloc((size_t)S * vs * sizeof(uint32_t));
@@ -91,7 +95,7 @@ static int decode_cases(uint32_t bs)
                                0.25f, 1));
         free(vis);
     }
-    free(bt); free(kc); free(vc); free(kf); free(vf); free(q); free(out);
+    free(bt); free(kc); free(vc); free(kf); free(vf); free(kb); free(vb); free(q); free(out);
     return 0;
 }
 
