@@ -19,7 +19,7 @@ word of every attended row, K and V) as GB/s, its fraction of the 8 TB/s HBM
 peak, decode (seq, head)/s, the roofline entry of the step's kernel, and the
 CPU oracle on the same workload (all cores of this process's share and one
 thread).  Beside it (skipped with --no-reference): the same step as two
-launches; 4-row causal decode; the f32-cache step; the norm + rotary step; the
+launches; 4-row causal decode; the f32- and bf16-cache steps; the norm + rotary step; the
 selected-token step; the long-context and MHA head_size=256 decodes and the
 padded 4096-token write; and the practical HBM ceiling (a streaming read and
 the step's own tiles read without arithmetic, libq8kv_bench.so).
@@ -413,7 +413,9 @@ def main():
     import torch
     from int8_paged_kv_amd import (q8_cache_write, q8_decode_step, q8_paged_decode, q8_paged_decode_rows,
                                    q8_paged_decode_workspace_bytes, q8_f32_cache_write, q8_f32_paged_decode,
-                                   q8_f32_paged_decode_workspace_bytes, q8_rope_table, q8_norm_rope,
+                                   q8_f32_paged_decode_workspace_bytes, q8_bf16_cache_write,
+                                   q8_bf16_paged_decode, q8_bf16_paged_decode_workspace_bytes,
+                                   q8_rope_table, q8_norm_rope,
                                    q8_norm_rope_cache_write, q8_norm_rope_qk_cache_write,
                                    q8_norm_rope_decode_step, q8_index_select, load_library)
     from int8_paged_kv_amd import workloads as wl
@@ -549,54 +551,61 @@ def main():
                          "for all its rows; per_row_rate counts every row's prefix separately (the rows share "
                          "the reads), so it is not a bandwidth"}
 
-    # ---- the same step over an f32 paged cache (4 bytes per element, no scale word) ----
-    f32ref = None
-    if not args.no_reference:
+    # ---- the same step over f32 and bfloat16 paged caches (no scale word) ----
+    def baseline_reference(kind, write_fn, decode_fn, ws_fn, dtype, poison, elem_bytes):
         nbt = w.num_blocks + 1          # the workload's caches carry one reserved block
-        f32_layers = []
-        for li in range(2):             # 2.6 GB per layer: a step's 1.27 GB of f32 KV already exceeds the MALL
-            kf = torch.full((nbt, Hkv, w.block_size, hs), float("nan"), dtype=torch.float32, device=dev)
-            vf = torch.full_like(kf, float("nan"))
-            f32_layers.append((kf, vf))
+        layers = []
+        for li in range(2):             # a step reads 0.63 GB (bf16) or 1.27 GB (f32): both above the MALL
+            kf = torch.full((nbt, Hkv, w.block_size, hs), poison, dtype=dtype, device=dev)
+            vf = torch.full_like(kf, poison)
+            layers.append((kf, vf))
         for slots, k, v in fill_host:
             sl, kd, vd = u32(slots), f32(k), f32(v)
-            for kf, vf in f32_layers:
-                q8_f32_cache_write(kd, vd, kf, vf, sl, Hkv, hs, w.block_size)
-        wsf = torch.zeros(max(16, q8_f32_paged_decode_workspace_bytes(S, H, Hkv, hs)), dtype=torch.uint8, device=dev)
+            for kf, vf in layers:
+                write_fn(kd, vd, kf, vf, sl, Hkv, hs, w.block_size)
+        wsf = torch.zeros(max(16, ws_fn(S, H, Hkv, hs)), dtype=torch.uint8, device=dev)
         outf = torch.empty((S, H, hs), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
-        def f32_step(i, ev=None):
-            kf, vf = f32_layers[i % len(f32_layers)]
+        def ref_step(i, ev=None):
+            kf, vf = layers[i % len(layers)]
             if ev is not None:
                 ev[0].record()
-            q8_f32_cache_write(sk, sv, kf, vf, ss, Hkv, hs, w.block_size)
+            write_fn(sk, sv, kf, vf, ss, Hkv, hs, w.block_size)
             if ev is not None:
                 ev[1].record()
-            q8_f32_paged_decode(q, kf, vf, bt, cl, w.scale, Hkv, w.block_size, max_context_len=mcl,
-                                out=outf, workspace=wsf)
+            decode_fn(q, kf, vf, bt, cl, w.scale, Hkv, w.block_size, max_context_len=mcl, out=outf, workspace=wsf)
             if ev is not None:
                 ev[2].record()
 
         for i in range(5):
-            f32_step(i)
+            ref_step(i)
         torch.cuda.synchronize()
         nf = min(100, max(20, args.steps // 4))
         evf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nf)]
         for i in range(nf):
-            f32_step(i, evf[i])
+            ref_step(i, evf[i])
         torch.cuda.synchronize()
         tfw = np.array([e[0].elapsed_time(e[1]) for e in evf]) * 1e3
         tfd = np.array([e[1].elapsed_time(e[2]) for e in evf]) * 1e3
-        Bf = int(w.attended_counts().sum()) * Hkv * 2 * hs * 4
-        f32ref = {"cache_write_us_mean": round(float(tfw.mean()), 2),
-                  "decode_us_mean": round(float(tfd.mean()), 2),
-                  "f32_kv_bytes": Bf,
-                  "decode_f32_kv_GBps": round(Bf / (float(tfd.mean()) * 1e-6) / 1e9, 1),
-                  "int8_step_speedup": round(float(tfw.mean() + tfd.mean()) / float(t_dec.mean()), 3),
-                  "note": "q8_f32_cache_write + q8_f32_paged_decode of the same step over an f32 cache "
-                          "[num_blocks, Hkv, bs, hs]; speedup = f32 step time / int8 one-launch step time"}
-        del f32_layers
+        Bf = int(w.attended_counts().sum()) * Hkv * 2 * hs * elem_bytes
+        del layers
+        return {"cache_write_us_mean": round(float(tfw.mean()), 2),
+                "decode_us_mean": round(float(tfd.mean()), 2),
+                "%s_kv_bytes" % kind: Bf,
+                "decode_%s_kv_GBps" % kind: round(Bf / (float(tfd.mean()) * 1e-6) / 1e9, 1),
+                "decode_frac_hbm_peak": round(Bf / (float(tfd.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "int8_step_speedup": round(float(tfw.mean() + tfd.mean()) / float(t_dec.mean()), 3),
+                "note": "q8_%s_cache_write + q8_%s_paged_decode of the same step over a %s cache "
+                        "[num_blocks, Hkv, bs, hs]; speedup = %s step time / int8 one-launch step time"
+                        % (kind, kind, kind, kind)}
+
+    f32ref = bf16ref = None
+    if not args.no_reference:
+        f32ref = baseline_reference("f32", q8_f32_cache_write, q8_f32_paged_decode,
+                                    q8_f32_paged_decode_workspace_bytes, torch.float32, float("nan"), 4)
+        bf16ref = baseline_reference("bf16", q8_bf16_cache_write, q8_bf16_paged_decode,
+                                     q8_bf16_paged_decode_workspace_bytes, torch.bfloat16, float("nan"), 2)
 
     # ---- per-head RMSNorm + partial rotary step ahead of the write (rot = head_size/2) ----
     normrope = None
@@ -879,6 +888,7 @@ def main():
         "two_launch_reference": reference,
         "multi_row_decode": multi,
         "f32_cache_reference": f32ref,
+        "bf16_cache_reference": bf16ref,
         "norm_rope_step": normrope,
         "selected_step": selected,
         "long_context": long_leg,

@@ -342,6 +342,39 @@ q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
                               void* stream);
 
 /*
+ * bfloat16 paged-cache baseline (not on the pages: the half-width cache most
+ * serving stacks keep, so the int8 cache can be measured against it too).
+ * Layout as the f32 baseline with 2-byte elements: a u16 buffer
+ * [num_blocks, num_kv_heads, block_size, head_size] for K and one for V, each
+ * element the bfloat16 encoding (the upper 16 bits of a binary32).
+ *
+ * q8_bf16_cache_write -- q8_f32_cache_write with every element rounded to the
+ * nearest bfloat16, ties to the even encoding (inputs finite).  Errors: those
+ * of q8_f32_cache_write, plus Q8_ERR_UNSUPPORTED when head_size is not a
+ * multiple of 8 (rows are written in 16-byte units of 8 elements).
+ *
+ * q8_bf16_paged_decode_workspace_bytes, q8_bf16_paged_decode -- as the f32
+ * calls, over the bfloat16 caches (each element widened to f32 exactly); the
+ * arguments, workspace rules and errors are the same.
+ */
+q8_status q8_bf16_cache_write(const float* key, uint32_t key_stride,
+                              const float* value, uint32_t value_stride,
+                              uint16_t* key_cache, uint16_t* value_cache,
+                              const uint32_t* slot_mapping, uint32_t num_tokens,
+                              uint32_t num_kv_heads, uint32_t head_size,
+                              uint32_t block_size, uint32_t num_blocks, void* stream);
+size_t q8_bf16_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
+                                            uint32_t num_kv_heads, uint32_t head_size);
+q8_status q8_bf16_paged_decode(float* out, const float* q, uint32_t q_stride,
+                               const uint16_t* key_cache, const uint16_t* value_cache,
+                               const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                               const uint32_t* context_lens, uint32_t max_context_len,
+                               uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                               uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Per-head RMSNorm + partial rotary embedding.  The "attention.rs" page
  * normalizes q and k per head with a learned weight (rms eps) and rotates
  * the first rot = head_dim * partial_rotary_factor elements at the row's

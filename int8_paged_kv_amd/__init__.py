@@ -13,8 +13,9 @@ Operations behind the C ABI of libq8kv.so (include/q8kv.h):
   sequence's new token appended at its last position, then attended).
 * ``q8_paged_decode_rows``: multi-row causal decode (several query rows per
   sequence at its last positions, each over its causal prefix).
-* ``q8_f32_cache_write`` / ``q8_f32_paged_decode``: the same write and decode
-  over an f32 paged cache, the baseline the int8 cache is measured against.
+* ``q8_f32_cache_write`` / ``q8_f32_paged_decode`` and ``q8_bf16_cache_write`` /
+  ``q8_bf16_paged_decode``: the same write and decode over f32 and bfloat16 paged
+  caches, the baselines the int8 cache is measured against.
 * ``q8_rope_table``, ``q8_norm_rope``, ``q8_norm_rope_cache_write``: per-head
   RMSNorm + partial rotary embedding of q rows, and fused ahead of the K
   quantizer in the cache write (the q/k norm-and-rope step of "attention.rs");
@@ -30,7 +31,8 @@ be imported on a machine without the library or a GPU.
 
 __all__ = ["q8_cache_write", "q8_paged_decode", "q8_paged_decode_noalloc", "q8_decode_step", "q8_paged_decode_rows",
            "q8_paged_decode_workspace_bytes", "q8_f32_cache_write", "q8_f32_paged_decode",
-           "q8_f32_paged_decode_workspace_bytes", "q8_rope_table", "q8_norm_rope", "q8_norm_rope_cache_write",
+           "q8_f32_paged_decode_workspace_bytes", "q8_bf16_cache_write", "q8_bf16_paged_decode",
+           "q8_bf16_paged_decode_workspace_bytes", "q8_rope_table", "q8_norm_rope", "q8_norm_rope_cache_write",
            "q8_norm_rope_qk_cache_write", "q8_norm_rope_decode_step", "q8_index_select",
            "load_library", "load_debug_library", "use_library", "bounds_flags", "Q8Error", "PAD_SLOT"]
 

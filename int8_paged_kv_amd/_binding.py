@@ -95,6 +95,12 @@ def _open(path: str) -> ctypes.CDLL:
     lib.q8_f32_paged_decode.argtypes = [P, P, U, P, P, P, U, P, U,
                                         U, U, U, U, U, U, ctypes.c_float, P, ctypes.c_size_t, P]
     lib.q8_f32_paged_decode.restype = ctypes.c_int
+    lib.q8_bf16_cache_write.argtypes = [P, U, P, U, P, P, P, U, U, U, U, U, P]
+    lib.q8_bf16_cache_write.restype = ctypes.c_int
+    lib.q8_bf16_paged_decode_workspace_bytes.argtypes = [U, U, U, U]
+    lib.q8_bf16_paged_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.q8_bf16_paged_decode.argtypes = lib.q8_f32_paged_decode.argtypes
+    lib.q8_bf16_paged_decode.restype = ctypes.c_int
     F = ctypes.c_float
     lib.q8_rope_table.argtypes = [P, U, U, F, P]
     lib.q8_rope_table.restype = ctypes.c_int
@@ -464,6 +470,67 @@ def q8_f32_paged_decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: t
                                  _u32(context_lens, "context_lens"), max_context_len, S, H, num_kv_heads, hs,
                                  block_size, num_blocks, float(scale), wp, wb, _stream(stream))
     _check(st, "q8_f32_paged_decode")
+    return out
+
+
+def _bf16(t: torch.Tensor, name: str) -> int:
+    """bfloat16 caches travel as torch.bfloat16 or int16 tensors (the same bits)."""
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype not in (torch.bfloat16, torch.int16):
+        raise ValueError("%s must be bfloat16 (or int16 holding bfloat16 bits), got %s" % (name, t.dtype))
+    return t.data_ptr()
+
+
+def q8_bf16_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                        value_cache: torch.Tensor, slot_mapping: torch.Tensor, num_kv_heads: int,
+                        head_size: int, block_size: int, num_blocks: Optional[int] = None, stream=None) -> None:
+    """Round K/V rows to bfloat16 (nearest, ties to even) into the bf16 paged caches
+    [num_blocks, Hkv, block_size, head_size] (baseline)."""
+    lib = load_library()
+    kp, ks = _rows(key, "key")
+    vp, vs = _rows(value, "value")
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * head_size)
+    st = lib.q8_bf16_cache_write(kp, ks, vp, vs, _bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache"),
+                                 _u32(slot_mapping, "slot_mapping"), slot_mapping.numel(), num_kv_heads,
+                                 head_size, block_size, num_blocks, _stream(stream))
+    _check(st, "q8_bf16_cache_write")
+
+
+def q8_bf16_paged_decode_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int) -> int:
+    return int(load_library().q8_bf16_paged_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size))
+
+
+def q8_bf16_paged_decode(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                         num_kv_heads: int, block_size: int, max_context_len: Optional[int] = None,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         num_blocks: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Single-query decode over the bf16 paged caches (baseline); arguments as q8_f32_paged_decode."""
+    lib = load_library()
+    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [num_seqs, num_heads, head_size] with dense heads")
+    S, H, hs = q.shape
+    if out is None:
+        out = torch.empty((S, H, hs), dtype=torch.float32, device=q.device)
+    if not out.is_contiguous() or tuple(out.shape) != (S, H, hs):
+        raise ValueError("out must be a dense [num_seqs, num_heads, head_size] tensor")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if context_lens.numel() else 0
+    if num_blocks is None:
+        num_blocks = key_cache.numel() // max(1, num_kv_heads * block_size * hs)
+    need = lib.q8_bf16_paged_decode_workspace_bytes(S, H, num_kv_heads, hs)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)   # zero before first use
+    wp = workspace.data_ptr()
+    wb = workspace.numel() * workspace.element_size()
+    st = lib.q8_bf16_paged_decode(_dev(out, "out", torch.float32), _dev(q, "q", torch.float32), q.stride(0),
+                                  _bf16(key_cache, "key_cache"), _bf16(value_cache, "value_cache"),
+                                  _u32(block_tables, "block_tables"), block_tables.shape[-1],
+                                  _u32(context_lens, "context_lens"), max_context_len, S, H, num_kv_heads, hs,
+                                  block_size, num_blocks, float(scale), wp, wb, _stream(stream))
+    _check(st, "q8_bf16_paged_decode")
     return out
 
 

@@ -362,24 +362,29 @@ q8_status q8_norm_rope_decode_step(float* out, const float* q, uint32_t q_stride
                          stream, &app, 1, false, &nr, q_head_stride);
 }
 
-q8_status q8_f32_cache_write(const float* key, uint32_t key_stride,
-                             const float* value, uint32_t value_stride,
-                             float* key_cache, float* value_cache,
-                             const uint32_t* slot_mapping, uint32_t num_tokens,
-                             uint32_t num_kv_heads, uint32_t head_size,
-                             uint32_t block_size, uint32_t num_blocks, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Writers and decodes of the full-width baseline caches: elem_bytes 4 (f32)
+// or 2 (bfloat16).
+q8_status baseline_write(const float* key, uint32_t key_stride, const float* value, uint32_t value_stride,
+                         void* key_cache, void* value_cache, const uint32_t* slot_mapping, uint32_t num_tokens,
+                         uint32_t num_kv_heads, uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                         uint32_t elem_bytes, void* stream) {
     if (!head_size_ok(head_size) || block_size == 0 || num_kv_heads == 0 || num_blocks == 0) return Q8_ERR_SHAPE;
     const uint64_t row = static_cast<uint64_t>(num_kv_heads) * head_size;
     if (key_stride < row || value_stride < row) return Q8_ERR_SHAPE;
     if (num_tokens == 0) return Q8_OK;
     if (!key || !value || !key_cache || !value_cache || !slot_mapping) return Q8_ERR_NULL;
-    // one thread per 16-byte piece of a (token, kv head) row, 256 per workgroup
-    if ((static_cast<uint64_t>(num_tokens) * num_kv_heads * (head_size / 4) + 255) / 256 > q8kv::kMaxGridBlocks)
+    // one thread per 16-byte unit of a (token, kv head) row, 256 per workgroup
+    const uint32_t epl = 16 / elem_bytes;
+    if ((static_cast<uint64_t>(num_tokens) * num_kv_heads * (head_size / epl) + 255) / 256 > q8kv::kMaxGridBlocks)
         return Q8_ERR_SHAPE;
+    if (head_size % epl != 0) return Q8_ERR_UNSUPPORTED;      // bfloat16 rows are written in units of 8
     if (reinterpret_cast<uintptr_t>(key_cache) % 16 != 0 || reinterpret_cast<uintptr_t>(value_cache) % 16 != 0)
         return Q8_ERR_UNSUPPORTED;
-    if (static_cast<uint64_t>(num_tokens) * row / 4 > 0xFFFFFFFFull * 256) return Q8_ERR_UNSUPPORTED;
-    q8kv::F32CacheWriteArgs a{};
+    q8kv::BaselineWriteArgs a{};
     a.key = key;
     a.value = value;
     a.key_cache = key_cache;
@@ -392,24 +397,22 @@ q8_status q8_f32_cache_write(const float* key, uint32_t key_stride,
     a.head_size = head_size;
     a.block_size = block_size;
     a.num_blocks = num_blocks;
-    const hipError_t e = q8kv::launch_f32_cache_write(a, static_cast<hipStream_t>(stream));
+    a.elem_bytes = elem_bytes;
+    const hipError_t e = q8kv::launch_baseline_write(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
 }
 
-size_t q8_f32_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
-                                           uint32_t num_kv_heads, uint32_t head_size) {
+size_t baseline_workspace_bytes(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads, uint32_t head_size) {
     if (num_kv_heads == 0 || num_heads == 0 || num_heads % num_kv_heads != 0) return 0;
-    return q8kv::plan_f32_decode(num_seqs, num_heads, num_kv_heads, head_size).bytes;
+    return q8kv::plan_baseline_decode(num_seqs, num_heads, num_kv_heads, head_size).bytes;
 }
 
-q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
-                              const float* key_cache, const float* value_cache,
-                              const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
-                              const uint32_t* context_lens, uint32_t max_context_len,
-                              uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
-                              uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
-                              float scale, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+q8_status baseline_decode(float* out, const float* q, uint32_t q_stride, const void* key_cache,
+                          const void* value_cache, const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                          const uint32_t* context_lens, uint32_t max_context_len, uint32_t num_seqs,
+                          uint32_t num_heads, uint32_t num_kv_heads, uint32_t head_size, uint32_t block_size,
+                          uint32_t num_blocks, float scale, void* workspace, size_t workspace_bytes,
+                          uint32_t elem_bytes, void* stream) {
     if (!head_size_ok(head_size) || block_size == 0 || num_heads == 0 || num_kv_heads == 0 ||
         num_heads % num_kv_heads != 0)
         return Q8_ERR_SHAPE;
@@ -421,14 +424,13 @@ q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
     if (max_context_len >= 0x80000000u || q_stride % 4 != 0) return Q8_ERR_UNSUPPORTED;
     if (num_seqs == 0) return Q8_OK;
     if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens) return Q8_ERR_NULL;
-    for (const void* p : {static_cast<const void*>(out), static_cast<const void*>(q),
-                          static_cast<const void*>(key_cache), static_cast<const void*>(value_cache)})
+    for (const void* p : {static_cast<const void*>(out), static_cast<const void*>(q), key_cache, value_cache})
         if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return Q8_ERR_UNSUPPORTED;
-    const q8kv::F32DecodePlan p = q8kv::plan_f32_decode(num_seqs, num_heads, num_kv_heads, head_size);
+    const q8kv::BaselineDecodePlan p = q8kv::plan_baseline_decode(num_seqs, num_heads, num_kv_heads, head_size);
     if (p.num_waves > 0x7FFFFFFFull || p.recs_per_rg > 0x7FFFFFFFull) return Q8_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < p.bytes || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
         return Q8_ERR_WORKSPACE;
-    q8kv::F32DecodeArgs a{};
+    q8kv::BaselineDecodeArgs a{};
     a.out = out;
     a.q = q;
     a.key_cache = key_cache;
@@ -452,10 +454,71 @@ q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
     a.num_groups = p.num_groups;
     a.waves_per_rg = p.waves_per_rg;
     a.recs_per_rg = static_cast<uint32_t>(p.recs_per_rg);
+    a.elem_bytes = elem_bytes;
     a.inv_block_size = 1.0f / static_cast<float>(block_size);
     a.scale_log2 = scale * 1.4426950408889634f;
-    const hipError_t e = q8kv::launch_f32_decode(a, p, static_cast<hipStream_t>(stream));
+    const hipError_t e = q8kv::launch_baseline_decode(a, p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+q8_status q8_f32_cache_write(const float* key, uint32_t key_stride,
+                             const float* value, uint32_t value_stride,
+                             float* key_cache, float* value_cache,
+                             const uint32_t* slot_mapping, uint32_t num_tokens,
+                             uint32_t num_kv_heads, uint32_t head_size,
+                             uint32_t block_size, uint32_t num_blocks, void* stream) {
+    return baseline_write(key, key_stride, value, value_stride, key_cache, value_cache, slot_mapping, num_tokens,
+                          num_kv_heads, head_size, block_size, num_blocks, 4, stream);
+}
+
+size_t q8_f32_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
+                                           uint32_t num_kv_heads, uint32_t head_size) {
+    return baseline_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size);
+}
+
+q8_status q8_f32_paged_decode(float* out, const float* q, uint32_t q_stride,
+                              const float* key_cache, const float* value_cache,
+                              const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                              const uint32_t* context_lens, uint32_t max_context_len,
+                              uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                              uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                              float scale, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    return baseline_decode(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
+                           context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                           num_blocks, scale, workspace, workspace_bytes, 4, stream);
+}
+
+q8_status q8_bf16_cache_write(const float* key, uint32_t key_stride,
+                              const float* value, uint32_t value_stride,
+                              uint16_t* key_cache, uint16_t* value_cache,
+                              const uint32_t* slot_mapping, uint32_t num_tokens,
+                              uint32_t num_kv_heads, uint32_t head_size,
+                              uint32_t block_size, uint32_t num_blocks, void* stream) {
+    return baseline_write(key, key_stride, value, value_stride, key_cache, value_cache, slot_mapping, num_tokens,
+                          num_kv_heads, head_size, block_size, num_blocks, 2, stream);
+}
+
+size_t q8_bf16_paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_heads,
+                                            uint32_t num_kv_heads, uint32_t head_size) {
+    return baseline_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size);
+}
+
+q8_status q8_bf16_paged_decode(float* out, const float* q, uint32_t q_stride,
+                               const uint16_t* key_cache, const uint16_t* value_cache,
+                               const uint32_t* block_tables, uint32_t max_num_blocks_per_seq,
+                               const uint32_t* context_lens, uint32_t max_context_len,
+                               uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                               uint32_t head_size, uint32_t block_size, uint32_t num_blocks,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return baseline_decode(out, q, q_stride, key_cache, value_cache, block_tables, max_num_blocks_per_seq,
+                           context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                           num_blocks, scale, workspace, workspace_bytes, 2, stream);
 }
 
 q8_status q8_rope_table(float* table, uint32_t num_positions, uint32_t rot, float theta, void* stream) {

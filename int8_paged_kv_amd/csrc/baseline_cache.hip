@@ -1,4 +1,5 @@
-// f32 paged-cache baseline: cache writer and single-query decode.
+// Full-width paged-cache baselines (f32 and bfloat16): cache writer and
+// single-query decode.
 //
 // The "paged_attn_q8.comp" page's header says the int8 decode keeps the math
 // and workgroup structure of an f32 paged decode whose cache holds 4 bytes per
@@ -6,18 +7,23 @@
 // "reshape_and_cache_q8.comp" page's header says its pad-slot rule mirrors the
 // f32 writer.  The f32 layout is not printed there; it is taken to be the int8
 // layout with one f32 per element: [num_blocks, num_kv_heads, block_size,
-// head_size].  These kernels serve to measure the int8 cache against the f32
-// one on the same batch.
+// head_size].  The bfloat16 cache (not on the pages; the half-width cache most
+// serving stacks keep) is the same layout with 2-byte elements, each the
+// nearest bfloat16 to the f32 input (ties to even).  These kernels serve to
+// measure the int8 cache against both on the same batch.
 //
-// Decode, MI355X mapping.  The work is a pure stream of f32 rows with about
-// one multiply-add per byte, far below the VALU rate, so it stays on the VALU
+// Decode, MI355X mapping.  The work is a pure stream of rows with about one
+// multiply-add per element, far below the VALU rate, so it stays on the VALU
 // and is laid out for the loads:
-//   * A row of head_size f32 is read by LPT = head_size/4 lanes with 16-byte
-//     loads; one load instruction covers 64/LPT consecutive positions, and a
-//     chunk is 8 such loads per tensor (8 KiB of K and 8 KiB of V per wave),
-//     fetched into registers one chunk ahead, the block ids two chunks ahead.
+//   * A row of head_size elements is read by LPT lanes with 16-byte loads of
+//     EPL elements (4 f32 or 8 bfloat16, widened to f32 on use), LPT =
+//     head_size/EPL; one load instruction covers 64/LPT consecutive
+//     positions, and a chunk is 8 such loads per tensor (8 KiB of K and 8 KiB
+//     of V per wave; 4 loads for bfloat16, whose q slices and accumulators
+//     take twice the registers), fetched into registers one chunk ahead, the
+//     block ids two chunks ahead.
 //   * A wave handles one row group: a kv head and G = 4, 2 or 1 of its query
-//     heads, whose q slices stay in registers.  q.k is a 4-element partial
+//     heads, whose q slices stay in registers.  q.k is an EPL-element partial
 //     per lane, summed over the row's LPT lanes with DPP and a swizzle; the
 //     softmax runs in the exp2 domain with the running max uniform over the
 //     wave and the running sum and output kept per lane group until the end
@@ -31,6 +37,7 @@
 #include "wave_ops.h"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace q8kv {
 namespace {
@@ -67,6 +74,7 @@ __device__ __forceinline__ float group_sum(float v) {
 // the groups, uniform over the wave.
 template <int LPT>
 __device__ __forceinline__ float groups_max(float v) {
+    if (LPT <= 2) v = fmaxf(v, dpp_mov<kRowRor2>(v));
     if (LPT <= 4) v = fmaxf(v, dpp_mov<kRowRor4>(v));
     if (LPT <= 8) v = fmaxf(v, dpp_mov<kRowRor8>(v));
     if (LPT >= 64) return readlane_f(v, 0);
@@ -78,6 +86,7 @@ __device__ __forceinline__ float groups_max(float v) {
 // group: lane i receives sum_g v[g*LPT + i % LPT].
 template <int LPT>
 __device__ __forceinline__ float groups_sum(float v) {
+    if (LPT <= 2) v += dpp_mov<kRowRor2>(v);
     if (LPT <= 4) v += dpp_mov<kRowRor4>(v);
     if (LPT <= 8) v += dpp_mov<kRowRor8>(v);
     if (LPT <= 16) v += swizzle_xor16(v);
@@ -87,7 +96,6 @@ __device__ __forceinline__ float groups_sum(float v) {
 
 __device__ __forceinline__ float4 f4_zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));   // vector type the nontemporal builtins accept
 
 // Device-coherent (agent scope) element accesses for the partial records
 // handed between waves that may run on different XCDs; they compile to sc1
@@ -102,40 +110,86 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 
 // ---------------------------------------------------------------- writer ----
 
-__global__ __launch_bounds__(256) void f32_cache_write_kernel(F32CacheWriteArgs a, bool vec4) {
-    const uint32_t hs4 = a.head_size / 4;
+// Element type of a cache: E = float (4 per 16-byte unit) or uint16_t holding
+// a bfloat16 (8 per unit).
+template <typename E>
+constexpr int epl() { return 16 / static_cast<int>(sizeof(E)); }
+
+// The bfloat16 nearest to finite x, ties to even, as its 16 bits: adding
+// 0x7FFF plus the lowest kept bit carries into the upper half exactly when the
+// dropped half is above half an ulp, or exactly half with an odd kept part.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) { return bf16_bits(lo) | (bf16_bits(hi) << 16); }
+
+__device__ __forceinline__ float4 load_f4(const float* p, bool vec4) {
+    return vec4 ? *reinterpret_cast<const float4*>(p) : make_float4(p[0], p[1], p[2], p[3]);
+}
+
+// One thread per 16-byte unit of a (token, kv head) row of the cache.
+template <typename E>
+__global__ __launch_bounds__(256) void baseline_write_kernel(BaselineWriteArgs a, bool vec4) {
+    constexpr int EPL = epl<E>();
+    const uint32_t units = a.head_size / EPL;
     const uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads * hs4) return;
-    const uint32_t w = static_cast<uint32_t>(i % hs4);
-    const uint64_t th = i / hs4;
+    if (i >= static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads * units) return;
+    const uint32_t w = static_cast<uint32_t>(i % units);
+    const uint64_t th = i / units;
     const uint32_t h = static_cast<uint32_t>(th % a.num_kv_heads);
     const uint32_t t = static_cast<uint32_t>(th / a.num_kv_heads);
     const uint32_t slot = a.slot_mapping[t];
     if (slot == kPadSlot) return;
     const uint64_t block = slot / a.block_size, off = slot % a.block_size;
     if (block >= a.num_blocks) return;   // out of contract; skipped rather than written out of bounds
-    const float* ks = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size + 4 * w;
-    const float* vs = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size + 4 * w;
-    const float4 k = vec4 ? *reinterpret_cast<const float4*>(ks) : make_float4(ks[0], ks[1], ks[2], ks[3]);
-    const float4 v = vec4 ? *reinterpret_cast<const float4*>(vs) : make_float4(vs[0], vs[1], vs[2], vs[3]);
-    const uint64_t dst = ((block * a.num_kv_heads + h) * a.block_size + off) * a.head_size + 4 * w;
-    *reinterpret_cast<float4*>(a.key_cache + dst) = k;
-    *reinterpret_cast<float4*>(a.value_cache + dst) = v;
+    const float* ks = a.key + static_cast<uint64_t>(t) * a.key_stride + static_cast<uint64_t>(h) * a.head_size + EPL * w;
+    const float* vs = a.value + static_cast<uint64_t>(t) * a.value_stride + static_cast<uint64_t>(h) * a.head_size + EPL * w;
+    const uint64_t dst = ((block * a.num_kv_heads + h) * a.block_size + off) * a.head_size + EPL * w;
+    if constexpr (EPL == 4) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.key_cache) + dst) = load_f4(ks, vec4);
+        *reinterpret_cast<float4*>(static_cast<float*>(a.value_cache) + dst) = load_f4(vs, vec4);
+    } else {
+        const float4 k0 = load_f4(ks, vec4), k1 = load_f4(ks + 4, vec4);
+        const float4 v0 = load_f4(vs, vec4), v1 = load_f4(vs + 4, vec4);
+        *reinterpret_cast<uint4*>(static_cast<E*>(a.key_cache) + dst) =
+            make_uint4(bf16_pair(k0.x, k0.y), bf16_pair(k0.z, k0.w), bf16_pair(k1.x, k1.y), bf16_pair(k1.z, k1.w));
+        *reinterpret_cast<uint4*>(static_cast<E*>(a.value_cache) + dst) =
+            make_uint4(bf16_pair(v0.x, v0.y), bf16_pair(v0.z, v0.w), bf16_pair(v1.x, v1.y), bf16_pair(v1.z, v1.w));
+    }
 }
 
 // ---------------------------------------------------------------- decode ----
 
 // Positions of sequence s (the context clamp applied).
-__device__ __forceinline__ uint32_t f32_positions(const F32DecodeArgs& a, uint32_t s) {
+__device__ __forceinline__ uint32_t f32_positions(const BaselineDecodeArgs& a, uint32_t s) {
     const uint32_t L = a.context_lens[s];
     return L < a.max_context_len ? L : a.max_context_len;
 }
 
-template <int LPT, int G>
-__global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
+// A 16-byte unit of a cache row as loaded: four f32, or eight bfloat16 as
+// four words.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+template <typename E>
+using unit_t = typename std::conditional<epl<E>() == 4, f32x4, u32x4v>::type;
+
+// Element e of a unit, as f32 (a bfloat16 is the upper half of its binary32
+// encoding, so widening is exact).
+__device__ __forceinline__ float unit_elem(const f32x4& w, int e) { return w[e]; }
+__device__ __forceinline__ float unit_elem(const u32x4v& w, int e) {
+    return __uint_as_float((e & 1) ? (w[e / 2] & 0xFFFF0000u) : (w[e / 2] << 16));
+}
+
+template <typename E, int LPT, int G>
+__global__ __launch_bounds__(256, 2) void baseline_decode_kernel(BaselineDecodeArgs a) {
+    constexpr int EPL = epl<E>();                       // elements per 16-byte unit
+    // 16-byte loads per lane and tensor per chunk: 8, or 4 for bfloat16,
+    // whose q slices and accumulators take twice the registers
+    constexpr int NL = EPL == 4 ? kLoadsPerChunk : kLoadsPerChunk / 2;
     constexpr int TPI = kWave / LPT;                    // positions per load instruction
-    constexpr uint32_t T = kLoadsPerChunk * TPI;        // positions per chunk
-    constexpr uint32_t HS = 4 * LPT;
+    constexpr uint32_t T = NL * TPI;                    // positions per chunk
+    constexpr uint32_t HS = EPL * LPT;
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t wid = uniform(blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave);
     // Row group fastest: the groups of one kv head, which read the same rows,
@@ -150,6 +204,14 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
     const uint32_t S = a.num_seqs;
     const uint32_t col = lane % LPT, grp_l = lane / LPT;
 
+    // EPL floats of an output row, from lane group column c
+    auto store_out = [&](uint64_t row, uint32_t c, const float (&x)[EPL]) {
+#pragma unroll
+        for (int u = 0; u < EPL / 4; ++u)
+            *reinterpret_cast<float4*>(a.out + row * HS + EPL * c + 4 * u) =
+                make_float4(x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]);
+    };
+
     // ---- chunk count C of the row group; empty sequences s = j (mod W) get zero rows ----
     uint32_t C = 0;
     for (uint32_t base = 0; base < S; base += kWave) {
@@ -163,9 +225,11 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
             const uint32_t zs = base + static_cast<uint32_t>(__builtin_ctzll(zmask));
             zmask &= zmask - 1;
             for (uint32_t e = lane; e < G * LPT; e += kWave) {
-                const uint32_t g = e / LPT, c4 = e % LPT;
-                *reinterpret_cast<float4*>(a.out + (static_cast<uint64_t>(zs) * a.num_heads + h0 + g) * HS + 4 * c4) =
-                    f4_zero();
+                const uint32_t g = e / LPT, c = e % LPT;
+#pragma unroll
+                for (int u = 0; u < EPL / 4; ++u)
+                    *reinterpret_cast<float4*>(a.out + (static_cast<uint64_t>(zs) * a.num_heads + h0 + g) * HS +
+                                               EPL * c + 4 * u) = f4_zero();
             }
         }
     }
@@ -216,22 +280,22 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
         }
     };
 
-    const float* kbase = a.key_cache + static_cast<uint64_t>(kvh) * a.block_size * HS + 4 * col;
-    const float* vbase = a.value_cache + static_cast<uint64_t>(kvh) * a.block_size * HS + 4 * col;
+    const E* kbase = static_cast<const E*>(a.key_cache) + static_cast<uint64_t>(kvh) * a.block_size * HS + EPL * col;
+    const E* vbase = static_cast<const E*>(a.value_cache) + static_cast<uint64_t>(kvh) * a.block_size * HS + EPL * col;
     const uint64_t block_stride = static_cast<uint64_t>(a.num_kv_heads) * a.block_size * HS;
 
-    // Row offsets (floats from kbase) of the lane's positions in chunk m; an
+    // Row offsets (elements from kbase) of the lane's positions in chunk m; an
     // invalid position gets ~0u.
-    auto rows_of = [&](const Meta& m, uint64_t (&row)[kLoadsPerChunk]) {
+    auto rows_of = [&](const Meta& m, uint64_t (&row)[NL]) {
         const uint32_t c0 = m.k * T;
         const uint32_t q0 = c0 / a.block_size, r0 = c0 % a.block_size;
         const uint32_t* bt = a.block_tables + static_cast<uint64_t>(m.s) * a.max_num_blocks_per_seq;
 #pragma unroll
-        for (int i = 0; i < kLoadsPerChunk; ++i) {
+        for (int i = 0; i < NL; ++i) {
             const uint32_t d = i * TPI + grp_l;
             const uint32_t t = r0 + d;
             // t < block_size + T: one step when block_size >= T, else an exact
-            // float quotient (t < 256, so t + 1/2 is at least 1/256 of a block
+            // float quotient (t < 512, so t + 1/2 is at least 1/512 of a block
             // away from a multiple of block_size).
             const uint32_t qt = a.block_size >= T ? static_cast<uint32_t>(t >= a.block_size)
                                                  : static_cast<uint32_t>((static_cast<float>(t) + 0.5f) * a.inv_block_size);
@@ -248,54 +312,60 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
         }
     };
 
+    typedef unit_t<E> U;
     struct Buf {
-        f32x4 k[kLoadsPerChunk], v[kLoadsPerChunk];
+        U k[NL], v[NL];
     };
-    auto issue = [&](const uint64_t (&row)[kLoadsPerChunk], Buf& b) {
+    auto issue = [&](const uint64_t (&row)[NL], Buf& b) {
 #pragma unroll
-        for (int i = 0; i < kLoadsPerChunk; ++i) {
+        for (int i = 0; i < NL; ++i) {
             if (row[i] != ~0ull) {
-                b.k[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kbase + row[i]));
-                b.v[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vbase + row[i]));
+                b.k[i] = __builtin_nontemporal_load(reinterpret_cast<const U*>(kbase + row[i]));
+                b.v[i] = __builtin_nontemporal_load(reinterpret_cast<const U*>(vbase + row[i]));
             } else {
-                b.k[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                b.v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                b.k[i] = U{};
+                b.v[i] = U{};
             }
         }
     };
-    auto load_q = [&](uint32_t s, float4 (&qv)[G]) {
+    auto load_q = [&](uint32_t s, float (&qv)[G][EPL]) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float4 x = *reinterpret_cast<const float4*>(a.q + static_cast<uint64_t>(s) * a.q_stride +
-                                                        static_cast<uint64_t>(h0 + g) * HS + 4 * col);
-            qv[g] = make_float4(x.x * a.scale_log2, x.y * a.scale_log2, x.z * a.scale_log2, x.w * a.scale_log2);
-        }
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int u = 0; u < EPL / 4; ++u) {
+                const float4 x = *reinterpret_cast<const float4*>(a.q + static_cast<uint64_t>(s) * a.q_stride +
+                                                                  static_cast<uint64_t>(h0 + g) * HS + EPL * col + 4 * u);
+                qv[g][4 * u] = x.x * a.scale_log2;
+                qv[g][4 * u + 1] = x.y * a.scale_log2;
+                qv[g][4 * u + 2] = x.z * a.scale_log2;
+                qv[g][4 * u + 3] = x.w * a.scale_log2;
+            }
     };
 
     // Online-softmax state of the current piece.
     float m_run[G], l_run[G];
-    float4 acc[G];
+    float acc[G][EPL];
     auto reset = [&]() {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             m_run[g] = -INFINITY;
             l_run[g] = 0.0f;
-            acc[g] = f4_zero();
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
         }
     };
 
-    auto process = [&](const Meta& m, const Buf& b, const float4 (&qv)[G]) {
+    auto process = [&](const Meta& m, const Buf& b, const float (&qv)[G][EPL]) {
         const uint32_t c0 = m.k * T;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float z[kLoadsPerChunk];
+            float z[NL];
             float cmax = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < kLoadsPerChunk; ++i) {
-                float p = qv[g].x * b.k[i].x;
-                p = fmaf(qv[g].y, b.k[i].y, p);
-                p = fmaf(qv[g].z, b.k[i].z, p);
-                p = fmaf(qv[g].w, b.k[i].w, p);
+            for (int i = 0; i < NL; ++i) {
+                float p = qv[g][0] * unit_elem(b.k[i], 0);
+#pragma unroll
+                for (int e = 1; e < EPL; ++e) p = fmaf(qv[g][e], unit_elem(b.k[i], e), p);
                 p = group_sum<LPT>(p);
                 z[i] = c0 + i * TPI + grp_l < m.L ? p : -INFINITY;
                 cmax = fmaxf(cmax, z[i]);
@@ -304,18 +374,19 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
             const float alpha = exp2f(m_run[g] - mn);
             m_run[g] = mn;
             float l = l_run[g] * alpha;
-            float4 o = make_float4(acc[g].x * alpha, acc[g].y * alpha, acc[g].z * alpha, acc[g].w * alpha);
+            float o[EPL];
 #pragma unroll
-            for (int i = 0; i < kLoadsPerChunk; ++i) {
+            for (int e = 0; e < EPL; ++e) o[e] = acc[g][e] * alpha;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
                 const float p = exp2f(z[i] - mn);
                 l += p;
-                o.x = fmaf(p, b.v[i].x, o.x);
-                o.y = fmaf(p, b.v[i].y, o.y);
-                o.z = fmaf(p, b.v[i].z, o.z);
-                o.w = fmaf(p, b.v[i].w, o.w);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, unit_elem(b.v[i], e), o[e]);
             }
             l_run[g] = l;
-            acc[g] = o;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[g][e] = o[e];
         }
     };
 
@@ -329,21 +400,22 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
     auto flush = [&](const Meta& m, uint32_t kfirst) {
         const uint32_t nc = (m.L + T - 1) / T;
         float l_tot[G];
-        float4 o[G];
+        float o[G][EPL];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             l_tot[g] = groups_sum<LPT>(l_run[g]);
-            o[g] = make_float4(groups_sum<LPT>(acc[g].x), groups_sum<LPT>(acc[g].y), groups_sum<LPT>(acc[g].z),
-                               groups_sum<LPT>(acc[g].w));
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[g][e] = groups_sum<LPT>(acc[g][e]);
         }
         if (kfirst == 0 && m.k + 1 == nc) {
             if (grp_l == 0) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const float inv = 1.0f / l_tot[g];
-                    *reinterpret_cast<float4*>(a.out + (static_cast<uint64_t>(m.s) * a.num_heads + h0 + g) * HS +
-                                               4 * col) =
-                        make_float4(o[g].x * inv, o[g].y * inv, o[g].z * inv, o[g].w * inv);
+                    float x[EPL];
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) x[e] = o[g][e] * inv;
+                    store_out(static_cast<uint64_t>(m.s) * a.num_heads + h0 + g, col, x);
                 }
             }
             return;
@@ -354,11 +426,9 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
         if (grp_l == 0) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                float* pa = a.part_acc + (rec * G + g) * HS + 4 * col;
-                store_coherent(pa + 0, o[g].x);
-                store_coherent(pa + 1, o[g].y);
-                store_coherent(pa + 2, o[g].z);
-                store_coherent(pa + 3, o[g].w);
+                float* pa = a.part_acc + (rec * G + g) * HS + EPL * col;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) store_coherent(pa + e, o[g][e]);
                 if (col == 0) {
                     store_coherent(a.part_ml + (rec * G + g) * 2 + 0, m_run[g]);
                     store_coherent(a.part_ml + (rec * G + g) * 2 + 1, l_tot[g]);
@@ -381,21 +451,24 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float M = -INFINITY, Lsum = 0.0f;
-            float4 A = f4_zero();
+            float A[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) A[e] = 0.0f;
             for (uint32_t r = grp_l; r < nrec; r += 4 * TPI) {
                 float mr[4], lr[4];
-                float4 ar[4];
+                float ar[4][EPL];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const uint32_t ri = r + u * TPI;
                     if (ri < nrec) {
-                        const float* pa = a.part_acc + ((r0 + ri) * G + g) * HS + 4 * col;
-                        ar[u] = make_float4(load_coherent(pa), load_coherent(pa + 1), load_coherent(pa + 2),
-                                            load_coherent(pa + 3));
+                        const float* pa = a.part_acc + ((r0 + ri) * G + g) * HS + EPL * col;
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) ar[u][e] = load_coherent(pa + e);
                         mr[u] = load_coherent(a.part_ml + ((r0 + ri) * G + g) * 2);
                         lr[u] = load_coherent(a.part_ml + ((r0 + ri) * G + g) * 2 + 1);
                     } else {
-                        ar[u] = f4_zero();
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) ar[u][e] = 0.0f;
                         mr[u] = -INFINITY;
                         lr[u] = 0.0f;
                     }
@@ -406,20 +479,21 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
                     const float Mn = fmaxf(M, mr[u]);
                     const float s0 = exp2f(M - Mn), s1 = exp2f(mr[u] - Mn);
                     Lsum = Lsum * s0 + lr[u] * s1;
-                    A = make_float4(A.x * s0 + ar[u].x * s1, A.y * s0 + ar[u].y * s1, A.z * s0 + ar[u].z * s1,
-                                    A.w * s0 + ar[u].w * s1);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) A[e] = A[e] * s0 + ar[u][e] * s1;
                     M = Mn;
                 }
             }
             const float Mg = groups_max<LPT>(M);
             const float sc = M == -INFINITY ? 0.0f : exp2f(M - Mg);
             Lsum = groups_sum<LPT>(Lsum * sc);
-            A = make_float4(groups_sum<LPT>(A.x * sc), groups_sum<LPT>(A.y * sc), groups_sum<LPT>(A.z * sc),
-                            groups_sum<LPT>(A.w * sc));
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) A[e] = groups_sum<LPT>(A[e] * sc);
             if (grp_l == 0) {
                 const float inv = 1.0f / Lsum;
-                *reinterpret_cast<float4*>(a.out + (static_cast<uint64_t>(m.s) * a.num_heads + h0 + g) * HS +
-                                           4 * col) = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) A[e] *= inv;
+                store_out(static_cast<uint64_t>(m.s) * a.num_heads + h0 + g, col, A);
             }
         }
     };
@@ -427,9 +501,9 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
     // ---- pipeline: block ids two chunks ahead, rows one chunk ahead ----
     reset();
     Meta mc{cs, ck, cL, cbefore};
-    uint64_t row_c[kLoadsPerChunk], row_n[kLoadsPerChunk];
+    uint64_t row_c[NL], row_n[NL];
     rows_of(mc, row_c);
-    float4 qv[G], qn[G];
+    float qv[G][EPL], qn[G][EPL];
     load_q(mc.s, qv);
     Buf bA, bB;
     issue(row_c, bA);
@@ -460,7 +534,9 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
             kfirst = mn.k;
             if (more) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) qv[g] = qn[g];
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) qv[g][e] = qn[g][e];
             }
         }
         mc = mn;
@@ -473,34 +549,52 @@ __global__ __launch_bounds__(256, 2) void f32_decode_kernel(F32DecodeArgs a) {
     }
 }
 
-template <int LPT>
-hipError_t launch_lpt(const F32DecodeArgs& a, dim3 grid, hipStream_t st) {
+template <typename E, int LPT>
+hipError_t launch_lpt(const BaselineDecodeArgs& a, dim3 grid, hipStream_t st) {
     switch (a.group) {
-        case 4: hipLaunchKernelGGL((f32_decode_kernel<LPT, 4>), grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((f32_decode_kernel<LPT, 2>), grid, dim3(256), 0, st, a); break;
-        default: hipLaunchKernelGGL((f32_decode_kernel<LPT, 1>), grid, dim3(256), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((baseline_decode_kernel<E, LPT, 4>), grid, dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((baseline_decode_kernel<E, LPT, 2>), grid, dim3(256), 0, st, a); break;
+        default: hipLaunchKernelGGL((baseline_decode_kernel<E, LPT, 1>), grid, dim3(256), 0, st, a); break;
     }
     return hipGetLastError();
 }
 
+// head_size / EPL lanes per row
+template <typename E>
+hipError_t launch_elem(const BaselineDecodeArgs& a, dim3 grid, hipStream_t st) {
+    constexpr int EPL = epl<E>();
+    switch (a.head_size) {
+        case 16: return launch_lpt<E, 16 / EPL>(a, grid, st);
+        case 32: return launch_lpt<E, 32 / EPL>(a, grid, st);
+        case 64: return launch_lpt<E, 64 / EPL>(a, grid, st);
+        case 128: return launch_lpt<E, 128 / EPL>(a, grid, st);
+        case 256: return launch_lpt<E, 256 / EPL>(a, grid, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-hipError_t launch_f32_cache_write(const F32CacheWriteArgs& a, hipStream_t stream) {
-    const uint64_t n = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads * (a.head_size / 4);
+hipError_t launch_baseline_write(const BaselineWriteArgs& a, hipStream_t stream) {
+    const uint32_t epl_ = a.elem_bytes == 2 ? 8u : 4u;
+    const uint64_t n = static_cast<uint64_t>(a.num_tokens) * a.num_kv_heads * (a.head_size / epl_);
     const bool vec4 = (reinterpret_cast<uintptr_t>(a.key) % 16 == 0) && (reinterpret_cast<uintptr_t>(a.value) % 16 == 0) &&
                       a.key_stride % 4 == 0 && a.value_stride % 4 == 0;
-    hipLaunchKernelGGL(f32_cache_write_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, stream, a, vec4);
+    const dim3 grid(static_cast<uint32_t>((n + 255) / 256));
+    if (a.elem_bytes == 2) hipLaunchKernelGGL(baseline_write_kernel<uint16_t>, grid, dim3(256), 0, stream, a, vec4);
+    else hipLaunchKernelGGL(baseline_write_kernel<float>, grid, dim3(256), 0, stream, a, vec4);
     return hipGetLastError();
 }
 
-F32DecodePlan plan_f32_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads, uint32_t head_size) {
-    F32DecodePlan p{};
+BaselineDecodePlan plan_baseline_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                                        uint32_t head_size) {
+    BaselineDecodePlan p{};
     const uint32_t n_rep = num_heads / num_kv_heads;
     p.group = n_rep % 4 == 0 ? 4 : (n_rep % 2 == 0 ? 2 : 1);
     p.num_groups = n_rep / p.group;
     // Q8KV_F32_DECODE_WAVES overrides the persistent wave count (tests use it
     // to move the boundaries between the waves' chunk ranges).
-    uint64_t target = kF32DecodeWaves;
+    uint64_t target = kBaselineDecodeWaves;
     if (const char* e = getenv("Q8KV_F32_DECODE_WAVES")) {
         const long v = atol(e);
         if (v >= 1 && v <= (1L << 20)) target = static_cast<uint64_t>(v);
@@ -518,16 +612,9 @@ F32DecodePlan plan_f32_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t nu
     return p;
 }
 
-hipError_t launch_f32_decode(const F32DecodeArgs& a, const F32DecodePlan& p, hipStream_t st) {
+hipError_t launch_baseline_decode(const BaselineDecodeArgs& a, const BaselineDecodePlan& p, hipStream_t st) {
     const dim3 grid(static_cast<uint32_t>((p.num_waves + 3) / 4));
-    switch (a.head_size) {
-        case 16: return launch_lpt<4>(a, grid, st);
-        case 32: return launch_lpt<8>(a, grid, st);
-        case 64: return launch_lpt<16>(a, grid, st);
-        case 128: return launch_lpt<32>(a, grid, st);
-        case 256: return launch_lpt<64>(a, grid, st);
-    }
-    return hipErrorInvalidValue;
+    return a.elem_bytes == 2 ? launch_elem<uint16_t>(a, grid, st) : launch_elem<float>(a, grid, st);
 }
 
 }  // namespace q8kv

@@ -163,39 +163,42 @@ hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_
 bool norm_rope_decode_supported(uint32_t head_size, uint32_t num_heads, uint32_t num_kv_heads, uint32_t block_size,
                                 const uint32_t* key_cache, const uint32_t* value_cache);
 
-// ---- f32 paged-cache baseline: cache [num_blocks, num_kv_heads, block_size, head_size] f32 ----
+// ---- full-width paged-cache baselines: cache [num_blocks, num_kv_heads, block_size, head_size] ----
+// of f32 elements (elem_bytes 4) or bfloat16 ones (elem_bytes 2).
 
-constexpr uint32_t kF32DecodeWaves = 2048;   // persistent waves: 8 per CU (2 workgroups of 4)
+constexpr uint32_t kBaselineDecodeWaves = 2048;   // persistent waves: 8 per CU (2 workgroups of 4)
 
-struct F32CacheWriteArgs {
+struct BaselineWriteArgs {
     const float* key;
     const float* value;
-    float* key_cache;
-    float* value_cache;
+    void* key_cache;
+    void* value_cache;
     const uint32_t* slot_mapping;
     uint32_t key_stride, value_stride;
     uint32_t num_tokens, num_kv_heads, head_size, block_size, num_blocks;
+    uint32_t elem_bytes;     // 4: f32 copies; 2: bfloat16, rounded to nearest, ties to even
 };
 
-hipError_t launch_f32_cache_write(const F32CacheWriteArgs& a, hipStream_t stream);
+hipError_t launch_baseline_write(const BaselineWriteArgs& a, hipStream_t stream);
 
 // Row groups are (kv head, group of `group` query heads); each has
 // waves_per_rg persistent waves over its chunk list and recs_per_rg partial
 // record slots.
-struct F32DecodePlan {
+struct BaselineDecodePlan {
     uint32_t group, num_groups, waves_per_rg;
     uint64_t recs_per_rg;    // 64-bit: no wrap for extreme sequence counts
     uint64_t num_waves;
     size_t counters_offset, ml_offset, acc_offset, bytes;
 };
 
-F32DecodePlan plan_f32_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads, uint32_t head_size);
+BaselineDecodePlan plan_baseline_decode(uint32_t num_seqs, uint32_t num_heads, uint32_t num_kv_heads,
+                                        uint32_t head_size);
 
-struct F32DecodeArgs {
+struct BaselineDecodeArgs {
     float* out;
     const float* q;
-    const float* key_cache;
-    const float* value_cache;
+    const void* key_cache;   // elem_bytes-wide elements
+    const void* value_cache;
     const uint32_t* block_tables;
     const uint32_t* context_lens;
     uint32_t* counters;      // [row group, seq]: arrivals of a sequence's waves; zero between calls
@@ -204,10 +207,11 @@ struct F32DecodeArgs {
     uint32_t q_stride, max_num_blocks_per_seq, max_context_len;
     uint32_t num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks;
     uint32_t group, num_groups, waves_per_rg, recs_per_rg;
+    uint32_t elem_bytes;     // 4 (f32) or 2 (bfloat16)
     float inv_block_size;    // 1 / block_size in binary32
     float scale_log2;        // softmax scale * log2(e)
 };
 
-hipError_t launch_f32_decode(const F32DecodeArgs& a, const F32DecodePlan& p, hipStream_t stream);
+hipError_t launch_baseline_decode(const BaselineDecodeArgs& a, const BaselineDecodePlan& p, hipStream_t stream);
 
 }  // namespace q8kv

@@ -48,6 +48,14 @@ def poison_cache_f32(num_blocks_total: int, num_kv_heads: int, block_size: int, 
     return np.full((num_blocks_total, num_kv_heads, block_size, head_size), np.nan, dtype=np.float32)
 
 
+POISON_BF16 = 0x7FC1      # a quiet NaN encoding
+
+
+def poison_cache_bf16(num_blocks_total: int, num_kv_heads: int, block_size: int, head_size: int) -> np.ndarray:
+    """A bfloat16 cache [num_blocks_total, Hkv, bs, hs] (uint16 encodings) with every element NaN."""
+    return np.full((num_blocks_total, num_kv_heads, block_size, head_size), POISON_BF16, dtype=np.uint16)
+
+
 @dataclasses.dataclass
 class Workload:
     name: str

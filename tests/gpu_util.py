@@ -19,6 +19,15 @@ def f32_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
 
 
+def bf16_dev(a: np.ndarray) -> torch.Tensor:
+    """uint16 bfloat16 encodings to a device int16 tensor holding the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(DEV)
+
+
+def bf16_host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
 def nan_out(S: int, H: int, hs: int) -> torch.Tensor:
     """Output buffer filled with NaN, so a row the decode never writes fails
     the comparison instead of passing on memory that happens to be zero."""

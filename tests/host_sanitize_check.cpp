@@ -2,7 +2,7 @@
 // UndefinedBehaviorSanitizer (test infrastructure; no GPU is touched).
 //
 // Built by tests/test_host_sanitize.py from the library's own api.hip,
-// decode.hip and f32_baseline.hip (their validation, split planning and
+// decode.hip and baseline_cache.hip (their validation, split planning and
 // workspace sizing), with the host pass instrumented.  The launchers of the
 // other translation units are replaced below by stubs that report an error:
 // no call here reaches a kernel.  Each entry point is called with arguments
@@ -130,6 +130,13 @@ static void decode_validation() {
                                100, 2, 4, 2, 96, 16, 64, 0.1f, ws, 1u << 30, nullptr) == Q8_ERR_UNSUPPORTED);
     EXPECT(q8_f32_paged_decode(out, q, 512, reinterpret_cast<const float*>(u), reinterpret_cast<const float*>(u), u, 8, u,
                                100, 2, 4, 2, 128, 16, 64, 0.1f, nullptr, 0, nullptr) == Q8_ERR_WORKSPACE);
+    // bf16 baseline
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(u);
+    EXPECT(q8_bf16_paged_decode(out, q, 512, b, b, u, 8, u, 100, 2, 4, 2, 96, 16, 64, 0.1f, ws, 1u << 30, nullptr) ==
+           Q8_ERR_UNSUPPORTED);
+    EXPECT(q8_bf16_paged_decode(out, q, 512, b, b, u, 8, u, 100, 2, 4, 2, 128, 16, 64, 0.1f, nullptr, 0, nullptr) ==
+           Q8_ERR_WORKSPACE);
+    EXPECT(q8_bf16_paged_decode_workspace_bytes(4, 3, 2, 128) == 0);
 }
 
 static void writer_and_step_validation() {
@@ -144,6 +151,11 @@ static void writer_and_step_validation() {
     EXPECT(q8_cache_write(k, 1024, k, 1024, c, c, sl, 0xFFFFFFFFu, 8, 128, 16, 8, nullptr) == Q8_ERR_SHAPE);
     EXPECT(q8_f32_cache_write(k, 256, k, 256, reinterpret_cast<float*>(fake(0x3004)), reinterpret_cast<float*>(c), sl, 4,
                               2, 128, 16, 8, nullptr) == Q8_ERR_UNSUPPORTED);
+    uint16_t* bc = reinterpret_cast<uint16_t*>(c);
+    EXPECT(q8_bf16_cache_write(k, 256, k, 256, bc, bc, sl, 4, 2, 20, 16, 8, nullptr) == Q8_ERR_UNSUPPORTED);
+    EXPECT(q8_bf16_cache_write(k, 256, k, 256, reinterpret_cast<uint16_t*>(fake(0x3008)), bc, sl, 4, 2, 128, 16, 8,
+                               nullptr) == Q8_ERR_UNSUPPORTED);
+    EXPECT(q8_bf16_cache_write(nullptr, 256, k, 256, bc, bc, sl, 4, 2, 128, 16, 8, nullptr) == Q8_ERR_NULL);
     // norm + rotary
     float* o = static_cast<float*>(fake(0x5000));
     const float* w = k;

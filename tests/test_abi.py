@@ -231,6 +231,38 @@ def test_f32_cache_write_null_empty_and_alignment(lib):
                                   None) == 5
 
 
+@pytest.mark.parametrize("kw,want", [
+    (dict(hs=130), 2), (dict(hs=512), 2), (dict(H=5), 2), (dict(bs=0), 2), (dict(q_stride=511), 2),
+    (dict(scale=float("inf")), 2), (dict(max_nb=0), 2), (dict(hs=96, q_stride=4 * 96), 5),
+    (dict(q_stride=514), 5), (dict(mcl=1 << 31), 5), (dict(out=None), 1), (dict(cl=None), 1),
+    (dict(kc=ctypes.c_void_p(0x1008)), 5), (dict(vc=ctypes.c_void_p(0x1002)), 5), (dict(ws=None), 3),
+    (dict(wsb=16), 3), (dict(S=0), 0),
+])
+def test_bf16_decode_validation(lib, kw, want):
+    assert lib.q8_bf16_paged_decode(*f32_args(**kw)) == want
+
+
+def test_bf16_workspace_is_the_f32_plan(lib):
+    for shape in [(64, 32, 8, 128), (3, 12, 2, 64), (5, 6, 2, 32), (1, 16, 16, 256), (2, 4, 3, 128)]:
+        assert lib.q8_bf16_paged_decode_workspace_bytes(*shape) == lib.q8_f32_paged_decode_workspace_bytes(*shape)
+
+
+@pytest.mark.parametrize("hs,bs,hkv,stride,nb,want", [
+    (0, 16, 2, 256, 8, 2), (6, 16, 2, 256, 8, 2), (260, 16, 1, 260, 8, 2), (128, 0, 2, 256, 8, 2),
+    (128, 16, 0, 256, 8, 2), (128, 16, 2, 255, 8, 2), (128, 16, 2, 256, 0, 2),
+    (20, 16, 2, 40, 8, 5), (12, 16, 1, 12, 8, 5),        # head_size not a multiple of 8
+])
+def test_bf16_cache_write_shape_errors(lib, hs, bs, hkv, stride, nb, want):
+    assert lib.q8_bf16_cache_write(FAKE, stride, FAKE, stride, FAKE, FAKE, FAKE, 4, hkv, hs, bs, nb, None) == want
+
+
+def test_bf16_cache_write_null_empty_and_alignment(lib):
+    assert lib.q8_bf16_cache_write(None, 256, FAKE, 256, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, None) == 1
+    assert lib.q8_bf16_cache_write(None, 256, None, 256, None, None, None, 0, 2, 128, 16, 8, None) == 0
+    assert lib.q8_bf16_cache_write(FAKE, 256, FAKE, 256, ctypes.c_void_p(0x1008), FAKE, FAKE, 4, 2, 128, 16, 8,
+                                   None) == 5
+
+
 # ---- per-head RMSNorm + partial rotary step ----
 
 def test_rope_table_validation(lib):

@@ -2,7 +2,7 @@
 (CPU only, no GPU touched).
 
 tests/host_sanitize_check.cpp is linked with the library's api.hip, decode.hip
-and f32_baseline.hip (argument validation, split planning, workspace sizing)
+and baseline_cache.hip (argument validation, split planning, workspace sizing)
 with the host pass instrumented (-Xarch_host before each -fsanitize, so no GPU
 code is built with a sanitizer), and the other launchers stubbed.  It calls
 every entry point with arguments that fail validation, up to 32-bit extremes,
@@ -29,7 +29,7 @@ def test_library_host_code_clean_under_asan_and_ubsan(tmp_path):
     cmd = ([hipcc, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + san +
            ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "decode.hip"), os.path.join(CSRC, "f32_baseline.hip"),
+            os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "decode.hip"), os.path.join(CSRC, "baseline_cache.hip"),
             "-x", "hip", os.path.join(ROOT, "tests", "host_sanitize_check.cpp"), "-o", exe])
     build = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     if build.returncode != 0 and "asan" in (build.stderr + build.stdout).lower():
