@@ -2,7 +2,7 @@
 visible-list), the one-launch step, multi-row decode, the cache writer
 (bit-exact; small and batched sizes, pads), block selection (lists, counts
 and bitmasks bit-exact), the q + K/V norm and rotary launch, the decode step
-with the norm and rotary step inside it, and the f32-cache decode, over random head
+with the norm and rotary step inside it, and the f32- and bf16-cache decodes, over random head
 sizes, block sizes, GQA ratios, batch sizes on both sides of the 64-sequence
 window, length mixes (empty, one token, block and chunk edges, long), clamps
 and forced wavefront counts.  Every case is drawn from a fixed seed and named
@@ -106,12 +106,14 @@ def test_random_case(oracle_mod, i):
         if p["kind"] == "write":
             run_write_case(oracle_mod, p)
         elif p["kind"] == "f32":
+            from test_gpu_bf16 import Bf16Gpu
             from test_gpu_f32 import F32Gpu
             from gpu_util import assert_close
             hs = {16: 16, 32: 32, 48: 64, 64: 64, 68: 64, 96: 128, 128: 128, 192: 256, 256: 256}[p["hs"]]
             if p["waves"] is not None:
                 os.environ["Q8KV_F32_DECODE_WAVES"] = str(p["waves"])
-            c = F32Gpu(oracle_mod, p["seed"], p["S"], p["H"], p["Hkv"], hs, p["bs"], p["lens"])
+            cls = Bf16Gpu if (i // 9) % 2 else F32Gpu          # alternate the two baseline caches
+            c = cls(oracle_mod, p["seed"], p["S"], p["H"], p["Hkv"], hs, p["bs"], p["lens"])
             assert_close(c.gpu(max_context_len=p["mcl"]), c.oracle(oracle_mod, max_context_len=p["mcl"]), name)
         elif p["kind"] == "select":
             run_select_case(oracle_mod, p)
