@@ -188,7 +188,7 @@ def main():
         allj = last_json(os.path.join(d, "trace_all.log"))
         out = [
             "# rocprofv3 kernel trace of every kernel the bench runs, Llama-3-8B-shaped batch",
-            "# (step, two-launch reference, 4-row decode, f32-cache step, norm + rotary step, 16384-token bulk",
+            "# (step, two-launch reference, 4-row decode, f32- and bf16-cache steps, norm + rotary step, 16384-token bulk",
             "# writes, selected-token step: block selection + visible-list decode, long-context decode,",
             "# MHA head_size=256 decode and its 4096-token padded write, and the measurement kernels of the",
             "# practical HBM ceiling)",
@@ -207,7 +207,8 @@ def main():
             out.append("%-60s %9d %5d %9.2f %9.2f %9.2f %5d %6d" % (
                 nm[:60], grid, len(durs), statistics.mean(durs), statistics.median(durs), max(durs), vgpr, lds))
         out += ["", "bench.py line of the same run (reference legs):"]
-        for k in ("two_launch_reference", "multi_row_decode", "f32_cache_reference", "norm_rope_step",
+        for k in ("two_launch_reference", "multi_row_decode", "f32_cache_reference", "bf16_cache_reference",
+                  "norm_rope_step",
                   "selected_step", "long_context", "mha256_decode", "mha256_write", "practical_ceiling"):
             out.append("  %s: %s" % (k, json.dumps(allj.get(k))))
         with open(os.path.join(ROOT, "profiles", "llama_step_all_kernels_trace.txt"), "w") as f:
@@ -355,8 +356,8 @@ def main():
                     acc[(r["Kernel_Name"], grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
             durs = {k: statistics.median(v) for k, v in acc.items()}
         out = [
-            "# HBM traffic of every kernel the bench runs (step, two-launch reference, 4-row decode, f32-cache",
-            "# step, norm + rotary step and 16384-token bulk writes, selected-token step, long-context and",
+            "# HBM traffic of every kernel the bench runs (step, two-launch reference, 4-row decode, f32- and",
+            "# bf16-cache steps, norm + rotary step and 16384-token bulk writes, selected-token step, long-context and",
             "# MHA-256 decodes, the padded 4096-token write, ceiling kernels), median per dispatch",
             "# of each (kernel, grid), calibrated by the plain copy as in q8_paged_decode_llama_traffic.txt",
             "# (FETCH_SIZE x %.4f, WRITE_SIZE x %.4f)" % (factor["FETCH_SIZE"], factor["WRITE_SIZE"]),
@@ -384,8 +385,8 @@ def main():
             out.append("%-62s %9d %5d %14.0f %13.0f %9s %9s" % (
                 nm[:62], key[1], len(cf[key]), rd, wr, "%.2f" % us if us else "-",
                 "%.0f" % ((rd + wr) / (us * 1e-6) / 1e9) if us else "-"))
-        mr, f32, nr, sel, lg, md, mw = (jf.get(k) or {} for k in (
-            "multi_row_decode", "f32_cache_reference", "norm_rope_step", "selected_step", "long_context",
+        mr, f32, b16, nr, sel, lg, md, mw = (jf.get(k) or {} for k in (
+            "multi_row_decode", "f32_cache_reference", "bf16_cache_reference", "norm_rope_step", "selected_step", "long_context",
             "mha256_decode", "mha256_write"))
         out += [
             "",
@@ -394,6 +395,7 @@ def main():
             "  4-row decode: the same prefixes, read once when the rows of a sequence share the reads: %d;"
             " counted per row: %s" % (eff, mr.get("per_row_kv_bytes")),
             "  f32-cache decode: %s" % f32.get("f32_kv_bytes"),
+            "  bf16-cache decode: %s" % b16.get("bf16_kv_bytes"),
             "  bulk writes (16384 tokens): %s" % nr.get("bulk_algorithmic_bytes"),
             "  selected-token decode: %s" % sel.get("effective_kv_bytes"),
             "  long-context decode: %s" % lg.get("effective_kv_bytes"),
