@@ -367,7 +367,18 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup, (HS4P <= 32 && (SEGR == 0 |
 
     const uint32_t lane = threadIdx.x % kWave;
     const uint32_t r = lane & 15, g = lane >> 4;
-    const uint32_t gw = blockIdx.x * kWavesPerGroup + wid;      // persistent wavefront index
+    // Workgroups are dispatched to the XCDs in turn (workgroup b to XCD
+    // b mod 8).  Within each span (the first and the second workgroup of
+    // every CU), workgroup numbers are regrouped so that consecutive ones run
+    // on one XCD: the row groups of the same chunk range (adjacent kv heads'
+    // tiles of the same blocks, which share lines at the tile edges) then
+    // meet in one L2.
+    uint32_t bl = blockIdx.x;
+    if (c.xcd_span) {
+        const uint32_t span0 = bl - bl % c.xcd_span, b = bl % c.xcd_span;
+        bl = span0 + (b % kXcds) * (c.xcd_span / kXcds) + b / kXcds;
+    }
+    const uint32_t gw = bl * kWavesPerGroup + wid;      // persistent wavefront index
     if (gw >= c.num_rg * c.waves_per_rg) return;
     const uint32_t rg = gw % c.num_rg;
     const uint32_t j = gw / c.num_rg;

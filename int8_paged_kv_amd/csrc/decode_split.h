@@ -30,6 +30,7 @@ struct SplitConsts {
     uint32_t tiled_ok;      // segment copies are legal (alignment, block_size shape)
     uint32_t q_vec_ok;      // q rows of every sequence are 16-byte aligned
     uint32_t young_from;    // first wave (of a row group) in the grid's second workgroup per CU; >= waves: none
+    uint32_t xcd_span;      // XCD-aware workgroup numbering over spans of this many workgroups; 0: none
 };
 
 // The split-kernel instantiation for these arguments: one translation unit

@@ -12,6 +12,7 @@ constexpr int kWave = 64;          // CDNA wavefront width
 // a launch takes as many as the device keeps resident for its kernel, up to
 // this bound, which also sizes the workspace.
 constexpr uint32_t kMaxDecodeWaves = 2048;
+constexpr uint32_t kXcds = 8;       // MI355X: accelerator complex dies, each with its own L2
 // Cache writers: from this many (token, kv head) pairs on, each wave takes
 // kWritePairsPerWave consecutive pairs with all their loads in flight.
 constexpr uint64_t kWriteBatchMinPairs = 32768;
