@@ -177,8 +177,9 @@ hipError_t launch_decode(const DecodeArgs& a, uint32_t max_positions, hipStream_
     // XCD-aware numbering (a permutation of the workgroups within each half
     // of the grid, so that the second-workgroup waves stay the second half),
     // for two resident workgroups per CU.  Measured: Llama-shaped step
-    // 63.75 -> 63.46 us; with one workgroup per CU the 32K-token decode went
-    // from 130.5 to 136.4 us, so those launches keep the plain numbering.
+    // 63.75 -> 63.46 us; with one workgroup per CU it gave no gain (the
+    // 32K-token decode was once 4% slower), so those launches keep the plain
+    // numbering.
     const uint64_t groups = (p.num_waves + kWavesPerGroup - 1) / kWavesPerGroup;
     c.xcd_span = 0;
     if (!decode_wave_override() && per_cu == 2 && groups % (2 * kXcds) == 0)
