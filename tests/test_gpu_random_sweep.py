@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-N_CASES = 144
+N_CASES = 432
 HEAD_SIZES = [16, 32, 48, 64, 68, 96, 128, 192, 256]
 BLOCK_SIZES = [1, 4, 5, 8, 16, 32, 64, 128]
 KV_HEADS = [1, 2, 3, 4, 8]
@@ -157,7 +157,7 @@ def test_random_case(oracle_mod, i):
         os.environ.pop("Q8KV_F32_DECODE_WAVES", None)
 
 
-N_NR_CASES = 24
+N_NR_CASES = 48
 
 
 def draw_nr(i):
