@@ -28,8 +28,9 @@
  *   - Two environment variables, meant for tests, force the number of
  *     persistent wavefronts the decodes split the batch over (otherwise:
  *     as many as the device keeps resident for the kernel, at most 2048 for
- *     the int8 decodes, and 2048 for the f32 decode): Q8KV_DECODE_WAVES (int8
- *     decodes and the decode step) and Q8KV_F32_DECODE_WAVES (f32 decode),
+ *     the int8 decodes, and 2048 for the f32 and bf16 decodes):
+ *     Q8KV_DECODE_WAVES (int8 decodes and the decode step) and
+ *     Q8KV_F32_DECODE_WAVES (the f32 and bf16 decodes),
  *     each an integer from 1 to 2^20, read by every call.  The workspace
  *     query reads the same variable, so a workspace sized under one setting
  *     must be used under it.  Results do not depend on the setting beyond

@@ -592,8 +592,9 @@ BaselineDecodePlan plan_baseline_decode(uint32_t num_seqs, uint32_t num_heads, u
     const uint32_t n_rep = num_heads / num_kv_heads;
     p.group = n_rep % 4 == 0 ? 4 : (n_rep % 2 == 0 ? 2 : 1);
     p.num_groups = n_rep / p.group;
-    // Q8KV_F32_DECODE_WAVES overrides the persistent wave count (tests use it
-    // to move the boundaries between the waves' chunk ranges).
+    // Q8KV_F32_DECODE_WAVES overrides the persistent wave count of the f32
+    // and bf16 decodes (tests use it to move the boundaries between the
+    // waves' chunk ranges).
     uint64_t target = kBaselineDecodeWaves;
     if (const char* e = getenv("Q8KV_F32_DECODE_WAVES")) {
         const long v = atol(e);
