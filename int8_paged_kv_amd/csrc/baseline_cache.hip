@@ -12,9 +12,11 @@
 // nearest bfloat16 to the f32 input (ties to even).  These kernels serve to
 // measure the int8 cache against both on the same batch.
 //
-// Decode, MI355X mapping.  The work is a pure stream of rows with about one
-// multiply-add per element, far below the VALU rate, so it stays on the VALU
-// and is laid out for the loads:
+// Decode, MI355X mapping.  The work is a stream of rows with one multiply-add
+// per element and query head for q.k and one for p.v, on the VALU.  For f32
+// that is below the rate at which HBM delivers elements; bfloat16 delivers
+// twice the elements per byte for the same arithmetic and is bound by VALU
+// issue at four query heads per row group.  Laid out for the loads:
 //   * A row of head_size elements is read by LPT lanes with 16-byte loads of
 //     EPL elements (4 f32 or 8 bfloat16, widened to f32 on use), LPT =
 //     head_size/EPL; one load instruction covers 64/LPT consecutive
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(256) void baseline_write_kernel(BaselineWriteArgs a
 // ---------------------------------------------------------------- decode ----
 
 // Positions of sequence s (the context clamp applied).
-__device__ __forceinline__ uint32_t f32_positions(const BaselineDecodeArgs& a, uint32_t s) {
+__device__ __forceinline__ uint32_t seq_positions(const BaselineDecodeArgs& a, uint32_t s) {
     const uint32_t L = a.context_lens[s];
     return L < a.max_context_len ? L : a.max_context_len;
 }
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void baseline_decode_kernel(BaselineDecodeA
     uint32_t C = 0;
     for (uint32_t base = 0; base < S; base += kWave) {
         const uint32_t s = base + lane;
-        const uint32_t L = s < S ? f32_positions(a, s) : 0;
+        const uint32_t L = s < S ? seq_positions(a, s) : 0;
         const uint32_t nc = (L + T - 1) / T;
         const uint32_t incl = wave_incl_scan(nc, lane);
         C += lane_value(incl, kWave - 1);
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void baseline_decode_kernel(BaselineDecodeA
         uint32_t acc = 0;
         for (uint32_t base = 0; base < S; base += kWave) {
             const uint32_t s = base + lane;
-            const uint32_t nc = s < S ? (f32_positions(a, s) + T - 1) / T : 0;
+            const uint32_t nc = s < S ? (seq_positions(a, s) + T - 1) / T : 0;
             const uint32_t incl = acc + wave_incl_scan(nc, lane);
             const uint64_t hit = __ballot(incl > x0);
             if (hit) {
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void baseline_decode_kernel(BaselineDecodeA
         cbefore = uniform(cbefore);
         ck = x0 - cbefore;
     }
-    uint32_t cL = uniform(f32_positions(a, cs));
+    uint32_t cL = uniform(seq_positions(a, cs));
 
     struct Meta {
         uint32_t s, k, L, before;   // sequence, chunk within it, its positions, chunks before it
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void baseline_decode_kernel(BaselineDecodeA
             ck = 0;
             do {
                 ++cs;
-                cL = uniform(f32_positions(a, cs));
+                cL = uniform(seq_positions(a, cs));
             } while (cL == 0);
         }
     };
