@@ -596,7 +596,7 @@ def main():
                 "decode_%s_kv_GBps" % kind: round(Bf / (float(tfd.mean()) * 1e-6) / 1e9, 1),
                 "decode_frac_hbm_peak": round(Bf / (float(tfd.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "int8_step_speedup": round(float(tfw.mean() + tfd.mean()) / float(t_dec.mean()), 3),
-                "note": "q8_%s_cache_write + q8_%s_paged_decode of the same step over a %s cache "
+                "note": "q8_%s_cache_write + q8_%s_paged_decode of the same step over the %s cache "
                         "[num_blocks, Hkv, bs, hs]; speedup = %s step time / int8 one-launch step time"
                         % (kind, kind, kind, kind)}
 
